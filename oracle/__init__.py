@@ -1,0 +1,199 @@
+"""Python access to the fp64 Simple GLA oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the bench's
+CPU-baseline leg may import this package; the library under
+``chunked_gated_linear_simple_amd`` never does. It shares no code with the HIP
+path: it compiles ``oracle.c`` with the host C compiler and calls it through
+ctypes on float64 numpy arrays.
+
+Layouts follow the library's: q, k are [B, H, T, d_k]; v, o, dO are
+[B, H, T, d_v]; states are [N, H, d_k, d_v]. With ``cu_seqlens`` (int array of
+N+1 offsets) the token axis is packed ([1, H, sum T, d]) and sequence n is the
+token range [cu[n], cu[n+1]).
+
+Parity status of each function is recorded in the test suite's pins
+(tests/test_oracle_pins.py); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so (plain gcc, no HIP)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-Wall", "-Wextra",
+               "-o", tmp, _SRC, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        lib.orc_decay_schedule.argtypes = [ctypes.c_int, ctypes.c_double, ctypes.c_double, _dp]
+        lib.orc_fwd.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                _dp, _dp, _dp, _dp, _dp, _dp, _dp]
+        lib.orc_bwd.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp]
+        lib.orc_decode_step.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                        _dp, _dp, _dp, _dp, _dp, _dp]
+        for f in (lib.orc_decay_schedule, lib.orc_fwd, lib.orc_bwd, lib.orc_decode_step):
+            f.restype = None
+        _lib = lib
+    return _lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    assert x.dtype == np.float64 and x.flags["C_CONTIGUOUS"]
+    return x.ctypes.data_as(_dp)
+
+
+def _f64(x):
+    if x is None:
+        return None
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def decay_schedule(H: int, t_min: float, t_max: float) -> np.ndarray:
+    lam = np.zeros(H, dtype=np.float64)
+    _load().orc_decay_schedule(H, t_min, t_max, _ptr(lam))
+    return lam
+
+
+def fwd_unit(q, k, v, lam, a=None, S0=None):
+    """One (sequence, head): q,k [T,dk], v [T,dv] -> (o [T,dv], S_final [dk,dv])."""
+    q, k, v, a, S0 = map(_f64, (q, k, v, a, S0))
+    T, dk = q.shape
+    dv = v.shape[1]
+    o = np.zeros((T, dv))
+    Sf = np.zeros((dk, dv))
+    _load().orc_fwd(T, dk, dv, float(lam), _ptr(a), _ptr(q), _ptr(k), _ptr(v), _ptr(S0),
+                    _ptr(o), _ptr(Sf))
+    return o, Sf
+
+
+def bwd_unit(q, k, v, dO, lam, a=None, S0=None, dSf=None):
+    """One (sequence, head) -> (dq, dk, dv, da [dk], dS0 [dk,dv])."""
+    q, k, v, dO, a, S0, dSf = map(_f64, (q, k, v, dO, a, S0, dSf))
+    T, dk = q.shape
+    dv = v.shape[1]
+    dq = np.zeros((T, dk))
+    dkk = np.zeros((T, dk))
+    dvv = np.zeros((T, dv))
+    da = np.zeros(dk)
+    dS0 = np.zeros((dk, dv))
+    _load().orc_bwd(T, dk, dv, float(lam), _ptr(a), _ptr(q), _ptr(k), _ptr(v), _ptr(S0),
+                    _ptr(dO), _ptr(dSf), _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(da), _ptr(dS0))
+    return dq, dkk, dvv, da, dS0
+
+
+def decode_step_unit(q, k, v, lam, a, S):
+    """One decode step for one (sequence, head); S [dk,dv] is updated in place."""
+    q, k, v, a = map(_f64, (q, k, v, a))
+    assert S.dtype == np.float64 and S.flags["C_CONTIGUOUS"]
+    o = np.zeros(v.shape[0])
+    _load().orc_decode_step(q.shape[0], v.shape[0], float(lam), _ptr(a), _ptr(q), _ptr(k),
+                            _ptr(v), _ptr(S), _ptr(o))
+    return o
+
+
+def _units(B, H, T, cu_seqlens):
+    """(n, h, token slice) for every unit, in (n, h) order."""
+    out = []
+    if cu_seqlens is None:
+        for b in range(B):
+            for h in range(H):
+                out.append((b, h, b, slice(0, T)))
+    else:
+        cu = [int(c) for c in cu_seqlens]
+        for n in range(len(cu) - 1):
+            for h in range(H):
+                out.append((n, h, 0, slice(cu[n], cu[n + 1])))
+    return out
+
+
+def fwd(q, k, v, lam, a=None, S0=None, cu_seqlens=None, units=None, threads=1):
+    """Batched forward over [B,H,T,d] (or packed with cu_seqlens).
+
+    Returns (o, S_final [N,H,dk,dv]). ``units`` restricts the work to a list of
+    (n, h) pairs (the other outputs stay zero)."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    N = B if cu_seqlens is None else len(cu_seqlens) - 1
+    o = np.zeros(v.shape, dtype=np.float64)
+    Sf = np.zeros((N, H, dk, dv), dtype=np.float64)
+    todo = _units(B, H, T, cu_seqlens)
+    if units is not None:
+        keep = set((int(n), int(h)) for n, h in units)
+        todo = [u for u in todo if (u[0], u[1]) in keep]
+
+    def run(u):
+        n, h, b, sl = u
+        oo, ss = fwd_unit(q[b, h, sl], k[b, h, sl], v[b, h, sl], lam[h],
+                          None if a is None else a[h], None if S0 is None else S0[n, h])
+        o[b, h, sl] = oo
+        Sf[n, h] = ss
+
+    if threads > 1:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(run, todo))
+    else:
+        for u in todo:
+            run(u)
+    return o, Sf
+
+
+def bwd(q, k, v, dO, lam, a=None, S0=None, dSf=None, cu_seqlens=None, units=None, threads=1):
+    """Batched backward. Returns (dq, dk, dv, da [H,dk], dS0 [N,H,dk,dv])."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    N = B if cu_seqlens is None else len(cu_seqlens) - 1
+    dq = np.zeros(q.shape)
+    dkk = np.zeros(k.shape)
+    dvv = np.zeros(v.shape)
+    da_parts = {}
+    dS0 = np.zeros((N, H, dk, dv))
+    todo = _units(B, H, T, cu_seqlens)
+    if units is not None:
+        keep = set((int(n), int(h)) for n, h in units)
+        todo = [u for u in todo if (u[0], u[1]) in keep]
+
+    def run(u):
+        n, h, b, sl = u
+        r = bwd_unit(q[b, h, sl], k[b, h, sl], v[b, h, sl], dO[b, h, sl], lam[h],
+                     None if a is None else a[h], None if S0 is None else S0[n, h],
+                     None if dSf is None else dSf[n, h])
+        dq[b, h, sl], dkk[b, h, sl], dvv[b, h, sl] = r[0], r[1], r[2]
+        da_parts[(n, h)] = r[3]
+        dS0[n, h] = r[4]
+
+    if threads > 1:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(run, todo))
+    else:
+        for u in todo:
+            run(u)
+    da = np.zeros((H, dk))
+    for (n, h) in sorted(da_parts):
+        da[h] += da_parts[(n, h)]
+    return dq, dkk, dvv, da, dS0

@@ -1,0 +1,219 @@
+/*
+ * Simple GLA oracle (fp64, token by token). TEST INFRASTRUCTURE ONLY: see
+ * oracle.h for who may use it and for the formulas it follows.
+ *
+ * Every function here is the plain definition, one token at a time, with no
+ * chunking, blocking or reordering. Citations name sections of the page
+ * "Beyond the KV cache: Training and serving i14's Laplace 3B linear attention
+ * model on AWS Trainium2 with native PyTorch" (the Laplace 3B post).
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Logistic sigmoid, evaluated so that neither branch overflows. */
+static double sigmoid(double z)
+{
+    if (z >= 0.0) {
+        return 1.0 / (1.0 + exp(-z));
+    }
+    double e = exp(z);
+    return e / (1.0 + e);
+}
+
+/* Self-augmentation gate argument z_t = sum_i a_i q_i k_i.
+ * Laplace 3B post, "GLA mixer": the gate is the query dotted with a learned
+ * per-channel rescaling (aug_balance, a) of the key. */
+static double aug_arg(int d_k, const double* a, const double* qt, const double* kt)
+{
+    double z = 0.0;
+    if (a == NULL) {
+        return 0.0;
+    }
+    for (int i = 0; i < d_k; ++i) {
+        z += a[i] * qt[i] * kt[i];
+    }
+    return z;
+}
+
+/* Decay schedule. Laplace 3B post, "Decay schedule" and "Decay schedule's
+ * reach": the per-head decays are fixed, geometric in the half-life, with
+ * half-lives T_min (head 0) to T_max (last head); a half-life of T tokens
+ * means lam^T = 1/2. */
+void orc_decay_schedule(int H, double t_min, double t_max, double* lam)
+{
+    for (int h = 0; h < H; ++h) {
+        double frac = (H > 1) ? (double)h / (double)(H - 1) : 0.0;
+        double half_life = t_min * pow(t_max / t_min, frac);
+        lam[h] = pow(2.0, -1.0 / half_life);
+    }
+}
+
+/* Forward recurrence. Laplace 3B post, "GLA mixer": state update, readout,
+ * then the self-augmentation term added to the head output. */
+void orc_fwd(int T, int d_k, int d_v, double lam, const double* a,
+             const double* q, const double* k, const double* v,
+             const double* S0, double* o, double* S_final)
+{
+    size_t ns = (size_t)d_k * (size_t)d_v;
+    double* S = (double*)calloc(ns, sizeof(double));
+    if (S0 != NULL) {
+        memcpy(S, S0, ns * sizeof(double));
+    }
+    for (int t = 0; t < T; ++t) {
+        const double* qt = q + (size_t)t * d_k;
+        const double* kt = k + (size_t)t * d_k;
+        const double* vt = v + (size_t)t * d_v;
+        double* ot = o + (size_t)t * d_v;
+        /* S_t = lam S_{t-1} + k_t v_t^T */
+        for (int i = 0; i < d_k; ++i) {
+            for (int j = 0; j < d_v; ++j) {
+                S[(size_t)i * d_v + j] = lam * S[(size_t)i * d_v + j] + kt[i] * vt[j];
+            }
+        }
+        /* o_t = S_t^T q_t + sigmoid(z_t) v_t */
+        double g = sigmoid(aug_arg(d_k, a, qt, kt));
+        for (int j = 0; j < d_v; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < d_k; ++i) {
+                acc += S[(size_t)i * d_v + j] * qt[i];
+            }
+            ot[j] = acc + g * vt[j];
+        }
+    }
+    if (S_final != NULL) {
+        memcpy(S_final, S, ns * sizeof(double));
+    }
+    free(S);
+}
+
+/* Gradients by reverse-mode differentiation of the forward recurrence above.
+ * Laplace 3B post, "Challenge 3: Backward-pass unrolling for a sequential
+ * recurrence": the backward differentiates through every sequential state
+ * update. Here that is done token by token, in two passes:
+ *
+ *  pass 1 (forward in t): recompute S_t and set
+ *      dq_t = S_t dO_t + sigmoid'(z_t) (dO_t . v_t) (a * k_t)
+ *  pass 2 (backward in t): G = dL/dS_t, starting from dS_final,
+ *      G <- lam G (for t < T-1), then G += q_t dO_t^T   (o_t reads S_t)
+ *      dk_t = G v_t + sigmoid'(z_t) (dO_t . v_t) (a * q_t)
+ *      dv_t = G^T k_t + sigmoid(z_t) dO_t
+ *      da  += sigmoid'(z_t) (dO_t . v_t) (q_t * k_t)
+ *  and finally dS0 = lam G (S_0 = lam S0 + k_0 v_0^T).
+ */
+void orc_bwd(int T, int d_k, int d_v, double lam, const double* a,
+             const double* q, const double* k, const double* v,
+             const double* S0, const double* dO, const double* dS_final,
+             double* dq, double* dk, double* dv, double* da, double* dS0)
+{
+    size_t ns = (size_t)d_k * (size_t)d_v;
+    double* S = (double*)calloc(ns, sizeof(double));
+    double* G = (double*)calloc(ns, sizeof(double));
+
+    /* pass 1: forward scan for dq */
+    if (S0 != NULL) {
+        memcpy(S, S0, ns * sizeof(double));
+    }
+    for (int t = 0; t < T; ++t) {
+        const double* qt = q + (size_t)t * d_k;
+        const double* kt = k + (size_t)t * d_k;
+        const double* vt = v + (size_t)t * d_v;
+        const double* dot = dO + (size_t)t * d_v;
+        double* dqt = dq + (size_t)t * d_k;
+        for (int i = 0; i < d_k; ++i) {
+            for (int j = 0; j < d_v; ++j) {
+                S[(size_t)i * d_v + j] = lam * S[(size_t)i * d_v + j] + kt[i] * vt[j];
+            }
+        }
+        double s = sigmoid(aug_arg(d_k, a, qt, kt));
+        double u = 0.0; /* dO_t . v_t */
+        for (int j = 0; j < d_v; ++j) {
+            u += dot[j] * vt[j];
+        }
+        double c = s * (1.0 - s) * u;
+        for (int i = 0; i < d_k; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < d_v; ++j) {
+                acc += S[(size_t)i * d_v + j] * dot[j];
+            }
+            dqt[i] = acc + ((a != NULL) ? c * a[i] * kt[i] : 0.0);
+        }
+    }
+
+    /* pass 2: reverse scan for dk, dv, da, dS0 */
+    if (dS_final != NULL) {
+        memcpy(G, dS_final, ns * sizeof(double));
+    }
+    for (int t = T - 1; t >= 0; --t) {
+        const double* qt = q + (size_t)t * d_k;
+        const double* kt = k + (size_t)t * d_k;
+        const double* vt = v + (size_t)t * d_v;
+        const double* dot = dO + (size_t)t * d_v;
+        double* dkt = dk + (size_t)t * d_k;
+        double* dvt = dv + (size_t)t * d_v;
+        if (t < T - 1) {
+            for (size_t e = 0; e < ns; ++e) {
+                G[e] *= lam;
+            }
+        }
+        for (int i = 0; i < d_k; ++i) {
+            for (int j = 0; j < d_v; ++j) {
+                G[(size_t)i * d_v + j] += qt[i] * dot[j];
+            }
+        }
+        double s = sigmoid(aug_arg(d_k, a, qt, kt));
+        double u = 0.0;
+        for (int j = 0; j < d_v; ++j) {
+            u += dot[j] * vt[j];
+        }
+        double c = s * (1.0 - s) * u;
+        for (int i = 0; i < d_k; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < d_v; ++j) {
+                acc += G[(size_t)i * d_v + j] * vt[j];
+            }
+            dkt[i] = acc + ((a != NULL) ? c * a[i] * qt[i] : 0.0);
+            if (a != NULL) {
+                da[i] += c * qt[i] * kt[i];
+            }
+        }
+        for (int j = 0; j < d_v; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < d_k; ++i) {
+                acc += G[(size_t)i * d_v + j] * kt[i];
+            }
+            dvt[j] = acc + s * dot[j];
+        }
+    }
+    if (dS0 != NULL) {
+        for (size_t e = 0; e < ns; ++e) {
+            dS0[e] = (T > 0) ? lam * G[e] : G[e];
+        }
+    }
+    free(S);
+    free(G);
+}
+
+/* One serving step. Laplace 3B post, "Inference optimization on Trainium2",
+ * "Constant serving state": the recurrent state is fixed-size per sequence and
+ * each new token is one step of the recurrence on it. */
+void orc_decode_step(int d_k, int d_v, double lam, const double* a,
+                     const double* q, const double* k, const double* v,
+                     double* S, double* o)
+{
+    for (int i = 0; i < d_k; ++i) {
+        for (int j = 0; j < d_v; ++j) {
+            S[(size_t)i * d_v + j] = lam * S[(size_t)i * d_v + j] + k[i] * v[j];
+        }
+    }
+    double g = sigmoid(aug_arg(d_k, a, q, k));
+    for (int j = 0; j < d_v; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < d_k; ++i) {
+            acc += S[(size_t)i * d_v + j] * q[i];
+        }
+        o[j] = acc + g * v[j];
+    }
+}

@@ -1,0 +1,58 @@
+/*
+ * Simple GLA oracle: a plain, slow, fp64 CPU reference.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may include, link,
+ * load or call this code: only the test suite, the smoke check and the
+ * bench's CPU-baseline leg use it. It shares no code with the HIP library.
+ *
+ * Source: "Beyond the KV cache: Training and serving i14's Laplace 3B linear
+ * attention model on AWS Trainium2 with native PyTorch" (AWS ML blog), section
+ * "i14 and the Laplace 3B architecture", paragraphs "GLA mixer" (state update,
+ * readout and self-augmentation equations), "Decay schedule" and "Decay
+ * schedule's reach". The display equations are missing from the page text;
+ * the formulas below are the plainest reading of the prose around them (the
+ * update is a rank-1 write of the current key/value pair into a state decayed
+ * by the fixed per-head rate; the readout queries the updated state; the gate
+ * is a sigmoid of the query dotted with a per-channel rescaled key), written
+ * out token by token:
+ *
+ *   S_t = lam * S_{t-1} + k_t v_t^T          (d_k x d_v state, S_{-1} = S0)
+ *   z_t = sum_i a_i q_{t,i} k_{t,i}
+ *   o_t = S_t^T q_t + sigmoid(z_t) v_t
+ *
+ * All arrays are row-major, token-major, for ONE (sequence, head) unit:
+ *   q, k, dq, dk : [T][d_k]     v, o, dO, dv : [T][d_v]
+ *   S0, S_final, dS_final, dS0 : [d_k][d_v]   a, da : [d_k]
+ * A NULL S0 / dS_final means zero. A NULL a means zero.
+ */
+#ifndef SGLA_ORACLE_H
+#define SGLA_ORACLE_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* lam[h] = 2^(-1/T_h), T_h = t_min * (t_max/t_min)^(h/(H-1)); T_0 = t_min when H == 1. */
+void orc_decay_schedule(int H, double t_min, double t_max, double* lam);
+
+/* Token-by-token forward. S_final may be NULL. */
+void orc_fwd(int T, int d_k, int d_v, double lam, const double* a,
+             const double* q, const double* k, const double* v,
+             const double* S0, double* o, double* S_final);
+
+/* Reverse-mode gradients of L = sum_t dO_t . o_t + sum(dS_final * S_final).
+ * da is ACCUMULATED into (caller zeroes it); dS0 may be NULL. */
+void orc_bwd(int T, int d_k, int d_v, double lam, const double* a,
+             const double* q, const double* k, const double* v,
+             const double* S0, const double* dO, const double* dS_final,
+             double* dq, double* dk, double* dv, double* da, double* dS0);
+
+/* One decode step on the state in place: S <- lam S + k v^T; o = S^T q + sigmoid(z) v. */
+void orc_decode_step(int d_k, int d_v, double lam, const double* a,
+                     const double* q, const double* k, const double* v,
+                     double* S, double* o);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

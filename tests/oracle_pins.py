@@ -1,0 +1,274 @@
+"""Pins for the fp64 oracle: checks against facts that do not come from the
+oracle itself (values printed on the page, closed forms, brute force, finite
+differences, invariants).
+
+Each ``check_*`` raises AssertionError on failure. They are collected by
+test_oracle_pins.py and re-run against deliberately broken copies of the
+oracle by test_oracle_mutations.py, to show that each plausible mistake is
+caught by at least one pin.
+
+Page citations name sections of "Beyond the KV cache: Training and serving
+i14's Laplace 3B linear attention model on AWS Trainium2 with native PyTorch"
+(the Laplace 3B post).
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+from scipy.special import expit
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _rand_unit(seed, T, dk, dv, s0=True, a_std=0.3):
+    r = _rng(seed)
+    q = r.standard_normal((T, dk)) * dk ** -0.5
+    k = r.standard_normal((T, dk))
+    v = r.standard_normal((T, dv))
+    a = r.standard_normal(dk) * a_std
+    S0 = r.standard_normal((dk, dv)) * 0.1 if s0 else None
+    return q, k, v, a, S0
+
+
+def brute_force(q, k, v, lam, a, S0):
+    """O(T^2) explicit sum: o_t = sum_{s<=t} lam^(t-s) (q_t.k_s) v_s
+    + lam^(t+1) S0^T q_t + sigmoid(sum_i a_i q_ti k_ti) v_t, and
+    S_final = lam^T S0 + sum_s lam^(T-1-s) k_s v_s^T."""
+    T, dk = q.shape
+    dv = v.shape[1]
+    o = np.zeros((T, dv))
+    for t in range(T):
+        acc = np.zeros(dv)
+        if S0 is not None:
+            acc += lam ** (t + 1) * (S0.T @ q[t])
+        for s in range(t + 1):
+            acc += lam ** (t - s) * float(q[t] @ k[s]) * v[s]
+        acc += expit(float(np.sum(a * q[t] * k[t]))) * v[t]
+        o[t] = acc
+    Sf = np.zeros((dk, dv)) if S0 is None else lam ** T * S0
+    for s in range(T):
+        Sf = Sf + lam ** (T - 1 - s) * np.outer(k[s], v[s])
+    return o, Sf
+
+
+def _close(x, y, rtol, what):
+    x = np.asarray(x)
+    y = np.asarray(y)
+    scale = max(1.0, float(np.max(np.abs(y)))) if y.size else 1.0
+    err = float(np.max(np.abs(x - y))) if y.size else 0.0
+    assert err <= rtol * scale, f"{what}: max abs err {err:.3e} > {rtol:.1e} * {scale:.3e}"
+
+
+# ---------------------------------------------------------------- schedule
+
+
+def check_schedule_printed_values():
+    """"Decay schedule's reach": lambda_0 = 0.5, lambda_15 ~= 0.9997 at T_min=1, T_max=2048."""
+    rows = [ln.split() for ln in open(os.path.join(GOLDEN, "decay_schedule_reach.txt"))
+            if ln.strip() and not ln.startswith("#")]
+    for H, tmin, tmax, h, lam, tol, hl in rows:
+        got = oracle.decay_schedule(int(H), float(tmin), float(tmax))[int(h)]
+        assert abs(got - float(lam)) <= float(tol), (h, got, lam)
+        # half-life of hl tokens: lam^hl = 1/2
+        assert abs(got ** float(hl) - 0.5) < 1e-12, (h, got ** float(hl))
+
+
+def check_schedule_geometric():
+    """"Decay schedule": half-lives spread geometrically from T_min to T_max."""
+    for H, tmin, tmax in ((16, 1.0, 2048.0), (2, 1.0, 256.0), (5, 3.0, 7.0)):
+        lam = oracle.decay_schedule(H, tmin, tmax)
+        half = -1.0 / np.log2(lam)  # half-life in tokens
+        assert abs(half[0] - tmin) < 1e-9 * tmax and abs(half[-1] - tmax) < 1e-9 * tmax
+        ratios = half[1:] / half[:-1]
+        assert np.allclose(ratios, (tmax / tmin) ** (1.0 / (H - 1)), rtol=1e-11, atol=0)
+        assert np.all(np.diff(lam) > 0)
+    lam1 = oracle.decay_schedule(1, 4.0, 100.0)
+    assert abs(lam1[0] - 2.0 ** -0.25) < 1e-15
+
+
+# ---------------------------------------------------------------- forward
+
+
+def check_fwd_brute_force():
+    """Recurrence == O(T^2) explicit sum (the brute-force evaluation)."""
+    for seed, (T, dk, dv), lam in ((1, (9, 3, 5), 0.83), (2, (17, 4, 6), 0.37),
+                                   (3, (32, 5, 4), 0.999), (4, (5, 2, 3), 0.5)):
+        q, k, v, a, S0 = _rand_unit(seed, T, dk, dv)
+        o, Sf = oracle.fwd_unit(q, k, v, lam, a, S0)
+        ob, Sb = brute_force(q, k, v, lam, a, S0)
+        _close(o, ob, 1e-12, "o vs brute force")
+        _close(Sf, Sb, 1e-12, "S_final vs brute force")
+        # no initial state
+        o, Sf = oracle.fwd_unit(q, k, v, lam, a, None)
+        ob, Sb = brute_force(q, k, v, lam, a, None)
+        _close(o, ob, 1e-12, "o vs brute force (S0=0)")
+        _close(Sf, Sb, 1e-12, "S_final vs brute force (S0=0)")
+
+
+def check_fwd_lambda_zero():
+    """lam = 0: o_t = (q_t.k_t) v_t + sigmoid(z_t) v_t and S_final = k_{T-1} v_{T-1}^T."""
+    q, k, v, a, S0 = _rand_unit(11, 7, 4, 6)
+    o, Sf = oracle.fwd_unit(q, k, v, 0.0, a, S0)
+    z = np.sum(a * q * k, axis=1)
+    want = (np.sum(q * k, axis=1) + expit(z))[:, None] * v
+    _close(o, want, 1e-14, "lam=0 closed form")
+    _close(Sf, np.outer(k[-1], v[-1]), 1e-15, "lam=0 final state")
+
+
+def check_fwd_lambda_one():
+    """lam = 1: plain causal linear attention, a running sum of k_s v_s^T."""
+    q, k, v, a, S0 = _rand_unit(12, 13, 3, 5)
+    o, Sf = oracle.fwd_unit(q, k, v, 1.0, a, S0)
+    outer = np.einsum("ti,tj->tij", k, v)
+    S = S0[None] + np.cumsum(outer, axis=0)
+    want = np.einsum("tij,ti->tj", S, q) + expit(np.sum(a * q * k, axis=1))[:, None] * v
+    _close(o, want, 1e-12, "lam=1 prefix sum")
+    _close(Sf, S[-1], 1e-12, "lam=1 final state")
+
+
+def check_fwd_T1():
+    """T = 1: o_0 = lam S0^T q_0 + (q_0.k_0) v_0 + sigmoid(z_0) v_0."""
+    q, k, v, a, S0 = _rand_unit(13, 1, 6, 4)
+    lam = 0.71
+    o, Sf = oracle.fwd_unit(q, k, v, lam, a, S0)
+    want = lam * S0.T @ q[0] + float(q[0] @ k[0]) * v[0] + expit(float(np.sum(a * q[0] * k[0]))) * v[0]
+    _close(o[0], want, 1e-14, "T=1 closed form")
+    _close(Sf, lam * S0 + np.outer(k[0], v[0]), 1e-15, "T=1 final state")
+
+
+def check_aug_half_skip():
+    """"GLA mixer": a = 0 gives a half-strength value skip (sigmoid(0) = 1/2)."""
+    rows = [ln.split() for ln in open(os.path.join(GOLDEN, "aug_half_skip.txt"))
+            if ln.strip() and not ln.startswith("#")]
+    gate = float(rows[0][1])
+    q, k, v, a, S0 = _rand_unit(14, 10, 4, 6)
+    # q = 0: the readout vanishes and z = 0 for any a -> o = gate * v exactly
+    o, _ = oracle.fwd_unit(np.zeros_like(q), k, v, 0.9, a, S0)
+    assert np.array_equal(o, gate * v), "q=0 must give exactly half of v"
+    # a = 0: o minus the aug-free readout (brute force with the gate removed) = gate * v
+    o, _ = oracle.fwd_unit(q, k, v, 0.9, np.zeros_like(a), S0)
+    ob, _ = brute_force(q, k, v, 0.9, np.full_like(a, 0.0), S0)
+    _close(o, ob, 1e-12, "a=0 brute force")
+    ob_noaug = ob - gate * v
+    _close(o - ob_noaug, gate * v, 1e-12, "a=0 half skip")
+
+
+def check_state_carry():
+    """Running [0,T) at once == running [0,t0) then [t0,T) from its final state."""
+    q, k, v, a, S0 = _rand_unit(15, 23, 4, 5)
+    lam = 0.93
+    o, Sf = oracle.fwd_unit(q, k, v, lam, a, S0)
+    for t0 in (1, 9, 22):
+        o1, S1 = oracle.fwd_unit(q[:t0], k[:t0], v[:t0], lam, a, S0)
+        o2, S2 = oracle.fwd_unit(q[t0:], k[t0:], v[t0:], lam, a, S1)
+        _close(np.concatenate([o1, o2]), o, 1e-13, "split output")
+        _close(S2, Sf, 1e-13, "split final state")
+
+
+def check_varlen_wrapper():
+    """Packed batch with cu_seqlens == independent runs per sequence."""
+    r = _rng(16)
+    L = [3, 8, 1, 6]
+    cu = np.concatenate([[0], np.cumsum(L)])
+    H, dk, dv = 2, 3, 4
+    q = r.standard_normal((1, H, cu[-1], dk))
+    k = r.standard_normal((1, H, cu[-1], dk))
+    v = r.standard_normal((1, H, cu[-1], dv))
+    a = r.standard_normal((H, dk)) * 0.2
+    S0 = r.standard_normal((len(L), H, dk, dv)) * 0.1
+    lam = np.array([0.5, 0.95])
+    o, Sf = oracle.fwd(q, k, v, lam, a, S0, cu_seqlens=cu)
+    for n in range(len(L)):
+        for h in range(H):
+            sl = slice(cu[n], cu[n + 1])
+            ob, Sb = brute_force(q[0, h, sl], k[0, h, sl], v[0, h, sl], lam[h], a[h], S0[n, h])
+            _close(o[0, h, sl], ob, 1e-12, "varlen o")
+            _close(Sf[n, h], Sb, 1e-12, "varlen S_final")
+
+
+def check_decode_brute_force():
+    """A run of decode steps == the brute-force sum over the tokens seen so far."""
+    q, k, v, a, S0 = _rand_unit(17, 6, 4, 5)
+    lam = 0.8
+    S = S0.copy()
+    ob, Sb = brute_force(q, k, v, lam, a, S0)
+    for t in range(len(q)):
+        o = oracle.decode_step_unit(q[t], k[t], v[t], lam, a, S)
+        _close(o, ob[t], 1e-12, "decode o")
+    _close(S, Sb, 1e-12, "decode state")
+
+
+# ---------------------------------------------------------------- backward
+
+
+def _loss(q, k, v, lam, a, S0, dO, dSf):
+    o, Sf = oracle.fwd_unit(q, k, v, lam, a, S0)
+    return float(np.sum(dO * o) + np.sum(dSf * Sf))
+
+
+def check_bwd_finite_differences():
+    """Analytic gradients == central finite differences of
+    L = sum_t dO_t.o_t + sum(dS_final * S_final), every coordinate."""
+    for seed, lam in ((21, 0.87), (22, 0.5)):
+        T, dk, dv = 16, 4, 8
+        q, k, v, a, S0 = _rand_unit(seed, T, dk, dv, a_std=0.8)
+        r = _rng(seed + 100)
+        dO = r.standard_normal((T, dv))
+        dSf = r.standard_normal((dk, dv)) * 0.3
+        dq, dk_, dv_, da, dS0 = oracle.bwd_unit(q, k, v, dO, lam, a, S0, dSf)
+        params = {"q": q, "k": k, "v": v, "a": a, "S0": S0}
+        grads = {"q": dq, "k": dk_, "v": dv_, "a": da, "S0": dS0}
+        for name, x in params.items():
+            fd = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                h = 1e-5 * max(1.0, abs(x[idx]))
+                keep = x[idx]
+                x[idx] = keep + h
+                lp = _loss(**params, lam=lam, dO=dO, dSf=dSf)
+                x[idx] = keep - h
+                lm = _loss(**params, lam=lam, dO=dO, dSf=dSf)
+                x[idx] = keep
+                fd[idx] = (lp - lm) / (2 * h)
+            scale = max(1e-3, float(np.max(np.abs(fd))))
+            err = float(np.max(np.abs(fd - grads[name])))
+            assert err <= 1e-6 * scale, f"d{name}: FD err {err:.3e} (scale {scale:.3e})"
+
+
+def check_bwd_lambda_zero():
+    """lam = 0, dS_final = 0: dq_t = (dO_t.v_t) k_t + aug, dk_t = (dO_t.v_t) q_t + aug,
+    dv_t = (q_t.k_t) dO_t + sigmoid(z_t) dO_t."""
+    T, dk, dv = 9, 3, 5
+    q, k, v, a, S0 = _rand_unit(23, T, dk, dv, a_std=0.5)
+    dO = _rng(123).standard_normal((T, dv))
+    dq, dk_, dv_, da, dS0 = oracle.bwd_unit(q, k, v, dO, 0.0, a, S0, None)
+    u = np.sum(dO * v, axis=1)
+    s = expit(np.sum(a * q * k, axis=1))
+    c = s * (1 - s) * u
+    _close(dq, u[:, None] * k + c[:, None] * a[None] * k, 1e-14, "lam=0 dq")
+    _close(dk_, u[:, None] * q + c[:, None] * a[None] * q, 1e-14, "lam=0 dk")
+    _close(dv_, (np.sum(q * k, axis=1) + s)[:, None] * dO, 1e-14, "lam=0 dv")
+    _close(da, np.sum(c[:, None] * q * k, axis=0), 1e-14, "lam=0 da")
+    _close(dS0, np.zeros((dk, dv)), 0, "lam=0 dS0")
+
+
+ALL_CHECKS = [
+    check_schedule_printed_values,
+    check_schedule_geometric,
+    check_fwd_brute_force,
+    check_fwd_lambda_zero,
+    check_fwd_lambda_one,
+    check_fwd_T1,
+    check_aug_half_skip,
+    check_state_carry,
+    check_varlen_wrapper,
+    check_decode_brute_force,
+    check_bwd_finite_differences,
+    check_bwd_lambda_zero,
+]

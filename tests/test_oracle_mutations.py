@@ -1,0 +1,74 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and show that
+the pins catch every one of them.
+
+Each mutation is a textual replacement in oracle.c; the mutated copy is built
+into a temporary shared library and every pin is run against it. A mutation
+that no pin detects fails this test.
+"""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+# (name, text to find, replacement); the find text must occur exactly once.
+MUTATIONS = [
+    ("no decay in update (fwd)",
+     "S[(size_t)i * d_v + j] = lam * S[(size_t)i * d_v + j] + kt[i] * vt[j];\n            }\n        }\n        /* o_t",
+     "S[(size_t)i * d_v + j] = S[(size_t)i * d_v + j] + kt[i] * vt[j];\n            }\n        }\n        /* o_t"),
+    ("readout uses k instead of q", "acc += S[(size_t)i * d_v + j] * qt[i];",
+     "acc += S[(size_t)i * d_v + j] * kt[i];"),
+    ("sigmoid sign flipped", "return 1.0 / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(z));"),
+    ("gate uses q twice", "z += a[i] * qt[i] * kt[i];", "z += a[i] * qt[i] * qt[i];"),
+    ("aug term dropped (fwd)", "ot[j] = acc + g * vt[j];", "ot[j] = acc;"),
+    ("outer product transposed index", "= lam * S[(size_t)i * d_v + j] + kt[i] * vt[j];\n            }\n        }\n        /* o_t",
+     "= lam * S[(size_t)i * d_v + j] + kt[j % d_k] * vt[j];\n            }\n        }\n        /* o_t"),
+    ("schedule exponent H instead of H-1", "(double)h / (double)(H - 1)", "(double)h / (double)H"),
+    ("schedule base e instead of 2", "lam[h] = pow(2.0, -1.0 / half_life);", "lam[h] = exp(-1.0 / half_life);"),
+    ("dq aug uses q", "dqt[i] = acc + ((a != NULL) ? c * a[i] * kt[i] : 0.0);",
+     "dqt[i] = acc + ((a != NULL) ? c * a[i] * qt[i] : 0.0);"),
+    ("no decay of G", "G[e] *= lam;", "G[e] *= 1.0;"),
+    ("G accumulates k dO^T", "G[(size_t)i * d_v + j] += qt[i] * dot[j];", "G[(size_t)i * d_v + j] += kt[i] * dot[j];"),
+    ("dS0 not decayed", "dS0[e] = (T > 0) ? lam * G[e] : G[e];", "dS0[e] = G[e];"),
+    ("dv aug sigma' instead of sigma", "dvt[j] = acc + s * dot[j];", "dvt[j] = acc + s * (1.0 - s) * dot[j];"),
+    ("da uses q twice", "da[i] += c * qt[i] * kt[i];", "da[i] += c * qt[i] * qt[i];"),
+    ("dk aug sign", "dkt[i] = acc + ((a != NULL) ? c * a[i] * qt[i] : 0.0);",
+     "dkt[i] = acc - ((a != NULL) ? c * a[i] * qt[i] : 0.0);"),
+    ("dv reads G transposed wrong", "acc += G[(size_t)i * d_v + j] * kt[i];", "acc += G[(size_t)i * d_v + j] * qt[i];"),
+    ("decode no decay", "S[(size_t)i * d_v + j] = lam * S[(size_t)i * d_v + j] + k[i] * v[j];",
+     "S[(size_t)i * d_v + j] = S[(size_t)i * d_v + j] + k[i] * v[j];"),
+    ("decode gate off", "o[j] = acc + g * v[j];", "o[j] = acc + 0.5 * v[j];"),
+]
+
+
+@pytest.mark.parametrize("name,find,repl", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_mutation_is_caught(name, find, repl, tmp_path):
+    src = open(SRC).read()
+    assert src.count(find) == 1, f"mutation site for '{name}' not unique ({src.count(find)})"
+    mutated = tmp_path / "oracle_mut.c"
+    mutated.write_text(src.replace(find, repl))
+    hdr_dir = os.path.dirname(SRC)
+    so = tmp_path / "liboracle_mut.so"
+    subprocess.check_call(["gcc", "-O1", "-std=c99", "-fPIC", "-shared", "-I", hdr_dir,
+                           "-o", str(so), str(mutated), "-lm"])
+    good = oracle._load()
+    bad = ctypes.CDLL(str(so))
+    for fn in ("orc_decay_schedule", "orc_fwd", "orc_bwd", "orc_decode_step"):
+        getattr(bad, fn).argtypes = getattr(good, fn).argtypes
+        getattr(bad, fn).restype = None
+    caught = []
+    oracle._lib = bad
+    try:
+        for check in oracle_pins.ALL_CHECKS:
+            try:
+                check()
+            except AssertionError:
+                caught.append(check.__name__)
+    finally:
+        oracle._lib = good
+    assert caught, f"no pin detects the planted mistake '{name}'"
