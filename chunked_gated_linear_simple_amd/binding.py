@@ -1,0 +1,213 @@
+"""Thin ctypes binding over libsgla (include/sgla.h).
+
+Functions keep the C names. They only marshal arguments: read sizes off the
+tensor shapes, check devices and dtypes, allocate outputs the caller did not
+pass (torch.empty on the inputs' device), and hand raw device pointers plus
+torch's current HIP stream to the library. Every step of the computation runs
+in the library's kernels; there is no fallback of any kind. If libsgla.so is
+not built, the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsgla.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "sgla.h")
+
+SGLA_OK, SGLA_ERR_INVALID_ARG, SGLA_ERR_UNSUPPORTED, SGLA_ERR_WORKSPACE, SGLA_ERR_HIP = range(5)
+SGLA_F32, SGLA_BF16 = 0, 1
+
+_lib = None
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+
+
+class SglaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} [status {status}]")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Open libsgla.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run "
+                               "`python -m chunked_gated_linear_simple_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.sgla_version.restype = _i
+        L.sgla_status_str.restype = ctypes.c_char_p
+        L.sgla_status_str.argtypes = [_i]
+        L.sgla_last_error.restype = ctypes.c_char_p
+        L.sgla_decay_schedule.argtypes = [_i, ctypes.c_double, ctypes.c_double,
+                                          ctypes.POINTER(ctypes.c_float)]
+        L.sgla_decay_schedule.restype = _i
+        L.sgla_chunk_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i,
+                                     _i, _i, _i, _i, _i, _i, _i, _vp]
+        L.sgla_chunk_fwd.restype = _i
+        L.sgla_chunk_bwd_workspace_bytes.argtypes = [_i, _i, _i]
+        L.sgla_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.sgla_chunk_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp,
+                                     ctypes.c_size_t, _vp]
+        L.sgla_chunk_bwd.restype = _i
+        L.sgla_decode_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
+                                       _i, _vp]
+        L.sgla_decode_step.restype = _i
+        _lib = L
+    return _lib
+
+
+def declared_functions() -> list:
+    """Names of the functions include/sgla.h declares."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sgla_\w+)\s*\(", text)))
+
+
+def _check(status: int):
+    if status != SGLA_OK:
+        msg = lib().sgla_last_error().decode()
+        raise SglaError(status, msg or lib().sgla_status_str(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else _vp(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SGLA_BF16
+    if t.dtype == torch.float32:
+        return SGLA_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _stream(dev: torch.device):
+    return _vp(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t, name, dtype=None, device=None, shape=None):
+    if t is None:
+        return
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def sgla_version() -> int:
+    return lib().sgla_version()
+
+
+def sgla_decay_schedule(H: int, t_min: float, t_max: float) -> torch.Tensor:
+    """[H] fp32 decays on the host."""
+    out = (ctypes.c_float * H)()
+    _check(lib().sgla_decay_schedule(int(H), float(t_min), float(t_max), out))
+    return torch.tensor(list(out), dtype=torch.float32)
+
+
+def _geometry(q, v, cu_seqlens):
+    B, H, T, d_k = q.shape
+    d_v = v.shape[-1]
+    n_seq = B if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    return B, H, T, d_k, d_v, n_seq
+
+
+def sgla_chunk_fwd(q, k, v, lam, a=None, init_state=None, final_state=None, o=None,
+                   cu_seqlens=None, chunk: int = 128, want_final: bool = False):
+    """Chunked forward. Returns (o, final_state) (final_state None unless passed
+    or want_final)."""
+    dev = q.device
+    B, H, T, d_k, d_v, n_seq = _geometry(q, v, cu_seqlens)
+    _need(q, "q", device=dev)
+    _need(k, "k", q.dtype, dev, q.shape)
+    _need(v, "v", q.dtype, dev, (B, H, T, d_v))
+    _need(lam, "lambda", torch.float32, dev, (H,))
+    _need(a, "a", torch.float32, dev, (H, d_k))
+    _need(init_state, "init_state", torch.float32, dev, (n_seq, H, d_k, d_v))
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    if o is None:
+        o = torch.empty((B, H, T, d_v), dtype=q.dtype, device=dev)
+    _need(o, "o", q.dtype, dev, (B, H, T, d_v))
+    if final_state is None and want_final:
+        final_state = torch.empty((n_seq, H, d_k, d_v), dtype=torch.float32, device=dev)
+    _need(final_state, "final_state", torch.float32, dev, (n_seq, H, d_k, d_v))
+    _check(lib().sgla_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(lam), _ptr(a),
+                                _ptr(init_state), _ptr(final_state), _ptr(o), _ptr(cu_seqlens),
+                                n_seq, B, H, T, d_k, d_v, int(chunk), _dtype_code(q),
+                                _stream(dev)))
+    return o, final_state
+
+
+def sgla_chunk_bwd_workspace_bytes(N: int, H: int, d_k: int) -> int:
+    return int(lib().sgla_chunk_bwd_workspace_bytes(int(N), int(H), int(d_k)))
+
+
+def sgla_chunk_bwd(q, k, v, dO, lam, a=None, init_state=None, d_final_state=None,
+                   cu_seqlens=None, chunk: int = 128, want_d_init: bool = False,
+                   dq=None, dk=None, dv=None, da=None, d_init_state=None, workspace=None):
+    """Chunked backward. Returns (dq, dk, dv, da, d_init_state)."""
+    dev = q.device
+    B, H, T, d_k, d_v, n_seq = _geometry(q, v, cu_seqlens)
+    _need(q, "q", device=dev)
+    _need(k, "k", q.dtype, dev, q.shape)
+    _need(v, "v", q.dtype, dev, (B, H, T, d_v))
+    _need(dO, "dO", q.dtype, dev, (B, H, T, d_v))
+    _need(lam, "lambda", torch.float32, dev, (H,))
+    _need(a, "a", torch.float32, dev, (H, d_k))
+    _need(init_state, "init_state", torch.float32, dev, (n_seq, H, d_k, d_v))
+    _need(d_final_state, "d_final_state", torch.float32, dev, (n_seq, H, d_k, d_v))
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    da = torch.empty((H, d_k), dtype=torch.float32, device=dev) if da is None else da
+    if d_init_state is None and want_d_init:
+        d_init_state = torch.empty((n_seq, H, d_k, d_v), dtype=torch.float32, device=dev)
+    for t, nm, shp in ((dq, "dq", q.shape), (dk, "dk", q.shape), (dv, "dv", v.shape)):
+        _need(t, nm, q.dtype, dev, shp)
+    _need(da, "da", torch.float32, dev, (H, d_k))
+    _need(d_init_state, "d_init_state", torch.float32, dev, (n_seq, H, d_k, d_v))
+    nbytes = sgla_chunk_bwd_workspace_bytes(n_seq, H, d_k)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    _check(lib().sgla_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lam), _ptr(a),
+                                _ptr(init_state), _ptr(d_final_state), _ptr(dq), _ptr(dk),
+                                _ptr(dv), _ptr(da), _ptr(d_init_state), _ptr(cu_seqlens), n_seq,
+                                B, H, T, d_k, d_v, int(chunk), _dtype_code(q), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(dev)))
+    return dq, dk, dv, da, d_init_state
+
+
+def sgla_decode_step(q, k, v, lam, a, state, o=None, slot=None):
+    """One in-place decode step. q,k [N,H,d_k], v [N,H,d_v], state [P,H,d_k,d_v].
+    Returns o [N,H,d_v]."""
+    dev = q.device
+    N, H, d_k = q.shape
+    d_v = v.shape[-1]
+    P = state.shape[0]
+    _need(q, "q", device=dev)
+    _need(k, "k", q.dtype, dev, q.shape)
+    _need(v, "v", q.dtype, dev, (N, H, d_v))
+    _need(lam, "lambda", torch.float32, dev, (H,))
+    _need(a, "a", torch.float32, dev, (H, d_k))
+    _need(state, "state", torch.float32, dev, (P, H, d_k, d_v))
+    _need(slot, "slot", torch.int32, dev, (N,))
+    if o is None:
+        o = torch.empty((N, H, d_v), dtype=q.dtype, device=dev)
+    _need(o, "o", q.dtype, dev, (N, H, d_v))
+    _check(lib().sgla_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(lam), _ptr(a), _ptr(state),
+                                  _ptr(slot), _ptr(o), N, P, H, d_k, d_v, _dtype_code(q),
+                                  _stream(dev)))
+    return o

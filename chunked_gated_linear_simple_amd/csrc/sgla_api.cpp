@@ -1,0 +1,240 @@
+// C-ABI entry points of libsgla (declared in include/sgla.h): argument
+// validation on the host, then dispatch to the HIP launchers. Validation runs
+// before any HIP call, so every error path can be exercised without a GPU.
+
+#include "sgla.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "sgla_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+sgla_status fail(sgla_status st, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+sgla_status ok()
+{
+    g_err[0] = '\0';
+    return SGLA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE_PTR(p)                                                          \
+    do {                                                                        \
+        if ((p) == nullptr) return fail(SGLA_ERR_INVALID_ARG, #p " is NULL");  \
+        if (!aligned16(p)) return fail(SGLA_ERR_INVALID_ARG, #p " is not 16-byte aligned"); \
+    } while (0)
+
+#define OPTIONAL_PTR(p)                                                         \
+    do {                                                                        \
+        if ((p) != nullptr && !aligned16(p))                                    \
+            return fail(SGLA_ERR_INVALID_ARG, #p " is not 16-byte aligned");   \
+    } while (0)
+
+// Shared checks of the chunked entry points; fills the launch description.
+sgla_status check_chunk(const void* q, const void* k, const void* v, const float* lambda,
+                        const float* a, const int32_t* cu_seqlens, int n_seq, int B, int H,
+                        int T, int d_k, int d_v, int chunk, sgla_dtype dtype,
+                        sgla::ChunkProblem* out)
+{
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(k);
+    REQUIRE_PTR(v);
+    REQUIRE_PTR(lambda);
+    OPTIONAL_PTR(a);
+    if (dtype != SGLA_F32 && dtype != SGLA_BF16)
+        return fail(SGLA_ERR_INVALID_ARG, "dtype %d is not SGLA_F32 or SGLA_BF16", (int)dtype);
+    if (B <= 0 || H <= 0 || T <= 0 || d_k <= 0 || d_v <= 0)
+        return fail(SGLA_ERR_INVALID_ARG, "sizes must be positive (B=%d H=%d T=%d d_k=%d d_v=%d)",
+                    B, H, T, d_k, d_v);
+    if (cu_seqlens != nullptr) {
+        if (!aligned16(cu_seqlens)) return fail(SGLA_ERR_INVALID_ARG, "cu_seqlens is not 16-byte aligned");
+        if (B != 1) return fail(SGLA_ERR_INVALID_ARG, "packed input (cu_seqlens) needs B == 1, got %d", B);
+        if (n_seq <= 0) return fail(SGLA_ERR_INVALID_ARG, "n_seq must be positive, got %d", n_seq);
+    } else {
+        n_seq = B;
+    }
+    // element counts must fit the kernels' 64-bit offsets and int grid sizes
+    const double toks = (double)B * H * T;
+    if (toks * (d_k > d_v ? d_k : d_v) > 9.0e18 || (double)n_seq * H > 2.0e8)
+        return fail(SGLA_ERR_INVALID_ARG, "problem too large");
+    if (dtype == SGLA_BF16) {
+        if (d_k > 96 || d_v > 192 || d_k % 8 != 0 || d_v % 8 != 0)
+            return fail(SGLA_ERR_UNSUPPORTED,
+                        "bf16 needs d_k <= 96 and d_v <= 192, multiples of 8 (got %d, %d)", d_k, d_v);
+        if (chunk != 64 && chunk != 128)
+            return fail(SGLA_ERR_UNSUPPORTED, "bf16 chunk must be 64 or 128, got %d", chunk);
+    } else {
+        if (d_k > 32 || d_v > 32 || d_k % 4 != 0 || d_v % 4 != 0)
+            return fail(SGLA_ERR_UNSUPPORTED,
+                        "f32 needs d_k <= 32 and d_v <= 32, multiples of 4 (got %d, %d)", d_k, d_v);
+        if (chunk != 64) return fail(SGLA_ERR_UNSUPPORTED, "f32 chunk must be 64, got %d", chunk);
+    }
+    out->bf16 = dtype == SGLA_BF16;
+    out->B = B;
+    out->H = H;
+    out->T = T;
+    out->n_seq = n_seq;
+    out->d_k = d_k;
+    out->d_v = d_v;
+    out->chunk = chunk;
+    out->lambda = lambda;
+    out->a = a;
+    out->cu = cu_seqlens;
+    return SGLA_OK;
+}
+
+bool overlaps(const void* x, size_t nx, const void* y, size_t ny)
+{
+    if (x == nullptr || y == nullptr) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(x), b0 = reinterpret_cast<uintptr_t>(y);
+    return a0 < b0 + ny && b0 < a0 + nx;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sgla_version(void) { return 100; }
+
+const char* sgla_status_str(int status)
+{
+    switch (status) {
+    case SGLA_OK: return "SGLA_OK";
+    case SGLA_ERR_INVALID_ARG: return "SGLA_ERR_INVALID_ARG";
+    case SGLA_ERR_UNSUPPORTED: return "SGLA_ERR_UNSUPPORTED";
+    case SGLA_ERR_WORKSPACE: return "SGLA_ERR_WORKSPACE";
+    case SGLA_ERR_HIP: return "SGLA_ERR_HIP";
+    default: return "unknown sgla_status";
+    }
+}
+
+const char* sgla_last_error(void) { return g_err; }
+
+sgla_status sgla_decay_schedule(int H, double t_min, double t_max, float* lambda_out)
+{
+    if (lambda_out == nullptr) return fail(SGLA_ERR_INVALID_ARG, "lambda_out is NULL");
+    if (H <= 0) return fail(SGLA_ERR_INVALID_ARG, "H must be positive, got %d", H);
+    if (!std::isfinite(t_min) || !std::isfinite(t_max) || t_min <= 0.0 || t_max < t_min)
+        return fail(SGLA_ERR_INVALID_ARG, "need 0 < t_min <= t_max (got %g, %g)", t_min, t_max);
+    // half-lives geometric in the head index, endpoints included
+    const double ratio = t_max / t_min;
+    for (int h = 0; h < H; ++h) {
+        const double e = (H == 1) ? 0.0 : (double)h / (double)(H - 1);
+        const double half_life = t_min * std::pow(ratio, e);
+        lambda_out[h] = (float)std::pow(2.0, -1.0 / half_life);
+    }
+    return ok();
+}
+
+sgla_status sgla_chunk_fwd(const void* q, const void* k, const void* v, const float* lambda,
+                           const float* a, const float* init_state, float* final_state, void* o,
+                           const int32_t* cu_seqlens, int n_seq, int B, int H, int T, int d_k,
+                           int d_v, int chunk, sgla_dtype dtype, void* hip_stream)
+{
+    sgla::ChunkProblem p;
+    sgla_status st = check_chunk(q, k, v, lambda, a, cu_seqlens, n_seq, B, H, T, d_k, d_v, chunk,
+                                 dtype, &p);
+    if (st != SGLA_OK) return st;
+    REQUIRE_PTR(o);
+    OPTIONAL_PTR(init_state);
+    OPTIONAL_PTR(final_state);
+    const size_t es = (dtype == SGLA_BF16) ? 2 : 4;
+    const size_t nqk = (size_t)B * H * T * d_k * es, nvo = (size_t)B * H * T * d_v * es;
+    if (overlaps(o, nvo, q, nqk) || overlaps(o, nvo, k, nqk) || overlaps(o, nvo, v, nvo))
+        return fail(SGLA_ERR_INVALID_ARG, "o must not alias q, k or v");
+    hipError_t e = sgla::launch_chunk_fwd(p, q, k, v, init_state, final_state, o,
+                                          reinterpret_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(SGLA_ERR_HIP, "chunk_fwd launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+size_t sgla_chunk_bwd_workspace_bytes(int N, int H, int d_k)
+{
+    if (N <= 0 || H <= 0 || d_k <= 0) return 0;
+    return (size_t)N * H * d_k * sizeof(float);
+}
+
+sgla_status sgla_chunk_bwd(const void* q, const void* k, const void* v, const void* dO,
+                           const float* lambda, const float* a, const float* init_state,
+                           const float* d_final_state, void* dq, void* dk, void* dv, float* da,
+                           float* d_init_state, const int32_t* cu_seqlens, int n_seq, int B,
+                           int H, int T, int d_k, int d_v, int chunk, sgla_dtype dtype,
+                           void* workspace, size_t workspace_bytes, void* hip_stream)
+{
+    sgla::ChunkProblem p;
+    sgla_status st = check_chunk(q, k, v, lambda, a, cu_seqlens, n_seq, B, H, T, d_k, d_v, chunk,
+                                 dtype, &p);
+    if (st != SGLA_OK) return st;
+    REQUIRE_PTR(dO);
+    REQUIRE_PTR(dq);
+    REQUIRE_PTR(dk);
+    REQUIRE_PTR(dv);
+    REQUIRE_PTR(da);
+    OPTIONAL_PTR(init_state);
+    OPTIONAL_PTR(d_final_state);
+    OPTIONAL_PTR(d_init_state);
+    const size_t need = sgla_chunk_bwd_workspace_bytes(p.n_seq, H, d_k);
+    if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
+        return fail(SGLA_ERR_WORKSPACE, "workspace needs %zu bytes, 16-byte aligned (got %zu at %p)",
+                    need, workspace_bytes, workspace);
+    const size_t es = (dtype == SGLA_BF16) ? 2 : 4;
+    const size_t nqk = (size_t)B * H * T * d_k * es, nvo = (size_t)B * H * T * d_v * es;
+    const void* ins[4] = {q, k, v, dO};
+    const size_t insz[4] = {nqk, nqk, nvo, nvo};
+    void* outs[3] = {dq, dk, dv};
+    const size_t outsz[3] = {nqk, nqk, nvo};
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 4; ++j)
+            if (overlaps(outs[i], outsz[i], ins[j], insz[j]))
+                return fail(SGLA_ERR_INVALID_ARG, "dq, dk and dv must not alias q, k, v or dO");
+    hipError_t e = sgla::launch_chunk_bwd(p, q, k, v, dO, init_state, d_final_state, dq, dk, dv,
+                                          da, d_init_state, reinterpret_cast<float*>(workspace),
+                                          reinterpret_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(SGLA_ERR_HIP, "chunk_bwd launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+sgla_status sgla_decode_step(const void* q, const void* k, const void* v, const float* lambda,
+                             const float* a, float* state, const int32_t* slot, void* o, int N,
+                             int P, int H, int d_k, int d_v, sgla_dtype dtype, void* hip_stream)
+{
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(k);
+    REQUIRE_PTR(v);
+    REQUIRE_PTR(lambda);
+    REQUIRE_PTR(state);
+    REQUIRE_PTR(o);
+    OPTIONAL_PTR(a);
+    OPTIONAL_PTR(slot);
+    if (dtype != SGLA_F32 && dtype != SGLA_BF16)
+        return fail(SGLA_ERR_INVALID_ARG, "dtype %d is not SGLA_F32 or SGLA_BF16", (int)dtype);
+    if (N <= 0 || P <= 0 || H <= 0)
+        return fail(SGLA_ERR_INVALID_ARG, "N, P, H must be positive (N=%d P=%d H=%d)", N, P, H);
+    if (slot == nullptr && P < N)
+        return fail(SGLA_ERR_INVALID_ARG, "without slot, the pool needs P >= N (P=%d N=%d)", P, N);
+    if ((double)N * H > 2.0e9) return fail(SGLA_ERR_INVALID_ARG, "N*H too large");
+    if (!((d_k == 96 && d_v == 192) || (d_k == 16 && d_v == 32)))
+        return fail(SGLA_ERR_UNSUPPORTED, "decode supports (d_k, d_v) = (96, 192) or (16, 32), got (%d, %d)",
+                    d_k, d_v);
+    hipError_t e = sgla::launch_decode_step(dtype == SGLA_BF16, q, k, v, lambda, a, state, slot, o,
+                                            N, P, H, d_k, d_v,
+                                            reinterpret_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(SGLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,618 @@
+// Chunked Simple GLA kernels for gfx950 (forward and backward).
+//
+// Method: "Beyond the KV cache: Training and serving i14's Laplace 3B linear
+// attention model on AWS Trainium2 with native PyTorch", section "Challenge 1:
+// Using native PyTorch on Trainium for GLA" (the chunked intra-chunk output
+// and chunk state update). For a chunk of C_c tokens (rows i, j) entered with
+// state S_in, and decay lam of the head:
+//
+//   o_i   = lam^(i+1) S_in^T q_i + sum_{j<=i} lam^(i-j) (q_i . k_j) v_j + aug_i
+//   S_out = lam^(C_c) S_in + sum_j lam^(C_c-1-j) k_j v_j^T
+//
+// One "role" body below evaluates this recurrence for generic operands
+// (q', k', v') and a generic per-token epilogue, optionally in reversed token
+// order. The forward is the role (q, k, v). The backward is three independent
+// roles that run concurrently in one launch:
+//   dq: forward order,  q'=dO, k'=v, v'=k, state S^T, + sigmoid'(z)(dO.v)(a*k)
+//   dk: reversed order, q'=v, k'=dO, v'=q, state G^T, + sigmoid'(z)(dO.v)(a*q)
+//   dv: reversed order, q'=k, k'=q, v'=dO, state G,   + sigmoid(z) dO
+// (G_t = dL/dS_t = sum_{i>=t} lam^(i-t) q_i dO_i^T + lam^(T-1-t) dS_final.)
+//
+// Work decomposition: one workgroup of 4 waves per (sequence, head, value
+// slice); the state slice stays in MFMA accumulators for the whole scan over
+// chunks. Per chunk the operands are staged in LDS:
+//   Qs, Ks   [C][DK]  natural (rows = tokens)       -- scores, Q'S
+//   KTs      [DK][C]  k' transposed, scaled by lam^(C_c-1-j)  -- state update
+//   VTs      [DVS][C] v' transposed                 -- P.V', state update, aug
+//   STs      [DVS][DK] state^T in the operand dtype  -- Q'S
+// Waves 0..C/32-1 each own 32 query rows: they compute Q'S, the decay-masked
+// score tiles K' Q'^T (kept in registers and fed straight back as the A
+// operand of P.V'), the epilogue, and store. Every wave then advances its
+// share of the state tiles with K~^T V' on the matrix cores.
+//
+// MFMA: v_mfma_f32_32x32x16_bf16 (bf16) or v_mfma_f32_32x32x2_f32 (fp32).
+// For a 32x32 result, lane l holds column l%32 and rows 8*(i/4)+4*(l/32)+i%4
+// in accumulator i. Operand lanes hold row (A) / column (B) l%32; lane group
+// l/32 selects the slice of the contraction index. The pairing of contraction
+// slots between A and B is lane-group- and slot-wise, so any assignment of
+// contraction indices to (group, slot) works if A and B use the same one.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sgla_internal.h"
+
+namespace sgla {
+namespace {
+
+typedef unsigned short u16;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef u16 u16x8_t __attribute__((ext_vector_type(8)));
+typedef u16 u16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int NTHREADS = 256;
+
+__device__ __forceinline__ float to_f(u16 x) { return __uint_as_float((uint32_t)x << 16); }
+__device__ __forceinline__ float to_f(float x) { return x; }
+
+template <typename E> __device__ __forceinline__ E from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ u16 from_f<u16>(float x)
+{
+    // round to nearest even (the C++ conversion to __bf16)
+    return __builtin_bit_cast(u16, static_cast<__bf16>(x));
+}
+
+// lam^m for an integer m >= 0 with lam^0 = 1 exactly (also for lam = 0).
+__device__ __forceinline__ float decay_pow(int m, float log2lam)
+{
+    return (m == 0) ? 1.0f : exp2f((float)m * log2lam);
+}
+
+__device__ __forceinline__ float sigmoidf_(float z)
+{
+    if (z >= 0.0f) return 1.0f / (1.0f + expf(-z));
+    float e = expf(z);
+    return e / (1.0f + e);
+}
+
+template <typename E> struct Mfma;
+template <> struct Mfma<u16> {
+    static constexpr int KSTEP = 16;  // contraction per instruction
+    static constexpr int NE = 8;      // operand elements per lane
+    typedef bf16x8_t op_t;
+    static __device__ __forceinline__ op_t load(const u16* p)
+    {
+        return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u16x8_t*>(p));
+    }
+    static __device__ __forceinline__ f32x16_t mma(op_t a, op_t b, f32x16_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Mfma<float> {
+    static constexpr int KSTEP = 2;
+    static constexpr int NE = 1;
+    typedef float op_t;
+    static __device__ __forceinline__ op_t load(const float* p) { return *p; }
+    static __device__ __forceinline__ f32x16_t mma(op_t a, op_t b, f32x16_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+    }
+};
+
+// Row (within a 32x32 tile) held by accumulator i of lane group g.
+__device__ __forceinline__ int acc_row(int i, int g) { return 8 * (i >> 2) + 4 * g + (i & 3); }
+
+enum { AUG_FWD = 0, AUG_GRAD = 1 };
+
+// Compile-time description of one role.
+//   DK:  padded width of q'/k' rows (= state rows), multiple of 32
+//   DVS: padded width of the value slice a workgroup owns, multiple of 32
+//   C:   chunk length (multiple of 32, <= 128)
+template <typename E_, int DK_, int DVS_, int C_, int AUG_, bool REV_>
+struct Role {
+    typedef E_ E;
+    static constexpr int DK = DK_, DVS = DVS_, C = C_, AUG = AUG_;
+    static constexpr bool REV = REV_;
+    static constexpr int PE = 16 / (int)sizeof(E);  // 16-byte row padding
+    static constexpr int LDQ = DK + PE;             // Qs, Ks, STs row stride
+    static constexpr int LDT = C + PE;              // KTs, VTs, XTs row stride
+    static constexpr int NSTRIP = C / 32;
+    static constexpr int NNT = DVS / 32;
+    static constexpr int NDB = DK / 32;
+    static constexpr int NTILES = NDB * NNT;
+    static constexpr int NTW = (NTILES + 3) / 4;
+    static constexpr size_t OFF_Q = 0;
+    static constexpr size_t OFF_K = OFF_Q + (size_t)C * LDQ * sizeof(E);
+    static constexpr size_t OFF_KT = OFF_K + (size_t)C * LDQ * sizeof(E);
+    static constexpr size_t OFF_VT = OFF_KT + (size_t)DK * LDT * sizeof(E);
+    static constexpr size_t OFF_ST = OFF_VT + (size_t)DVS * LDT * sizeof(E);
+    static constexpr size_t OFF_XT = OFF_ST + (size_t)DVS * LDQ * sizeof(E);
+    static constexpr size_t OFF_COEF = OFF_XT + (AUG == AUG_GRAD ? (size_t)DVS * LDT * sizeof(E) : 0);
+    static constexpr size_t OFF_DA = OFF_COEF + (size_t)C * sizeof(float);
+    static constexpr size_t LDS = OFF_DA + (AUG == AUG_GRAD ? (size_t)NSTRIP * DVS * sizeof(float) : 0);
+    static_assert(DK % 32 == 0 && DVS % 32 == 0 && C % 32 == 0 && C <= 128, "tile shape");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+struct Common {
+    const float* lambda;
+    const float* a;      // [H, a_len] or NULL
+    const int32_t* cu;   // NULL when dense
+    int H, T, n_units;
+};
+
+struct RoleArgs {
+    const void* qp;  // q' rows of width dkr
+    const void* kp;  // k' rows of width dkr
+    const void* vp;  // v' rows of width dvr
+    const void* xp;  // AUG_GRAD: second operand of the gate, rows of width dvr
+    void* op;        // output rows of width dvr
+    const float* s_init;  // [units, ...] or NULL
+    float* s_final;       // [units, ...] or NULL
+    float* da_part;       // AUG_GRAD: [units, dvr] partial da, or NULL
+    int dkr, dvr;         // real widths (<= DK, <= DVS * slices)
+    int state_t;          // state stored [dvr][dkr] instead of [dkr][dvr]
+    int final_times_lam;  // final state scaled by lam (non-empty sequences)
+};
+
+template <class R>
+__device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, int unit,
+                                          int slice, char* smem)
+{
+    typedef typename R::E E;
+    typedef Mfma<E> M;
+    constexpr int C = R::C, DK = R::DK, DVS = R::DVS, LDQ = R::LDQ, LDT = R::LDT;
+    constexpr int NSTRIP = R::NSTRIP, NNT = R::NNT, NTILES = R::NTILES, NTW = R::NTW;
+    constexpr int KSTEP = M::KSTEP, NE = M::NE;
+    constexpr int V16 = 16 / (int)sizeof(E);  // elements per 16-byte segment
+
+    E* Qs = reinterpret_cast<E*>(smem + R::OFF_Q);
+    E* Ks = reinterpret_cast<E*>(smem + R::OFF_K);
+    E* KTs = reinterpret_cast<E*>(smem + R::OFF_KT);
+    E* VTs = reinterpret_cast<E*>(smem + R::OFF_VT);
+    E* STs = reinterpret_cast<E*>(smem + R::OFF_ST);
+    E* XTs = reinterpret_cast<E*>(smem + R::OFF_XT);
+    float* coef = reinterpret_cast<float*>(smem + R::OFF_COEF);
+    float* dared = reinterpret_cast<float*>(smem + R::OFF_DA);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, g = lane >> 5;
+
+    const int H = cm.H;
+    const int seq = unit / H, h = unit - seq * H;
+    long row0;
+    int len;
+    if (cm.cu != nullptr) {
+        int s0 = cm.cu[seq], s1 = cm.cu[seq + 1];
+        s0 = min(max(s0, 0), cm.T);
+        s1 = min(max(s1, s0), cm.T);
+        row0 = (long)h * cm.T + s0;
+        len = s1 - s0;
+    } else {
+        row0 = ((long)seq * H + h) * cm.T;
+        len = cm.T;
+    }
+    const float lam = cm.lambda[h];
+    const float l2 = log2f(lam);  // -inf for lam = 0
+    const int n0 = slice * DVS;
+    const int dkr = ra.dkr, dvr = ra.dvr;
+    const size_t sbase = (size_t)unit * dkr * dvr;
+
+    const E* gq = reinterpret_cast<const E*>(ra.qp);
+    const E* gk = reinterpret_cast<const E*>(ra.kp);
+    const E* gv = reinterpret_cast<const E*>(ra.vp);
+    const E* gx = reinterpret_cast<const E*>(ra.xp);
+    E* go = reinterpret_cast<E*>(ra.op);
+
+    // ---- state slice in accumulators: tile tau = db*NNT + nb, owned by wave tau%4
+    f32x16_t sacc[NTW];
+#pragma unroll
+    for (int kk = 0; kk < NTW; ++kk) {
+        const int tau = wave + 4 * kk;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[kk][i] = 0.0f;
+        if (tau < NTILES && ra.s_init != nullptr) {
+            const int db = tau / NNT, nb = tau - (tau / NNT) * NNT;
+            const int nn = n0 + 32 * nb + l32;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int d = 32 * db + acc_row(i, g);
+                if (d < dkr && nn < dvr)
+                    sacc[kk][i] = ra.state_t ? ra.s_init[sbase + (size_t)nn * dkr + d]
+                                             : ra.s_init[sbase + (size_t)d * dvr + nn];
+            }
+        }
+    }
+
+    float da_acc[NNT];
+#pragma unroll
+    for (int nt = 0; nt < NNT; ++nt) da_acc[nt] = 0.0f;
+
+    // lam^(t+1) for the strip rows this lane holds
+    float lq[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) lq[i] = decay_pow(32 * wave + acc_row(i, g) + 1, l2);
+
+    const int nchunks = (len + C - 1) / C;
+    for (int ci = 0; ci < nchunks; ++ci) {
+        const int c = R::REV ? (nchunks - 1 - ci) : ci;
+        const int cstart = c * C;
+        const int clen = min(C, len - cstart);
+
+        __syncthreads();  // previous chunk's LDS readers are done
+
+        // state before this chunk -> STs (operand dtype), transposed
+#pragma unroll
+        for (int kk = 0; kk < NTW; ++kk) {
+            const int tau = wave + 4 * kk;
+            if (tau < NTILES) {
+                const int db = tau / NNT, nb = tau - (tau / NNT) * NNT;
+                const int nl = 32 * nb + l32;
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    STs[nl * LDQ + 32 * db + acc_row(i, g)] = from_f<E>(sacc[kk][i]);
+            }
+        }
+
+        // q', k' rows (natural) and k' scaled + transposed
+        constexpr int SEGQ = DK / V16;
+        for (int idx = tid; idx < C * SEGQ; idx += NTHREADS) {
+            const int r = idx / SEGQ, col = (idx - (idx / SEGQ) * SEGQ) * V16;
+            uint4 qv = make_uint4(0, 0, 0, 0), kv = make_uint4(0, 0, 0, 0);
+            if (r < clen && col < dkr) {
+                const int tok = R::REV ? (cstart + clen - 1 - r) : (cstart + r);
+                const size_t off = (size_t)(row0 + tok) * dkr + col;
+                qv = *reinterpret_cast<const uint4*>(gq + off);
+                kv = *reinterpret_cast<const uint4*>(gk + off);
+            }
+            *reinterpret_cast<uint4*>(Qs + r * LDQ + col) = qv;
+            *reinterpret_cast<uint4*>(Ks + r * LDQ + col) = kv;
+            const float sk = (r < clen) ? decay_pow(clen - 1 - r, l2) : 0.0f;
+            const E* ke = reinterpret_cast<const E*>(&kv);
+#pragma unroll
+            for (int e = 0; e < V16; ++e) KTs[(col + e) * LDT + r] = from_f<E>(sk * to_f(ke[e]));
+        }
+        // v' slice (and the gate's second operand) transposed
+        constexpr int SEGV = DVS / V16;
+        for (int idx = tid; idx < C * SEGV; idx += NTHREADS) {
+            const int r = idx / SEGV, col = (idx - (idx / SEGV) * SEGV) * V16;
+            const int gcol = n0 + col;
+            uint4 vv = make_uint4(0, 0, 0, 0), xv = make_uint4(0, 0, 0, 0);
+            if (r < clen && gcol < dvr) {
+                const int tok = R::REV ? (cstart + clen - 1 - r) : (cstart + r);
+                const size_t off = (size_t)(row0 + tok) * dvr + gcol;
+                vv = *reinterpret_cast<const uint4*>(gv + off);
+                if (R::AUG == AUG_GRAD) xv = *reinterpret_cast<const uint4*>(gx + off);
+            }
+            const E* ve = reinterpret_cast<const E*>(&vv);
+            const E* xe = reinterpret_cast<const E*>(&xv);
+#pragma unroll
+            for (int e = 0; e < V16; ++e) {
+                VTs[(col + e) * LDT + r] = ve[e];
+                if (R::AUG == AUG_GRAD) XTs[(col + e) * LDT + r] = xe[e];
+            }
+        }
+        __syncthreads();
+
+        // per-token epilogue coefficient (two threads per token)
+        if (tid < 2 * C) {
+            const int r = tid >> 1, half = tid & 1;
+            const float* ah = (cm.a != nullptr) ? cm.a + (size_t)h * (R::AUG == AUG_FWD ? dkr : dvr)
+                                                : nullptr;
+            float z = 0.0f, u = 0.0f;
+            if (R::AUG == AUG_FWD) {
+                if (ah != nullptr)
+                    for (int d = half; d < dkr; d += 2)
+                        z += ah[d] * to_f(Qs[r * LDQ + d]) * to_f(Ks[r * LDQ + d]);
+            } else {
+                if (ah != nullptr)
+                    for (int nn = half; nn < dvr; nn += 2)
+                        z += ah[nn] * to_f(VTs[nn * LDT + r]) * to_f(XTs[nn * LDT + r]);
+                for (int d = half; d < dkr; d += 2) u += to_f(Qs[r * LDQ + d]) * to_f(Ks[r * LDQ + d]);
+            }
+            z += __shfl_xor(z, 1);
+            u += __shfl_xor(u, 1);
+            if (half == 0) {
+                const float s = sigmoidf_(z);
+                coef[r] = (R::AUG == AUG_FWD) ? s : s * (1.0f - s) * u;
+            }
+        }
+        __syncthreads();
+
+        // ---- query strips
+        if (wave < NSTRIP) {
+            const int t0 = 32 * wave;
+            f32x16_t oacc[NNT];
+#pragma unroll
+            for (int nt = 0; nt < NNT; ++nt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[nt][i] = 0.0f;
+
+            // inter-chunk: Q' S_in
+#pragma unroll 2
+            for (int kb = 0; kb < DK / KSTEP; ++kb) {
+                const typename M::op_t av = M::load(Qs + (t0 + l32) * LDQ + kb * KSTEP + g * NE);
+#pragma unroll
+                for (int nt = 0; nt < NNT; ++nt) {
+                    const typename M::op_t bv = M::load(STs + (32 * nt + l32) * LDQ + kb * KSTEP + g * NE);
+                    oacc[nt] = M::mma(av, bv, oacc[nt]);
+                }
+            }
+#pragma unroll
+            for (int nt = 0; nt < NNT; ++nt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[nt][i] *= lq[i];
+
+            // intra-chunk: decay-masked scores, then P V'
+            for (int jb = 0; jb <= wave; ++jb) {
+                if (32 * jb >= clen) break;
+                f32x16_t sc;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sc[i] = 0.0f;
+#pragma unroll 2
+                for (int kb = 0; kb < DK / KSTEP; ++kb) {
+                    const typename M::op_t av = M::load(Ks + (32 * jb + l32) * LDQ + kb * KSTEP + g * NE);
+                    const typename M::op_t bv = M::load(Qs + (t0 + l32) * LDQ + kb * KSTEP + g * NE);
+                    sc = M::mma(av, bv, sc);
+                }
+                // sc[i] = k'_j . q'_t with j = 32 jb + acc_row(i, g), t = t0 + l32
+                const int t = t0 + l32;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int diff = t - (32 * jb + acc_row(i, g));
+                    sc[i] = (diff < 0) ? 0.0f : (diff == 0 ? sc[i] : sc[i] * exp2f((float)diff * l2));
+                }
+                if constexpr (sizeof(E) == 2) {
+                    // two contraction steps of 16 keys: step hh uses sc[8hh..8hh+7],
+                    // i.e. keys 16hh + {4g..4g+3, 8+4g..8+4g+3}
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        u16x8_t pw;
+#pragma unroll
+                        for (int s = 0; s < 8; ++s) pw[s] = from_f<u16>(sc[8 * hh + s]);
+                        const bf16x8_t pa = __builtin_bit_cast(bf16x8_t, pw);
+#pragma unroll
+                        for (int nt = 0; nt < NNT; ++nt) {
+                            const E* vb = VTs + (32 * nt + l32) * LDT + 32 * jb + 16 * hh + 4 * g;
+                            const u16x4_t lo = *reinterpret_cast<const u16x4_t*>(vb);
+                            const u16x4_t hi = *reinterpret_cast<const u16x4_t*>(vb + 8);
+                            const u16x8_t bw = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                            oacc[nt] = M::mma(pa, __builtin_bit_cast(bf16x8_t, bw), oacc[nt]);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int s = 0; s < 16; ++s) {
+#pragma unroll
+                        for (int nt = 0; nt < NNT; ++nt) {
+                            const float bv = to_f(VTs[(32 * nt + l32) * LDT + 32 * jb + acc_row(s, g)]);
+                            oacc[nt] = M::mma(sc[s], bv, oacc[nt]);
+                        }
+                    }
+                }
+            }
+
+            // epilogue: + coef_t * w_n * v'_t[n]  (w = 1, or a for the gradient roles)
+#pragma unroll
+            for (int nt = 0; nt < NNT; ++nt) {
+                const int nl = 32 * nt + l32;
+                const int gcol = n0 + nl;
+                float wn = 1.0f;
+                if (R::AUG == AUG_GRAD)
+                    wn = (cm.a != nullptr && gcol < dvr) ? cm.a[(size_t)h * dvr + gcol] : 0.0f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int t = t0 + acc_row(i, g);
+                    const float vt = to_f(VTs[nl * LDT + t]);
+                    const float cf = coef[t];
+                    oacc[nt][i] += cf * wn * vt;
+                    if (R::AUG == AUG_GRAD) da_acc[nt] += cf * vt * to_f(XTs[nl * LDT + t]);
+                }
+                if (gcol < dvr) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int t = t0 + acc_row(i, g);
+                        if (t < clen) {
+                            const int tok = R::REV ? (cstart + clen - 1 - t) : (cstart + t);
+                            go[(size_t)(row0 + tok) * dvr + gcol] = from_f<E>(oacc[nt][i]);
+                        }
+                    }
+                }
+            }
+        }
+
+        // ---- state advance: S = lam^(C_c) S + K~^T V'
+        const float fc = decay_pow(clen, l2);
+#pragma unroll
+        for (int kk = 0; kk < NTW; ++kk) {
+            const int tau = wave + 4 * kk;
+            if (tau < NTILES) {
+                const int db = tau / NNT, nb = tau - (tau / NNT) * NNT;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sacc[kk][i] *= fc;
+#pragma unroll 2
+                for (int kb = 0; kb < C / KSTEP; ++kb) {
+                    const typename M::op_t av = M::load(KTs + (32 * db + l32) * LDT + kb * KSTEP + g * NE);
+                    const typename M::op_t bv = M::load(VTs + (32 * nb + l32) * LDT + kb * KSTEP + g * NE);
+                    sacc[kk] = M::mma(av, bv, sacc[kk]);
+                }
+            }
+        }
+    }
+
+    // ---- final state
+    if (ra.s_final != nullptr) {
+        const float fs = (ra.final_times_lam && len > 0) ? lam : 1.0f;
+#pragma unroll
+        for (int kk = 0; kk < NTW; ++kk) {
+            const int tau = wave + 4 * kk;
+            if (tau < NTILES) {
+                const int db = tau / NNT, nb = tau - (tau / NNT) * NNT;
+                const int nn = n0 + 32 * nb + l32;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int d = 32 * db + acc_row(i, g);
+                    if (d < dkr && nn < dvr) {
+                        const float val = sacc[kk][i] * fs;
+                        if (ra.state_t) ra.s_final[sbase + (size_t)nn * dkr + d] = val;
+                        else ra.s_final[sbase + (size_t)d * dvr + nn] = val;
+                    }
+                }
+            }
+        }
+    }
+
+    // ---- partial da of this (sequence, head): fixed-order reduction
+    if (R::AUG == AUG_GRAD && ra.da_part != nullptr) {
+        __syncthreads();
+        if (wave < NSTRIP) {
+#pragma unroll
+            for (int nt = 0; nt < NNT; ++nt) {
+                const float s = da_acc[nt] + __shfl_xor(da_acc[nt], 32);
+                if (g == 0) dared[wave * DVS + 32 * nt + l32] = s;
+            }
+        }
+        __syncthreads();
+        for (int nl = tid; nl < DVS; nl += NTHREADS) {
+            float s = 0.0f;
+            for (int w = 0; w < NSTRIP; ++w) s += dared[w * DVS + nl];
+            if (n0 + nl < dvr) ra.da_part[(size_t)unit * dvr + n0 + nl] = s;
+        }
+    }
+}
+
+// blockIdx -> (unit, slice): consecutive slices of one unit land on the same
+// XCD (blocks are dealt to the 8 XCDs round-robin), so their shared q'/k'
+// reads hit the same L2.
+__device__ __forceinline__ bool map_block(int nsl, int n_units, int& unit, int& slice)
+{
+    const int b = blockIdx.x;
+    const int xcd = b & 7, loc = b >> 3;
+    slice = loc % nsl;
+    unit = (loc / nsl) * 8 + xcd;
+    return unit < n_units;
+}
+
+template <class R>
+__global__ __launch_bounds__(NTHREADS) void k_chunk_fwd(Common cm, RoleArgs ra, int nsl)
+{
+    __shared__ __attribute__((aligned(16))) char smem[R::LDS];
+    int unit, slice;
+    if (!map_block(nsl, cm.n_units, unit, slice)) return;
+    role_body<R>(cm, ra, unit, slice, smem);
+}
+
+constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
+
+template <class RQ, class RK, class RV>
+__global__ __launch_bounds__(NTHREADS) void k_chunk_bwd(Common cm, RoleArgs aq, RoleArgs ak,
+                                                        RoleArgs av, int nslv)
+{
+    __shared__ __attribute__((aligned(16))) char smem[cmax(RQ::LDS, cmax(RK::LDS, RV::LDS))];
+    int unit, vs;
+    if (!map_block(2 + nslv, cm.n_units, unit, vs)) return;
+    if (vs == 0) role_body<RQ>(cm, aq, unit, 0, smem);
+    else if (vs == 1) role_body<RK>(cm, ak, unit, 0, smem);
+    else role_body<RV>(cm, av, unit, vs - 2, smem);
+}
+
+// da[h][d] = sum over sequences n (in order) of da_part[n*H + h][d]
+__global__ void k_da_reduce(const float* da_part, float* da, int n_seq, int H, int dkr)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= H * dkr) return;
+    const int h = i / dkr, d = i - (i / dkr) * dkr;
+    float s = 0.0f;
+    for (int n = 0; n < n_seq; ++n) s += da_part[((size_t)n * H + h) * dkr + d];
+    da[i] = s;
+}
+
+__global__ void k_fill_zero(float* p, int n)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0.0f;
+}
+
+int round8(int x) { return (x + 7) / 8 * 8; }
+
+template <class R>
+hipError_t run_fwd(const ChunkProblem& p, const RoleArgs& ra, int nsl, hipStream_t stream)
+{
+    Common cm{p.lambda, p.a, p.cu, p.H, p.T, p.n_seq * p.H};
+    const int grid = round8(cm.n_units) * nsl;
+    hipLaunchKernelGGL(k_chunk_fwd<R>, dim3(grid), dim3(NTHREADS), 0, stream, cm, ra, nsl);
+    return hipGetLastError();
+}
+
+template <class RQ, class RK, class RV>
+hipError_t run_bwd(const ChunkProblem& p, const RoleArgs& aq, const RoleArgs& ak,
+                   const RoleArgs& av, int nslv, float* da, hipStream_t stream)
+{
+    Common cm{p.lambda, p.a, p.cu, p.H, p.T, p.n_seq * p.H};
+    const int grid = round8(cm.n_units) * (2 + nslv);
+    hipLaunchKernelGGL((k_chunk_bwd<RQ, RK, RV>), dim3(grid), dim3(NTHREADS), 0, stream, cm, aq, ak,
+                       av, nslv);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nda = p.H * p.d_k;
+    if (p.a != nullptr) {
+        hipLaunchKernelGGL(k_da_reduce, dim3((nda + 255) / 256), dim3(256), 0, stream, aq.da_part, da,
+                           p.n_seq, p.H, p.d_k);
+    } else {
+        hipLaunchKernelGGL(k_fill_zero, dim3((nda + 255) / 256), dim3(256), 0, stream, da, nda);
+    }
+    return hipGetLastError();
+}
+
+// Role instantiations
+typedef Role<u16, 96, 96, 128, AUG_FWD, false> BfFwd128;
+typedef Role<u16, 96, 96, 64, AUG_FWD, false> BfFwd64;
+typedef Role<u16, 192, 96, 64, AUG_GRAD, false> BfDq;
+typedef Role<u16, 192, 96, 64, AUG_GRAD, true> BfDk;
+typedef Role<u16, 96, 96, 128, AUG_FWD, true> BfDv128;
+typedef Role<u16, 96, 96, 64, AUG_FWD, true> BfDv64;
+typedef Role<float, 32, 32, 64, AUG_FWD, false> F32Fwd;
+typedef Role<float, 32, 32, 64, AUG_GRAD, false> F32Dq;
+typedef Role<float, 32, 32, 64, AUG_GRAD, true> F32Dk;
+typedef Role<float, 32, 32, 64, AUG_FWD, true> F32Dv;
+
+}  // namespace
+
+hipError_t launch_chunk_fwd(const ChunkProblem& p, const void* q, const void* k, const void* v,
+                            const float* init_state, float* final_state, void* o,
+                            hipStream_t stream)
+{
+    RoleArgs ra{q, k, v, nullptr, o, init_state, final_state, nullptr, p.d_k, p.d_v, 0, 0};
+    if (p.bf16) {
+        const int nsl = (p.d_v + 95) / 96;
+        if (p.chunk == 128) return run_fwd<BfFwd128>(p, ra, nsl, stream);
+        return run_fwd<BfFwd64>(p, ra, nsl, stream);
+    }
+    return run_fwd<F32Fwd>(p, ra, (p.d_v + 31) / 32, stream);
+}
+
+hipError_t launch_chunk_bwd(const ChunkProblem& p, const void* q, const void* k, const void* v,
+                            const void* dO, const float* init_state, const float* d_final_state,
+                            void* dq, void* dk, void* dv, float* da, float* d_init_state,
+                            float* da_partial, hipStream_t stream)
+{
+    // dq: forward scan of S^T ([d_v][d_k]); q'=dO, k'=v, v'=k, gate operand q
+    RoleArgs aq{dO, v, k, q, dq, init_state, nullptr,
+                p.a != nullptr ? da_partial : nullptr, p.d_v, p.d_k, 1, 0};
+    // dk: reverse scan of G^T ([d_v][d_k]); q'=v, k'=dO, v'=q, gate operand k
+    RoleArgs ak{v, dO, q, k, dk, d_final_state, nullptr, nullptr, p.d_v, p.d_k, 1, 0};
+    // dv: reverse scan of G ([d_k][d_v]); q'=k, k'=q, v'=dO; final G -> d_init_state
+    RoleArgs av{k, q, dO, nullptr, dv, d_final_state, d_init_state, nullptr, p.d_k, p.d_v, 0, 1};
+    if (p.bf16) {
+        const int nslv = (p.d_v + 95) / 96;
+        if (p.chunk == 128) return run_bwd<BfDq, BfDk, BfDv128>(p, aq, ak, av, nslv, da, stream);
+        return run_bwd<BfDq, BfDk, BfDv64>(p, aq, ak, av, nslv, da, stream);
+    }
+    return run_bwd<F32Dq, F32Dk, F32Dv>(p, aq, ak, av, (p.d_v + 31) / 32, da, stream);
+}
+
+}  // namespace sgla

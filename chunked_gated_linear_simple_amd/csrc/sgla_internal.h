@@ -1,0 +1,39 @@
+// Internal interface between the C-ABI host layer (sgla_api.cpp) and the HIP
+// launchers (sgla_chunk.hip, sgla_decode.hip). Not installed, not part of the ABI.
+#ifndef SGLA_INTERNAL_H
+#define SGLA_INTERNAL_H
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sgla {
+
+// Everything a chunked launch needs, already validated on the host.
+struct ChunkProblem {
+    int bf16;          // 1: bf16 tensors, 0: fp32 tensors
+    int B, H, T;       // T = tokens per sequence (dense) or total tokens (packed)
+    int n_seq;         // sequences N (= B when dense)
+    int d_k, d_v;
+    int chunk;
+    const float* lambda;
+    const float* a;
+    const int32_t* cu;  // NULL when dense
+};
+
+hipError_t launch_chunk_fwd(const ChunkProblem& p, const void* q, const void* k, const void* v,
+                            const float* init_state, float* final_state, void* o,
+                            hipStream_t stream);
+
+hipError_t launch_chunk_bwd(const ChunkProblem& p, const void* q, const void* k, const void* v,
+                            const void* dO, const float* init_state, const float* d_final_state,
+                            void* dq, void* dk, void* dv, float* da, float* d_init_state,
+                            float* da_partial, hipStream_t stream);
+
+hipError_t launch_decode_step(int bf16, const void* q, const void* k, const void* v,
+                              const float* lambda, const float* a, float* state,
+                              const int32_t* slot, void* o, int N, int P, int H, int d_k,
+                              int d_v, hipStream_t stream);
+
+}  // namespace sgla
+
+#endif

@@ -1,0 +1,192 @@
+/*
+ * libsgla: Simple Gated Linear Attention (Simple GLA) on AMD Instinct MI355X
+ * (gfx950). C ABI.
+ *
+ * The method is the token mixer of the Laplace 3B model, as described in the
+ * page "Beyond the KV cache: Training and serving i14's Laplace 3B linear
+ * attention model on AWS Trainium2 with native PyTorch" (the Laplace 3B post),
+ * section "i14 and the Laplace 3B architecture", paragraph "GLA mixer". Per
+ * sequence and head h, with a d_k x d_v state S and a fixed decay lam_h:
+ *
+ *   S_t = lam_h S_{t-1} + k_t v_t^T                    (state update)
+ *   o_t = S_t^T q_t + sigmoid(sum_i a_{h,i} q_{t,i} k_{t,i}) v_t
+ *                                  (readout of the updated state, plus the
+ *                                   self-augmentation term)
+ *
+ * The page's display equations are missing from its text; the readings taken
+ * (readout after the update, a per (head, key channel), no scaling of q inside
+ * the library, zero initial state by default) are listed with the reasons for
+ * each in the design notes.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers: every tensor argument is DEVICE memory owned by the caller, except
+ *   where a comment says "host". The library allocates nothing and keeps no
+ *   state between calls, apart from the thread-local error message.
+ * Streams: GPU work is enqueued on `hip_stream` (a hipStream_t; NULL = the
+ *   default stream) and the call returns without synchronizing. Outputs are
+ *   valid once the stream reaches them.
+ * dtype: q, k, v, o (and dO, dq, dk, dv) are all SGLA_BF16 or all SGLA_F32.
+ *   States, lambda, a and da are always fp32. Arithmetic is fp32 throughout
+ *   (bf16 operands into fp32-accumulating matrix cores for SGLA_BF16).
+ * Layouts (row-major, last index fastest):
+ *   dense:  q, k [B, H, T, d_k];  v, o [B, H, T, d_v];  N = B sequences.
+ *   packed: with cu_seqlens != NULL: B must be 1, T is the total token count,
+ *           q, k [1, H, T, d_k], v, o [1, H, T, d_v], and sequence n holds
+ *           tokens [cu_seqlens[n], cu_seqlens[n+1]) (int32, n_seq+1 entries,
+ *           non-decreasing, cu_seqlens[0] = 0, cu_seqlens[n_seq] <= T).
+ *   states: [N, H, d_k, d_v] fp32.   lambda: [H] fp32.   a, da: [H, d_k] fp32.
+ * Alignment: every tensor pointer must be 16-byte aligned.
+ * Errors: argument errors are detected on the host before anything is
+ *   enqueued; the call returns a non-zero status and sgla_last_error() gives a
+ *   message. A launch failure returns SGLA_ERR_HIP. Device memory contents are
+ *   not inspected: NaN inputs propagate; lambda outside [0, 1] gives whatever
+ *   the recurrence gives; cu_seqlens entries are clamped into [0, T] on the
+ *   device (a decreasing entry yields an empty sequence) so that no access
+ *   leaves the buffers.
+ * Determinism: the same inputs on the same device give bitwise-identical
+ *   outputs, including da (fixed-order reductions, no float atomics).
+ * Supported shapes:
+ *   SGLA_BF16: d_k <= 96, d_v <= 192, both multiples of 8; chunk 64 or 128.
+ *   SGLA_F32:  d_k <= 32, d_v <= 32, both multiples of 4; chunk 64.
+ *   Anything else returns SGLA_ERR_UNSUPPORTED.
+ */
+#ifndef SGLA_H
+#define SGLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SGLA_OK = 0,
+    SGLA_ERR_INVALID_ARG = 1,
+    SGLA_ERR_UNSUPPORTED = 2,
+    SGLA_ERR_WORKSPACE = 3,
+    SGLA_ERR_HIP = 4
+} sgla_status;
+
+typedef enum { SGLA_F32 = 0, SGLA_BF16 = 1 } sgla_dtype;
+
+/* Library version as major*10000 + minor*100 + patch. */
+int sgla_version(void);
+
+/* Static text for a status code. Never NULL. */
+const char* sgla_status_str(int status);
+
+/* Message of the last failed call on this thread ("" if none). Never NULL. */
+const char* sgla_last_error(void);
+
+/*
+ * Decay schedule. Laplace 3B post, "i14 and the Laplace 3B architecture",
+ * paragraphs "Decay schedule" and "Decay schedule's reach": fixed per-head
+ * decays with half-lives spread geometrically from t_min (head 0) to t_max
+ * (head H-1); a half-life of T tokens means lam^T = 1/2. So
+ *   T_h = t_min * (t_max / t_min)^(h / (H-1))   (T_0 = t_min when H == 1)
+ *   lambda_out[h] = 2^(-1 / T_h)
+ * computed in fp64 and rounded to fp32. With H = 16, t_min = 1, t_max = 2048
+ * this gives lambda_0 = 0.5 and lambda_15 = 0.99966 (the page: ~0.9997).
+ *
+ * lambda_out: HOST array of H floats, written. Runs on the host, no GPU work.
+ * Errors: SGLA_ERR_INVALID_ARG if lambda_out is NULL, H <= 0, t_min <= 0 or
+ * t_max < t_min (or either is not finite).
+ */
+sgla_status sgla_decay_schedule(int H, double t_min, double t_max, float* lambda_out);
+
+/*
+ * Chunked forward. Laplace 3B post, "Challenge 1: Using native PyTorch on
+ * Trainium for GLA": the sequence is cut into chunks of `chunk` tokens; inside
+ * a chunk the output is decay-masked linear attention plus the contribution of
+ * the running state carried in from earlier chunks, and the state then
+ * advances by the chunk's decay compounded over the chunk plus the chunk's
+ * decayed key/value outer products. This is an exact rewrite of the token
+ * recurrence above, so the result does not depend on `chunk` beyond rounding.
+ *
+ * q, k, v:     inputs (dtype, layouts above); q is used as given (no scale).
+ * lambda:      [H] per-head decay.
+ * a:           [H, d_k] self-augmentation scale (aug_balance), or NULL = 0.
+ * init_state:  [N, H, d_k, d_v] state before the first token, or NULL = 0.
+ * final_state: [N, H, d_k, d_v] state after the last token, or NULL (not
+ *              written). May equal init_state (in-place carry).
+ * o:           output [.., d_v] (dtype). Must not alias any input.
+ * cu_seqlens:  packed-sequence offsets (see layouts) or NULL (dense).
+ * n_seq:       number of sequences when cu_seqlens != NULL; ignored otherwise.
+ * chunk:       tokens per chunk (64 or 128 for SGLA_BF16, 64 for SGLA_F32).
+ */
+sgla_status sgla_chunk_fwd(const void* q, const void* k, const void* v,
+                           const float* lambda, const float* a,
+                           const float* init_state, float* final_state, void* o,
+                           const int32_t* cu_seqlens, int n_seq,
+                           int B, int H, int T, int d_k, int d_v, int chunk,
+                           sgla_dtype dtype, void* hip_stream);
+
+/*
+ * Bytes of device workspace sgla_chunk_bwd needs for these sizes (the per
+ * sequence-head partial sums of da). N is n_seq for packed input, else B.
+ */
+size_t sgla_chunk_bwd_workspace_bytes(int N, int H, int d_k);
+
+/*
+ * Chunked backward: gradients of the forward above for a loss L with
+ * dL/do = dO and dL/d(final_state) = d_final_state. Laplace 3B post,
+ * "Challenge 3: Backward-pass unrolling for a sequential recurrence": the
+ * backward differentiates through every sequential state update. Written as
+ *   dq_t = S_t dO_t + sigmoid'(z_t) (dO_t . v_t) (a * k_t)
+ *   G_t  = dL/dS_t = lam G_{t+1} + q_t dO_t^T      (G_{T-1} = dS_final + q dO^T)
+ *   dk_t = G_t v_t + sigmoid'(z_t) (dO_t . v_t) (a * q_t)
+ *   dv_t = G_t^T k_t + sigmoid(z_t) dO_t
+ *   da   = sum over sequences and t of sigmoid'(z_t) (dO_t . v_t) (q_t * k_t)
+ *   d_init_state = lam G_0   (= d_final_state for an empty sequence)
+ * and evaluated chunk-wise, as three independent recurrences run at once
+ * (a forward scan for dq and two reverse scans for dk and dv).
+ *
+ * q, k, v, lambda, a, init_state, cu_seqlens, n_seq, sizes, chunk, dtype:
+ *              as for sgla_chunk_fwd (same values as the forward call).
+ * dO:          [.., d_v] upstream gradient of o (dtype).
+ * d_final_state: [N, H, d_k, d_v] or NULL = 0.
+ * dq, dk, dv:  outputs (dtype), shaped like q, k, v; must not alias inputs.
+ * da:          [H, d_k] fp32, overwritten (zeros when a is NULL).
+ * d_init_state: [N, H, d_k, d_v] or NULL (not written).
+ * workspace:   device buffer of at least sgla_chunk_bwd_workspace_bytes()
+ *              bytes, 16-byte aligned, owned by the caller; its contents on
+ *              entry do not matter and are clobbered.
+ * Errors: as sgla_chunk_fwd, plus SGLA_ERR_WORKSPACE if workspace is NULL or
+ * too small.
+ */
+sgla_status sgla_chunk_bwd(const void* q, const void* k, const void* v, const void* dO,
+                           const float* lambda, const float* a,
+                           const float* init_state, const float* d_final_state,
+                           void* dq, void* dk, void* dv, float* da, float* d_init_state,
+                           const int32_t* cu_seqlens, int n_seq,
+                           int B, int H, int T, int d_k, int d_v, int chunk,
+                           sgla_dtype dtype, void* workspace, size_t workspace_bytes,
+                           void* hip_stream);
+
+/*
+ * One decode step for N sequences, in place on their states. Laplace 3B post,
+ * "Inference optimization on Trainium2", paragraphs "Constant serving state"
+ * and "Unmodified vLLM": each sequence keeps a fixed-size recurrent state in
+ * a page of a state pool, and each new token reads and writes that page:
+ *   S <- lam_h S + k v^T;   o = S^T q + sigmoid(sum_i a_{h,i} q_i k_i) v
+ *
+ * q, k:    [N, H, d_k] (dtype).   v, o: [N, H, d_v] (dtype).
+ * state:   [P, H, d_k, d_v] fp32 pool, read and written in place.
+ * slot:    [N] int32 page index of each sequence, or NULL (sequence n uses
+ *          page n, and then P >= N is required). Entries must be distinct;
+ *          an entry outside [0, P) skips that sequence and writes NaN to its o.
+ * Supported: d_k = 96, d_v = 192 or d_k = 16, d_v = 32, either dtype.
+ * The output of one sequence does not depend on N or on the other sequences.
+ */
+sgla_status sgla_decode_step(const void* q, const void* k, const void* v,
+                             const float* lambda, const float* a,
+                             float* state, const int32_t* slot, void* o,
+                             int N, int P, int H, int d_k, int d_v,
+                             sgla_dtype dtype, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SGLA_H */

@@ -1,0 +1,196 @@
+"""The C ABI on the CPU: the library loads, exports what include/sgla.h
+declares, computes the decay schedule, and rejects bad arguments on the host
+before anything reaches the GPU (no kernel is launched by these tests)."""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from chunked_gated_linear_simple_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        from chunked_gated_linear_simple_amd import build
+        build.build()
+    return B.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    declared = B.declared_functions()
+    assert set(declared) >= {"sgla_decay_schedule", "sgla_chunk_fwd", "sgla_chunk_bwd",
+                             "sgla_chunk_bwd_workspace_bytes", "sgla_decode_step",
+                             "sgla_last_error", "sgla_status_str", "sgla_version"}
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s+(sgla_\w+)", out))
+    missing = [f for f in declared if f not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    for f in declared:
+        getattr(L, f)  # resolvable through ctypes
+
+
+def test_version_and_status_strings(L):
+    assert B.sgla_version() >= 100
+    for code, name in enumerate(["SGLA_OK", "SGLA_ERR_INVALID_ARG", "SGLA_ERR_UNSUPPORTED",
+                                 "SGLA_ERR_WORKSPACE", "SGLA_ERR_HIP"]):
+        assert L.sgla_status_str(code).decode() == name
+    assert L.sgla_status_str(99).decode() == "unknown sgla_status"
+
+
+def test_decay_schedule_matches_oracle(L):
+    for H, tmin, tmax in ((16, 1.0, 2048.0), (2, 1.0, 256.0), (1, 3.0, 3.0), (7, 0.5, 9.0)):
+        got = B.sgla_decay_schedule(H, tmin, tmax).numpy()
+        want = oracle.decay_schedule(H, tmin, tmax).astype(np.float32)
+        # same fp64 formula rounded once to fp32: equal to within one fp32 ulp
+        ulps = np.abs(got.view(np.int32).astype(np.int64) - want.view(np.int32).astype(np.int64))
+        assert ulps.max() <= 1, (H, got, want)
+    lam = B.sgla_decay_schedule(16, 1.0, 2048.0).numpy()
+    assert lam[0] == 0.5
+    assert abs(lam[15] - 0.9997) < 5e-5
+
+
+@pytest.mark.parametrize("args", [(0, 1.0, 2.0), (4, 0.0, 2.0), (4, 3.0, 2.0),
+                                  (4, float("nan"), 2.0), (4, 1.0, float("inf"))])
+def test_decay_schedule_rejects(L, args):
+    out = (ctypes.c_float * 8)()
+    assert L.sgla_decay_schedule(args[0], args[1], args[2], out) == B.SGLA_ERR_INVALID_ARG
+    assert L.sgla_last_error().decode()
+    assert L.sgla_decay_schedule(4, 1.0, 2.0, None) == B.SGLA_ERR_INVALID_ARG
+    assert L.sgla_decay_schedule(4, 1.0, 2.0, out) == B.SGLA_OK
+    assert L.sgla_last_error().decode() == ""
+
+
+# Fake, never-dereferenced device addresses: validation only looks at the values.
+BASE = 0x7F0000000000
+P = {n: BASE + i * 0x100000000 for i, n in enumerate(
+    ["q", "k", "v", "lam", "a", "s0", "sf", "o", "cu", "dO", "dq", "dk", "dv", "da", "ds0", "ws",
+     "state", "slot"])}
+
+
+def fwd_args(**kw):
+    a = dict(q=P["q"], k=P["k"], v=P["v"], lam=P["lam"], a=P["a"], s0=P["s0"], sf=P["sf"],
+             o=P["o"], cu=None, n_seq=0, B=2, H=16, T=256, d_k=96, d_v=192, chunk=128,
+             dt=B.SGLA_BF16)
+    a.update(kw)
+    return [a["q"], a["k"], a["v"], a["lam"], a["a"], a["s0"], a["sf"], a["o"], a["cu"],
+            a["n_seq"], a["B"], a["H"], a["T"], a["d_k"], a["d_v"], a["chunk"], a["dt"], None]
+
+
+FWD_BAD = [
+    ("q null", dict(q=None), B.SGLA_ERR_INVALID_ARG),
+    ("k misaligned", dict(k=P["k"] + 8), B.SGLA_ERR_INVALID_ARG),
+    ("o null", dict(o=None), B.SGLA_ERR_INVALID_ARG),
+    ("lambda null", dict(lam=None), B.SGLA_ERR_INVALID_ARG),
+    ("a misaligned", dict(a=P["a"] + 4), B.SGLA_ERR_INVALID_ARG),
+    ("init misaligned", dict(s0=P["s0"] + 4), B.SGLA_ERR_INVALID_ARG),
+    ("B zero", dict(B=0), B.SGLA_ERR_INVALID_ARG),
+    ("T negative", dict(T=-5), B.SGLA_ERR_INVALID_ARG),
+    ("H zero", dict(H=0), B.SGLA_ERR_INVALID_ARG),
+    ("bad dtype", dict(dt=7), B.SGLA_ERR_INVALID_ARG),
+    ("d_k too big", dict(d_k=128), B.SGLA_ERR_UNSUPPORTED),
+    ("d_v too big", dict(d_v=256), B.SGLA_ERR_UNSUPPORTED),
+    ("d_k not mult 8", dict(d_k=20), B.SGLA_ERR_UNSUPPORTED),
+    ("chunk 32", dict(chunk=32), B.SGLA_ERR_UNSUPPORTED),
+    ("f32 d_k 96", dict(dt=B.SGLA_F32), B.SGLA_ERR_UNSUPPORTED),
+    ("f32 chunk 128", dict(dt=B.SGLA_F32, d_k=16, d_v=32, chunk=128), B.SGLA_ERR_UNSUPPORTED),
+    ("o aliases q", dict(o=P["q"]), B.SGLA_ERR_INVALID_ARG),
+    ("o overlaps v", dict(o=P["v"] + 1024), B.SGLA_ERR_INVALID_ARG),
+    ("packed with B=2", dict(cu=P["cu"], n_seq=3), B.SGLA_ERR_INVALID_ARG),
+    ("packed n_seq 0", dict(cu=P["cu"], n_seq=0, B=1), B.SGLA_ERR_INVALID_ARG),
+    ("cu misaligned", dict(cu=P["cu"] + 4, n_seq=2, B=1), B.SGLA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", FWD_BAD, ids=[x[0] for x in FWD_BAD])
+def test_chunk_fwd_rejects(L, name, kw, code):
+    assert L.sgla_chunk_fwd(*fwd_args(**kw)) == code
+    assert L.sgla_last_error().decode() != ""
+
+
+def bwd_args(**kw):
+    a = dict(q=P["q"], k=P["k"], v=P["v"], dO=P["dO"], lam=P["lam"], a=P["a"], s0=P["s0"],
+             dsf=P["sf"], dq=P["dq"], dk=P["dk"], dv=P["dv"], da=P["da"], ds0=P["ds0"], cu=None,
+             n_seq=0, B=2, H=16, T=256, d_k=96, d_v=192, chunk=128, dt=B.SGLA_BF16, ws=P["ws"],
+             wsb=2 * 16 * 96 * 4)
+    a.update(kw)
+    return [a["q"], a["k"], a["v"], a["dO"], a["lam"], a["a"], a["s0"], a["dsf"], a["dq"],
+            a["dk"], a["dv"], a["da"], a["ds0"], a["cu"], a["n_seq"], a["B"], a["H"], a["T"],
+            a["d_k"], a["d_v"], a["chunk"], a["dt"], a["ws"], a["wsb"], None]
+
+
+BWD_BAD = [
+    ("dO null", dict(dO=None), B.SGLA_ERR_INVALID_ARG),
+    ("dq null", dict(dq=None), B.SGLA_ERR_INVALID_ARG),
+    ("da null", dict(da=None), B.SGLA_ERR_INVALID_ARG),
+    ("ds0 misaligned", dict(ds0=P["ds0"] + 2), B.SGLA_ERR_INVALID_ARG),
+    ("workspace null", dict(ws=None), B.SGLA_ERR_WORKSPACE),
+    ("workspace small", dict(wsb=100), B.SGLA_ERR_WORKSPACE),
+    ("workspace misaligned", dict(ws=P["ws"] + 4), B.SGLA_ERR_WORKSPACE),
+    ("dq aliases dO", dict(dq=P["dO"]), B.SGLA_ERR_INVALID_ARG),
+    ("dv aliases v", dict(dv=P["v"]), B.SGLA_ERR_INVALID_ARG),
+    ("unsupported dims", dict(d_v=200), B.SGLA_ERR_UNSUPPORTED),
+    ("T zero", dict(T=0), B.SGLA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", BWD_BAD, ids=[x[0] for x in BWD_BAD])
+def test_chunk_bwd_rejects(L, name, kw, code):
+    assert L.sgla_chunk_bwd(*bwd_args(**kw)) == code
+    assert L.sgla_last_error().decode() != ""
+
+
+def test_workspace_bytes(L):
+    assert B.sgla_chunk_bwd_workspace_bytes(4, 16, 96) == 4 * 16 * 96 * 4
+    assert B.sgla_chunk_bwd_workspace_bytes(0, 16, 96) == 0
+
+
+def dec_args(**kw):
+    a = dict(q=P["q"], k=P["k"], v=P["v"], lam=P["lam"], a=P["a"], state=P["state"], slot=None,
+             o=P["o"], N=8, Pg=8, H=16, d_k=96, d_v=192, dt=B.SGLA_BF16)
+    a.update(kw)
+    return [a["q"], a["k"], a["v"], a["lam"], a["a"], a["state"], a["slot"], a["o"], a["N"],
+            a["Pg"], a["H"], a["d_k"], a["d_v"], a["dt"], None]
+
+
+DEC_BAD = [
+    ("state null", dict(state=None), B.SGLA_ERR_INVALID_ARG),
+    ("o null", dict(o=None), B.SGLA_ERR_INVALID_ARG),
+    ("N zero", dict(N=0), B.SGLA_ERR_INVALID_ARG),
+    ("pool too small", dict(Pg=4), B.SGLA_ERR_INVALID_ARG),
+    ("slot misaligned", dict(slot=P["slot"] + 4), B.SGLA_ERR_INVALID_ARG),
+    ("dims", dict(d_k=64, d_v=64), B.SGLA_ERR_UNSUPPORTED),
+    ("dtype", dict(dt=3), B.SGLA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", DEC_BAD, ids=[x[0] for x in DEC_BAD])
+def test_decode_rejects(L, name, kw, code):
+    assert L.sgla_decode_step(*dec_args(**kw)) == code
+    assert L.sgla_last_error().decode() != ""
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    code = ("import chunked_gated_linear_simple_amd.binding as b\n"
+            "b.LIB_PATH = '/nonexistent/libsgla.so'\n"
+            "try:\n    b.lib()\nexcept RuntimeError as e:\n    print('RAISED', e)\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
+    assert "RAISED" in r.stdout, r.stdout + r.stderr
+
+
+def test_product_path_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "chunked_gated_linear_simple_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
+                assert "liboracle" not in text and "orc_" not in text, f

@@ -1,0 +1,208 @@
+"""GPU parity of sgla_chunk_fwd / sgla_chunk_bwd against the fp64 oracle, at
+sizes the oracle finishes in seconds that still span several chunks and a
+ragged tail, plus the edge cases of the method."""
+import numpy as np
+import pytest
+import torch
+
+from chunked_gated_linear_simple_amd import binding as Bd
+from chunked_gated_linear_simple_amd import inputs as I
+from tests.parity_util import (DEV, TOL, assert_close, device_inputs, gpu_unit, oracle_bwd_units,
+                               oracle_fwd_units, schedule32, to_dev, to_host64)
+
+pytestmark = pytest.mark.gpu
+
+
+def _units(N, H):
+    return [(n, h) for n in range(N) for h in range(H)]
+
+
+def run_fwd_case(inp, lam, chunk, cu=None, units=None):
+    d = device_inputs(inp, cu)
+    lam_d = to_dev(lam)
+    o, Sf = Bd.sgla_chunk_fwd(d["q"], d["k"], d["v"], lam_d, d["a"], init_state=d["S0"],
+                              cu_seqlens=d["cu"], chunk=chunk, want_final=True)
+    torch.cuda.synchronize()
+    oh, Sh = to_host64(o), to_host64(Sf)
+    units = units or _units(inp["N"], inp["H"])
+    ref = oracle_fwd_units(inp, lam, units, cu)
+    og = np.concatenate([gpu_unit(oh, n, h, cu).ravel() for n, h in units])
+    orf = np.concatenate([ref[u][0].ravel() for u in units])
+    sg = np.concatenate([Sh[n, h].ravel() for n, h in units])
+    sr = np.concatenate([ref[u][1].ravel() for u in units])
+    tol = TOL[inp["dtype"]]
+    assert_close(og, orf, tol, "o")
+    assert_close(sg, sr, tol, "final_state")
+    return o, Sf
+
+
+def run_bwd_case(inp, lam, chunk, cu=None, units=None):
+    d = device_inputs(inp, cu)
+    lam_d = to_dev(lam)
+    dq, dk, dv, da, dS0 = Bd.sgla_chunk_bwd(d["q"], d["k"], d["v"], d["dO"], lam_d, d["a"],
+                                            init_state=d["S0"], d_final_state=d["dSf"],
+                                            cu_seqlens=d["cu"], chunk=chunk, want_d_init=True)
+    torch.cuda.synchronize()
+    units = units or _units(inp["N"], inp["H"])
+    ref = oracle_bwd_units(inp, lam, units, cu)
+    tol = TOL[inp["dtype"]]
+    for idx, (name, t) in enumerate((("dq", dq), ("dk", dk), ("dv", dv))):
+        th = to_host64(t)
+        g = np.concatenate([gpu_unit(th, n, h, cu).ravel() for n, h in units])
+        r = np.concatenate([ref[u][idx].ravel() for u in units])
+        assert_close(g, r, tol, name)
+    if len(units) == inp["N"] * inp["H"]:
+        da_ref = np.zeros_like(inp["a"], dtype=np.float64)
+        for (n, h) in units:
+            da_ref[h] += ref[(n, h)][3]
+        assert_close(to_host64(da), da_ref, tol, "da")
+    dsh = to_host64(dS0)
+    assert_close(np.concatenate([dsh[n, h].ravel() for n, h in units]),
+                 np.concatenate([ref[u][4].ravel() for u in units]), tol, "d_init_state")
+    return dq, dk, dv, da, dS0
+
+
+# ------------------------------------------------------------------ fp32 (1e-4 gate)
+
+
+def test_fwd_f32_tiny_config():
+    """B=1 H=2 T=256 d_k=16 d_v=32 chunk 64, fp32, schedule 1..256, zero init."""
+    inp = I.chunk_inputs(1, 2, 256, 16, 32, "f32", seed=1, a_std=0.1)
+    run_fwd_case(inp, schedule32(2, 1.0, 256.0), 64)
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 200])
+def test_fwd_f32_ragged_with_state(T):
+    inp = I.chunk_inputs(2, 4, T, 16, 32, "f32", seed=10 + T, a_std=0.3, s0_std=0.2)
+    lam = np.array([0.0, 0.5, 0.99, 1.0], np.float32)  # lam = 0 and 1 included
+    run_fwd_case(inp, lam, 64)
+
+
+def test_fwd_f32_other_widths():
+    inp = I.chunk_inputs(1, 3, 130, 8, 24, "f32", seed=30, a_std=0.3, s0_std=0.1)
+    run_fwd_case(inp, np.array([0.3, 0.8, 0.999], np.float32), 64)
+
+
+@pytest.mark.parametrize("T", [1, 64, 150])
+def test_bwd_f32(T):
+    inp = I.chunk_inputs(2, 3, T, 16, 32, "f32", seed=40 + T, a_std=0.5, s0_std=0.2,
+                         with_grad=True, dsf_std=0.3)
+    run_bwd_case(inp, np.array([0.0, 0.9, 1.0], np.float32), 64)
+
+
+def test_bwd_f32_no_aug_no_state():
+    inp = I.chunk_inputs(1, 2, 100, 16, 32, "f32", seed=50, a_std=None, with_grad=True)
+    dq, dk, dv, da, _ = run_bwd_case(inp, np.array([0.6, 0.97], np.float32), 64)
+    assert torch.count_nonzero(da).item() == 0
+
+
+def test_varlen_f32_fwd_bwd():
+    L = [1, 0, 130, 64, 65, 7]
+    cu = I.cu_from_lengths(L)
+    inp = I.chunk_inputs(1, 2, int(cu[-1]), 16, 32, "f32", seed=60, a_std=0.4, s0_std=0.2,
+                         n_seq=len(L), with_grad=True, dsf_std=0.2)
+    lam = np.array([0.7, 0.995], np.float32)
+    run_fwd_case(inp, lam, 64, cu=cu)
+    run_bwd_case(inp, lam, 64, cu=cu)
+
+
+# ------------------------------------------------------------------ bf16 (2e-2 gate)
+
+
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_fwd_bf16_several_chunks(chunk):
+    inp = I.chunk_inputs(2, 16, 320, 96, 192, "bf16", seed=70, a_std=0.1, s0_std=0.02)
+    run_fwd_case(inp, schedule32(16, 1.0, 2048.0), chunk)
+
+
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_bwd_bf16_several_chunks(chunk):
+    inp = I.chunk_inputs(1, 16, 300, 96, 192, "bf16", seed=80, a_std=0.1, s0_std=0.02,
+                         with_grad=True, dsf_std=0.02)
+    run_bwd_case(inp, schedule32(16, 1.0, 2048.0), chunk)
+
+
+def test_bf16_special_decays_and_short():
+    inp = I.chunk_inputs(1, 4, 37, 96, 192, "bf16", seed=90, a_std=0.2, s0_std=0.05,
+                         with_grad=True, dsf_std=0.05)
+    lam = np.array([0.0, 0.5, 0.9997, 1.0], np.float32)
+    run_fwd_case(inp, lam, 128)
+    run_bwd_case(inp, lam, 128)
+
+
+def test_bf16_narrow_dims():
+    inp = I.chunk_inputs(1, 2, 140, 32, 64, "bf16", seed=95, a_std=0.2, s0_std=0.05,
+                         with_grad=True, dsf_std=0.05)
+    lam = np.array([0.8, 0.99], np.float32)
+    run_fwd_case(inp, lam, 64)
+    run_bwd_case(inp, lam, 64)
+
+
+def test_varlen_bf16_fwd_bwd():
+    L = [1, 0, 257, 128, 5, 300]
+    cu = I.cu_from_lengths(L)
+    inp = I.chunk_inputs(1, 16, int(cu[-1]), 96, 192, "bf16", seed=100, a_std=0.1, s0_std=0.02,
+                         n_seq=len(L), with_grad=True, dsf_std=0.02)
+    lam = schedule32(16, 1.0, 2048.0)
+    run_fwd_case(inp, lam, 128, cu=cu)
+    run_bwd_case(inp, lam, 128, cu=cu)
+
+
+# ------------------------------------------------------------------ invariants
+
+
+def test_chunk_size_invariance_bf16():
+    """Chunk 64 and chunk 128 evaluate the same recurrence."""
+    inp = I.chunk_inputs(1, 16, 256, 96, 192, "bf16", seed=110, a_std=0.1)
+    d = device_inputs(inp)
+    lam = to_dev(schedule32(16, 1.0, 2048.0))
+    o64, _ = Bd.sgla_chunk_fwd(d["q"], d["k"], d["v"], lam, d["a"], chunk=64)
+    o128, _ = Bd.sgla_chunk_fwd(d["q"], d["k"], d["v"], lam, d["a"], chunk=128)
+    assert_close(to_host64(o64), to_host64(o128), TOL["bf16"], "chunk 64 vs 128")
+
+
+def test_state_carry_bf16():
+    """Running [0,T) at once == [0,t0) then [t0,T) from the carried state."""
+    T, t0 = 384, 200
+    inp = I.chunk_inputs(2, 16, T, 96, 192, "bf16", seed=120, a_std=0.1, s0_std=0.02)
+    d = device_inputs(inp)
+    lam = to_dev(schedule32(16, 1.0, 2048.0))
+    o, Sf = Bd.sgla_chunk_fwd(d["q"], d["k"], d["v"], lam, d["a"], init_state=d["S0"],
+                              want_final=True)
+    part = lambda x, sl: x[:, :, sl].contiguous()
+    o1, S1 = Bd.sgla_chunk_fwd(part(d["q"], slice(0, t0)), part(d["k"], slice(0, t0)),
+                               part(d["v"], slice(0, t0)), lam, d["a"], init_state=d["S0"],
+                               want_final=True)
+    o2, S2 = Bd.sgla_chunk_fwd(part(d["q"], slice(t0, T)), part(d["k"], slice(t0, T)),
+                               part(d["v"], slice(t0, T)), lam, d["a"], init_state=S1,
+                               final_state=S1)  # in-place carry
+    assert_close(to_host64(torch.cat([o1, o2], dim=2)), to_host64(o), TOL["bf16"], "split o")
+    assert_close(to_host64(S1), to_host64(Sf), TOL["bf16"], "split state")
+
+
+def test_deterministic_bitwise():
+    inp = I.chunk_inputs(2, 16, 300, 96, 192, "bf16", seed=130, a_std=0.1, s0_std=0.02,
+                         with_grad=True, dsf_std=0.02)
+    d = device_inputs(inp)
+    lam = to_dev(schedule32(16, 1.0, 2048.0))
+    r1 = Bd.sgla_chunk_fwd(d["q"], d["k"], d["v"], lam, d["a"], d["S0"], want_final=True)
+    r2 = Bd.sgla_chunk_fwd(d["q"], d["k"], d["v"], lam, d["a"], d["S0"], want_final=True)
+    g1 = Bd.sgla_chunk_bwd(d["q"], d["k"], d["v"], d["dO"], lam, d["a"], d["S0"], d["dSf"],
+                           want_d_init=True)
+    g2 = Bd.sgla_chunk_bwd(d["q"], d["k"], d["v"], d["dO"], lam, d["a"], d["S0"], d["dSf"],
+                           want_d_init=True)
+    for x, y in list(zip(r1, r2)) + list(zip(g1, g2)):
+        assert torch.equal(x, y)
+
+
+def test_nan_in_q_stays_in_its_row():
+    inp = I.chunk_inputs(1, 2, 200, 96, 192, "bf16", seed=140, a_std=0.1)
+    d = device_inputs(inp)
+    q = d["q"].clone()
+    q[0, 1, 77, 5] = float("nan")
+    lam = to_dev(np.array([0.5, 0.99], np.float32))
+    o, _ = Bd.sgla_chunk_fwd(q, d["k"], d["v"], lam, d["a"])
+    bad = torch.isnan(o.float())
+    assert bad[0, 1, 77].all(), "NaN must propagate to its own output row"
+    bad[0, 1, 77] = False
+    assert not bad.any(), "NaN leaked outside its row"

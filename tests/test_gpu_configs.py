@@ -1,0 +1,165 @@
+"""The benchmark workloads at their full sizes, in the launch configuration the
+bench times, checked against the oracle on sampled (sequence, head) units
+(every output of a sampled unit is compared) plus properties over all units.
+
+Workloads (H=16, d_k=96, d_v=192, bf16, decays from the 1..2048 schedule):
+  Laplace layer fwd:      B=8,  T=2048, chunk 128, a = 0 and a ~ N(0, 0.1)
+  Laplace layer fwd+bwd:  B=4,  T=2048, dO ~ N(0, 1); T=64 slice vs finite
+                          differences of the oracle
+  Decode:                 1280 sequences, state ~ N(0, 0.02), 64 steps
+  Packed varlen fwd:      32 sequences, lengths log-uniform in [128, 32768]
+                          (one of 32768), init states ~ N(0, 0.02)
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from chunked_gated_linear_simple_amd import binding as Bd
+from chunked_gated_linear_simple_amd import inputs as I
+from tests.parity_util import (TOL, assert_close, device_inputs, gpu_unit, oracle_bwd_units,
+                               oracle_fwd_units, schedule32, to_dev, to_host64)
+
+pytestmark = pytest.mark.gpu
+
+H, DK, DV = 16, 96, 192
+LAM = schedule32(H, 1.0, 2048.0)
+
+
+def _finite(t, what):
+    assert torch.isfinite(t.float()).all().item(), f"{what}: non-finite values"
+
+
+@pytest.mark.parametrize("a_std", [None, 0.1], ids=["a_zero", "a_normal"])
+def test_laplace_fwd_full(a_std):
+    inp = I.chunk_inputs(8, H, 2048, DK, DV, "bf16", seed=2, a_std=a_std)
+    d = device_inputs(inp)
+    o, Sf = Bd.sgla_chunk_fwd(d["q"], d["k"], d["v"], to_dev(LAM), d["a"], chunk=128,
+                              want_final=True)
+    torch.cuda.synchronize()
+    _finite(o, "o")
+    _finite(Sf, "final_state")
+    units = [(0, 0), (0, 15), (3, 7), (7, 0), (7, 15), (5, 11)]
+    ref = oracle_fwd_units(inp, LAM, units)
+    oh, Sh = to_host64(o), to_host64(Sf)
+    assert_close(np.concatenate([oh[u].ravel() for u in units]),
+                 np.concatenate([ref[u][0].ravel() for u in units]), TOL["bf16"], "o")
+    assert_close(np.concatenate([Sh[u].ravel() for u in units]),
+                 np.concatenate([ref[u][1].ravel() for u in units]), TOL["bf16"], "final_state")
+
+
+@pytest.mark.parametrize("a_std", [None, 0.1], ids=["a_zero", "a_normal"])
+def test_laplace_fwd_bwd_full(a_std):
+    inp = I.chunk_inputs(4, H, 2048, DK, DV, "bf16", seed=3, a_std=a_std, with_grad=True)
+    d = device_inputs(inp)
+    lam = to_dev(LAM)
+    o, _ = Bd.sgla_chunk_fwd(d["q"], d["k"], d["v"], lam, d["a"], chunk=128)
+    dq, dk, dv, da, _ = Bd.sgla_chunk_bwd(d["q"], d["k"], d["v"], d["dO"], lam, d["a"], chunk=128)
+    torch.cuda.synchronize()
+    for t, nm in ((o, "o"), (dq, "dq"), (dk, "dk"), (dv, "dv"), (da, "da")):
+        _finite(t, nm)
+    heads = (0, 9, 15)
+    units = [(b, h) for b in range(4) for h in heads]  # all b for these heads -> exact da
+    ref = oracle_bwd_units(inp, LAM, units)
+    for idx, (nm, t) in enumerate((("dq", dq), ("dk", dk), ("dv", dv))):
+        th = to_host64(t)
+        assert_close(np.concatenate([th[u].ravel() for u in units]),
+                     np.concatenate([ref[u][idx].ravel() for u in units]), TOL["bf16"], nm)
+    da_ref = np.stack([sum(ref[(b, h)][3] for b in range(4)) for h in heads])
+    dah = to_host64(da)[list(heads)]
+    if a_std is None:
+        assert np.count_nonzero(dah) == 0
+    else:
+        assert_close(dah, da_ref, TOL["bf16"], "da")
+    fref = oracle_fwd_units(inp, LAM, units)
+    oh = to_host64(o)
+    assert_close(np.concatenate([oh[u].ravel() for u in units]),
+                 np.concatenate([fref[u][0].ravel() for u in units]), TOL["bf16"], "o")
+
+
+def test_laplace_bwd_slice_finite_differences():
+    """GPU gradients on the T=64 slice (batch row 0, all heads) against central
+    finite differences of the fp64 oracle loss L = sum dO . o, on 128 sampled
+    coordinates of each of dq, dk, dv, da."""
+    full = I.chunk_inputs(4, H, 2048, DK, DV, "bf16", seed=3, a_std=0.1, with_grad=True)
+    sl = {k: (v[0:1, :, :64].copy() if isinstance(v, np.ndarray) and v.ndim == 4 else v)
+          for k, v in full.items()}
+    d = device_inputs(sl)
+    dq, dk, dv, da, _ = Bd.sgla_chunk_bwd(d["q"], d["k"], d["v"], d["dO"], to_dev(LAM), d["a"],
+                                          chunk=128)
+    torch.cuda.synchronize()
+    g = {"q": to_host64(dq)[0], "k": to_host64(dk)[0], "v": to_host64(dv)[0], "a": to_host64(da)}
+    X = {nm: I.widen(sl[nm][0], "bf16") for nm in ("q", "k", "v")}
+    dO = I.widen(sl["dO"][0], "bf16")
+    A = sl["a"].astype(np.float64)
+
+    def loss(h):
+        o, _ = oracle.fwd_unit(X["q"][h], X["k"][h], X["v"][h], float(LAM[h]), A[h], None)
+        return float(np.sum(dO[h] * o))
+
+    rng = np.random.default_rng(64)
+    for nm in ("q", "k", "v", "a"):
+        arr = A if nm == "a" else X[nm]
+        idxs = [tuple(int(rng.integers(0, s)) for s in arr.shape) for _ in range(128)]
+        fd, an = [], []
+        for idx in idxs:
+            h = idx[0]
+            keep = arr[idx]
+            step = 1e-4 * max(1.0, abs(keep))
+            arr[idx] = keep + step
+            lp = loss(h)
+            arr[idx] = keep - step
+            lm = loss(h)
+            arr[idx] = keep
+            fd.append((lp - lm) / (2 * step))
+            an.append(g[nm][idx])
+        assert_close(np.array(an), np.array(fd), TOL["bf16"], f"d{nm} vs finite differences")
+
+
+def test_decode_full_64_steps():
+    N, steps = 1280, 64
+    S0 = I.gaussian(4, I.STREAM_S0, (N, H, DK, DV), 0.02)
+    a = I.gaussian(4, I.STREAM_A, (H, DK), 0.1)
+    state = to_dev(S0)
+    units = [(0, 0), (0, 15), (640, 3), (1279, 15), (77, 8), (1001, 12)]
+    Sref = {u: S0[u].astype(np.float64).copy() for u in units}
+    del S0
+    lam_d, a_d = to_dev(LAM), to_dev(a)
+    for s in range(steps):
+        q, k, v = I.decode_token_inputs(4, s, N, H, DK, DV, "bf16")
+        o = Bd.sgla_decode_step(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), lam_d,
+                                a_d, state)
+        oh = to_host64(o)
+        assert np.isfinite(oh).all()
+        want = []
+        for (n, h) in units:
+            want.append(oracle.decode_step_unit(I.widen(q[n, h], "bf16"), I.widen(k[n, h], "bf16"),
+                                                I.widen(v[n, h], "bf16"), float(LAM[h]),
+                                                a[h].astype(np.float64), Sref[(n, h)]))
+        got = np.stack([oh[u] for u in units])
+        assert_close(got, np.stack(want), TOL["bf16"], f"o step {s}")
+    _finite(state, "state")
+    sh = torch.stack([state[n, h] for n, h in units]).double().cpu().numpy()
+    assert_close(sh, np.stack([Sref[u] for u in units]), TOL["bf16"], "final state")
+
+
+def test_varlen_full():
+    L = I.varlen_lengths(5)
+    cu = I.cu_from_lengths(L)
+    inp = I.chunk_inputs(1, H, int(cu[-1]), DK, DV, "bf16", seed=5, a_std=0.1, s0_std=0.02,
+                         n_seq=len(L))
+    d = device_inputs(inp, cu)
+    o, Sf = Bd.sgla_chunk_fwd(d["q"], d["k"], d["v"], to_dev(LAM), d["a"], init_state=d["S0"],
+                              cu_seqlens=d["cu"], chunk=128, want_final=True)
+    torch.cuda.synchronize()
+    _finite(o, "o")
+    _finite(Sf, "final_states")
+    longest = int(np.argmax(L))
+    shortest = int(np.argmin(L))
+    units = [(longest, 0), (longest, 15), (shortest, 0), (shortest, 15), (3, 8), (17, 12)]
+    ref = oracle_fwd_units(inp, LAM, units, cu)
+    oh, Sh = to_host64(o), to_host64(Sf)
+    assert_close(np.concatenate([gpu_unit(oh, n, h, cu).ravel() for n, h in units]),
+                 np.concatenate([ref[u][0].ravel() for u in units]), TOL["bf16"], "o")
+    assert_close(np.concatenate([Sh[u].ravel() for u in units]),
+                 np.concatenate([ref[u][1].ravel() for u in units]), TOL["bf16"], "final_states")
