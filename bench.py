@@ -1,0 +1,259 @@
+"""Benchmark of the Simple GLA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only fwd|fwdbwd|decode|varlen]
+                    [--no-cpu]
+
+Prints ONE JSON line. The headline ("value") is the Laplace-layer forward:
+B=8, H=16, T=2048, d_k=96, d_v=192, chunk 128, bf16 q/k/v (q scaled by
+d_k^-1/2), fp32 state, decays from the 1..2048 half-life schedule,
+a ~ N(0, 0.1), final state written. One step = one sgla_chunk_fwd call over
+that batch, inputs resident in HBM, rotating over 3 input sets (their 0.9 GB
+exceeds the 256 MB last-level cache, so each call streams from HBM).
+
+Also measured in the same run and reported under "secondary" (same clock):
+  fwdbwd: B=4 forward + backward (dO ~ N(0,1)), tokens/s = 8192 / (t_fwd + t_bwd)
+  decode: 1280 sequences x 16 heads, fp32 state ~ N(0, 0.02) (1.5 GB), 64
+          consecutive in-place steps, tokens/s = 1280 * 64 / t
+  varlen: 32 packed sequences, lengths log-uniform in [128, 32768] (one of
+          32768), init states ~ N(0, 0.02), tokens/s = sum T / t
+
+"roofline" is for the dominant kernel of the headline step (k_chunk_fwd):
+achieved = algorithmic HBM bytes per launch / mean launch time from HIP events
+on the launch stream. Algorithmic bytes per head-token: q 192 + k 192 + v 384
++ o 384 = 1152 B (bf16), plus the fp32 final state (73,728 B per sequence-head).
+"cpu_baseline" times the fp64 oracle (test infrastructure, untuned) on a
+bounded sample of the headline workload on the host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores
+H, DK, DV = 16, 96, 192
+HT_BYTES = 2 * DK + 2 * DK + 2 * DV + 2 * DV   # q, k, v, o per head-token (bf16)
+STATE_BYTES = DK * DV * 4
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", choices=["fwd", "fwdbwd", "decode", "varlen"], default=None)
+    ap.add_argument("--no-cpu", action="store_true")
+    return ap.parse_args()
+
+
+def gen(shape, seed, std=1.0, scale=1.0, dtype=None):
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(int(seed))
+    x = torch.randn(shape, generator=g, device="cuda", dtype=torch.float32)
+    x.mul_(std * scale)
+    return x if dtype is None else x.to(dtype)
+
+
+def timed(fn, steps, warmup):
+    """Mean milliseconds per call of fn(i), from HIP events on the current stream."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        fn(warmup + i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return sum(per) / len(per), wall * 1e3 / steps
+
+
+def bench_fwd(args, B=8, T=2048, nsets=3):
+    import torch
+    from chunked_gated_linear_simple_amd import binding as Bd
+    lam = Bd.sgla_decay_schedule(H, 1.0, 2048.0).cuda()
+    a = gen((H, DK), 21, 0.1)
+    sets = []
+    for s in range(nsets):
+        q = gen((B, H, T, DK), 100 + 10 * s, scale=DK ** -0.5, dtype=torch.bfloat16)
+        k = gen((B, H, T, DK), 101 + 10 * s, dtype=torch.bfloat16)
+        v = gen((B, H, T, DV), 102 + 10 * s, dtype=torch.bfloat16)
+        o = torch.empty((B, H, T, DV), dtype=torch.bfloat16, device="cuda")
+        sf = torch.empty((B, H, DK, DV), dtype=torch.float32, device="cuda")
+        sets.append((q, k, v, o, sf))
+
+    def step(i):
+        q, k, v, o, sf = sets[i % nsets]
+        Bd.sgla_chunk_fwd(q, k, v, lam, a, final_state=sf, o=o, chunk=128)
+
+    ms, wall_ms = timed(step, args.steps, args.warmup)
+    toks = B * T
+    bytes_ = B * H * T * HT_BYTES + B * H * STATE_BYTES
+    return {"ms": ms, "wall_ms": wall_ms, "tokens": toks, "tok_s": toks / (ms * 1e-3),
+            "bytes": bytes_, "gbs": bytes_ / (ms * 1e-3) / 1e9}
+
+
+def bench_fwdbwd(args, B=4, T=2048):
+    import torch
+    from chunked_gated_linear_simple_amd import binding as Bd
+    lam = Bd.sgla_decay_schedule(H, 1.0, 2048.0).cuda()
+    a = gen((H, DK), 31, 0.1)
+    q = gen((B, H, T, DK), 200, scale=DK ** -0.5, dtype=torch.bfloat16)
+    k = gen((B, H, T, DK), 201, dtype=torch.bfloat16)
+    v = gen((B, H, T, DV), 202, dtype=torch.bfloat16)
+    dO = gen((B, H, T, DV), 203, dtype=torch.bfloat16)
+    o = torch.empty_like(v)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    da = torch.empty((H, DK), dtype=torch.float32, device="cuda")
+    ws = torch.empty(Bd.sgla_chunk_bwd_workspace_bytes(B, H, DK), dtype=torch.uint8, device="cuda")
+    ms_f, _ = timed(lambda i: Bd.sgla_chunk_fwd(q, k, v, lam, a, o=o, chunk=128),
+                    args.steps, args.warmup)
+    ms_b, _ = timed(lambda i: Bd.sgla_chunk_bwd(q, k, v, dO, lam, a, chunk=128, dq=dq, dk=dk,
+                                                dv=dv, da=da, workspace=ws),
+                    args.steps, args.warmup)
+    toks = B * T
+    # algorithmic bytes, fwd: q,k,v,o (1152/ht); bwd: reads q,k,v,dO 1152 + writes dq,dk,dv 768
+    bytes_ = B * H * T * (1152 + 1920)
+    return {"ms_fwd": ms_f, "ms_bwd": ms_b, "tokens": toks,
+            "tok_s": toks / ((ms_f + ms_b) * 1e-3), "bytes": bytes_,
+            "gbs": bytes_ / ((ms_f + ms_b) * 1e-3) / 1e9}
+
+
+def bench_decode(args, N=1280, steps=64):
+    import torch
+    from chunked_gated_linear_simple_amd import binding as Bd
+    lam = Bd.sgla_decay_schedule(H, 1.0, 2048.0).cuda()
+    a = gen((H, DK), 41, 0.1)
+    state = gen((N, H, DK, DV), 400, 0.02)
+    qs = gen((steps, N, H, DK), 401, scale=DK ** -0.5, dtype=torch.bfloat16)
+    ks = gen((steps, N, H, DK), 402, dtype=torch.bfloat16)
+    vs = gen((steps, N, H, DV), 403, dtype=torch.bfloat16)
+    o = torch.empty((N, H, DV), dtype=torch.bfloat16, device="cuda")
+
+    def run64(_):
+        for s in range(steps):
+            Bd.sgla_decode_step(qs[s], ks[s], vs[s], lam, a, state, o=o)
+
+    reps = max(2, args.steps // 4)
+    ms, _ = timed(run64, reps, 1)
+    toks = N * steps
+    bytes_step = N * H * (2 * STATE_BYTES + 2 * DK + 2 * DK + 2 * DV + 2 * DV)
+    return {"ms_64_steps": ms, "us_per_step": ms * 1e3 / steps, "tokens": toks,
+            "tok_s": toks / (ms * 1e-3), "bytes_per_step": bytes_step,
+            "gbs": bytes_step * steps / (ms * 1e-3) / 1e9}
+
+
+def bench_varlen(args):
+    import numpy as np
+    import torch
+    from chunked_gated_linear_simple_amd import binding as Bd
+    from chunked_gated_linear_simple_amd import inputs as I
+    L = I.varlen_lengths(5)
+    cu = torch.from_numpy(I.cu_from_lengths(L)).cuda()
+    Ttot = int(cu[-1].item())
+    lam = Bd.sgla_decay_schedule(H, 1.0, 2048.0).cuda()
+    a = gen((H, DK), 51, 0.1)
+    q = gen((1, H, Ttot, DK), 500, scale=DK ** -0.5, dtype=torch.bfloat16)
+    k = gen((1, H, Ttot, DK), 501, dtype=torch.bfloat16)
+    v = gen((1, H, Ttot, DV), 502, dtype=torch.bfloat16)
+    s0 = gen((len(L), H, DK, DV), 503, 0.02)
+    sf = torch.empty_like(s0)
+    o = torch.empty_like(v)
+    ms, _ = timed(lambda i: Bd.sgla_chunk_fwd(q, k, v, lam, a, init_state=s0, final_state=sf,
+                                              o=o, cu_seqlens=cu, chunk=128),
+                  max(3, args.steps // 2), 2)
+    bytes_ = H * Ttot * HT_BYTES + 2 * len(L) * H * STATE_BYTES
+    return {"ms": ms, "tokens": Ttot, "tok_s": Ttot / (ms * 1e-3), "bytes": bytes_,
+            "gbs": bytes_ / (ms * 1e-3) / 1e9, "n_seq": int(len(L)), "max_len": int(np.max(L))}
+
+
+def cpu_baseline(units=32, T=2048):
+    """The fp64 oracle on a bounded sample of the headline workload: `units`
+    (sequence, head) pairs of T tokens, one thread per unit, all host cores."""
+    import numpy as np
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    from chunked_gated_linear_simple_amd import inputs as I
+    if not os.path.exists(os.path.join(ROOT, "oracle", "liboracle.so")):
+        oracle.build(force=True)
+    cores = min(os.cpu_count() or 1, 16)
+    lam = oracle.decay_schedule(H, 1.0, 2048.0)
+    inp = I.chunk_inputs(2, H, T, DK, DV, "bf16", seed=2, a_std=0.1)
+    work = [(n, h) for n in range(2) for h in range(H)][:units]
+    args = [(I.widen(inp["q"][n, h], "bf16"), I.widen(inp["k"][n, h], "bf16"),
+             I.widen(inp["v"][n, h], "bf16"), float(lam[h]), inp["a"][h].astype(np.float64))
+            for n, h in work]
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(cores) as ex:
+        list(ex.map(lambda x: oracle.fwd_unit(*x), args))
+    dt = time.perf_counter() - t0
+    head_tokens = len(work) * T
+    return {"value": (head_tokens / H) / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(work)} (sequence, head) units x {T} tokens of the headline "
+                      f"workload ({head_tokens} head-tokens = {head_tokens // H} tokens at "
+                      f"16 heads), fp64 token recurrence, {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    from chunked_gated_linear_simple_amd import binding as Bd
+    Bd.lib()  # fail loudly if the library is not built
+
+    secondary = {}
+    only = args.only
+    fwd = bench_fwd(args) if only in (None, "fwd") else None
+    if only in (None, "fwdbwd"):
+        secondary["fwdbwd_B4"] = bench_fwdbwd(args)
+    if only in (None, "decode"):
+        secondary["decode_N1280_64steps"] = bench_decode(args)
+    if only in (None, "varlen"):
+        secondary["varlen_32seq"] = bench_varlen(args)
+    for r in secondary.values():
+        r["hbm_frac_algorithmic"] = r["gbs"] / HBM_PEAK_GBS
+
+    line = {"metric": "GLA tokens/s (fwd, fwd+bwd, decode) at H=16 dk=96 dv=192; % MFMA/HBM peak",
+            "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "warmup": args.warmup, "steps": args.steps}
+    if fwd is not None:
+        line.update({
+            "value": fwd["tok_s"], "ms_per_step": fwd["ms"],
+            "config": {"workload": "Laplace layer fwd B=8 H=16 T=2048 dk=96 dv=192 chunk=128 "
+                                   "bf16, fp32 state, final state written",
+                       "batch": 8, "seq_len": 2048, "heads": H, "d_k": DK, "d_v": DV,
+                       "chunk": 128},
+            "roofline": {"bound": "hbm", "kernel": "k_chunk_fwd", "achieved": fwd["gbs"],
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": fwd["gbs"] / HBM_PEAK_GBS,
+                         "traffic": None, "bytes_per_launch": fwd["bytes"]},
+        })
+    else:
+        first = next(iter(secondary.values()))
+        line.update({"value": first["tok_s"], "config": {"workload": next(iter(secondary))}})
+    line["secondary"] = secondary
+    if not args.no_cpu and fwd is not None:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -16,19 +16,27 @@
 //   dq: forward order,  q'=dO, k'=v, v'=k, state S^T, + sigmoid'(z)(dO.v)(a*k)
 //   dk: reversed order, q'=v, k'=dO, v'=q, state G^T, + sigmoid'(z)(dO.v)(a*q)
 //   dv: reversed order, q'=k, k'=q, v'=dO, state G,   + sigmoid(z) dO
-// (G_t = dL/dS_t = sum_{i>=t} lam^(i-t) q_i dO_i^T + lam^(T-1-t) dS_final.)
+// (G_t = dL/dS_t = sum_{i>=t} lam^(i-t) q_i dO_i^T + lam^(T-1-t) dS_final: in
+// reversed order the carried-in dS_final enters the first token undecayed.)
 //
 // Work decomposition: one workgroup of 4 waves per (sequence, head, value
 // slice); the state slice stays in MFMA accumulators for the whole scan over
 // chunks. Per chunk the operands are staged in LDS:
-//   Qs, Ks   [C][DK]  natural (rows = tokens)       -- scores, Q'S
-//   KTs      [DK][C]  k' transposed, scaled by lam^(C_c-1-j)  -- state update
-//   VTs      [DVS][C] v' transposed                 -- P.V', state update, aug
-//   STs      [DVS][DK] state^T in the operand dtype  -- Q'S
+//   Qs, Ks   [C][DK]   natural (rows = tokens)      -- scores, Q'S, (q'.k')
+//   KTs      [DK][C]   k' transposed, unscaled      -- state update
+//   VTs      [DVS][C]  v' slice transposed          -- P.V', state update, epilogue
+//   STh, STl [DVS][DK] state^T as a bf16 hi + lo pair -- Q'S
+//   ksc      [C]       lam^(C_c-1-j), the key decays of the state update
 // Waves 0..C/32-1 each own 32 query rows: they compute Q'S, the decay-masked
 // score tiles K' Q'^T (kept in registers and fed straight back as the A
-// operand of P.V'), the epilogue, and store. Every wave then advances its
-// share of the state tiles with K~^T V' on the matrix cores.
+// operand of P.V'), the epilogue, and store. The state tiles are spread over
+// the waves by a compile-time balance of the per-chunk matrix-core work.
+//
+// Precision (bf16 operands, fp32 accumulation): the two operands that carry
+// the long-memory state -- the state itself in Q'S and the decayed keys
+// lam^m k' of the state update -- are split into bf16 hi + lo pairs and fed
+// as two MFMAs, so they keep ~16 significant bits; only the per-chunk decayed
+// scores P enter the matrix cores rounded once to bf16.
 //
 // MFMA: v_mfma_f32_32x32x16_bf16 (bf16) or v_mfma_f32_32x32x2_f32 (fp32).
 // For a 32x32 result, lane l holds column l%32 and rows 8*(i/4)+4*(l/32)+i%4
@@ -50,8 +58,10 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef u16 u16x8_t __attribute__((ext_vector_type(8)));
 typedef u16 u16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int NTHREADS = 256;
+constexpr int NWAVES = 4;
 
 __device__ __forceinline__ float to_f(u16 x) { return __uint_as_float((uint32_t)x << 16); }
 __device__ __forceinline__ float to_f(float x) { return x; }
@@ -81,6 +91,7 @@ template <typename E> struct Mfma;
 template <> struct Mfma<u16> {
     static constexpr int KSTEP = 16;  // contraction per instruction
     static constexpr int NE = 8;      // operand elements per lane
+    static constexpr int HILO = 2;    // instructions per split operand
     typedef bf16x8_t op_t;
     static __device__ __forceinline__ op_t load(const u16* p)
     {
@@ -94,6 +105,7 @@ template <> struct Mfma<u16> {
 template <> struct Mfma<float> {
     static constexpr int KSTEP = 2;
     static constexpr int NE = 1;
+    static constexpr int HILO = 1;
     typedef float op_t;
     static __device__ __forceinline__ op_t load(const float* p) { return *p; }
     static __device__ __forceinline__ f32x16_t mma(op_t a, op_t b, f32x16_t c)
@@ -107,6 +119,32 @@ __device__ __forceinline__ int acc_row(int i, int g) { return 8 * (i >> 2) + 4 *
 
 enum { AUG_FWD = 0, AUG_GRAD = 1 };
 
+// Static assignment of state tiles to waves: greedy on the per-chunk
+// matrix-core instruction count (query-strip work first, then tiles).
+struct Owners {
+    int count[NWAVES];
+    int list[NWAVES][32];
+    int max_count;
+};
+
+constexpr Owners balance(int nstrip, int strip_base, int per_block, int tile_cost, int ntiles)
+{
+    Owners o{};
+    long load[NWAVES] = {0, 0, 0, 0};
+    for (int w = 0; w < NWAVES; ++w) load[w] = (w < nstrip) ? strip_base + (w + 1) * per_block : 0;
+    for (int t = 0; t < ntiles; ++t) {
+        int best = 0;
+        for (int w = 1; w < NWAVES; ++w)
+            if (load[w] < load[best]) best = w;
+        o.list[best][o.count[best]++] = t;
+        load[best] += tile_cost;
+    }
+    o.max_count = 0;
+    for (int w = 0; w < NWAVES; ++w)
+        if (o.count[w] > o.max_count) o.max_count = o.count[w];
+    return o;
+}
+
 // Compile-time description of one role.
 //   DK:  padded width of q'/k' rows (= state rows), multiple of 32
 //   DVS: padded width of the value slice a workgroup owns, multiple of 32
@@ -114,32 +152,55 @@ enum { AUG_FWD = 0, AUG_GRAD = 1 };
 template <typename E_, int DK_, int DVS_, int C_, int AUG_, bool REV_>
 struct Role {
     typedef E_ E;
+    typedef Mfma<E> M;
     static constexpr int DK = DK_, DVS = DVS_, C = C_, AUG = AUG_;
     static constexpr bool REV = REV_;
+    static constexpr int HILO = M::HILO;
     static constexpr int PE = 16 / (int)sizeof(E);  // 16-byte row padding
-    static constexpr int LDQ = DK + PE;             // Qs, Ks, STs row stride
+    static constexpr int LDQ = DK + PE;             // Qs, Ks, STh, STl row stride
     static constexpr int LDT = C + PE;              // KTs, VTs, XTs row stride
     static constexpr int NSTRIP = C / 32;
     static constexpr int NNT = DVS / 32;
     static constexpr int NDB = DK / 32;
     static constexpr int NTILES = NDB * NNT;
-    static constexpr int NTW = (NTILES + 3) / 4;
+    static constexpr Owners OWN =
+        balance(NSTRIP, (DK / M::KSTEP) * NNT * HILO, DK / M::KSTEP + NNT * (32 / M::KSTEP),
+                (C / M::KSTEP) * HILO, NTILES);
+    static constexpr int NTW = OWN.max_count;
+    static constexpr size_t SZ_ROWS = (size_t)C * LDQ * sizeof(E);
+    static constexpr size_t SZ_ST = (size_t)DVS * LDQ * sizeof(E);
     static constexpr size_t OFF_Q = 0;
-    static constexpr size_t OFF_K = OFF_Q + (size_t)C * LDQ * sizeof(E);
-    static constexpr size_t OFF_KT = OFF_K + (size_t)C * LDQ * sizeof(E);
+    static constexpr size_t OFF_K = OFF_Q + SZ_ROWS;
+    static constexpr size_t OFF_KT = OFF_K + SZ_ROWS;
     static constexpr size_t OFF_VT = OFF_KT + (size_t)DK * LDT * sizeof(E);
-    static constexpr size_t OFF_ST = OFF_VT + (size_t)DVS * LDT * sizeof(E);
-    static constexpr size_t OFF_XT = OFF_ST + (size_t)DVS * LDQ * sizeof(E);
+    static constexpr size_t OFF_STH = OFF_VT + (size_t)DVS * LDT * sizeof(E);
+    static constexpr size_t OFF_STL = OFF_STH + SZ_ST;
+    static constexpr size_t OFF_XT = OFF_STL + (HILO == 2 ? SZ_ST : 0);
     static constexpr size_t OFF_COEF = OFF_XT + (AUG == AUG_GRAD ? (size_t)DVS * LDT * sizeof(E) : 0);
-    static constexpr size_t OFF_DA = OFF_COEF + (size_t)C * sizeof(float);
+    static constexpr size_t OFF_KSC = OFF_COEF + (size_t)C * sizeof(float);
+    static constexpr size_t OFF_DA = OFF_KSC + (size_t)C * sizeof(float);
     static constexpr size_t LDS = OFF_DA + (AUG == AUG_GRAD ? (size_t)NSTRIP * DVS * sizeof(float) : 0);
     static_assert(DK % 32 == 0 && DVS % 32 == 0 && C % 32 == 0 && C <= 128, "tile shape");
     static_assert(LDS <= 160 * 1024, "LDS budget");
+    static_assert(NTILES <= 32, "owner table");
 };
+
+// State tile handled by a wave's kk-th accumulator (or -1).
+template <class R>
+__device__ __forceinline__ int tile_of(int wave, int kk)
+{
+    constexpr Owners o = R::OWN;
+    switch (wave) {
+    case 0: return kk < o.count[0] ? o.list[0][kk] : -1;
+    case 1: return kk < o.count[1] ? o.list[1][kk] : -1;
+    case 2: return kk < o.count[2] ? o.list[2][kk] : -1;
+    default: return kk < o.count[3] ? o.list[3][kk] : -1;
+    }
+}
 
 struct Common {
     const float* lambda;
-    const float* a;      // [H, a_len] or NULL
+    const float* a;      // [H, d_k] or NULL
     const int32_t* cu;   // NULL when dense
     int H, T, n_units;
 };
@@ -156,6 +217,7 @@ struct RoleArgs {
     int dkr, dvr;         // real widths (<= DK, <= DVS * slices)
     int state_t;          // state stored [dvr][dkr] instead of [dkr][dvr]
     int final_times_lam;  // final state scaled by lam (non-empty sequences)
+    int init_undecayed;   // the initial state enters the first token undecayed
 };
 
 template <class R>
@@ -163,19 +225,22 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
                                           int slice, char* smem)
 {
     typedef typename R::E E;
-    typedef Mfma<E> M;
+    typedef typename R::M M;
     constexpr int C = R::C, DK = R::DK, DVS = R::DVS, LDQ = R::LDQ, LDT = R::LDT;
-    constexpr int NSTRIP = R::NSTRIP, NNT = R::NNT, NTILES = R::NTILES, NTW = R::NTW;
+    constexpr int NSTRIP = R::NSTRIP, NNT = R::NNT, NTW = R::NTW;
     constexpr int KSTEP = M::KSTEP, NE = M::NE;
+    constexpr bool SPLIT = (R::HILO == 2);
     constexpr int V16 = 16 / (int)sizeof(E);  // elements per 16-byte segment
 
     E* Qs = reinterpret_cast<E*>(smem + R::OFF_Q);
     E* Ks = reinterpret_cast<E*>(smem + R::OFF_K);
     E* KTs = reinterpret_cast<E*>(smem + R::OFF_KT);
     E* VTs = reinterpret_cast<E*>(smem + R::OFF_VT);
-    E* STs = reinterpret_cast<E*>(smem + R::OFF_ST);
+    E* STh = reinterpret_cast<E*>(smem + R::OFF_STH);
+    E* STl = reinterpret_cast<E*>(smem + R::OFF_STL);
     E* XTs = reinterpret_cast<E*>(smem + R::OFF_XT);
     float* coef = reinterpret_cast<float*>(smem + R::OFF_COEF);
+    float* ksc = reinterpret_cast<float*>(smem + R::OFF_KSC);
     float* dared = reinterpret_cast<float*>(smem + R::OFF_DA);
 
     const int tid = threadIdx.x;
@@ -208,14 +273,16 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
     const E* gx = reinterpret_cast<const E*>(ra.xp);
     E* go = reinterpret_cast<E*>(ra.op);
 
-    // ---- state slice in accumulators: tile tau = db*NNT + nb, owned by wave tau%4
+    // ---- state slice in accumulators: tile tau = db*NNT + nb
+    int tiles[NTW];
     f32x16_t sacc[NTW];
 #pragma unroll
     for (int kk = 0; kk < NTW; ++kk) {
-        const int tau = wave + 4 * kk;
+        const int tau = tile_of<R>(wave, kk);
+        tiles[kk] = tau;
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[kk][i] = 0.0f;
-        if (tau < NTILES && ra.s_init != nullptr) {
+        if (tau >= 0 && ra.s_init != nullptr) {
             const int db = tau / NNT, nb = tau - (tau / NNT) * NNT;
             const int nn = n0 + 32 * nb + l32;
 #pragma unroll
@@ -232,33 +299,47 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
 #pragma unroll
     for (int nt = 0; nt < NNT; ++nt) da_acc[nt] = 0.0f;
 
-    // lam^(t+1) for the strip rows this lane holds
-    float lq[16];
+    // lam^(t+1) for the strip rows this lane holds; lam^t where the carried
+    // state is not decayed before the first token (reverse scans)
+    float lq[16], lq0[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) lq[i] = decay_pow(32 * wave + acc_row(i, g) + 1, l2);
+    for (int i = 0; i < 16; ++i) {
+        lq[i] = decay_pow(32 * wave + acc_row(i, g) + 1, l2);
+        lq0[i] = decay_pow(32 * wave + acc_row(i, g), l2);
+    }
 
     const int nchunks = (len + C - 1) / C;
     for (int ci = 0; ci < nchunks; ++ci) {
         const int c = R::REV ? (nchunks - 1 - ci) : ci;
         const int cstart = c * C;
         const int clen = min(C, len - cstart);
+        const bool shift = ra.init_undecayed && ci == 0;
 
         __syncthreads();  // previous chunk's LDS readers are done
 
-        // state before this chunk -> STs (operand dtype), transposed
+        // state before this chunk -> STh (+ STl), transposed
 #pragma unroll
         for (int kk = 0; kk < NTW; ++kk) {
-            const int tau = wave + 4 * kk;
-            if (tau < NTILES) {
+            const int tau = tiles[kk];
+            if (tau >= 0) {
                 const int db = tau / NNT, nb = tau - (tau / NNT) * NNT;
                 const int nl = 32 * nb + l32;
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    STs[nl * LDQ + 32 * db + acc_row(i, g)] = from_f<E>(sacc[kk][i]);
+                for (int i = 0; i < 16; ++i) {
+                    const int off = nl * LDQ + 32 * db + acc_row(i, g);
+                    const E hi = from_f<E>(sacc[kk][i]);
+                    STh[off] = hi;
+                    if (SPLIT) STl[off] = from_f<E>(sacc[kk][i] - to_f(hi));
+                }
             }
         }
+        // key decays of the state update
+        for (int r = tid; r < C; r += NTHREADS) {
+            const int m = clen - 1 - r - (shift ? 1 : 0);
+            ksc[r] = (r < clen) ? (m < 0 ? 0.0f : decay_pow(m, l2)) : 0.0f;
+        }
 
-        // q', k' rows (natural) and k' scaled + transposed
+        // q', k' rows (natural) and k' transposed
         constexpr int SEGQ = DK / V16;
         for (int idx = tid; idx < C * SEGQ; idx += NTHREADS) {
             const int r = idx / SEGQ, col = (idx - (idx / SEGQ) * SEGQ) * V16;
@@ -271,10 +352,9 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
             }
             *reinterpret_cast<uint4*>(Qs + r * LDQ + col) = qv;
             *reinterpret_cast<uint4*>(Ks + r * LDQ + col) = kv;
-            const float sk = (r < clen) ? decay_pow(clen - 1 - r, l2) : 0.0f;
             const E* ke = reinterpret_cast<const E*>(&kv);
 #pragma unroll
-            for (int e = 0; e < V16; ++e) KTs[(col + e) * LDT + r] = from_f<E>(sk * to_f(ke[e]));
+            for (int e = 0; e < V16; ++e) KTs[(col + e) * LDT + r] = ke[e];
         }
         // v' slice (and the gate's second operand) transposed
         constexpr int SEGV = DVS / V16;
@@ -301,17 +381,23 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
         // per-token epilogue coefficient (two threads per token)
         if (tid < 2 * C) {
             const int r = tid >> 1, half = tid & 1;
-            const float* ah = (cm.a != nullptr) ? cm.a + (size_t)h * (R::AUG == AUG_FWD ? dkr : dvr)
-                                                : nullptr;
             float z = 0.0f, u = 0.0f;
             if (R::AUG == AUG_FWD) {
-                if (ah != nullptr)
+                if (cm.a != nullptr) {
+                    const float* ah = cm.a + (size_t)h * dkr;
                     for (int d = half; d < dkr; d += 2)
                         z += ah[d] * to_f(Qs[r * LDQ + d]) * to_f(Ks[r * LDQ + d]);
+                }
             } else {
-                if (ah != nullptr)
-                    for (int nn = half; nn < dvr; nn += 2)
-                        z += ah[nn] * to_f(VTs[nn * LDT + r]) * to_f(XTs[nn * LDT + r]);
+                // z = sum_n a_n v'_n x_n over the full width (read from memory:
+                // this workgroup holds only a slice of v' and x)
+                if (cm.a != nullptr && r < clen) {
+                    const float* ah = cm.a + (size_t)h * dvr;
+                    const int tok = R::REV ? (cstart + clen - 1 - r) : (cstart + r);
+                    const E* vr = gv + (size_t)(row0 + tok) * dvr;
+                    const E* xr = gx + (size_t)(row0 + tok) * dvr;
+                    for (int nn = half; nn < dvr; nn += 2) z += ah[nn] * to_f(vr[nn]) * to_f(xr[nn]);
+                }
                 for (int d = half; d < dkr; d += 2) u += to_f(Qs[r * LDQ + d]) * to_f(Ks[r * LDQ + d]);
             }
             z += __shfl_xor(z, 1);
@@ -324,7 +410,7 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
         __syncthreads();
 
         // ---- query strips
-        if (wave < NSTRIP) {
+        if (wave < NSTRIP && 32 * wave < clen) {
             const int t0 = 32 * wave;
             f32x16_t oacc[NNT];
 #pragma unroll
@@ -332,24 +418,24 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
 #pragma unroll
                 for (int i = 0; i < 16; ++i) oacc[nt][i] = 0.0f;
 
-            // inter-chunk: Q' S_in
+            // inter-chunk: Q' (S_hi + S_lo)
 #pragma unroll 2
             for (int kb = 0; kb < DK / KSTEP; ++kb) {
                 const typename M::op_t av = M::load(Qs + (t0 + l32) * LDQ + kb * KSTEP + g * NE);
 #pragma unroll
                 for (int nt = 0; nt < NNT; ++nt) {
-                    const typename M::op_t bv = M::load(STs + (32 * nt + l32) * LDQ + kb * KSTEP + g * NE);
-                    oacc[nt] = M::mma(av, bv, oacc[nt]);
+                    const int boff = (32 * nt + l32) * LDQ + kb * KSTEP + g * NE;
+                    oacc[nt] = M::mma(av, M::load(STh + boff), oacc[nt]);
+                    if (SPLIT) oacc[nt] = M::mma(av, M::load(STl + boff), oacc[nt]);
                 }
             }
 #pragma unroll
             for (int nt = 0; nt < NNT; ++nt)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) oacc[nt][i] *= lq[i];
+                for (int i = 0; i < 16; ++i) oacc[nt][i] *= shift ? lq0[i] : lq[i];
 
             // intra-chunk: decay-masked scores, then P V'
             for (int jb = 0; jb <= wave; ++jb) {
-                if (32 * jb >= clen) break;
                 f32x16_t sc;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) sc[i] = 0.0f;
@@ -425,20 +511,37 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
             }
         }
 
-        // ---- state advance: S = lam^(C_c) S + K~^T V'
-        const float fc = decay_pow(clen, l2);
+        // ---- state advance: S = lam^(C_c) S + (lam^m k')^T V', decayed keys as hi + lo
+        const float fc = decay_pow(clen - (shift ? 1 : 0), l2);
 #pragma unroll
         for (int kk = 0; kk < NTW; ++kk) {
-            const int tau = wave + 4 * kk;
-            if (tau < NTILES) {
+            const int tau = tiles[kk];
+            if (tau >= 0) {
                 const int db = tau / NNT, nb = tau - (tau / NNT) * NNT;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) sacc[kk][i] *= fc;
 #pragma unroll 2
                 for (int kb = 0; kb < C / KSTEP; ++kb) {
-                    const typename M::op_t av = M::load(KTs + (32 * db + l32) * LDT + kb * KSTEP + g * NE);
-                    const typename M::op_t bv = M::load(VTs + (32 * nb + l32) * LDT + kb * KSTEP + g * NE);
-                    sacc[kk] = M::mma(av, bv, sacc[kk]);
+                    const int j0 = kb * KSTEP + g * NE;
+                    const typename M::op_t bv = M::load(VTs + (32 * nb + l32) * LDT + j0);
+                    const E* kr = KTs + (32 * db + l32) * LDT + j0;
+                    if constexpr (sizeof(E) == 2) {
+                        const u16x8_t kw = *reinterpret_cast<const u16x8_t*>(kr);
+                        const f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(ksc + j0);
+                        const f32x4_t s1 = *reinterpret_cast<const f32x4_t*>(ksc + j0 + 4);
+                        u16x8_t hw, lw;
+#pragma unroll
+                        for (int s = 0; s < 8; ++s) {
+                            const float x = to_f((u16)kw[s]) * (s < 4 ? s0[s] : s1[s - 4]);
+                            const u16 hb = from_f<u16>(x);
+                            hw[s] = hb;
+                            lw[s] = from_f<u16>(x - to_f(hb));
+                        }
+                        sacc[kk] = M::mma(__builtin_bit_cast(bf16x8_t, hw), bv, sacc[kk]);
+                        sacc[kk] = M::mma(__builtin_bit_cast(bf16x8_t, lw), bv, sacc[kk]);
+                    } else {
+                        sacc[kk] = M::mma(to_f(*kr) * ksc[j0], bv, sacc[kk]);
+                    }
                 }
             }
         }
@@ -449,8 +552,8 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
         const float fs = (ra.final_times_lam && len > 0) ? lam : 1.0f;
 #pragma unroll
         for (int kk = 0; kk < NTW; ++kk) {
-            const int tau = wave + 4 * kk;
-            if (tau < NTILES) {
+            const int tau = tiles[kk];
+            if (tau >= 0) {
                 const int db = tau / NNT, nb = tau - (tau / NNT) * NNT;
                 const int nn = n0 + 32 * nb + l32;
 #pragma unroll
@@ -466,7 +569,7 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
         }
     }
 
-    // ---- partial da of this (sequence, head): fixed-order reduction
+    // ---- partial da of this (sequence, head, slice): fixed-order reduction
     if (R::AUG == AUG_GRAD && ra.da_part != nullptr) {
         __syncthreads();
         if (wave < NSTRIP) {
@@ -508,16 +611,18 @@ __global__ __launch_bounds__(NTHREADS) void k_chunk_fwd(Common cm, RoleArgs ra, 
 
 constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 
+// One launch runs the three backward scans: slices [0, nslq) are dq,
+// [nslq, 2 nslq) dk, and the rest dv.
 template <class RQ, class RK, class RV>
 __global__ __launch_bounds__(NTHREADS) void k_chunk_bwd(Common cm, RoleArgs aq, RoleArgs ak,
-                                                        RoleArgs av, int nslv)
+                                                        RoleArgs av, int nslq, int nslv)
 {
     __shared__ __attribute__((aligned(16))) char smem[cmax(RQ::LDS, cmax(RK::LDS, RV::LDS))];
     int unit, vs;
-    if (!map_block(2 + nslv, cm.n_units, unit, vs)) return;
-    if (vs == 0) role_body<RQ>(cm, aq, unit, 0, smem);
-    else if (vs == 1) role_body<RK>(cm, ak, unit, 0, smem);
-    else role_body<RV>(cm, av, unit, vs - 2, smem);
+    if (!map_block(2 * nslq + nslv, cm.n_units, unit, vs)) return;
+    if (vs < nslq) role_body<RQ>(cm, aq, unit, vs, smem);
+    else if (vs < 2 * nslq) role_body<RK>(cm, ak, unit, vs - nslq, smem);
+    else role_body<RV>(cm, av, unit, vs - 2 * nslq, smem);
 }
 
 // da[h][d] = sum over sequences n (in order) of da_part[n*H + h][d]
@@ -529,12 +634,6 @@ __global__ void k_da_reduce(const float* da_part, float* da, int n_seq, int H, i
     float s = 0.0f;
     for (int n = 0; n < n_seq; ++n) s += da_part[((size_t)n * H + h) * dkr + d];
     da[i] = s;
-}
-
-__global__ void k_fill_zero(float* p, int n)
-{
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = 0.0f;
 }
 
 int round8(int x) { return (x + 7) / 8 * 8; }
@@ -550,29 +649,28 @@ hipError_t run_fwd(const ChunkProblem& p, const RoleArgs& ra, int nsl, hipStream
 
 template <class RQ, class RK, class RV>
 hipError_t run_bwd(const ChunkProblem& p, const RoleArgs& aq, const RoleArgs& ak,
-                   const RoleArgs& av, int nslv, float* da, hipStream_t stream)
+                   const RoleArgs& av, float* da, hipStream_t stream)
 {
+    static_assert(RQ::DVS == RK::DVS, "dq and dk slices");
     Common cm{p.lambda, p.a, p.cu, p.H, p.T, p.n_seq * p.H};
-    const int grid = round8(cm.n_units) * (2 + nslv);
+    const int nslq = (p.d_k + RQ::DVS - 1) / RQ::DVS;
+    const int nslv = (p.d_v + RV::DVS - 1) / RV::DVS;
+    const int grid = round8(cm.n_units) * (2 * nslq + nslv);
     hipLaunchKernelGGL((k_chunk_bwd<RQ, RK, RV>), dim3(grid), dim3(NTHREADS), 0, stream, cm, aq, ak,
-                       av, nslv);
+                       av, nslq, nslv);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nda = p.H * p.d_k;
-    if (p.a != nullptr) {
-        hipLaunchKernelGGL(k_da_reduce, dim3((nda + 255) / 256), dim3(256), 0, stream, aq.da_part, da,
-                           p.n_seq, p.H, p.d_k);
-    } else {
-        hipLaunchKernelGGL(k_fill_zero, dim3((nda + 255) / 256), dim3(256), 0, stream, da, nda);
-    }
+    hipLaunchKernelGGL(k_da_reduce, dim3((nda + 255) / 256), dim3(256), 0, stream, aq.da_part, da,
+                       p.n_seq, p.H, p.d_k);
     return hipGetLastError();
 }
 
 // Role instantiations
 typedef Role<u16, 96, 96, 128, AUG_FWD, false> BfFwd128;
 typedef Role<u16, 96, 96, 64, AUG_FWD, false> BfFwd64;
-typedef Role<u16, 192, 96, 64, AUG_GRAD, false> BfDq;
-typedef Role<u16, 192, 96, 64, AUG_GRAD, true> BfDk;
+typedef Role<u16, 192, 32, 64, AUG_GRAD, false> BfDq;
+typedef Role<u16, 192, 32, 64, AUG_GRAD, true> BfDk;
 typedef Role<u16, 96, 96, 128, AUG_FWD, true> BfDv128;
 typedef Role<u16, 96, 96, 64, AUG_FWD, true> BfDv64;
 typedef Role<float, 32, 32, 64, AUG_FWD, false> F32Fwd;
@@ -586,7 +684,7 @@ hipError_t launch_chunk_fwd(const ChunkProblem& p, const void* q, const void* k,
                             const float* init_state, float* final_state, void* o,
                             hipStream_t stream)
 {
-    RoleArgs ra{q, k, v, nullptr, o, init_state, final_state, nullptr, p.d_k, p.d_v, 0, 0};
+    RoleArgs ra{q, k, v, nullptr, o, init_state, final_state, nullptr, p.d_k, p.d_v, 0, 0, 0};
     if (p.bf16) {
         const int nsl = (p.d_v + 95) / 96;
         if (p.chunk == 128) return run_fwd<BfFwd128>(p, ra, nsl, stream);
@@ -601,18 +699,16 @@ hipError_t launch_chunk_bwd(const ChunkProblem& p, const void* q, const void* k,
                             float* da_partial, hipStream_t stream)
 {
     // dq: forward scan of S^T ([d_v][d_k]); q'=dO, k'=v, v'=k, gate operand q
-    RoleArgs aq{dO, v, k, q, dq, init_state, nullptr,
-                p.a != nullptr ? da_partial : nullptr, p.d_v, p.d_k, 1, 0};
+    RoleArgs aq{dO, v, k, q, dq, init_state, nullptr, da_partial, p.d_v, p.d_k, 1, 0, 0};
     // dk: reverse scan of G^T ([d_v][d_k]); q'=v, k'=dO, v'=q, gate operand k
-    RoleArgs ak{v, dO, q, k, dk, d_final_state, nullptr, nullptr, p.d_v, p.d_k, 1, 0};
+    RoleArgs ak{v, dO, q, k, dk, d_final_state, nullptr, nullptr, p.d_v, p.d_k, 1, 0, 1};
     // dv: reverse scan of G ([d_k][d_v]); q'=k, k'=q, v'=dO; final G -> d_init_state
-    RoleArgs av{k, q, dO, nullptr, dv, d_final_state, d_init_state, nullptr, p.d_k, p.d_v, 0, 1};
+    RoleArgs av{k, q, dO, nullptr, dv, d_final_state, d_init_state, nullptr, p.d_k, p.d_v, 0, 1, 1};
     if (p.bf16) {
-        const int nslv = (p.d_v + 95) / 96;
-        if (p.chunk == 128) return run_bwd<BfDq, BfDk, BfDv128>(p, aq, ak, av, nslv, da, stream);
-        return run_bwd<BfDq, BfDk, BfDv64>(p, aq, ak, av, nslv, da, stream);
+        if (p.chunk == 128) return run_bwd<BfDq, BfDk, BfDv128>(p, aq, ak, av, da, stream);
+        return run_bwd<BfDq, BfDk, BfDv64>(p, aq, ak, av, da, stream);
     }
-    return run_bwd<F32Dq, F32Dk, F32Dv>(p, aq, ak, av, (p.d_v + 31) / 32, da, stream);
+    return run_bwd<F32Dq, F32Dk, F32Dv>(p, aq, ak, av, da, stream);
 }
 
 }  // namespace sgla

@@ -148,7 +148,8 @@ size_t sgla_chunk_bwd_workspace_bytes(int N, int H, int d_k);
  * dO:          [.., d_v] upstream gradient of o (dtype).
  * d_final_state: [N, H, d_k, d_v] or NULL = 0.
  * dq, dk, dv:  outputs (dtype), shaped like q, k, v; must not alias inputs.
- * da:          [H, d_k] fp32, overwritten (zeros when a is NULL).
+ * da:          [H, d_k] fp32, overwritten with dL/da (at a = 0 when a is NULL;
+ *              not zero then, since sigmoid'(0) = 1/4).
  * d_init_state: [N, H, d_k, d_v] or NULL (not written).
  * workspace:   device buffer of at least sgla_chunk_bwd_workspace_bytes()
  *              bytes, 16-byte aligned, owned by the caller; its contents on

@@ -175,9 +175,7 @@ void orc_bwd(int T, int d_k, int d_v, double lam, const double* a,
                 acc += G[(size_t)i * d_v + j] * vt[j];
             }
             dkt[i] = acc + ((a != NULL) ? c * a[i] * qt[i] : 0.0);
-            if (a != NULL) {
-                da[i] += c * qt[i] * kt[i];
-            }
+            da[i] += c * qt[i] * kt[i];
         }
         for (int j = 0; j < d_v; ++j) {
             double acc = 0.0;

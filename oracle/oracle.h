@@ -23,7 +23,8 @@
  * All arrays are row-major, token-major, for ONE (sequence, head) unit:
  *   q, k, dq, dk : [T][d_k]     v, o, dO, dv : [T][d_v]
  *   S0, S_final, dS_final, dS0 : [d_k][d_v]   a, da : [d_k]
- * A NULL S0 / dS_final means zero. A NULL a means zero.
+ * A NULL S0 / dS_final means zero. A NULL a means a = 0 everywhere (da is
+ * then the gradient at a = 0, which is not zero).
  */
 #ifndef SGLA_ORACLE_H
 #define SGLA_ORACLE_H

@@ -1,8 +1,17 @@
 """Helpers shared by the GPU parity tests: moving seeded inputs to the device,
 per-unit oracle references, and the error metric.
 
-Error metric (per output tensor): max |gpu - oracle| / RMS(oracle), over the
-elements compared. Gates: 1e-4 for fp32 inputs, 2e-2 for bf16 inputs.
+Error metric (per output tensor, over the elements compared):
+
+    err = max_i max(|gpu_i - ref_i| - half_ulp(gpu_i), 0) / RMS(ref)
+
+where half_ulp is half a unit in the last place of the format the output is
+stored in (bf16: 8 significant bits, fp32: 24). Subtracting it removes the
+rounding of the result to its own storage format, which no kernel can avoid:
+a bf16 copy of the exact result already scores up to 2^-8 max|ref|/RMS(ref)
+on the raw metric max|gpu - ref|/RMS(ref) (about 2.3e-2 on these workloads;
+see test_metric.py). The raw figure is printed beside the gated one.
+Gates: 1e-4 for fp32 inputs, 2e-2 for bf16 inputs.
 """
 from __future__ import annotations
 
@@ -29,20 +38,39 @@ def to_host64(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def rel_err(gpu, ref):
+SIG_BITS = {"bf16": 8, "f32": 24}
+
+
+def half_ulp(x, store):
+    """Half a unit in the last place of |x| in the given storage format."""
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    _, e = np.frexp(ax)  # ax = m * 2^e, m in [0.5, 1)
+    h = np.ldexp(1.0, e - SIG_BITS[store] - 1)
+    return np.where(ax == 0.0, 0.0, h)
+
+
+def rel_err(gpu, ref, store="f32", ref_store=None):
+    """(gated error, raw error), both normalised by RMS(ref)."""
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
-    rms = float(np.sqrt(np.mean(ref * ref)))
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    diff = np.abs(gpu - ref)
+    slack = half_ulp(gpu, store)
+    if ref_store is not None:
+        slack = slack + half_ulp(ref, ref_store)
+    adj = np.maximum(diff - slack, 0.0)
     if rms == 0.0:
-        return float(np.max(np.abs(gpu))) if gpu.size else 0.0
-    return float(np.max(np.abs(gpu - ref))) / rms
+        return (float(np.max(adj)) if adj.size else 0.0), (float(np.max(diff)) if diff.size else 0.0)
+    return float(np.max(adj)) / rms, float(np.max(diff)) / rms
 
 
-def assert_close(gpu, ref, tol, what):
+def assert_close(gpu, ref, tol, what, store="f32", ref_store=None):
+    """Gate the error of GPU values stored in ``store`` against reference values
+    (``ref_store`` when the reference is itself a rounded GPU output)."""
     assert np.all(np.isfinite(gpu)), f"{what}: non-finite GPU values"
-    e = rel_err(gpu, ref)
-    print(f"    {what}: err {e:.3e} (gate {tol:.0e})", flush=True)
-    assert e <= tol, f"{what}: max err / RMS = {e:.3e} > {tol:.1e}"
+    e, raw = rel_err(gpu, ref, store, ref_store)
+    print(f"    {what}: err {e:.3e} (raw {raw:.3e}, gate {tol:.0e})", flush=True)
+    assert e <= tol, f"{what}: err / RMS = {e:.3e} > {tol:.1e} (raw {raw:.3e})"
     return e
 
 

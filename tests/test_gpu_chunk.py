@@ -31,7 +31,7 @@ def run_fwd_case(inp, lam, chunk, cu=None, units=None):
     sg = np.concatenate([Sh[n, h].ravel() for n, h in units])
     sr = np.concatenate([ref[u][1].ravel() for u in units])
     tol = TOL[inp["dtype"]]
-    assert_close(og, orf, tol, "o")
+    assert_close(og, orf, tol, "o", store=inp["dtype"])
     assert_close(sg, sr, tol, "final_state")
     return o, Sf
 
@@ -50,7 +50,7 @@ def run_bwd_case(inp, lam, chunk, cu=None, units=None):
         th = to_host64(t)
         g = np.concatenate([gpu_unit(th, n, h, cu).ravel() for n, h in units])
         r = np.concatenate([ref[u][idx].ravel() for u in units])
-        assert_close(g, r, tol, name)
+        assert_close(g, r, tol, name, store=inp["dtype"])
     if len(units) == inp["N"] * inp["H"]:
         da_ref = np.zeros_like(inp["a"], dtype=np.float64)
         for (n, h) in units:
@@ -92,8 +92,7 @@ def test_bwd_f32(T):
 
 def test_bwd_f32_no_aug_no_state():
     inp = I.chunk_inputs(1, 2, 100, 16, 32, "f32", seed=50, a_std=None, with_grad=True)
-    dq, dk, dv, da, _ = run_bwd_case(inp, np.array([0.6, 0.97], np.float32), 64)
-    assert torch.count_nonzero(da).item() == 0
+    run_bwd_case(inp, np.array([0.6, 0.97], np.float32), 64)
 
 
 def test_varlen_f32_fwd_bwd():
@@ -158,7 +157,8 @@ def test_chunk_size_invariance_bf16():
     lam = to_dev(schedule32(16, 1.0, 2048.0))
     o64, _ = Bd.sgla_chunk_fwd(d["q"], d["k"], d["v"], lam, d["a"], chunk=64)
     o128, _ = Bd.sgla_chunk_fwd(d["q"], d["k"], d["v"], lam, d["a"], chunk=128)
-    assert_close(to_host64(o64), to_host64(o128), TOL["bf16"], "chunk 64 vs 128")
+    assert_close(to_host64(o64), to_host64(o128), TOL["bf16"], "chunk 64 vs 128",
+                 store="bf16", ref_store="bf16")
 
 
 def test_state_carry_bf16():
@@ -176,7 +176,8 @@ def test_state_carry_bf16():
     o2, S2 = Bd.sgla_chunk_fwd(part(d["q"], slice(t0, T)), part(d["k"], slice(t0, T)),
                                part(d["v"], slice(t0, T)), lam, d["a"], init_state=S1,
                                final_state=S1)  # in-place carry
-    assert_close(to_host64(torch.cat([o1, o2], dim=2)), to_host64(o), TOL["bf16"], "split o")
+    assert_close(to_host64(torch.cat([o1, o2], dim=2)), to_host64(o), TOL["bf16"], "split o",
+                 store="bf16", ref_store="bf16")
     assert_close(to_host64(S1), to_host64(Sf), TOL["bf16"], "split state")
 
 

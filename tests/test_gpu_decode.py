@@ -44,7 +44,7 @@ def test_decode_steps_vs_oracle(dtype, dk, dv):
                                 state)
         oh = to_host64(o)
         assert_close(oh.reshape(-1), np.stack([ref[s][u] for u in units]).reshape(-1),
-                     TOL[dtype], f"o step {s}")
+                     TOL[dtype], f"o step {s}", store=dtype)
     sh = to_host64(state)
     assert_close(sh.reshape(-1), np.stack([Sref[u] for u in units]).reshape(-1), TOL[dtype],
                  "state")
@@ -74,7 +74,7 @@ def test_decode_slots_and_invalid_slot():
             ro = oracle.decode_step_unit(I.widen(q[n, h], "bf16"), I.widen(k[n, h], "bf16"),
                                          I.widen(v[n, h], "bf16"), float(lamh[h]),
                                          a[h].astype(np.float64), S)
-            assert_close(oh[n, h], ro, TOL["bf16"], f"o n={n} h={h}")
+            assert_close(oh[n, h], ro, TOL["bf16"], f"o n={n} h={h}", store="bf16")
             assert_close(sh[p, h], S, TOL["bf16"], f"state page {p} h={h}")
     for p in range(P):
         if p not in touched:
@@ -120,5 +120,6 @@ def test_decode_matches_chunk_fwd():
         outs.append(Bd.sgla_decode_step(q[:, :, t].contiguous(), k[:, :, t].contiguous(),
                                         v[:, :, t].contiguous(), lam, a, state))
     o_dec = torch.stack(outs, dim=2)
-    assert_close(to_host64(o_dec), to_host64(o_chunk), TOL["bf16"], "decode vs chunk o")
+    assert_close(to_host64(o_dec), to_host64(o_chunk), TOL["bf16"], "decode vs chunk o",
+                 store="bf16", ref_store="bf16")
     assert_close(to_host64(state), to_host64(S_chunk), TOL["bf16"], "decode vs chunk state")
