@@ -59,6 +59,7 @@ typedef u16 u16x8_t __attribute__((ext_vector_type(8)));
 typedef u16 u16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int NTHREADS = 256;
 constexpr int NWAVES = 4;
@@ -74,10 +75,14 @@ template <> __device__ __forceinline__ u16 from_f<u16>(float x)
     return __builtin_bit_cast(u16, static_cast<__bf16>(x));
 }
 
+// 2^x on the transcendental unit (v_exp_f32). Results below the smallest
+// normal fp32 flush to zero; decays that small contribute nothing here.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // lam^m for an integer m >= 0 with lam^0 = 1 exactly (also for lam = 0).
 __device__ __forceinline__ float decay_pow(int m, float log2lam)
 {
-    return (m == 0) ? 1.0f : exp2f((float)m * log2lam);
+    return (m == 0) ? 1.0f : fast_exp2((float)m * log2lam);
 }
 
 __device__ __forceinline__ float sigmoidf_(float z)
@@ -85,6 +90,19 @@ __device__ __forceinline__ float sigmoidf_(float z)
     if (z >= 0.0f) return 1.0f / (1.0f + expf(-z));
     float e = expf(z);
     return e / (1.0f + e);
+}
+
+// Element e of a 16-byte register vector holding E values, widened to fp32.
+// (Bit operations on native vectors keep these registers out of memory.)
+template <typename E> __device__ __forceinline__ float vget(const u32x4_t& v, int e);
+template <> __device__ __forceinline__ float vget<u16>(const u32x4_t& v, int e)
+{
+    const uint32_t w = v[e >> 1];
+    return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+}
+template <> __device__ __forceinline__ float vget<float>(const u32x4_t& v, int e)
+{
+    return __uint_as_float(v[e]);
 }
 
 template <typename E> struct Mfma;
@@ -114,13 +132,24 @@ template <> struct Mfma<float> {
     }
 };
 
+// Workgroup barrier for LDS hand-offs. It waits only for this wave's LDS (and
+// scalar) operations, not for its global loads: __syncthreads() would also
+// drain vmcnt and so stall on the next chunk's prefetch it is meant to overlap.
+// Every cross-wave exchange in these kernels goes through LDS.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Row (within a 32x32 tile) held by accumulator i of lane group g.
 __device__ __forceinline__ int acc_row(int i, int g) { return 8 * (i >> 2) + 4 * g + (i & 3); }
 
 enum { AUG_FWD = 0, AUG_GRAD = 1 };
 
-// Static assignment of state tiles to waves: greedy on the per-chunk
-// matrix-core instruction count (query-strip work first, then tiles).
+// Static assignment of state d-blocks (32 state rows x all value tiles of the
+// slice) to waves: greedy on the per-chunk matrix-core instruction count,
+// query-strip work first. Owning whole d-blocks lets one converted key
+// operand of the state update feed every value tile of that block.
 struct Owners {
     int count[NWAVES];
     int list[NWAVES][32];
@@ -165,8 +194,8 @@ struct Role {
     static constexpr int NTILES = NDB * NNT;
     static constexpr Owners OWN =
         balance(NSTRIP, (DK / M::KSTEP) * NNT * HILO, DK / M::KSTEP + NNT * (32 / M::KSTEP),
-                (C / M::KSTEP) * HILO, NTILES);
-    static constexpr int NTW = OWN.max_count;
+                NNT * (C / M::KSTEP) * HILO, NDB);
+    static constexpr int NDBW = OWN.max_count;  // d-blocks per wave (at most)
     static constexpr size_t SZ_ROWS = (size_t)C * LDQ * sizeof(E);
     static constexpr size_t SZ_ST = (size_t)DVS * LDQ * sizeof(E);
     static constexpr size_t OFF_Q = 0;
@@ -178,16 +207,18 @@ struct Role {
     static constexpr size_t OFF_XT = OFF_STL + (HILO == 2 ? SZ_ST : 0);
     static constexpr size_t OFF_COEF = OFF_XT + (AUG == AUG_GRAD ? (size_t)DVS * LDT * sizeof(E) : 0);
     static constexpr size_t OFF_KSC = OFF_COEF + (size_t)C * sizeof(float);
-    static constexpr size_t OFF_DA = OFF_KSC + (size_t)C * sizeof(float);
+    static constexpr int AWN = DK > 128 ? DK : 128;  // staged width of a
+    static constexpr size_t OFF_A = OFF_KSC + (size_t)C * sizeof(float);
+    static constexpr size_t OFF_DA = OFF_A + (size_t)AWN * sizeof(float);
     static constexpr size_t LDS = OFF_DA + (AUG == AUG_GRAD ? (size_t)NSTRIP * DVS * sizeof(float) : 0);
     static_assert(DK % 32 == 0 && DVS % 32 == 0 && C % 32 == 0 && C <= 128, "tile shape");
     static_assert(LDS <= 160 * 1024, "LDS budget");
-    static_assert(NTILES <= 32, "owner table");
+    static_assert(NDB <= 32, "owner table");
 };
 
-// State tile handled by a wave's kk-th accumulator (or -1).
+// State d-block handled by a wave's kk-th accumulator group (or -1).
 template <class R>
-__device__ __forceinline__ int tile_of(int wave, int kk)
+__device__ __forceinline__ int dblock_of(int wave, int kk)
 {
     constexpr Owners o = R::OWN;
     switch (wave) {
@@ -227,7 +258,7 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
     typedef typename R::E E;
     typedef typename R::M M;
     constexpr int C = R::C, DK = R::DK, DVS = R::DVS, LDQ = R::LDQ, LDT = R::LDT;
-    constexpr int NSTRIP = R::NSTRIP, NNT = R::NNT, NTW = R::NTW;
+    constexpr int NSTRIP = R::NSTRIP, NNT = R::NNT, NDBW = R::NDBW;
     constexpr int KSTEP = M::KSTEP, NE = M::NE;
     constexpr bool SPLIT = (R::HILO == 2);
     constexpr int V16 = 16 / (int)sizeof(E);  // elements per 16-byte segment
@@ -242,6 +273,7 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
     float* coef = reinterpret_cast<float*>(smem + R::OFF_COEF);
     float* ksc = reinterpret_cast<float*>(smem + R::OFF_KSC);
     float* dared = reinterpret_cast<float*>(smem + R::OFF_DA);
+    float* a_lds = reinterpret_cast<float*>(smem + R::OFF_A);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -273,24 +305,28 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
     const E* gx = reinterpret_cast<const E*>(ra.xp);
     E* go = reinterpret_cast<E*>(ra.op);
 
-    // ---- state slice in accumulators: tile tau = db*NNT + nb
-    int tiles[NTW];
-    f32x16_t sacc[NTW];
+    // ---- state slice in accumulators: d-block dbs[kk], value tile nb in
+    // sacc[kk * NNT + nb]
+    int dbs[NDBW];
+    f32x16_t sacc[NDBW * NNT];
 #pragma unroll
-    for (int kk = 0; kk < NTW; ++kk) {
-        const int tau = tile_of<R>(wave, kk);
-        tiles[kk] = tau;
+    for (int kk = 0; kk < NDBW; ++kk) {
+        const int db = dblock_of<R>(wave, kk);
+        dbs[kk] = db;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kk][i] = 0.0f;
-        if (tau >= 0 && ra.s_init != nullptr) {
-            const int db = tau / NNT, nb = tau - (tau / NNT) * NNT;
-            const int nn = n0 + 32 * nb + l32;
+        for (int nb = 0; nb < NNT; ++nb) {
+            f32x16_t& acc = sacc[kk * NNT + nb];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int d = 32 * db + acc_row(i, g);
-                if (d < dkr && nn < dvr)
-                    sacc[kk][i] = ra.state_t ? ra.s_init[sbase + (size_t)nn * dkr + d]
-                                             : ra.s_init[sbase + (size_t)d * dvr + nn];
+            for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+            if (db >= 0 && ra.s_init != nullptr) {
+                const int nn = n0 + 32 * nb + l32;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int d = 32 * db + acc_row(i, g);
+                    if (d < dkr && nn < dvr)
+                        acc[i] = ra.state_t ? ra.s_init[sbase + (size_t)nn * dkr + d]
+                                            : ra.s_init[sbase + (size_t)d * dvr + nn];
+                }
             }
         }
     }
@@ -299,115 +335,215 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
 #pragma unroll
     for (int nt = 0; nt < NNT; ++nt) da_acc[nt] = 0.0f;
 
-    // lam^(t+1) for the strip rows this lane holds; lam^t where the carried
-    // state is not decayed before the first token (reverse scans)
-    float lq[16], lq0[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        lq[i] = decay_pow(32 * wave + acc_row(i, g) + 1, l2);
-        lq0[i] = decay_pow(32 * wave + acc_row(i, g), l2);
+    // a (aug_balance) of this head, staged once; indexed by d (forward-type
+    // roles) or by the value column (gradient roles), zero past the width
+    {
+        const int aw = (R::AUG == AUG_FWD) ? dkr : dvr;
+        for (int i = tid; i < R::AWN; i += NTHREADS)
+            a_lds[i] = (cm.a != nullptr && i < aw) ? cm.a[(size_t)h * aw + i] : 0.0f;
     }
 
+    // ---- operand staging, software-pipelined: chunk ci+1 is read from HBM
+    // into registers while chunk ci is computed out of LDS.
+    constexpr bool GRAD = (R::AUG == AUG_GRAD);
+    constexpr int SEGQ = DK / V16, SEGV = DVS / V16, RP = C / 2;
+    constexpr int NBQ = (RP * SEGQ + NTHREADS - 1) / NTHREADS;
+    constexpr int NBV = (RP * SEGV + NTHREADS - 1) / NTHREADS;
+    static_assert(RP % 16 == 0 && SEGQ % 4 == 0 && SEGV % 4 == 0, "staging map");
+    u32x4_t pq[NBQ][2], pk[NBQ][2], pv[NBV][2], px[GRAD ? NBV : 1][2];
+
+    // Staging block b -> (row pair rp, 16-byte column segment cg). Sixteen
+    // consecutive lanes take sixteen row pairs of one segment, so their
+    // transposed LDS writes fall in distinct banks; four such lane groups take
+    // four adjacent segments, i.e. 64 contiguous bytes of every row they read.
+    auto block_rc = [](int b, int nseg, int& rp, int& cg) {
+        const int rest = b >> 6;
+        rp = (rest % (RP / 16)) * 16 + (b & 15);
+        cg = (rest / (RP / 16)) * 4 + ((b >> 4) & 3);
+        (void)nseg;
+    };
     const int nchunks = (len + C - 1) / C;
+    // The loads are unconditional, from clamped in-bounds addresses: a load
+    // under a lane mask followed by a merge with zero would have to wait for
+    // the data right away. Rows past the chunk and columns past the real
+    // width are zeroed later, when store_chunk consumes the registers.
+    auto load_chunk = [&](int cj) {
+        const int cc = R::REV ? (nchunks - 1 - cj) : cj;
+        const int cs = cc * C, cl = min(C, len - cs);
+#pragma unroll
+        for (int m = 0; m < NBQ; ++m) {
+            const int b = tid + NTHREADS * m;
+            int rp, cg;
+            block_rc(b, SEGQ, rp, cg);
+            const int col = min(cg * V16, dkr - V16);
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr) {
+                const int r = min(2 * rp + rr, cl - 1);
+                const int tok = R::REV ? (cs + cl - 1 - r) : (cs + r);
+                const size_t off = (size_t)(row0 + tok) * dkr + col;
+                pq[m][rr] = *reinterpret_cast<const u32x4_t*>(gq + off);
+                pk[m][rr] = *reinterpret_cast<const u32x4_t*>(gk + off);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < NBV; ++m) {
+            const int b = tid + NTHREADS * m;
+            int rp, cg;
+            block_rc(b, SEGV, rp, cg);
+            const int gcol = min(n0 + cg * V16, dvr - V16);
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr) {
+                const int r = min(2 * rp + rr, cl - 1);
+                const int tok = R::REV ? (cs + cl - 1 - r) : (cs + r);
+                const size_t off = (size_t)(row0 + tok) * dvr + gcol;
+                pv[m][rr] = *reinterpret_cast<const u32x4_t*>(gv + off);
+                if (GRAD) px[m][rr] = *reinterpret_cast<const u32x4_t*>(gx + off);
+            }
+        }
+    };
+    // element e of two rows, packed for a single transposed LDS write
+    auto put_pair = [](E* dst, const u32x4_t& r0, const u32x4_t& r1, int e) {
+        if constexpr (sizeof(E) == 2) {
+            const uint32_t w0 = r0[e >> 1], w1 = r1[e >> 1];
+            *reinterpret_cast<uint32_t*>(dst) =
+                (e & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u)) : ((w0 & 0xffffu) | (w1 << 16));
+        } else {
+            typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+            u32x2_t pr = {r0[e], r1[e]};
+            *reinterpret_cast<u32x2_t*>(dst) = pr;
+        }
+    };
+    const u32x4_t zero4 = {0u, 0u, 0u, 0u};
+    auto store_chunk = [&](int cl) {
+#pragma unroll
+        for (int m = 0; m < NBQ; ++m) {
+            const int b = tid + NTHREADS * m;
+            if (b < RP * SEGQ) {
+                int rp, cg;
+                block_rc(b, SEGQ, rp, cg);
+                const int col = cg * V16;
+#pragma unroll
+                for (int rr = 0; rr < 2; ++rr) {
+                    const bool ok = (2 * rp + rr < cl) && (col < dkr);
+                    pq[m][rr] = ok ? pq[m][rr] : zero4;
+                    pk[m][rr] = ok ? pk[m][rr] : zero4;
+                }
+#pragma unroll
+                for (int rr = 0; rr < 2; ++rr) {
+                    *reinterpret_cast<u32x4_t*>(Qs + (2 * rp + rr) * LDQ + col) = pq[m][rr];
+                    *reinterpret_cast<u32x4_t*>(Ks + (2 * rp + rr) * LDQ + col) = pk[m][rr];
+                }
+#pragma unroll
+                for (int e = 0; e < V16; ++e) put_pair(KTs + (col + e) * LDT + 2 * rp, pk[m][0], pk[m][1], e);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < NBV; ++m) {
+            const int b = tid + NTHREADS * m;
+            if (b < RP * SEGV) {
+                int rp, cg;
+                block_rc(b, SEGV, rp, cg);
+                const int col = cg * V16;
+#pragma unroll
+                for (int rr = 0; rr < 2; ++rr) {
+                    const bool ok = (2 * rp + rr < cl) && (n0 + col < dvr);
+                    pv[m][rr] = ok ? pv[m][rr] : zero4;
+                    if (GRAD) px[m][rr] = ok ? px[m][rr] : zero4;
+                }
+#pragma unroll
+                for (int e = 0; e < V16; ++e) {
+                    put_pair(VTs + (col + e) * LDT + 2 * rp, pv[m][0], pv[m][1], e);
+                    if (GRAD) put_pair(XTs + (col + e) * LDT + 2 * rp, px[m][0], px[m][1], e);
+                }
+            }
+        }
+    };
+
+    if (nchunks > 0) load_chunk(0);
     for (int ci = 0; ci < nchunks; ++ci) {
         const int c = R::REV ? (nchunks - 1 - ci) : ci;
         const int cstart = c * C;
         const int clen = min(C, len - cstart);
         const bool shift = ra.init_undecayed && ci == 0;
 
-        __syncthreads();  // previous chunk's LDS readers are done
+        lds_barrier();  // previous chunk's LDS readers are done
 
-        // state before this chunk -> STh (+ STl), transposed
+        // state before this chunk -> STh (+ STl), transposed; the four
+        // consecutive state rows of an accumulator group go out as one write
 #pragma unroll
-        for (int kk = 0; kk < NTW; ++kk) {
-            const int tau = tiles[kk];
-            if (tau >= 0) {
-                const int db = tau / NNT, nb = tau - (tau / NNT) * NNT;
+        for (int kt = 0; kt < NDBW * NNT; ++kt) {
+            const int db = dbs[kt / NNT], nb = kt % NNT;
+            if (db >= 0) {
+                const f32x16_t& acc = sacc[kt];
                 const int nl = 32 * nb + l32;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int off = nl * LDQ + 32 * db + acc_row(i, g);
-                    const E hi = from_f<E>(sacc[kk][i]);
-                    STh[off] = hi;
-                    if (SPLIT) STl[off] = from_f<E>(sacc[kk][i] - to_f(hi));
+                for (int qd = 0; qd < 4; ++qd) {
+                    const int off = nl * LDQ + 32 * db + 8 * qd + 4 * g;
+                    if constexpr (sizeof(E) == 2) {
+                        u16x4_t hv, lv;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float x = acc[4 * qd + e];
+                            const u16 hb = from_f<u16>(x);
+                            hv[e] = hb;
+                            lv[e] = from_f<u16>(x - to_f(hb));
+                        }
+                        *reinterpret_cast<u16x4_t*>(STh + off) = hv;
+                        *reinterpret_cast<u16x4_t*>(STl + off) = lv;
+                    } else {
+                        f32x4_t hv;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) hv[e] = acc[4 * qd + e];
+                        *reinterpret_cast<f32x4_t*>(STh + off) = hv;
+                    }
                 }
             }
         }
-        // key decays of the state update
-        for (int r = tid; r < C; r += NTHREADS) {
-            const int m = clen - 1 - r - (shift ? 1 : 0);
-            ksc[r] = (r < clen) ? (m < 0 ? 0.0f : decay_pow(m, l2)) : 0.0f;
-        }
+        // key decays of the state update (not shifted: only the carried-in
+        // state enters the first reversed token undecayed)
+        for (int r = tid; r < C; r += NTHREADS) ksc[r] = (r < clen) ? decay_pow(clen - 1 - r, l2) : 0.0f;
+        store_chunk(clen);
+        if (ci + 1 < nchunks) load_chunk(ci + 1);  // in flight during this chunk's math
+        lds_barrier();
 
-        // q', k' rows (natural) and k' transposed
-        constexpr int SEGQ = DK / V16;
-        for (int idx = tid; idx < C * SEGQ; idx += NTHREADS) {
-            const int r = idx / SEGQ, col = (idx - (idx / SEGQ) * SEGQ) * V16;
-            uint4 qv = make_uint4(0, 0, 0, 0), kv = make_uint4(0, 0, 0, 0);
-            if (r < clen && col < dkr) {
-                const int tok = R::REV ? (cstart + clen - 1 - r) : (cstart + r);
-                const size_t off = (size_t)(row0 + tok) * dkr + col;
-                qv = *reinterpret_cast<const uint4*>(gq + off);
-                kv = *reinterpret_cast<const uint4*>(gk + off);
-            }
-            *reinterpret_cast<uint4*>(Qs + r * LDQ + col) = qv;
-            *reinterpret_cast<uint4*>(Ks + r * LDQ + col) = kv;
-            const E* ke = reinterpret_cast<const E*>(&kv);
-#pragma unroll
-            for (int e = 0; e < V16; ++e) KTs[(col + e) * LDT + r] = ke[e];
-        }
-        // v' slice (and the gate's second operand) transposed
-        constexpr int SEGV = DVS / V16;
-        for (int idx = tid; idx < C * SEGV; idx += NTHREADS) {
-            const int r = idx / SEGV, col = (idx - (idx / SEGV) * SEGV) * V16;
-            const int gcol = n0 + col;
-            uint4 vv = make_uint4(0, 0, 0, 0), xv = make_uint4(0, 0, 0, 0);
-            if (r < clen && gcol < dvr) {
-                const int tok = R::REV ? (cstart + clen - 1 - r) : (cstart + r);
-                const size_t off = (size_t)(row0 + tok) * dvr + gcol;
-                vv = *reinterpret_cast<const uint4*>(gv + off);
-                if (R::AUG == AUG_GRAD) xv = *reinterpret_cast<const uint4*>(gx + off);
-            }
-            const E* ve = reinterpret_cast<const E*>(&vv);
-            const E* xe = reinterpret_cast<const E*>(&xv);
-#pragma unroll
-            for (int e = 0; e < V16; ++e) {
-                VTs[(col + e) * LDT + r] = ve[e];
-                if (R::AUG == AUG_GRAD) XTs[(col + e) * LDT + r] = xe[e];
-            }
-        }
-        __syncthreads();
-
-        // per-token epilogue coefficient (two threads per token)
+        // per-token epilogue coefficient (two threads per token, 16-byte reads)
         if (tid < 2 * C) {
             const int r = tid >> 1, half = tid & 1;
+            constexpr int HV = DK / V16 / 2;  // 16-byte vectors per half row
             float z = 0.0f, u = 0.0f;
-            if (R::AUG == AUG_FWD) {
-                if (cm.a != nullptr) {
-                    const float* ah = cm.a + (size_t)h * dkr;
-                    for (int d = half; d < dkr; d += 2)
-                        z += ah[d] * to_f(Qs[r * LDQ + d]) * to_f(Ks[r * LDQ + d]);
+#pragma unroll
+            for (int vi = 0; vi < HV; ++vi) {
+                const int col = (half * HV + vi) * V16;
+                const u32x4_t qv = *reinterpret_cast<const u32x4_t*>(Qs + r * LDQ + col);
+                const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(Ks + r * LDQ + col);
+#pragma unroll
+                for (int e = 0; e < V16; ++e) {
+                    const float p = vget<E>(qv, e) * vget<E>(kv, e);
+                    if (GRAD) u += p;
+                    else z += a_lds[col + e] * p;
                 }
-            } else {
-                // z = sum_n a_n v'_n x_n over the full width (read from memory:
-                // this workgroup holds only a slice of v' and x)
-                if (cm.a != nullptr && r < clen) {
-                    const float* ah = cm.a + (size_t)h * dvr;
-                    const int tok = R::REV ? (cstart + clen - 1 - r) : (cstart + r);
-                    const E* vr = gv + (size_t)(row0 + tok) * dvr;
-                    const E* xr = gx + (size_t)(row0 + tok) * dvr;
-                    for (int nn = half; nn < dvr; nn += 2) z += ah[nn] * to_f(vr[nn]) * to_f(xr[nn]);
+            }
+            if (GRAD && cm.a != nullptr && r < clen) {
+                // z = sum_n a_n v'_n x_n over the full width, read from memory:
+                // this workgroup stages only a slice of v' and x
+                const int tok = R::REV ? (cstart + clen - 1 - r) : (cstart + r);
+                const E* vr = gv + (size_t)(row0 + tok) * dvr;
+                const E* xr = gx + (size_t)(row0 + tok) * dvr;
+                for (int col = half * V16; col < dvr; col += 2 * V16) {
+                    const u32x4_t vv = *reinterpret_cast<const u32x4_t*>(vr + col);
+                    const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xr + col);
+#pragma unroll
+                    for (int e = 0; e < V16; ++e) z += a_lds[col + e] * vget<E>(vv, e) * vget<E>(xv, e);
                 }
-                for (int d = half; d < dkr; d += 2) u += to_f(Qs[r * LDQ + d]) * to_f(Ks[r * LDQ + d]);
             }
             z += __shfl_xor(z, 1);
             u += __shfl_xor(u, 1);
             if (half == 0) {
                 const float s = sigmoidf_(z);
-                coef[r] = (R::AUG == AUG_FWD) ? s : s * (1.0f - s) * u;
+                coef[r] = GRAD ? s * (1.0f - s) * u : s;
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- query strips
         if (wave < NSTRIP && 32 * wave < clen) {
@@ -429,10 +565,14 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
                     if (SPLIT) oacc[nt] = M::mma(av, M::load(STl + boff), oacc[nt]);
                 }
             }
+            // rows scale by lam^(t+1), or lam^t where the carried state enters
+            // the first token undecayed (first chunk of a reverse scan)
 #pragma unroll
-            for (int nt = 0; nt < NNT; ++nt)
+            for (int i = 0; i < 16; ++i) {
+                const float f = decay_pow(t0 + acc_row(i, g) + (shift ? 0 : 1), l2);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) oacc[nt][i] *= shift ? lq0[i] : lq[i];
+                for (int nt = 0; nt < NNT; ++nt) oacc[nt][i] *= f;
+            }
 
             // intra-chunk: decay-masked scores, then P V'
             for (int jb = 0; jb <= wave; ++jb) {
@@ -450,7 +590,8 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int diff = t - (32 * jb + acc_row(i, g));
-                    sc[i] = (diff < 0) ? 0.0f : (diff == 0 ? sc[i] : sc[i] * exp2f((float)diff * l2));
+                    const float f = (diff == 0) ? 1.0f : fast_exp2((float)diff * l2);
+                    sc[i] = (diff < 0) ? 0.0f : sc[i] * f;
                 }
                 if constexpr (sizeof(E) == 2) {
                     // two contraction steps of 16 keys: step hh uses sc[8hh..8hh+7],
@@ -482,30 +623,49 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
                 }
             }
 
-            // epilogue: + coef_t * w_n * v'_t[n]  (w = 1, or a for the gradient roles)
+            // epilogue: + coef_t * w_n * v'_t[n]  (w = 1, or a for the gradient
+            // roles); accumulator group qd holds 4 consecutive rows t
+            E* obase = go + (size_t)(row0 + (R::REV ? cstart + clen - 1 : cstart)) * dvr + n0;
+            const int ostep = R::REV ? -dvr : dvr;
 #pragma unroll
             for (int nt = 0; nt < NNT; ++nt) {
                 const int nl = 32 * nt + l32;
-                const int gcol = n0 + nl;
-                float wn = 1.0f;
-                if (R::AUG == AUG_GRAD)
-                    wn = (cm.a != nullptr && gcol < dvr) ? cm.a[(size_t)h * dvr + gcol] : 0.0f;
+                const float wn = (R::AUG == AUG_GRAD) ? a_lds[n0 + nl] : 1.0f;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int t = t0 + acc_row(i, g);
-                    const float vt = to_f(VTs[nl * LDT + t]);
-                    const float cf = coef[t];
-                    oacc[nt][i] += cf * wn * vt;
-                    if (R::AUG == AUG_GRAD) da_acc[nt] += cf * vt * to_f(XTs[nl * LDT + t]);
+                for (int qd = 0; qd < 4; ++qd) {
+                    const int t = t0 + 8 * qd + 4 * g;
+                    const f32x4_t cf = *reinterpret_cast<const f32x4_t*>(coef + t);
+                    float vt[4], xt[4];
+                    if constexpr (sizeof(E) == 2) {
+                        const u16x4_t v4 = *reinterpret_cast<const u16x4_t*>(VTs + nl * LDT + t);
+                        u16x4_t x4 = {0, 0, 0, 0};
+                        if (R::AUG == AUG_GRAD) x4 = *reinterpret_cast<const u16x4_t*>(XTs + nl * LDT + t);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            vt[e] = to_f((u16)v4[e]);
+                            xt[e] = to_f((u16)x4[e]);
+                        }
+                    } else {
+                        const f32x4_t v4 = *reinterpret_cast<const f32x4_t*>(VTs + nl * LDT + t);
+                        f32x4_t x4 = {0.f, 0.f, 0.f, 0.f};
+                        if (R::AUG == AUG_GRAD) x4 = *reinterpret_cast<const f32x4_t*>(XTs + nl * LDT + t);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            vt[e] = v4[e];
+                            xt[e] = x4[e];
+                        }
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        oacc[nt][4 * qd + e] += cf[e] * wn * vt[e];
+                        if (R::AUG == AUG_GRAD) da_acc[nt] += cf[e] * vt[e] * xt[e];
+                    }
                 }
-                if (gcol < dvr) {
+                if (n0 + nl < dvr) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int t = t0 + acc_row(i, g);
-                        if (t < clen) {
-                            const int tok = R::REV ? (cstart + clen - 1 - t) : (cstart + t);
-                            go[(size_t)(row0 + tok) * dvr + gcol] = from_f<E>(oacc[nt][i]);
-                        }
+                        if (t < clen) obase[t * ostep + nl] = from_f<E>(oacc[nt][i]);
                     }
                 }
             }
@@ -514,16 +674,16 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
         // ---- state advance: S = lam^(C_c) S + (lam^m k')^T V', decayed keys as hi + lo
         const float fc = decay_pow(clen - (shift ? 1 : 0), l2);
 #pragma unroll
-        for (int kk = 0; kk < NTW; ++kk) {
-            const int tau = tiles[kk];
-            if (tau >= 0) {
-                const int db = tau / NNT, nb = tau - (tau / NNT) * NNT;
+        for (int kk = 0; kk < NDBW; ++kk) {
+            const int db = dbs[kk];
+            if (db >= 0) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) sacc[kk][i] *= fc;
+                for (int nb = 0; nb < NNT; ++nb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) sacc[kk * NNT + nb][i] *= fc;
 #pragma unroll 2
                 for (int kb = 0; kb < C / KSTEP; ++kb) {
                     const int j0 = kb * KSTEP + g * NE;
-                    const typename M::op_t bv = M::load(VTs + (32 * nb + l32) * LDT + j0);
                     const E* kr = KTs + (32 * db + l32) * LDT + j0;
                     if constexpr (sizeof(E) == 2) {
                         const u16x8_t kw = *reinterpret_cast<const u16x8_t*>(kr);
@@ -537,10 +697,21 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
                             hw[s] = hb;
                             lw[s] = from_f<u16>(x - to_f(hb));
                         }
-                        sacc[kk] = M::mma(__builtin_bit_cast(bf16x8_t, hw), bv, sacc[kk]);
-                        sacc[kk] = M::mma(__builtin_bit_cast(bf16x8_t, lw), bv, sacc[kk]);
+                        const bf16x8_t ha = __builtin_bit_cast(bf16x8_t, hw);
+                        const bf16x8_t la = __builtin_bit_cast(bf16x8_t, lw);
+#pragma unroll
+                        for (int nb = 0; nb < NNT; ++nb) {
+                            const typename M::op_t bv = M::load(VTs + (32 * nb + l32) * LDT + j0);
+                            sacc[kk * NNT + nb] = M::mma(ha, bv, sacc[kk * NNT + nb]);
+                            sacc[kk * NNT + nb] = M::mma(la, bv, sacc[kk * NNT + nb]);
+                        }
                     } else {
-                        sacc[kk] = M::mma(to_f(*kr) * ksc[j0], bv, sacc[kk]);
+                        const float av = to_f(*kr) * ksc[j0];
+#pragma unroll
+                        for (int nb = 0; nb < NNT; ++nb) {
+                            const typename M::op_t bv = M::load(VTs + (32 * nb + l32) * LDT + j0);
+                            sacc[kk * NNT + nb] = M::mma(av, bv, sacc[kk * NNT + nb]);
+                        }
                     }
                 }
             }
@@ -551,16 +722,15 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
     if (ra.s_final != nullptr) {
         const float fs = (ra.final_times_lam && len > 0) ? lam : 1.0f;
 #pragma unroll
-        for (int kk = 0; kk < NTW; ++kk) {
-            const int tau = tiles[kk];
-            if (tau >= 0) {
-                const int db = tau / NNT, nb = tau - (tau / NNT) * NNT;
+        for (int kt = 0; kt < NDBW * NNT; ++kt) {
+            const int db = dbs[kt / NNT], nb = kt % NNT;
+            if (db >= 0) {
                 const int nn = n0 + 32 * nb + l32;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int d = 32 * db + acc_row(i, g);
                     if (d < dkr && nn < dvr) {
-                        const float val = sacc[kk][i] * fs;
+                        const float val = sacc[kt][i] * fs;
                         if (ra.state_t) ra.s_final[sbase + (size_t)nn * dkr + d] = val;
                         else ra.s_final[sbase + (size_t)d * dvr + nn] = val;
                     }
@@ -571,7 +741,7 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
 
     // ---- partial da of this (sequence, head, slice): fixed-order reduction
     if (R::AUG == AUG_GRAD && ra.da_part != nullptr) {
-        __syncthreads();
+        lds_barrier();
         if (wave < NSTRIP) {
 #pragma unroll
             for (int nt = 0; nt < NNT; ++nt) {
@@ -579,7 +749,7 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
                 if (g == 0) dared[wave * DVS + 32 * nt + l32] = s;
             }
         }
-        __syncthreads();
+        lds_barrier();
         for (int nl = tid; nl < DVS; nl += NTHREADS) {
             float s = 0.0f;
             for (int w = 0; w < NSTRIP; ++w) s += dared[w * DVS + nl];
