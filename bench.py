@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["fwd", "fwdbwd", "decode", "varlen"], default=None)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="first run a plain 1 GiB elementwise copy (read 1 GiB, write 1 GiB) "
+                         "so a counter pass can scale FETCH_SIZE / WRITE_SIZE")
     return ap.parse_args()
 
 
@@ -223,6 +226,14 @@ def main():
         sys.exit(1)
     from chunked_gated_linear_simple_amd import binding as Bd
     Bd.lib()  # fail loudly if the library is not built
+
+    if args.calib_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     secondary = {}
     only = args.only

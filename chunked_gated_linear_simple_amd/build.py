@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsgla.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["sgla_api.cpp", "sgla_chunk.hip", "sgla_decode.hip"]
+SOURCES = ["sgla_api.cpp", "sgla_chunk.hip", "sgla_fwd.hip", "sgla_decode.hip"]
 ARCH = "gfx950"
 
 

@@ -854,6 +854,7 @@ hipError_t launch_chunk_fwd(const ChunkProblem& p, const void* q, const void* k,
                             const float* init_state, float* final_state, void* o,
                             hipStream_t stream)
 {
+    if (p.bf16 && p.d_k <= 96) return launch_fwd_bf16(p, q, k, v, init_state, final_state, o, stream);
     RoleArgs ra{q, k, v, nullptr, o, init_state, final_state, nullptr, p.d_k, p.d_v, 0, 0, 0};
     if (p.bf16) {
         const int nsl = (p.d_v + 95) / 96;

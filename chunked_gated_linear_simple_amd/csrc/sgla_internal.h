@@ -24,6 +24,11 @@ hipError_t launch_chunk_fwd(const ChunkProblem& p, const void* q, const void* k,
                             const float* init_state, float* final_state, void* o,
                             hipStream_t stream);
 
+// bf16 forward, d_k <= 96: the column-owner kernel of sgla_fwd.hip.
+hipError_t launch_fwd_bf16(const ChunkProblem& p, const void* q, const void* k, const void* v,
+                           const float* init_state, float* final_state, void* o,
+                           hipStream_t stream);
+
 hipError_t launch_chunk_bwd(const ChunkProblem& p, const void* q, const void* k, const void* v,
                             const void* dO, const float* init_state, const float* d_final_state,
                             void* dq, void* dk, void* dv, float* da, float* d_init_state,
