@@ -17,6 +17,10 @@ LIB = os.path.join(PKG, "libsgla.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["sgla_api.cpp", "sgla_chunk.hip", "sgla_fwd.hip", "sgla_decode.hip"]
+# Per-source flags. The column-owner kernels keep matrix-core accumulators in
+# architectural VGPRs: their state and output tiles are read by VALU code every
+# tile, and accumulators placed in AGPRs cost a copy in each direction.
+EXTRA_FLAGS = {"sgla_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 ARCH = "gfx950"
 
 
@@ -43,7 +47,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-        cmd = [cc, *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *common_flags(), *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

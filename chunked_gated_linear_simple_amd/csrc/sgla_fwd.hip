@@ -18,24 +18,33 @@
 // Work decomposition. One workgroup per (sequence, head, 96-column value
 // slice), four waves:
 //   * waves 0..2 ("column owners") each own 32 value columns. A wave keeps its
-//     96 x 32 fp32 slice of the state in matrix-core accumulators for the whole
-//     sequence and computes every output of its columns, so the state never
-//     leaves the wave and no wave waits on another for it;
-//   * wave 3 ("producer") reads the next tile from HBM into registers while
-//     the owners compute the current one, then writes it to the other half of a
-//     double-buffered LDS stage: Q and K row-major, K^T and V^T token-minor, and
-//     the per-token gate sigmoid(z). One barrier per tile.
+//     d_k x 32 fp32 slice of the state in matrix-core accumulators for the
+//     whole sequence and computes every output of its columns, so the state
+//     never leaves the wave;
+//   * wave 3 ("producer") streams the tiles from HBM straight into a 3-deep
+//     LDS ring (global_load_lds: no registers, two tiles in flight while the
+//     owners compute a third), and for the next tile computes the gate
+//     sigmoid(z) and the decay-masked score tiles P^T = mask(K Q^T), with the
+//     gate added on the diagonal so that P V carries the self-augmentation
+//     term. The owners take P as bf16 matrix-core fragments. One barrier per
+//     tile.
+//
+// LDS tiles are row-major (Q, K: [64][d_k], V: [64][96]) with 16-byte segments
+// permuted within each row, segment c of row r stored at c ^ sw(r), so that
+// both the row reads of the score operands and the transposing reads below
+// touch distinct banks.
 //
 // Matrix-core mapping, v_mfma_f32_32x32x16_bf16. Accumulator lane l holds
-// column l%32, rows 8(i/4) + 4(l/32) + i%4 in register i. Any accumulator read
-// back as an operand of a contraction over its rows therefore carries, for the
-// 16-wide step h, the rows 16h + 8a + 4g + b in slot 4a + b (g = l/32), and the
-// other operand is loaded with the same row-to-slot map (two 8-byte LDS reads).
+// column l%32, rows 8(i/4) + 4(l/32) + i%4 in register i. An accumulator used
+// as an operand of a contraction over its rows therefore carries, for the
+// 16-wide step h, rows 16h + 8a + 4g + b in slot 4a + b (g = l/32); the other
+// operand is read with the same row-to-slot map. Operands that contract over
+// tokens (V^T, K^T) come from the row-major tiles through ds_read_b64_tr_b16:
+// within a 16-lane group, lanes 4s + q address token T0 + s at columns
+// c0 + 4q, and lane i receives column c0 + i of the four tokens T0..T0+3.
 // Per tile and owner wave:
 //   O^T  = S^T Q^T            A = state (bf16 hi + lo pair), B = Q
-//   P^T  = mask(K Q^T)        scores, kept in registers; the gate is added to
-//                             the diagonal before the mask, so P V carries it
-//   O^T += V^T P^T            A = V^T, B = scores as bf16
+//   O^T += V^T P^T            A = V^T, B = P^T from the producer
 //   S    = lam^C S + K^T V - K^T (c * V),   c_j = 1 - lam^(C_c-1-j)
 // The output tile is O^T (lane = token), so a lane stores 4 adjacent bf16
 // columns at a time. The decayed values enter the state update as the exact
@@ -56,12 +65,16 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int C = 64;             // tokens per tile
 constexpr int NOW = 3;            // column-owner waves
 constexpr int DVS = 32 * NOW;     // value columns per workgroup
 constexpr int NTHREADS = 64 * (NOW + 1);
 constexpr int PRODUCER = NOW;     // wave index of the producer
+constexpr int NR = 3;             // LDS ring depth (tiles)
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -74,12 +87,6 @@ __device__ __forceinline__ uint32_t pack2(float a, float b)
     return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ __forceinline__ bf16x8_t frag(u32x2_t lo, u32x2_t hi)
-{
-    u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
-    return __builtin_bit_cast(bf16x8_t, w);
-}
-
 __device__ __forceinline__ f32x16_t mma(bf16x8_t a, bf16x8_t b, f32x16_t c)
 {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -88,8 +95,7 @@ __device__ __forceinline__ f32x16_t mma(bf16x8_t a, bf16x8_t b, f32x16_t c)
 // Row of accumulator register i for lane group g.
 __device__ __forceinline__ constexpr int acc_row(int i, int g) { return 8 * (i >> 2) + 4 * g + (i & 3); }
 
-// Barrier for LDS hand-offs: waits for this wave's LDS operations only, so
-// outstanding global loads (the producer's prefetch) stay in flight.
+// Barrier for LDS hand-offs: waits for this wave's LDS operations only.
 __device__ __forceinline__ void lds_barrier()
 {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -103,26 +109,62 @@ __device__ __forceinline__ float sigmoid_f(float z)
     return z >= 0.0f ? r : e * r;
 }
 
+// Segment permutation of a tile row: segment c of row r lives at c ^ sw(r).
+__device__ __forceinline__ int sw(int r)
+{
+    const int x = (r >> 1) & 3;
+    return ((x & 1) << 1) | (x >> 1);
+}
+
+// Byte offset of element e of row r in a swizzled tile with SEG 16-byte segments per row.
+template <int SEG>
+__device__ __forceinline__ int toff(int r, int e)
+{
+    return r * (SEG * 16) + (((e >> 3) ^ sw(r)) << 4) + ((e & 7) << 1);
+}
+
+__device__ __forceinline__ u32x2_t lds_u32x2(const char* base, int off)
+{
+    return *reinterpret_cast<const u32x2_t*>(base + off);
+}
+
+// Four tokens T0..T0+3 of column c0 + (lane % 16): the lane of a 16-lane group
+// passes the address of token T0 + (lane % 16) / 4, columns c0 + 4 (lane % 4).
+template <int SEG>
+__device__ __forceinline__ u32x2_t tr_read(const char* tile, int T0, int c0, int lane)
+{
+    const int j = lane & 15;
+    const int off = toff<SEG>(T0 + (j >> 2), c0 + 4 * (j & 3));
+    const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4_t*)(tile + off));
+    return __builtin_bit_cast(u32x2_t, v);
+}
+
+__device__ __forceinline__ bf16x8_t frag(u32x2_t lo, u32x2_t hi)
+{
+    u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
+    return __builtin_bit_cast(bf16x8_t, w);
+}
+
 template <int DK>
 struct Lay {
     static constexpr int NDB = DK / 32;        // 32-row blocks of the state
-    static constexpr int NSEG = DK / 8;        // 16-byte segments of a q/k row
-    static constexpr int LDQ = DK + 4;         // Q, K row stride (elements): 8 x odd bytes
-    static constexpr int LDT = C + 4;          // K^T, V^T row stride: 136 bytes
-    static constexpr int SZ_Q = C * LDQ * 2;
-    static constexpr int SZ_KT = DK * LDT * 2;
-    static constexpr int SZ_VT = DVS * LDT * 2;
-    static constexpr int OFF_Q = 0;
-    static constexpr int OFF_K = OFF_Q + SZ_Q;
-    static constexpr int OFF_KT = OFF_K + SZ_Q;
-    static constexpr int OFF_VT = OFF_KT + SZ_KT;
-    static constexpr int OFF_G = OFF_VT + SZ_VT;   // gate sigmoid(z) [C]
-    static constexpr int STAGE = OFF_G + C * 4;
-    static constexpr int OFF_CORR = 2 * STAGE;     // c_j for a full tile and the last tile [2][C]
+    static constexpr int SEGK = DK / 8;        // 16-byte segments of a q/k row
+    static constexpr int SEGV = DVS / 8;       // ... of a v row
+    static constexpr int SZ_Q = C * DK * 2;
+    static constexpr int SZ_V = C * DVS * 2;
+    static constexpr int SLOT = 2 * SZ_Q + SZ_V;  // Q, K, V of one tile
+    static constexpr int OFF_P = NR * SLOT;       // 2 x [3 score tiles][2 steps][64 lanes][16 B]
+    static constexpr int SZ_P = 3 * 2 * 64 * 16;
+    static constexpr int OFF_G = OFF_P + 2 * SZ_P;   // producer scratch: gate [C]
+    static constexpr int OFF_A = OFF_G + C * 4;      // aug_balance of the head [DK]
+    static constexpr int OFF_CORR = OFF_A + DK * 4;  // c_j for a full and the last tile [2][C]
     static constexpr int LDS = OFF_CORR + 2 * C * 4;
-    static constexpr int NQI = NSEG / 4;           // producer q/k items per lane
-    static constexpr int NVI = DVS / 8 / 4;        // producer v items per lane (3)
+    static constexpr int NLQ = SZ_Q / 1024;          // 1 KB load instructions per q (or k) tile
+    static constexpr int NLV = SZ_V / 1024;
+    static constexpr int NLOAD = 2 * NLQ + NLV;
     static_assert(DK % 32 == 0 && DK <= 96, "DK");
+    static_assert(NLOAD <= 63, "vmcnt");
     static_assert(LDS <= 160 * 1024, "LDS");
 };
 
@@ -139,11 +181,17 @@ struct Args {
     int H, T, n_units, nsl, dkr, dvr;
 };
 
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 template <int DK>
 __global__ __launch_bounds__(NTHREADS) void k_fwd(Args p)
 {
     typedef Lay<DK> Ly;
-    constexpr int NDB = Ly::NDB, LDQ = Ly::LDQ, LDT = Ly::LDT;
+    constexpr int NDB = Ly::NDB, SEGK = Ly::SEGK, SEGV = Ly::SEGV;
     __shared__ __attribute__((aligned(16))) char smem[Ly::LDS];
 
     // blockIdx -> (unit, slice); the slices of one unit share an XCD (blocks
@@ -186,135 +234,155 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd(Args p)
         const int m = cl - 1 - j;
         corr[i] = (j < cl) ? ((m == 0) ? 0.0f : 1.0f - __builtin_amdgcn_exp2f((float)m * l2)) : 0.0f;
     }
+    float* a_lds = reinterpret_cast<float*>(smem + Ly::OFF_A);
+    for (int i = tid; i < DK; i += NTHREADS)
+        a_lds[i] = (p.a != nullptr && i < dkr) ? p.a[(size_t)h * dkr + i] : 0.0f;
 
     if (wave == PRODUCER) {
         // ------------------------------------------------------------ producer
-        constexpr int NQI = Ly::NQI, NVI = Ly::NVI;
-        const int tg = lane & 15, cb = lane >> 4;   // token group of 4, first segment
-        float av[NQI][8];
+        // tile c -> ring slot c % NR, global rows row0 + 64 c + r (the last
+        // tile's rows past the sequence are clamped, then zeroed in LDS)
+        auto issue = [&](int c) {
+            char* st = smem + (c % NR) * Ly::SLOT;
+            const int cl = min(C, len - c * C);
+            const uint16_t* qb = p.q + (row0 + (long)c * C) * dkr;
+            const uint16_t* kb = p.k + (row0 + (long)c * C) * dkr;
+            const uint16_t* vb = p.v + (row0 + (long)c * C) * dvr;
 #pragma unroll
-        for (int m = 0; m < NQI; ++m)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int col = 8 * (cb + 4 * m) + e;
-                av[m][e] = (p.a != nullptr && col < dkr) ? p.a[(size_t)h * dkr + col] : 0.0f;
+            for (int m = 0; m < Ly::NLQ; ++m) {
+                const int P = 64 * m + lane;              // physical 16-byte slot
+                const int r = P / SEGK;
+                const int cs = (P - r * SEGK) ^ sw(r);    // logical segment
+                const int off = min(r, cl - 1) * dkr + min(8 * cs, dkr - 8);
+                __builtin_amdgcn_global_load_lds(qb + off, (lds_void*)(st + 1024 * m), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(kb + off, (lds_void*)(st + Ly::SZ_Q + 1024 * m), 16, 0, 0);
             }
-        u32x4_t rq[NQI][4], rk[NQI][4], rv[NVI][4];
-        // rows 4 tg + r of tile c; clamped into the sequence only on the last tile
-        auto load = [&](int c) {
-            const int cs0 = c * C;
-            const bool last = (c == nch - 1);
-            const int cl = min(C, len - cs0);
-            const uint16_t* qb = p.q + (row0 + cs0) * dkr;
-            const uint16_t* kb = p.k + (row0 + cs0) * dkr;
-            const uint16_t* vb = p.v + (row0 + cs0) * dvr;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int rr = last ? min(4 * tg + r, cl - 1) : 4 * tg + r;
-#pragma unroll
-                for (int m = 0; m < NQI; ++m) {
-                    const int col = min(8 * (cb + 4 * m), dkr - 8);
-                    rq[m][r] = *reinterpret_cast<const u32x4_t*>(qb + rr * dkr + col);
-                    rk[m][r] = *reinterpret_cast<const u32x4_t*>(kb + rr * dkr + col);
-                }
-#pragma unroll
-                for (int m = 0; m < NVI; ++m) {
-                    const int col = min(n0 + 8 * (cb + 4 * m), dvr - 8);
-                    rv[m][r] = *reinterpret_cast<const u32x4_t*>(vb + rr * dvr + col);
-                }
+            for (int m = 0; m < Ly::NLV; ++m) {
+                const int P = 64 * m + lane;
+                const int r = P / SEGV;
+                const int cs = (P - r * SEGV) ^ sw(r);
+                const int off = min(r, cl - 1) * dvr + min(n0 + 8 * cs, dvr - 8);
+                __builtin_amdgcn_global_load_lds(vb + off, (lds_void*)(st + 2 * Ly::SZ_Q + 1024 * m), 16, 0, 0);
             }
         };
-        // low halves of x, y -> one word (x low); high halves likewise
-        auto lo2 = [](uint32_t x, uint32_t y) { return __builtin_amdgcn_perm(y, x, 0x05040100u); };
-        auto hi2 = [](uint32_t x, uint32_t y) { return __builtin_amdgcn_perm(y, x, 0x07060302u); };
-        auto put = [&](int c) {
-            char* st = smem + (c & 1) * Ly::STAGE;
-            uint16_t* Qs = reinterpret_cast<uint16_t*>(st + Ly::OFF_Q);
-            uint16_t* Ks = reinterpret_cast<uint16_t*>(st + Ly::OFF_K);
-            uint16_t* KT = reinterpret_cast<uint16_t*>(st + Ly::OFF_KT);
-            uint16_t* VT = reinterpret_cast<uint16_t*>(st + Ly::OFF_VT);
-            float* gate = reinterpret_cast<float*>(st + Ly::OFF_G);
+        // rows past the tile and columns past the real widths read as zero
+        auto fixup = [&](int c) {
             const int cl = min(C, len - c * C);
+            if (cl == C && dkr == DK && n0 + DVS <= dvr) return;
+            char* st = smem + (c % NR) * Ly::SLOT;
             const u32x4_t zero = {0u, 0u, 0u, 0u};
-            if (cl < C || dkr < DK || n0 + DVS > dvr) {
-                // rows past the tile and columns past the real widths read as zero
-#pragma unroll
-                for (int m = 0; m < NQI; ++m)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const bool okq = (4 * tg + r < cl) && (8 * (cb + 4 * m) < dkr);
-                        rq[m][r] = okq ? rq[m][r] : zero;
-                        rk[m][r] = okq ? rk[m][r] : zero;
-                    }
-#pragma unroll
-                for (int m = 0; m < NVI; ++m)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const bool okv = (4 * tg + r < cl) && (n0 + 8 * (cb + 4 * m) < dvr);
-                        rv[m][r] = okv ? rv[m][r] : zero;
-                    }
+            for (int P = lane; P < C * SEGK; P += 64) {
+                const int r = P / SEGK;
+                const int cs = (P - r * SEGK) ^ sw(r);
+                if (r >= cl || 8 * cs >= dkr) {
+                    *reinterpret_cast<u32x4_t*>(st + 16 * P) = zero;
+                    *reinterpret_cast<u32x4_t*>(st + Ly::SZ_Q + 16 * P) = zero;
+                }
             }
-            float z[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int P = lane; P < C * SEGV; P += 64) {
+                const int r = P / SEGV;
+                const int cs = (P - r * SEGV) ^ sw(r);
+                if (r >= cl || n0 + 8 * cs >= dvr)
+                    *reinterpret_cast<u32x4_t*>(st + 2 * Ly::SZ_Q + 16 * P) = zero;
+            }
+        };
+
+        // decay-and-mask factors of the score tiles (constant over tiles):
+        // diagonal tile: lam^(t-j) for j <= t else 0; below it: lam^(32 + t - j)
+        float dmd[16], dmo[16];
 #pragma unroll
-            for (int m = 0; m < NQI; ++m) {
-                const int col = 8 * (cb + 4 * m);
+        for (int i = 0; i < 16; ++i) {
+            const int diff = l32 - acc_row(i, g);
+            dmd[i] = diff < 0 ? 0.0f : (diff == 0 ? 1.0f : __builtin_amdgcn_exp2f((float)diff * l2));
+            dmo[i] = __builtin_amdgcn_exp2f((float)(32 + diff) * l2);
+        }
+        float* gsc = reinterpret_cast<float*>(smem + Ly::OFF_G);
+
+        // gate and masked scores of tile c (its loads have landed)
+        auto scores = [&](int c) {
+            const char* st = smem + (c % NR) * Ly::SLOT;
+            const char* Qs = st;
+            const char* Ks = st + Ly::SZ_Q;
+            // gate: lane t sums a_d q_td k_td over its row
+            {
+                float z = 0.0f;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int ro = (4 * tg + r) * LDQ + col;
-                    *reinterpret_cast<u32x2_t*>(Qs + ro) = u32x2_t{rq[m][r][0], rq[m][r][1]};
-                    *reinterpret_cast<u32x2_t*>(Qs + ro + 4) = u32x2_t{rq[m][r][2], rq[m][r][3]};
-                    *reinterpret_cast<u32x2_t*>(Ks + ro) = u32x2_t{rk[m][r][0], rk[m][r][1]};
-                    *reinterpret_cast<u32x2_t*>(Ks + ro + 4) = u32x2_t{rk[m][r][2], rk[m][r][3]};
-                    // gate argument z = sum_d a_d q_d k_d in fp32 (the bf16 dot2 builtin is
-                    // not used: this compiler feeds it element 0 of a vector for every element)
+                for (int cs = 0; cs < SEGK; ++cs) {
+                    const int off = lane * (SEGK * 16) + ((cs ^ sw(lane)) << 4);
+                    const u32x4_t qw = *reinterpret_cast<const u32x4_t*>(Qs + off);
+                    const u32x4_t kw = *reinterpret_cast<const u32x4_t*>(Ks + off);
+                    const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(a_lds + 8 * cs);
+                    const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(a_lds + 8 * cs + 4);
 #pragma unroll
                     for (int w2 = 0; w2 < 4; ++w2) {
-                        const uint32_t qw = rq[m][r][w2], kw = rk[m][r][w2];
-                        z[r] = fmaf(av[m][2 * w2], bf_lo(qw) * bf_lo(kw), z[r]);
-                        z[r] = fmaf(av[m][2 * w2 + 1], bf_hi(qw) * bf_hi(kw), z[r]);
+                        const float alo = (w2 < 2) ? a0[2 * w2] : a1[2 * w2 - 4];
+                        const float ahi = (w2 < 2) ? a0[2 * w2 + 1] : a1[2 * w2 - 3];
+                        z = fmaf(alo, bf_lo(qw[w2]) * bf_lo(kw[w2]), z);
+                        z = fmaf(ahi, bf_hi(qw[w2]) * bf_hi(kw[w2]), z);
                     }
                 }
-                // K^T: column d of four consecutive tokens in one 8-byte write
+                gsc[lane] = sigmoid_f(z);
+            }
+            char* Pb = smem + Ly::OFF_P + (c & 1) * Ly::SZ_P;
 #pragma unroll
-                for (int w2 = 0; w2 < 4; ++w2) {
-                    const uint32_t k0 = rk[m][0][w2], k1 = rk[m][1][w2], k2 = rk[m][2][w2], k3 = rk[m][3][w2];
-                    *reinterpret_cast<u32x2_t*>(KT + (col + 2 * w2) * LDT + 4 * tg) = u32x2_t{lo2(k0, k1), lo2(k2, k3)};
-                    *reinterpret_cast<u32x2_t*>(KT + (col + 2 * w2 + 1) * LDT + 4 * tg) = u32x2_t{hi2(k0, k1), hi2(k2, k3)};
+            for (int s = 0; s < 2; ++s) {
+                // Q rows of the strip as B operands (lane group g: d = 16 kb + 8 g + 0..7)
+                bf16x8_t qf[DK / 16];
+#pragma unroll
+                for (int kb = 0; kb < DK / 16; ++kb)
+                    qf[kb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
+                                                              Qs + toff<SEGK>(32 * s + l32, 16 * kb + 8 * g)));
+                const float gt = gsc[32 * s + l32];
+#pragma unroll
+                for (int jb = 0; jb <= s; ++jb) {
+                    f32x16_t sc;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) sc[i] = (jb == s && acc_row(i, g) == l32) ? gt : 0.0f;
+#pragma unroll
+                    for (int kb = 0; kb < DK / 16; ++kb) {
+                        const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
+                                                                             Ks + toff<SEGK>(32 * jb + l32, 16 * kb + 8 * g)));
+                        sc = mma(kf, qf[kb], sc);
+                    }
+                    // sc[i]: column t, key 32 jb + acc_row(i, g); the gate sits on the diagonal
+                    const int tile = s + jb;  // (0,0) -> 0, (1,0) -> 1, (1,1) -> 2
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        u32x4_t pw;
+#pragma unroll
+                        for (int s2 = 0; s2 < 4; ++s2) {
+                            const int i0 = 8 * hh + 2 * s2;
+                            const float m0 = (jb == s) ? dmd[i0] : dmo[i0];
+                            const float m1 = (jb == s) ? dmd[i0 + 1] : dmo[i0 + 1];
+                            pw[s2] = pack2(sc[i0] * m0, sc[i0 + 1] * m1);
+                        }
+                        *reinterpret_cast<u32x4_t*>(Pb + ((tile * 2 + hh) * 64 + lane) * 16) = pw;
+                    }
                 }
-            }
-#pragma unroll
-            for (int m = 0; m < NVI; ++m) {
-                const int col = 8 * (cb + 4 * m);
-#pragma unroll
-                for (int w2 = 0; w2 < 4; ++w2) {
-                    const uint32_t v0 = rv[m][0][w2], v1 = rv[m][1][w2], v2 = rv[m][2][w2], v3 = rv[m][3][w2];
-                    *reinterpret_cast<u32x2_t*>(VT + (col + 2 * w2) * LDT + 4 * tg) = u32x2_t{lo2(v0, v1), lo2(v2, v3)};
-                    *reinterpret_cast<u32x2_t*>(VT + (col + 2 * w2 + 1) * LDT + 4 * tg) = u32x2_t{hi2(v0, v1), hi2(v2, v3)};
-                }
-            }
-            // the four lanes sharing a token group hold the partial sums of all segments
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                z[r] += __shfl_xor(z[r], 16);
-                z[r] += __shfl_xor(z[r], 32);
-            }
-            if (cb == 0) {
-                f32x4_t gv;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) gv[r] = sigmoid_f(z[r]);
-                *reinterpret_cast<f32x4_t*>(gate + 4 * tg) = gv;
             }
         };
 
         if (nch > 0) {
-            load(0);
-            put(0);
-            if (nch > 1) load(1);
+            issue(0);
+            if (nch > 1) {
+                issue(1);
+                wait_vm<Ly::NLOAD>();
+            } else {
+                wait_vm<0>();
+            }
+            fixup(0);
+            scores(0);
         }
         lds_barrier();
         for (int c = 0; c < nch; ++c) {
-            if (c + 1 < nch) put(c + 1);
-            if (c + 2 < nch) load(c + 2);
+            if (c + 2 < nch) issue(c + 2);
+            if (c + 1 < nch) {
+                if (c + 2 < nch) wait_vm<Ly::NLOAD>();
+                else wait_vm<0>();
+                fixup(c + 1);
+                scores(c + 1);
+            }
             lds_barrier();
         }
         return;
@@ -335,48 +403,23 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd(Args p)
                               ? p.s_init[sbase + (size_t)d * dvr + ncol] : 0.0f;
         }
     }
-
-    // decay-and-mask factors of the score tiles (constant over tiles):
-    // diagonal tile: lam^(t-j) for j <= t else 0; below it: lam^(32 + t - j)
-    float dmd[16], dmo[16];
-    bool dsel[16];  // the diagonal element of this lane's column
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int diff = l32 - acc_row(i, g);
-        dmd[i] = diff < 0 ? 0.0f : (diff == 0 ? 1.0f : __builtin_amdgcn_exp2f((float)diff * l2));
-        dmo[i] = __builtin_amdgcn_exp2f((float)(32 + diff) * l2);
-        dsel[i] = (diff == 0);
-    }
     // readout decays lam^(t+1) of this lane's token in each 32-row strip
     const float tdec0 = __builtin_amdgcn_exp2f((float)(l32 + 1) * l2);
     const float tdec1 = __builtin_amdgcn_exp2f((float)(l32 + 33) * l2);
 
     lds_barrier();
     for (int c = 0; c < nch; ++c) {
-        const char* st = smem + (c & 1) * Ly::STAGE;
-        const uint16_t* Qs = reinterpret_cast<const uint16_t*>(st + Ly::OFF_Q);
-        const uint16_t* Ks = reinterpret_cast<const uint16_t*>(st + Ly::OFF_K);
-        const uint16_t* KT = reinterpret_cast<const uint16_t*>(st + Ly::OFF_KT);
-        const uint16_t* VT = reinterpret_cast<const uint16_t*>(st + Ly::OFF_VT);
-        const float* gate = reinterpret_cast<const float*>(st + Ly::OFF_G);
+        const char* st = smem + (c % NR) * Ly::SLOT;
+        const char* Qs = st;
+        const char* Ks = st + Ly::SZ_Q;
+        const char* Vs = st + 2 * Ly::SZ_Q;
+        const char* Pb = smem + Ly::OFF_P + (c & 1) * Ly::SZ_P;
         const int cstart = c * C;
         const int cl = min(C, len - cstart);
         const float* cf = corr + ((c == nch - 1) ? C : 0);
 
-        // V^T operand fragments of this lane's column, tokens 16 kb + 8a + 4g + b
-        bf16x8_t vf[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const uint16_t* vr = VT + nloc * LDT + 16 * kb + 4 * g;
-            vf[kb] = frag(*reinterpret_cast<const u32x2_t*>(vr), *reinterpret_cast<const u32x2_t*>(vr + 8));
-        }
-        auto qfrag = [&](int t, int db, int hh) {
-            const uint16_t* qr = Qs + t * LDQ + 32 * db + 16 * hh + 4 * g;
-            return frag(*reinterpret_cast<const u32x2_t*>(qr), *reinterpret_cast<const u32x2_t*>(qr + 8));
-        };
-
         // ---- readout of the carried state, both strips: O^T = S^T Q^T with the
-        // state as a bf16 hi + lo pair (A operand), built once per tile
+        // state as a bf16 hi + lo pair (A operand)
         f32x16_t oq[2] = {};
         {
             bf16x8_t sh[NDB][2], sl[NDB][2];
@@ -401,52 +444,36 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd(Args p)
                 for (int db = 0; db < NDB; ++db)
 #pragma unroll
                     for (int hh = 0; hh < 2; ++hh) {
-                        const bf16x8_t qf = qfrag(32 * s + l32, db, hh);
+                        // Q row t, d = 32 db + 16 hh + 8a + 4g + b in slot 4a + b
+                        const int t = 32 * s + l32;
+                        const bf16x8_t qf = frag(lds_u32x2(Qs, toff<SEGK>(t, 32 * db + 16 * hh + 4 * g)),
+                                                 lds_u32x2(Qs, toff<SEGK>(t, 32 * db + 16 * hh + 8 + 4 * g)));
                         oq[s] = mma(sh[db][hh], qf, oq[s]);
                         oq[s] = mma(sl[db][hh], qf, oq[s]);
                     }
         }
 
-        // ---- intra-tile part of the two 32-token strips (a strip past a short
-        // last tile computes on zeros; its stores are masked)
+        // V^T fragments of this lane's column: tokens 16 kb + 8a + 4g + b in slot 4a + b
+        bf16x8_t vf[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+            vf[kb] = frag(tr_read<SEGV>(Vs, 16 * kb + 4 * g, 32 * wave + 16 * ((lane >> 4) & 1), lane),
+                          tr_read<SEGV>(Vs, 16 * kb + 8 + 4 * g, 32 * wave + 16 * ((lane >> 4) & 1), lane));
+
+        // ---- intra-tile part: O^T += V^T P^T (a strip past a short last tile
+        // computes on zeros; its stores are masked)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const int t = 32 * s + l32;
-            bf16x8_t qf[NDB][2];
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) qf[db][hh] = qfrag(t, db, hh);
             f32x16_t o = {};
-            const float gt = gate[t];
 #pragma unroll
-            for (int jb = 0; jb <= s; ++jb) {
-                f32x16_t sc;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) sc[i] = (jb == s && dsel[i]) ? gt : 0.0f;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        const uint16_t* kr = Ks + (32 * jb + l32) * LDQ + 32 * db + 16 * hh + 4 * g;
-                        const bf16x8_t kf = frag(*reinterpret_cast<const u32x2_t*>(kr),
-                                                 *reinterpret_cast<const u32x2_t*>(kr + 8));
-                        sc = mma(kf, qf[db][hh], sc);
-                    }
-                // sc[i]: column t, key 32 jb + acc_row(i, g); the gate sits on the diagonal
+            for (int jb = 0; jb <= s; ++jb)
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
-                    u32x4_t pw;
-#pragma unroll
-                    for (int s2 = 0; s2 < 4; ++s2) {
-                        const int i0 = 8 * hh + 2 * s2;
-                        const float m0 = (jb == s) ? dmd[i0] : dmo[i0];
-                        const float m1 = (jb == s) ? dmd[i0 + 1] : dmo[i0 + 1];
-                        pw[s2] = pack2(sc[i0] * m0, sc[i0 + 1] * m1);
-                    }
-                    o = mma(vf[2 * jb + hh], __builtin_bit_cast(bf16x8_t, pw), o);
+                    const bf16x8_t pf = __builtin_bit_cast(
+                        bf16x8_t, *reinterpret_cast<const u32x4_t*>(Pb + (((s + jb) * 2 + hh) * 64 + lane) * 16));
+                    o = mma(vf[2 * jb + hh], pf, o);
                 }
-            }
             // O^T: lane = token t, registers = columns 32 wave + acc_row(i, g)
             const float td = s ? tdec1 : tdec0;
             if (t < cl) {
@@ -464,8 +491,7 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd(Args p)
         }
 
         // ---- state advance: S = lam^cl S + K^T V - K^T (c V)
-        const float fcl = (cl == C) ? __builtin_amdgcn_exp2f((float)C * l2)
-                                    : __builtin_amdgcn_exp2f((float)cl * l2);
+        const float fcl = __builtin_amdgcn_exp2f((float)cl * l2);
         bf16x8_t vc[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
@@ -485,9 +511,9 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd(Args p)
             for (int i = 0; i < 16; ++i) sacc[db][i] *= fcl;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-                const uint16_t* kr = KT + (32 * db + l32) * LDT + 16 * kb + 4 * g;
-                const bf16x8_t kf = frag(*reinterpret_cast<const u32x2_t*>(kr),
-                                         *reinterpret_cast<const u32x2_t*>(kr + 8));
+                // K^T fragment: key column 32 db + l32, tokens 16 kb + 8a + 4g + b
+                const bf16x8_t kf = frag(tr_read<SEGK>(Ks, 16 * kb + 4 * g, 32 * db + 16 * ((lane >> 4) & 1), lane),
+                                         tr_read<SEGK>(Ks, 16 * kb + 8 + 4 * g, 32 * db + 16 * ((lane >> 4) & 1), lane));
                 sacc[db] = mma(kf, vf[kb], sacc[db]);
                 sacc[db] = mma(kf, vc[kb], sacc[db]);
             }
