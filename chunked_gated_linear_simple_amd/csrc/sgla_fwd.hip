@@ -55,6 +55,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "sgla_internal.h"
 
 namespace sgla {
@@ -123,6 +125,13 @@ __device__ __forceinline__ int toff(int r, int e)
     return r * (SEG * 16) + (((e >> 3) ^ sw(r)) << 4) + ((e & 7) << 1);
 }
 
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at dst + 16 l (global_load_lds_dwordx4; completion is counted by vmcnt).
+__device__ __forceinline__ void dma16(const uint16_t* src, char* dst)
+{
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+}
+
 __device__ __forceinline__ u32x2_t lds_u32x2(const char* base, int off)
 {
     return *reinterpret_cast<const u32x2_t*>(base + off);
@@ -156,9 +165,7 @@ struct Lay {
     static constexpr int SLOT = 2 * SZ_Q + SZ_V;  // Q, K, V of one tile
     static constexpr int OFF_P = NR * SLOT;       // 2 x [3 score tiles][2 steps][64 lanes][16 B]
     static constexpr int SZ_P = 3 * 2 * 64 * 16;
-    static constexpr int OFF_G = OFF_P + 2 * SZ_P;   // producer scratch: gate [C]
-    static constexpr int OFF_A = OFF_G + C * 4;      // aug_balance of the head [DK]
-    static constexpr int OFF_CORR = OFF_A + DK * 4;  // c_j for a full and the last tile [2][C]
+    static constexpr int OFF_CORR = OFF_P + 2 * SZ_P;  // c_j for a full and the last tile [2][C]
     static constexpr int LDS = OFF_CORR + 2 * C * 4;
     static constexpr int NLQ = SZ_Q / 1024;          // 1 KB load instructions per q (or k) tile
     static constexpr int NLV = SZ_V / 1024;
@@ -234,37 +241,45 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd(Args p)
         const int m = cl - 1 - j;
         corr[i] = (j < cl) ? ((m == 0) ? 0.0f : 1.0f - __builtin_amdgcn_exp2f((float)m * l2)) : 0.0f;
     }
-    float* a_lds = reinterpret_cast<float*>(smem + Ly::OFF_A);
-    for (int i = tid; i < DK; i += NTHREADS)
-        a_lds[i] = (p.a != nullptr && i < dkr) ? p.a[(size_t)h * dkr + i] : 0.0f;
 
     if (wave == PRODUCER) {
         // ------------------------------------------------------------ producer
         // tile c -> ring slot c % NR, global rows row0 + 64 c + r (the last
         // tile's rows past the sequence are clamped, then zeroed in LDS)
-        auto issue = [&](int c) {
-            char* st = smem + (c % NR) * Ly::SLOT;
-            const int cl = min(C, len - c * C);
-            const uint16_t* qb = p.q + (row0 + (long)c * C) * dkr;
-            const uint16_t* kb = p.k + (row0 + (long)c * C) * dkr;
-            const uint16_t* vb = p.v + (row0 + (long)c * C) * dvr;
+        // per-lane element offsets of the 1 KB load blocks within a tile (rows
+        // clamped to the tile length, columns to the real widths)
+        int offq[Ly::NLQ], offv[Ly::NLV];
+        auto offsets = [&](int cl) {
 #pragma unroll
             for (int m = 0; m < Ly::NLQ; ++m) {
                 const int P = 64 * m + lane;              // physical 16-byte slot
                 const int r = P / SEGK;
                 const int cs = (P - r * SEGK) ^ sw(r);    // logical segment
-                const int off = min(r, cl - 1) * dkr + min(8 * cs, dkr - 8);
-                __builtin_amdgcn_global_load_lds(qb + off, (lds_void*)(st + 1024 * m), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(kb + off, (lds_void*)(st + Ly::SZ_Q + 1024 * m), 16, 0, 0);
+                offq[m] = min(r, cl - 1) * dkr + min(8 * cs, dkr - 8);
             }
 #pragma unroll
             for (int m = 0; m < Ly::NLV; ++m) {
                 const int P = 64 * m + lane;
                 const int r = P / SEGV;
                 const int cs = (P - r * SEGV) ^ sw(r);
-                const int off = min(r, cl - 1) * dvr + min(n0 + 8 * cs, dvr - 8);
-                __builtin_amdgcn_global_load_lds(vb + off, (lds_void*)(st + 2 * Ly::SZ_Q + 1024 * m), 16, 0, 0);
+                offv[m] = min(r, cl - 1) * dvr + min(n0 + 8 * cs, dvr - 8);
             }
+        };
+        offsets(nch > 1 ? C : clast);
+        auto issue = [&](int c) {
+            char* st = smem + (c % NR) * Ly::SLOT;
+            if (c == nch - 1 && clast < C) offsets(clast);
+            const uint16_t* qb = p.q + (row0 + (long)c * C) * dkr;
+            const uint16_t* kb = p.k + (row0 + (long)c * C) * dkr;
+            const uint16_t* vb = p.v + (row0 + (long)c * C) * dvr;
+#pragma unroll
+            for (int m = 0; m < Ly::NLQ; ++m) {
+                dma16(qb + offq[m], st + 1024 * m);
+                dma16(kb + offq[m], st + Ly::SZ_Q + 1024 * m);
+            }
+#pragma unroll
+            for (int m = 0; m < Ly::NLV; ++m)
+                dma16(vb + offv[m], st + 2 * Ly::SZ_Q + 1024 * m);
         };
         // rows past the tile and columns past the real widths read as zero
         auto fixup = [&](int c) {
@@ -290,40 +305,37 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd(Args p)
 
         // decay-and-mask factors of the score tiles (constant over tiles):
         // diagonal tile: lam^(t-j) for j <= t else 0; below it: lam^(32 + t - j)
-        float dmd[16], dmo[16];
+        float dmd[16], dmo[16], dsel[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int diff = l32 - acc_row(i, g);
             dmd[i] = diff < 0 ? 0.0f : (diff == 0 ? 1.0f : __builtin_amdgcn_exp2f((float)diff * l2));
             dmo[i] = __builtin_amdgcn_exp2f((float)(32 + diff) * l2);
+            dsel[i] = (diff == 0) ? 1.0f : 0.0f;   // this lane's diagonal element
         }
-        float* gsc = reinterpret_cast<float*>(smem + Ly::OFF_G);
+        // diag(a) as A operands: lane (row d = 32 db + l32, group g) holds, for
+        // the 16-wide step h, slots d' = 32 db + 16 h + 8 g + j; only d' = d is
+        // non-zero (a_d rounded to bf16)
+        bf16x8_t adiag[NDB][2];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int j = l32 - 16 * hh - 8 * g;
+                const int dcol = 32 * db + l32;
+                const float ad = (p.a != nullptr && dcol < dkr) ? p.a[(size_t)h * dkr + dcol] : 0.0f;
+                u32x4_t w;
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2)
+                    w[s2] = pack2(j == 2 * s2 ? ad : 0.0f, j == 2 * s2 + 1 ? ad : 0.0f);
+                adiag[db][hh] = __builtin_bit_cast(bf16x8_t, w);
+            }
 
         // gate and masked scores of tile c (its loads have landed)
         auto scores = [&](int c) {
             const char* st = smem + (c % NR) * Ly::SLOT;
             const char* Qs = st;
             const char* Ks = st + Ly::SZ_Q;
-            // gate: lane t sums a_d q_td k_td over its row
-            {
-                float z = 0.0f;
-#pragma unroll
-                for (int cs = 0; cs < SEGK; ++cs) {
-                    const int off = lane * (SEGK * 16) + ((cs ^ sw(lane)) << 4);
-                    const u32x4_t qw = *reinterpret_cast<const u32x4_t*>(Qs + off);
-                    const u32x4_t kw = *reinterpret_cast<const u32x4_t*>(Ks + off);
-                    const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(a_lds + 8 * cs);
-                    const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(a_lds + 8 * cs + 4);
-#pragma unroll
-                    for (int w2 = 0; w2 < 4; ++w2) {
-                        const float alo = (w2 < 2) ? a0[2 * w2] : a1[2 * w2 - 4];
-                        const float ahi = (w2 < 2) ? a0[2 * w2 + 1] : a1[2 * w2 - 3];
-                        z = fmaf(alo, bf_lo(qw[w2]) * bf_lo(kw[w2]), z);
-                        z = fmaf(ahi, bf_hi(qw[w2]) * bf_hi(kw[w2]), z);
-                    }
-                }
-                gsc[lane] = sigmoid_f(z);
-            }
             char* Pb = smem + Ly::OFF_P + (c & 1) * Ly::SZ_P;
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
@@ -333,12 +345,40 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd(Args p)
                 for (int kb = 0; kb < DK / 16; ++kb)
                     qf[kb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
                                                               Qs + toff<SEGK>(32 * s + l32, 16 * kb + 8 * g)));
-                const float gt = gsc[32 * s + l32];
+                // gate argument on the matrix cores: Q'^T = diag(a) Q^T (a one-hot A
+                // operand per 16-wide step), then z_t = (K Q'^T)[t][t]
+                float gt;
+                {
+                    f32x16_t zt = {};
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        f32x16_t qa = {};
+                        qa = mma(adiag[db][0], qf[2 * db], qa);
+                        qa = mma(adiag[db][1], qf[2 * db + 1], qa);
+                        // qa[i]: a_d q_td for d = 32 db + acc_row(i, g), column t
+#pragma unroll
+                        for (int hh = 0; hh < 2; ++hh) {
+                            u32x4_t bw;
+#pragma unroll
+                            for (int s2 = 0; s2 < 4; ++s2) bw[s2] = pack2(qa[8 * hh + 2 * s2], qa[8 * hh + 2 * s2 + 1]);
+                            const int e0 = 32 * db + 16 * hh + 4 * g;
+                            const bf16x8_t kz = frag(lds_u32x2(Ks, toff<SEGK>(32 * s + l32, e0)),
+                                                     lds_u32x2(Ks, toff<SEGK>(32 * s + l32, e0 + 8)));
+                            zt = mma(kz, __builtin_bit_cast(bf16x8_t, bw), zt);
+                        }
+                    }
+                    // the diagonal element (j = t) sits in one lane group
+                    float z = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) z = fmaf(dsel[i], zt[i], z);
+                    z += __shfl_xor(z, 32);
+                    gt = sigmoid_f(z);
+                }
 #pragma unroll
                 for (int jb = 0; jb <= s; ++jb) {
                     f32x16_t sc;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) sc[i] = (jb == s && acc_row(i, g) == l32) ? gt : 0.0f;
+                    for (int i = 0; i < 16; ++i) sc[i] = (jb == s) ? dsel[i] * gt : 0.0f;
 #pragma unroll
                     for (int kb = 0; kb < DK / 16; ++kb) {
                         const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
@@ -407,58 +447,73 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd(Args p)
     const float tdec0 = __builtin_amdgcn_exp2f((float)(l32 + 1) * l2);
     const float tdec1 = __builtin_amdgcn_exp2f((float)(l32 + 33) * l2);
 
-    lds_barrier();
-    for (int c = 0; c < nch; ++c) {
+    const float fC = __builtin_amdgcn_exp2f((float)C * l2);  // lam^C
+    // one tile; FULL: all 64 tokens and all 96 columns are real (no masking,
+    // so the whole tile is one branch-free scheduling region)
+    auto tile = [&](int c, auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
         const char* st = smem + (c % NR) * Ly::SLOT;
         const char* Qs = st;
         const char* Ks = st + Ly::SZ_Q;
         const char* Vs = st + 2 * Ly::SZ_Q;
         const char* Pb = smem + Ly::OFF_P + (c & 1) * Ly::SZ_P;
         const int cstart = c * C;
-        const int cl = min(C, len - cstart);
-        const float* cf = corr + ((c == nch - 1) ? C : 0);
+        const int cl = FULL ? C : min(C, len - cstart);
+        const float* cf = corr + ((!FULL && c == nch - 1) ? C : 0);
 
-        // ---- readout of the carried state, both strips: O^T = S^T Q^T with the
-        // state as a bf16 hi + lo pair (A operand)
-        f32x16_t oq[2] = {};
-        {
-            bf16x8_t sh[NDB][2], sl[NDB][2];
+        // operand reads of the tile, issued ahead of the math that uses them
+        bf16x8_t kf[NDB][4], vf[4], pf[3][2];
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    u32x4_t hw, lw;
-#pragma unroll
-                    for (int s2 = 0; s2 < 4; ++s2) {
-                        const float x0 = sacc[db][8 * hh + 2 * s2], x1 = sacc[db][8 * hh + 2 * s2 + 1];
-                        const uint32_t hp = pack2(x0, x1);
-                        hw[s2] = hp;
-                        lw[s2] = pack2(x0 - bf_lo(hp), x1 - bf_hi(hp));
-                    }
-                    sh[db][hh] = __builtin_bit_cast(bf16x8_t, hw);
-                    sl[db][hh] = __builtin_bit_cast(bf16x8_t, lw);
-                }
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        // Q row t, d = 32 db + 16 hh + 8a + 4g + b in slot 4a + b
-                        const int t = 32 * s + l32;
-                        const bf16x8_t qf = frag(lds_u32x2(Qs, toff<SEGK>(t, 32 * db + 16 * hh + 4 * g)),
-                                                 lds_u32x2(Qs, toff<SEGK>(t, 32 * db + 16 * hh + 8 + 4 * g)));
-                        oq[s] = mma(sh[db][hh], qf, oq[s]);
-                        oq[s] = mma(sl[db][hh], qf, oq[s]);
-                    }
-        }
-
-        // V^T fragments of this lane's column: tokens 16 kb + 8a + 4g + b in slot 4a + b
-        bf16x8_t vf[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 4; ++kb) {
+            // V^T of this lane's column: tokens 16 kb + 8a + 4g + b in slot 4a + b
             vf[kb] = frag(tr_read<SEGV>(Vs, 16 * kb + 4 * g, 32 * wave + 16 * ((lane >> 4) & 1), lane),
                           tr_read<SEGV>(Vs, 16 * kb + 8 + 4 * g, 32 * wave + 16 * ((lane >> 4) & 1), lane));
+        }
+#pragma unroll
+        for (int tl = 0; tl < 3; ++tl)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                pf[tl][hh] = __builtin_bit_cast(
+                    bf16x8_t, *reinterpret_cast<const u32x4_t*>(Pb + ((tl * 2 + hh) * 64 + lane) * 16));
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                // K^T: key column 32 db + l32, tokens 16 kb + 8a + 4g + b
+                kf[db][kb] = frag(tr_read<SEGK>(Ks, 16 * kb + 4 * g, 32 * db + 16 * ((lane >> 4) & 1), lane),
+                                  tr_read<SEGK>(Ks, 16 * kb + 8 + 4 * g, 32 * db + 16 * ((lane >> 4) & 1), lane));
+
+        // ---- readout of the carried state, both strips: O^T = S^T Q^T, the
+        // state entering as a bf16 hi + lo pair (A operand) built block by
+        // block; each block is then decayed for the state advance
+        const float fcl = FULL ? fC : __builtin_amdgcn_exp2f((float)cl * l2);
+        f32x16_t oq[2] = {};
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                u32x4_t hw, lw;
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) {
+                    const float x0 = sacc[db][8 * hh + 2 * s2], x1 = sacc[db][8 * hh + 2 * s2 + 1];
+                    const uint32_t hp = pack2(x0, x1);
+                    hw[s2] = hp;
+                    lw[s2] = pack2(x0 - bf_lo(hp), x1 - bf_hi(hp));
+                }
+                const bf16x8_t sh = __builtin_bit_cast(bf16x8_t, hw), sl = __builtin_bit_cast(bf16x8_t, lw);
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    // Q row t, d = 32 db + 16 hh + 8a + 4g + b in slot 4a + b
+                    const int t = 32 * s + l32;
+                    const bf16x8_t qf = frag(lds_u32x2(Qs, toff<SEGK>(t, 32 * db + 16 * hh + 4 * g)),
+                                             lds_u32x2(Qs, toff<SEGK>(t, 32 * db + 16 * hh + 8 + 4 * g)));
+                    oq[s] = mma(sh, qf, oq[s]);
+                    oq[s] = mma(sl, qf, oq[s]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sacc[db][i] *= fcl;
+        }
 
         // ---- intra-tile part: O^T += V^T P^T (a strip past a short last tile
         // computes on zeros; its stores are masked)
@@ -469,18 +524,14 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd(Args p)
 #pragma unroll
             for (int jb = 0; jb <= s; ++jb)
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const bf16x8_t pf = __builtin_bit_cast(
-                        bf16x8_t, *reinterpret_cast<const u32x4_t*>(Pb + (((s + jb) * 2 + hh) * 64 + lane) * 16));
-                    o = mma(vf[2 * jb + hh], pf, o);
-                }
+                for (int hh = 0; hh < 2; ++hh) o = mma(vf[2 * jb + hh], pf[s + jb][hh], o);
             // O^T: lane = token t, registers = columns 32 wave + acc_row(i, g)
             const float td = s ? tdec1 : tdec0;
-            if (t < cl) {
+            if (FULL || t < cl) {
                 uint16_t* orow = p.o + (row0 + cstart + t) * dvr + n0 + 32 * wave + 4 * g;
 #pragma unroll
                 for (int qd = 0; qd < 4; ++qd) {
-                    if (n0 + 32 * wave + 8 * qd + 4 * g < dvr) {
+                    if (FULL || n0 + 32 * wave + 8 * qd + 4 * g < dvr) {
                         const int i0 = 4 * qd;
                         u32x2_t w2 = {pack2(fmaf(td, oq[s][i0], o[i0]), fmaf(td, oq[s][i0 + 1], o[i0 + 1])),
                                       pack2(fmaf(td, oq[s][i0 + 2], o[i0 + 2]), fmaf(td, oq[s][i0 + 3], o[i0 + 3]))};
@@ -490,8 +541,7 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd(Args p)
             }
         }
 
-        // ---- state advance: S = lam^cl S + K^T V - K^T (c V)
-        const float fcl = __builtin_amdgcn_exp2f((float)cl * l2);
+        // ---- state advance: S = lam^cl S + K^T V - K^T (c V)  (S already decayed)
         bf16x8_t vc[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
@@ -506,18 +556,19 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd(Args p)
             vc[kb] = __builtin_bit_cast(bf16x8_t, cw);
         }
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sacc[db][i] *= fcl;
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-                // K^T fragment: key column 32 db + l32, tokens 16 kb + 8a + 4g + b
-                const bf16x8_t kf = frag(tr_read<SEGK>(Ks, 16 * kb + 4 * g, 32 * db + 16 * ((lane >> 4) & 1), lane),
-                                         tr_read<SEGK>(Ks, 16 * kb + 8 + 4 * g, 32 * db + 16 * ((lane >> 4) & 1), lane));
-                sacc[db] = mma(kf, vf[kb], sacc[db]);
-                sacc[db] = mma(kf, vc[kb], sacc[db]);
+                sacc[db] = mma(kf[db][kb], vf[kb], sacc[db]);
+                sacc[db] = mma(kf[db][kb], vc[kb], sacc[db]);
             }
-        }
+    };
+
+    const bool cols_full = (n0 + DVS <= dvr);
+    lds_barrier();
+    for (int c = 0; c < nch; ++c) {
+        if (cols_full && (c < nch - 1 || clast == C)) tile(c, std::true_type{});
+        else tile(c, std::false_type{});
         lds_barrier();
     }
 
