@@ -17,7 +17,7 @@ Also measured in the same run and reported under "secondary" (same clock):
   varlen: 32 packed sequences, lengths log-uniform in [128, 32768] (one of
           32768), init states ~ N(0, 0.02), tokens/s = sum T / t
 
-"roofline" is for the dominant kernel of the headline step (k_chunk_fwd):
+"roofline" is for the dominant kernel of the headline step (k_fwd, bf16 forward):
 achieved = algorithmic HBM bytes per launch / mean launch time from HIP events
 on the launch stream. Algorithmic bytes per head-token: q 192 + k 192 + v 384
 + o 384 = 1152 B (bf16), plus the fp32 final state (73,728 B per sequence-head).
@@ -41,15 +41,19 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores
 H, DK, DV = 16, 96, 192
 HT_BYTES = 2 * DK + 2 * DK + 2 * DV + 2 * DV   # q, k, v, o per head-token (bf16)
 STATE_BYTES = DK * DV * 4
+MIN_WARM_S = 1.5               # untimed warm-up floor per workload, seconds
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", choices=["fwd", "fwdbwd", "decode", "varlen"], default=None)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--min-warm-s", type=float, default=1.5,
+                    help="untimed warm-up continues past --warmup steps until this many "
+                         "seconds have passed (clock ramp)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run a plain 1 GiB elementwise copy (read 1 GiB, write 1 GiB) "
                          "so a counter pass can scale FETCH_SIZE / WRITE_SIZE")
@@ -64,12 +68,25 @@ def gen(shape, seed, std=1.0, scale=1.0, dtype=None):
     return x if dtype is None else x.to(dtype)
 
 
-def timed(fn, steps, warmup):
-    """Mean milliseconds per call of fn(i), from HIP events on the current stream."""
+def timed(fn, steps, warmup, min_warm_s=None):
+    """Mean milliseconds per call of fn(i), from HIP events on the current stream.
+
+    Runs `warmup` untimed calls, then keeps calling (untimed) until at least
+    `min_warm_s` seconds of warm-up have passed: the chip's clocks take on the
+    order of a second of sustained load to settle, and a handful of calls
+    measures the ramp instead of the kernel."""
     import torch
-    for i in range(warmup):
+    if min_warm_s is None:
+        min_warm_s = MIN_WARM_S
+    t_w = time.perf_counter()
+    i = 0
+    while i < warmup or time.perf_counter() - t_w < min_warm_s:
         fn(i)
+        i += 1
+        if i >= warmup and i % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    warmup = i
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t0 = time.perf_counter()
@@ -215,7 +232,9 @@ def cpu_baseline(min_seconds=10.0, B=8, T=2048):
 
 
 def main():
+    global MIN_WARM_S
     args = parse()
+    MIN_WARM_S = args.min_warm_s
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -250,7 +269,7 @@ def main():
     line = {"metric": "GLA tokens/s (fwd, fwd+bwd, decode) at H=16 dk=96 dv=192; % MFMA/HBM peak",
             "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-            "warmup": args.warmup, "steps": args.steps}
+            "warmup": args.warmup, "min_warm_s": args.min_warm_s, "steps": args.steps}
     if fwd is not None:
         line.update({
             "value": fwd["tok_s"], "ms_per_step": fwd["ms"],
@@ -258,7 +277,7 @@ def main():
                                    "bf16, fp32 state, final state written",
                        "batch": 8, "seq_len": 2048, "heads": H, "d_k": DK, "d_v": DV,
                        "chunk": 128},
-            "roofline": {"bound": "hbm", "kernel": "k_chunk_fwd", "achieved": fwd["gbs"],
+            "roofline": {"bound": "hbm", "kernel": "k_fwd", "achieved": fwd["gbs"],
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": fwd["gbs"] / HBM_PEAK_GBS,
                          "traffic": None, "bytes_per_launch": fwd["bytes"]},
         })

@@ -10,7 +10,8 @@
 // The step is a pure streaming read-modify-write of the fp32 state (d_k*d_v*4
 // bytes in and out per sequence-head, 0.5 flop/byte), so the kernel is built
 // for HBM bandwidth: one workgroup per (sequence, head); thread (rg, cg) owns
-// four adjacent state columns (one 16-byte vector) in rows rg, rg+RG, ...; all
+// four adjacent state columns (one 16-byte vector) in rows rg, rg+RG, ... (12
+// row groups of 8 rows for a 96 x 192 state, 576 threads); all
 // of its state loads are issued before any use; loads and stores are
 // non-temporal (the pool is far larger than the caches and is not re-read
 // within a step); the readout reduction over rows is per-thread partial sums
@@ -166,8 +167,8 @@ hipError_t launch_decode_step(int bf16, const void* q, const void* k, const void
                               hipStream_t stream)
 {
     if (d_k == 96 && d_v == 192) {
-        if (bf16) return run_decode<u16, 96, 192, 4>(q, k, v, lambda, a, state, slot, o, N, P, H, stream);
-        return run_decode<float, 96, 192, 4>(q, k, v, lambda, a, state, slot, o, N, P, H, stream);
+        if (bf16) return run_decode<u16, 96, 192, 12>(q, k, v, lambda, a, state, slot, o, N, P, H, stream);
+        return run_decode<float, 96, 192, 12>(q, k, v, lambda, a, state, slot, o, N, P, H, stream);
     }
     // d_k == 16 && d_v == 32 (checked by the caller)
     if (bf16) return run_decode<u16, 16, 32, 8>(q, k, v, lambda, a, state, slot, o, N, P, H, stream);
