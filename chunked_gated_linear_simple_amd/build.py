@@ -16,11 +16,12 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsgla.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["sgla_api.cpp", "sgla_chunk.hip", "sgla_fwd.hip", "sgla_decode.hip"]
+SOURCES = ["sgla_api.cpp", "sgla_chunk.hip", "sgla_fwd.hip", "sgla_bwd.hip", "sgla_decode.hip"]
 # Per-source flags. The column-owner kernels keep matrix-core accumulators in
 # architectural VGPRs: their state and output tiles are read by VALU code every
 # tile, and accumulators placed in AGPRs cost a copy in each direction.
-EXTRA_FLAGS = {"sgla_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+EXTRA_FLAGS = {"sgla_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+               "sgla_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 ARCH = "gfx950"
 
 

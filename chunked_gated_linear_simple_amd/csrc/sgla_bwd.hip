@@ -1,0 +1,141 @@
+// Chunked Simple GLA backward for gfx950, bf16 inputs: the DV, DQ and DK roles
+// of the tile-scan body in sgla_scan.hpp, all in one launch.
+//
+// Method: "Beyond the KV cache: Training and serving i14's Laplace 3B linear
+// attention model on AWS Trainium2 with native PyTorch", section "Challenge 1:
+// Using native PyTorch on Trainium for GLA" (the backward pass differentiates
+// through the chunk recurrence, so the state gradient runs through the chunks
+// in reverse), with the self-augmentation of section "i14 and the Laplace 3B
+// architecture", paragraph "GLA mixer" (a is learned, so it has a gradient).
+// For every token t of a sequence (s over the same sequence):
+//   dv_s = sum_{t>=s} lam^(t-s) (q_t . k_s) dO_t + lam^(..) G k_s + sigmoid(z_s) dO_s
+//   dk_s = sum_{t>=s} lam^(t-s) (dO_t . v_s) q_t + lam^(..) G v_s + c_s (a (.) q_s)
+//   dq_t = sum_{s<=t} lam^(t-s) (dO_t . v_s) k_s + lam^(..) S dO_t + c_t (a (.) k_t)
+//   da   = sum_t c_t q_t (.) k_t,   c_t = sigmoid'(z_t) (dO_t . v_t)
+// with S the forward state and G the state gradient. DV is a reverse scan of G
+// ([d_k][d_v], sliced by d_v columns), DQ a forward scan of S^T and DK a
+// reverse scan of G^T ([d_v][d_k], all d_k columns in one workgroup).
+//
+// Workgroups per (sequence, head): DQ, DK, then one DV per 96 columns of d_v;
+// all of a unit's workgroups land on one XCD. The gradient of a is summed per
+// sequence-head by DQ and then over sequences in a fixed order, so the result
+// is bitwise reproducible.
+
+#include "sgla_scan.hpp"
+#include "sgla_internal.h"
+
+namespace sgla {
+namespace scan {
+
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+// The three scans' operands; role = 0 (DQ), 1 (DK), 2 (DV, nsl slices).
+struct BwdArgs {
+    Args role[3];
+};
+
+template <int DKV, int DKG>
+__global__ __launch_bounds__(NTHREADS) void k_bwd(BwdArgs ba)
+{
+    constexpr int LDS = cmax(Lay<RDv<DKV>>::LDS, cmax(Lay<RDq<DKG>>::LDS, Lay<RDk<DKG>>::LDS));
+    __shared__ __attribute__((aligned(16))) char smem[LDS];
+    const int nr = ba.role[2].nsl + 2;
+    const int b = blockIdx.x;
+    const int r = (b >> 3) % nr;
+    const int unit = ((b >> 3) / nr) * 8 + (b & 7);
+    if (unit >= ba.role[2].n_units) return;
+    // one role's operands, picked at run time so that only they are loaded
+    const int ri = r < 2 ? r : 2;
+    const Args& p = ba.role[ri];
+    if (r == 0) body<RDq<DKG>>(p, unit, 0, smem);
+    else if (r == 1) body<RDk<DKG>>(p, unit, 0, smem);
+    else body<RDv<DKV>>(p, unit, r - 2, smem);
+}
+
+// da[h][d] = sum over sequences n (in order) of part[n H + h][d]
+__global__ void k_da_sum(const float* __restrict__ part, float* __restrict__ da, int n_seq, int H, int dk)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= H * dk) return;
+    const int h = i / dk, d = i - (i / dk) * dk;
+    float s = 0.0f;
+    for (int n = 0; n < n_seq; ++n) s += part[((size_t)n * H + h) * dk + d];
+    da[i] = s;
+}
+
+template <int DKV, int DKG>
+hipError_t run_bwd(const Args& av, const Args& aq, const Args& ak, hipStream_t stream)
+{
+    BwdArgs ba;
+    ba.role[0] = aq;
+    ba.role[1] = ak;
+    ba.role[2] = av;
+    const int grid = ((av.n_units + 7) / 8) * 8 * (av.nsl + 2);
+    hipLaunchKernelGGL((k_bwd<DKV, DKG>), dim3(grid), dim3(NTHREADS), 0, stream, ba);
+    return hipGetLastError();
+}
+
+}  // namespace scan
+
+// bf16 backward with d_k <= 96 and d_v <= 192.
+hipError_t launch_bwd_bf16(const ChunkProblem& p, const void* q, const void* k, const void* v,
+                           const void* dO, const float* init_state, const float* d_final_state,
+                           void* dq, void* dk, void* dv, float* da, float* d_init_state,
+                           float* da_partial, hipStream_t stream)
+{
+    typedef const uint16_t* cp;
+    scan::Args base{};
+    base.lambda = p.lambda;
+    base.a = p.a;
+    base.cu = p.cu;
+    base.H = p.H;
+    base.T = p.T;
+    base.n_units = p.n_seq * p.H;
+
+    // dv: reverse scan of G; q'=k, k'=q, v'=dO; final G -> d_init_state
+    scan::Args av = base;
+    av.q = reinterpret_cast<cp>(k);
+    av.k = reinterpret_cast<cp>(q);
+    av.v = reinterpret_cast<cp>(dO);
+    av.o = reinterpret_cast<uint16_t*>(dv);
+    av.s_init = d_final_state;
+    av.s_final = d_init_state;
+    av.dkr = p.d_k;
+    av.dvr = p.d_v;
+    av.nsl = (p.d_v + scan::DVS - 1) / scan::DVS;
+    // dq: forward scan of S^T; q'=dO, k'=v, v'=k, gate operand q
+    scan::Args aq = base;
+    aq.q = reinterpret_cast<cp>(dO);
+    aq.k = reinterpret_cast<cp>(v);
+    aq.v = reinterpret_cast<cp>(k);
+    aq.x = reinterpret_cast<cp>(q);
+    aq.o = reinterpret_cast<uint16_t*>(dq);
+    aq.s_init = init_state;
+    aq.da_part = da_partial;
+    aq.dkr = p.d_v;
+    aq.dvr = p.d_k;
+    aq.nsl = 1;
+    // dk: reverse scan of G^T; q'=v, k'=dO, v'=q, gate operand k
+    scan::Args ak = aq;
+    ak.q = reinterpret_cast<cp>(v);
+    ak.k = reinterpret_cast<cp>(dO);
+    ak.v = reinterpret_cast<cp>(q);
+    ak.x = reinterpret_cast<cp>(k);
+    ak.o = reinterpret_cast<uint16_t*>(dk);
+    ak.s_init = d_final_state;
+    ak.da_part = nullptr;
+
+    hipError_t e;
+    if (p.d_k <= 32) {
+        e = (p.d_v <= 96) ? scan::run_bwd<32, 96>(av, aq, ak, stream) : scan::run_bwd<32, 192>(av, aq, ak, stream);
+    } else {
+        e = (p.d_v <= 96) ? scan::run_bwd<96, 96>(av, aq, ak, stream) : scan::run_bwd<96, 192>(av, aq, ak, stream);
+    }
+    if (e != hipSuccess) return e;
+    const int nda = p.H * p.d_k;
+    hipLaunchKernelGGL(scan::k_da_sum, dim3((nda + 255) / 256), dim3(256), 0, stream, da_partial, da,
+                       p.n_seq, p.H, p.d_k);
+    return hipGetLastError();
+}
+
+}  // namespace sgla

@@ -869,6 +869,9 @@ hipError_t launch_chunk_bwd(const ChunkProblem& p, const void* q, const void* k,
                             void* dq, void* dk, void* dv, float* da, float* d_init_state,
                             float* da_partial, hipStream_t stream)
 {
+    if (p.bf16 && p.d_k <= 96 && p.d_v <= 192)
+        return launch_bwd_bf16(p, q, k, v, dO, init_state, d_final_state, dq, dk, dv, da,
+                               d_init_state, da_partial, stream);
     // dq: forward scan of S^T ([d_v][d_k]); q'=dO, k'=v, v'=k, gate operand q
     RoleArgs aq{dO, v, k, q, dq, init_state, nullptr, da_partial, p.d_v, p.d_k, 1, 0, 0};
     // dk: reverse scan of G^T ([d_v][d_k]); q'=v, k'=dO, v'=q, gate operand k

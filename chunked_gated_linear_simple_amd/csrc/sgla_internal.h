@@ -24,10 +24,16 @@ hipError_t launch_chunk_fwd(const ChunkProblem& p, const void* q, const void* k,
                             const float* init_state, float* final_state, void* o,
                             hipStream_t stream);
 
-// bf16 forward, d_k <= 96: the column-owner kernel of sgla_fwd.hip.
+// bf16 forward, d_k <= 96: the FWD role of sgla_fwd.hip.
 hipError_t launch_fwd_bf16(const ChunkProblem& p, const void* q, const void* k, const void* v,
                            const float* init_state, float* final_state, void* o,
                            hipStream_t stream);
+
+// bf16 backward, d_k <= 96, d_v <= 192: the DV/DQ/DK roles of sgla_bwd.hip.
+hipError_t launch_bwd_bf16(const ChunkProblem& p, const void* q, const void* k, const void* v,
+                           const void* dO, const float* init_state, const float* d_final_state,
+                           void* dq, void* dk, void* dv, float* da, float* d_init_state,
+                           float* da_partial, hipStream_t stream);
 
 hipError_t launch_chunk_bwd(const ChunkProblem& p, const void* q, const void* k, const void* v,
                             const void* dO, const float* init_state, const float* d_final_state,
