@@ -145,9 +145,11 @@ __device__ __forceinline__ int toff(int r, int e)
 
 // 16 bytes per lane from global memory straight into LDS: lane l's bytes land
 // at dst + 16 l (global_load_lds_dwordx4; completion is counted by vmcnt).
-__device__ __forceinline__ void dma16(const uint16_t* src, char* dst)
+// The address is a uniform base plus a 32-bit lane offset in bytes, so the
+// load takes its base from scalar registers.
+__device__ __forceinline__ void dma16(const char* base, uint32_t off, char* dst)
 {
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(base + off, (lds_void*)dst, 16, 0, 0);
 }
 
 __device__ __forceinline__ u32x2_t lds_u32x2(const char* base, int off)
@@ -298,45 +300,48 @@ __device__ __forceinline__ void body(const Args& p, int unit, int slice, char* s
     if (wave == PRODUCER) {
         // ------------------------------------------------------------ producer
         // tile c -> ring slot c % NR; the last tile's rows past the sequence
-        // are clamped, then zeroed in LDS. Per-lane element offsets of the 1 KB
-        // load blocks within a tile, relative to the tile's first row (rows
-        // clamped to the tile length, columns to the real widths)
-        int offq[Ly::NLQ], offv[Ly::NLV];
+        // are clamped, then zeroed in LDS. Per-lane byte offsets of the 1 KB
+        // load blocks within a tile, relative to the tile's lowest global row
+        // (rows clamped to the tile length, columns to the real widths)
+        uint32_t offq[Ly::NLQ], offv[Ly::NLV];
         auto offsets = [&](int cl) {
 #pragma unroll
             for (int m = 0; m < Ly::NLQ; ++m) {
                 const int P = 64 * m + lane;              // physical 16-byte slot
                 const int r = P / SEGK;
                 const int cs = (P - r * SEGK) ^ sw(r);    // logical segment
-                offq[m] = RS * min(r, cl - 1) * dkr + min(8 * cs, dkr - 8);
+                const int rr = R::REV ? cl - 1 - min(r, cl - 1) : min(r, cl - 1);
+                offq[m] = (uint32_t)(rr * dkr + min(8 * cs, dkr - 8)) * 2u;
             }
 #pragma unroll
             for (int m = 0; m < Ly::NLV; ++m) {
                 const int P = 64 * m + lane;
                 const int r = P / SEGV;
                 const int cs = (P - r * SEGV) ^ sw(r);
-                offv[m] = RS * min(r, cl - 1) * dvr + min(n0 + 8 * cs, dvr - 8);
+                const int rr = R::REV ? cl - 1 - min(r, cl - 1) : min(r, cl - 1);
+                offv[m] = (uint32_t)(rr * dvr + min(n0 + 8 * cs, dvr - 8)) * 2u;
             }
         };
         offsets(nch > 1 ? C : clast);
         auto issue = [&](int c) {
             char* st = smem + (c % R::NR) * Ly::SLOT;
+            const int cl = min(C, len - c * C);
             if (c == nch - 1 && clast < C) offsets(clast);
-            const long r0 = grow(c, 0);
-            const uint16_t* qb = p.q + r0 * dkr;
-            const uint16_t* kb = p.k + r0 * dkr;
-            const uint16_t* vb = p.v + r0 * dvr;
+            const long rb = R::REV ? grow(c, cl - 1) : grow(c, 0);   // lowest row of the tile
+            const char* qb = reinterpret_cast<const char*>(p.q + rb * dkr);
+            const char* kb = reinterpret_cast<const char*>(p.k + rb * dkr);
+            const char* vb = reinterpret_cast<const char*>(p.v + rb * dvr);
 #pragma unroll
             for (int m = 0; m < Ly::NLQ; ++m) {
-                dma16(qb + offq[m], st + 1024 * m);
-                dma16(kb + offq[m], st + Ly::OFF_K + 1024 * m);
+                dma16(qb, offq[m], st + 1024 * m);
+                dma16(kb, offq[m], st + Ly::OFF_K + 1024 * m);
             }
 #pragma unroll
-            for (int m = 0; m < Ly::NLV; ++m) dma16(vb + offv[m], st + Ly::OFF_V + 1024 * m);
+            for (int m = 0; m < Ly::NLV; ++m) dma16(vb, offv[m], st + Ly::OFF_V + 1024 * m);
             if constexpr (R::GRAD) {
-                const uint16_t* xb = p.x + r0 * dvr;
+                const char* xb = reinterpret_cast<const char*>(p.x + rb * dvr);
 #pragma unroll
-                for (int m = 0; m < Ly::NLV; ++m) dma16(xb + offv[m], st + Ly::OFF_X + 1024 * m);
+                for (int m = 0; m < Ly::NLV; ++m) dma16(xb, offv[m], st + Ly::OFF_X + 1024 * m);
             }
         };
         // rows past the tile and columns past the real widths read as zero
@@ -452,14 +457,18 @@ __device__ __forceinline__ void body(const Args& p, int unit, int slice, char* s
                 }
 #pragma unroll
                 for (int jb = 0; jb <= s; ++jb) {
-                    f32x16_t sc;
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) sc[i] = (!R::GRAD && jb == s) ? dsel[i] * gt : 0.0f;
+                    f32x16_t sc = {};
 #pragma unroll
                     for (int kb = 0; kb < DK / 16; ++kb) {
                         const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
                                                                              Ks + toff<SEGK>(32 * jb + l32, 16 * kb + 8 * g)));
                         sc = mma(kf, qf[kb], sc);
+                    }
+                    // the gate joins on the diagonal after the product, so that
+                    // the two matrix-core chains are independent
+                    if (!R::GRAD && jb == s) {
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) sc[i] = fmaf(dsel[i], gt, sc[i]);
                     }
                     if constexpr (R::GRAD) {
                         if (jb == s) {
