@@ -44,6 +44,33 @@ STATE_BYTES = DK * DV * 4
 MIN_WARM_S = 1.5               # untimed warm-up floor per workload, seconds
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_fwd__laplace_fwd_B8_hbm_traffic.txt")
+FWD_SOURCES = [os.path.join(ROOT, "chunked_gated_linear_simple_amd", "csrc", f)
+               for f in ("sgla_scan.hpp", "sgla_fwd.hip")]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the forward kernel from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE scaled by a copy kernel of known
+    size), or None when the kernel sources have changed since it was taken."""
+    import hashlib
+    try:
+        kv = {}
+        for line in open(TRAFFIC_FILE):
+            if line.startswith("#") or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+        h = hashlib.sha256()
+        for f in FWD_SOURCES:
+            h.update(open(f, "rb").read())
+        if h.hexdigest()[:16] != kv.get("sources_sha256"):
+            return None
+        return int(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -279,7 +306,7 @@ def main():
                        "chunk": 128},
             "roofline": {"bound": "hbm", "kernel": "k_fwd", "achieved": fwd["gbs"],
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": fwd["gbs"] / HBM_PEAK_GBS,
-                         "traffic": None, "bytes_per_launch": fwd["bytes"]},
+                         "traffic": measured_traffic(), "bytes_per_launch": fwd["bytes"]},
         })
     else:
         first = next(iter(secondary.values()))

@@ -1,4 +1,6 @@
-// Chunked Simple GLA kernels for gfx950 (forward and backward).
+// Chunked Simple GLA kernels for gfx950, fp32 tensors (forward and backward),
+// and the dispatch of bf16 calls to the tile-scan kernels of sgla_fwd.hip and
+// sgla_bwd.hip.
 //
 // Method: "Beyond the KV cache: Training and serving i14's Laplace 3B linear
 // attention model on AWS Trainium2 with native PyTorch", section "Challenge 1:
@@ -836,13 +838,8 @@ hipError_t run_bwd(const ChunkProblem& p, const RoleArgs& aq, const RoleArgs& ak
     return hipGetLastError();
 }
 
-// Role instantiations
-typedef Role<u16, 96, 96, 128, AUG_FWD, false> BfFwd128;
-typedef Role<u16, 96, 96, 64, AUG_FWD, false> BfFwd64;
-typedef Role<u16, 192, 32, 64, AUG_GRAD, false> BfDq;
-typedef Role<u16, 192, 32, 64, AUG_GRAD, true> BfDk;
-typedef Role<u16, 96, 96, 128, AUG_FWD, true> BfDv128;
-typedef Role<u16, 96, 96, 64, AUG_FWD, true> BfDv64;
+// Role instantiations (fp32 tensors; bf16 runs on the kernels of sgla_fwd.hip
+// and sgla_bwd.hip)
 typedef Role<float, 32, 32, 64, AUG_FWD, false> F32Fwd;
 typedef Role<float, 32, 32, 64, AUG_GRAD, false> F32Dq;
 typedef Role<float, 32, 32, 64, AUG_GRAD, true> F32Dk;
@@ -854,13 +851,9 @@ hipError_t launch_chunk_fwd(const ChunkProblem& p, const void* q, const void* k,
                             const float* init_state, float* final_state, void* o,
                             hipStream_t stream)
 {
-    if (p.bf16 && p.d_k <= 96) return launch_fwd_bf16(p, q, k, v, init_state, final_state, o, stream);
+    // bf16 shapes are limited to d_k <= 96, d_v <= 192 by the host checks
+    if (p.bf16) return launch_fwd_bf16(p, q, k, v, init_state, final_state, o, stream);
     RoleArgs ra{q, k, v, nullptr, o, init_state, final_state, nullptr, p.d_k, p.d_v, 0, 0, 0};
-    if (p.bf16) {
-        const int nsl = (p.d_v + 95) / 96;
-        if (p.chunk == 128) return run_fwd<BfFwd128>(p, ra, nsl, stream);
-        return run_fwd<BfFwd64>(p, ra, nsl, stream);
-    }
     return run_fwd<F32Fwd>(p, ra, (p.d_v + 31) / 32, stream);
 }
 
@@ -869,7 +862,7 @@ hipError_t launch_chunk_bwd(const ChunkProblem& p, const void* q, const void* k,
                             void* dq, void* dk, void* dv, float* da, float* d_init_state,
                             float* da_partial, hipStream_t stream)
 {
-    if (p.bf16 && p.d_k <= 96 && p.d_v <= 192)
+    if (p.bf16)
         return launch_bwd_bf16(p, q, k, v, dO, init_state, d_final_state, dq, dk, dv, da,
                                d_init_state, da_partial, stream);
     // dq: forward scan of S^T ([d_v][d_k]); q'=dO, k'=v, v'=k, gate operand q
@@ -878,10 +871,6 @@ hipError_t launch_chunk_bwd(const ChunkProblem& p, const void* q, const void* k,
     RoleArgs ak{v, dO, q, k, dk, d_final_state, nullptr, nullptr, p.d_v, p.d_k, 1, 0, 1};
     // dv: reverse scan of G ([d_k][d_v]); q'=k, k'=q, v'=dO; final G -> d_init_state
     RoleArgs av{k, q, dO, nullptr, dv, d_final_state, d_init_state, nullptr, p.d_k, p.d_v, 0, 1, 1};
-    if (p.bf16) {
-        if (p.chunk == 128) return run_bwd<BfDq, BfDk, BfDv128>(p, aq, ak, av, da, stream);
-        return run_bwd<BfDq, BfDk, BfDv64>(p, aq, ak, av, da, stream);
-    }
     return run_bwd<F32Dq, F32Dk, F32Dv>(p, aq, ak, av, da, stream);
 }
 
