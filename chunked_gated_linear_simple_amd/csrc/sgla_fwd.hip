@@ -23,11 +23,23 @@ __global__ __launch_bounds__(NTHREADS) void k_fwd(Args p)
     body<RFwd<DK>>(p, unit, slice, smem);
 }
 
+// Eight-wave variant (two waves per SIMD).
+template <int DK>
+__global__ __launch_bounds__(NTHREADS_W) void k_fwd_w(Args p)
+{
+    __shared__ __attribute__((aligned(16))) char smem[LayW<RFwd<DK>>::LDS];
+    const int b = blockIdx.x;
+    const int slice = (b >> 3) % p.nsl;
+    const int unit = ((b >> 3) / p.nsl) * 8 + (b & 7);
+    if (unit >= p.n_units) return;
+    body_wide<RFwd<DK>>(p, unit, slice, smem);
+}
+
 template <int DK>
 hipError_t run_fwd(const Args& a, hipStream_t stream)
 {
     const int grid = ((a.n_units + 7) / 8) * 8 * a.nsl;
-    hipLaunchKernelGGL(k_fwd<DK>, dim3(grid), dim3(NTHREADS), 0, stream, a);
+    hipLaunchKernelGGL(k_fwd_w<DK>, dim3(grid), dim3(NTHREADS_W), 0, stream, a);
     return hipGetLastError();
 }
 

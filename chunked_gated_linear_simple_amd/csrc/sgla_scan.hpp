@@ -766,6 +766,462 @@ __device__ __forceinline__ void body(const Args& p, int unit, int slice, char* s
     }
 }
 
+
+// ----------------------------------------------------------------------------
+// Eight-wave body for the scans without the gate-derivative epilogue (FWD, DV).
+//
+// The four-wave body above keeps one wave per SIMD, and each of its waves is
+// bound by the latency of its own dependency chain (state readout -> output,
+// decay -> update) rather than by matrix-core, VALU or LDS throughput. Here a
+// workgroup has eight waves, two per SIMD, over the same 96-column slice:
+//   * waves 0..5 ("column owners") own 16 columns each, with the state slice
+//     in v_mfma_f32_16x16x32_bf16 accumulators (lane l: column l%16, rows
+//     4(l/16) + r of each 16-row block; A and B operands: row or column l%16,
+//     contraction index 8(l/16) + slot);
+//   * wave 6 ("loader") streams tiles into a 4-deep LDS ring and computes the
+//     gate sigmoid(z) of the tile two ahead;
+//   * wave 7 ("scorer") computes the decay-masked scores of the next tile,
+//     adds the gate on the diagonal, and writes P^T in the owners' operand
+//     order (a 16-token x 32-key block is one 1 KB fragment, 16 B per lane).
+// A tile's data is waited for by the loader two iterations before the owners
+// use it, so the gate and the scores of tile c+1 both run during iteration c.
+// Per tile and owner wave:
+//   O^T  = S^T Q'^T    4 token blocks x 3 steps x (hi, lo)    24 MFMA
+//   O^T += V'^T P^T    6 blocks                                  6 MFMA
+//   S    = lam^C S + K'^T V' - K'^T (c * V')                    24 MFMA
+// with the 32-row operand slots of the state taken as rows 4(l/16) + s of two
+// consecutive 16-row blocks (the Q' operand is read with the same map).
+constexpr int NOW_W = 6;                   // owner waves
+constexpr int OWC = 16;                    // columns per owner
+constexpr int NTHREADS_W = 64 * (NOW_W + 2);
+constexpr int LOADER_W = NOW_W, SCORER_W = NOW_W + 1;
+constexpr int NR_W = 4;                    // ring depth
+constexpr int NPB = 6;                     // P fragments per tile: (tb, ks) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+
+__device__ __forceinline__ f32x4_t mma16(bf16x8_t a, bf16x8_t b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ constexpr int pblk(int tb, int ks) { return tb < 2 ? tb : 2 + 2 * (tb - 2) + ks; }
+
+template <class R>
+struct LayW {
+    static constexpr int DK = R::DK;
+    static constexpr int NDB16 = DK / 16;      // 16-row blocks of the state
+    static constexpr int NKS = DK / 32;        // 32-wide contraction steps over d
+    static constexpr int SEGK = DK / 8;
+    static constexpr int SEGV = DVS / 8;
+    static constexpr int SZ_Q = C * DK * 2;
+    static constexpr int SZ_V = C * DVS * 2;
+    static constexpr int OFF_K = SZ_Q;
+    static constexpr int OFF_V = 2 * SZ_Q;
+    static constexpr int SLOT = 2 * SZ_Q + SZ_V;
+    static constexpr int OFF_P = NR_W * SLOT;               // 2 x [NPB][64 lanes][16 B]
+    static constexpr int SZ_P = NPB * 64 * 16;
+    static constexpr int OFF_CORR = OFF_P + 2 * SZ_P;       // [2][C]
+    static constexpr int OFF_GT = OFF_CORR + 2 * C * 4;     // gate sigmoid(z) [2][C]
+    static constexpr int LDS = OFF_GT + 2 * C * 4;
+    static constexpr int NLQ = SZ_Q / 1024;
+    static constexpr int NLV = SZ_V / 1024;
+    static constexpr int NLOAD = 2 * NLQ + NLV;
+    static_assert(!R::GRAD && !R::DA, "eight-wave body: FWD and DV scans only");
+    static_assert(DK % 32 == 0 && DK <= 96, "DK");
+    static_assert(NLOAD <= 63, "vmcnt");
+    static_assert(LDS <= 160 * 1024, "LDS");
+};
+
+template <class R>
+__device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, char* smem)
+{
+    typedef LayW<R> Ly;
+    constexpr int DK = R::DK;
+    constexpr int SEGK = Ly::SEGK, SEGV = Ly::SEGV;
+    constexpr int E = R::E;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int H = p.H;
+    const int seq = unit / H, h = unit - seq * H;
+    const int dkr = p.dkr, dvr = p.dvr;
+    const int n0 = slice * DVS;
+
+    long row0;
+    int len;
+    if (p.cu != nullptr) {
+        int s0 = p.cu[seq], s1 = p.cu[seq + 1];
+        s0 = min(max(s0, 0), p.T);
+        s1 = min(max(s1, s0), p.T);
+        row0 = (long)h * p.T + s0;
+        len = s1 - s0;
+    } else {
+        row0 = ((long)seq * H + h) * p.T;
+        len = p.T;
+    }
+    auto grow = [&](int c, int r) -> long { return R::REV ? row0 + len - 1 - (c * C + r) : row0 + c * C + r; };
+    const int nch = (len + C - 1) / C;
+    const int clast = len - (nch - 1) * C;
+    const float lam = p.lambda[h];
+    const float l2 = log2f(lam);
+
+    float* corr = reinterpret_cast<float*>(smem + Ly::OFF_CORR);
+    for (int i = tid; i < 2 * C; i += NTHREADS_W) {
+        const int cl = (i < C) ? C : clast;
+        const int j = i & (C - 1);
+        corr[i] = (j < cl) ? 1.0f - powl2(cl - E - j, l2) : 0.0f;
+    }
+    float* gtb = reinterpret_cast<float*>(smem + Ly::OFF_GT);
+
+    if (wave == LOADER_W) {
+        // ---------------------------------------------------------- loader
+        const int l32 = lane & 31, g = lane >> 5;
+        uint32_t offq[Ly::NLQ], offv[Ly::NLV];
+        auto offsets = [&](int cl) {
+#pragma unroll
+            for (int m = 0; m < Ly::NLQ; ++m) {
+                const int P = 64 * m + lane;
+                const int r = P / SEGK;
+                const int cs = (P - r * SEGK) ^ sw(r);
+                const int rr = R::REV ? cl - 1 - min(r, cl - 1) : min(r, cl - 1);
+                offq[m] = (uint32_t)(rr * dkr + min(8 * cs, dkr - 8)) * 2u;
+            }
+#pragma unroll
+            for (int m = 0; m < Ly::NLV; ++m) {
+                const int P = 64 * m + lane;
+                const int r = P / SEGV;
+                const int cs = (P - r * SEGV) ^ sw(r);
+                const int rr = R::REV ? cl - 1 - min(r, cl - 1) : min(r, cl - 1);
+                offv[m] = (uint32_t)(rr * dvr + min(n0 + 8 * cs, dvr - 8)) * 2u;
+            }
+        };
+        offsets(nch > 1 ? C : clast);
+        auto issue = [&](int c) {
+            char* st = smem + (c % NR_W) * Ly::SLOT;
+            const int cl = min(C, len - c * C);
+            if (c == nch - 1 && clast < C) offsets(clast);
+            const long rb = R::REV ? grow(c, cl - 1) : grow(c, 0);
+            const char* qb = reinterpret_cast<const char*>(p.q + rb * dkr);
+            const char* kb = reinterpret_cast<const char*>(p.k + rb * dkr);
+            const char* vb = reinterpret_cast<const char*>(p.v + rb * dvr);
+#pragma unroll
+            for (int m = 0; m < Ly::NLQ; ++m) {
+                dma16(qb, offq[m], st + 1024 * m);
+                dma16(kb, offq[m], st + Ly::OFF_K + 1024 * m);
+            }
+#pragma unroll
+            for (int m = 0; m < Ly::NLV; ++m) dma16(vb, offv[m], st + Ly::OFF_V + 1024 * m);
+        };
+        auto fixup = [&](int c) {
+            const int cl = min(C, len - c * C);
+            if (cl == C && dkr == DK && n0 + DVS <= dvr) return;
+            char* st = smem + (c % NR_W) * Ly::SLOT;
+            const u32x4_t zero = {0u, 0u, 0u, 0u};
+            for (int P = lane; P < C * SEGK; P += 64) {
+                const int r = P / SEGK;
+                const int cs = (P - r * SEGK) ^ sw(r);
+                if (r >= cl || 8 * cs >= dkr) {
+                    *reinterpret_cast<u32x4_t*>(st + 16 * P) = zero;
+                    *reinterpret_cast<u32x4_t*>(st + Ly::OFF_K + 16 * P) = zero;
+                }
+            }
+            for (int P = lane; P < C * SEGV; P += 64) {
+                const int r = P / SEGV;
+                const int cs = (P - r * SEGV) ^ sw(r);
+                if (r >= cl || n0 + 8 * cs >= dvr) *reinterpret_cast<u32x4_t*>(st + Ly::OFF_V + 16 * P) = zero;
+            }
+        };
+        float dsel[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dsel[i] = (l32 == acc_row(i, g)) ? 1.0f : 0.0f;
+        constexpr int GDB = DK / 32;
+        bf16x8_t adiag[GDB][2];
+#pragma unroll
+        for (int db = 0; db < GDB; ++db)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int j = l32 - 16 * hh - 8 * g;
+                const int dcol = 32 * db + l32;
+                const float ad = (p.a != nullptr && dcol < dkr) ? p.a[(size_t)h * dkr + dcol] : 0.0f;
+                u32x4_t w;
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2)
+                    w[s2] = pack2(j == 2 * s2 ? ad : 0.0f, j == 2 * s2 + 1 ? ad : 0.0f);
+                adiag[db][hh] = __builtin_bit_cast(bf16x8_t, w);
+            }
+        // sigmoid(z_t) of tile c: z_t = (K (diag(a) Q^T))[t][t] on the matrix cores
+        auto gate = [&](int c) {
+            const char* st = smem + (c % NR_W) * Ly::SLOT;
+            const char* Qs = st;
+            const char* Ks = st + Ly::OFF_K;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                f32x16_t zt = {};
+#pragma unroll
+                for (int db = 0; db < GDB; ++db) {
+                    f32x16_t qa = {};
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const bf16x8_t xf = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
+                                                                            Qs + toff<SEGK>(32 * s + l32, 32 * db + 16 * hh + 8 * g)));
+                        qa = mma(adiag[db][hh], xf, qa);
+                    }
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        u32x4_t bw;
+#pragma unroll
+                        for (int s2 = 0; s2 < 4; ++s2) bw[s2] = pack2(qa[8 * hh + 2 * s2], qa[8 * hh + 2 * s2 + 1]);
+                        const int e0 = 32 * db + 16 * hh + 4 * g;
+                        const bf16x8_t kz = frag(lds_u32x2(Ks, toff<SEGK>(32 * s + l32, e0)),
+                                                 lds_u32x2(Ks, toff<SEGK>(32 * s + l32, e0 + 8)));
+                        zt = mma(kz, __builtin_bit_cast(bf16x8_t, bw), zt);
+                    }
+                }
+                float z = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) z = fmaf(dsel[i], zt[i], z);
+                z += __shfl_xor(z, 32);
+                if (g == 0) gtb[(c & 1) * C + 32 * s + l32] = sigmoid_f(z);
+            }
+        };
+        if (nch > 0) {
+            issue(0);
+            if (nch > 1) {
+                issue(1);
+                wait_vm<Ly::NLOAD>();
+            } else {
+                wait_vm<0>();
+            }
+            fixup(0);
+            gate(0);
+            if (nch > 1) {
+                if (nch > 2) {
+                    issue(2);
+                    wait_vm<Ly::NLOAD>();
+                } else {
+                    wait_vm<0>();
+                }
+                fixup(1);
+                gate(1);
+            }
+        }
+        lds_barrier();
+        lds_barrier();
+        for (int c = 0; c < nch; ++c) {
+            if (c + 3 < nch) issue(c + 3);
+            if (c + 2 < nch) {
+                if (c + 3 < nch) wait_vm<Ly::NLOAD>();
+                else wait_vm<0>();
+                fixup(c + 2);
+                gate(c + 2);
+            }
+            lds_barrier();
+        }
+        return;
+    }
+
+    if (wave == SCORER_W) {
+        // ---------------------------------------------------------- scorer
+        const int l32 = lane & 31, g = lane >> 5;
+        float dmd[16], dmo[16], dsel[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int diff = l32 - acc_row(i, g);
+            dmd[i] = diff < 0 ? 0.0f : powl2(diff, l2);
+            dmo[i] = powl2(32 + diff, l2);
+            dsel[i] = (diff == 0) ? 1.0f : 0.0f;
+        }
+        // scores of tile c: 32 x 32 blocks (s, jb), jb <= s, in the 32x32x16
+        // accumulator layout (column t = 32 s + l32, keys 32 jb + acc_row(i, g));
+        // each lane writes its masked values into the 16x16x32 B-operand
+        // fragments of the owners: token block tb = t / 16, step ks = jb, lane
+        // (t % 16) + 16 (i / 4), slots 4 g + i % 4
+        auto scores = [&](int c) {
+            const char* st = smem + (c % NR_W) * Ly::SLOT;
+            const char* Qs = st;
+            const char* Ks = st + Ly::OFF_K;
+            char* Pb = smem + Ly::OFF_P + (c & 1) * Ly::SZ_P;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                bf16x8_t qf[DK / 16];
+#pragma unroll
+                for (int kb = 0; kb < DK / 16; ++kb)
+                    qf[kb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
+                                                              Qs + toff<SEGK>(32 * s + l32, 16 * kb + 8 * g)));
+                const float gt = gtb[(c & 1) * C + 32 * s + l32];
+                const int tb = 2 * s + (l32 >> 4);
+#pragma unroll
+                for (int jb = 0; jb <= s; ++jb) {
+                    f32x16_t sc = {};
+#pragma unroll
+                    for (int kb = 0; kb < DK / 16; ++kb) {
+                        const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
+                                                                             Ks + toff<SEGK>(32 * jb + l32, 16 * kb + 8 * g)));
+                        sc = mma(kf, qf[kb], sc);
+                    }
+                    if (jb == s) {
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) sc[i] = fmaf(dsel[i], gt, sc[i]);
+                    }
+                    char* blk = Pb + pblk(tb, jb) * 1024;
+#pragma unroll
+                    for (int a4 = 0; a4 < 4; ++a4) {
+                        const int i0 = 4 * a4;
+                        const float m0 = (jb == s) ? dmd[i0] : dmo[i0], m1 = (jb == s) ? dmd[i0 + 1] : dmo[i0 + 1];
+                        const float m2 = (jb == s) ? dmd[i0 + 2] : dmo[i0 + 2], m3 = (jb == s) ? dmd[i0 + 3] : dmo[i0 + 3];
+                        const u32x2_t w2 = {pack2(sc[i0] * m0, sc[i0 + 1] * m1), pack2(sc[i0 + 2] * m2, sc[i0 + 3] * m3)};
+                        *reinterpret_cast<u32x2_t*>(blk + ((l32 & 15) + 16 * a4) * 16 + 8 * g) = w2;
+                    }
+                }
+            }
+        };
+        lds_barrier();
+        if (nch > 0) scores(0);
+        lds_barrier();
+        for (int c = 0; c < nch; ++c) {
+            if (c + 1 < nch) scores(c + 1);
+            lds_barrier();
+        }
+        return;
+    }
+
+    // -------------------------------------------------------------- owners
+    constexpr int NDB16 = Ly::NDB16, NKS = Ly::NKS;
+    const int w = wave;
+    const int l16 = lane & 15, qg = lane >> 4;
+    const int ncol = n0 + OWC * w + l16;       // this lane's v' column in the row
+    const size_t sbase = (size_t)unit * dkr * dvr;
+
+    f32x4_t sacc[NDB16];
+#pragma unroll
+    for (int db = 0; db < NDB16; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int d = 16 * db + 4 * qg + r;
+            sacc[db][r] = (p.s_init != nullptr && d < dkr && ncol < dvr) ? p.s_init[sbase + (size_t)d * dvr + ncol] : 0.0f;
+        }
+    float tdec[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) tdec[tb] = powl2(16 * tb + l16 + E, l2);
+    const float fC = __builtin_amdgcn_exp2f((float)C * l2);
+
+    auto tile = [&](int c, auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        const char* st = smem + (c % NR_W) * Ly::SLOT;
+        const char* Qs = st;
+        const char* Ks = st + Ly::OFF_K;
+        const char* Vs = st + Ly::OFF_V;
+        const char* Pb = smem + Ly::OFF_P + (c & 1) * Ly::SZ_P;
+        const int cstart = c * C;
+        const int cl = FULL ? C : min(C, len - cstart);
+        const float* cf = corr + ((!FULL && c == nch - 1) ? C : 0);
+        const float fcl = FULL ? fC : __builtin_amdgcn_exp2f((float)cl * l2);
+
+        // V'^T (A operand of P V') and V' (B operand of the update) share one
+        // register layout: lane (column l16, step slice qg) holds tokens
+        // 32 ks + 8 qg + 0..7
+        bf16x8_t vf[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            vf[ks] = frag(tr_read<SEGV>(Vs, 32 * ks + 8 * qg, OWC * w, lane),
+                          tr_read<SEGV>(Vs, 32 * ks + 8 * qg + 4, OWC * w, lane));
+        bf16x8_t pf[NPB];
+#pragma unroll
+        for (int b = 0; b < NPB; ++b)
+            pf[b] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(Pb + (b * 64 + lane) * 16));
+
+        // ---- readout: O^T = S^T Q'^T, state as a bf16 hi + lo pair
+        f32x4_t oq[4] = {};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            u32x4_t hw, lw;
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                const f32x4_t& blk = (s2 < 2) ? sacc[2 * ks] : sacc[2 * ks + 1];
+                const float x0 = blk[2 * (s2 & 1)], x1 = blk[2 * (s2 & 1) + 1];
+                const uint32_t hp = pack2(x0, x1);
+                hw[s2] = hp;
+                lw[s2] = pack2(x0 - bf_lo(hp), x1 - bf_hi(hp));
+            }
+            const bf16x8_t sh = __builtin_bit_cast(bf16x8_t, hw), sl = __builtin_bit_cast(bf16x8_t, lw);
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                // Q' row 16 tb + l16, d = 32 ks + 4 qg + 0..3 and 32 ks + 16 + 4 qg + 0..3
+                const int t = 16 * tb + l16;
+                const bf16x8_t qf = frag(lds_u32x2(Qs, toff<SEGK>(t, 32 * ks + 4 * qg)),
+                                         lds_u32x2(Qs, toff<SEGK>(t, 32 * ks + 16 + 4 * qg)));
+                oq[tb] = mma16(sh, qf, oq[tb]);
+                oq[tb] = mma16(sl, qf, oq[tb]);
+            }
+        }
+#pragma unroll
+        for (int db = 0; db < NDB16; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sacc[db][r] *= fcl;
+
+        // ---- intra-tile part and output (lane = token 16 tb + l16, columns 4 qg + r)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            f32x4_t o = {};
+            o = mma16(vf[0], pf[pblk(tb, 0)], o);
+            if (tb >= 2) o = mma16(vf[1], pf[pblk(tb, 1)], o);
+            const int t = 16 * tb + l16;
+            if (FULL || t < cl) {
+                const int col = n0 + OWC * w + 4 * qg;
+                if (FULL || col < dvr) {
+                    uint16_t* orow = p.o + grow(c, t) * dvr + col;
+                    const u32x2_t w2 = {pack2(fmaf(tdec[tb], oq[tb][0], o[0]), fmaf(tdec[tb], oq[tb][1], o[1])),
+                                        pack2(fmaf(tdec[tb], oq[tb][2], o[2]), fmaf(tdec[tb], oq[tb][3], o[3]))};
+                    *reinterpret_cast<u32x2_t*>(orow) = w2;
+                }
+            }
+        }
+
+        // ---- state advance: S = lam^cl S + K'^T V' - K'^T (c V')
+        bf16x8_t vc[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const f32x4_t c0 = *reinterpret_cast<const f32x4_t*>(cf + 32 * ks + 8 * qg);
+            const f32x4_t c1 = *reinterpret_cast<const f32x4_t*>(cf + 32 * ks + 8 * qg + 4);
+            const u32x4_t vw = __builtin_bit_cast(u32x4_t, vf[ks]);
+            u32x4_t cw;
+            cw[0] = pack2(-c0[0] * bf_lo(vw[0]), -c0[1] * bf_hi(vw[0]));
+            cw[1] = pack2(-c0[2] * bf_lo(vw[1]), -c0[3] * bf_hi(vw[1]));
+            cw[2] = pack2(-c1[0] * bf_lo(vw[2]), -c1[1] * bf_hi(vw[2]));
+            cw[3] = pack2(-c1[2] * bf_lo(vw[3]), -c1[3] * bf_hi(vw[3]));
+            vc[ks] = __builtin_bit_cast(bf16x8_t, cw);
+        }
+#pragma unroll
+        for (int db = 0; db < NDB16; ++db)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                // K'^T: rows d = 16 db + l16, tokens 32 ks + 8 qg + 0..7
+                const bf16x8_t kf = frag(tr_read<SEGK>(Ks, 32 * ks + 8 * qg, 16 * db, lane),
+                                         tr_read<SEGK>(Ks, 32 * ks + 8 * qg + 4, 16 * db, lane));
+                sacc[db] = mma16(kf, vf[ks], sacc[db]);
+                sacc[db] = mma16(kf, vc[ks], sacc[db]);
+            }
+    };
+
+    const bool cols_full = (n0 + DVS <= dvr);
+    lds_barrier();
+    lds_barrier();
+    for (int c = 0; c < nch; ++c) {
+        if (cols_full && (c < nch - 1 || clast == C)) tile(c, std::true_type{});
+        else tile(c, std::false_type{});
+        lds_barrier();
+    }
+
+    if (p.s_final != nullptr && ncol < dvr) {
+#pragma unroll
+        for (int db = 0; db < NDB16; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int d = 16 * db + 4 * qg + r;
+                if (d < dkr) p.s_final[sbase + (size_t)d * dvr + ncol] = sacc[db][r];
+            }
+    }
+}
+
 }  // namespace scan
 }  // namespace sgla
 
