@@ -169,6 +169,18 @@ __device__ __forceinline__ u32x2_t tr_read(const char* tile, int T0, int c0, int
     return __builtin_bit_cast(u32x2_t, v);
 }
 
+// As tr_read, but lanes 4s + q address columns c0 + 8q: lane i receives
+// column c0 + 8 (i / 4) + i % 4 of the four tokens T0..T0+3.
+template <int SEG>
+__device__ __forceinline__ u32x2_t tr_read8(const char* tile, int T0, int c0, int lane)
+{
+    const int j = lane & 15;
+    const int off = toff<SEG>(T0 + (j >> 2), c0 + 8 * (j & 3));
+    const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4_t*)(tile + off));
+    return __builtin_bit_cast(u32x2_t, v);
+}
+
 __device__ __forceinline__ bf16x8_t frag(u32x2_t lo, u32x2_t hi)
 {
     u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
@@ -789,8 +801,11 @@ __device__ __forceinline__ void body(const Args& p, int unit, int slice, char* s
 //   O^T  = S^T Q'^T    4 token blocks x 3 steps x (hi, lo)    24 MFMA
 //   O^T += V'^T P^T    6 blocks                                  6 MFMA
 //   S    = lam^C S + K'^T V' - K'^T (c * V')                    24 MFMA
-// with the 32-row operand slots of the state taken as rows 4(l/16) + s of two
-// consecutive 16-row blocks (the Q' operand is read with the same map).
+// The state's 16-row accumulator blocks are interleaved in groups of four rows
+// (block 2m + h, row 4g + r holds state row 32m + 8g + 4h + r), which makes
+// the eight contraction slots of each lane group contiguous state rows, so the
+// Q' operand is one 16-byte LDS read; the K'^T operand of the update reads
+// key columns in the same order.
 constexpr int NOW_W = 6;                   // owner waves
 constexpr int OWC = 16;                    // columns per owner
 constexpr int NTHREADS_W = 64 * (NOW_W + 2);
@@ -1091,12 +1106,17 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
     const int ncol = n0 + OWC * w + l16;       // this lane's v' column in the row
     const size_t sbase = (size_t)unit * dkr * dvr;
 
+    // Accumulator row 4 qg + r of 16-row block db holds state row
+    // d = 32 (db / 2) + 8 qg + 4 (db % 2) + r: the two blocks of a 32-row step
+    // interleave in groups of four, so that the readout's eight contraction
+    // slots of lane group qg are the contiguous rows 32 ks + 8 qg + 0..7.
+    auto srow = [&](int db, int r) { return 32 * (db >> 1) + 8 * qg + 4 * (db & 1) + r; };
     f32x4_t sacc[NDB16];
 #pragma unroll
     for (int db = 0; db < NDB16; ++db)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int d = 16 * db + 4 * qg + r;
+            const int d = srow(db, r);
             sacc[db][r] = (p.s_init != nullptr && d < dkr && ncol < dvr) ? p.s_init[sbase + (size_t)d * dvr + ncol] : 0.0f;
         }
     float tdec[4];
@@ -1129,7 +1149,8 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
         for (int b = 0; b < NPB; ++b)
             pf[b] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(Pb + (b * 64 + lane) * 16));
 
-        // ---- readout: O^T = S^T Q'^T, state as a bf16 hi + lo pair
+        // ---- readout: O^T = S^T Q'^T, the state as a bf16 pair: hi = the
+        // truncated upper half, lo = the remainder (exact in fp32) rounded
         f32x4_t oq[4] = {};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
@@ -1138,17 +1159,16 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
             for (int s2 = 0; s2 < 4; ++s2) {
                 const f32x4_t& blk = (s2 < 2) ? sacc[2 * ks] : sacc[2 * ks + 1];
                 const float x0 = blk[2 * (s2 & 1)], x1 = blk[2 * (s2 & 1) + 1];
-                const uint32_t hp = pack2(x0, x1);
-                hw[s2] = hp;
-                lw[s2] = pack2(x0 - bf_lo(hp), x1 - bf_hi(hp));
+                const uint32_t b0 = __float_as_uint(x0), b1 = __float_as_uint(x1);
+                hw[s2] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+                lw[s2] = pack2(x0 - __uint_as_float(b0 & 0xffff0000u), x1 - __uint_as_float(b1 & 0xffff0000u));
             }
             const bf16x8_t sh = __builtin_bit_cast(bf16x8_t, hw), sl = __builtin_bit_cast(bf16x8_t, lw);
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
-                // Q' row 16 tb + l16, d = 32 ks + 4 qg + 0..3 and 32 ks + 16 + 4 qg + 0..3
-                const int t = 16 * tb + l16;
-                const bf16x8_t qf = frag(lds_u32x2(Qs, toff<SEGK>(t, 32 * ks + 4 * qg)),
-                                         lds_u32x2(Qs, toff<SEGK>(t, 32 * ks + 16 + 4 * qg)));
+                // Q' row 16 tb + l16, d = 32 ks + 8 qg + 0..7
+                const bf16x8_t qf = __builtin_bit_cast(
+                    bf16x8_t, *reinterpret_cast<const u32x4_t*>(Qs + toff<SEGK>(16 * tb + l16, 32 * ks + 8 * qg)));
                 oq[tb] = mma16(sh, qf, oq[tb]);
                 oq[tb] = mma16(sl, qf, oq[tb]);
             }
@@ -1194,9 +1214,11 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
         for (int db = 0; db < NDB16; ++db)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                // K'^T: rows d = 16 db + l16, tokens 32 ks + 8 qg + 0..7
-                const bf16x8_t kf = frag(tr_read<SEGK>(Ks, 32 * ks + 8 * qg, 16 * db, lane),
-                                         tr_read<SEGK>(Ks, 32 * ks + 8 * qg + 4, 16 * db, lane));
+                // K'^T: row l16 of block db (key column srow with qg -> l16 / 4,
+                // r -> l16 % 4), tokens 32 ks + 8 qg + 0..7
+                const int kc0 = 32 * (db >> 1) + 4 * (db & 1);
+                const bf16x8_t kf = frag(tr_read8<SEGK>(Ks, 32 * ks + 8 * qg, kc0, lane),
+                                         tr_read8<SEGK>(Ks, 32 * ks + 8 * qg + 4, kc0, lane));
                 sacc[db] = mma16(kf, vf[ks], sacc[db]);
                 sacc[db] = mma16(kf, vc[ks], sacc[db]);
             }
@@ -1216,7 +1238,7 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
         for (int db = 0; db < NDB16; ++db)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int d = 16 * db + 4 * qg + r;
+                const int d = srow(db, r);
                 if (d < dkr) p.s_final[sbase + (size_t)d * dvr + ncol] = sacc[db][r];
             }
     }
