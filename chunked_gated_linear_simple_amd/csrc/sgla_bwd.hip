@@ -35,9 +35,9 @@ struct BwdArgs {
 };
 
 template <int DKV, int DKG>
-__global__ __launch_bounds__(NTHREADS) void k_bwd(BwdArgs ba)
+__global__ __launch_bounds__(NTHREADS_W) void k_bwd(BwdArgs ba)
 {
-    constexpr int LDS = cmax(Lay<RDv<DKV>>::LDS, cmax(Lay<RDq<DKG>>::LDS, Lay<RDk<DKG>>::LDS));
+    constexpr int LDS = cmax(LayW<WDv<DKV>>::LDS, cmax(LayW<WDq<DKG>>::LDS, LayW<WDk<DKG>>::LDS));
     __shared__ __attribute__((aligned(16))) char smem[LDS];
     const int nr = ba.role[2].nsl + 2;
     const int b = blockIdx.x;
@@ -47,9 +47,9 @@ __global__ __launch_bounds__(NTHREADS) void k_bwd(BwdArgs ba)
     // one role's operands, picked at run time so that only they are loaded
     const int ri = r < 2 ? r : 2;
     const Args& p = ba.role[ri];
-    if (r == 0) body<RDq<DKG>>(p, unit, 0, smem);
-    else if (r == 1) body<RDk<DKG>>(p, unit, 0, smem);
-    else body<RDv<DKV>>(p, unit, r - 2, smem);
+    if (r == 0) body_wide<WDq<DKG>>(p, unit, 0, smem);
+    else if (r == 1) body_wide<WDk<DKG>>(p, unit, 0, smem);
+    else body_wide<WDv<DKV>>(p, unit, r - 2, smem);
 }
 
 // da[h][d] = sum over sequences n (in order) of part[n H + h][d]
@@ -71,7 +71,7 @@ hipError_t run_bwd(const Args& av, const Args& aq, const Args& ak, hipStream_t s
     ba.role[1] = ak;
     ba.role[2] = av;
     const int grid = ((av.n_units + 7) / 8) * 8 * (av.nsl + 2);
-    hipLaunchKernelGGL((k_bwd<DKV, DKG>), dim3(grid), dim3(NTHREADS), 0, stream, ba);
+    hipLaunchKernelGGL((k_bwd<DKV, DKG>), dim3(grid), dim3(NTHREADS_W), 0, stream, ba);
     return hipGetLastError();
 }
 

@@ -2,7 +2,6 @@
 // tile-scan body in sgla_scan.hpp (method: "Beyond the KV cache: Training and
 // serving i14's Laplace 3B linear attention model on AWS Trainium2 with native
 // PyTorch", section "Challenge 1: Using native PyTorch on Trainium for GLA").
-// One workgroup per (sequence, head, 96-column value slice).
 
 #include "sgla_scan.hpp"
 #include "sgla_internal.h"
@@ -10,29 +9,18 @@
 namespace sgla {
 namespace scan {
 
-template <int DK>
-__global__ __launch_bounds__(NTHREADS) void k_fwd(Args p)
-{
-    __shared__ __attribute__((aligned(16))) char smem[Lay<RFwd<DK>>::LDS];
-    // blockIdx -> (unit, slice); the slices of one unit share an XCD (blocks
-    // are dealt to the eight XCDs round-robin) and so share its L2
-    const int b = blockIdx.x;
-    const int slice = (b >> 3) % p.nsl;
-    const int unit = ((b >> 3) / p.nsl) * 8 + (b & 7);
-    if (unit >= p.n_units) return;
-    body<RFwd<DK>>(p, unit, slice, smem);
-}
-
-// Eight-wave variant (two waves per SIMD).
+// One workgroup of eight waves per (sequence, head, 96-column value slice);
+// the slices of one unit share an XCD (blocks are dealt to the eight XCDs
+// round-robin) and so share its L2.
 template <int DK>
 __global__ __launch_bounds__(NTHREADS_W) void k_fwd_w(Args p)
 {
-    __shared__ __attribute__((aligned(16))) char smem[LayW<RFwd<DK>>::LDS];
+    __shared__ __attribute__((aligned(16))) char smem[LayW<WFwd<DK>>::LDS];
     const int b = blockIdx.x;
     const int slice = (b >> 3) % p.nsl;
     const int unit = ((b >> 3) / p.nsl) * 8 + (b & 7);
     if (unit >= p.n_units) return;
-    body_wide<RFwd<DK>>(p, unit, slice, smem);
+    body_wide<WFwd<DK>>(p, unit, slice, smem);
 }
 
 template <int DK>
