@@ -13,7 +13,7 @@ namespace scan {
 // the slices of one unit share an XCD (blocks are dealt to the eight XCDs
 // round-robin) and so share its L2.
 template <int DK>
-__global__ __launch_bounds__(NTHREADS_W) void k_fwd_w(Args p)
+__global__ __launch_bounds__(NTHREADS_W) void k_fwd(Args p)
 {
     __shared__ __attribute__((aligned(16))) char smem[LayW<WFwd<DK>>::LDS];
     const int b = blockIdx.x;
@@ -27,7 +27,7 @@ template <int DK>
 hipError_t run_fwd(const Args& a, hipStream_t stream)
 {
     const int grid = ((a.n_units + 7) / 8) * 8 * a.nsl;
-    hipLaunchKernelGGL(k_fwd_w<DK>, dim3(grid), dim3(NTHREADS_W), 0, stream, a);
+    hipLaunchKernelGGL(k_fwd<DK>, dim3(grid), dim3(NTHREADS_W), 0, stream, a);
     return hipGetLastError();
 }
 
