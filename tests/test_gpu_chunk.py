@@ -137,6 +137,18 @@ def test_bf16_narrow_dims():
     run_bwd_case(inp, lam, 64)
 
 
+@pytest.mark.parametrize("dk,dv,T", [(8, 8, 70), (40, 136, 97), (64, 96, 130), (96, 152, 33)])
+def test_bf16_padded_and_partial_widths(dk, dv, T):
+    """Widths that are not multiples of the kernels' 32-row blocks or 96-column
+    slices (zero-padded operand columns, a partial second value slice) and
+    lengths with a ragged last tile, forward and backward."""
+    inp = I.chunk_inputs(2, 3, T, dk, dv, "bf16", seed=97 + dk + dv, a_std=0.2, s0_std=0.05,
+                         with_grad=True, dsf_std=0.05)
+    lam = np.array([0.7, 0.98, 0.9995], np.float32)
+    run_fwd_case(inp, lam, 64)
+    run_bwd_case(inp, lam, 64)
+
+
 def test_varlen_bf16_fwd_bwd():
     L = [1, 0, 257, 128, 5, 300]
     cu = I.cu_from_lengths(L)
