@@ -55,7 +55,10 @@ def _load():
                                 _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp]
         lib.orc_decode_step.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                         _dp, _dp, _dp, _dp, _dp, _dp]
-        for f in (lib.orc_decay_schedule, lib.orc_fwd, lib.orc_bwd, lib.orc_decode_step):
+        lib.orc_conv_fwd.argtypes = [ctypes.c_int, ctypes.c_int, _dp, _dp, _dp, _dp, _dp, _dp]
+        lib.orc_conv_decode_step.argtypes = [ctypes.c_int, _dp, _dp, _dp, _dp, _dp]
+        for f in (lib.orc_decay_schedule, lib.orc_fwd, lib.orc_bwd, lib.orc_decode_step,
+                  lib.orc_conv_fwd, lib.orc_conv_decode_step):
             f.restype = None
         _lib = lib
     return _lib
@@ -197,3 +200,48 @@ def bwd(q, k, v, dO, lam, a=None, S0=None, dSf=None, cu_seqlens=None, units=None
     for (n, h) in sorted(da_parts):
         da[h] += da_parts[(n, h)]
     return dq, dkk, dvv, da, dS0
+
+
+# ------------------------------------------------------------ conv prologue
+
+
+def conv_fwd_unit(u, w, b=None, st=None):
+    """One sequence: u [L, D], w [D, 4], b [D] or None, st [3, D] or None ->
+    (y [L, D], st_out [3, D])."""
+    u, w, b, st = _f64(u), _f64(w), _f64(b), _f64(st)
+    L, D = u.shape
+    y = np.zeros((L, D))
+    st_out = np.zeros((3, D))
+    _load().orc_conv_fwd(L, D, _ptr(w), _ptr(b), _ptr(u), _ptr(st), _ptr(y), _ptr(st_out))
+    return y, st_out
+
+
+def conv_fwd(x, w, b=None, st=None, cu_seqlens=None):
+    """x [B, T, D] (or packed [S, D] with cu_seqlens); st [N, 3, D] or None.
+    Returns (y like x, final state [N, 3, D])."""
+    x = np.asarray(x)
+    if cu_seqlens is None:
+        B, T, D = x.shape
+        spans = [(n, None) for n in range(B)]
+    else:
+        D = x.shape[-1]
+        cu = np.asarray(cu_seqlens)
+        spans = [(n, (int(cu[n]), int(cu[n + 1]))) for n in range(len(cu) - 1)]
+    y = np.zeros(x.shape)
+    fin = np.zeros((len(spans), 3, D))
+    for n, sp in spans:
+        s0 = None if st is None else st[n]
+        if sp is None:
+            y[n], fin[n] = conv_fwd_unit(x[n], w, b, s0)
+        else:
+            y[sp[0]:sp[1]], fin[n] = conv_fwd_unit(x[sp[0]:sp[1]], w, b, s0)
+    return y, fin
+
+
+def conv_decode_step_unit(x, w, b, st):
+    """x [D]; st [3, D] float64, updated in place. Returns y [D]."""
+    x, w, b = _f64(x), _f64(w), _f64(b)
+    assert st.dtype == np.float64 and st.flags["C_CONTIGUOUS"]
+    y = np.zeros(x.shape[0])
+    _load().orc_conv_decode_step(x.shape[0], _ptr(w), _ptr(b), _ptr(x), _ptr(st), _ptr(y))
+    return y

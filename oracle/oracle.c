@@ -215,3 +215,83 @@ void orc_decode_step(int d_k, int d_v, double lam, const double* a,
         o[j] = acc + g * v[j];
     }
 }
+
+/* ------------------------------------------------------------------------
+ * Convolution prologue of the mixer. Laplace 3B post, "i14 and the Laplace 3B
+ * architecture": before the QKVG projection every token's (normalised)
+ * residual vector goes through a depthwise causal Conv1d of width 4 with a
+ * SiLU, which hands each position a 4-gram summary of its own and the three
+ * previous tokens (the architecture table lists the same: depthwise causal
+ * Conv1d, kernel width 4, SiLU). Channel by channel, with the filter taps
+ * ordered oldest first (as a PyTorch depthwise Conv1d weight [D, 1, 4] with
+ * three zeros of left padding):
+ *
+ *   y_t[c] = silu(b[c] + sum_{j=0..3} w[c][j] u_{t-3+j}[c]),   silu(x) = x sigmoid(x)
+ *
+ * For serving, the three previous inputs are the per-sequence conv state
+ * ("Inference optimization on Trainium2", "Constant serving state": the fixed
+ * per-sequence state that a generated token reads and updates).
+ */
+static double silu(double x)
+{
+    return x * sigmoid(x);
+}
+
+/* One sequence of L tokens. u_{-3..-1} = st[0..2] (NULL: zero); st_out (may be
+ * NULL, may equal st) receives u_{L-3}, u_{L-2}, u_{L-1}, reaching back into
+ * st when L < 3. */
+void orc_conv_fwd(int L, int D, const double* w, const double* b, const double* u,
+                  const double* st, double* y, double* st_out)
+{
+    for (int t = 0; t < L; ++t) {
+        for (int c = 0; c < D; ++c) {
+            double acc = (b != NULL) ? b[c] : 0.0;
+            for (int j = 0; j < 4; ++j) {
+                const int s = t - 3 + j;
+                double x;
+                if (s >= 0) {
+                    x = u[(size_t)s * D + c];
+                } else {
+                    x = (st != NULL) ? st[(size_t)(3 + s) * D + c] : 0.0;
+                }
+                acc += w[(size_t)c * 4 + j] * x;
+            }
+            y[(size_t)t * D + c] = silu(acc);
+        }
+    }
+    if (st_out != NULL) {
+        double* nxt = (double*)malloc(sizeof(double) * 3 * (size_t)D);
+        for (int j = 0; j < 3; ++j) {
+            const int s = L - 3 + j;
+            for (int c = 0; c < D; ++c) {
+                double x;
+                if (s >= 0) {
+                    x = u[(size_t)s * D + c];
+                } else {
+                    x = (st != NULL) ? st[(size_t)(3 + s) * D + c] : 0.0;
+                }
+                nxt[(size_t)j * D + c] = x;
+            }
+        }
+        memcpy(st_out, nxt, sizeof(double) * 3 * (size_t)D);
+        free(nxt);
+    }
+}
+
+/* One serving step on the conv state in place: y = silu(b + w . [st0, st1, st2, x]),
+ * then the state shifts by one token. */
+void orc_conv_decode_step(int D, const double* w, const double* b, const double* x,
+                          double* st, double* y)
+{
+    for (int c = 0; c < D; ++c) {
+        double acc = (b != NULL) ? b[c] : 0.0;
+        acc += w[(size_t)c * 4 + 0] * st[c];
+        acc += w[(size_t)c * 4 + 1] * st[(size_t)D + c];
+        acc += w[(size_t)c * 4 + 2] * st[(size_t)2 * D + c];
+        acc += w[(size_t)c * 4 + 3] * x[c];
+        y[c] = silu(acc);
+        st[c] = st[(size_t)D + c];
+        st[(size_t)D + c] = st[(size_t)2 * D + c];
+        st[(size_t)2 * D + c] = x[c];
+    }
+}

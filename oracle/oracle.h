@@ -53,6 +53,18 @@ void orc_decode_step(int d_k, int d_v, double lam, const double* a,
                      const double* q, const double* k, const double* v,
                      double* S, double* o);
 
+/* Convolution prologue (depthwise causal, width 4, SiLU) for ONE sequence:
+ *   y_t[c] = silu(b[c] + sum_{j=0..3} w[c][j] u_{t-3+j}[c])
+ * u, y : [L][D]; w : [D][4] (oldest tap first); b : [D] or NULL (zero);
+ * st, st_out : [3][D] = u_{-3}, u_{-2}, u_{-1} before / u_{L-3..L-1} after
+ * (NULL st means zero history; st_out may be NULL or equal st). */
+void orc_conv_fwd(int L, int D, const double* w, const double* b, const double* u,
+                  const double* st, double* y, double* st_out);
+
+/* One conv decode step, state [3][D] in place. */
+void orc_conv_decode_step(int D, const double* w, const double* b, const double* x,
+                          double* st, double* y);
+
 #ifdef __cplusplus
 }
 #endif

@@ -258,6 +258,75 @@ def check_bwd_lambda_zero():
     _close(dS0, np.zeros((dk, dv)), 0, "lam=0 dS0")
 
 
+# ---------------------------------------------------------- conv prologue
+
+
+def _silu(x):
+    return x * expit(x)
+
+
+def _conv_case(seed, L, D, st=True, bias=True):
+    r = _rng(seed)
+    u = r.standard_normal((L, D))
+    w = r.standard_normal((D, 4)) * 0.5
+    b = r.standard_normal(D) * 0.3 if bias else None
+    s0 = r.standard_normal((3, D)) if st else None
+    return u, w, b, s0
+
+
+def check_conv_correlate():
+    """Against numpy's cross-correlation, channel by channel: with the history
+    p = [u_-3, u_-2, u_-1, u_0, ...], y_t = silu(b + sum_j w_j p_{t+j})."""
+    for st in (True, False):
+        u, w, b, s0 = _conv_case(31 + st, 11, 5, st=st)
+        y, _ = oracle.conv_fwd_unit(u, w, b, s0)
+        hist = s0 if s0 is not None else np.zeros((3, 5))
+        p = np.concatenate([hist, u], axis=0)
+        ref = np.stack([np.correlate(p[:, c], w[c], mode="valid") for c in range(5)], axis=1) + b
+        _close(y, _silu(ref), 1e-13, "conv vs correlate")
+
+
+def check_conv_single_taps():
+    """w = e_3 (current token only): y = silu(u + b). w = e_0: y_t = silu(u_{t-3}),
+    the first three from the conv state."""
+    u, _, b, s0 = _conv_case(33, 9, 4)
+    w = np.zeros((4, 4))
+    w[:, 3] = 1.0
+    y, _ = oracle.conv_fwd_unit(u, w, b, s0)
+    _close(y, _silu(u + b), 1e-14, "current tap")
+    w = np.zeros((4, 4))
+    w[:, 0] = 1.0
+    y, _ = oracle.conv_fwd_unit(u, w, None, s0)
+    _close(y, _silu(np.concatenate([s0, u[:-3]], axis=0)), 1e-14, "oldest tap")
+
+
+def check_conv_state_carry():
+    """Running [0, L) at once == [0, t0) then [t0, L) from the carried state,
+    also for pieces shorter than the three-token state."""
+    u, w, b, s0 = _conv_case(35, 10, 6)
+    y, sf = oracle.conv_fwd_unit(u, w, b, s0)
+    for cuts in ([4], [1, 2], [2, 3, 9]):
+        st = s0
+        ys = []
+        edges = [0] + cuts + [10]
+        for a0, a1 in zip(edges, edges[1:]):
+            yp, st = oracle.conv_fwd_unit(u[a0:a1], w, b, st)
+            ys.append(yp)
+        _close(np.concatenate(ys, axis=0), y, 1e-14, f"carry y {cuts}")
+        _close(st, sf, 0, f"carry state {cuts}")
+    _close(sf, u[-3:], 0, "final state = last three inputs")
+
+
+def check_conv_decode_steps():
+    """Decode steps from the conv state reproduce the sequence forward."""
+    u, w, b, s0 = _conv_case(37, 6, 5)
+    y, sf = oracle.conv_fwd_unit(u, w, b, s0)
+    st = s0.copy()
+    yd = np.stack([oracle.conv_decode_step_unit(u[t], w, b, st) for t in range(6)])
+    _close(yd, y, 1e-14, "conv decode y")
+    _close(st, sf, 0, "conv decode state")
+
+
 ALL_CHECKS = [
     check_schedule_printed_values,
     check_schedule_geometric,
@@ -271,4 +340,8 @@ ALL_CHECKS = [
     check_decode_brute_force,
     check_bwd_finite_differences,
     check_bwd_lambda_zero,
+    check_conv_correlate,
+    check_conv_single_taps,
+    check_conv_state_carry,
+    check_conv_decode_steps,
 ]

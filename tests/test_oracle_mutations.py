@@ -43,6 +43,16 @@ MUTATIONS = [
     ("decode no decay", "S[(size_t)i * d_v + j] = lam * S[(size_t)i * d_v + j] + k[i] * v[j];",
      "S[(size_t)i * d_v + j] = S[(size_t)i * d_v + j] + k[i] * v[j];"),
     ("decode gate off", "o[j] = acc + g * v[j];", "o[j] = acc + 0.5 * v[j];"),
+    ("conv taps reversed", "acc += w[(size_t)c * 4 + j] * x;", "acc += w[(size_t)c * 4 + (3 - j)] * x;"),
+    ("conv bias dropped", "double acc = (b != NULL) ? b[c] : 0.0;\n            for (int j = 0; j < 4; ++j) {",
+     "double acc = 0.0;\n            for (int j = 0; j < 4; ++j) {"),
+    ("conv history ignored", "x = (st != NULL) ? st[(size_t)(3 + s) * D + c] : 0.0;\n                }\n                acc +=",
+     "x = 0.0;\n                }\n                acc +="),
+    ("silu is sigmoid", "return x * sigmoid(x);", "return sigmoid(x);"),
+    ("conv final state one token early", "const int s = L - 3 + j;", "const int s = L - 4 + j;"),
+    ("conv decode state not shifted", "st[c] = st[(size_t)D + c];", "st[c] = st[c];"),
+    ("conv decode tap 2 reads x", "acc += w[(size_t)c * 4 + 2] * st[(size_t)2 * D + c];",
+     "acc += w[(size_t)c * 4 + 2] * x[c];"),
 ]
 
 
@@ -58,7 +68,8 @@ def test_mutation_is_caught(name, find, repl, tmp_path):
                            "-o", str(so), str(mutated), "-lm"])
     good = oracle._load()
     bad = ctypes.CDLL(str(so))
-    for fn in ("orc_decay_schedule", "orc_fwd", "orc_bwd", "orc_decode_step"):
+    for fn in ("orc_decay_schedule", "orc_fwd", "orc_bwd", "orc_decode_step", "orc_conv_fwd",
+               "orc_conv_decode_step"):
         getattr(bad, fn).argtypes = getattr(good, fn).argtypes
         getattr(bad, fn).restype = None
     caught = []
