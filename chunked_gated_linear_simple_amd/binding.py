@@ -60,6 +60,10 @@ def lib() -> ctypes.CDLL:
         L.sgla_decode_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
                                        _i, _vp]
         L.sgla_decode_step.restype = _i
+        L.sgla_conv_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]
+        L.sgla_conv_fwd.restype = _i
+        L.sgla_conv_decode_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]
+        L.sgla_conv_decode_step.restype = _i
         _lib = L
     return _lib
 
@@ -211,3 +215,51 @@ def sgla_decode_step(q, k, v, lam, a, state, o=None, slot=None):
                                   _ptr(slot), _ptr(o), N, P, H, d_k, d_v, _dtype_code(q),
                                   _stream(dev)))
     return o
+
+
+def sgla_conv_fwd(u, w, b=None, init_state=None, final_state=None, y=None, cu_seqlens=None,
+                  want_final=False):
+    """Conv prologue over whole sequences. u [B, T, D] (or [T, D] packed with
+    cu_seqlens [N+1] int32), w [D, 4] fp32, b [D] fp32 or None, init_state /
+    final_state [N, 3, D] fp32 or None. Returns (y, final_state or None)."""
+    dev = u.device
+    if cu_seqlens is None:
+        Bn, T, D = u.shape
+        n_seq = Bn
+    else:
+        T, D = u.shape
+        Bn = 1
+        n_seq = cu_seqlens.numel() - 1
+    _need(u, "u", device=dev)
+    _need(w, "w", torch.float32, dev, (D, 4))
+    _need(b, "b", torch.float32, dev, (D,))
+    _need(init_state, "init_state", torch.float32, dev, (n_seq, 3, D))
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev, (n_seq + 1,))
+    if final_state is None and want_final:
+        final_state = torch.empty((n_seq, 3, D), dtype=torch.float32, device=dev)
+    _need(final_state, "final_state", torch.float32, dev, (n_seq, 3, D))
+    if y is None:
+        y = torch.empty_like(u)
+    _need(y, "y", u.dtype, dev, tuple(u.shape))
+    _check(lib().sgla_conv_fwd(_ptr(u), _ptr(w), _ptr(b), _ptr(init_state), _ptr(final_state),
+                               _ptr(y), _ptr(cu_seqlens), n_seq, Bn, T, D, _dtype_code(u),
+                               _stream(dev)))
+    return y, final_state
+
+
+def sgla_conv_decode_step(x, w, b, state, y=None, slot=None):
+    """One in-place conv decode step. x [N, D], state [P, 3, D] fp32. Returns y [N, D]."""
+    dev = x.device
+    N, D = x.shape
+    P = state.shape[0]
+    _need(x, "x", device=dev)
+    _need(w, "w", torch.float32, dev, (D, 4))
+    _need(b, "b", torch.float32, dev, (D,))
+    _need(state, "state", torch.float32, dev, (P, 3, D))
+    _need(slot, "slot", torch.int32, dev, (N,))
+    if y is None:
+        y = torch.empty_like(x)
+    _need(y, "y", x.dtype, dev, (N, D))
+    _check(lib().sgla_conv_decode_step(_ptr(x), _ptr(w), _ptr(b), _ptr(state), _ptr(slot),
+                                       _ptr(y), N, P, D, _dtype_code(x), _stream(dev)))
+    return y

@@ -237,4 +237,63 @@ sgla_status sgla_decode_step(const void* q, const void* k, const void* v, const 
     return ok();
 }
 
+sgla_status sgla_conv_fwd(const void* u, const float* w, const float* b, const float* init_state,
+                          float* final_state, void* y, const int32_t* cu_seqlens, int n_seq, int B, int T,
+                          int D, sgla_dtype dtype, void* hip_stream)
+{
+    REQUIRE_PTR(u);
+    REQUIRE_PTR(w);
+    REQUIRE_PTR(y);
+    OPTIONAL_PTR(b);
+    OPTIONAL_PTR(init_state);
+    OPTIONAL_PTR(final_state);
+    if (dtype != SGLA_F32 && dtype != SGLA_BF16)
+        return fail(SGLA_ERR_INVALID_ARG, "dtype %d is not SGLA_F32 or SGLA_BF16", (int)dtype);
+    if (B <= 0 || T <= 0 || D <= 0)
+        return fail(SGLA_ERR_INVALID_ARG, "sizes must be positive (B=%d T=%d D=%d)", B, T, D);
+    if (cu_seqlens != nullptr) {
+        if (B != 1) return fail(SGLA_ERR_INVALID_ARG, "packed sequences need B = 1 (got %d)", B);
+        if (n_seq <= 0) return fail(SGLA_ERR_INVALID_ARG, "n_seq must be positive (got %d)", n_seq);
+        if (!aligned16(cu_seqlens)) return fail(SGLA_ERR_INVALID_ARG, "cu_seqlens is not 16-byte aligned");
+    } else if (n_seq != B) {
+        return fail(SGLA_ERR_INVALID_ARG, "dense input needs n_seq == B (got %d, %d)", n_seq, B);
+    }
+    if ((double)B * T * D > 4.0e9) return fail(SGLA_ERR_INVALID_ARG, "B*T*D too large");
+    const int vec = (dtype == SGLA_BF16) ? 8 : 4;
+    if (D % vec != 0)
+        return fail(SGLA_ERR_UNSUPPORTED, "D must be a multiple of %d for this dtype (got %d)", vec, D);
+    const size_t nb = (size_t)B * T * D * (dtype == SGLA_BF16 ? 2 : 4);
+    if (overlaps(y, nb, u, nb)) return fail(SGLA_ERR_INVALID_ARG, "y must not overlap u");
+    hipError_t e = sgla::launch_conv_fwd(dtype == SGLA_BF16, u, w, b, init_state, final_state, y, cu_seqlens,
+                                         n_seq, B, T, D, reinterpret_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(SGLA_ERR_HIP, "conv_fwd launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+sgla_status sgla_conv_decode_step(const void* x, const float* w, const float* b, float* state,
+                                  const int32_t* slot, void* y, int N, int P, int D, sgla_dtype dtype,
+                                  void* hip_stream)
+{
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(w);
+    REQUIRE_PTR(state);
+    REQUIRE_PTR(y);
+    OPTIONAL_PTR(b);
+    OPTIONAL_PTR(slot);
+    if (dtype != SGLA_F32 && dtype != SGLA_BF16)
+        return fail(SGLA_ERR_INVALID_ARG, "dtype %d is not SGLA_F32 or SGLA_BF16", (int)dtype);
+    if (N <= 0 || P <= 0 || D <= 0)
+        return fail(SGLA_ERR_INVALID_ARG, "N, P, D must be positive (N=%d P=%d D=%d)", N, P, D);
+    if (slot == nullptr && P < N)
+        return fail(SGLA_ERR_INVALID_ARG, "without slot, the pool needs P >= N (P=%d N=%d)", P, N);
+    if ((double)P * 3 * D > 4.0e9 || (double)N * D > 4.0e9) return fail(SGLA_ERR_INVALID_ARG, "N*D or P*D too large");
+    const int vec = (dtype == SGLA_BF16) ? 8 : 4;
+    if (D % vec != 0)
+        return fail(SGLA_ERR_UNSUPPORTED, "D must be a multiple of %d for this dtype (got %d)", vec, D);
+    hipError_t e = sgla::launch_conv_decode(dtype == SGLA_BF16, x, w, b, state, slot, y, N, P, D,
+                                            reinterpret_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(SGLA_ERR_HIP, "conv decode launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // extern "C"

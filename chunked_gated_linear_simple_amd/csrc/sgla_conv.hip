@@ -1,0 +1,334 @@
+// Convolution prologue of the mixer for gfx950: depthwise causal Conv1d of
+// width 4 with SiLU, over whole sequences and as a decode step on a pool of
+// per-sequence conv states.
+//
+// Method: "Beyond the KV cache: Training and serving i14's Laplace 3B linear
+// attention model on AWS Trainium2 with native PyTorch", section "i14 and the
+// Laplace 3B architecture" (normalisation-and-convolution paragraph; the
+// architecture table's Conv row): each channel c of token t is
+//
+//   y_t[c] = silu(b[c] + sum_{j=0..3} w[c][j] u_{t-3+j}[c]),   silu(x) = x sigmoid(x)
+//
+// with the three inputs before a sequence taken from its conv state (or zero),
+// and section "Inference optimization on Trainium2" ("Constant serving
+// state") for the state that a generated token reads and shifts.
+//
+// The operation is a pure stream (one read and one write of each activation,
+// 4 multiply-adds and a SiLU per element), so the kernels are built for HBM
+// bandwidth: a thread owns one 16-byte group of channels (8 bf16 or 4 fp32)
+// and walks a run of consecutive tokens, keeping the three previous inputs in
+// registers, so every input is read once (plus a three-token halo per run).
+// Consecutive threads own consecutive channel groups, so each token row is
+// read and written as contiguous 1 KB wave accesses.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sgla_internal.h"
+
+namespace sgla {
+namespace {
+
+typedef unsigned short u16;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int RUN = 32;          // tokens per thread
+constexpr int CONV_THREADS = 256;
+
+__device__ __forceinline__ float silu_f(float x)
+{
+    // x / (1 + e^-x); e^-x overflows to inf for very negative x, giving -0
+    const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * x);
+    return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// A channel group: 8 bf16 or 4 fp32 values in 16 bytes.
+template <typename E> struct Grp;
+template <> struct Grp<u16> {
+    static constexpr int V = 8;
+    static __device__ __forceinline__ void load(const u16* p, float* x)
+    {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(w[i] << 16);
+            x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+    static __device__ __forceinline__ void store(u16* p, const float* y)
+    {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        u32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            bf16x2 v = {static_cast<__bf16>(y[2 * i]), static_cast<__bf16>(y[2 * i + 1])};
+            w[i] = __builtin_bit_cast(uint32_t, v);
+        }
+        *reinterpret_cast<u32x4*>(p) = w;
+    }
+};
+template <> struct Grp<float> {
+    static constexpr int V = 4;
+    static __device__ __forceinline__ void load(const float* p, float* x)
+    {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = v[i];
+    }
+    static __device__ __forceinline__ void store(float* p, const float* y)
+    {
+        const f32x4 v = {y[0], y[1], y[2], y[3]};
+        *reinterpret_cast<f32x4*>(p) = v;
+    }
+};
+
+struct Seqs {
+    const int32_t* cu;  // NULL when dense
+    int n_seq, T, S;    // S = total token rows
+    // token range of sequence n, clamped to [0, S]
+    __device__ __forceinline__ void range(int n, int& s0, int& s1) const
+    {
+        if (cu == nullptr) {
+            s0 = n * T;
+            s1 = s0 + T;
+        } else {
+            s0 = min(max(cu[n], 0), S);
+            s1 = min(max(cu[n + 1], s0), S);
+        }
+    }
+    // the sequence holding row t (the last n with start <= t)
+    __device__ __forceinline__ int find(int t) const
+    {
+        if (cu == nullptr) return t / T;
+        int lo = 0, hi = n_seq - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (min(max(cu[mid], 0), S) <= t) lo = mid;
+            else hi = mid - 1;
+        }
+        return lo;
+    }
+};
+
+// y for rows [RUN * blockIdx.x, ...) of channel group blockIdx.y * 256 + tid
+template <typename E>
+__global__ __launch_bounds__(CONV_THREADS) void k_conv_fwd(const E* __restrict__ u, const float* __restrict__ w,
+                                                           const float* __restrict__ b,
+                                                           const float* __restrict__ init, E* __restrict__ y,
+                                                           Seqs sq, int D)
+{
+    constexpr int V = Grp<E>::V;
+    const int grp = blockIdx.y * CONV_THREADS + threadIdx.x;
+    if (grp * V >= D) return;
+    const int c0 = grp * V;
+    const int t0 = blockIdx.x * RUN;
+    if (t0 >= sq.S) return;
+    const int t1 = min(t0 + RUN, sq.S);
+
+    float wt[V][4], bias[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const f32x4 wv = *reinterpret_cast<const f32x4*>(w + (size_t)(c0 + i) * 4);
+        wt[i][0] = wv[0];
+        wt[i][1] = wv[1];
+        wt[i][2] = wv[2];
+        wt[i][3] = wv[3];
+        bias[i] = (b != nullptr) ? b[c0 + i] : 0.0f;
+    }
+
+    int n = sq.find(t0), s0, s1;
+    sq.range(n, s0, s1);
+    // h[j] = u_{t-3+j} for the next token t
+    float h[3][V];
+    auto history = [&](int t) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int p = t - 3 + j;
+            if (p >= s0) {
+                Grp<E>::load(u + (size_t)p * D + c0, h[j]);
+            } else if (init != nullptr) {
+                const f32x4* sp = reinterpret_cast<const f32x4*>(init + ((size_t)n * 3 + (3 + p - s0)) * D + c0);
+#pragma unroll
+                for (int i = 0; i < V; i += 4) {
+                    const f32x4 v = sp[i / 4];
+                    h[j][i] = v[0];
+                    h[j][i + 1] = v[1];
+                    h[j][i + 2] = v[2];
+                    h[j][i + 3] = v[3];
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < V; ++i) h[j][i] = 0.0f;
+            }
+        }
+    };
+    history(t0);
+    for (int t = t0; t < t1; ++t) {
+        if (t >= s1) {
+            // next non-empty sequence: its history is its own conv state
+            while (t >= s1 && n + 1 < sq.n_seq) {
+                ++n;
+                sq.range(n, s0, s1);
+            }
+            if (t >= s1) break;  // rows past the last sequence belong to none
+            history(t);
+        }
+        float x[V], out[V];
+        Grp<E>::load(u + (size_t)t * D + c0, x);
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            float acc = bias[i];
+            acc = fmaf(wt[i][0], h[0][i], acc);
+            acc = fmaf(wt[i][1], h[1][i], acc);
+            acc = fmaf(wt[i][2], h[2][i], acc);
+            acc = fmaf(wt[i][3], x[i], acc);
+            out[i] = silu_f(acc);
+            h[0][i] = h[1][i];
+            h[1][i] = h[2][i];
+            h[2][i] = x[i];
+        }
+        Grp<E>::store(y + (size_t)t * D + c0, out);
+    }
+}
+
+// final[n] = the last three inputs of sequence n (reaching into init)
+template <typename E>
+__global__ __launch_bounds__(CONV_THREADS) void k_conv_state(const E* __restrict__ u, const float* init,
+                                                             float* fin, Seqs sq, int D)
+{
+    constexpr int V = Grp<E>::V;
+    const int grp = blockIdx.y * CONV_THREADS + threadIdx.x;
+    const int n = blockIdx.x;
+    if (grp * V >= D) return;
+    const int c0 = grp * V;
+    int s0, s1;
+    sq.range(n, s0, s1);
+    const int L = s1 - s0;
+    float h[3][V];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int p = L - 3 + j;
+        if (p >= 0) {
+            Grp<E>::load(u + (size_t)(s0 + p) * D + c0, h[j]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < V; ++i)
+                h[j][i] = (init != nullptr) ? init[((size_t)n * 3 + (3 + p)) * D + c0 + i] : 0.0f;
+        }
+    }
+    // all reads above happen before any write: fin may equal init
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+        for (int i = 0; i < V; ++i) fin[((size_t)n * 3 + j) * D + c0 + i] = h[j][i];
+}
+
+// one decode step: thread = (sequence, 4 channels)
+template <typename E>
+__global__ __launch_bounds__(CONV_THREADS) void k_conv_decode(const E* __restrict__ x, const float* __restrict__ w,
+                                                              const float* __restrict__ b, float* __restrict__ state,
+                                                              const int32_t* __restrict__ slot, E* __restrict__ y,
+                                                              int N, int P, int D)
+{
+    const int grp = blockIdx.y * CONV_THREADS + threadIdx.x;
+    const int n = blockIdx.x;
+    if (grp * 4 >= D) return;
+    const int c0 = grp * 4;
+    const int page = (slot != nullptr) ? slot[n] : n;
+    E* yr = y + (size_t)n * D + c0;
+    if (page < 0 || page >= P) {
+        if constexpr (sizeof(E) == 2) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) reinterpret_cast<u16*>(yr)[i] = 0x7fc0;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) reinterpret_cast<float*>(yr)[i] = __builtin_nanf("");
+        }
+        return;
+    }
+    f32x4* st = reinterpret_cast<f32x4*>(state + (size_t)page * 3 * D + c0);
+    const size_t rs = D / 4;  // one state row in f32x4 units
+    const f32x4 s0 = st[0], s1 = st[rs], s2 = st[2 * rs];
+    float xv[4];
+    const E* xr = x + (size_t)n * D + c0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (sizeof(E) == 2)
+            xv[i] = __uint_as_float((uint32_t)reinterpret_cast<const u16*>(xr)[i] << 16);
+        else
+            xv[i] = reinterpret_cast<const float*>(xr)[i];
+    }
+    float out[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f32x4 wv = *reinterpret_cast<const f32x4*>(w + (size_t)(c0 + i) * 4);
+        float acc = (b != nullptr) ? b[c0 + i] : 0.0f;
+        acc = fmaf(wv[0], s0[i], acc);
+        acc = fmaf(wv[1], s1[i], acc);
+        acc = fmaf(wv[2], s2[i], acc);
+        acc = fmaf(wv[3], xv[i], acc);
+        out[i] = silu_f(acc);
+    }
+    st[0] = s1;
+    st[rs] = s2;
+    const f32x4 xn = {xv[0], xv[1], xv[2], xv[3]};
+    st[2 * rs] = xn;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (sizeof(E) == 2) {
+            reinterpret_cast<u16*>(yr)[i] = __builtin_bit_cast(u16, static_cast<__bf16>(out[i]));
+        } else {
+            reinterpret_cast<float*>(yr)[i] = out[i];
+        }
+    }
+}
+
+template <typename E>
+hipError_t run_conv_fwd(const void* u, const float* w, const float* b, const float* init, float* fin,
+                        void* y, const int32_t* cu, int n_seq, int B, int T, int D, hipStream_t stream)
+{
+    constexpr int V = Grp<E>::V;
+    Seqs sq{cu, n_seq, T, cu != nullptr ? T : B * T};
+    const int groups = D / V;
+    const dim3 grid((sq.S + RUN - 1) / RUN, (groups + CONV_THREADS - 1) / CONV_THREADS);
+    if (sq.S > 0) {
+        hipLaunchKernelGGL(k_conv_fwd<E>, grid, dim3(CONV_THREADS), 0, stream, reinterpret_cast<const E*>(u), w, b,
+                           init, reinterpret_cast<E*>(y), sq, D);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (fin != nullptr) {
+        const dim3 g2(n_seq, (groups + CONV_THREADS - 1) / CONV_THREADS);
+        hipLaunchKernelGGL(k_conv_state<E>, g2, dim3(CONV_THREADS), 0, stream, reinterpret_cast<const E*>(u), init,
+                           fin, sq, D);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_conv_fwd(int bf16, const void* u, const float* w, const float* b, const float* init_state,
+                           float* final_state, void* y, const int32_t* cu, int n_seq, int B, int T, int D,
+                           hipStream_t stream)
+{
+    if (bf16) return run_conv_fwd<u16>(u, w, b, init_state, final_state, y, cu, n_seq, B, T, D, stream);
+    return run_conv_fwd<float>(u, w, b, init_state, final_state, y, cu, n_seq, B, T, D, stream);
+}
+
+hipError_t launch_conv_decode(int bf16, const void* x, const float* w, const float* b, float* state,
+                              const int32_t* slot, void* y, int N, int P, int D, hipStream_t stream)
+{
+    const dim3 grid(N, (D / 4 + CONV_THREADS - 1) / CONV_THREADS);
+    if (bf16)
+        hipLaunchKernelGGL(k_conv_decode<u16>, grid, dim3(CONV_THREADS), 0, stream,
+                           reinterpret_cast<const u16*>(x), w, b, state, slot, reinterpret_cast<u16*>(y), N, P, D);
+    else
+        hipLaunchKernelGGL(k_conv_decode<float>, grid, dim3(CONV_THREADS), 0, stream,
+                           reinterpret_cast<const float*>(x), w, b, state, slot, reinterpret_cast<float*>(y), N,
+                           P, D);
+    return hipGetLastError();
+}
+
+}  // namespace sgla

@@ -45,6 +45,14 @@ hipError_t launch_decode_step(int bf16, const void* q, const void* k, const void
                               const int32_t* slot, void* o, int N, int P, int H, int d_k,
                               int d_v, hipStream_t stream);
 
+// Convolution prologue (sgla_conv.hip).
+hipError_t launch_conv_fwd(int bf16, const void* u, const float* w, const float* b,
+                           const float* init_state, float* final_state, void* y,
+                           const int32_t* cu, int n_seq, int B, int T, int D, hipStream_t stream);
+
+hipError_t launch_conv_decode(int bf16, const void* x, const float* w, const float* b, float* state,
+                              const int32_t* slot, void* y, int N, int P, int D, hipStream_t stream);
+
 }  // namespace sgla
 
 #endif

@@ -109,3 +109,22 @@ def decode_token_inputs(seed: int, step: int, N: int, H: int, d_k: int, d_v: int
     k = gaussian(seed, base + 1, (N, H, d_k))
     v = gaussian(seed, base + 2, (N, H, d_v))
     return store(q, dtype), store(k, dtype), store(v, dtype)
+
+
+STREAM_CONV = 2000  # conv prologue: u, w, b, init state, decode tokens 2004 + step
+
+
+def conv_inputs(seed: int, shape, D: int, dtype: str, n_seq: int, w_std: float = 0.5,
+                b_std: float = 0.1, s0_std: float = 1.0, bias: bool = True, state: bool = True):
+    """Seeded inputs of the conv prologue: u (shape, last axis D) in the storage
+    dtype, taps w [D, 4], bias b [D] and initial conv states [n_seq, 3, D] in fp32
+    (the states hold past inputs, so they are drawn like u and rounded to the
+    input dtype's values)."""
+    u = store(gaussian(seed, STREAM_CONV, tuple(shape)), dtype)
+    w = gaussian(seed, STREAM_CONV + 1, (D, 4), w_std)
+    b = gaussian(seed, STREAM_CONV + 2, (D,), b_std) if bias else None
+    s0 = None
+    if state:
+        s0 = gaussian(seed, STREAM_CONV + 3, (n_seq, 3, D), s0_std)
+        s0 = widen(store(s0, dtype), dtype).astype(np.float32)
+    return {"u": u, "w": w, "b": b, "S0": s0, "dtype": dtype, "D": D, "N": n_seq}

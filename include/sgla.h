@@ -187,6 +187,52 @@ sgla_status sgla_decode_step(const void* q, const void* k, const void* v,
                              int N, int P, int H, int d_k, int d_v,
                              sgla_dtype dtype, void* hip_stream);
 
+/*
+ * Convolution prologue of the mixer (the step before the QKVG projection),
+ * over whole sequences. Laplace 3B post, "i14 and the Laplace 3B
+ * architecture", normalisation-and-convolution paragraph and the architecture
+ * table's Conv row: every channel of every token goes through a depthwise
+ * causal Conv1d of width 4 with a SiLU, a 4-gram summary of the token and its
+ * three predecessors:
+ *   y_t[c] = silu(b[c] + sum_{j=0..3} w[c][j] u_{t-3+j}[c]),   silu(x) = x sigmoid(x)
+ * Taps are oldest first (a PyTorch depthwise Conv1d weight [D, 1, 4] with
+ * three zeros of left padding). Before the first token of a sequence the three
+ * previous inputs are that sequence's conv state, or zero.
+ *
+ * u, y:        [B, T, D] (dtype); packed (cu_seqlens != NULL): [T, D] with
+ *              B = 1, sequence n holding rows [cu_seqlens[n], cu_seqlens[n+1]).
+ *              y must not alias u.
+ * w:           [D, 4] fp32 taps.   b: [D] fp32 bias, or NULL = none.
+ * init_state:  [N, 3, D] fp32, row j = u_{-3+j} of sequence n, or NULL = zero.
+ * final_state: [N, 3, D] fp32 or NULL: row j = u_{L-3+j} of sequence n (reaching
+ *              into init_state when L < 3); may equal init_state.
+ * n_seq:       N (= B when dense).
+ * Supported: D a multiple of 8 (bf16) or 4 (fp32). All pointers 16-byte aligned.
+ * Errors: SGLA_ERR_INVALID_ARG (NULL required pointer, non-positive size,
+ * misaligned pointer), SGLA_ERR_UNSUPPORTED (D), SGLA_ERR_HIP (launch).
+ */
+sgla_status sgla_conv_fwd(const void* u, const float* w, const float* b,
+                          const float* init_state, float* final_state, void* y,
+                          const int32_t* cu_seqlens, int n_seq, int B, int T, int D,
+                          sgla_dtype dtype, void* hip_stream);
+
+/*
+ * One conv decode step for N sequences, in place on their conv states (the
+ * per-sequence serving state of "Inference optimization on Trainium2",
+ * "Constant serving state", next to the mixer state):
+ *   y[c] = silu(b[c] + w[c][0] s0[c] + w[c][1] s1[c] + w[c][2] s2[c] + w[c][3] x[c]);
+ *   (s0, s1, s2) <- (s1, s2, x)
+ * x, y:   [N, D] (dtype).   w, b: as sgla_conv_fwd.
+ * state:  [P, 3, D] fp32 pool, read and written in place.
+ * slot:   [N] int32 page index, or NULL (sequence n uses page n, P >= N).
+ *         Entries must be distinct; one outside [0, P) skips that sequence
+ *         and writes NaN to its y.
+ * Supported and errors: as sgla_conv_fwd.
+ */
+sgla_status sgla_conv_decode_step(const void* x, const float* w, const float* b,
+                                  float* state, const int32_t* slot, void* y,
+                                  int N, int P, int D, sgla_dtype dtype, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

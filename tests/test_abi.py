@@ -28,6 +28,7 @@ def test_exports_every_declared_symbol(L):
     declared = B.declared_functions()
     assert set(declared) >= {"sgla_decay_schedule", "sgla_chunk_fwd", "sgla_chunk_bwd",
                              "sgla_chunk_bwd_workspace_bytes", "sgla_decode_step",
+                             "sgla_conv_fwd", "sgla_conv_decode_step",
                              "sgla_last_error", "sgla_status_str", "sgla_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -73,7 +74,7 @@ def test_decay_schedule_rejects(L, args):
 BASE = 0x7F0000000000
 P = {n: BASE + i * 0x100000000 for i, n in enumerate(
     ["q", "k", "v", "lam", "a", "s0", "sf", "o", "cu", "dO", "dq", "dk", "dv", "da", "ds0", "ws",
-     "state", "slot"])}
+     "state", "slot", "u", "w", "b", "y"])}
 
 
 def fwd_args(**kw):
@@ -194,3 +195,60 @@ def test_product_path_never_touches_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
                 assert "liboracle" not in text and "orc_" not in text, f
+
+
+def conv_args(**kw):
+    a = dict(u=P["u"], w=P["w"], b=P["b"], s0=P["s0"], sf=P["sf"], y=P["y"], cu=None, n_seq=2,
+             B=2, T=64, D=3072, dt=B.SGLA_BF16)
+    a.update(kw)
+    return [a["u"], a["w"], a["b"], a["s0"], a["sf"], a["y"], a["cu"], a["n_seq"], a["B"], a["T"],
+            a["D"], a["dt"], None]
+
+
+CONV_BAD = [
+    ("u null", dict(u=None), B.SGLA_ERR_INVALID_ARG),
+    ("w null", dict(w=None), B.SGLA_ERR_INVALID_ARG),
+    ("y null", dict(y=None), B.SGLA_ERR_INVALID_ARG),
+    ("b misaligned", dict(b=P["b"] + 4), B.SGLA_ERR_INVALID_ARG),
+    ("init misaligned", dict(s0=P["s0"] + 8), B.SGLA_ERR_INVALID_ARG),
+    ("D zero", dict(D=0), B.SGLA_ERR_INVALID_ARG),
+    ("T negative", dict(T=-1), B.SGLA_ERR_INVALID_ARG),
+    ("bad dtype", dict(dt=3), B.SGLA_ERR_INVALID_ARG),
+    ("bf16 D not mult 8", dict(D=3076), B.SGLA_ERR_UNSUPPORTED),
+    ("f32 D not mult 4", dict(D=3074, dt=B.SGLA_F32), B.SGLA_ERR_UNSUPPORTED),
+    ("y aliases u", dict(y=P["u"]), B.SGLA_ERR_INVALID_ARG),
+    ("y overlaps u", dict(y=P["u"] + 4096), B.SGLA_ERR_INVALID_ARG),
+    ("dense n_seq != B", dict(n_seq=3), B.SGLA_ERR_INVALID_ARG),
+    ("packed with B=2", dict(cu=P["cu"], n_seq=2), B.SGLA_ERR_INVALID_ARG),
+    ("cu misaligned", dict(cu=P["cu"] + 4, n_seq=2, B=1), B.SGLA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", CONV_BAD, ids=[x[0] for x in CONV_BAD])
+def test_conv_fwd_rejects(L, name, kw, code):
+    assert L.sgla_conv_fwd(*conv_args(**kw)) == code
+    assert L.sgla_last_error().decode() != ""
+
+
+def conv_dec_args(**kw):
+    a = dict(x=P["u"], w=P["w"], b=P["b"], state=P["state"], slot=None, y=P["y"], N=8, Pg=8,
+             D=3072, dt=B.SGLA_BF16)
+    a.update(kw)
+    return [a["x"], a["w"], a["b"], a["state"], a["slot"], a["y"], a["N"], a["Pg"], a["D"],
+            a["dt"], None]
+
+
+CONV_DEC_BAD = [
+    ("x null", dict(x=None), B.SGLA_ERR_INVALID_ARG),
+    ("state null", dict(state=None), B.SGLA_ERR_INVALID_ARG),
+    ("slot misaligned", dict(slot=P["slot"] + 4), B.SGLA_ERR_INVALID_ARG),
+    ("N zero", dict(N=0), B.SGLA_ERR_INVALID_ARG),
+    ("pool smaller than N without slot", dict(Pg=4), B.SGLA_ERR_INVALID_ARG),
+    ("bf16 D not mult 8", dict(D=12), B.SGLA_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", CONV_DEC_BAD, ids=[x[0] for x in CONV_DEC_BAD])
+def test_conv_decode_rejects(L, name, kw, code):
+    assert L.sgla_conv_decode_step(*conv_dec_args(**kw)) == code
+    assert L.sgla_last_error().decode() != ""
