@@ -1,6 +1,6 @@
 """Benchmark of the Simple GLA hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only fwd|fwdbwd|decode|varlen]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only fwd|fwdbwd|decode|varlen|conv]
                     [--no-cpu]
 
 Prints ONE JSON line. The headline ("value") is the Laplace-layer forward:
@@ -16,6 +16,9 @@ Also measured in the same run and reported under "secondary" (same clock):
           consecutive in-place steps, tokens/s = 1280 * 64 / t
   varlen: 32 packed sequences, lengths log-uniform in [128, 32768] (one of
           32768), init states ~ N(0, 0.02), tokens/s = sum T / t
+  conv:   the conv prologue (depthwise causal width-4 Conv1d + SiLU) at the
+          layer's width D=3072: forward B=8 T=2048 bf16 with conv states in and
+          out, and 64 decode steps of 1280 sequences' conv states
 
 "roofline" is for the dominant kernel of the headline step (k_fwd, bf16 forward):
 achieved = algorithmic HBM bytes per launch / mean launch time from HIP events
@@ -76,7 +79,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--only", choices=["fwd", "fwdbwd", "decode", "varlen"], default=None)
+    ap.add_argument("--only", choices=["fwd", "fwdbwd", "decode", "varlen", "conv"], default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--min-warm-s", type=float, default=1.5,
                     help="untimed warm-up continues past --warmup steps until this many "
@@ -202,6 +205,55 @@ def bench_decode(args, N=1280, steps=64):
             "gbs": bytes_step * steps / (ms * 1e-3) / 1e9}
 
 
+DMODEL = 3072  # residual width of the Laplace layer (the conv prologue's channels)
+
+
+def bench_conv(args, B=8, T=2048, D=DMODEL, nsets=3):
+    """Conv prologue forward: y = silu(depthwise causal width-4 conv(u)), bf16,
+    conv states in and out, rotating over input sets (0.6 GB)."""
+    import torch
+    from chunked_gated_linear_simple_amd import binding as Bd
+    w = gen((D, 4), 60, 0.5)
+    b = gen((D,), 61, 0.1)
+    sets = []
+    for s in range(nsets):
+        u = gen((B, T, D), 62 + s, dtype=torch.bfloat16)
+        sets.append((u, torch.empty_like(u), gen((B, 3, D), 70 + s), torch.empty((B, 3, D), device="cuda")))
+
+    def step(i):
+        u, y, s0, sf = sets[i % nsets]
+        Bd.sgla_conv_fwd(u, w, b, init_state=s0, final_state=sf, y=y)
+
+    ms, _ = timed(step, args.steps, args.warmup)
+    toks = B * T
+    bytes_ = 2 * B * T * D * 2 + 2 * B * 3 * D * 4 + D * 20
+    return {"ms": ms, "tokens": toks, "tok_s": toks / (ms * 1e-3), "bytes": bytes_,
+            "gbs": bytes_ / (ms * 1e-3) / 1e9}
+
+
+def bench_conv_decode(args, N=1280, D=DMODEL, steps=64):
+    """Conv decode: 64 consecutive in-place steps of 1280 sequences' conv states."""
+    import torch
+    from chunked_gated_linear_simple_amd import binding as Bd
+    w = gen((D, 4), 80, 0.5)
+    b = gen((D,), 81, 0.1)
+    state = gen((N, 3, D), 82)
+    xs = gen((steps, N, D), 83, dtype=torch.bfloat16)
+    y = torch.empty((N, D), dtype=torch.bfloat16, device="cuda")
+
+    def run(_):
+        for s in range(steps):
+            Bd.sgla_conv_decode_step(xs[s], w, b, state, y=y)
+
+    reps = max(2, args.steps // 4)
+    ms, _ = timed(run, reps, 1)
+    toks = N * steps
+    bytes_step = N * (2 * 3 * D * 4 + 2 * D * 2) + D * 20
+    return {"ms_64_steps": ms, "us_per_step": ms * 1e3 / steps, "tokens": toks,
+            "tok_s": toks / (ms * 1e-3), "bytes_per_step": bytes_step,
+            "gbs": bytes_step * steps / (ms * 1e-3) / 1e9}
+
+
 def bench_varlen(args):
     import numpy as np
     import torch
@@ -290,6 +342,9 @@ def main():
         secondary["decode_N1280_64steps"] = bench_decode(args)
     if only in (None, "varlen"):
         secondary["varlen_32seq"] = bench_varlen(args)
+    if only in (None, "conv"):
+        secondary["conv_fwd_B8_T2048_D3072"] = bench_conv(args)
+        secondary["conv_decode_N1280_D3072_64steps"] = bench_conv_decode(args)
     for r in secondary.values():
         r["hbm_frac_algorithmic"] = r["gbs"] / HBM_PEAK_GBS
 
