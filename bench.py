@@ -231,19 +231,21 @@ def bench_conv(args, B=8, T=2048, D=DMODEL, nsets=3):
             "gbs": bytes_ / (ms * 1e-3) / 1e9}
 
 
-def bench_conv_decode(args, N=1280, D=DMODEL, steps=64):
-    """Conv decode: 64 consecutive in-place steps of 1280 sequences' conv states."""
+def bench_conv_decode(args, N=1280, D=DMODEL, steps=64, npools=8):
+    """Conv decode: 64 consecutive in-place steps of 1280 sequences' conv
+    states. Step s uses pool s % 8 (8 x 47 MB, beyond the on-die caches), as a
+    whole decode step's other traffic would evict one pool between steps."""
     import torch
     from chunked_gated_linear_simple_amd import binding as Bd
     w = gen((D, 4), 80, 0.5)
     b = gen((D,), 81, 0.1)
-    state = gen((N, 3, D), 82)
-    xs = gen((steps, N, D), 83, dtype=torch.bfloat16)
+    pools = [gen((N, 3, D), 82 + i) for i in range(npools)]
+    xs = gen((steps, N, D), 83 + npools, dtype=torch.bfloat16)
     y = torch.empty((N, D), dtype=torch.bfloat16, device="cuda")
 
     def run(_):
         for s in range(steps):
-            Bd.sgla_conv_decode_step(xs[s], w, b, state, y=y)
+            Bd.sgla_conv_decode_step(xs[s], w, b, pools[s % npools], y=y)
 
     reps = max(2, args.steps // 4)
     ms, _ = timed(run, reps, 1)

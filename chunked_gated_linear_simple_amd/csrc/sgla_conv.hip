@@ -15,11 +15,20 @@
 //
 // The operation is a pure stream (one read and one write of each activation,
 // 4 multiply-adds and a SiLU per element), so the kernels are built for HBM
-// bandwidth: a thread owns one 16-byte group of channels (8 bf16 or 4 fp32)
-// and walks a run of consecutive tokens, keeping the three previous inputs in
+// bandwidth.
+// Forward: a thread owns one 16-byte group of channels (8 bf16 or 4 fp32) and
+// walks a run of 64 consecutive tokens, keeping the three previous inputs in
 // registers, so every input is read once (plus a three-token halo per run).
-// Consecutive threads own consecutive channel groups, so each token row is
-// read and written as contiguous 1 KB wave accesses.
+// The run is software-pipelined in blocks of 8 rows: the next block's loads
+// are issued before the current block is computed and stored, so a wave keeps
+// 8-16 row loads in flight while it writes. (Issuing all of a run's loads up
+// front instead makes every wave load, then store, in lock step, and is
+// slower.) Consecutive threads own consecutive channel groups, so each token
+// row is read and written as contiguous 1 KB wave accesses. A run that crosses
+// a sequence boundary or the end of the rows takes a row-at-a-time path.
+// Decode: a thread owns 4 channels of 4 sequences; its tap weights are loaded
+// once for the 4, and all 4 sequences' state and input loads are issued before
+// any is used.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -33,8 +42,11 @@ typedef unsigned short u16;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int RUN = 32;          // tokens per thread
-constexpr int CONV_THREADS = 256;
+constexpr int CONV_RUN = 64;      // tokens per thread in the forward
+constexpr int CONV_PD = 8;        // rows per pipelined block
+constexpr int CONV_THREADS = 128; // forward workgroup
+constexpr int DEC_SEQ = 4;        // sequences per decode thread
+constexpr int DEC_THREADS = 256;  // decode workgroup
 
 __device__ __forceinline__ float silu_f(float x)
 {
@@ -47,14 +59,17 @@ __device__ __forceinline__ float silu_f(float x)
 template <typename E> struct Grp;
 template <> struct Grp<u16> {
     static constexpr int V = 8;
-    static __device__ __forceinline__ void load(const u16* p, float* x)
+    static __device__ __forceinline__ void unpack(u32x4 w, float* x)
     {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(p);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             x[2 * i] = __uint_as_float(w[i] << 16);
             x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
         }
+    }
+    static __device__ __forceinline__ void load(const u16* p, float* x)
+    {
+        unpack(*reinterpret_cast<const u32x4*>(p), x);
     }
     static __device__ __forceinline__ void store(u16* p, const float* y)
     {
@@ -70,11 +85,14 @@ template <> struct Grp<u16> {
 };
 template <> struct Grp<float> {
     static constexpr int V = 4;
+    static __device__ __forceinline__ void unpack(u32x4 w, float* x)
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(w[i]);
+    }
     static __device__ __forceinline__ void load(const float* p, float* x)
     {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(p);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = v[i];
+        unpack(*reinterpret_cast<const u32x4*>(p), x);
     }
     static __device__ __forceinline__ void store(float* p, const float* y)
     {
@@ -111,13 +129,14 @@ struct Seqs {
     }
 };
 
-// y for rows [RUN * blockIdx.x, ...) of channel group blockIdx.y * 256 + tid
-template <typename E>
+// y for rows [RUN * blockIdx.x, ...) of channel group blockIdx.y * CONV_THREADS + tid
+template <typename E, int RUN, int PD>
 __global__ __launch_bounds__(CONV_THREADS) void k_conv_fwd(const E* __restrict__ u, const float* __restrict__ w,
                                                            const float* __restrict__ b,
                                                            const float* __restrict__ init, E* __restrict__ y,
                                                            Seqs sq, int D)
 {
+    static_assert(RUN % (2 * PD) == 0, "a run is an even number of blocks");
     constexpr int V = Grp<E>::V;
     const int grp = blockIdx.y * CONV_THREADS + threadIdx.x;
     if (grp * V >= D) return;
@@ -163,19 +182,9 @@ __global__ __launch_bounds__(CONV_THREADS) void k_conv_fwd(const E* __restrict__
             }
         }
     };
-    history(t0);
-    for (int t = t0; t < t1; ++t) {
-        if (t >= s1) {
-            // next non-empty sequence: its history is its own conv state
-            while (t >= s1 && n + 1 < sq.n_seq) {
-                ++n;
-                sq.range(n, s0, s1);
-            }
-            if (t >= s1) break;  // rows past the last sequence belong to none
-            history(t);
-        }
-        float x[V], out[V];
-        Grp<E>::load(u + (size_t)t * D + c0, x);
+    // one token: y_t from x = u_t and the history, which then shifts
+    auto token = [&](const float* x, int t) {
+        float out[V];
 #pragma unroll
         for (int i = 0; i < V; ++i) {
             float acc = bias[i];
@@ -189,6 +198,56 @@ __global__ __launch_bounds__(CONV_THREADS) void k_conv_fwd(const E* __restrict__
             h[2][i] = x[i];
         }
         Grp<E>::store(y + (size_t)t * D + c0, out);
+    };
+    // rows before the first sequence's start belong to none (only a malformed
+    // cu_seqlens has them); history(t) needs t >= s0
+    const int ts = max(t0, s0);
+    history(ts);
+
+    if (t1 - t0 == RUN && t0 >= s0 && t1 <= s1) {
+        // the whole run lies in one sequence: pipelined blocks of PD rows
+        const u32x4* up = reinterpret_cast<const u32x4*>(u + (size_t)t0 * D + c0);
+        const size_t rs = (size_t)D / V;  // one row in 16-byte units
+        u32x4 bufA[PD], bufB[PD];
+        auto block = [&](const u32x4* buf, int tb) {
+#pragma unroll
+            for (int r = 0; r < PD; ++r) {
+                float x[V];
+                Grp<E>::unpack(buf[r], x);
+                token(x, tb + r);
+            }
+        };
+#pragma unroll
+        for (int r = 0; r < PD; ++r) bufA[r] = up[r * rs];
+#pragma unroll 1
+        for (int k = 0; k < RUN / PD; k += 2) {
+#pragma unroll
+            for (int r = 0; r < PD; ++r) bufB[r] = up[((size_t)(k + 1) * PD + r) * rs];
+            block(bufA, t0 + k * PD);
+            if (k + 2 < RUN / PD) {
+#pragma unroll
+                for (int r = 0; r < PD; ++r) bufA[r] = up[((size_t)(k + 2) * PD + r) * rs];
+            }
+            block(bufB, t0 + (k + 1) * PD);
+        }
+        return;
+    }
+
+    // general path, one row at a time
+#pragma unroll 1
+    for (int t = ts; t < t1; ++t) {
+        if (t >= s1) {
+            // next non-empty sequence: its history is its own conv state
+            while (t >= s1 && n + 1 < sq.n_seq) {
+                ++n;
+                sq.range(n, s0, s1);
+            }
+            if (t >= s1) break;  // rows past the last sequence belong to none
+            history(t);
+        }
+        float x[V];
+        Grp<E>::load(u + (size_t)t * D + c0, x);
+        token(x, t);
     }
 }
 
@@ -224,63 +283,109 @@ __global__ __launch_bounds__(CONV_THREADS) void k_conv_state(const E* __restrict
         for (int i = 0; i < V; ++i) fin[((size_t)n * 3 + j) * D + c0 + i] = h[j][i];
 }
 
-// one decode step: thread = (sequence, 4 channels)
-template <typename E>
-__global__ __launch_bounds__(CONV_THREADS) void k_conv_decode(const E* __restrict__ x, const float* __restrict__ w,
-                                                              const float* __restrict__ b, float* __restrict__ state,
-                                                              const int32_t* __restrict__ slot, E* __restrict__ y,
-                                                              int N, int P, int D)
+// 4 channels of one token row: 8 bytes of bf16 or 16 of fp32
+template <typename E> struct Quad;
+template <> struct Quad<u16> {
+    typedef uint2 Raw;
+    static __device__ __forceinline__ Raw load(const u16* p) { return *reinterpret_cast<const uint2*>(p); }
+    static __device__ __forceinline__ void unpack(Raw r, float* x)
+    {
+        x[0] = __uint_as_float(r.x << 16);
+        x[1] = __uint_as_float(r.x & 0xffff0000u);
+        x[2] = __uint_as_float(r.y << 16);
+        x[3] = __uint_as_float(r.y & 0xffff0000u);
+    }
+    static __device__ __forceinline__ void store(u16* p, const float* y)
+    {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 lo = {static_cast<__bf16>(y[0]), static_cast<__bf16>(y[1])};
+        const bf16x2 hi = {static_cast<__bf16>(y[2]), static_cast<__bf16>(y[3])};
+        *reinterpret_cast<uint2*>(p) = uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+    }
+    static __device__ __forceinline__ void store_nan(u16* p) { *reinterpret_cast<uint2*>(p) = uint2{0x7fc07fc0u, 0x7fc07fc0u}; }
+};
+template <> struct Quad<float> {
+    typedef f32x4 Raw;
+    static __device__ __forceinline__ Raw load(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+    static __device__ __forceinline__ void unpack(Raw r, float* x)
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = r[i];
+    }
+    static __device__ __forceinline__ void store(float* p, const float* y)
+    {
+        *reinterpret_cast<f32x4*>(p) = f32x4{y[0], y[1], y[2], y[3]};
+    }
+    static __device__ __forceinline__ void store_nan(float* p)
+    {
+        const float q = __builtin_nanf("");
+        *reinterpret_cast<f32x4*>(p) = f32x4{q, q, q, q};
+    }
+};
+
+// one decode step: thread = (channels 4g..4g+3, sequences SEQ*blockIdx.x + m)
+template <typename E, int SEQ>
+__global__ __launch_bounds__(DEC_THREADS) void k_conv_decode(const E* __restrict__ x, const float* __restrict__ w,
+                                                             const float* __restrict__ b, float* __restrict__ state,
+                                                             const int32_t* __restrict__ slot, E* __restrict__ y,
+                                                             int N, int P, int D)
 {
-    const int grp = blockIdx.y * CONV_THREADS + threadIdx.x;
-    const int n = blockIdx.x;
+    const int grp = blockIdx.y * DEC_THREADS + threadIdx.x;
     if (grp * 4 >= D) return;
     const int c0 = grp * 4;
-    const int page = (slot != nullptr) ? slot[n] : n;
-    E* yr = y + (size_t)n * D + c0;
-    if (page < 0 || page >= P) {
-        if constexpr (sizeof(E) == 2) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) reinterpret_cast<u16*>(yr)[i] = 0x7fc0;
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) reinterpret_cast<float*>(yr)[i] = __builtin_nanf("");
-        }
-        return;
-    }
-    f32x4* st = reinterpret_cast<f32x4*>(state + (size_t)page * 3 * D + c0);
+    const int n0 = blockIdx.x * SEQ;
     const size_t rs = D / 4;  // one state row in f32x4 units
-    const f32x4 s0 = st[0], s1 = st[rs], s2 = st[2 * rs];
-    float xv[4];
-    const E* xr = x + (size_t)n * D + c0;
+
+    // every load of the SEQ sequences first
+    int page[SEQ];
+    f32x4 s[SEQ][3];
+    typename Quad<E>::Raw xr[SEQ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if constexpr (sizeof(E) == 2)
-            xv[i] = __uint_as_float((uint32_t)reinterpret_cast<const u16*>(xr)[i] << 16);
-        else
-            xv[i] = reinterpret_cast<const float*>(xr)[i];
-    }
-    float out[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const f32x4 wv = *reinterpret_cast<const f32x4*>(w + (size_t)(c0 + i) * 4);
-        float acc = (b != nullptr) ? b[c0 + i] : 0.0f;
-        acc = fmaf(wv[0], s0[i], acc);
-        acc = fmaf(wv[1], s1[i], acc);
-        acc = fmaf(wv[2], s2[i], acc);
-        acc = fmaf(wv[3], xv[i], acc);
-        out[i] = silu_f(acc);
-    }
-    st[0] = s1;
-    st[rs] = s2;
-    const f32x4 xn = {xv[0], xv[1], xv[2], xv[3]};
-    st[2 * rs] = xn;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if constexpr (sizeof(E) == 2) {
-            reinterpret_cast<u16*>(yr)[i] = __builtin_bit_cast(u16, static_cast<__bf16>(out[i]));
-        } else {
-            reinterpret_cast<float*>(yr)[i] = out[i];
+    for (int m = 0; m < SEQ; ++m) {
+        const int n = n0 + m;
+        page[m] = -1;
+        if (n < N) {
+            const int pg = (slot != nullptr) ? slot[n] : n;
+            if (pg >= 0 && pg < P) {
+                page[m] = pg;
+                const f32x4* st = reinterpret_cast<const f32x4*>(state + (size_t)pg * 3 * D + c0);
+                s[m][0] = st[0];
+                s[m][1] = st[rs];
+                s[m][2] = st[2 * rs];
+                xr[m] = Quad<E>::load(x + (size_t)n * D + c0);
+            }
         }
+    }
+    f32x4 wv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[i] = *reinterpret_cast<const f32x4*>(w + (size_t)(c0 + i) * 4);
+    const f32x4 bv = (b != nullptr) ? *reinterpret_cast<const f32x4*>(b + c0) : f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int m = 0; m < SEQ; ++m) {
+        const int n = n0 + m;
+        if (n >= N) break;
+        E* yr = y + (size_t)n * D + c0;
+        if (page[m] < 0) {
+            Quad<E>::store_nan(yr);
+            continue;
+        }
+        float xv[4], out[4];
+        Quad<E>::unpack(xr[m], xv);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float acc = bv[i];
+            acc = fmaf(wv[i][0], s[m][0][i], acc);
+            acc = fmaf(wv[i][1], s[m][1][i], acc);
+            acc = fmaf(wv[i][2], s[m][2][i], acc);
+            acc = fmaf(wv[i][3], xv[i], acc);
+            out[i] = silu_f(acc);
+        }
+        f32x4* st = reinterpret_cast<f32x4*>(state + (size_t)page[m] * 3 * D + c0);
+        st[0] = s[m][1];
+        st[rs] = s[m][2];
+        st[2 * rs] = f32x4{xv[0], xv[1], xv[2], xv[3]};
+        Quad<E>::store(yr, out);
     }
 }
 
@@ -291,9 +396,9 @@ hipError_t run_conv_fwd(const void* u, const float* w, const float* b, const flo
     constexpr int V = Grp<E>::V;
     Seqs sq{cu, n_seq, T, cu != nullptr ? T : B * T};
     const int groups = D / V;
-    const dim3 grid((sq.S + RUN - 1) / RUN, (groups + CONV_THREADS - 1) / CONV_THREADS);
+    const dim3 grid((sq.S + CONV_RUN - 1) / CONV_RUN, (groups + CONV_THREADS - 1) / CONV_THREADS);
     if (sq.S > 0) {
-        hipLaunchKernelGGL(k_conv_fwd<E>, grid, dim3(CONV_THREADS), 0, stream, reinterpret_cast<const E*>(u), w, b,
+        hipLaunchKernelGGL((k_conv_fwd<E, CONV_RUN, CONV_PD>), grid, dim3(CONV_THREADS), 0, stream, reinterpret_cast<const E*>(u), w, b,
                            init, reinterpret_cast<E*>(y), sq, D);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -320,12 +425,12 @@ hipError_t launch_conv_fwd(int bf16, const void* u, const float* w, const float*
 hipError_t launch_conv_decode(int bf16, const void* x, const float* w, const float* b, float* state,
                               const int32_t* slot, void* y, int N, int P, int D, hipStream_t stream)
 {
-    const dim3 grid(N, (D / 4 + CONV_THREADS - 1) / CONV_THREADS);
+    const dim3 grid((N + DEC_SEQ - 1) / DEC_SEQ, (D / 4 + DEC_THREADS - 1) / DEC_THREADS);
     if (bf16)
-        hipLaunchKernelGGL(k_conv_decode<u16>, grid, dim3(CONV_THREADS), 0, stream,
+        hipLaunchKernelGGL((k_conv_decode<u16, DEC_SEQ>), grid, dim3(DEC_THREADS), 0, stream,
                            reinterpret_cast<const u16*>(x), w, b, state, slot, reinterpret_cast<u16*>(y), N, P, D);
     else
-        hipLaunchKernelGGL(k_conv_decode<float>, grid, dim3(CONV_THREADS), 0, stream,
+        hipLaunchKernelGGL((k_conv_decode<float, DEC_SEQ>), grid, dim3(DEC_THREADS), 0, stream,
                            reinterpret_cast<const float*>(x), w, b, state, slot, reinterpret_cast<float*>(y), N,
                            P, D);
     return hipGetLastError();

@@ -60,6 +60,35 @@ def test_conv_varlen():
     _check(y, fin, _ref(inp, cu), inp)
 
 
+def test_conv_varlen_long():
+    """Sequences longer than a 64-token run: runs that lie inside one sequence
+    (pipelined blocks of 8 rows) and runs that cross one or more boundaries."""
+    L = [130, 64, 0, 200, 5, 128, 1, 67]
+    cu = I.cu_from_lengths(L)
+    for dtype, D in (("bf16", 512), ("f32", 128)):
+        inp = I.conv_inputs(225, (int(cu[-1]), D), D, dtype, len(L))
+        u, w, b, s0 = _dev_inputs(inp)
+        y, fin = Bd.sgla_conv_fwd(u, w, b, init_state=s0, cu_seqlens=to_dev(cu), want_final=True)
+        torch.cuda.synchronize()
+        _check(y, fin, _ref(inp, cu), inp, f" {dtype}")
+
+
+def test_conv_rows_outside_sequences_untouched():
+    """Packed rows before cu_seqlens[0] and after cu_seqlens[-1] belong to no
+    sequence: y keeps what it held there, the sequences match the oracle."""
+    S, D = 300, 256
+    cu = np.array([70, 71, 150, 290], np.int32)
+    inp = I.conv_inputs(227, (S, D), D, "bf16", len(cu) - 1)
+    u, w, b, s0 = _dev_inputs(inp)
+    y = torch.full((S, D), 7.0, dtype=torch.bfloat16, device="cuda")
+    Bd.sgla_conv_fwd(u, w, b, init_state=s0, y=y, cu_seqlens=to_dev(cu))
+    torch.cuda.synchronize()
+    ref = _ref(inp, cu)[0]
+    yh = to_host64(y)
+    assert (yh[:70] == 7.0).all() and (yh[290:] == 7.0).all(), "rows outside every sequence written"
+    assert_close(yh[70:290].ravel(), ref[70:290].ravel(), TOL["bf16"], "y", store="bf16")
+
+
 def test_conv_state_carry_in_place():
     """[0, T) at once == [0, t0) then [t0, T) with the state carried in place."""
     T, t0, D = 90, 37, 512
@@ -114,3 +143,26 @@ def test_conv_decode_pool(dtype):
     for p in range(P):
         if p not in used:
             assert torch.equal(pool[p], pool0[p]), f"page {p} touched"
+
+
+def test_conv_decode_full_size():
+    """Decode at serving size (1280 sequences, D=3072, bf16, pages = sequence
+    index): three steps equal the sequence forward over the same three tokens
+    from the same states bit for bit (same fp32 multiply-adds in the same
+    order), and sampled sequences match the oracle's decode steps."""
+    N, D, steps = 1280, 3072, 3
+    inp = I.conv_inputs(260, (N, steps, D), D, "bf16", N)
+    u, w, b, s0 = _dev_inputs(inp)
+    pool = s0.clone()
+    ys = [Bd.sgla_conv_decode_step(u[:, s].contiguous(), w, b, pool) for s in range(steps)]
+    yf, fin = Bd.sgla_conv_fwd(u, w, b, init_state=s0, want_final=True)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.stack(ys, dim=1), yf), "decode steps != forward"
+    assert torch.equal(pool, fin), "decode state != forward final state"
+    uh = I.widen(inp["u"], "bf16")
+    for n in (0, 1, 2, 3, 511, 1277, 1278, 1279):
+        st = inp["S0"][n].astype(np.float64).copy()
+        for s in range(steps):
+            r = oracle.conv_decode_step_unit(uh[n, s], inp["w"], inp["b"], st)
+            assert_close(to_host64(ys[s][n]), r, TOL["bf16"], f"decode y n={n} s={s}", store="bf16")
+        assert np.array_equal(to_host64(pool[n]), st), f"decode state n={n}"
