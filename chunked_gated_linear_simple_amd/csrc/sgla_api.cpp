@@ -263,7 +263,13 @@ sgla_status sgla_conv_fwd(const void* u, const float* w, const float* b, const f
     if (D % vec != 0)
         return fail(SGLA_ERR_UNSUPPORTED, "D must be a multiple of %d for this dtype (got %d)", vec, D);
     const size_t nb = (size_t)B * T * D * (dtype == SGLA_BF16 ? 2 : 4);
+    const size_t ns = (size_t)n_seq * 3 * D * sizeof(float);
     if (overlaps(y, nb, u, nb)) return fail(SGLA_ERR_INVALID_ARG, "y must not overlap u");
+    if (overlaps(y, nb, init_state, ns)) return fail(SGLA_ERR_INVALID_ARG, "y must not overlap init_state");
+    if (overlaps(final_state, ns, u, nb) || overlaps(final_state, ns, y, nb))
+        return fail(SGLA_ERR_INVALID_ARG, "final_state must not overlap u or y");
+    if (final_state != init_state && overlaps(final_state, ns, init_state, ns))
+        return fail(SGLA_ERR_INVALID_ARG, "final_state must equal init_state or not overlap it");
     hipError_t e = sgla::launch_conv_fwd(dtype == SGLA_BF16, u, w, b, init_state, final_state, y, cu_seqlens,
                                          n_seq, B, T, D, reinterpret_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return fail(SGLA_ERR_HIP, "conv_fwd launch: %s", hipGetErrorString(e));
@@ -290,6 +296,10 @@ sgla_status sgla_conv_decode_step(const void* x, const float* w, const float* b,
     const int vec = (dtype == SGLA_BF16) ? 8 : 4;
     if (D % vec != 0)
         return fail(SGLA_ERR_UNSUPPORTED, "D must be a multiple of %d for this dtype (got %d)", vec, D);
+    const size_t nx = (size_t)N * D * (dtype == SGLA_BF16 ? 2 : 4), ps = (size_t)P * 3 * D * sizeof(float);
+    if (overlaps(y, nx, x, nx)) return fail(SGLA_ERR_INVALID_ARG, "y must not overlap x");
+    if (overlaps(state, ps, x, nx) || overlaps(state, ps, y, nx))
+        return fail(SGLA_ERR_INVALID_ARG, "state must not overlap x or y");
     hipError_t e = sgla::launch_conv_decode(dtype == SGLA_BF16, x, w, b, state, slot, y, N, P, D,
                                             reinterpret_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return fail(SGLA_ERR_HIP, "conv decode launch: %s", hipGetErrorString(e));

@@ -129,17 +129,64 @@ struct Seqs {
     }
 };
 
-// y for rows [RUN * blockIdx.x, ...) of channel group blockIdx.y * CONV_THREADS + tid
+// fin[n] = the last three inputs of sequence n (reaching into init), for the
+// channel group grp
+template <typename E>
+__device__ __forceinline__ void final_state(const E* __restrict__ u, const float* init, float* fin, const Seqs& sq,
+                                            int D, int n, int grp)
+{
+    constexpr int V = Grp<E>::V;
+    const int c0 = grp * V;
+    int s0, s1;
+    sq.range(n, s0, s1);
+    const int L = s1 - s0;
+    float h[3][V];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int p = L - 3 + j;
+        if (p >= 0) {
+            Grp<E>::load(u + (size_t)(s0 + p) * D + c0, h[j]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < V; ++i)
+                h[j][i] = (init != nullptr) ? init[((size_t)n * 3 + (3 + p)) * D + c0 + i] : 0.0f;
+        }
+    }
+    // all reads above happen before any write: fin may equal init
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+        for (int i = 0; i < V; ++i) fin[((size_t)n * 3 + j) * D + c0 + i] = h[j][i];
+}
+
+// the final states alone, after every read of init (fin may equal init)
+template <typename E>
+__global__ __launch_bounds__(CONV_THREADS) void k_conv_state(const E* __restrict__ u, const float* init,
+                                                             float* fin, Seqs sq, int D)
+{
+    const int grp = blockIdx.y * CONV_THREADS + threadIdx.x;
+    if (grp * Grp<E>::V >= D) return;
+    final_state<E>(u, init, fin, sq, D, blockIdx.x, grp);
+}
+
+// y for rows [RUN * blockIdx.x, ...) of channel group blockIdx.y * CONV_THREADS + tid;
+// blocks runs + n (when fin is given, which then overlaps no input) write
+// sequence n's final state
+
 template <typename E, int RUN, int PD>
 __global__ __launch_bounds__(CONV_THREADS) void k_conv_fwd(const E* __restrict__ u, const float* __restrict__ w,
                                                            const float* __restrict__ b,
                                                            const float* __restrict__ init, E* __restrict__ y,
-                                                           Seqs sq, int D)
+                                                           float* __restrict__ fin, Seqs sq, int D, int runs)
 {
     static_assert(RUN % (2 * PD) == 0, "a run is an even number of blocks");
     constexpr int V = Grp<E>::V;
     const int grp = blockIdx.y * CONV_THREADS + threadIdx.x;
     if (grp * V >= D) return;
+    if ((int)blockIdx.x >= runs) {
+        final_state<E>(u, init, fin, sq, D, blockIdx.x - runs, grp);
+        return;
+    }
     const int c0 = grp * V;
     const int t0 = blockIdx.x * RUN;
     if (t0 >= sq.S) return;
@@ -249,38 +296,6 @@ __global__ __launch_bounds__(CONV_THREADS) void k_conv_fwd(const E* __restrict__
         Grp<E>::load(u + (size_t)t * D + c0, x);
         token(x, t);
     }
-}
-
-// final[n] = the last three inputs of sequence n (reaching into init)
-template <typename E>
-__global__ __launch_bounds__(CONV_THREADS) void k_conv_state(const E* __restrict__ u, const float* init,
-                                                             float* fin, Seqs sq, int D)
-{
-    constexpr int V = Grp<E>::V;
-    const int grp = blockIdx.y * CONV_THREADS + threadIdx.x;
-    const int n = blockIdx.x;
-    if (grp * V >= D) return;
-    const int c0 = grp * V;
-    int s0, s1;
-    sq.range(n, s0, s1);
-    const int L = s1 - s0;
-    float h[3][V];
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-        const int p = L - 3 + j;
-        if (p >= 0) {
-            Grp<E>::load(u + (size_t)(s0 + p) * D + c0, h[j]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < V; ++i)
-                h[j][i] = (init != nullptr) ? init[((size_t)n * 3 + (3 + p)) * D + c0 + i] : 0.0f;
-        }
-    }
-    // all reads above happen before any write: fin may equal init
-#pragma unroll
-    for (int j = 0; j < 3; ++j)
-#pragma unroll
-        for (int i = 0; i < V; ++i) fin[((size_t)n * 3 + j) * D + c0 + i] = h[j][i];
 }
 
 // 4 channels of one token row: 8 bytes of bf16 or 16 of fp32
@@ -396,15 +411,18 @@ hipError_t run_conv_fwd(const void* u, const float* w, const float* b, const flo
     constexpr int V = Grp<E>::V;
     Seqs sq{cu, n_seq, T, cu != nullptr ? T : B * T};
     const int groups = D / V;
-    const dim3 grid((sq.S + CONV_RUN - 1) / CONV_RUN, (groups + CONV_THREADS - 1) / CONV_THREADS);
-    if (sq.S > 0) {
-        hipLaunchKernelGGL((k_conv_fwd<E, CONV_RUN, CONV_PD>), grid, dim3(CONV_THREADS), 0, stream, reinterpret_cast<const E*>(u), w, b,
-                           init, reinterpret_cast<E*>(y), sq, D);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    if (fin != nullptr) {
-        const dim3 g2(n_seq, (groups + CONV_THREADS - 1) / CONV_THREADS);
+    const int gy = (groups + CONV_THREADS - 1) / CONV_THREADS;
+    const int runs = (sq.S + CONV_RUN - 1) / CONV_RUN;
+    // a final state that is not the initial one (the caller guarantees it then
+    // overlaps no input) is written by extra blocks of the same launch
+    const bool fused = fin != nullptr && fin != init;
+    hipLaunchKernelGGL((k_conv_fwd<E, CONV_RUN, CONV_PD>), dim3(runs + (fused ? n_seq : 0), gy), dim3(CONV_THREADS), 0,
+                       stream, reinterpret_cast<const E*>(u), w, b, init, reinterpret_cast<E*>(y),
+                       fused ? fin : nullptr, sq, D, runs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (fin != nullptr && !fused) {
+        const dim3 g2(n_seq, gy);
         hipLaunchKernelGGL(k_conv_state<E>, g2, dim3(CONV_THREADS), 0, stream, reinterpret_cast<const E*>(u), init,
                            fin, sq, D);
         return hipGetLastError();

@@ -205,11 +205,14 @@ sgla_status sgla_decode_step(const void* q, const void* k, const void* v,
  * w:           [D, 4] fp32 taps.   b: [D] fp32 bias, or NULL = none.
  * init_state:  [N, 3, D] fp32, row j = u_{-3+j} of sequence n, or NULL = zero.
  * final_state: [N, 3, D] fp32 or NULL: row j = u_{L-3+j} of sequence n (reaching
- *              into init_state when L < 3); may equal init_state.
+ *              into init_state when L < 3). It may equal init_state (in-place
+ *              carry); otherwise it must not overlap init_state, u or y.
+ *              y must not overlap init_state either.
  * n_seq:       N (= B when dense).
  * Supported: D a multiple of 8 (bf16) or 4 (fp32). All pointers 16-byte aligned.
  * Errors: SGLA_ERR_INVALID_ARG (NULL required pointer, non-positive size,
- * misaligned pointer), SGLA_ERR_UNSUPPORTED (D), SGLA_ERR_HIP (launch).
+ * misaligned pointer, overlapping buffers), SGLA_ERR_UNSUPPORTED (D),
+ * SGLA_ERR_HIP (launch).
  */
 sgla_status sgla_conv_fwd(const void* u, const float* w, const float* b,
                           const float* init_state, float* final_state, void* y,
@@ -227,6 +230,7 @@ sgla_status sgla_conv_fwd(const void* u, const float* w, const float* b,
  * slot:   [N] int32 page index, or NULL (sequence n uses page n, P >= N).
  *         Entries must be distinct; one outside [0, P) skips that sequence
  *         and writes NaN to its y.
+ * y must not overlap x; the pool must overlap neither.
  * Supported and errors: as sgla_conv_fwd.
  */
 sgla_status sgla_conv_decode_step(const void* x, const float* w, const float* b,

@@ -221,6 +221,10 @@ CONV_BAD = [
     ("dense n_seq != B", dict(n_seq=3), B.SGLA_ERR_INVALID_ARG),
     ("packed with B=2", dict(cu=P["cu"], n_seq=2), B.SGLA_ERR_INVALID_ARG),
     ("cu misaligned", dict(cu=P["cu"] + 4, n_seq=2, B=1), B.SGLA_ERR_INVALID_ARG),
+    ("final state overlaps u", dict(sf=P["u"] + 1024), B.SGLA_ERR_INVALID_ARG),
+    ("final state overlaps y", dict(sf=P["y"]), B.SGLA_ERR_INVALID_ARG),
+    ("final state partly overlaps init", dict(sf=P["s0"] + 4096), B.SGLA_ERR_INVALID_ARG),
+    ("y overlaps init", dict(y=P["s0"]), B.SGLA_ERR_INVALID_ARG),
 ]
 
 
@@ -245,6 +249,9 @@ CONV_DEC_BAD = [
     ("N zero", dict(N=0), B.SGLA_ERR_INVALID_ARG),
     ("pool smaller than N without slot", dict(Pg=4), B.SGLA_ERR_INVALID_ARG),
     ("bf16 D not mult 8", dict(D=12), B.SGLA_ERR_UNSUPPORTED),
+    ("y overlaps x", dict(y=P["u"] + 2048), B.SGLA_ERR_INVALID_ARG),
+    ("state overlaps x", dict(state=P["u"]), B.SGLA_ERR_INVALID_ARG),
+    ("state overlaps y", dict(state=P["y"] + 1024), B.SGLA_ERR_INVALID_ARG),
 ]
 
 
