@@ -57,8 +57,10 @@ def _load():
                                         _dp, _dp, _dp, _dp, _dp, _dp]
         lib.orc_conv_fwd.argtypes = [ctypes.c_int, ctypes.c_int, _dp, _dp, _dp, _dp, _dp, _dp]
         lib.orc_conv_decode_step.argtypes = [ctypes.c_int, _dp, _dp, _dp, _dp, _dp]
+        lib.orc_head_norm_gate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_double, _dp, _dp, _dp, _dp]
         for f in (lib.orc_decay_schedule, lib.orc_fwd, lib.orc_bwd, lib.orc_decode_step,
-                  lib.orc_conv_fwd, lib.orc_conv_decode_step):
+                  lib.orc_conv_fwd, lib.orc_conv_decode_step, lib.orc_head_norm_gate):
             f.restype = None
         _lib = lib
     return _lib
@@ -245,3 +247,26 @@ def conv_decode_step_unit(x, w, b, st):
     y = np.zeros(x.shape[0])
     _load().orc_conv_decode_step(x.shape[0], _ptr(w), _ptr(b), _ptr(x), _ptr(st), _ptr(y))
     return y
+
+
+def head_norm_gate_token(o, g, gamma, n_tiers, eps):
+    """One token: o, g [H, d_v]; gamma [n_tiers, d_v] or None -> out [H, d_v]."""
+    o, g, gamma = _f64(o), _f64(g), _f64(gamma)
+    H, d_v = o.shape
+    out = np.zeros((H, d_v))
+    _load().orc_head_norm_gate(H, d_v, int(n_tiers), float(eps), _ptr(o), _ptr(g), _ptr(gamma),
+                               _ptr(out))
+    return out
+
+
+def head_norm_gate(o, g, gamma=None, n_tiers=1, eps=1e-6):
+    """Mixer epilogue over a batch: o [B, H, T, d_v] (the mixer's layout),
+    g [B, T, H, d_v] (token-major gate stream), gamma [n_tiers, d_v] or None.
+    Returns out [B, T, H, d_v] (token-major, heads concatenated)."""
+    o = np.asarray(o)
+    B, H, T, d_v = o.shape
+    out = np.zeros((B, T, H, d_v))
+    for b in range(B):
+        for t in range(T):
+            out[b, t] = head_norm_gate_token(o[b, :, t, :], g[b, t], gamma, n_tiers, eps)
+    return out

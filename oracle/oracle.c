@@ -295,3 +295,30 @@ void orc_conv_decode_step(int D, const double* w, const double* b, const double*
         st[(size_t)2 * D + c] = x[c];
     }
 }
+
+/* Mixer epilogue for ONE token. Laplace 3B post, "i14 and the Laplace 3B
+ * architecture", end of the "GLA mixer" paragraph and the "Decay schedule's
+ * reach" paragraph: each head's output goes through a Head RMSNorm, the heads
+ * of a decay tier share that norm (its learned per-channel scale), the heads
+ * are concatenated and the result is gated by SiLU(g_t).
+ * Tiers are n_tiers contiguous runs of H / n_tiers heads. */
+void orc_head_norm_gate(int H, int d_v, int n_tiers, double eps, const double* o,
+                        const double* g, const double* gamma, double* out)
+{
+    const int per_tier = H / n_tiers;
+    for (int h = 0; h < H; ++h) {
+        const double* oh = o + (size_t)h * d_v;
+        /* root mean square of this head's d_v outputs */
+        double ss = 0.0;
+        for (int c = 0; c < d_v; ++c) {
+            ss += oh[c] * oh[c];
+        }
+        const double inv_rms = 1.0 / sqrt(ss / d_v + eps);
+        const int tier = h / per_tier;
+        for (int c = 0; c < d_v; ++c) {
+            const double scale = (gamma != NULL) ? gamma[(size_t)tier * d_v + c] : 1.0;
+            const double gc = g[(size_t)h * d_v + c];
+            out[(size_t)h * d_v + c] = silu(gc) * (scale * oh[c] * inv_rms);
+        }
+    }
+}

@@ -65,6 +65,14 @@ void orc_conv_fwd(int L, int D, const double* w, const double* b, const double* 
 void orc_conv_decode_step(int D, const double* w, const double* b, const double* x,
                           double* st, double* y);
 
+/* Mixer epilogue (Head RMSNorm per decay tier, concatenation, SiLU(g) gate)
+ * for ONE token:
+ *   out[h][c] = silu(g[h][c]) * gamma[tier(h)][c] * o[h][c] / sqrt(mean_c' o[h][c']^2 + eps)
+ * o, g, out : [H][d_v] (the token's heads, concatenated); gamma : [n_tiers][d_v]
+ * or NULL (one); tier(h) = h / (H / n_tiers), H a multiple of n_tiers. */
+void orc_head_norm_gate(int H, int d_v, int n_tiers, double eps, const double* o,
+                        const double* g, const double* gamma, double* out);
+
 #ifdef __cplusplus
 }
 #endif

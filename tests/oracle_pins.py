@@ -327,6 +327,81 @@ def check_conv_decode_steps():
     _close(st, sf, 0, "conv decode state")
 
 
+# ------------------------------------------------- mixer epilogue (Head RMSNorm + gate)
+
+def _hng_case(seed, H, d_v, n_tiers, B=1, T=3):
+    r = _rng(seed)
+    o = r.standard_normal((B, H, T, d_v)) * 0.7
+    g = r.standard_normal((B, T, H, d_v)) * 2.0
+    gamma = 1.0 + 0.3 * r.standard_normal((n_tiers, d_v))
+    return o, g, gamma
+
+
+def check_hng_unit_rms():
+    """With gamma = 1 and eps = 0, dividing out the gate (SiLU from scipy's
+    logistic function) leaves every head of every token with mean square
+    exactly 1 over its d_v channels, pointing along that head's own o."""
+    o, g, _ = _hng_case(41, 4, 24, 2)
+    out = oracle.head_norm_gate(o, g, None, 2, 0.0)
+    pre = out / _silu(g)
+    ms = np.mean(pre ** 2, axis=-1)
+    _close(ms, np.ones_like(ms), 1e-12, "unit mean square")
+    ratio = pre / np.transpose(o, (0, 2, 1, 3))
+    _close(ratio, np.broadcast_to(ratio[..., :1], ratio.shape), 1e-12, "multiple of o")
+    assert (ratio > 0).all(), "pre-gate output is not a positive multiple of o"
+
+
+def check_hng_scale_sign():
+    """eps = 0: invariant to a positive scale of the outputs, odd in their
+    sign, and invariant to scaling ONE head alone (the statistic is per head,
+    not per tier)."""
+    o, g, gamma = _hng_case(43, 6, 16, 3, B=2, T=2)
+    out = oracle.head_norm_gate(o, g, gamma, 3, 0.0)
+    _close(oracle.head_norm_gate(3.7 * o, g, gamma, 3, 0.0), out, 1e-13, "scale")
+    _close(oracle.head_norm_gate(-o, g, gamma, 3, 0.0), -out, 1e-13, "sign")
+    o2 = o.copy()
+    o2[:, 1] *= 5.0
+    _close(oracle.head_norm_gate(o2, g, gamma, 3, 0.0), out, 1e-13, "one head scaled")
+
+
+def check_hng_tiers_and_channels():
+    """A constant head vector normalises to +-1 in every channel, so
+    out[h][c] = +-silu(g[h][c]) gamma[tier(h)][c]: with distinct gamma entries
+    this fixes which tier each head uses (contiguous groups of H / n_tiers)
+    and that gamma is indexed by channel."""
+    H, d_v, n_tiers = 8, 6, 4
+    r = _rng(45)
+    vals = r.uniform(0.5, 2.0, H) * np.where(np.arange(H) % 3 == 1, -1.0, 1.0)
+    o = np.broadcast_to(vals[None, :, None, None], (1, H, 1, d_v)).copy()
+    g = r.standard_normal((1, 1, H, d_v))
+    gamma = np.arange(1.0, n_tiers * d_v + 1.0).reshape(n_tiers, d_v)
+    out = oracle.head_norm_gate(o, g, gamma, n_tiers, 0.0)
+    for h in range(H):
+        ref = np.sign(vals[h]) * _silu(g[0, 0, h]) * gamma[h // (H // n_tiers)]
+        _close(out[0, 0, h], ref, 1e-14, f"head {h}")
+
+
+def check_hng_eps():
+    """eps sits inside the square root: a constant head of value sqrt(eps)
+    normalises to 1/sqrt(2); an all-zero head gives zeros, not NaN."""
+    H, d_v, eps = 2, 8, 0.25
+    o = np.full((1, H, 1, d_v), 0.5)
+    o[0, 1] = 0.0
+    g = np.full((1, 1, H, d_v), 3.0)
+    out = oracle.head_norm_gate(o, g, None, 1, eps)
+    _close(out[0, 0, 0], np.full(d_v, _silu(3.0) / np.sqrt(2.0)), 1e-14, "eps inside sqrt")
+    _close(out[0, 0, 1], np.zeros(d_v), 0, "zero head")
+
+
+def check_hng_gate_silu():
+    """The gate is SiLU, channel by channel, also far into both tails: with
+    a normalised constant head and gamma = 1, out = g * logistic(g) (scipy)."""
+    g = np.array([-30.0, -5.0, -1.0, -1e-3, 0.0, 1e-3, 1.0, 5.0, 30.0])
+    d_v = g.size
+    out = oracle.head_norm_gate(np.ones((1, 1, 1, d_v)), g.reshape(1, 1, 1, d_v), None, 1, 0.0)
+    _close(out[0, 0, 0], g * expit(g), 1e-15, "silu")
+
+
 ALL_CHECKS = [
     check_schedule_printed_values,
     check_schedule_geometric,
@@ -344,4 +419,9 @@ ALL_CHECKS = [
     check_conv_single_taps,
     check_conv_state_carry,
     check_conv_decode_steps,
+    check_hng_unit_rms,
+    check_hng_scale_sign,
+    check_hng_tiers_and_channels,
+    check_hng_eps,
+    check_hng_gate_silu,
 ]

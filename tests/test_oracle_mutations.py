@@ -53,6 +53,14 @@ MUTATIONS = [
     ("conv decode state not shifted", "st[c] = st[(size_t)D + c];", "st[c] = st[c];"),
     ("conv decode tap 2 reads x", "acc += w[(size_t)c * 4 + 2] * st[(size_t)2 * D + c];",
      "acc += w[(size_t)c * 4 + 2] * x[c];"),
+    ("norm eps dropped", "sqrt(ss / d_v + eps)", "sqrt(ss / d_v)"),
+    ("norm eps outside the root", "1.0 / sqrt(ss / d_v + eps)", "1.0 / (sqrt(ss / d_v) + eps)"),
+    ("norm sums instead of averaging", "sqrt(ss / d_v + eps)", "sqrt(ss + eps)"),
+    ("norm tier by head modulo", "const int tier = h / per_tier;", "const int tier = h % n_tiers;"),
+    ("norm gamma transposed", "gamma[(size_t)tier * d_v + c]", "gamma[(size_t)c * n_tiers + tier]"),
+    ("norm gate sigmoid instead of silu", "out[(size_t)h * d_v + c] = silu(gc) *",
+     "out[(size_t)h * d_v + c] = sigmoid(gc) *"),
+    ("norm gate dropped", "out[(size_t)h * d_v + c] = silu(gc) *", "out[(size_t)h * d_v + c] = 1.0 *"),
 ]
 
 
@@ -69,7 +77,7 @@ def test_mutation_is_caught(name, find, repl, tmp_path):
     good = oracle._load()
     bad = ctypes.CDLL(str(so))
     for fn in ("orc_decay_schedule", "orc_fwd", "orc_bwd", "orc_decode_step", "orc_conv_fwd",
-               "orc_conv_decode_step"):
+               "orc_conv_decode_step", "orc_head_norm_gate"):
         getattr(bad, fn).argtypes = getattr(good, fn).argtypes
         getattr(bad, fn).restype = None
     caught = []
