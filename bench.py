@@ -1,6 +1,6 @@
 """Benchmark of the Simple GLA hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only fwd|fwdbwd|decode|varlen|conv]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only fwd|fwdbwd|decode|varlen|norm|conv]
                     [--no-cpu]
 
 Prints ONE JSON line. The headline ("value") is the Laplace-layer forward:
@@ -16,6 +16,9 @@ Also measured in the same run and reported under "secondary" (same clock):
           consecutive in-place steps, tokens/s = 1280 * 64 / t
   varlen: 32 packed sequences, lengths log-uniform in [128, 32768] (one of
           32768), init states ~ N(0, 0.02), tokens/s = sum T / t
+  norm:   the mixer epilogue (Head RMSNorm per decay tier, 4 tiers, + SiLU(g)
+          gate) on a B=8 T=2048 forward's output: o and g in, out written,
+          bf16, tokens/s = 16384 / t
   conv:   the conv prologue (depthwise causal width-4 Conv1d + SiLU) at the
           layer's width D=3072: forward B=8 T=2048 bf16 with conv states in and
           out, and 64 decode steps of 1280 sequences' conv states
@@ -79,7 +82,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--only", choices=["fwd", "fwdbwd", "decode", "varlen", "conv"], default=None)
+    ap.add_argument("--only", choices=["fwd", "fwdbwd", "decode", "varlen", "norm", "conv"],
+                    default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--min-warm-s", type=float, default=1.5,
                     help="untimed warm-up continues past --warmup steps until this many "
@@ -256,6 +260,30 @@ def bench_conv_decode(args, N=1280, D=DMODEL, steps=64, npools=8):
             "gbs": bytes_step * steps / (ms * 1e-3) / 1e9}
 
 
+def bench_norm(args, B=8, T=2048, n_tiers=4, nsets=3):
+    """Mixer epilogue (Head RMSNorm per decay tier + SiLU(g) gate) on the
+    Laplace layer's forward output: o [B, H, T, d_v] and g [B, T, H, d_v] bf16
+    in, out [B, T, H, d_v] bf16; 3 input sets rotated (0.9 GB)."""
+    import torch
+    from chunked_gated_linear_simple_amd import binding as Bd
+    gm = (1.0 + gen((n_tiers, DV), 90, 0.1)).contiguous()
+    sets = []
+    for s in range(nsets):
+        o = gen((B, H, T, DV), 91 + 2 * s, dtype=torch.bfloat16)
+        g = gen((B, T, H, DV), 92 + 2 * s, dtype=torch.bfloat16)
+        sets.append((o, g, torch.empty_like(g)))
+
+    def step(i):
+        o, g, out = sets[i % nsets]
+        Bd.sgla_head_norm_gate(o, g, gm, n_tiers, 1e-6, out=out)
+
+    ms, _ = timed(step, args.steps, args.warmup)
+    toks = B * T
+    bytes_ = 3 * B * T * H * DV * 2 + n_tiers * DV * 4
+    return {"ms": ms, "tokens": toks, "tok_s": toks / (ms * 1e-3), "bytes": bytes_,
+            "gbs": bytes_ / (ms * 1e-3) / 1e9}
+
+
 def bench_varlen(args):
     import numpy as np
     import torch
@@ -344,6 +372,8 @@ def main():
         secondary["decode_N1280_64steps"] = bench_decode(args)
     if only in (None, "varlen"):
         secondary["varlen_32seq"] = bench_varlen(args)
+    if only in (None, "norm"):
+        secondary["head_norm_gate_B8_T2048"] = bench_norm(args)
     if only in (None, "conv"):
         secondary["conv_fwd_B8_T2048_D3072"] = bench_conv(args)
         secondary["conv_decode_N1280_D3072_64steps"] = bench_conv_decode(args)

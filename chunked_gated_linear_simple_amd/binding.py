@@ -64,6 +64,9 @@ def lib() -> ctypes.CDLL:
         L.sgla_conv_fwd.restype = _i
         L.sgla_conv_decode_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]
         L.sgla_conv_decode_step.restype = _i
+        L.sgla_head_norm_gate.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, ctypes.c_float, _i,
+                                          _vp]
+        L.sgla_head_norm_gate.restype = _i
         _lib = L
     return _lib
 
@@ -263,3 +266,23 @@ def sgla_conv_decode_step(x, w, b, state, y=None, slot=None):
     _check(lib().sgla_conv_decode_step(_ptr(x), _ptr(w), _ptr(b), _ptr(state), _ptr(slot),
                                        _ptr(y), N, P, D, _dtype_code(x), _stream(dev)))
     return y
+
+
+def sgla_head_norm_gate(o, g, gamma=None, n_tiers=1, eps=1e-6, out=None):
+    """Head RMSNorm per decay tier + SiLU(g) gate. o [B, H, T, d_v] (the mixer's
+    layout), g [B, T, H, d_v] or [B, T, H * d_v], gamma [n_tiers, d_v] fp32 or
+    None. Returns out shaped like g (token-major, heads concatenated)."""
+    dev = o.device
+    B, H, T, d_v = o.shape
+    _need(o, "o", device=dev)
+    if g.dim() == 3:
+        _need(g, "g", o.dtype, dev, (B, T, H * d_v))
+    else:
+        _need(g, "g", o.dtype, dev, (B, T, H, d_v))
+    _need(gamma, "gamma", torch.float32, dev, (n_tiers, d_v))
+    if out is None:
+        out = torch.empty_like(g)
+    _need(out, "out", o.dtype, dev, tuple(g.shape))
+    _check(lib().sgla_head_norm_gate(_ptr(o), _ptr(g), _ptr(gamma), _ptr(out), B, H, T, d_v,
+                                     int(n_tiers), float(eps), _dtype_code(o), _stream(dev)))
+    return out

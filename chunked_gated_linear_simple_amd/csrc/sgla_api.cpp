@@ -306,4 +306,33 @@ sgla_status sgla_conv_decode_step(const void* x, const float* w, const float* b,
     return ok();
 }
 
+sgla_status sgla_head_norm_gate(const void* o, const void* g, const float* gamma, void* out, int B, int H,
+                                int T, int d_v, int n_tiers, float eps, sgla_dtype dtype, void* hip_stream)
+{
+    REQUIRE_PTR(o);
+    REQUIRE_PTR(g);
+    REQUIRE_PTR(out);
+    OPTIONAL_PTR(gamma);
+    if (dtype != SGLA_F32 && dtype != SGLA_BF16)
+        return fail(SGLA_ERR_INVALID_ARG, "dtype %d is not SGLA_F32 or SGLA_BF16", (int)dtype);
+    if (B <= 0 || H <= 0 || T <= 0 || d_v <= 0 || n_tiers <= 0)
+        return fail(SGLA_ERR_INVALID_ARG, "sizes must be positive (B=%d H=%d T=%d d_v=%d n_tiers=%d)", B, H, T,
+                    d_v, n_tiers);
+    if (H % n_tiers != 0)
+        return fail(SGLA_ERR_INVALID_ARG, "n_tiers (%d) must divide H (%d)", n_tiers, H);
+    if (!(eps >= 0.0f) || !std::isfinite(eps))
+        return fail(SGLA_ERR_INVALID_ARG, "eps must be finite and >= 0 (got %g)", (double)eps);
+    if ((double)B * H * T * d_v > 2.0e9) return fail(SGLA_ERR_INVALID_ARG, "B*H*T*d_v too large");
+    if (d_v % 4 != 0 || d_v > 256)
+        return fail(SGLA_ERR_UNSUPPORTED, "d_v must be a multiple of 4, at most 256 (got %d)", d_v);
+    const size_t nb = (size_t)B * H * T * d_v * (dtype == SGLA_BF16 ? 2 : 4);
+    if (overlaps(out, nb, o, nb)) return fail(SGLA_ERR_INVALID_ARG, "out must not overlap o");
+    if (out != g && overlaps(out, nb, g, nb))
+        return fail(SGLA_ERR_INVALID_ARG, "out must equal g or not overlap it");
+    hipError_t e = sgla::launch_head_norm_gate(dtype == SGLA_BF16, o, g, gamma, out, B, H, T, d_v, n_tiers, eps,
+                                               reinterpret_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(SGLA_ERR_HIP, "head_norm_gate launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // extern "C"

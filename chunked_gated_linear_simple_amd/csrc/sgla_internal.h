@@ -53,6 +53,10 @@ hipError_t launch_conv_fwd(int bf16, const void* u, const float* w, const float*
 hipError_t launch_conv_decode(int bf16, const void* x, const float* w, const float* b, float* state,
                               const int32_t* slot, void* y, int N, int P, int D, hipStream_t stream);
 
+// Mixer epilogue: Head RMSNorm per decay tier + SiLU(g) gate (sgla_norm.hip).
+hipError_t launch_head_norm_gate(int bf16, const void* o, const void* g, const float* gamma, void* out, int B,
+                                 int H, int T, int d_v, int n_tiers, float eps, hipStream_t stream);
+
 }  // namespace sgla
 
 #endif

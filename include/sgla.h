@@ -237,6 +237,37 @@ sgla_status sgla_conv_decode_step(const void* x, const float* w, const float* b,
                                   float* state, const int32_t* slot, void* y,
                                   int N, int P, int D, sgla_dtype dtype, void* hip_stream);
 
+/*
+ * Mixer epilogue: Head RMSNorm per decay tier, concatenation of the heads and
+ * the SiLU(g) output gate. Laplace 3B post, "i14 and the Laplace 3B
+ * architecture", the end of the "GLA mixer" paragraph (the per-head outputs
+ * go through a Head RMSNorm within each decay tier, are concatenated and
+ * gated by SiLU(g_t)) and "Decay schedule's reach" (the heads of a tier share
+ * one Head RMSNorm, i.e. its learned per-channel scale):
+ *   out[b,t,h,c] = silu(g[b,t,h,c]) * gamma[tier(h)][c] * o[b,h,t,c]
+ *                  / sqrt(mean_c' o[b,h,t,c']^2 + eps),   tier(h) = h / (H / n_tiers)
+ * The statistic is per head (over its d_v channels); tiers are contiguous
+ * groups of H / n_tiers heads, which the monotone decay schedule makes heads
+ * of similar reach.
+ *
+ * o:       [B, H, T, d_v] (dtype), the layout sgla_chunk_fwd writes (packed
+ *          sequences: B = 1, T = total tokens); a decode step's o [N, H, d_v]
+ *          is B = N, T = 1.
+ * g:       [B, T, H, d_v] (dtype), the gate stream, token-major.
+ * gamma:   [n_tiers, d_v] fp32, or NULL (one).
+ * out:     [B, T, H, d_v] (dtype), token-major (heads concatenated). It may
+ *          equal g (in place); otherwise it must not overlap g. It must not
+ *          overlap o.
+ * n_tiers: divides H. eps: finite, >= 0 (with eps = 0 an all-zero head gives NaN).
+ * Supported: d_v a multiple of 4, at most 256. All pointers 16-byte aligned.
+ * Errors: SGLA_ERR_INVALID_ARG (NULL required pointer, non-positive size,
+ * n_tiers not dividing H, bad eps, misaligned or overlapping buffers),
+ * SGLA_ERR_UNSUPPORTED (d_v), SGLA_ERR_HIP (launch).
+ */
+sgla_status sgla_head_norm_gate(const void* o, const void* g, const float* gamma, void* out,
+                                int B, int H, int T, int d_v, int n_tiers, float eps,
+                                sgla_dtype dtype, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(L):
     declared = B.declared_functions()
     assert set(declared) >= {"sgla_decay_schedule", "sgla_chunk_fwd", "sgla_chunk_bwd",
                              "sgla_chunk_bwd_workspace_bytes", "sgla_decode_step",
-                             "sgla_conv_fwd", "sgla_conv_decode_step",
+                             "sgla_conv_fwd", "sgla_conv_decode_step", "sgla_head_norm_gate",
                              "sgla_last_error", "sgla_status_str", "sgla_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -74,7 +74,7 @@ def test_decay_schedule_rejects(L, args):
 BASE = 0x7F0000000000
 P = {n: BASE + i * 0x100000000 for i, n in enumerate(
     ["q", "k", "v", "lam", "a", "s0", "sf", "o", "cu", "dO", "dq", "dk", "dv", "da", "ds0", "ws",
-     "state", "slot", "u", "w", "b", "y"])}
+     "state", "slot", "u", "w", "b", "y", "no", "ng", "gm", "nout"])}
 
 
 def fwd_args(**kw):
@@ -258,4 +258,37 @@ CONV_DEC_BAD = [
 @pytest.mark.parametrize("name,kw,code", CONV_DEC_BAD, ids=[x[0] for x in CONV_DEC_BAD])
 def test_conv_decode_rejects(L, name, kw, code):
     assert L.sgla_conv_decode_step(*conv_dec_args(**kw)) == code
+    assert L.sgla_last_error().decode() != ""
+
+
+def hng_args(**kw):
+    a = dict(o=P["no"], g=P["ng"], gamma=P["gm"], out=P["nout"], B=2, H=16, T=64, d_v=192,
+             n_tiers=4, eps=1e-6, dt=B.SGLA_BF16)
+    a.update(kw)
+    return [a["o"], a["g"], a["gamma"], a["out"], a["B"], a["H"], a["T"], a["d_v"], a["n_tiers"],
+            a["eps"], a["dt"], None]
+
+
+HNG_BAD = [
+    ("o null", dict(o=None), B.SGLA_ERR_INVALID_ARG),
+    ("g null", dict(g=None), B.SGLA_ERR_INVALID_ARG),
+    ("out null", dict(out=None), B.SGLA_ERR_INVALID_ARG),
+    ("gamma misaligned", dict(gamma=P["gm"] + 4), B.SGLA_ERR_INVALID_ARG),
+    ("T zero", dict(T=0), B.SGLA_ERR_INVALID_ARG),
+    ("n_tiers zero", dict(n_tiers=0), B.SGLA_ERR_INVALID_ARG),
+    ("n_tiers not dividing H", dict(n_tiers=3), B.SGLA_ERR_INVALID_ARG),
+    ("eps negative", dict(eps=-1e-6), B.SGLA_ERR_INVALID_ARG),
+    ("eps nan", dict(eps=float("nan")), B.SGLA_ERR_INVALID_ARG),
+    ("eps inf", dict(eps=float("inf")), B.SGLA_ERR_INVALID_ARG),
+    ("bad dtype", dict(dt=7), B.SGLA_ERR_INVALID_ARG),
+    ("d_v not mult 4", dict(d_v=190), B.SGLA_ERR_UNSUPPORTED),
+    ("d_v above 256", dict(d_v=260), B.SGLA_ERR_UNSUPPORTED),
+    ("out overlaps o", dict(out=P["no"] + 4096), B.SGLA_ERR_INVALID_ARG),
+    ("out partly overlaps g", dict(out=P["ng"] + 64), B.SGLA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", HNG_BAD, ids=[x[0] for x in HNG_BAD])
+def test_head_norm_gate_rejects(L, name, kw, code):
+    assert L.sgla_head_norm_gate(*hng_args(**kw)) == code
     assert L.sgla_last_error().decode() != ""
