@@ -34,8 +34,10 @@
 // body_wide below):
 //   * LDS tiles are row-major ([CT][d'] for q', k'; [CT][96] for v', x) with
 //     16-byte segments permuted within each row, segment c of row r stored at
-//     c ^ sw(r), so that both the row reads of the score operands and the
-//     transposing reads touch distinct banks.
+//     c ^ sw<SEG>(r), so that the 16-byte row reads, the 8-byte row reads
+//     and the 4-column transposing reads are free of bank conflicts (the
+//     8-column transposing reads of K' take two passes per 32 lanes, the
+//     least any segment permutation allows them).
 //   * Operands that contract over tokens (V'^T, K'^T) come from the row-major
 //     tiles through ds_read_b64_tr_b16: within a 16-lane group, lanes 4s + q
 //     address token T0 + s at columns c0 + 4q (tr_read), and lane i receives
@@ -111,18 +113,27 @@ __device__ __forceinline__ float powl2(int m, float l2)
     return m == 0 ? 1.0f : __builtin_amdgcn_exp2f((float)m * l2);
 }
 
-// Segment permutation of a tile row: segment c of row r lives at c ^ sw(r).
+// Segment permutation of a tile row with SEG 16-byte segments: segment c of
+// row r lives at c ^ sw<SEG>(r). gfx950's LDS has 64 four-byte banks and
+// serves a 16-byte-per-lane access 16 lanes at a time (8-byte: 32 lanes), so
+// 16 consecutive rows at one logical segment must land on 16 distinct 16-byte
+// bank groups. Rows of 4 or 12 segments repeat their bank offset every 4 rows,
+// so the mask cycles with r / 4; rows of 8 or 24 segments repeat it every
+// 2 rows, so the mask (up to 7, which keeps c ^ mask inside the row because
+// SEG is a multiple of 8) cycles with r / 2.
+template <int SEG>
 __device__ __forceinline__ int sw(int r)
 {
-    const int x = (r >> 1) & 3;
-    return ((x & 1) << 1) | (x >> 1);
+    static_assert(SEG % 4 == 0, "SEG");
+    if constexpr (SEG % 8 == 0) return (r >> 1) & 7;
+    else return (r >> 2) & 3;
 }
 
 // Byte offset of element e of row r in a swizzled tile with SEG 16-byte segments per row.
 template <int SEG>
 __device__ __forceinline__ int toff(int r, int e)
 {
-    return r * (SEG * 16) + (((e >> 3) ^ sw(r)) << 4) + ((e & 7) << 1);
+    return r * (SEG * 16) + (((e >> 3) ^ sw<SEG>(r)) << 4) + ((e & 7) << 1);
 }
 
 // 16 bytes per lane from global memory straight into LDS: lane l's bytes land
@@ -340,7 +351,7 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
             for (int m = 0; m < Ly::NLQ; ++m) {
                 const int P = 64 * m + lane;
                 const int r = P / SEGK;
-                const int cs = (P - r * SEGK) ^ sw(r);
+                const int cs = (P - r * SEGK) ^ sw<SEGK>(r);
                 const int rr = R::REV ? cl - 1 - min(r, cl - 1) : min(r, cl - 1);
                 offq[m] = (uint32_t)(rr * dkr + min(8 * cs, dkr - 8)) * 2u;
             }
@@ -348,7 +359,7 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
             for (int m = 0; m < Ly::NLV; ++m) {
                 const int P = 64 * m + lane;
                 const int r = P / SEGV;
-                const int cs = (P - r * SEGV) ^ sw(r);
+                const int cs = (P - r * SEGV) ^ sw<SEGV>(r);
                 const int rr = R::REV ? cl - 1 - min(r, cl - 1) : min(r, cl - 1);
                 offv[m] = (uint32_t)(rr * dvr + min(n0 + 8 * cs, dvr - 8)) * 2u;
             }
@@ -382,7 +393,7 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
             const u32x4_t zero = {0u, 0u, 0u, 0u};
             for (int P = lane; P < CT * SEGK; P += 64) {
                 const int r = P / SEGK;
-                const int cs = (P - r * SEGK) ^ sw(r);
+                const int cs = (P - r * SEGK) ^ sw<SEGK>(r);
                 if (r >= cl || 8 * cs >= dkr) {
                     *reinterpret_cast<u32x4_t*>(st + 16 * P) = zero;
                     *reinterpret_cast<u32x4_t*>(st + Ly::OFF_K + 16 * P) = zero;
@@ -390,7 +401,7 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
             }
             for (int P = lane; P < CT * SEGV; P += 64) {
                 const int r = P / SEGV;
-                const int cs = (P - r * SEGV) ^ sw(r);
+                const int cs = (P - r * SEGV) ^ sw<SEGV>(r);
                 if (r >= cl || n0 + 8 * cs >= dvr) {
                     *reinterpret_cast<u32x4_t*>(st + Ly::OFF_V + 16 * P) = zero;
                     if constexpr (R::GRAD) *reinterpret_cast<u32x4_t*>(st + Ly::OFF_X + 16 * P) = zero;
