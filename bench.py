@@ -1,6 +1,6 @@
 """Benchmark of the Simple GLA hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only fwd|fwdbwd|decode|varlen|norm|conv]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only fwd|fwdbwd|decode|varlen|long|norm|conv]
                     [--no-cpu]
 
 Prints ONE JSON line. The headline ("value") is the Laplace-layer forward:
@@ -16,6 +16,9 @@ Also measured in the same run and reported under "secondary" (same clock):
           consecutive in-place steps, tokens/s = 1280 * 64 / t
   varlen: 32 packed sequences, lengths log-uniform in [128, 32768] (one of
           32768), init states ~ N(0, 0.02), tokens/s = sum T / t
+  long:   one sequence of T=32768 (B=1, H=16) with initial and final state,
+          single pass and segmented (8 segments joined by a state scan),
+          tokens/s = 32768 / t
   norm:   the mixer epilogue (Head RMSNorm per decay tier, 4 tiers, + SiLU(g)
           gate) on a B=8 T=2048 forward's output: o and g in, out written,
           bf16, tokens/s = 16384 / t
@@ -82,7 +85,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--only", choices=["fwd", "fwdbwd", "decode", "varlen", "norm", "conv"],
+    ap.add_argument("--only", choices=["fwd", "fwdbwd", "decode", "varlen", "long", "norm", "conv"],
                     default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--min-warm-s", type=float, default=1.5,
@@ -308,6 +311,35 @@ def bench_varlen(args):
             "gbs": bytes_ / (ms * 1e-3) / 1e9, "n_seq": int(len(L)), "max_len": int(np.max(L))}
 
 
+def bench_long(args, T=32768, n_segments=8):
+    """One long sequence (B=1, H=16, T=32768: the longest sequence of the
+    packed workload as a batch of its own), initial and final state: the
+    single-pass forward runs 32 workgroups down a 512-tile chain; the
+    segmented forward cuts it into n_segments runs joined by a state scan."""
+    import torch
+    from chunked_gated_linear_simple_amd import binding as Bd
+    lam = Bd.sgla_decay_schedule(H, 1.0, 2048.0).cuda()
+    a = gen((H, DK), 61, 0.1)
+    q = gen((1, H, T, DK), 600, scale=DK ** -0.5, dtype=torch.bfloat16)
+    k = gen((1, H, T, DK), 601, dtype=torch.bfloat16)
+    v = gen((1, H, T, DV), 602, dtype=torch.bfloat16)
+    s0 = gen((1, H, DK, DV), 603, 0.02)
+    sf = torch.empty_like(s0)
+    o = torch.empty_like(v)
+    ws = torch.empty(Bd.sgla_chunk_fwd_segmented_workspace_bytes(1, H, DK, DV, n_segments) // 4,
+                     dtype=torch.float32, device="cuda")
+    steps = max(3, args.steps // 4)
+    ms1, _ = timed(lambda i: Bd.sgla_chunk_fwd(q, k, v, lam, a, init_state=s0, final_state=sf,
+                                               o=o, chunk=128), steps, 2)
+    ms, _ = timed(lambda i: Bd.sgla_chunk_fwd_segmented(q, k, v, lam, a, init_state=s0,
+                                                        final_state=sf, o=o, n_segments=n_segments,
+                                                        workspace=ws), steps, 2)
+    bytes_ = H * T * HT_BYTES + 2 * H * STATE_BYTES
+    return {"ms": ms, "ms_single_pass": ms1, "tokens": T, "tok_s": T / (ms * 1e-3),
+            "tok_s_single_pass": T / (ms1 * 1e-3), "n_segments": n_segments, "bytes": bytes_,
+            "gbs": bytes_ / (ms * 1e-3) / 1e9}
+
+
 def cpu_baseline(min_seconds=10.0, B=8, T=2048):
     """The fp64 oracle (untuned test infrastructure) on the headline workload:
     all B*H (sequence, head) units of B=8, T=2048, one thread per unit over
@@ -372,6 +404,8 @@ def main():
         secondary["decode_N1280_64steps"] = bench_decode(args)
     if only in (None, "varlen"):
         secondary["varlen_32seq"] = bench_varlen(args)
+    if only in (None, "long"):
+        secondary["long_B1_T32768_segmented"] = bench_long(args)
     if only in (None, "norm"):
         secondary["head_norm_gate_B8_T2048"] = bench_norm(args)
     if only in (None, "conv"):

@@ -51,6 +51,11 @@ def lib() -> ctypes.CDLL:
         L.sgla_chunk_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i,
                                      _i, _i, _i, _i, _i, _i, _i, _vp]
         L.sgla_chunk_fwd.restype = _i
+        L.sgla_chunk_fwd_segmented_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
+        L.sgla_chunk_fwd_segmented_workspace_bytes.restype = ctypes.c_size_t
+        L.sgla_chunk_fwd_segmented.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i,
+                                               _i, _i, _i, _i, _i, _vp, ctypes.c_size_t, _vp]
+        L.sgla_chunk_fwd_segmented.restype = _i
         L.sgla_chunk_bwd_workspace_bytes.argtypes = [_i, _i, _i]
         L.sgla_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.sgla_chunk_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -154,6 +159,43 @@ def sgla_chunk_fwd(q, k, v, lam, a=None, init_state=None, final_state=None, o=No
                                 _ptr(init_state), _ptr(final_state), _ptr(o), _ptr(cu_seqlens),
                                 n_seq, B, H, T, d_k, d_v, int(chunk), _dtype_code(q),
                                 _stream(dev)))
+    return o, final_state
+
+
+def sgla_chunk_fwd_segmented_workspace_bytes(B: int, H: int, d_k: int, d_v: int,
+                                              n_segments: int) -> int:
+    return int(lib().sgla_chunk_fwd_segmented_workspace_bytes(int(B), int(H), int(d_k), int(d_v),
+                                                              int(n_segments)))
+
+
+def sgla_chunk_fwd_segmented(q, k, v, lam, a=None, init_state=None, final_state=None, o=None,
+                             n_segments: int = 2, chunk: int = 128, want_final: bool = False,
+                             workspace=None):
+    """Segment-parallel forward of dense sequences. Returns (o, final_state)
+    (final_state None unless passed or want_final)."""
+    dev = q.device
+    B, H, T, d_k, d_v, _ = _geometry(q, v, None)
+    _need(q, "q", device=dev)
+    _need(k, "k", q.dtype, dev, q.shape)
+    _need(v, "v", q.dtype, dev, (B, H, T, d_v))
+    _need(lam, "lambda", torch.float32, dev, (H,))
+    _need(a, "a", torch.float32, dev, (H, d_k))
+    _need(init_state, "init_state", torch.float32, dev, (B, H, d_k, d_v))
+    if o is None:
+        o = torch.empty((B, H, T, d_v), dtype=q.dtype, device=dev)
+    _need(o, "o", q.dtype, dev, (B, H, T, d_v))
+    if final_state is None and want_final:
+        final_state = torch.empty((B, H, d_k, d_v), dtype=torch.float32, device=dev)
+    _need(final_state, "final_state", torch.float32, dev, (B, H, d_k, d_v))
+    nbytes = sgla_chunk_fwd_segmented_workspace_bytes(B, H, d_k, d_v, n_segments)
+    if workspace is None:
+        workspace = torch.empty((max(nbytes, 16) + 3) // 4, dtype=torch.float32, device=dev)
+    _need(workspace, "workspace", device=dev)
+    _check(lib().sgla_chunk_fwd_segmented(_ptr(q), _ptr(k), _ptr(v), _ptr(lam), _ptr(a),
+                                          _ptr(init_state), _ptr(final_state), _ptr(o), B, H, T,
+                                          d_k, d_v, int(chunk), _dtype_code(q), int(n_segments),
+                                          _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                          _stream(dev)))
     return o, final_state
 
 

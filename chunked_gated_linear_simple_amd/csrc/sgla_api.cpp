@@ -162,6 +162,54 @@ sgla_status sgla_chunk_fwd(const void* q, const void* k, const void* v, const fl
     return ok();
 }
 
+size_t sgla_chunk_fwd_segmented_workspace_bytes(int B, int H, int d_k, int d_v, int n_segments)
+{
+    if (B <= 0 || H <= 0 || d_k <= 0 || d_v <= 0 || n_segments <= 0) return 0;
+    return 2 * (size_t)B * n_segments * H * d_k * d_v * sizeof(float);
+}
+
+sgla_status sgla_chunk_fwd_segmented(const void* q, const void* k, const void* v,
+                                     const float* lambda, const float* a,
+                                     const float* init_state, float* final_state, void* o,
+                                     int B, int H, int T, int d_k, int d_v, int chunk,
+                                     sgla_dtype dtype, int n_segments, void* workspace,
+                                     size_t workspace_bytes, void* hip_stream)
+{
+    sgla::ChunkProblem p;
+    sgla_status st = check_chunk(q, k, v, lambda, a, nullptr, 0, B, H, T, d_k, d_v, chunk, dtype, &p);
+    if (st != SGLA_OK) return st;
+    if (dtype != SGLA_BF16)
+        return fail(SGLA_ERR_UNSUPPORTED, "the segmented forward needs SGLA_BF16");
+    if (n_segments <= 0) return fail(SGLA_ERR_INVALID_ARG, "n_segments must be positive, got %d", n_segments);
+    REQUIRE_PTR(o);
+    OPTIONAL_PTR(init_state);
+    OPTIONAL_PTR(final_state);
+    const size_t need = sgla_chunk_fwd_segmented_workspace_bytes(B, H, d_k, d_v, n_segments);
+    if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
+        return fail(SGLA_ERR_WORKSPACE, "workspace needs %zu bytes, 16-byte aligned (got %zu at %p)",
+                    need, workspace_bytes, workspace);
+    const size_t nqk = (size_t)B * H * T * d_k * 2, nvo = (size_t)B * H * T * d_v * 2;
+    if (overlaps(o, nvo, q, nqk) || overlaps(o, nvo, k, nqk) || overlaps(o, nvo, v, nvo))
+        return fail(SGLA_ERR_INVALID_ARG, "o must not alias q, k or v");
+    // segments of whole 64-token tiles (the tile of the bf16 kernels)
+    const int tiles = (T + 63) / 64;
+    const int g = n_segments < tiles ? n_segments : tiles;
+    const int seg_len = ((tiles + g - 1) / g) * 64;
+    const int nseg = (T + seg_len - 1) / seg_len;
+    const hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+    hipError_t e;
+    if (nseg <= 1) {
+        e = sgla::launch_chunk_fwd(p, q, k, v, init_state, final_state, o, stream);
+    } else {
+        float* ws_loc = reinterpret_cast<float*>(workspace);
+        float* ws_in = ws_loc + (size_t)B * nseg * H * d_k * d_v;
+        e = sgla::launch_fwd_bf16_segmented(p, q, k, v, init_state, final_state, o, nseg, seg_len,
+                                            ws_loc, ws_in, stream);
+    }
+    if (e != hipSuccess) return fail(SGLA_ERR_HIP, "chunk_fwd_segmented launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 size_t sgla_chunk_bwd_workspace_bytes(int N, int H, int d_k)
 {
     if (N <= 0 || H <= 0 || d_k <= 0) return 0;

@@ -31,12 +31,36 @@ hipError_t run_fwd(const Args& a, hipStream_t stream)
     return hipGetLastError();
 }
 
+// Segment scan of the states: a run of L tokens maps the state S entering it
+// to lam^L S + S_loc, with S_loc the state it leaves from a zero start. With
+// loc[n][g] the state leaving segment g (segment 0 from the true initial
+// state, the others from zero), the state entering segment g >= 1 is
+//   in[n][1] = loc[n][0],  in[n][g] = lam^L in[n][g-1] + loc[n][g-1].
+// One thread per four state elements of one (sequence, head), in order over g.
+__global__ void k_seg_scan(const float* __restrict__ loc, float* __restrict__ in,
+                           const float* __restrict__ lambda, int n_seq, int nseg, int H,
+                           int ssz4, int seg_len)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    const int nh = blockIdx.y;                 // n H + h
+    if (i >= ssz4) return;
+    const int n = nh / H, h = nh - n * H;
+    const float fL = __builtin_amdgcn_exp2f((float)seg_len * log2f(lambda[h]));
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    auto at = [&](int g) -> size_t { return (((size_t)n * nseg + g) * H + h) * (size_t)ssz4 + i; };
+    f4 s = reinterpret_cast<const f4*>(loc)[at(0)];
+    reinterpret_cast<f4*>(in)[at(1)] = s;
+    for (int g = 2; g < nseg; ++g) {
+        const f4 l = reinterpret_cast<const f4*>(loc)[at(g - 1)];
+        s = fL * s + l;
+        reinterpret_cast<f4*>(in)[at(g)] = s;
+    }
+}
+
 }  // namespace scan
 
-// bf16 forward with d_k <= 96 (padded to 32, 64 or 96) and any d_v (96-column slices).
-hipError_t launch_fwd_bf16(const ChunkProblem& p, const void* q, const void* k, const void* v,
-                           const float* init_state, float* final_state, void* o,
-                           hipStream_t stream)
+static scan::Args fwd_args(const ChunkProblem& p, const void* q, const void* k, const void* v,
+                           const float* init_state, float* final_state, void* o)
 {
     scan::Args a{};
     a.q = reinterpret_cast<const uint16_t*>(q);
@@ -56,9 +80,51 @@ hipError_t launch_fwd_bf16(const ChunkProblem& p, const void* q, const void* k, 
     a.nsl = (p.d_v + scan::DVS - 1) / scan::DVS;
     a.dkr = p.d_k;
     a.dvr = p.d_v;
-    if (p.d_k <= 32) return scan::run_fwd<32>(a, stream);
-    if (p.d_k <= 64) return scan::run_fwd<64>(a, stream);
+    return a;
+}
+
+static hipError_t run_fwd_any(const scan::Args& a, int d_k, hipStream_t stream)
+{
+    if (d_k <= 32) return scan::run_fwd<32>(a, stream);
+    if (d_k <= 64) return scan::run_fwd<64>(a, stream);
     return scan::run_fwd<96>(a, stream);
+}
+
+// Segment-parallel bf16 forward of dense sequences (see sgla_chunk_fwd_segmented):
+// segments 0 .. nseg-2 from their provisional starts, the scan of the states,
+// then segments 1 .. nseg-1 from their true starts (rewriting their outputs).
+hipError_t launch_fwd_bf16_segmented(const ChunkProblem& p, const void* q, const void* k,
+                                     const void* v, const float* init_state, float* final_state,
+                                     void* o, int nseg, int seg_len, float* ws_loc, float* ws_in,
+                                     hipStream_t stream)
+{
+    scan::Args a = fwd_args(p, q, k, v, init_state, final_state, o);
+    a.nseg = nseg;
+    a.seg_len = seg_len;
+    a.seg_first = 0;
+    a.seg_count = nseg - 1;
+    a.s_in_seg = nullptr;
+    a.s_out_seg = ws_loc;
+    a.n_units = p.n_seq * (nseg - 1) * p.H;
+    hipError_t e = run_fwd_any(a, p.d_k, stream);
+    if (e != hipSuccess) return e;
+    const int ssz4 = p.d_k * p.d_v / 4;
+    hipLaunchKernelGGL(scan::k_seg_scan, dim3((ssz4 + 255) / 256, p.n_seq * p.H), dim3(256), 0, stream,
+                       ws_loc, ws_in, p.lambda, p.n_seq, nseg, p.H, ssz4, seg_len);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.seg_first = 1;
+    a.s_in_seg = ws_in;
+    a.s_out_seg = nullptr;
+    return run_fwd_any(a, p.d_k, stream);
+}
+
+// bf16 forward with d_k <= 96 (padded to 32, 64 or 96) and any d_v (96-column slices).
+hipError_t launch_fwd_bf16(const ChunkProblem& p, const void* q, const void* k, const void* v,
+                           const float* init_state, float* final_state, void* o,
+                           hipStream_t stream)
+{
+    return run_fwd_any(fwd_args(p, q, k, v, init_state, final_state, o), p.d_k, stream);
 }
 
 }  // namespace sgla

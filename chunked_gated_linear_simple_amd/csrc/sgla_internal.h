@@ -29,6 +29,13 @@ hipError_t launch_fwd_bf16(const ChunkProblem& p, const void* q, const void* k, 
                            const float* init_state, float* final_state, void* o,
                            hipStream_t stream);
 
+// bf16 forward of dense sequences cut into nseg >= 2 segments of seg_len
+// tokens (sgla_fwd.hip); ws_loc and ws_in hold [n_seq][nseg][H][d_k][d_v] fp32.
+hipError_t launch_fwd_bf16_segmented(const ChunkProblem& p, const void* q, const void* k,
+                                     const void* v, const float* init_state, float* final_state,
+                                     void* o, int nseg, int seg_len, float* ws_loc, float* ws_in,
+                                     hipStream_t stream);
+
 // bf16 backward, d_k <= 96, d_v <= 192: the DV/DQ/DK roles of sgla_bwd.hip.
 hipError_t launch_bwd_bf16(const ChunkProblem& p, const void* q, const void* k, const void* v,
                            const void* dO, const float* init_state, const float* d_final_state,

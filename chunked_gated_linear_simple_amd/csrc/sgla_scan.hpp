@@ -203,6 +203,15 @@ struct Args {
     float* s_final;          // [units][dkr][dvr] or NULL
     float* da_part;          // [units][dvr] (DA roles)
     int H, T, n_units, nsl, dkr, dvr;
+    // Segments (dense FWD only; nseg <= 1: whole sequences). Sequence n is cut
+    // into nseg segments of seg_len tokens (the last one shorter); a launch
+    // runs segments seg_first .. seg_first + seg_count - 1 of every sequence,
+    // unit = ((n seg_count) + i) H + h. Segment 0 enters with s_init and the
+    // last one leaves into s_final; the others enter with s_in_seg and leave
+    // into s_out_seg, both [n][nseg][H][dkr][dvr] (NULL: zero / not written).
+    int nseg, seg_len, seg_first, seg_count;
+    const float* s_in_seg;
+    float* s_out_seg;
 };
 
 // ----------------------------------------------------------------------------
@@ -306,7 +315,13 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int H = p.H;
-    const int seq = unit / H, h = unit - seq * H;
+    int seq = unit / H;
+    const int h = unit - seq * H;
+    int g = 0;                     // segment
+    if (p.nseg > 1) {
+        g = p.seg_first + seq % p.seg_count;
+        seq /= p.seg_count;
+    }
     const int dkr = p.dkr, dvr = p.dvr;
     const int n0 = slice * DVS;
 
@@ -321,6 +336,10 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
     } else {
         row0 = ((long)seq * H + h) * p.T;
         len = p.T;
+        if (p.nseg > 1) {
+            row0 += (long)g * p.seg_len;
+            len = min(p.seg_len, p.T - g * p.seg_len);
+        }
     }
     auto grow = [&](int c, int r) -> long { return R::REV ? row0 + len - 1 - (c * CT + r) : row0 + c * CT + r; };
     const int nch = (len + CT - 1) / CT;
@@ -581,7 +600,15 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
     const int w = wave;
     const int l16 = lane & 15, qg = lane >> 4;
     const int ncol = n0 + OWC * w + l16;       // this lane's v' column in the row
-    const size_t sbase = (size_t)unit * dkr * dvr;
+    // the state entering and leaving this unit's run of tokens
+    const size_t ssz = (size_t)dkr * dvr;
+    const size_t shead = ((size_t)seq * H + h) * ssz;
+    const size_t sseg = (((size_t)seq * max(p.nseg, 1) + g) * H + h) * ssz;
+    const bool last_seg = p.nseg <= 1 || g == p.nseg - 1;
+    const float* s_in = (g == 0) ? (p.s_init != nullptr ? p.s_init + shead : nullptr)
+                                 : (p.s_in_seg != nullptr ? p.s_in_seg + sseg : nullptr);
+    float* s_out = last_seg ? (p.s_final != nullptr ? p.s_final + shead : nullptr)
+                            : (p.s_out_seg != nullptr ? p.s_out_seg + sseg : nullptr);
 
     // Accumulator row 4 qg + r of 16-row block db holds state row srow(db, r)
     auto srow = [&](int db, int r) { return 32 * (db >> 1) + 8 * qg + 4 * (db & 1) + r; };
@@ -591,8 +618,8 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int d = srow(db, r);
-            const size_t si = R::INIT_T ? sbase + (size_t)ncol * dkr + d : sbase + (size_t)d * dvr + ncol;
-            sacc[db][r] = (p.s_init != nullptr && d < dkr && ncol < dvr) ? p.s_init[si] : 0.0f;
+            const size_t si = R::INIT_T ? (size_t)ncol * dkr + d : (size_t)d * dvr + ncol;
+            sacc[db][r] = (s_in != nullptr && d < dkr && ncol < dvr) ? s_in[si] : 0.0f;
         }
     float tdec[NTB];
 #pragma unroll
@@ -734,13 +761,13 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
     }
 
     // (the gradient scans of q and k end without a state output)
-    if (!R::GRAD && p.s_final != nullptr && ncol < dvr) {
+    if (!R::GRAD && s_out != nullptr && ncol < dvr) {
 #pragma unroll
         for (int db = 0; db < NDB16; ++db)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int d = srow(db, r);
-                if (d < dkr) p.s_final[sbase + (size_t)d * dvr + ncol] = sacc[db][r];
+                if (d < dkr) s_out[(size_t)d * dvr + ncol] = sacc[db][r];
             }
     }
     if constexpr (R::DA) {

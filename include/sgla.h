@@ -124,6 +124,50 @@ sgla_status sgla_chunk_fwd(const void* q, const void* k, const void* v,
                            sgla_dtype dtype, void* hip_stream);
 
 /*
+ * Bytes of device workspace sgla_chunk_fwd_segmented needs: two arrays of
+ * B * n_segments * H states of d_k * d_v fp32.
+ */
+size_t sgla_chunk_fwd_segmented_workspace_bytes(int B, int H, int d_k, int d_v, int n_segments);
+
+/*
+ * Segment-parallel chunked forward of long dense sequences, for when B * H
+ * (sequence, head) pairs are too few to occupy the GPU. Same result as
+ * sgla_chunk_fwd up to rounding. Laplace 3B post, "Challenge 1: Using native
+ * PyTorch on Trainium for GLA": only the state update is sequential, and the
+ * state after a run of L tokens is lam^L times the state before it plus the
+ * run's own decayed key/value sum (the chunk state-advance equation applied
+ * over the run). Each sequence is cut into segments of whole 64-token tiles,
+ * ceil(T / n_segments) tokens rounded up (fewer segments when T is short):
+ *   1. the forward over segments 0 .. G-2, segment 0 from init_state and the
+ *      others from zero, keeping the state each one leaves;
+ *   2. a scan of those states: entering segment g, lam^L (entering g-1) plus
+ *      (leaving g-1 from zero), the first being the state leaving segment 0;
+ *   3. the forward over segments 1 .. G-1 from their true entering states,
+ *      which rewrites their outputs and writes final_state.
+ * Three kernel launches on hip_stream, about (2G - 2) / G times the work of
+ * sgla_chunk_fwd over G times as many workgroups.
+ *
+ * q, k, v, lambda, a, init_state, final_state, o, B, H, T, d_k, d_v, chunk:
+ *              as for sgla_chunk_fwd, dense layout only (no cu_seqlens);
+ *              final_state may equal init_state.
+ * dtype:       SGLA_BF16 only (SGLA_ERR_UNSUPPORTED otherwise).
+ * n_segments:  segments per sequence requested, >= 1; 1 is sgla_chunk_fwd.
+ * workspace:   device buffer of at least
+ *              sgla_chunk_fwd_segmented_workspace_bytes(B, H, d_k, d_v,
+ *              n_segments) bytes, 16-byte aligned, owned by the caller, not
+ *              overlapping any other argument; contents on entry do not
+ *              matter and are clobbered.
+ * Errors: as sgla_chunk_fwd, plus SGLA_ERR_INVALID_ARG for n_segments < 1
+ * and SGLA_ERR_WORKSPACE if workspace is NULL, unaligned or too small.
+ */
+sgla_status sgla_chunk_fwd_segmented(const void* q, const void* k, const void* v,
+                                     const float* lambda, const float* a,
+                                     const float* init_state, float* final_state, void* o,
+                                     int B, int H, int T, int d_k, int d_v, int chunk,
+                                     sgla_dtype dtype, int n_segments, void* workspace,
+                                     size_t workspace_bytes, void* hip_stream);
+
+/*
  * Bytes of device workspace sgla_chunk_bwd needs for these sizes (the per
  * sequence-head partial sums of da). N is n_seq for packed input, else B.
  */

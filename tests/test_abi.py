@@ -117,6 +117,43 @@ def test_chunk_fwd_rejects(L, name, kw, code):
     assert L.sgla_last_error().decode() != ""
 
 
+def seg_args(**kw):
+    a = dict(q=P["q"], k=P["k"], v=P["v"], lam=P["lam"], a=P["a"], s0=P["s0"], sf=P["sf"],
+             o=P["o"], B=2, H=16, T=4096, d_k=96, d_v=192, chunk=128, dt=B.SGLA_BF16, nseg=4,
+             ws=P["ws"], wsb=2 * 2 * 4 * 16 * 96 * 192 * 4)
+    a.update(kw)
+    return [a["q"], a["k"], a["v"], a["lam"], a["a"], a["s0"], a["sf"], a["o"], a["B"], a["H"],
+            a["T"], a["d_k"], a["d_v"], a["chunk"], a["dt"], a["nseg"], a["ws"], a["wsb"], None]
+
+
+SEG_BAD = [
+    ("q null", dict(q=None), B.SGLA_ERR_INVALID_ARG),
+    ("o null", dict(o=None), B.SGLA_ERR_INVALID_ARG),
+    ("n_segments zero", dict(nseg=0), B.SGLA_ERR_INVALID_ARG),
+    ("n_segments negative", dict(nseg=-2), B.SGLA_ERR_INVALID_ARG),
+    ("f32", dict(dt=B.SGLA_F32, d_k=16, d_v=32, chunk=64), B.SGLA_ERR_UNSUPPORTED),
+    ("d_k too big", dict(d_k=128), B.SGLA_ERR_UNSUPPORTED),
+    ("workspace null", dict(ws=None), B.SGLA_ERR_WORKSPACE),
+    ("workspace small", dict(wsb=2 * 2 * 4 * 16 * 96 * 192 * 4 - 16), B.SGLA_ERR_WORKSPACE),
+    ("workspace misaligned", dict(ws=P["ws"] + 8), B.SGLA_ERR_WORKSPACE),
+    ("o aliases k", dict(o=P["k"]), B.SGLA_ERR_INVALID_ARG),
+    ("final misaligned", dict(sf=P["sf"] + 4), B.SGLA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", SEG_BAD, ids=[x[0] for x in SEG_BAD])
+def test_chunk_fwd_segmented_rejects(L, name, kw, code):
+    assert L.sgla_chunk_fwd_segmented(*seg_args(**kw)) == code
+    assert L.sgla_last_error().decode() != ""
+
+
+def test_segmented_workspace_bytes(L):
+    # two arrays of B * n_segments * H states of d_k * d_v fp32
+    assert B.sgla_chunk_fwd_segmented_workspace_bytes(1, 16, 96, 192, 8) == 2 * 8 * 16 * 96 * 192 * 4
+    assert B.sgla_chunk_fwd_segmented_workspace_bytes(2, 4, 32, 64, 3) == 2 * 2 * 3 * 4 * 32 * 64 * 4
+    assert B.sgla_chunk_fwd_segmented_workspace_bytes(1, 16, 96, 192, 0) == 0
+
+
 def bwd_args(**kw):
     a = dict(q=P["q"], k=P["k"], v=P["v"], dO=P["dO"], lam=P["lam"], a=P["a"], s0=P["s0"],
              dsf=P["sf"], dq=P["dq"], dk=P["dk"], dv=P["dv"], da=P["da"], ds0=P["ds0"], cu=None,
