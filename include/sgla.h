@@ -152,6 +152,11 @@ size_t sgla_chunk_fwd_segmented_workspace_bytes(int B, int H, int d_k, int d_v, 
  *              final_state may equal init_state.
  * dtype:       SGLA_BF16 only (SGLA_ERR_UNSUPPORTED otherwise).
  * n_segments:  segments per sequence requested, >= 1; 1 is sgla_chunk_fwd.
+ *              Each forward launch runs (G - 1) * B * H * ceil(d_v / 96)
+ *              workgroups of one per CU, so G - 1 = CUs / (B * H * ceil(d_v
+ *              / 96)) fills the GPU once (on 256 CUs at H = 16, d_v = 192:
+ *              G = 9 for B = 1, 5 for B = 2); at B * H * ceil(d_v / 96) >=
+ *              CUs / 2 the single pass is as fast or faster.
  * workspace:   device buffer of at least
  *              sgla_chunk_fwd_segmented_workspace_bytes(B, H, d_k, d_v,
  *              n_segments) bytes, 16-byte aligned, owned by the caller, not
