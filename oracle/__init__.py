@@ -59,8 +59,11 @@ def _load():
         lib.orc_conv_decode_step.argtypes = [ctypes.c_int, _dp, _dp, _dp, _dp, _dp]
         lib.orc_head_norm_gate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_double, _dp, _dp, _dp, _dp]
+        lib.orc_head_norm_gate_bwd.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_double, _dp, _dp, _dp, _dp, _dp, _dp, _dp]
         for f in (lib.orc_decay_schedule, lib.orc_fwd, lib.orc_bwd, lib.orc_decode_step,
-                  lib.orc_conv_fwd, lib.orc_conv_decode_step, lib.orc_head_norm_gate):
+                  lib.orc_conv_fwd, lib.orc_conv_decode_step, lib.orc_head_norm_gate,
+                  lib.orc_head_norm_gate_bwd):
             f.restype = None
         _lib = lib
     return _lib
@@ -270,3 +273,28 @@ def head_norm_gate(o, g, gamma=None, n_tiers=1, eps=1e-6):
         for t in range(T):
             out[b, t] = head_norm_gate_token(o[b, :, t, :], g[b, t], gamma, n_tiers, eps)
     return out
+
+
+def head_norm_gate_bwd(o, g, gamma, dout, n_tiers=1, eps=1e-6):
+    """Gradients of head_norm_gate for L = sum(dout * out): o [B, H, T, d_v],
+    g and dout [B, T, H, d_v], gamma [n_tiers, d_v] or None (one). Returns
+    (d_o [B, H, T, d_v], dg [B, T, H, d_v], dgamma [n_tiers, d_v]); dgamma is
+    the gradient at gamma = 1 when gamma is None."""
+    o = np.asarray(o)
+    B, H, T, d_v = o.shape
+    gam = _f64(gamma)
+    d_o = np.zeros((B, H, T, d_v))
+    dg = np.zeros((B, T, H, d_v))
+    dgamma = np.zeros((n_tiers, d_v))
+    lib = _load()
+    for b in range(B):
+        for t in range(T):
+            ot = _f64(o[b, :, t, :])
+            do_t = np.zeros((H, d_v))
+            dg_t = np.zeros((H, d_v))
+            lib.orc_head_norm_gate_bwd(H, d_v, int(n_tiers), float(eps), _ptr(ot), _ptr(_f64(g[b, t])),
+                                       _ptr(gam), _ptr(_f64(dout[b, t])), _ptr(do_t), _ptr(dg_t),
+                                       _ptr(dgamma))
+            d_o[b, :, t, :] = do_t
+            dg[b, t] = dg_t
+    return d_o, dg, dgamma

@@ -322,3 +322,47 @@ void orc_head_norm_gate(int H, int d_v, int n_tiers, double eps, const double* o
         }
     }
 }
+
+/* Gradients of the mixer epilogue for ONE token, given dout = dL/dout [H][d_v].
+ * With r = sqrt(mean_c o[h][c]^2 + eps), y = o / r, s = silu(g) and the scale
+ * gm = gamma[tier(h)][c] (1 when gamma is NULL), out = s gm y, so
+ *   dL/dg[h][c]     = dout gm y silu'(g),    silu'(x) = sigmoid(x) (1 + x (1 - sigmoid(x)))
+ *   dL/dgamma[t][c] += sum over the heads h of tier t of dout s y
+ *   dL/dy[h][c]     = w = dout s gm
+ *   dL/do[h][c]     = (w - y mean_c' (w y)) / r
+ * (the last by differentiating y = o / r through r). dgamma is accumulated,
+ * not overwritten, so that callers can sum it over tokens; NULL skips it. */
+void orc_head_norm_gate_bwd(int H, int d_v, int n_tiers, double eps, const double* o,
+                            const double* g, const double* gamma, const double* dout,
+                            double* d_o, double* dg, double* dgamma)
+{
+    const int per_tier = H / n_tiers;
+    for (int h = 0; h < H; ++h) {
+        const double* oh = o + (size_t)h * d_v;
+        double ss = 0.0;
+        for (int c = 0; c < d_v; ++c) {
+            ss += oh[c] * oh[c];
+        }
+        const double r = sqrt(ss / d_v + eps);
+        const int tier = h / per_tier;
+        double wy = 0.0;
+        for (int c = 0; c < d_v; ++c) {
+            const size_t i = (size_t)h * d_v + c;
+            const double gm = (gamma != NULL) ? gamma[(size_t)tier * d_v + c] : 1.0;
+            const double y = oh[c] / r;
+            const double sg = sigmoid(g[i]);
+            const double s = g[i] * sg;
+            dg[i] = dout[i] * gm * y * sg * (1.0 + g[i] * (1.0 - sg));
+            if (dgamma != NULL) {
+                dgamma[(size_t)tier * d_v + c] += dout[i] * s * y;
+            }
+            wy += dout[i] * s * gm * y;
+        }
+        for (int c = 0; c < d_v; ++c) {
+            const size_t i = (size_t)h * d_v + c;
+            const double gm = (gamma != NULL) ? gamma[(size_t)tier * d_v + c] : 1.0;
+            const double w = dout[i] * silu(g[i]) * gm;
+            d_o[i] = (w - (oh[c] / r) * (wy / d_v)) / r;
+        }
+    }
+}

@@ -73,6 +73,13 @@ void orc_conv_decode_step(int D, const double* w, const double* b, const double*
 void orc_head_norm_gate(int H, int d_v, int n_tiers, double eps, const double* o,
                         const double* g, const double* gamma, double* out);
 
+/* Gradients of orc_head_norm_gate for ONE token given dout [H][d_v]: d_o and
+ * dg [H][d_v] are overwritten, dgamma [n_tiers][d_v] is accumulated (NULL:
+ * skipped). gamma NULL means one, as in the forward. */
+void orc_head_norm_gate_bwd(int H, int d_v, int n_tiers, double eps, const double* o,
+                            const double* g, const double* gamma, const double* dout,
+                            double* d_o, double* dg, double* dgamma);
+
 #ifdef __cplusplus
 }
 #endif

@@ -402,6 +402,51 @@ def check_hng_gate_silu():
     _close(out[0, 0, 0], g * expit(g), 1e-15, "silu")
 
 
+def _hng_loss(o, g, gamma, dout, n_tiers, eps):
+    return float(np.sum(dout * oracle.head_norm_gate(o, g, gamma, n_tiers, eps)))
+
+
+def check_hng_bwd_finite_differences():
+    """Gradients of the epilogue against central finite differences of
+    L = sum(dout * out) in every coordinate of o, g and gamma (eps > 0, two
+    tiers, two tokens)."""
+    n_tiers, eps = 2, 1e-3
+    o, g, gamma = _hng_case(51, 4, 6, n_tiers, B=1, T=2)
+    dout = _rng(52).standard_normal(g.shape)
+    d_o, dg, dgamma = oracle.head_norm_gate_bwd(o, g, gamma, dout, n_tiers, eps)
+    for name, x, grad in (("o", o, d_o), ("g", g, dg), ("gamma", gamma, dgamma)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            h = 1e-6 * max(1.0, abs(x[idx]))
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args = {"o": o, "g": g, "gamma": gamma}
+            args[name] = xp
+            lp = _hng_loss(args["o"], args["g"], args["gamma"], dout, n_tiers, eps)
+            args[name] = xm
+            lm = _hng_loss(args["o"], args["g"], args["gamma"], dout, n_tiers, eps)
+            fd[idx] = (lp - lm) / (2 * h)
+        err = np.max(np.abs(fd - grad)) / max(np.max(np.abs(fd)), 1e-300)
+        assert err < 1e-7, f"epilogue d{name}: FD mismatch {err:.2e}"
+
+
+def check_hng_bwd_scale_invariance():
+    """eps = 0: the output does not change when a head's o is scaled, so the
+    gradient in o is orthogonal to o, head by head; gamma = None matches
+    gamma = 1 in every gradient."""
+    o, g, gamma = _hng_case(53, 4, 10, 2, B=2, T=3)
+    dout = _rng(54).standard_normal(g.shape)
+    d_o, _, _ = oracle.head_norm_gate_bwd(o, g, gamma, dout, 2, 0.0)
+    dots = np.sum(d_o * o, axis=-1)
+    scale = np.sum(np.abs(d_o) * np.abs(o), axis=-1)
+    assert np.max(np.abs(dots) / scale) < 1e-13, "d_o not orthogonal to o"
+    a = oracle.head_norm_gate_bwd(o, g, None, dout, 2, 1e-4)
+    b = oracle.head_norm_gate_bwd(o, g, np.ones_like(gamma), dout, 2, 1e-4)
+    for x, y, nm in zip(a, b, ("d_o", "dg", "dgamma")):
+        _close(x, y, 0, nm + " (gamma None vs ones)")
+
+
 ALL_CHECKS = [
     check_schedule_printed_values,
     check_schedule_geometric,
@@ -424,4 +469,6 @@ ALL_CHECKS = [
     check_hng_tiers_and_channels,
     check_hng_eps,
     check_hng_gate_silu,
+    check_hng_bwd_finite_differences,
+    check_hng_bwd_scale_invariance,
 ]

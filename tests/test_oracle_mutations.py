@@ -53,14 +53,24 @@ MUTATIONS = [
     ("conv decode state not shifted", "st[c] = st[(size_t)D + c];", "st[c] = st[c];"),
     ("conv decode tap 2 reads x", "acc += w[(size_t)c * 4 + 2] * st[(size_t)2 * D + c];",
      "acc += w[(size_t)c * 4 + 2] * x[c];"),
-    ("norm eps dropped", "sqrt(ss / d_v + eps)", "sqrt(ss / d_v)"),
+    ("norm eps dropped", "inv_rms = 1.0 / sqrt(ss / d_v + eps)", "inv_rms = 1.0 / sqrt(ss / d_v)"),
     ("norm eps outside the root", "1.0 / sqrt(ss / d_v + eps)", "1.0 / (sqrt(ss / d_v) + eps)"),
-    ("norm sums instead of averaging", "sqrt(ss / d_v + eps)", "sqrt(ss + eps)"),
-    ("norm tier by head modulo", "const int tier = h / per_tier;", "const int tier = h % n_tiers;"),
-    ("norm gamma transposed", "gamma[(size_t)tier * d_v + c]", "gamma[(size_t)c * n_tiers + tier]"),
+    ("norm sums instead of averaging", "inv_rms = 1.0 / sqrt(ss / d_v + eps)", "inv_rms = 1.0 / sqrt(ss + eps)"),
+    ("norm tier by head modulo", "const double inv_rms = 1.0 / sqrt(ss / d_v + eps);\n        const int tier = h / per_tier;",
+     "const double inv_rms = 1.0 / sqrt(ss / d_v + eps);\n        const int tier = h % n_tiers;"),
+    ("norm gamma transposed", "const double scale = (gamma != NULL) ? gamma[(size_t)tier * d_v + c] : 1.0;",
+     "const double scale = (gamma != NULL) ? gamma[(size_t)c * n_tiers + tier] : 1.0;"),
+    ("norm bwd tier by head modulo", "const double r = sqrt(ss / d_v + eps);\n        const int tier = h / per_tier;",
+     "const double r = sqrt(ss / d_v + eps);\n        const int tier = h % n_tiers;"),
     ("norm gate sigmoid instead of silu", "out[(size_t)h * d_v + c] = silu(gc) *",
      "out[(size_t)h * d_v + c] = sigmoid(gc) *"),
     ("norm gate dropped", "out[(size_t)h * d_v + c] = silu(gc) *", "out[(size_t)h * d_v + c] = 1.0 *"),
+    ("norm bwd eps dropped", "const double r = sqrt(ss / d_v + eps);", "const double r = sqrt(ss / d_v);"),
+    ("norm bwd silu' without the x term", "sg * (1.0 + g[i] * (1.0 - sg))", "sg * (1.0 - sg)"),
+    ("norm bwd projection dropped", "d_o[i] = (w - (oh[c] / r) * (wy / d_v)) / r;", "d_o[i] = w / r;"),
+    ("norm bwd dgamma without the gate", "dgamma[(size_t)tier * d_v + c] += dout[i] * s * y;",
+     "dgamma[(size_t)tier * d_v + c] += dout[i] * y;"),
+    ("norm bwd dg without gamma", "dg[i] = dout[i] * gm * y *", "dg[i] = dout[i] * y *"),
 ]
 
 
@@ -77,7 +87,7 @@ def test_mutation_is_caught(name, find, repl, tmp_path):
     good = oracle._load()
     bad = ctypes.CDLL(str(so))
     for fn in ("orc_decay_schedule", "orc_fwd", "orc_bwd", "orc_decode_step", "orc_conv_fwd",
-               "orc_conv_decode_step", "orc_head_norm_gate"):
+               "orc_conv_decode_step", "orc_head_norm_gate", "orc_head_norm_gate_bwd"):
         getattr(bad, fn).argtypes = getattr(good, fn).argtypes
         getattr(bad, fn).restype = None
     caught = []
