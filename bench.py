@@ -21,7 +21,8 @@ Also measured in the same run and reported under "secondary" (same clock):
           tokens/s = 32768 / t
   norm:   the mixer epilogue (Head RMSNorm per decay tier, 4 tiers, + SiLU(g)
           gate) on a B=8 T=2048 forward's output: o and g in, out written,
-          bf16, tokens/s = 16384 / t
+          bf16, tokens/s = 16384 / t; and its gradients (o, g, dout in, d_o,
+          dg, dgamma out)
   conv:   the conv prologue (depthwise causal width-4 Conv1d + SiLU) at the
           layer's width D=3072: forward B=8 T=2048 bf16 with conv states in and
           out, and 64 decode steps of 1280 sequences' conv states
@@ -287,6 +288,35 @@ def bench_norm(args, B=8, T=2048, n_tiers=4, nsets=3):
             "gbs": bytes_ / (ms * 1e-3) / 1e9}
 
 
+def bench_norm_bwd(args, B=8, T=2048, n_tiers=4, nsets=2):
+    """Gradients of the mixer epilogue at the Laplace layer's size: o, g,
+    dout in (bf16), d_o and dg out (bf16), dgamma [4, 192] fp32 through the
+    fixed-order partial sums; 2 input sets rotated (1.0 GB)."""
+    import torch
+    from chunked_gated_linear_simple_amd import binding as Bd
+    gm = (1.0 + gen((n_tiers, DV), 95, 0.1)).contiguous()
+    dgm = torch.empty_like(gm)
+    ws = torch.empty(Bd.sgla_head_norm_gate_bwd_workspace_bytes(B, H, T, DV) // 4,
+                     dtype=torch.float32, device="cuda")
+    sets = []
+    for s in range(nsets):
+        o = gen((B, H, T, DV), 96 + 3 * s, dtype=torch.bfloat16)
+        g = gen((B, T, H, DV), 97 + 3 * s, dtype=torch.bfloat16)
+        dout = gen((B, T, H, DV), 98 + 3 * s, dtype=torch.bfloat16)
+        sets.append((o, g, dout, torch.empty_like(o), torch.empty_like(g)))
+
+    def step(i):
+        o, g, dout, d_o, dg = sets[i % nsets]
+        Bd.sgla_head_norm_gate_bwd(o, g, dout, gm, n_tiers, 1e-6, d_o=d_o, dg=dg, dgamma=dgm,
+                                   workspace=ws)
+
+    ms, _ = timed(step, args.steps, args.warmup)
+    toks = B * T
+    bytes_ = 5 * B * T * H * DV * 2 + 2 * n_tiers * DV * 4
+    return {"ms": ms, "tokens": toks, "tok_s": toks / (ms * 1e-3), "bytes": bytes_,
+            "gbs": bytes_ / (ms * 1e-3) / 1e9}
+
+
 def bench_varlen(args):
     import numpy as np
     import torch
@@ -410,6 +440,7 @@ def main():
         secondary["long_B1_T32768_segmented"] = bench_long(args)
     if only in (None, "norm"):
         secondary["head_norm_gate_B8_T2048"] = bench_norm(args)
+        secondary["head_norm_gate_bwd_B8_T2048"] = bench_norm_bwd(args)
     if only in (None, "conv"):
         secondary["conv_fwd_B8_T2048_D3072"] = bench_conv(args)
         secondary["conv_decode_N1280_D3072_64steps"] = bench_conv_decode(args)

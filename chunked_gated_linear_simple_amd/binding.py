@@ -72,6 +72,11 @@ def lib() -> ctypes.CDLL:
         L.sgla_head_norm_gate.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, ctypes.c_float, _i,
                                           _vp]
         L.sgla_head_norm_gate.restype = _i
+        L.sgla_head_norm_gate_bwd_workspace_bytes.argtypes = [_i, _i, _i, _i]
+        L.sgla_head_norm_gate_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.sgla_head_norm_gate_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
+                                              ctypes.c_float, _i, _vp, ctypes.c_size_t, _vp]
+        L.sgla_head_norm_gate_bwd.restype = _i
         _lib = L
     return _lib
 
@@ -328,3 +333,40 @@ def sgla_head_norm_gate(o, g, gamma=None, n_tiers=1, eps=1e-6, out=None):
     _check(lib().sgla_head_norm_gate(_ptr(o), _ptr(g), _ptr(gamma), _ptr(out), B, H, T, d_v,
                                      int(n_tiers), float(eps), _dtype_code(o), _stream(dev)))
     return out
+
+
+def sgla_head_norm_gate_bwd_workspace_bytes(B: int, H: int, T: int, d_v: int) -> int:
+    return int(lib().sgla_head_norm_gate_bwd_workspace_bytes(int(B), int(H), int(T), int(d_v)))
+
+
+def sgla_head_norm_gate_bwd(o, g, dout, gamma=None, n_tiers=1, eps=1e-6, want_dgamma=True,
+                            d_o=None, dg=None, dgamma=None, workspace=None):
+    """Gradients of sgla_head_norm_gate. o [B, H, T, d_v]; g and dout shaped
+    like the forward's g ([B, T, H, d_v] or [B, T, H * d_v]). Returns
+    (d_o [B, H, T, d_v], dg shaped like g, dgamma [n_tiers, d_v] fp32 or None)."""
+    dev = o.device
+    B, H, T, d_v = o.shape
+    _need(o, "o", device=dev)
+    gshape = (B, T, H * d_v) if g.dim() == 3 else (B, T, H, d_v)
+    _need(g, "g", o.dtype, dev, gshape)
+    _need(dout, "dout", o.dtype, dev, gshape)
+    _need(gamma, "gamma", torch.float32, dev, (n_tiers, d_v))
+    if d_o is None:
+        d_o = torch.empty_like(o)
+    _need(d_o, "d_o", o.dtype, dev, (B, H, T, d_v))
+    if dg is None:
+        dg = torch.empty_like(g)
+    _need(dg, "dg", o.dtype, dev, gshape)
+    if dgamma is None and want_dgamma:
+        dgamma = torch.empty((n_tiers, d_v), dtype=torch.float32, device=dev)
+    _need(dgamma, "dgamma", torch.float32, dev, (n_tiers, d_v))
+    nbytes = sgla_head_norm_gate_bwd_workspace_bytes(B, H, T, d_v)
+    if workspace is None and dgamma is not None:
+        workspace = torch.empty((max(nbytes, 16) + 3) // 4, dtype=torch.float32, device=dev)
+    _need(workspace, "workspace", device=dev)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().sgla_head_norm_gate_bwd(_ptr(o), _ptr(g), _ptr(gamma), _ptr(dout), _ptr(d_o),
+                                         _ptr(dg), _ptr(dgamma), B, H, T, d_v, int(n_tiers),
+                                         float(eps), _dtype_code(o), _ptr(workspace), wsb,
+                                         _stream(dev)))
+    return d_o, dg, dgamma

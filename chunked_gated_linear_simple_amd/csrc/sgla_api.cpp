@@ -383,4 +383,56 @@ sgla_status sgla_head_norm_gate(const void* o, const void* g, const float* gamma
     return ok();
 }
 
+size_t sgla_head_norm_gate_bwd_workspace_bytes(int B, int H, int T, int d_v)
+{
+    if (B <= 0 || H <= 0 || T <= 0 || d_v <= 0) return 0;
+    return sgla::head_norm_gate_bwd_part_floats(B, H, T, d_v) * sizeof(float);
+}
+
+sgla_status sgla_head_norm_gate_bwd(const void* o, const void* g, const float* gamma, const void* dout,
+                                    void* d_o, void* dg, float* dgamma, int B, int H, int T, int d_v,
+                                    int n_tiers, float eps, sgla_dtype dtype, void* workspace,
+                                    size_t workspace_bytes, void* hip_stream)
+{
+    REQUIRE_PTR(o);
+    REQUIRE_PTR(g);
+    REQUIRE_PTR(dout);
+    REQUIRE_PTR(d_o);
+    REQUIRE_PTR(dg);
+    OPTIONAL_PTR(gamma);
+    OPTIONAL_PTR(dgamma);
+    if (dtype != SGLA_F32 && dtype != SGLA_BF16)
+        return fail(SGLA_ERR_INVALID_ARG, "dtype %d is not SGLA_F32 or SGLA_BF16", (int)dtype);
+    if (B <= 0 || H <= 0 || T <= 0 || d_v <= 0 || n_tiers <= 0)
+        return fail(SGLA_ERR_INVALID_ARG, "sizes must be positive (B=%d H=%d T=%d d_v=%d n_tiers=%d)", B, H, T,
+                    d_v, n_tiers);
+    if (H % n_tiers != 0)
+        return fail(SGLA_ERR_INVALID_ARG, "n_tiers (%d) must divide H (%d)", n_tiers, H);
+    if (!(eps >= 0.0f) || !std::isfinite(eps))
+        return fail(SGLA_ERR_INVALID_ARG, "eps must be finite and >= 0 (got %g)", (double)eps);
+    if ((double)B * H * T * d_v > 2.0e9) return fail(SGLA_ERR_INVALID_ARG, "B*H*T*d_v too large");
+    if (d_v % 4 != 0 || d_v > 256)
+        return fail(SGLA_ERR_UNSUPPORTED, "d_v must be a multiple of 4, at most 256 (got %d)", d_v);
+    if (dgamma != nullptr) {
+        const size_t need = sgla_head_norm_gate_bwd_workspace_bytes(B, H, T, d_v);
+        if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
+            return fail(SGLA_ERR_WORKSPACE, "workspace needs %zu bytes, 16-byte aligned (got %zu at %p)", need,
+                        workspace_bytes, workspace);
+    }
+    const size_t nb = (size_t)B * H * T * d_v * (dtype == SGLA_BF16 ? 2 : 4);
+    const void* ins[3] = {o, g, dout};
+    for (int i = 0; i < 3; ++i) {
+        if (overlaps(d_o, nb, ins[i], nb)) return fail(SGLA_ERR_INVALID_ARG, "d_o must not overlap o, g or dout");
+        if (i < 2 && overlaps(dg, nb, ins[i], nb)) return fail(SGLA_ERR_INVALID_ARG, "dg must not overlap o or g");
+    }
+    if (dg != dout && overlaps(dg, nb, dout, nb))
+        return fail(SGLA_ERR_INVALID_ARG, "dg must equal dout or not overlap it");
+    if (overlaps(d_o, nb, dg, nb)) return fail(SGLA_ERR_INVALID_ARG, "d_o must not overlap dg");
+    hipError_t e = sgla::launch_head_norm_gate_bwd(dtype == SGLA_BF16, o, g, gamma, dout, d_o, dg, dgamma,
+                                                   reinterpret_cast<float*>(workspace), B, H, T, d_v, n_tiers,
+                                                   eps, reinterpret_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(SGLA_ERR_HIP, "head_norm_gate_bwd launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // extern "C"

@@ -64,6 +64,13 @@ hipError_t launch_conv_decode(int bf16, const void* x, const float* w, const flo
 hipError_t launch_head_norm_gate(int bf16, const void* o, const void* g, const float* gamma, void* out, int B,
                                  int H, int T, int d_v, int n_tiers, float eps, hipStream_t stream);
 
+// Gradients of the mixer epilogue (sgla_norm.hip); part holds
+// head_norm_gate_bwd_part_floats() floats when dgamma is wanted.
+size_t head_norm_gate_bwd_part_floats(int B, int H, int T, int d_v);
+hipError_t launch_head_norm_gate_bwd(int bf16, const void* o, const void* g, const float* gamma, const void* dout,
+                                     void* d_o, void* dg, float* dgamma, float* part, int B, int H, int T, int d_v,
+                                     int n_tiers, float eps, hipStream_t stream);
+
 }  // namespace sgla
 
 #endif

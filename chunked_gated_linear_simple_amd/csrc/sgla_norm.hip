@@ -203,7 +203,263 @@ hipError_t run_norm_dv(const void* o, const void* g, const float* gamma, void* o
     }
 }
 
+// ---------------------------------------------------------------------------
+// Gradients of the epilogue. Per (b, h, t) row, with r = sqrt(mean o^2 + eps),
+// y = o / r, s = silu(g), gm = gamma[tier(h)] (one without gamma) and
+// w = dout s gm:
+//   dg     = dout gm y silu'(g),   silu'(x) = sigmoid(x) (1 + x (1 - sigmoid(x)))
+//   d_o    = (w - y mean_c (w y)) / r
+//   dgamma[tier] = sum over the tier's rows of dout s y
+// A block takes 64 consecutive tokens of one (b, h) (so one tier): lane group
+// q of wave w owns tokens 16 w + 4 s + q, 16 lanes per row as in the forward.
+// Its dgamma contribution is summed over its 16 lane groups in a fixed order
+// into part[(b H + h) nTB + tb][d_v]; k_dgamma_sum then adds the partials of
+// each tier in a fixed order, so dgamma is bitwise reproducible.
+constexpr int NB_TOK = 64;  // tokens per block
+
+__device__ __forceinline__ float sigmoid_g(float x)
+{
+    // 1 / (1 + e^-x); e^-x -> inf for very negative x gives 0
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
+
+template <typename E, int NC, bool FULL, bool GAMMA, bool DGAMMA>
+__global__ __launch_bounds__(NORM_THREADS) void k_head_norm_gate_bwd(
+    const E* __restrict__ o, const E* __restrict__ g, const float* __restrict__ gamma, const E* dout,
+    E* __restrict__ d_o, E* dg, float* __restrict__ part, int H, int T, int d_v, int per_tier, float inv_dv,
+    float eps)
+{
+    constexpr int S = NORM_STEPS;
+    const int lane = threadIdx.x & 63;
+    const int q = lane >> 4, j = lane & 15;
+    const int w = threadIdx.x >> 6;
+    const int tb = blockIdx.x, bh = blockIdx.y;
+    const int b = bh / H, h = bh - b * H;
+    const int tier = h / per_tier;
+    auto in_row = [&](int m) { return FULL || 64 * m + 4 * j < d_v; };
+
+    int oo[S], go[S];
+    bool live[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int t = tb * NB_TOK + 16 * w + 4 * s + q;
+        live[s] = t < T;
+        const int tt = live[s] ? t : T - 1;  // a dead row reads a valid one and stores nothing
+        oo[s] = (bh * T + tt) * d_v;
+        go[s] = ((b * T + tt) * H + h) * d_v;
+    }
+    float gm[NC][4];
+#pragma unroll
+    for (int m = 0; m < NC; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gm[m][i] = 1.0f;
+    if (GAMMA) {
+#pragma unroll
+        for (int m = 0; m < NC; ++m)
+            if (in_row(m)) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(gamma + (size_t)tier * d_v + 64 * m + 4 * j);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) gm[m][i] = x[i];
+            }
+    }
+
+    // every load first
+    typename Ch4<E>::Raw ro[S][NC], rg[S][NC], rd[S][NC];
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int m = 0; m < NC; ++m) {
+            const int c = 64 * m + 4 * j;
+            if (in_row(m)) {
+                ro[s][m] = Ch4<E>::load(o + (size_t)oo[s] + c);
+                rg[s][m] = Ch4<E>::load(g + (size_t)go[s] + c);
+                rd[s][m] = Ch4<E>::load(dout + (size_t)go[s] + c);
+            } else {
+                ro[s][m] = Ch4<E>::zero();
+                rg[s][m] = Ch4<E>::zero();
+                rd[s][m] = Ch4<E>::zero();
+            }
+        }
+
+    float acc[NC][4];
+#pragma unroll
+    for (int m = 0; m < NC; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[m][i] = 0.0f;
+
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        float x[NC][4], gv[NC][4], dv[NC][4];
+        float ss = 0.0f;
+#pragma unroll
+        for (int m = 0; m < NC; ++m) {
+            Ch4<E>::unpack(ro[s][m], x[m]);
+            Ch4<E>::unpack(rg[s][m], gv[m]);
+            Ch4<E>::unpack(rd[s][m], dv[m]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ss = fmaf(x[m][i], x[m][i], ss);
+        }
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+        const float inv = __builtin_amdgcn_rsqf(fmaf(ss, inv_dv, eps));
+        // y, silu and w; the row's sum of w y
+        float y[NC][4], sg[NC][4], wv[NC][4];
+        float p = 0.0f;
+#pragma unroll
+        for (int m = 0; m < NC; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                y[m][i] = x[m][i] * inv;
+                sg[m][i] = sigmoid_g(gv[m][i]);
+                wv[m][i] = dv[m][i] * (gv[m][i] * sg[m][i]) * gm[m][i];
+                p = fmaf(wv[m][i], y[m][i], p);
+            }
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) p += __shfl_xor(p, off);
+        const float pm = p * inv_dv;
+        if (!live[s]) continue;
+#pragma unroll
+        for (int m = 0; m < NC; ++m) {
+            if (!in_row(m)) continue;
+            const int c = 64 * m + 4 * j;
+            float a[4], bgr[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                a[i] = inv * fmaf(-y[m][i], pm, wv[m][i]);
+                bgr[i] = dv[m][i] * gm[m][i] * y[m][i] * sg[m][i] * fmaf(gv[m][i], 1.0f - sg[m][i], 1.0f);
+                if (DGAMMA) acc[m][i] = fmaf(dv[m][i] * (gv[m][i] * sg[m][i]), y[m][i], acc[m][i]);
+            }
+            Ch4<E>::store(d_o + (size_t)oo[s] + c, a);
+            Ch4<E>::store(dg + (size_t)go[s] + c, bgr);
+        }
+    }
+
+    if (DGAMMA) {
+        // the block's dgamma row: 16 lane groups (4 per wave) summed in order
+        __shared__ float red[16][NC * 64];
+        const int grp = 4 * w + q;
+#pragma unroll
+        for (int m = 0; m < NC; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[grp][64 * m + 4 * j + i] = acc[m][i];
+        __syncthreads();
+        const int nTB = gridDim.x;
+        for (int c = threadIdx.x; c < d_v; c += NORM_THREADS) {
+            float t = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) t += red[k][c];
+            part[((size_t)bh * nTB + tb) * d_v + c] = t;
+        }
+    }
+}
+
+// dgamma[tier][c] = sum over b, the tier's heads and the token blocks, in
+// that fixed order split 16 ways: thread (k, c) sums entries k, k + 16, ...;
+// then the 16 sums are added in order.
+__global__ __launch_bounds__(1024) void k_dgamma_sum(const float* __restrict__ part, float* __restrict__ dgamma,
+                                                     int B, int H, int nTB, int d_v, int per_tier)
+{
+    __shared__ float red[16][64];
+    const int tier = blockIdx.x;
+    const int cl = threadIdx.x & 63, k = threadIdx.x >> 6;
+    const int c = blockIdx.y * 64 + cl;
+    const int n_ent = B * per_tier * nTB;
+    float t = 0.0f;
+    if (c < d_v) {
+        for (int e = k; e < n_ent; e += 16) {
+            const int bb = e / (per_tier * nTB);
+            const int rem = e - bb * per_tier * nTB;
+            const int hh = tier * per_tier + rem / nTB;
+            const int tb = rem - (rem / nTB) * nTB;
+            t += part[(((size_t)bb * H + hh) * nTB + tb) * d_v + c];
+        }
+    }
+    red[k][cl] = t;
+    __syncthreads();
+    if (k == 0 && c < d_v) {
+        float x = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x += red[i][cl];
+        dgamma[(size_t)tier * d_v + c] = x;
+    }
+}
+
+template <typename E, int NC, bool FULL, bool GAMMA>
+hipError_t run_norm_bwd(const void* o, const void* g, const float* gamma, const void* dout, void* d_o,
+                        void* dg, float* dgamma, float* part, int B, int H, int T, int d_v, int n_tiers,
+                        float eps, hipStream_t stream)
+{
+    const int nTB = (T + NB_TOK - 1) / NB_TOK;
+    const dim3 grid(nTB, B * H);
+    const float inv_dv = 1.0f / (float)d_v;
+    if (dgamma != nullptr) {
+        hipLaunchKernelGGL((k_head_norm_gate_bwd<E, NC, FULL, GAMMA, true>), grid, dim3(NORM_THREADS), 0, stream,
+                           reinterpret_cast<const E*>(o), reinterpret_cast<const E*>(g), gamma,
+                           reinterpret_cast<const E*>(dout), reinterpret_cast<E*>(d_o), reinterpret_cast<E*>(dg),
+                           part, H, T, d_v, H / n_tiers, inv_dv, eps);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k_dgamma_sum, dim3(n_tiers, (d_v + 63) / 64), dim3(1024), 0, stream, part, dgamma, B, H,
+                           nTB, d_v, H / n_tiers);
+    } else {
+        hipLaunchKernelGGL((k_head_norm_gate_bwd<E, NC, FULL, GAMMA, false>), grid, dim3(NORM_THREADS), 0, stream,
+                           reinterpret_cast<const E*>(o), reinterpret_cast<const E*>(g), gamma,
+                           reinterpret_cast<const E*>(dout), reinterpret_cast<E*>(d_o), reinterpret_cast<E*>(dg),
+                           part, H, T, d_v, H / n_tiers, inv_dv, eps);
+    }
+    return hipGetLastError();
+}
+
+template <typename E, int NC, bool FULL>
+hipError_t run_norm_bwd_g(const void* o, const void* g, const float* gamma, const void* dout, void* d_o, void* dg,
+                          float* dgamma, float* part, int B, int H, int T, int d_v, int n_tiers, float eps,
+                          hipStream_t stream)
+{
+    if (gamma != nullptr)
+        return run_norm_bwd<E, NC, FULL, true>(o, g, gamma, dout, d_o, dg, dgamma, part, B, H, T, d_v, n_tiers,
+                                               eps, stream);
+    return run_norm_bwd<E, NC, FULL, false>(o, g, gamma, dout, d_o, dg, dgamma, part, B, H, T, d_v, n_tiers, eps,
+                                            stream);
+}
+
+template <typename E>
+hipError_t run_norm_bwd_dv(const void* o, const void* g, const float* gamma, const void* dout, void* d_o,
+                           void* dg, float* dgamma, float* part, int B, int H, int T, int d_v, int n_tiers,
+                           float eps, hipStream_t stream)
+{
+#define SGLA_NB(NC, FULL) \
+    return run_norm_bwd_g<E, NC, FULL>(o, g, gamma, dout, d_o, dg, dgamma, part, B, H, T, d_v, n_tiers, eps, stream)
+    switch (d_v) {
+    case 64: SGLA_NB(1, true);
+    case 128: SGLA_NB(2, true);
+    case 192: SGLA_NB(3, true);
+    case 256: SGLA_NB(4, true);
+    default: break;
+    }
+    switch ((d_v + 63) / 64) {
+    case 1: SGLA_NB(1, false);
+    case 2: SGLA_NB(2, false);
+    case 3: SGLA_NB(3, false);
+    default: SGLA_NB(4, false);
+    }
+#undef SGLA_NB
+}
+
 }  // namespace
+
+size_t head_norm_gate_bwd_part_floats(int B, int H, int T, int d_v)
+{
+    return (size_t)B * H * ((T + NB_TOK - 1) / NB_TOK) * d_v;
+}
+
+hipError_t launch_head_norm_gate_bwd(int bf16, const void* o, const void* g, const float* gamma, const void* dout,
+                                     void* d_o, void* dg, float* dgamma, float* part, int B, int H, int T, int d_v,
+                                     int n_tiers, float eps, hipStream_t stream)
+{
+    if (bf16)
+        return run_norm_bwd_dv<u16>(o, g, gamma, dout, d_o, dg, dgamma, part, B, H, T, d_v, n_tiers, eps, stream);
+    return run_norm_bwd_dv<float>(o, g, gamma, dout, d_o, dg, dgamma, part, B, H, T, d_v, n_tiers, eps, stream);
+}
 
 hipError_t launch_head_norm_gate(int bf16, const void* o, const void* g, const float* gamma, void* out, int B,
                                  int H, int T, int d_v, int n_tiers, float eps, hipStream_t stream)

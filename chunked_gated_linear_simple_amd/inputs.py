@@ -130,18 +130,23 @@ def conv_inputs(seed: int, shape, D: int, dtype: str, n_seq: int, w_std: float =
     return {"u": u, "w": w, "b": b, "S0": s0, "dtype": dtype, "D": D, "N": n_seq}
 
 
-STREAM_NORM = 3000  # mixer epilogue: o, g, gamma
+STREAM_NORM = 3000  # mixer epilogue: o, g, gamma, dout
 
 
 def norm_inputs(seed: int, B: int, H: int, T: int, d_v: int, n_tiers: int, dtype: str,
-                o_std: float = 1.0, g_std: float = 1.0, gamma_std: float = 0.1, gamma: bool = True):
+                o_std: float = 1.0, g_std: float = 1.0, gamma_std: float = 0.1, gamma: bool = True,
+                with_dout: bool = False):
     """Seeded inputs of the mixer epilogue: o [B, H, T, d_v] (the mixer's
     head-major output) and the gate stream g [B, T, H, d_v] in the storage
     dtype, and the per-tier scales gamma [n_tiers, d_v] = 1 + N(0, gamma_std)
-    in fp32 (or None)."""
+    in fp32 (or None); with_dout adds the upstream gradient dout ~ N(0, 1)
+    [B, T, H, d_v] in the storage dtype."""
     o = store(gaussian(seed, STREAM_NORM, (B, H, T, d_v), o_std), dtype)
     g = store(gaussian(seed, STREAM_NORM + 1, (B, T, H, d_v), g_std), dtype)
     gm = None
     if gamma:
         gm = (1.0 + gaussian(seed, STREAM_NORM + 2, (n_tiers, d_v), gamma_std)).astype(np.float32)
-    return {"o": o, "g": g, "gamma": gm, "dtype": dtype, "n_tiers": n_tiers}
+    out = {"o": o, "g": g, "gamma": gm, "dtype": dtype, "n_tiers": n_tiers}
+    if with_dout:
+        out["dout"] = store(gaussian(seed, STREAM_NORM + 3, (B, T, H, d_v)), dtype)
+    return out

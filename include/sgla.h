@@ -317,6 +317,43 @@ sgla_status sgla_head_norm_gate(const void* o, const void* g, const float* gamma
                                 int B, int H, int T, int d_v, int n_tiers, float eps,
                                 sgla_dtype dtype, void* hip_stream);
 
+/*
+ * Bytes of device workspace sgla_head_norm_gate_bwd needs when dgamma is
+ * wanted: one fp32 row of d_v per 64 tokens of each (b, h).
+ */
+size_t sgla_head_norm_gate_bwd_workspace_bytes(int B, int H, int T, int d_v);
+
+/*
+ * Gradients of sgla_head_norm_gate for a loss L with dL/dout = dout (same
+ * passages). With r = sqrt(mean_c o^2 + eps), y = o / r, s = silu(g),
+ * gm = gamma[tier(h)][c] (one when gamma is NULL) and w = dout s gm, per
+ * (b, h, t) row:
+ *   dg     = dout gm y silu'(g),     silu'(x) = sigmoid(x) (1 + x (1 - sigmoid(x)))
+ *   d_o    = (w - y mean_c (w y)) / r
+ *   dgamma[tier][c] = sum over b, t and the tier's heads of dout s y
+ * dgamma is the gradient at gamma = 1 when gamma is NULL; it is summed in a
+ * fixed order (per-block partials, then a second kernel), so it is bitwise
+ * reproducible.
+ *
+ * o, g, gamma, B, H, T, d_v, n_tiers, eps, dtype: as for the forward call.
+ * dout:    [B, T, H, d_v] (dtype), token-major like out.
+ * d_o:     [B, H, T, d_v] (dtype), head-major like o (the upstream gradient
+ *          the chunked backward takes); must not overlap any other buffer.
+ * dg:      [B, T, H, d_v] (dtype); may equal dout (in place), otherwise must
+ *          not overlap it; must not overlap o or g.
+ * dgamma:  [n_tiers, d_v] fp32, overwritten, or NULL (not computed).
+ * workspace: device buffer of at least
+ *          sgla_head_norm_gate_bwd_workspace_bytes(B, H, T, d_v) bytes,
+ *          16-byte aligned, owned by the caller, clobbered; needed only when
+ *          dgamma is not NULL (may be NULL otherwise).
+ * Errors: as sgla_head_norm_gate, plus SGLA_ERR_WORKSPACE (dgamma wanted
+ * and workspace NULL, misaligned or too small).
+ */
+sgla_status sgla_head_norm_gate_bwd(const void* o, const void* g, const float* gamma, const void* dout,
+                                    void* d_o, void* dg, float* dgamma, int B, int H, int T, int d_v,
+                                    int n_tiers, float eps, sgla_dtype dtype, void* workspace,
+                                    size_t workspace_bytes, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

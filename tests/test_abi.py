@@ -74,7 +74,7 @@ def test_decay_schedule_rejects(L, args):
 BASE = 0x7F0000000000
 P = {n: BASE + i * 0x100000000 for i, n in enumerate(
     ["q", "k", "v", "lam", "a", "s0", "sf", "o", "cu", "dO", "dq", "dk", "dv", "da", "ds0", "ws",
-     "state", "slot", "u", "w", "b", "y", "no", "ng", "gm", "nout"])}
+     "state", "slot", "u", "w", "b", "y", "no", "ng", "gm", "nout", "ndo", "ndg", "ndout", "ndgm"])}
 
 
 def fwd_args(**kw):
@@ -329,3 +329,42 @@ HNG_BAD = [
 def test_head_norm_gate_rejects(L, name, kw, code):
     assert L.sgla_head_norm_gate(*hng_args(**kw)) == code
     assert L.sgla_last_error().decode() != ""
+
+
+def hngb_args(**kw):
+    a = dict(o=P["no"], g=P["ng"], gamma=P["gm"], dout=P["ndout"], do=P["ndo"], dg=P["ndg"],
+             dgm=P["ndgm"], B=2, H=16, T=64, d_v=192, n_tiers=4, eps=1e-6, dt=B.SGLA_BF16,
+             ws=P["ws"], wsb=2 * 16 * 1 * 192 * 4)
+    a.update(kw)
+    return [a["o"], a["g"], a["gamma"], a["dout"], a["do"], a["dg"], a["dgm"], a["B"], a["H"],
+            a["T"], a["d_v"], a["n_tiers"], a["eps"], a["dt"], a["ws"], a["wsb"], None]
+
+
+HNGB_BAD = [
+    ("dout null", dict(dout=None), B.SGLA_ERR_INVALID_ARG),
+    ("d_o null", dict(do=None), B.SGLA_ERR_INVALID_ARG),
+    ("dg null", dict(dg=None), B.SGLA_ERR_INVALID_ARG),
+    ("dgamma misaligned", dict(dgm=P["ndgm"] + 4), B.SGLA_ERR_INVALID_ARG),
+    ("tiers not dividing H", dict(n_tiers=3), B.SGLA_ERR_INVALID_ARG),
+    ("eps negative", dict(eps=-1.0), B.SGLA_ERR_INVALID_ARG),
+    ("d_v 260", dict(d_v=260), B.SGLA_ERR_UNSUPPORTED),
+    ("workspace null", dict(ws=None), B.SGLA_ERR_WORKSPACE),
+    ("workspace small", dict(wsb=64), B.SGLA_ERR_WORKSPACE),
+    ("d_o aliases o", dict(do=P["no"]), B.SGLA_ERR_INVALID_ARG),
+    ("dg aliases g", dict(dg=P["ng"]), B.SGLA_ERR_INVALID_ARG),
+    ("dg overlaps dout", dict(dg=P["ndout"] + 256), B.SGLA_ERR_INVALID_ARG),
+    ("d_o overlaps dg", dict(do=P["ndg"] + 512), B.SGLA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", HNGB_BAD, ids=[x[0] for x in HNGB_BAD])
+def test_head_norm_gate_bwd_rejects(L, name, kw, code):
+    assert L.sgla_head_norm_gate_bwd(*hngb_args(**kw)) == code
+    assert L.sgla_last_error().decode() != ""
+
+
+def test_head_norm_gate_bwd_workspace_bytes(L):
+    # one fp32 row of d_v per 64 tokens of each (b, h)
+    assert B.sgla_head_norm_gate_bwd_workspace_bytes(8, 16, 2048, 192) == 8 * 16 * 32 * 192 * 4
+    assert B.sgla_head_norm_gate_bwd_workspace_bytes(1, 2, 65, 64) == 1 * 2 * 2 * 64 * 4
+    assert B.sgla_head_norm_gate_bwd_workspace_bytes(0, 2, 65, 64) == 0
