@@ -61,9 +61,11 @@ def _load():
                                            ctypes.c_double, _dp, _dp, _dp, _dp]
         lib.orc_head_norm_gate_bwd.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                ctypes.c_double, _dp, _dp, _dp, _dp, _dp, _dp, _dp]
+        lib.orc_conv_bwd.argtypes = [ctypes.c_int, ctypes.c_int, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
+                                     _dp, _dp, _dp]
         for f in (lib.orc_decay_schedule, lib.orc_fwd, lib.orc_bwd, lib.orc_decode_step,
                   lib.orc_conv_fwd, lib.orc_conv_decode_step, lib.orc_head_norm_gate,
-                  lib.orc_head_norm_gate_bwd):
+                  lib.orc_head_norm_gate_bwd, lib.orc_conv_bwd):
             f.restype = None
         _lib = lib
     return _lib
@@ -298,3 +300,18 @@ def head_norm_gate_bwd(o, g, gamma, dout, n_tiers=1, eps=1e-6):
             d_o[b, :, t, :] = do_t
             dg[b, t] = dg_t
     return d_o, dg, dgamma
+
+
+def conv_bwd_unit(u, w, b, st, dy, d_st_out=None):
+    """Gradients of conv_fwd_unit for one sequence: u, dy [L, D]; w [D, 4];
+    b [D] or None; st, d_st_out [3, D] or None. Returns (du [L, D],
+    d_st [3, D], dw [D, 4], db [D])."""
+    u, w, b, st, dy, dso = _f64(u), _f64(w), _f64(b), _f64(st), _f64(dy), _f64(d_st_out)
+    L, D = u.shape
+    du = np.zeros((L, D))
+    d_st = np.zeros((3, D))
+    dw = np.zeros((D, 4))
+    db = np.zeros(D)
+    _load().orc_conv_bwd(L, D, _ptr(w), _ptr(b), _ptr(u), _ptr(st), _ptr(dy), _ptr(dso), _ptr(du),
+                         _ptr(d_st), _ptr(dw), _ptr(db))
+    return du, d_st, dw, db

@@ -366,3 +366,63 @@ void orc_head_norm_gate_bwd(int H, int d_v, int n_tiers, double eps, const doubl
         }
     }
 }
+
+/* Gradients of orc_conv_fwd for ONE sequence of L tokens, given dy [L][D] and
+ * d_st_out [3][D] (the gradient of the final conv state, or NULL). With
+ * x_s = u_s for s >= 0 and st[3 + s] for s < 0 (zero without st), and
+ * pre_t = b + sum_j w_j x_{t-3+j}, y_t = silu(pre_t):
+ *   dpre_t       = dy_t silu'(pre_t)
+ *   dL/dx_s      = sum over j with 0 <= s + 3 - j < L of w_j dpre_{s+3-j}
+ *                  (+ d_st_out[i] when x_s is row i of the final state, s = L - 3 + i)
+ *   du_s = dL/dx_s for s >= 0;  d_st[i] = dL/dx_{i-3} (NULL: not written)
+ *   dw[c][j] += sum_t dpre_t x_{t-3+j};  db[c] += sum_t dpre_t (accumulated; NULL: skipped)
+ * The last two are accumulated so that callers can sum them over sequences. */
+void orc_conv_bwd(int L, int D, const double* w, const double* b, const double* u,
+                  const double* st, const double* dy, const double* d_st_out, double* du,
+                  double* d_st, double* dw, double* db)
+{
+    for (int c = 0; c < D; ++c) {
+        /* x_s for s = -3 .. L-1 and dpre_t for t = 0 .. L-1 of this channel */
+        double* x = (double*)malloc(sizeof(double) * (size_t)(L + 3));
+        double* dpre = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+        for (int s = -3; s < L; ++s) {
+            x[s + 3] = (s >= 0) ? u[(size_t)s * D + c] : ((st != NULL) ? st[(size_t)(3 + s) * D + c] : 0.0);
+        }
+        for (int t = 0; t < L; ++t) {
+            double pre = (b != NULL) ? b[c] : 0.0;
+            for (int j = 0; j < 4; ++j) {
+                pre += w[(size_t)c * 4 + j] * x[t + j];
+            }
+            const double sg = sigmoid(pre);
+            dpre[t] = dy[(size_t)t * D + c] * sg * (1.0 + pre * (1.0 - sg));
+            for (int j = 0; j < 4; ++j) {
+                if (dw != NULL) {
+                    dw[(size_t)c * 4 + j] += dpre[t] * x[t + j];
+                }
+            }
+            if (db != NULL) {
+                db[c] += dpre[t];
+            }
+        }
+        for (int s = -3; s < L; ++s) {
+            double g = 0.0;
+            for (int j = 0; j < 4; ++j) {
+                const int t = s + 3 - j;
+                if (t >= 0 && t < L) {
+                    g += w[(size_t)c * 4 + j] * dpre[t];
+                }
+            }
+            const int i = s - (L - 3);
+            if (d_st_out != NULL && i >= 0 && i < 3) {
+                g += d_st_out[(size_t)i * D + c];
+            }
+            if (s >= 0) {
+                du[(size_t)s * D + c] = g;
+            } else if (d_st != NULL) {
+                d_st[(size_t)(3 + s) * D + c] = g;
+            }
+        }
+        free(x);
+        free(dpre);
+    }
+}

@@ -61,6 +61,13 @@ void orc_decode_step(int d_k, int d_v, double lam, const double* a,
 void orc_conv_fwd(int L, int D, const double* w, const double* b, const double* u,
                   const double* st, double* y, double* st_out);
 
+/* Gradients of orc_conv_fwd for ONE sequence: du [L][D] and d_st [3][D]
+ * (NULL: not written) are overwritten, dw [D][4] and db [D] accumulated
+ * (NULL: skipped); d_st_out [3][D] is the final state's gradient or NULL. */
+void orc_conv_bwd(int L, int D, const double* w, const double* b, const double* u,
+                  const double* st, const double* dy, const double* d_st_out, double* du,
+                  double* d_st, double* dw, double* db);
+
 /* One conv decode step, state [3][D] in place. */
 void orc_conv_decode_step(int D, const double* w, const double* b, const double* x,
                           double* st, double* y);

@@ -402,6 +402,64 @@ def check_hng_gate_silu():
     _close(out[0, 0, 0], g * expit(g), 1e-15, "silu")
 
 
+def _conv_loss(u, w, b, st, dy, dso):
+    y, so = oracle.conv_fwd_unit(u, w, b, st)
+    return float(np.sum(dy * y) + np.sum(dso * so))
+
+
+def check_conv_bwd_finite_differences():
+    """Gradients of the conv against central finite differences of
+    L = sum(dy * y) + sum(d_final * final_state) in every coordinate of u, the
+    initial state, the taps and the bias, for a sequence longer than the
+    history (L = 6) and one shorter (L = 2, whose final state reaches into
+    the initial state)."""
+    for seed, L in ((61, 6), (62, 2)):
+        u, w, b, st = _conv_case(seed, L, 3)
+        r = _rng(seed + 100)
+        dy = r.standard_normal(u.shape)
+        dso = r.standard_normal((3, 3))
+        du, d_st, dw, db = oracle.conv_bwd_unit(u, w, b, st, dy, dso)
+        for name, grad in (("u", du), ("st", d_st), ("w", dw), ("b", db)):
+            args = {"u": u, "w": w, "b": b, "st": st}
+            x = args[name]
+            fd = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                h = 1e-6 * max(1.0, abs(x[idx]))
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                args[name] = xp
+                lp = _conv_loss(args["u"], args["w"], args["b"], args["st"], dy, dso)
+                args[name] = xm
+                lm = _conv_loss(args["u"], args["w"], args["b"], args["st"], dy, dso)
+                fd[idx] = (lp - lm) / (2 * h)
+            args[name] = x
+            err = np.max(np.abs(fd - grad)) / max(np.max(np.abs(fd)), 1e-300)
+            assert err < 1e-7, f"conv d{name} (L={L}): FD mismatch {err:.2e}"
+
+
+def check_conv_bwd_single_tap():
+    """w = e_3 (the current token only): y_t = silu(b + u_t), so du_t =
+    dy_t silu'(b + u_t) with silu' from scipy's logistic, the initial state
+    gets nothing, and the final state's gradient passes straight to the last
+    three inputs."""
+    L, D = 5, 4
+    u, _, b, st = _conv_case(63, L, D)
+    w = np.zeros((D, 4))
+    w[:, 3] = 1.0
+    dy = _rng(64).standard_normal((L, D))
+    dso = _rng(65).standard_normal((3, D))
+    du, d_st, dw, db = oracle.conv_bwd_unit(u, w, b, st, dy, dso)
+    pre = u + b
+    sg = expit(pre)
+    ref = dy * sg * (1.0 + pre * (1.0 - sg))
+    _close(db, ref.sum(axis=0), 1e-13, "db")
+    ref = ref.copy()
+    ref[L - 3:] += dso
+    _close(du, ref, 1e-13, "du")
+    _close(d_st, np.zeros((3, D)), 0, "d_st")
+
+
 def _hng_loss(o, g, gamma, dout, n_tiers, eps):
     return float(np.sum(dout * oracle.head_norm_gate(o, g, gamma, n_tiers, eps)))
 
@@ -471,4 +529,6 @@ ALL_CHECKS = [
     check_hng_gate_silu,
     check_hng_bwd_finite_differences,
     check_hng_bwd_scale_invariance,
+    check_conv_bwd_finite_differences,
+    check_conv_bwd_single_tap,
 ]

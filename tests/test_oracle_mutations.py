@@ -65,6 +65,14 @@ MUTATIONS = [
     ("norm gate sigmoid instead of silu", "out[(size_t)h * d_v + c] = silu(gc) *",
      "out[(size_t)h * d_v + c] = sigmoid(gc) *"),
     ("norm gate dropped", "out[(size_t)h * d_v + c] = silu(gc) *", "out[(size_t)h * d_v + c] = 1.0 *"),
+    ("conv bwd silu' without the x term", "dpre[t] = dy[(size_t)t * D + c] * sg * (1.0 + pre * (1.0 - sg));",
+     "dpre[t] = dy[(size_t)t * D + c] * sg * (1.0 - sg);"),
+    ("conv bwd taps not flipped", "g += w[(size_t)c * 4 + j] * dpre[t];", "g += w[(size_t)c * 4 + (3 - j)] * dpre[t];"),
+    ("conv bwd final-state gradient dropped", "g += d_st_out[(size_t)i * D + c];", "g += 0.0;"),
+    ("conv bwd dw from the wrong input", "dw[(size_t)c * 4 + j] += dpre[t] * x[t + j];",
+     "dw[(size_t)c * 4 + j] += dpre[t] * x[t + 3];"),
+    ("conv bwd history ignored", "x[s + 3] = (s >= 0) ? u[(size_t)s * D + c] : ((st != NULL) ? st[(size_t)(3 + s) * D + c] : 0.0);",
+     "x[s + 3] = (s >= 0) ? u[(size_t)s * D + c] : 0.0;"),
     ("norm bwd eps dropped", "const double r = sqrt(ss / d_v + eps);", "const double r = sqrt(ss / d_v);"),
     ("norm bwd silu' without the x term", "sg * (1.0 + g[i] * (1.0 - sg))", "sg * (1.0 - sg)"),
     ("norm bwd projection dropped", "d_o[i] = (w - (oh[c] / r) * (wy / d_v)) / r;", "d_o[i] = w / r;"),
@@ -87,7 +95,7 @@ def test_mutation_is_caught(name, find, repl, tmp_path):
     good = oracle._load()
     bad = ctypes.CDLL(str(so))
     for fn in ("orc_decay_schedule", "orc_fwd", "orc_bwd", "orc_decode_step", "orc_conv_fwd",
-               "orc_conv_decode_step", "orc_head_norm_gate", "orc_head_norm_gate_bwd"):
+               "orc_conv_decode_step", "orc_head_norm_gate", "orc_head_norm_gate_bwd", "orc_conv_bwd"):
         getattr(bad, fn).argtypes = getattr(good, fn).argtypes
         getattr(bad, fn).restype = None
     caught = []
