@@ -239,6 +239,37 @@ def bench_conv(args, B=8, T=2048, D=DMODEL, nsets=3):
             "gbs": bytes_ / (ms * 1e-3) / 1e9}
 
 
+def bench_conv_bwd(args, B=8, T=2048, D=DMODEL, nsets=2):
+    """Conv prologue gradients at the layer's width: u, dy in (bf16), du out
+    (bf16), dw, db and the initial states' gradient (fp32) out, final states'
+    gradient in; 2 input sets rotated (0.8 GB)."""
+    import torch
+    from chunked_gated_linear_simple_amd import binding as Bd
+    w = gen((D, 4), 64, 0.5)
+    b = gen((D,), 65, 0.1)
+    dw = torch.empty((D, 4), device="cuda")
+    db = torch.empty((D,), device="cuda")
+    ws = torch.empty(Bd.sgla_conv_bwd_workspace_bytes(B, T, D) // 4, device="cuda")
+    sets = []
+    for s in range(nsets):
+        sets.append((gen((B, T, D), 66 + 4 * s, dtype=torch.bfloat16),
+                     gen((B, T, D), 67 + 4 * s, dtype=torch.bfloat16),
+                     gen((B, 3, D), 68 + 4 * s), gen((B, 3, D), 69 + 4 * s),
+                     torch.empty((B, T, D), dtype=torch.bfloat16, device="cuda"),
+                     torch.empty((B, 3, D), device="cuda")))
+
+    def step(i):
+        u, dy, s0, dsf, du, ds0 = sets[i % nsets]
+        Bd.sgla_conv_bwd(u, w, dy, b=b, init_state=s0, d_final_state=dsf, du=du, dw=dw, db=db,
+                         d_init_state=ds0, workspace=ws)
+
+    ms, _ = timed(step, args.steps, args.warmup)
+    toks = B * T
+    bytes_ = 3 * B * T * D * 2 + 3 * B * 3 * D * 4 + D * 40
+    return {"ms": ms, "tokens": toks, "tok_s": toks / (ms * 1e-3), "bytes": bytes_,
+            "gbs": bytes_ / (ms * 1e-3) / 1e9}
+
+
 def bench_conv_decode(args, N=1280, D=DMODEL, steps=64, npools=8):
     """Conv decode: 64 consecutive in-place steps of 1280 sequences' conv
     states. Step s uses pool s % 8 (8 x 47 MB, beyond the on-die caches), as a
@@ -444,6 +475,7 @@ def main():
     if only in (None, "conv"):
         secondary["conv_fwd_B8_T2048_D3072"] = bench_conv(args)
         secondary["conv_decode_N1280_D3072_64steps"] = bench_conv_decode(args)
+        secondary["conv_bwd_B8_T2048_D3072"] = bench_conv_bwd(args)
     for r in secondary.values():
         r["hbm_frac_algorithmic"] = r["gbs"] / HBM_PEAK_GBS
 

@@ -72,6 +72,11 @@ def lib() -> ctypes.CDLL:
         L.sgla_head_norm_gate.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, ctypes.c_float, _i,
                                           _vp]
         L.sgla_head_norm_gate.restype = _i
+        L.sgla_conv_bwd_workspace_bytes.argtypes = [_i, _i, _i]
+        L.sgla_conv_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.sgla_conv_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i,
+                                    _i, _i, _vp, ctypes.c_size_t, _vp]
+        L.sgla_conv_bwd.restype = _i
         L.sgla_head_norm_gate_bwd_workspace_bytes.argtypes = [_i, _i, _i, _i]
         L.sgla_head_norm_gate_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.sgla_head_norm_gate_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
@@ -295,6 +300,54 @@ def sgla_conv_fwd(u, w, b=None, init_state=None, final_state=None, y=None, cu_se
                                _ptr(y), _ptr(cu_seqlens), n_seq, Bn, T, D, _dtype_code(u),
                                _stream(dev)))
     return y, final_state
+
+
+def sgla_conv_bwd_workspace_bytes(B: int, T: int, D: int) -> int:
+    return int(lib().sgla_conv_bwd_workspace_bytes(int(B), int(T), int(D)))
+
+
+def sgla_conv_bwd(u, w, dy, b=None, init_state=None, d_final_state=None, cu_seqlens=None,
+                  want_db=True, want_d_init=False, du=None, dw=None, db=None, d_init_state=None,
+                  workspace=None):
+    """Gradients of sgla_conv_fwd. u, dy [B, T, D] (or [T, D] packed with
+    cu_seqlens). Returns (du, dw [D, 4], db [D] or None, d_init_state
+    [N, 3, D] or None)."""
+    dev = u.device
+    if cu_seqlens is None:
+        Bn, T, D = u.shape
+        n_seq = Bn
+    else:
+        T, D = u.shape
+        Bn = 1
+        n_seq = cu_seqlens.numel() - 1
+    _need(u, "u", device=dev)
+    _need(dy, "dy", u.dtype, dev, tuple(u.shape))
+    _need(w, "w", torch.float32, dev, (D, 4))
+    _need(b, "b", torch.float32, dev, (D,))
+    _need(init_state, "init_state", torch.float32, dev, (n_seq, 3, D))
+    _need(d_final_state, "d_final_state", torch.float32, dev, (n_seq, 3, D))
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev, (n_seq + 1,))
+    if du is None:
+        du = torch.empty_like(u)
+    _need(du, "du", u.dtype, dev, tuple(u.shape))
+    if dw is None:
+        dw = torch.empty((D, 4), dtype=torch.float32, device=dev)
+    _need(dw, "dw", torch.float32, dev, (D, 4))
+    if db is None and want_db:
+        db = torch.empty((D,), dtype=torch.float32, device=dev)
+    _need(db, "db", torch.float32, dev, (D,))
+    if d_init_state is None and want_d_init:
+        d_init_state = torch.empty((n_seq, 3, D), dtype=torch.float32, device=dev)
+    _need(d_init_state, "d_init_state", torch.float32, dev, (n_seq, 3, D))
+    nbytes = sgla_conv_bwd_workspace_bytes(Bn, T, D)
+    if workspace is None:
+        workspace = torch.empty((max(nbytes, 16) + 3) // 4, dtype=torch.float32, device=dev)
+    _need(workspace, "workspace", device=dev)
+    _check(lib().sgla_conv_bwd(_ptr(u), _ptr(w), _ptr(b), _ptr(init_state), _ptr(dy),
+                               _ptr(d_final_state), _ptr(du), _ptr(dw), _ptr(db), _ptr(d_init_state),
+                               _ptr(cu_seqlens), n_seq, Bn, T, D, _dtype_code(u), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(dev)))
+    return du, dw, db, d_init_state
 
 
 def sgla_conv_decode_step(x, w, b, state, y=None, slot=None):

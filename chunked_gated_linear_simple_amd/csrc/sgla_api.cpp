@@ -324,6 +324,60 @@ sgla_status sgla_conv_fwd(const void* u, const float* w, const float* b, const f
     return ok();
 }
 
+size_t sgla_conv_bwd_workspace_bytes(int B, int T, int D)
+{
+    if (B <= 0 || T <= 0 || D <= 0) return 0;
+    return sgla::conv_bwd_part_floats(B, T, D, 0) * sizeof(float);
+}
+
+sgla_status sgla_conv_bwd(const void* u, const float* w, const float* b, const float* init_state, const void* dy,
+                          const float* d_final_state, void* du, float* dw, float* db, float* d_init_state,
+                          const int32_t* cu_seqlens, int n_seq, int B, int T, int D, sgla_dtype dtype,
+                          void* workspace, size_t workspace_bytes, void* hip_stream)
+{
+    REQUIRE_PTR(u);
+    REQUIRE_PTR(w);
+    REQUIRE_PTR(dy);
+    REQUIRE_PTR(du);
+    REQUIRE_PTR(dw);
+    OPTIONAL_PTR(b);
+    OPTIONAL_PTR(init_state);
+    OPTIONAL_PTR(d_final_state);
+    OPTIONAL_PTR(db);
+    OPTIONAL_PTR(d_init_state);
+    if (dtype != SGLA_F32 && dtype != SGLA_BF16)
+        return fail(SGLA_ERR_INVALID_ARG, "dtype %d is not SGLA_F32 or SGLA_BF16", (int)dtype);
+    if (B <= 0 || T <= 0 || D <= 0)
+        return fail(SGLA_ERR_INVALID_ARG, "sizes must be positive (B=%d T=%d D=%d)", B, T, D);
+    if (cu_seqlens != nullptr) {
+        if (B != 1) return fail(SGLA_ERR_INVALID_ARG, "packed sequences need B = 1 (got %d)", B);
+        if (n_seq <= 0) return fail(SGLA_ERR_INVALID_ARG, "n_seq must be positive (got %d)", n_seq);
+        if (!aligned16(cu_seqlens)) return fail(SGLA_ERR_INVALID_ARG, "cu_seqlens is not 16-byte aligned");
+    } else if (n_seq != B) {
+        return fail(SGLA_ERR_INVALID_ARG, "dense input needs n_seq == B (got %d, %d)", n_seq, B);
+    }
+    if ((double)B * T * D > 4.0e9) return fail(SGLA_ERR_INVALID_ARG, "B*T*D too large");
+    const int vec = (dtype == SGLA_BF16) ? 8 : 4;
+    if (D % vec != 0)
+        return fail(SGLA_ERR_UNSUPPORTED, "D must be a multiple of %d for this dtype (got %d)", vec, D);
+    const size_t need = sgla_conv_bwd_workspace_bytes(B, T, D);
+    if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
+        return fail(SGLA_ERR_WORKSPACE, "workspace needs %zu bytes, 16-byte aligned (got %zu at %p)", need,
+                    workspace_bytes, workspace);
+    const size_t nb = (size_t)B * T * D * (dtype == SGLA_BF16 ? 2 : 4);
+    const size_t ns = (size_t)n_seq * 3 * D * sizeof(float);
+    if (overlaps(du, nb, u, nb) || overlaps(du, nb, dy, nb))
+        return fail(SGLA_ERR_INVALID_ARG, "du must not overlap u or dy");
+    if (overlaps(d_init_state, ns, du, nb) || overlaps(d_init_state, ns, init_state, ns) ||
+        overlaps(d_init_state, ns, d_final_state, ns))
+        return fail(SGLA_ERR_INVALID_ARG, "d_init_state must not overlap du, init_state or d_final_state");
+    hipError_t e = sgla::launch_conv_bwd(dtype == SGLA_BF16, u, dy, w, b, init_state, d_final_state, du, dw, db,
+                                         d_init_state, cu_seqlens, n_seq, B, T, D,
+                                         reinterpret_cast<float*>(workspace), reinterpret_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(SGLA_ERR_HIP, "conv_bwd launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 sgla_status sgla_conv_decode_step(const void* x, const float* w, const float* b, float* state,
                                   const int32_t* slot, void* y, int N, int P, int D, sgla_dtype dtype,
                                   void* hip_stream)

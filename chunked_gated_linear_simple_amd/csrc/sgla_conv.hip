@@ -430,7 +430,247 @@ hipError_t run_conv_fwd(const void* u, const float* w, const float* b, const flo
     return hipSuccess;
 }
 
+// ---------------------------------------------------------------------------
+// Gradients. Per sequence and channel, with x_s = u_s (s >= 0) or the initial
+// state's row 3 + s, pre_t = b + sum_j w_j x_{t-3+j} and y_t = silu(pre_t):
+//   dpre_t = dy_t silu'(pre_t),   silu'(x) = sigmoid(x) (1 + x (1 - sigmoid(x)))
+//   du_s   = w_3 dpre_s + w_2 dpre_{s+1} + w_1 dpre_{s+2} + w_0 dpre_{s+3}
+//            (dpre = 0 past the sequence) + d_final[s - (L - 3)] for s >= L - 3
+//   dw_j   = sum_t dpre_t x_{t-3+j},  db = sum_t dpre_t
+// k_conv_bwd: a thread owns one channel group and a run of BWD_RUN rows; for
+// each sequence meeting the run it walks tau from max(run start, sequence
+// start) to three rows past the run's end (within the sequence), computing
+// dpre_tau and, three rows behind, du. dw and db of the run's rows go to
+// part[run][5][D]. k_conv_bwd_init writes the initial state's gradient (also
+// for empty sequences) and k_conv_wsum adds the run partials in order.
+constexpr int BWD_RUN = 32;
+constexpr int BWD_THREADS = 128;
+
+__device__ __forceinline__ float dsilu_f(float x)
+{
+    const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+    return sg * fmaf(x, 1.0f - sg, 1.0f);
+}
+
+template <typename E>
+__global__ __launch_bounds__(BWD_THREADS) void k_conv_bwd(const E* __restrict__ u, const E* __restrict__ dy,
+                                                          const float* __restrict__ w, const float* __restrict__ b,
+                                                          const float* __restrict__ init,
+                                                          const float* __restrict__ dfin, E* __restrict__ du,
+                                                          float* __restrict__ part, Seqs sq, int D)
+{
+    constexpr int V = Grp<E>::V;
+    const int grp = blockIdx.y * BWD_THREADS + threadIdx.x;
+    if (grp * V >= D) return;
+    const int c0 = grp * V;
+    const int run = blockIdx.x;
+    const int r0 = run * BWD_RUN, r1 = min(r0 + BWD_RUN, sq.S);
+
+    float wt[V][4], bias[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        const f32x4 t = *reinterpret_cast<const f32x4*>(w + (size_t)(c0 + v) * 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wt[v][j] = t[j];
+        bias[v] = (b != nullptr) ? b[c0 + v] : 0.0f;
+    }
+    float aw[V][4], ab[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        ab[v] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) aw[v][j] = 0.0f;
+    }
+
+    for (int n = sq.find(r0); n < sq.n_seq; ++n) {
+        int s0, s1;
+        sq.range(n, s0, s1);
+        if (s0 >= r1) break;
+        if (s1 <= r0) continue;
+        const int a = max(r0, s0), e = min(r1 + 3, s1 + 3);
+        // x_{a-1}, x_{a-2}, x_{a-3}: rows of the sequence or its initial state
+        float x1[V], x2[V], x3[V];
+        auto xrow = [&](int s, float* x) {
+            if (s >= s0) {
+                Grp<E>::load(u + (size_t)s * D + c0, x);
+            } else if (init != nullptr) {
+                const float* p = init + ((size_t)n * 3 + (3 + s - s0)) * D + c0;
+#pragma unroll
+                for (int v = 0; v < V; ++v) x[v] = p[v];
+            } else {
+#pragma unroll
+                for (int v = 0; v < V; ++v) x[v] = 0.0f;
+            }
+        };
+        xrow(a - 1, x1);
+        xrow(a - 2, x2);
+        xrow(a - 3, x3);
+        float p1[V], p2[V], p3[V];  // dpre_{tau-1}, dpre_{tau-2}, dpre_{tau-3}
+#pragma unroll
+        for (int v = 0; v < V; ++v) p1[v] = p2[v] = p3[v] = 0.0f;
+        for (int tau = a; tau < e; ++tau) {
+            float p0[V];
+            if (tau < s1) {
+                float xu[V], g[V];
+                Grp<E>::load(u + (size_t)tau * D + c0, xu);
+                Grp<E>::load(dy + (size_t)tau * D + c0, g);
+                const bool own = tau < r1;
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    const float pre = bias[v] + wt[v][0] * x3[v] + wt[v][1] * x2[v] + wt[v][2] * x1[v] + wt[v][3] * xu[v];
+                    p0[v] = g[v] * dsilu_f(pre);
+                    if (own) {
+                        aw[v][0] = fmaf(p0[v], x3[v], aw[v][0]);
+                        aw[v][1] = fmaf(p0[v], x2[v], aw[v][1]);
+                        aw[v][2] = fmaf(p0[v], x1[v], aw[v][2]);
+                        aw[v][3] = fmaf(p0[v], xu[v], aw[v][3]);
+                        ab[v] += p0[v];
+                    }
+                    x3[v] = x2[v];
+                    x2[v] = x1[v];
+                    x1[v] = xu[v];
+                }
+            } else {
+#pragma unroll
+                for (int v = 0; v < V; ++v) p0[v] = 0.0f;
+            }
+            // du of row tau - 3, complete now
+            const int s = tau - 3;
+            if (s >= a && s < min(r1, s1)) {
+                const int k = s - (s1 - 3);
+                float o[V];
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    o[v] = wt[v][3] * p3[v] + wt[v][2] * p2[v] + wt[v][1] * p1[v] + wt[v][0] * p0[v];
+                    if (dfin != nullptr && k >= 0) o[v] += dfin[((size_t)n * 3 + k) * D + c0 + v];
+                }
+                Grp<E>::store(du + (size_t)s * D + c0, o);
+            }
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                p3[v] = p2[v];
+                p2[v] = p1[v];
+                p1[v] = p0[v];
+            }
+        }
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) part[((size_t)run * 5 + j) * D + c0 + v] = aw[v][j];
+        part[((size_t)run * 5 + 4) * D + c0 + v] = ab[v];
+    }
+}
+
+// The initial state's gradient of sequence n: d_init[i] = sum_{j <= i} w_j
+// dpre_{i-j} (rows inside the sequence) + d_final[i - L] when the final state
+// reaches back into the initial state (L < 3).
+template <typename E>
+__global__ __launch_bounds__(BWD_THREADS) void k_conv_bwd_init(const E* __restrict__ u, const E* __restrict__ dy,
+                                                               const float* __restrict__ w,
+                                                               const float* __restrict__ b,
+                                                               const float* __restrict__ init,
+                                                               const float* __restrict__ dfin,
+                                                               float* __restrict__ dinit, Seqs sq, int D)
+{
+    constexpr int V = Grp<E>::V;
+    const int grp = blockIdx.y * BWD_THREADS + threadIdx.x;
+    if (grp * V >= D) return;
+    const int c0 = grp * V;
+    const int n = blockIdx.x;
+    int s0, s1;
+    sq.range(n, s0, s1);
+    const int L = s1 - s0;
+    for (int v = 0; v < V; ++v) {
+        const int c = c0 + v;
+        float wt[4];
+        for (int j = 0; j < 4; ++j) wt[j] = w[(size_t)c * 4 + j];
+        const float bc = (b != nullptr) ? b[c] : 0.0f;
+        // x_{-3..2} of this channel and dpre_{0..2}
+        float x[6], p[3];
+        for (int i = 0; i < 3; ++i) x[i] = (init != nullptr) ? init[((size_t)n * 3 + i) * D + c] : 0.0f;
+        for (int t = 0; t < 3; ++t) {
+            float xu = 0.0f, g = 0.0f;
+            if (t < L) {
+                float row[V], grow[V];
+                Grp<E>::load(u + (size_t)(s0 + t) * D + c0, row);
+                Grp<E>::load(dy + (size_t)(s0 + t) * D + c0, grow);
+                xu = row[v];
+                g = grow[v];
+            }
+            x[3 + t] = xu;
+            const float pre = bc + wt[0] * x[t] + wt[1] * x[t + 1] + wt[2] * x[t + 2] + wt[3] * xu;
+            p[t] = (t < L) ? g * dsilu_f(pre) : 0.0f;
+        }
+        for (int i = 0; i < 3; ++i) {
+            float acc = 0.0f;
+            for (int j = 0; j <= i; ++j) acc += wt[j] * p[i - j];
+            if (dfin != nullptr && i - L >= 0) acc += dfin[((size_t)n * 3 + (i - L)) * D + c];
+            dinit[((size_t)n * 3 + i) * D + c] = acc;
+        }
+    }
+}
+
+// dw[c][j] and db[c]: the run partials added in run order.
+__global__ void k_conv_wsum(const float* __restrict__ part, float* __restrict__ dw, float* __restrict__ db,
+                            int n_runs, int D)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= 5 * D) return;
+    const int j = i / D, c = i - (i / D) * D;
+    float acc = 0.0f;
+    for (int r = 0; r < n_runs; ++r) acc += part[((size_t)r * 5 + j) * D + c];
+    if (j < 4) dw[(size_t)c * 4 + j] = acc;
+    else if (db != nullptr) db[c] = acc;
+}
+
+template <typename E>
+hipError_t run_conv_bwd(const void* u, const void* dy, const float* w, const float* b, const float* init,
+                        const float* dfin, void* du, float* dw, float* db, float* dinit, const int32_t* cu, int n_seq,
+                        int B, int T, int D, float* part, hipStream_t stream)
+{
+    Seqs sq;
+    sq.cu = cu;
+    sq.n_seq = n_seq;
+    sq.T = T;
+    sq.S = (cu != nullptr) ? T : B * T;
+    const int n_runs = (sq.S + BWD_RUN - 1) / BWD_RUN;
+    const int groups = D / Grp<E>::V;
+    const int gy = (groups + BWD_THREADS - 1) / BWD_THREADS;
+    hipLaunchKernelGGL(k_conv_bwd<E>, dim3(n_runs, gy), dim3(BWD_THREADS), 0, stream, reinterpret_cast<const E*>(u),
+                       reinterpret_cast<const E*>(dy), w, b, init, dfin, reinterpret_cast<E*>(du), part, sq, D);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (dinit != nullptr) {
+        hipLaunchKernelGGL(k_conv_bwd_init<E>, dim3(n_seq, gy), dim3(BWD_THREADS), 0, stream,
+                           reinterpret_cast<const E*>(u), reinterpret_cast<const E*>(dy), w, b, init, dfin, dinit, sq,
+                           D);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_conv_wsum, dim3((5 * D + 255) / 256), dim3(256), 0, stream, part, dw, db, n_runs, D);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+size_t conv_bwd_part_floats(int B, int T, int D, int packed)
+{
+    const long S = packed ? (long)T : (long)B * T;
+    return (size_t)((S + BWD_RUN - 1) / BWD_RUN) * 5 * D;
+}
+
+hipError_t launch_conv_bwd(int bf16, const void* u, const void* dy, const float* w, const float* b,
+                           const float* init_state, const float* d_final_state, void* du, float* dw, float* db,
+                           float* d_init_state, const int32_t* cu, int n_seq, int B, int T, int D, float* part,
+                           hipStream_t stream)
+{
+    if (bf16)
+        return run_conv_bwd<u16>(u, dy, w, b, init_state, d_final_state, du, dw, db, d_init_state, cu, n_seq, B, T,
+                                 D, part, stream);
+    return run_conv_bwd<float>(u, dy, w, b, init_state, d_final_state, du, dw, db, d_init_state, cu, n_seq, B, T, D,
+                               part, stream);
+}
 
 hipError_t launch_conv_fwd(int bf16, const void* u, const float* w, const float* b, const float* init_state,
                            float* final_state, void* y, const int32_t* cu, int n_seq, int B, int T, int D,

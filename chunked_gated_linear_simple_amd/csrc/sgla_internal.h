@@ -64,6 +64,14 @@ hipError_t launch_conv_decode(int bf16, const void* x, const float* w, const flo
 hipError_t launch_head_norm_gate(int bf16, const void* o, const void* g, const float* gamma, void* out, int B,
                                  int H, int T, int d_v, int n_tiers, float eps, hipStream_t stream);
 
+// Gradients of the conv prologue (sgla_conv.hip); part holds
+// conv_bwd_part_floats() floats.
+size_t conv_bwd_part_floats(int B, int T, int D, int packed);
+hipError_t launch_conv_bwd(int bf16, const void* u, const void* dy, const float* w, const float* b,
+                           const float* init_state, const float* d_final_state, void* du, float* dw, float* db,
+                           float* d_init_state, const int32_t* cu, int n_seq, int B, int T, int D, float* part,
+                           hipStream_t stream);
+
 // Gradients of the mixer epilogue (sgla_norm.hip); part holds
 // head_norm_gate_bwd_part_floats() floats when dgamma is wanted.
 size_t head_norm_gate_bwd_part_floats(int B, int H, int T, int d_v);

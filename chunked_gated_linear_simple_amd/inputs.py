@@ -112,14 +112,17 @@ def decode_token_inputs(seed: int, step: int, N: int, H: int, d_k: int, d_v: int
 
 
 STREAM_CONV = 2000  # conv prologue: u, w, b, init state, decode tokens 2004 + step
+STREAM_CONV_GRAD = 2500  # conv prologue gradients: dy, final states' gradient
 
 
 def conv_inputs(seed: int, shape, D: int, dtype: str, n_seq: int, w_std: float = 0.5,
-                b_std: float = 0.1, s0_std: float = 1.0, bias: bool = True, state: bool = True):
+                b_std: float = 0.1, s0_std: float = 1.0, bias: bool = True, state: bool = True,
+                with_grad: bool = False):
     """Seeded inputs of the conv prologue: u (shape, last axis D) in the storage
     dtype, taps w [D, 4], bias b [D] and initial conv states [n_seq, 3, D] in fp32
     (the states hold past inputs, so they are drawn like u and rounded to the
-    input dtype's values)."""
+    input dtype's values). with_grad adds dy ~ N(0, 1) like u (storage dtype)
+    and the final states' gradient dSf ~ N(0, 1) [n_seq, 3, D] fp32."""
     u = store(gaussian(seed, STREAM_CONV, tuple(shape)), dtype)
     w = gaussian(seed, STREAM_CONV + 1, (D, 4), w_std)
     b = gaussian(seed, STREAM_CONV + 2, (D,), b_std) if bias else None
@@ -127,7 +130,11 @@ def conv_inputs(seed: int, shape, D: int, dtype: str, n_seq: int, w_std: float =
     if state:
         s0 = gaussian(seed, STREAM_CONV + 3, (n_seq, 3, D), s0_std)
         s0 = widen(store(s0, dtype), dtype).astype(np.float32)
-    return {"u": u, "w": w, "b": b, "S0": s0, "dtype": dtype, "D": D, "N": n_seq}
+    out = {"u": u, "w": w, "b": b, "S0": s0, "dtype": dtype, "D": D, "N": n_seq}
+    if with_grad:
+        out["dy"] = store(gaussian(seed, STREAM_CONV_GRAD, tuple(shape)), dtype)
+        out["dSf"] = gaussian(seed, STREAM_CONV_GRAD + 1, (n_seq, 3, D))
+    return out
 
 
 STREAM_NORM = 3000  # mixer epilogue: o, g, gamma, dout

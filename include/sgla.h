@@ -269,6 +269,43 @@ sgla_status sgla_conv_fwd(const void* u, const float* w, const float* b,
                           sgla_dtype dtype, void* hip_stream);
 
 /*
+ * Bytes of device workspace sgla_conv_bwd needs: five fp32 rows of D per 32
+ * token rows (the per-run partial sums of the tap and bias gradients). T is
+ * the total token count when packed (B = 1).
+ */
+size_t sgla_conv_bwd_workspace_bytes(int B, int T, int D);
+
+/*
+ * Gradients of sgla_conv_fwd for a loss L with dL/dy = dy and
+ * dL/d(final_state) = d_final_state (same passages). Per sequence and
+ * channel, with x_s = u_s (s >= 0) or row 3 + s of the initial state and
+ * pre_t = b + sum_j w_j x_{t-3+j}:
+ *   dpre_t = dy_t silu'(pre_t),     silu'(x) = sigmoid(x) (1 + x (1 - sigmoid(x)))
+ *   dL/dx_s = sum_j w_j dpre_{s+3-j}  (within the sequence)
+ *             + d_final_state[s - (L - 3)]  for the last three inputs
+ *   du_s = dL/dx_s (s >= 0);  d_init_state[i] = dL/dx_{i-3}
+ *   dw[c][j] = sum over sequences and t of dpre_t x_{t-3+j};  db[c] = sum of dpre_t
+ * dw and db are summed in a fixed order (per-run partials, then a second
+ * kernel), so they are bitwise reproducible.
+ *
+ * u, w, b, init_state, cu_seqlens, n_seq, B, T, D, dtype: as for the forward.
+ * dy:            [B, T, D] (dtype), like y.
+ * d_final_state: [N, 3, D] fp32 or NULL = 0.
+ * du:            [B, T, D] (dtype); must not overlap u or dy.
+ * dw:            [D, 4] fp32, overwritten.   db: [D] fp32 or NULL (not computed).
+ * d_init_state:  [N, 3, D] fp32 or NULL (not written); must not overlap du,
+ *                init_state or d_final_state.
+ * workspace:     device buffer of at least sgla_conv_bwd_workspace_bytes(B,
+ *                T, D) bytes, 16-byte aligned, owned by the caller, clobbered.
+ * Errors: as sgla_conv_fwd, plus SGLA_ERR_WORKSPACE.
+ */
+sgla_status sgla_conv_bwd(const void* u, const float* w, const float* b, const float* init_state,
+                          const void* dy, const float* d_final_state, void* du, float* dw, float* db,
+                          float* d_init_state, const int32_t* cu_seqlens, int n_seq, int B, int T,
+                          int D, sgla_dtype dtype, void* workspace, size_t workspace_bytes,
+                          void* hip_stream);
+
+/*
  * One conv decode step for N sequences, in place on their conv states (the
  * per-sequence serving state of "Inference optimization on Trainium2",
  * "Constant serving state", next to the mixer state):

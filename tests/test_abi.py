@@ -368,3 +368,42 @@ def test_head_norm_gate_bwd_workspace_bytes(L):
     assert B.sgla_head_norm_gate_bwd_workspace_bytes(8, 16, 2048, 192) == 8 * 16 * 32 * 192 * 4
     assert B.sgla_head_norm_gate_bwd_workspace_bytes(1, 2, 65, 64) == 1 * 2 * 2 * 64 * 4
     assert B.sgla_head_norm_gate_bwd_workspace_bytes(0, 2, 65, 64) == 0
+
+
+def cbwd_args(**kw):
+    a = dict(u=P["u"], w=P["w"], b=P["b"], s0=P["s0"], dy=P["dO"], dsf=P["sf"], du=P["y"],
+             dw=P["dq"], db=P["db"] if "db" in P else P["dk"], ds0=P["ds0"], cu=None, n_seq=2, B=2,
+             T=256, D=3072, dt=B.SGLA_BF16, ws=P["ws"], wsb=16 * 5 * 3072 * 4)
+    a.update(kw)
+    return [a["u"], a["w"], a["b"], a["s0"], a["dy"], a["dsf"], a["du"], a["dw"], a["db"], a["ds0"],
+            a["cu"], a["n_seq"], a["B"], a["T"], a["D"], a["dt"], a["ws"], a["wsb"], None]
+
+
+CBWD_BAD = [
+    ("u null", dict(u=None), B.SGLA_ERR_INVALID_ARG),
+    ("dy null", dict(dy=None), B.SGLA_ERR_INVALID_ARG),
+    ("du null", dict(du=None), B.SGLA_ERR_INVALID_ARG),
+    ("dw null", dict(dw=None), B.SGLA_ERR_INVALID_ARG),
+    ("db misaligned", dict(db=P["dk"] + 4), B.SGLA_ERR_INVALID_ARG),
+    ("dense n_seq != B", dict(n_seq=3), B.SGLA_ERR_INVALID_ARG),
+    ("packed with B=2", dict(cu=P["cu"]), B.SGLA_ERR_INVALID_ARG),
+    ("D not mult 8", dict(D=100), B.SGLA_ERR_UNSUPPORTED),
+    ("workspace null", dict(ws=None), B.SGLA_ERR_WORKSPACE),
+    ("workspace small", dict(wsb=1024), B.SGLA_ERR_WORKSPACE),
+    ("du aliases u", dict(du=P["u"]), B.SGLA_ERR_INVALID_ARG),
+    ("du overlaps dy", dict(du=P["dO"] + 4096), B.SGLA_ERR_INVALID_ARG),
+    ("d_init aliases init", dict(ds0=P["s0"]), B.SGLA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", CBWD_BAD, ids=[x[0] for x in CBWD_BAD])
+def test_conv_bwd_rejects(L, name, kw, code):
+    assert L.sgla_conv_bwd(*cbwd_args(**kw)) == code
+    assert L.sgla_last_error().decode() != ""
+
+
+def test_conv_bwd_workspace_bytes(L):
+    # five fp32 rows of D per 32 token rows
+    assert B.sgla_conv_bwd_workspace_bytes(8, 2048, 3072) == 512 * 5 * 3072 * 4
+    assert B.sgla_conv_bwd_workspace_bytes(1, 33, 16) == 2 * 5 * 16 * 4
+    assert B.sgla_conv_bwd_workspace_bytes(0, 33, 16) == 0
