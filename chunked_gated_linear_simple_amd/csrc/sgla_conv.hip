@@ -442,7 +442,7 @@ hipError_t run_conv_fwd(const void* u, const float* w, const float* b, const flo
 // start) to three rows past the run's end (within the sequence), computing
 // dpre_tau and, three rows behind, du. dw and db of the run's rows go to
 // part[run][5][D]. k_conv_bwd_init writes the initial state's gradient (also
-// for empty sequences) and k_conv_wsum adds the run partials in order.
+// for empty sequences) and k_conv_wsum adds the run partials in a fixed order.
 constexpr int BWD_RUN = 32;
 constexpr int BWD_THREADS = 128;
 
@@ -508,12 +508,23 @@ __global__ __launch_bounds__(BWD_THREADS) void k_conv_bwd(const E* __restrict__ 
         float p1[V], p2[V], p3[V];  // dpre_{tau-1}, dpre_{tau-2}, dpre_{tau-3}
 #pragma unroll
         for (int v = 0; v < V; ++v) p1[v] = p2[v] = p3[v] = 0.0f;
+        // rows are loaded one step ahead of their use
+        const int e_in = min(e, s1);
+        u32x4 nu = {0u, 0u, 0u, 0u}, ng = {0u, 0u, 0u, 0u};
+        if (a < e_in) {
+            nu = *reinterpret_cast<const u32x4*>(u + (size_t)a * D + c0);
+            ng = *reinterpret_cast<const u32x4*>(dy + (size_t)a * D + c0);
+        }
         for (int tau = a; tau < e; ++tau) {
             float p0[V];
             if (tau < s1) {
                 float xu[V], g[V];
-                Grp<E>::load(u + (size_t)tau * D + c0, xu);
-                Grp<E>::load(dy + (size_t)tau * D + c0, g);
+                Grp<E>::unpack(nu, xu);
+                Grp<E>::unpack(ng, g);
+                if (tau + 1 < e_in) {
+                    nu = *reinterpret_cast<const u32x4*>(u + (size_t)(tau + 1) * D + c0);
+                    ng = *reinterpret_cast<const u32x4*>(dy + (size_t)(tau + 1) * D + c0);
+                }
                 const bool own = tau < r1;
 #pragma unroll
                 for (int v = 0; v < V; ++v) {
@@ -611,17 +622,27 @@ __global__ __launch_bounds__(BWD_THREADS) void k_conv_bwd_init(const E* __restri
     }
 }
 
-// dw[c][j] and db[c]: the run partials added in run order.
-__global__ void k_conv_wsum(const float* __restrict__ part, float* __restrict__ dw, float* __restrict__ db,
-                            int n_runs, int D)
+// dw[c][j] and db[c]: the run partials, split 16 ways (thread k adds runs
+// k, k + 16, ... in order) and the 16 sums added in order.
+__global__ __launch_bounds__(1024) void k_conv_wsum(const float* __restrict__ part, float* __restrict__ dw,
+                                                    float* __restrict__ db, int n_runs, int D)
 {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= 5 * D) return;
-    const int j = i / D, c = i - (i / D) * D;
+    __shared__ float red[16][64];
+    const int j = blockIdx.y;                  // 0..3 taps, 4 bias
+    const int cl = threadIdx.x & 63, k = threadIdx.x >> 6;
+    const int c = blockIdx.x * 64 + cl;
     float acc = 0.0f;
-    for (int r = 0; r < n_runs; ++r) acc += part[((size_t)r * 5 + j) * D + c];
-    if (j < 4) dw[(size_t)c * 4 + j] = acc;
-    else if (db != nullptr) db[c] = acc;
+    if (c < D)
+        for (int r = k; r < n_runs; r += 16) acc += part[((size_t)r * 5 + j) * D + c];
+    red[k][cl] = acc;
+    __syncthreads();
+    if (k == 0 && c < D) {
+        float x = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x += red[i][cl];
+        if (j < 4) dw[(size_t)c * 4 + j] = x;
+        else if (db != nullptr) db[c] = x;
+    }
 }
 
 template <typename E>
@@ -648,7 +669,7 @@ hipError_t run_conv_bwd(const void* u, const void* dy, const float* w, const flo
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_conv_wsum, dim3((5 * D + 255) / 256), dim3(256), 0, stream, part, dw, db, n_runs, D);
+    hipLaunchKernelGGL(k_conv_wsum, dim3((D + 63) / 64, 5), dim3(1024), 0, stream, part, dw, db, n_runs, D);
     return hipGetLastError();
 }
 
