@@ -446,6 +446,9 @@ hipError_t run_conv_fwd(const void* u, const float* w, const float* b, const flo
 constexpr int BWD_RUN = 32;
 constexpr int BWD_THREADS = 128;
 
+__device__ __forceinline__ float ld_elem(const u16* p, size_t i) { return __uint_as_float((uint32_t)p[i] << 16); }
+__device__ __forceinline__ float ld_elem(const float* p, size_t i) { return p[i]; }
+
 __device__ __forceinline__ float dsilu_f(float x)
 {
     const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
@@ -575,7 +578,7 @@ __global__ __launch_bounds__(BWD_THREADS) void k_conv_bwd(const E* __restrict__ 
 
 // The initial state's gradient of sequence n: d_init[i] = sum_{j <= i} w_j
 // dpre_{i-j} (rows inside the sequence) + d_final[i - L] when the final state
-// reaches back into the initial state (L < 3).
+// reaches back into the initial state (L < 3). One thread per channel.
 template <typename E>
 __global__ __launch_bounds__(BWD_THREADS) void k_conv_bwd_init(const E* __restrict__ u, const E* __restrict__ dy,
                                                                const float* __restrict__ w,
@@ -584,62 +587,52 @@ __global__ __launch_bounds__(BWD_THREADS) void k_conv_bwd_init(const E* __restri
                                                                const float* __restrict__ dfin,
                                                                float* __restrict__ dinit, Seqs sq, int D)
 {
-    constexpr int V = Grp<E>::V;
-    const int grp = blockIdx.y * BWD_THREADS + threadIdx.x;
-    if (grp * V >= D) return;
-    const int c0 = grp * V;
+    const int c = blockIdx.y * BWD_THREADS + threadIdx.x;
+    if (c >= D) return;
     const int n = blockIdx.x;
     int s0, s1;
     sq.range(n, s0, s1);
     const int L = s1 - s0;
-    for (int v = 0; v < V; ++v) {
-        const int c = c0 + v;
-        float wt[4];
-        for (int j = 0; j < 4; ++j) wt[j] = w[(size_t)c * 4 + j];
-        const float bc = (b != nullptr) ? b[c] : 0.0f;
-        // x_{-3..2} of this channel and dpre_{0..2}
-        float x[6], p[3];
-        for (int i = 0; i < 3; ++i) x[i] = (init != nullptr) ? init[((size_t)n * 3 + i) * D + c] : 0.0f;
-        for (int t = 0; t < 3; ++t) {
-            float xu = 0.0f, g = 0.0f;
-            if (t < L) {
-                float row[V], grow[V];
-                Grp<E>::load(u + (size_t)(s0 + t) * D + c0, row);
-                Grp<E>::load(dy + (size_t)(s0 + t) * D + c0, grow);
-                xu = row[v];
-                g = grow[v];
-            }
-            x[3 + t] = xu;
-            const float pre = bc + wt[0] * x[t] + wt[1] * x[t + 1] + wt[2] * x[t + 2] + wt[3] * xu;
-            p[t] = (t < L) ? g * dsilu_f(pre) : 0.0f;
+    const f32x4 wv = *reinterpret_cast<const f32x4*>(w + (size_t)c * 4);
+    const float bc = (b != nullptr) ? b[c] : 0.0f;
+    // x_{-3..2} of this channel and dpre_{0..2}
+    float x[6], p[3];
+    for (int i = 0; i < 3; ++i) x[i] = (init != nullptr) ? init[((size_t)n * 3 + i) * D + c] : 0.0f;
+    for (int t = 0; t < 3; ++t) {
+        float xu = 0.0f, g = 0.0f;
+        if (t < L) {
+            xu = ld_elem(u, (size_t)(s0 + t) * D + c);
+            g = ld_elem(dy, (size_t)(s0 + t) * D + c);
         }
-        for (int i = 0; i < 3; ++i) {
-            float acc = 0.0f;
-            for (int j = 0; j <= i; ++j) acc += wt[j] * p[i - j];
-            if (dfin != nullptr && i - L >= 0) acc += dfin[((size_t)n * 3 + (i - L)) * D + c];
-            dinit[((size_t)n * 3 + i) * D + c] = acc;
-        }
+        x[3 + t] = xu;
+        const float pre = bc + wv[0] * x[t] + wv[1] * x[t + 1] + wv[2] * x[t + 2] + wv[3] * xu;
+        p[t] = (t < L) ? g * dsilu_f(pre) : 0.0f;
+    }
+    for (int i = 0; i < 3; ++i) {
+        float acc = 0.0f;
+        for (int j = 0; j <= i; ++j) acc += wv[j] * p[i - j];
+        if (dfin != nullptr && i - L >= 0) acc += dfin[((size_t)n * 3 + (i - L)) * D + c];
+        dinit[((size_t)n * 3 + i) * D + c] = acc;
     }
 }
 
-// dw[c][j] and db[c]: the run partials, split 16 ways (thread k adds runs
-// k, k + 16, ... in order) and the 16 sums added in order.
+// dw[c][j] and db[c]: the run partials, split 64 ways (thread k of a block of
+// 16 channels adds runs k, k + 64, ... in order) and the 64 sums added in order.
 __global__ __launch_bounds__(1024) void k_conv_wsum(const float* __restrict__ part, float* __restrict__ dw,
                                                     float* __restrict__ db, int n_runs, int D)
 {
-    __shared__ float red[16][64];
+    __shared__ float red[64][16];
     const int j = blockIdx.y;                  // 0..3 taps, 4 bias
-    const int cl = threadIdx.x & 63, k = threadIdx.x >> 6;
-    const int c = blockIdx.x * 64 + cl;
+    const int cl = threadIdx.x & 15, k = threadIdx.x >> 4;
+    const int c = blockIdx.x * 16 + cl;
     float acc = 0.0f;
     if (c < D)
-        for (int r = k; r < n_runs; r += 16) acc += part[((size_t)r * 5 + j) * D + c];
+        for (int r = k; r < n_runs; r += 64) acc += part[((size_t)r * 5 + j) * D + c];
     red[k][cl] = acc;
     __syncthreads();
     if (k == 0 && c < D) {
         float x = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) x += red[i][cl];
+        for (int i = 0; i < 64; ++i) x += red[i][cl];
         if (j < 4) dw[(size_t)c * 4 + j] = x;
         else if (db != nullptr) db[c] = x;
     }
@@ -663,13 +656,14 @@ hipError_t run_conv_bwd(const void* u, const void* dy, const float* w, const flo
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (dinit != nullptr) {
-        hipLaunchKernelGGL(k_conv_bwd_init<E>, dim3(n_seq, gy), dim3(BWD_THREADS), 0, stream,
+        hipLaunchKernelGGL(k_conv_bwd_init<E>, dim3(n_seq, (D + BWD_THREADS - 1) / BWD_THREADS), dim3(BWD_THREADS), 0,
+                           stream,
                            reinterpret_cast<const E*>(u), reinterpret_cast<const E*>(dy), w, b, init, dfin, dinit, sq,
                            D);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_conv_wsum, dim3((D + 63) / 64, 5), dim3(1024), 0, stream, part, dw, db, n_runs, D);
+    hipLaunchKernelGGL(k_conv_wsum, dim3((D + 15) / 16, 5), dim3(1024), 0, stream, part, dw, db, n_runs, D);
     return hipGetLastError();
 }
 

@@ -354,19 +354,19 @@ __global__ __launch_bounds__(NORM_THREADS) void k_head_norm_gate_bwd(
 }
 
 // dgamma[tier][c] = sum over b, the tier's heads and the token blocks, in
-// that fixed order split 16 ways: thread (k, c) sums entries k, k + 16, ...;
-// then the 16 sums are added in order.
+// that fixed order split 64 ways: thread (k, c) of a block of 16 channels sums
+// entries k, k + 64, ...; then the 64 sums are added in order.
 __global__ __launch_bounds__(1024) void k_dgamma_sum(const float* __restrict__ part, float* __restrict__ dgamma,
                                                      int B, int H, int nTB, int d_v, int per_tier)
 {
-    __shared__ float red[16][64];
+    __shared__ float red[64][16];
     const int tier = blockIdx.x;
-    const int cl = threadIdx.x & 63, k = threadIdx.x >> 6;
-    const int c = blockIdx.y * 64 + cl;
+    const int cl = threadIdx.x & 15, k = threadIdx.x >> 4;
+    const int c = blockIdx.y * 16 + cl;
     const int n_ent = B * per_tier * nTB;
     float t = 0.0f;
     if (c < d_v) {
-        for (int e = k; e < n_ent; e += 16) {
+        for (int e = k; e < n_ent; e += 64) {
             const int bb = e / (per_tier * nTB);
             const int rem = e - bb * per_tier * nTB;
             const int hh = tier * per_tier + rem / nTB;
@@ -378,8 +378,7 @@ __global__ __launch_bounds__(1024) void k_dgamma_sum(const float* __restrict__ p
     __syncthreads();
     if (k == 0 && c < d_v) {
         float x = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) x += red[i][cl];
+        for (int i = 0; i < 64; ++i) x += red[i][cl];
         dgamma[(size_t)tier * d_v + c] = x;
     }
 }
@@ -399,7 +398,7 @@ hipError_t run_norm_bwd(const void* o, const void* g, const float* gamma, const 
                            part, H, T, d_v, H / n_tiers, inv_dv, eps);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(k_dgamma_sum, dim3(n_tiers, (d_v + 63) / 64), dim3(1024), 0, stream, part, dgamma, B, H,
+        hipLaunchKernelGGL(k_dgamma_sum, dim3(n_tiers, (d_v + 15) / 16), dim3(1024), 0, stream, part, dgamma, B, H,
                            nTB, d_v, H / n_tiers);
     } else {
         hipLaunchKernelGGL((k_head_norm_gate_bwd<E, NC, FULL, GAMMA, false>), grid, dim3(NORM_THREADS), 0, stream,
