@@ -437,7 +437,7 @@ hipError_t run_conv_fwd(const void* u, const float* w, const float* b, const flo
 //   du_s   = w_3 dpre_s + w_2 dpre_{s+1} + w_1 dpre_{s+2} + w_0 dpre_{s+3}
 //            (dpre = 0 past the sequence) + d_final[s - (L - 3)] for s >= L - 3
 //   dw_j   = sum_t dpre_t x_{t-3+j},  db = sum_t dpre_t
-// k_conv_bwd: a thread owns one channel group and a run of BWD_RUN rows; for
+// k_conv_bwd: a thread owns four channels and a run of BWD_RUN rows; for
 // each sequence meeting the run it walks tau from max(run start, sequence
 // start) to three rows past the run's end (within the sequence), computing
 // dpre_tau and, three rows behind, du. dw and db of the run's rows go to
@@ -445,6 +445,38 @@ hipError_t run_conv_fwd(const void* u, const float* w, const float* b, const flo
 // for empty sequences) and k_conv_wsum adds the run partials in a fixed order.
 constexpr int BWD_RUN = 32;
 constexpr int BWD_THREADS = 128;
+
+// Four channels per access for the backward (8 bytes of bf16, 16 of fp32),
+// so that a thread's windows fit a register budget of four or more waves per SIMD.
+template <typename E> struct Q4;
+template <> struct Q4<u16> {
+    static constexpr int V = 4;
+    typedef uint2 Raw;
+    static __device__ __forceinline__ Raw ld(const u16* p) { return *reinterpret_cast<const uint2*>(p); }
+    static __device__ __forceinline__ Raw zero() { return uint2{0u, 0u}; }
+    static __device__ __forceinline__ void unpack(Raw r, float* x)
+    {
+        x[0] = __uint_as_float(r.x << 16);
+        x[1] = __uint_as_float(r.x & 0xffff0000u);
+        x[2] = __uint_as_float(r.y << 16);
+        x[3] = __uint_as_float(r.y & 0xffff0000u);
+    }
+    static __device__ __forceinline__ void store(u16* p, const float* y)
+    {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 lo = {static_cast<__bf16>(y[0]), static_cast<__bf16>(y[1])};
+        const bf16x2 hi = {static_cast<__bf16>(y[2]), static_cast<__bf16>(y[3])};
+        *reinterpret_cast<uint2*>(p) = uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+    }
+};
+template <> struct Q4<float> {
+    static constexpr int V = 4;
+    typedef u32x4 Raw;
+    static __device__ __forceinline__ Raw ld(const float* p) { return *reinterpret_cast<const u32x4*>(p); }
+    static __device__ __forceinline__ Raw zero() { return u32x4{0u, 0u, 0u, 0u}; }
+    static __device__ __forceinline__ void unpack(Raw r, float* x) { Grp<float>::unpack(r, x); }
+    static __device__ __forceinline__ void store(float* p, const float* y) { Grp<float>::store(p, y); }
+};
 
 __device__ __forceinline__ float ld_elem(const u16* p, size_t i) { return __uint_as_float((uint32_t)p[i] << 16); }
 __device__ __forceinline__ float ld_elem(const float* p, size_t i) { return p[i]; }
@@ -462,7 +494,8 @@ __global__ __launch_bounds__(BWD_THREADS) void k_conv_bwd(const E* __restrict__ 
                                                           const float* __restrict__ dfin, E* __restrict__ du,
                                                           float* __restrict__ part, Seqs sq, int D)
 {
-    constexpr int V = Grp<E>::V;
+    typedef Q4<E> G;
+    constexpr int V = G::V;
     const int grp = blockIdx.y * BWD_THREADS + threadIdx.x;
     if (grp * V >= D) return;
     const int c0 = grp * V;
@@ -495,7 +528,7 @@ __global__ __launch_bounds__(BWD_THREADS) void k_conv_bwd(const E* __restrict__ 
         float x1[V], x2[V], x3[V];
         auto xrow = [&](int s, float* x) {
             if (s >= s0) {
-                Grp<E>::load(u + (size_t)s * D + c0, x);
+                G::unpack(G::ld(u + (size_t)s * D + c0), x);
             } else if (init != nullptr) {
                 const float* p = init + ((size_t)n * 3 + (3 + s - s0)) * D + c0;
 #pragma unroll
@@ -513,20 +546,20 @@ __global__ __launch_bounds__(BWD_THREADS) void k_conv_bwd(const E* __restrict__ 
         for (int v = 0; v < V; ++v) p1[v] = p2[v] = p3[v] = 0.0f;
         // rows are loaded one step ahead of their use
         const int e_in = min(e, s1);
-        u32x4 nu = {0u, 0u, 0u, 0u}, ng = {0u, 0u, 0u, 0u};
+        typename G::Raw nu = G::zero(), ng = G::zero();
         if (a < e_in) {
-            nu = *reinterpret_cast<const u32x4*>(u + (size_t)a * D + c0);
-            ng = *reinterpret_cast<const u32x4*>(dy + (size_t)a * D + c0);
+            nu = G::ld(u + (size_t)a * D + c0);
+            ng = G::ld(dy + (size_t)a * D + c0);
         }
         for (int tau = a; tau < e; ++tau) {
             float p0[V];
             if (tau < s1) {
                 float xu[V], g[V];
-                Grp<E>::unpack(nu, xu);
-                Grp<E>::unpack(ng, g);
+                G::unpack(nu, xu);
+                G::unpack(ng, g);
                 if (tau + 1 < e_in) {
-                    nu = *reinterpret_cast<const u32x4*>(u + (size_t)(tau + 1) * D + c0);
-                    ng = *reinterpret_cast<const u32x4*>(dy + (size_t)(tau + 1) * D + c0);
+                    nu = G::ld(u + (size_t)(tau + 1) * D + c0);
+                    ng = G::ld(dy + (size_t)(tau + 1) * D + c0);
                 }
                 const bool own = tau < r1;
 #pragma unroll
@@ -558,7 +591,7 @@ __global__ __launch_bounds__(BWD_THREADS) void k_conv_bwd(const E* __restrict__ 
                     o[v] = wt[v][3] * p3[v] + wt[v][2] * p2[v] + wt[v][1] * p1[v] + wt[v][0] * p0[v];
                     if (dfin != nullptr && k >= 0) o[v] += dfin[((size_t)n * 3 + k) * D + c0 + v];
                 }
-                Grp<E>::store(du + (size_t)s * D + c0, o);
+                G::store(du + (size_t)s * D + c0, o);
             }
 #pragma unroll
             for (int v = 0; v < V; ++v) {
@@ -649,7 +682,7 @@ hipError_t run_conv_bwd(const void* u, const void* dy, const float* w, const flo
     sq.T = T;
     sq.S = (cu != nullptr) ? T : B * T;
     const int n_runs = (sq.S + BWD_RUN - 1) / BWD_RUN;
-    const int groups = D / Grp<E>::V;
+    const int groups = D / Q4<E>::V;
     const int gy = (groups + BWD_THREADS - 1) / BWD_THREADS;
     hipLaunchKernelGGL(k_conv_bwd<E>, dim3(n_runs, gy), dim3(BWD_THREADS), 0, stream, reinterpret_cast<const E*>(u),
                        reinterpret_cast<const E*>(dy), w, b, init, dfin, reinterpret_cast<E*>(du), part, sq, D);
