@@ -56,6 +56,12 @@ def lib() -> ctypes.CDLL:
         L.sgla_chunk_fwd_segmented.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i,
                                                _i, _i, _i, _i, _i, _vp, ctypes.c_size_t, _vp]
         L.sgla_chunk_fwd_segmented.restype = _i
+        L.sgla_chunk_bwd_segmented_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
+        L.sgla_chunk_bwd_segmented_workspace_bytes.restype = ctypes.c_size_t
+        L.sgla_chunk_bwd_segmented.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                               _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp,
+                                               ctypes.c_size_t, _vp]
+        L.sgla_chunk_bwd_segmented.restype = _i
         L.sgla_chunk_bwd_workspace_bytes.argtypes = [_i, _i, _i]
         L.sgla_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.sgla_chunk_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -207,6 +213,48 @@ def sgla_chunk_fwd_segmented(q, k, v, lam, a=None, init_state=None, final_state=
                                           _ptr(workspace), workspace.numel() * workspace.element_size(),
                                           _stream(dev)))
     return o, final_state
+
+
+def sgla_chunk_bwd_segmented_workspace_bytes(B: int, H: int, d_k: int, d_v: int,
+                                              n_segments: int) -> int:
+    return int(lib().sgla_chunk_bwd_segmented_workspace_bytes(int(B), int(H), int(d_k), int(d_v),
+                                                              int(n_segments)))
+
+
+def sgla_chunk_bwd_segmented(q, k, v, dO, lam, a=None, init_state=None, d_final_state=None,
+                             n_segments: int = 2, chunk: int = 128, want_d_init: bool = False,
+                             dq=None, dk=None, dv=None, da=None, d_init_state=None, workspace=None):
+    """Segment-parallel backward of dense sequences. Returns (dq, dk, dv, da,
+    d_init_state)."""
+    dev = q.device
+    B, H, T, d_k, d_v, _ = _geometry(q, v, None)
+    _need(q, "q", device=dev)
+    _need(k, "k", q.dtype, dev, q.shape)
+    _need(v, "v", q.dtype, dev, (B, H, T, d_v))
+    _need(dO, "dO", q.dtype, dev, (B, H, T, d_v))
+    _need(lam, "lambda", torch.float32, dev, (H,))
+    _need(a, "a", torch.float32, dev, (H, d_k))
+    _need(init_state, "init_state", torch.float32, dev, (B, H, d_k, d_v))
+    _need(d_final_state, "d_final_state", torch.float32, dev, (B, H, d_k, d_v))
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    da = torch.empty((H, d_k), dtype=torch.float32, device=dev) if da is None else da
+    if d_init_state is None and want_d_init:
+        d_init_state = torch.empty((B, H, d_k, d_v), dtype=torch.float32, device=dev)
+    _need(d_init_state, "d_init_state", torch.float32, dev, (B, H, d_k, d_v))
+    nbytes = sgla_chunk_bwd_segmented_workspace_bytes(B, H, d_k, d_v, n_segments)
+    if workspace is None:
+        workspace = torch.empty((max(nbytes, 16) + 3) // 4, dtype=torch.float32, device=dev)
+    _need(workspace, "workspace", device=dev)
+    _check(lib().sgla_chunk_bwd_segmented(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lam), _ptr(a),
+                                          _ptr(init_state), _ptr(d_final_state), _ptr(dq), _ptr(dk),
+                                          _ptr(dv), _ptr(da), _ptr(d_init_state), B, H, T, d_k, d_v,
+                                          int(chunk), _dtype_code(q), int(n_segments),
+                                          _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(),
+                                          _stream(dev)))
+    return dq, dk, dv, da, d_init_state
 
 
 def sgla_chunk_bwd_workspace_bytes(N: int, H: int, d_k: int) -> int:

@@ -210,6 +210,72 @@ sgla_status sgla_chunk_fwd_segmented(const void* q, const void* k, const void* v
     return ok();
 }
 
+size_t sgla_chunk_bwd_segmented_workspace_bytes(int B, int H, int d_k, int d_v, int n_segments)
+{
+    if (B <= 0 || H <= 0 || d_k <= 0 || d_v <= 0 || n_segments <= 0) return 0;
+    const size_t units = (size_t)B * n_segments * H;
+    return (4 * units * d_k * d_v + units * d_k) * sizeof(float);
+}
+
+sgla_status sgla_chunk_bwd_segmented(const void* q, const void* k, const void* v, const void* dO,
+                                     const float* lambda, const float* a, const float* init_state,
+                                     const float* d_final_state, void* dq, void* dk, void* dv, float* da,
+                                     float* d_init_state, int B, int H, int T, int d_k, int d_v, int chunk,
+                                     sgla_dtype dtype, int n_segments, void* workspace, size_t workspace_bytes,
+                                     void* hip_stream)
+{
+    sgla::ChunkProblem p;
+    sgla_status st = check_chunk(q, k, v, lambda, a, nullptr, 0, B, H, T, d_k, d_v, chunk, dtype, &p);
+    if (st != SGLA_OK) return st;
+    if (dtype != SGLA_BF16)
+        return fail(SGLA_ERR_UNSUPPORTED, "the segmented backward needs SGLA_BF16");
+    if (n_segments <= 0) return fail(SGLA_ERR_INVALID_ARG, "n_segments must be positive, got %d", n_segments);
+    REQUIRE_PTR(dO);
+    REQUIRE_PTR(dq);
+    REQUIRE_PTR(dk);
+    REQUIRE_PTR(dv);
+    REQUIRE_PTR(da);
+    OPTIONAL_PTR(init_state);
+    OPTIONAL_PTR(d_final_state);
+    OPTIONAL_PTR(d_init_state);
+    const size_t need = sgla_chunk_bwd_segmented_workspace_bytes(B, H, d_k, d_v, n_segments);
+    if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
+        return fail(SGLA_ERR_WORKSPACE, "workspace needs %zu bytes, 16-byte aligned (got %zu at %p)",
+                    need, workspace_bytes, workspace);
+    const size_t nqk = (size_t)B * H * T * d_k * 2, nvo = (size_t)B * H * T * d_v * 2;
+    const void* ins[4] = {q, k, v, dO};
+    const size_t insz[4] = {nqk, nqk, nvo, nvo};
+    void* outs[3] = {dq, dk, dv};
+    const size_t outsz[3] = {nqk, nqk, nvo};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 4; ++j)
+            if (overlaps(outs[i], outsz[i], ins[j], insz[j]))
+                return fail(SGLA_ERR_INVALID_ARG, "dq, dk and dv must not alias q, k, v or dO");
+        for (int j = 0; j < i; ++j)
+            if (overlaps(outs[i], outsz[i], outs[j], outsz[j]))
+                return fail(SGLA_ERR_INVALID_ARG, "dq, dk and dv must not overlap each other");
+    }
+    const int tiles = (T + 63) / 64;
+    const int g = n_segments < tiles ? n_segments : tiles;
+    const int seg_len = ((tiles + g - 1) / g) * 64;
+    const int nseg = (T + seg_len - 1) / seg_len;
+    const hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+    float* ws = reinterpret_cast<float*>(workspace);
+    const size_t arr4 = 4 * (size_t)B * n_segments * H * d_k * d_v;
+    hipError_t e;
+    if (nseg <= 1) {
+        e = sgla::launch_chunk_bwd(p, q, k, v, dO, init_state, d_final_state, dq, dk, dv, da, d_init_state,
+                                   ws + arr4, stream);
+    } else {
+        // the four state arrays are sized for nseg <= n_segments segments
+        const size_t arr = (size_t)B * nseg * H * d_k * d_v;
+        e = sgla::launch_bwd_bf16_segmented(p, q, k, v, dO, init_state, d_final_state, dq, dk, dv, da,
+                                            d_init_state, ws + 4 * arr, nseg, seg_len, ws, stream);
+    }
+    if (e != hipSuccess) return fail(SGLA_ERR_HIP, "chunk_bwd_segmented launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 size_t sgla_chunk_bwd_workspace_bytes(int N, int H, int d_k)
 {
     if (N <= 0 || H <= 0 || d_k <= 0) return 0;

@@ -63,6 +63,42 @@ __global__ void k_da_sum(const float* __restrict__ part, float* __restrict__ da,
     da[i] = s;
 }
 
+// The DV scan alone (units x value slices), for the segment states of the
+// segmented backward.
+template <int DKV>
+__global__ __launch_bounds__(NTHREADS_W) void k_bwd_dv(Args p)
+{
+    __shared__ __attribute__((aligned(16))) char smem[LayW<WDv<DKV>>::LDS];
+    const int b = blockIdx.x;
+    const int slice = (b >> 3) % p.nsl;
+    const int unit = ((b >> 3) / p.nsl) * 8 + (b & 7);
+    if (unit >= p.n_units) return;
+    body_wide<WDv<DKV>>(p, unit, slice, smem);
+}
+
+// Reverse scan of the state gradients over segments: with loc[n][g] the
+// gradient state leaving segment g at its front (segment nseg-1 from
+// d_final_state, the others from zero), the one entering segment g from the
+// back is in[n][nseg-2] = loc[n][nseg-1], in[n][g] = lam^L in[n][g+1] + loc[n][g+1].
+__global__ void k_seg_rscan(const float* __restrict__ loc, float* __restrict__ in,
+                            const float* __restrict__ lambda, int nseg, int H, int ssz4, int seg_len)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    const int nh = blockIdx.y;
+    if (i >= ssz4) return;
+    const int n = nh / H, h = nh - n * H;
+    const float fL = __builtin_amdgcn_exp2f((float)seg_len * log2f(lambda[h]));
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    auto at = [&](int g) -> size_t { return (((size_t)n * nseg + g) * H + h) * (size_t)ssz4 + i; };
+    f4 s = reinterpret_cast<const f4*>(loc)[at(nseg - 1)];
+    reinterpret_cast<f4*>(in)[at(nseg - 2)] = s;
+    for (int g = nseg - 3; g >= 0; --g) {
+        const f4 l = reinterpret_cast<const f4*>(loc)[at(g + 1)];
+        s = fL * s + l;
+        reinterpret_cast<f4*>(in)[at(g)] = s;
+    }
+}
+
 template <int DKV, int DKG>
 hipError_t run_bwd(const Args& av, const Args& aq, const Args& ak, hipStream_t stream)
 {
@@ -76,6 +112,109 @@ hipError_t run_bwd(const Args& av, const Args& aq, const Args& ak, hipStream_t s
 }
 
 }  // namespace scan
+
+// bf16 backward of dense sequences cut into nseg >= 2 segments (see
+// sgla_chunk_bwd_segmented). ws holds four [n_seq][nseg][H][d_k][d_v] arrays:
+// forward states leaving / entering segments, gradient states leaving /
+// entering segments; da_partial holds n_seq nseg H d_k floats. dv serves as
+// scratch for the provisional outputs of the state passes.
+hipError_t launch_bwd_bf16_segmented(const ChunkProblem& p, const void* q, const void* k, const void* v,
+                                     const void* dO, const float* init_state, const float* d_final_state,
+                                     void* dq, void* dk, void* dv, float* da, float* d_init_state,
+                                     float* da_partial, int nseg, int seg_len, float* ws, hipStream_t stream)
+{
+    const size_t ssz = (size_t)p.d_k * p.d_v;
+    const size_t arr = (size_t)p.n_seq * nseg * p.H * ssz;
+    float* f_loc = ws;
+    float* f_in = ws + arr;
+    float* g_loc = ws + 2 * arr;
+    float* g_in = ws + 3 * arr;
+    // 1. forward states entering segments 1 .. nseg-1
+    hipError_t e = launch_fwd_bf16_seg_states(p, q, k, v, init_state, dv, nseg, seg_len, f_loc, f_in, stream);
+    if (e != hipSuccess) return e;
+
+    typedef const uint16_t* cp;
+    scan::Args base{};
+    base.lambda = p.lambda;
+    base.a = p.a;
+    base.cu = nullptr;
+    base.H = p.H;
+    base.T = p.T;
+    base.nseg = nseg;
+    base.seg_len = seg_len;
+    scan::Args av = base;
+    av.q = reinterpret_cast<cp>(k);
+    av.k = reinterpret_cast<cp>(q);
+    av.v = reinterpret_cast<cp>(dO);
+    av.o = reinterpret_cast<uint16_t*>(dv);
+    av.dkr = p.d_k;
+    av.dvr = p.d_v;
+    av.nsl = (p.d_v + scan::DVS - 1) / scan::DVS;
+
+    // 2. gradient states leaving segments 1 .. nseg-1 at their fronts (the last
+    // from d_final_state, the others from zero), then their reverse scan
+    scan::Args a2 = av;
+    a2.s_init = d_final_state;
+    a2.s_final = nullptr;
+    a2.s_in_seg = nullptr;
+    a2.s_out_seg = g_loc;
+    a2.seg_first = 1;
+    a2.seg_count = nseg - 1;
+    a2.n_units = p.n_seq * (nseg - 1) * p.H;
+    {
+        const int grid = ((a2.n_units + 7) / 8) * 8 * a2.nsl;
+        if (p.d_k <= 32) hipLaunchKernelGGL(scan::k_bwd_dv<32>, dim3(grid), dim3(scan::NTHREADS_W), 0, stream, a2);
+        else hipLaunchKernelGGL(scan::k_bwd_dv<96>, dim3(grid), dim3(scan::NTHREADS_W), 0, stream, a2);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int ssz4 = (int)(ssz / 4);
+    hipLaunchKernelGGL(scan::k_seg_rscan, dim3((ssz4 + 255) / 256, p.n_seq * p.H), dim3(256), 0, stream, g_loc,
+                       g_in, p.lambda, nseg, p.H, ssz4, seg_len);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    // 3. every segment from its true states
+    av.s_init = d_final_state;
+    av.s_final = d_init_state;
+    av.s_in_seg = g_in;
+    av.s_out_seg = nullptr;
+    av.seg_first = 0;
+    av.seg_count = nseg;
+    av.n_units = p.n_seq * nseg * p.H;
+    scan::Args aq = av;
+    aq.q = reinterpret_cast<cp>(dO);
+    aq.k = reinterpret_cast<cp>(v);
+    aq.v = reinterpret_cast<cp>(k);
+    aq.x = reinterpret_cast<cp>(q);
+    aq.o = reinterpret_cast<uint16_t*>(dq);
+    aq.s_init = init_state;
+    aq.s_final = nullptr;
+    aq.s_in_seg = f_in;
+    aq.da_part = da_partial;
+    aq.dkr = p.d_v;
+    aq.dvr = p.d_k;
+    aq.nsl = 1;
+    scan::Args ak = aq;
+    ak.q = reinterpret_cast<cp>(v);
+    ak.k = reinterpret_cast<cp>(dO);
+    ak.v = reinterpret_cast<cp>(q);
+    ak.x = reinterpret_cast<cp>(k);
+    ak.o = reinterpret_cast<uint16_t*>(dk);
+    ak.s_init = d_final_state;
+    ak.s_in_seg = g_in;
+    ak.da_part = nullptr;
+    if (p.d_k <= 32) {
+        e = (p.d_v <= 96) ? scan::run_bwd<32, 96>(av, aq, ak, stream) : scan::run_bwd<32, 192>(av, aq, ak, stream);
+    } else {
+        e = (p.d_v <= 96) ? scan::run_bwd<96, 96>(av, aq, ak, stream) : scan::run_bwd<96, 192>(av, aq, ak, stream);
+    }
+    if (e != hipSuccess) return e;
+    const int nda = p.H * p.d_k;
+    hipLaunchKernelGGL(scan::k_da_sum, dim3((nda + 255) / 256), dim3(256), 0, stream, da_partial, da,
+                       p.n_seq * nseg, p.H, p.d_k);
+    return hipGetLastError();
+}
 
 // bf16 backward with d_k <= 96 and d_v <= 192.
 hipError_t launch_bwd_bf16(const ChunkProblem& p, const void* q, const void* k, const void* v,

@@ -90,15 +90,14 @@ static hipError_t run_fwd_any(const scan::Args& a, int d_k, hipStream_t stream)
     return scan::run_fwd<96>(a, stream);
 }
 
-// Segment-parallel bf16 forward of dense sequences (see sgla_chunk_fwd_segmented):
-// segments 0 .. nseg-2 from their provisional starts, the scan of the states,
-// then segments 1 .. nseg-1 from their true starts (rewriting their outputs).
-hipError_t launch_fwd_bf16_segmented(const ChunkProblem& p, const void* q, const void* k,
-                                     const void* v, const float* init_state, float* final_state,
-                                     void* o, int nseg, int seg_len, float* ws_loc, float* ws_in,
-                                     hipStream_t stream)
+// The states entering segments 1 .. nseg-1 of dense sequences (ws_in): the
+// forward over segments 0 .. nseg-2 (provisional outputs into o) keeping the
+// states they leave (ws_loc), then the scan of those states.
+hipError_t launch_fwd_bf16_seg_states(const ChunkProblem& p, const void* q, const void* k, const void* v,
+                                      const float* init_state, void* o, int nseg, int seg_len, float* ws_loc,
+                                      float* ws_in, hipStream_t stream)
 {
-    scan::Args a = fwd_args(p, q, k, v, init_state, final_state, o);
+    scan::Args a = fwd_args(p, q, k, v, init_state, nullptr, o);
     a.nseg = nseg;
     a.seg_len = seg_len;
     a.seg_first = 0;
@@ -111,8 +110,24 @@ hipError_t launch_fwd_bf16_segmented(const ChunkProblem& p, const void* q, const
     const int ssz4 = p.d_k * p.d_v / 4;
     hipLaunchKernelGGL(scan::k_seg_scan, dim3((ssz4 + 255) / 256, p.n_seq * p.H), dim3(256), 0, stream,
                        ws_loc, ws_in, p.lambda, p.n_seq, nseg, p.H, ssz4, seg_len);
-    e = hipGetLastError();
+    return hipGetLastError();
+}
+
+// Segment-parallel bf16 forward of dense sequences (see sgla_chunk_fwd_segmented):
+// segments 0 .. nseg-2 from their provisional starts, the scan of the states,
+// then segments 1 .. nseg-1 from their true starts (rewriting their outputs).
+hipError_t launch_fwd_bf16_segmented(const ChunkProblem& p, const void* q, const void* k,
+                                     const void* v, const float* init_state, float* final_state,
+                                     void* o, int nseg, int seg_len, float* ws_loc, float* ws_in,
+                                     hipStream_t stream)
+{
+    hipError_t e = launch_fwd_bf16_seg_states(p, q, k, v, init_state, o, nseg, seg_len, ws_loc, ws_in, stream);
     if (e != hipSuccess) return e;
+    scan::Args a = fwd_args(p, q, k, v, init_state, final_state, o);
+    a.nseg = nseg;
+    a.seg_len = seg_len;
+    a.seg_count = nseg - 1;
+    a.n_units = p.n_seq * (nseg - 1) * p.H;
     a.seg_first = 1;
     a.s_in_seg = ws_in;
     a.s_out_seg = nullptr;

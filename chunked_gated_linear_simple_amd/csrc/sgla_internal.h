@@ -36,6 +36,19 @@ hipError_t launch_fwd_bf16_segmented(const ChunkProblem& p, const void* q, const
                                      void* o, int nseg, int seg_len, float* ws_loc, float* ws_in,
                                      hipStream_t stream);
 
+// The forward states entering segments 1 .. nseg-1 (ws_in), with provisional
+// outputs of segments 0 .. nseg-2 written into o (sgla_fwd.hip).
+hipError_t launch_fwd_bf16_seg_states(const ChunkProblem& p, const void* q, const void* k, const void* v,
+                                      const float* init_state, void* o, int nseg, int seg_len, float* ws_loc,
+                                      float* ws_in, hipStream_t stream);
+
+// bf16 backward of dense sequences cut into nseg >= 2 segments (sgla_bwd.hip);
+// ws holds 4 n_seq nseg H d_k d_v floats, da_partial n_seq nseg H d_k.
+hipError_t launch_bwd_bf16_segmented(const ChunkProblem& p, const void* q, const void* k, const void* v,
+                                     const void* dO, const float* init_state, const float* d_final_state,
+                                     void* dq, void* dk, void* dv, float* da, float* d_init_state,
+                                     float* da_partial, int nseg, int seg_len, float* ws, hipStream_t stream);
+
 // bf16 backward, d_k <= 96, d_v <= 192: the DV/DQ/DK roles of sgla_bwd.hip.
 hipError_t launch_bwd_bf16(const ChunkProblem& p, const void* q, const void* k, const void* v,
                            const void* dO, const float* init_state, const float* d_final_state,

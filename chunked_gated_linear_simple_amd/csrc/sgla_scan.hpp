@@ -203,12 +203,14 @@ struct Args {
     float* s_final;          // [units][dkr][dvr] or NULL
     float* da_part;          // [units][dvr] (DA roles)
     int H, T, n_units, nsl, dkr, dvr;
-    // Segments (dense FWD only; nseg <= 1: whole sequences). Sequence n is cut
-    // into nseg segments of seg_len tokens (the last one shorter); a launch
-    // runs segments seg_first .. seg_first + seg_count - 1 of every sequence,
-    // unit = ((n seg_count) + i) H + h. Segment 0 enters with s_init and the
-    // last one leaves into s_final; the others enter with s_in_seg and leave
-    // into s_out_seg, both [n][nseg][H][dkr][dvr] (NULL: zero / not written).
+    // Segments (dense sequences only; nseg <= 1: whole sequences). Sequence n
+    // is cut into nseg segments of seg_len tokens (the last one shorter); a
+    // launch runs segments seg_first .. seg_first + seg_count - 1 of every
+    // sequence, unit = ((n seg_count) + i) H + h. The segment where the scan
+    // enters the sequence (0, or the last for a reverse scan) starts from
+    // s_init, the one where it leaves writes s_final; the others start from
+    // s_in_seg and write s_out_seg, both [n][nseg][H][state] (NULL: zero / not
+    // written).
     int nseg, seg_len, seg_first, seg_count;
     const float* s_in_seg;
     float* s_out_seg;
@@ -604,11 +606,15 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
     const size_t ssz = (size_t)dkr * dvr;
     const size_t shead = ((size_t)seq * H + h) * ssz;
     const size_t sseg = (((size_t)seq * max(p.nseg, 1) + g) * H + h) * ssz;
+    // a scan in time order enters the sequence at segment 0 and leaves it at
+    // the last one; a reverse scan enters at the last and leaves at segment 0
     const bool last_seg = p.nseg <= 1 || g == p.nseg - 1;
-    const float* s_in = (g == 0) ? (p.s_init != nullptr ? p.s_init + shead : nullptr)
-                                 : (p.s_in_seg != nullptr ? p.s_in_seg + sseg : nullptr);
-    float* s_out = last_seg ? (p.s_final != nullptr ? p.s_final + shead : nullptr)
-                            : (p.s_out_seg != nullptr ? p.s_out_seg + sseg : nullptr);
+    const bool enters_seq = R::REV ? last_seg : g == 0;
+    const bool leaves_seq = R::REV ? g == 0 : last_seg;
+    const float* s_in = enters_seq ? (p.s_init != nullptr ? p.s_init + shead : nullptr)
+                                   : (p.s_in_seg != nullptr ? p.s_in_seg + sseg : nullptr);
+    float* s_out = leaves_seq ? (p.s_final != nullptr ? p.s_final + shead : nullptr)
+                              : (p.s_out_seg != nullptr ? p.s_out_seg + sseg : nullptr);
 
     // Accumulator row 4 qg + r of 16-row block db holds state row srow(db, r)
     auto srow = [&](int db, int r) { return 32 * (db >> 1) + 8 * qg + 4 * (db & 1) + r; };

@@ -173,6 +173,51 @@ sgla_status sgla_chunk_fwd_segmented(const void* q, const void* k, const void* v
                                      size_t workspace_bytes, void* hip_stream);
 
 /*
+ * Bytes of device workspace sgla_chunk_bwd_segmented needs: four arrays of
+ * B * n_segments * H states of d_k * d_v fp32 and B * n_segments * H * d_k
+ * fp32 partial sums of da.
+ */
+size_t sgla_chunk_bwd_segmented_workspace_bytes(int B, int H, int d_k, int d_v, int n_segments);
+
+/*
+ * Segment-parallel chunked backward of long dense sequences: the gradients of
+ * sgla_chunk_fwd (same result as sgla_chunk_bwd up to rounding, da summed in
+ * a fixed order). Segments as for sgla_chunk_fwd_segmented. The dq scan needs
+ * the forward state entering each segment, and the dk and dv scans (which run
+ * from the back) need the state gradient G entering each segment from its
+ * end. Both follow from the affine maps of the runs, as in the forward
+ * ("Challenge 3: Backward-pass unrolling for a sequential recurrence": the
+ * state gradient flows back through every state update). Four steps on
+ * hip_stream:
+ *   1. the forward over segments 0 .. G-2 (provisional outputs into dv) and
+ *      the scan of their leaving states;
+ *   2. the dv scan over segments 1 .. G-1 from their ends (the last from
+ *      d_final_state, the others from zero; provisional outputs into dv),
+ *      keeping the G each leaves at its front;
+ *   3. the reverse scan of those: G entering segment g from its end is
+ *      lam^L (G entering g+1) + (G leaving g+1 from zero);
+ *   4. the full backward over every segment from its true states, which
+ *      writes dq, dk, dv, the da partial sums and d_init_state, then the
+ *      fixed-order sum of da.
+ *
+ * Arguments as for sgla_chunk_bwd, dense layout only (no cu_seqlens), plus:
+ * dtype:       SGLA_BF16 only (SGLA_ERR_UNSUPPORTED otherwise).
+ * n_segments:  segments per sequence requested, >= 1; 1 is sgla_chunk_bwd.
+ * workspace:   device buffer of at least
+ *              sgla_chunk_bwd_segmented_workspace_bytes(B, H, d_k, d_v,
+ *              n_segments) bytes, 16-byte aligned, owned by the caller, not
+ *              overlapping any other argument; clobbered.
+ * Errors: as sgla_chunk_bwd, plus SGLA_ERR_INVALID_ARG for n_segments < 1.
+ */
+sgla_status sgla_chunk_bwd_segmented(const void* q, const void* k, const void* v, const void* dO,
+                                     const float* lambda, const float* a,
+                                     const float* init_state, const float* d_final_state,
+                                     void* dq, void* dk, void* dv, float* da, float* d_init_state,
+                                     int B, int H, int T, int d_k, int d_v, int chunk,
+                                     sgla_dtype dtype, int n_segments, void* workspace,
+                                     size_t workspace_bytes, void* hip_stream);
+
+/*
  * Bytes of device workspace sgla_chunk_bwd needs for these sizes (the per
  * sequence-head partial sums of da). N is n_seq for packed input, else B.
  */

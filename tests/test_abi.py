@@ -407,3 +407,39 @@ def test_conv_bwd_workspace_bytes(L):
     assert B.sgla_conv_bwd_workspace_bytes(8, 2048, 3072) == 512 * 5 * 3072 * 4
     assert B.sgla_conv_bwd_workspace_bytes(1, 33, 16) == 2 * 5 * 16 * 4
     assert B.sgla_conv_bwd_workspace_bytes(0, 33, 16) == 0
+
+
+def segb_args(**kw):
+    nbytes = (4 * 2 * 4 * 16 * 96 * 192 + 2 * 4 * 16 * 96) * 4
+    a = dict(q=P["q"], k=P["k"], v=P["v"], dO=P["dO"], lam=P["lam"], a=P["a"], s0=P["s0"],
+             dsf=P["sf"], dq=P["dq"], dk=P["dk"], dv=P["dv"], da=P["da"], ds0=P["ds0"], B=2, H=16,
+             T=4096, d_k=96, d_v=192, chunk=128, dt=B.SGLA_BF16, nseg=4, ws=P["ws"], wsb=nbytes)
+    a.update(kw)
+    return [a["q"], a["k"], a["v"], a["dO"], a["lam"], a["a"], a["s0"], a["dsf"], a["dq"], a["dk"],
+            a["dv"], a["da"], a["ds0"], a["B"], a["H"], a["T"], a["d_k"], a["d_v"], a["chunk"],
+            a["dt"], a["nseg"], a["ws"], a["wsb"], None]
+
+
+SEGB_BAD = [
+    ("dO null", dict(dO=None), B.SGLA_ERR_INVALID_ARG),
+    ("da null", dict(da=None), B.SGLA_ERR_INVALID_ARG),
+    ("n_segments zero", dict(nseg=0), B.SGLA_ERR_INVALID_ARG),
+    ("f32", dict(dt=B.SGLA_F32, d_k=16, d_v=32, chunk=64), B.SGLA_ERR_UNSUPPORTED),
+    ("workspace null", dict(ws=None), B.SGLA_ERR_WORKSPACE),
+    ("workspace small", dict(wsb=1 << 20), B.SGLA_ERR_WORKSPACE),
+    ("dq aliases dO", dict(dq=P["dO"]), B.SGLA_ERR_INVALID_ARG),
+    ("dv overlaps dk", dict(dv=P["dk"] + 1024), B.SGLA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", SEGB_BAD, ids=[x[0] for x in SEGB_BAD])
+def test_chunk_bwd_segmented_rejects(L, name, kw, code):
+    assert L.sgla_chunk_bwd_segmented(*segb_args(**kw)) == code
+    assert L.sgla_last_error().decode() != ""
+
+
+def test_segmented_bwd_workspace_bytes(L):
+    # four state arrays and the da partial sums, B * n_segments * H units
+    u = 1 * 8 * 16
+    assert B.sgla_chunk_bwd_segmented_workspace_bytes(1, 16, 96, 192, 8) == (4 * u * 96 * 192 + u * 96) * 4
+    assert B.sgla_chunk_bwd_segmented_workspace_bytes(1, 16, 96, 192, 0) == 0

@@ -93,3 +93,72 @@ def test_segmented_fwd_long_sequence_sampled_heads():
     T = 32768
     inp = I.chunk_inputs(1, 16, T, 96, 192, "bf16", seed=95, a_std=0.1, s0_std=0.02)
     run_segmented_case(inp, schedule32(16, 1.0, 2048.0), 8, units=[(0, 0), (0, 15)])
+
+
+# ---------------------------------------------------------------- backward
+
+def run_segmented_bwd_case(inp, lam, n_segments, units=None):
+    from tests.parity_util import oracle_bwd_units
+    d = device_inputs(inp)
+    lam_d = to_dev(lam)
+    print(f"  segmented bwd B={inp['B']} H={inp['H']} T={inp['T']} n_segments={n_segments}",
+          flush=True)
+    dq, dk, dv, da, dS0 = Bd.sgla_chunk_bwd_segmented(d["q"], d["k"], d["v"], d["dO"], lam_d, d["a"],
+                                                      init_state=d["S0"], d_final_state=d["dSf"],
+                                                      n_segments=n_segments, want_d_init=True)
+    torch.cuda.synchronize()
+    units = units or [(n, h) for n in range(inp["B"]) for h in range(inp["H"])]
+    ref = oracle_bwd_units(inp, lam, units)
+    tol = TOL[inp["dtype"]]
+    for idx, (name, t) in enumerate((("dq", dq), ("dk", dk), ("dv", dv))):
+        th = to_host64(t)
+        assert_close(np.concatenate([th[n, h].ravel() for n, h in units]),
+                     np.concatenate([ref[u][idx].ravel() for u in units]), tol, name, store="bf16")
+    if len(units) == inp["B"] * inp["H"]:
+        da_ref = np.zeros_like(inp["a"], dtype=np.float64)
+        for u in units:
+            da_ref[u[1]] += ref[u][3]
+        assert_close(to_host64(da), da_ref, tol, "da")
+    dsh = to_host64(dS0)
+    assert_close(np.concatenate([dsh[n, h].ravel() for n, h in units]),
+                 np.concatenate([ref[u][4].ravel() for u in units]), tol, "d_init_state")
+    return (dq, dk, dv, da, dS0), d
+
+
+@pytest.mark.parametrize("T,n_segments", [(1000, 2), (1000, 3), (700, 5), (2048, 4)])
+def test_segmented_bwd_matches_oracle(T, n_segments):
+    """Ragged T, initial state, final-state gradient, a != 0, the 1..2048
+    schedule; every gradient against the oracle's token-by-token backward."""
+    inp = I.chunk_inputs(2, 4, T, 96, 192, "bf16", seed=600 + T + n_segments, a_std=0.1,
+                         s0_std=0.02, with_grad=True, dsf_std=0.02)
+    run_segmented_bwd_case(inp, schedule32(4, 1.0, 2048.0), n_segments)
+
+
+def test_segmented_bwd_agrees_with_single_pass():
+    """Against sgla_chunk_bwd on the same inputs (rounding apart); one segment
+    is the single pass, bit for bit."""
+    inp = I.chunk_inputs(1, 4, 1500, 96, 192, "bf16", seed=97, a_std=0.1, s0_std=0.02,
+                         with_grad=True, dsf_std=0.02)
+    lam = schedule32(4, 1.0, 2048.0)
+    seg, d = run_segmented_bwd_case(inp, lam, 3)
+    lam_d = to_dev(lam)
+    one = Bd.sgla_chunk_bwd(d["q"], d["k"], d["v"], d["dO"], lam_d, d["a"], init_state=d["S0"],
+                            d_final_state=d["dSf"], want_d_init=True)
+    one_s = Bd.sgla_chunk_bwd_segmented(d["q"], d["k"], d["v"], d["dO"], lam_d, d["a"],
+                                        init_state=d["S0"], d_final_state=d["dSf"], n_segments=1,
+                                        want_d_init=True)
+    torch.cuda.synchronize()
+    for x, y in zip(one, one_s):
+        assert torch.equal(x, y)
+    for name, x, y, st in zip(("dq", "dk", "dv", "da", "d_init_state"), seg, one,
+                              ("bf16", "bf16", "bf16", "f32", "f32")):
+        assert_close(to_host64(x).ravel(), to_host64(y).ravel(), TOL["bf16"], name + " vs single pass",
+                     store=st, ref_store=st)
+
+
+def test_segmented_bwd_long_sequence_sampled_heads():
+    """B = 1, H = 16, T = 16384 with eight segments; the oracle checks the
+    shortest- and the longest-memory heads."""
+    inp = I.chunk_inputs(1, 16, 16384, 96, 192, "bf16", seed=99, a_std=0.1, s0_std=0.02,
+                         with_grad=True, dsf_std=0.02)
+    run_segmented_bwd_case(inp, schedule32(16, 1.0, 2048.0), 8, units=[(0, 0), (0, 15)])
