@@ -17,7 +17,8 @@ Also measured in the same run and reported under "secondary" (same clock):
   varlen: 32 packed sequences, lengths log-uniform in [128, 32768] (one of
           32768), init states ~ N(0, 0.02), tokens/s = sum T / t
   long:   one sequence of T=32768 (B=1, H=16) with initial and final state,
-          single pass and segmented (9 segments joined by a state scan),
+          single pass and segmented (9 segments joined by a state scan), and
+          its backward, single pass and segmented (4 segments),
           tokens/s = 32768 / t
   norm:   the mixer epilogue (Head RMSNorm per decay tier, 4 tiers, + SiLU(g)
           gate) on a B=8 T=2048 forward's output: o and g in, out written,
@@ -398,9 +399,28 @@ def bench_long(args, T=32768, n_segments=9):
                                                         final_state=sf, o=o, n_segments=n_segments,
                                                         workspace=ws), steps, 2)
     bytes_ = H * T * HT_BYTES + 2 * H * STATE_BYTES
+    # the backward of the same sequence: single pass, and 4 segments (its last
+    # launch then runs 4 x 64 = 256 workgroups)
+    nsb = 4
+    dO = gen((1, H, T, DV), 604, dtype=torch.bfloat16)
+    dsf = gen((1, H, DK, DV), 605, 0.02)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    da = torch.empty((H, DK), device="cuda")
+    ds0 = torch.empty_like(s0)
+    wsb = torch.empty(Bd.sgla_chunk_bwd_segmented_workspace_bytes(1, H, DK, DV, nsb) // 4,
+                      dtype=torch.float32, device="cuda")
+    msb1, _ = timed(lambda i: Bd.sgla_chunk_bwd(q, k, v, dO, lam, a, init_state=s0,
+                                                d_final_state=dsf, dq=dq, dk=dk, dv=dv, da=da,
+                                                d_init_state=ds0), steps, 2)
+    msb, _ = timed(lambda i: Bd.sgla_chunk_bwd_segmented(q, k, v, dO, lam, a, init_state=s0,
+                                                         d_final_state=dsf, n_segments=nsb,
+                                                         dq=dq, dk=dk, dv=dv, da=da,
+                                                         d_init_state=ds0, workspace=wsb),
+                   steps, 2)
     return {"ms": ms, "ms_single_pass": ms1, "tokens": T, "tok_s": T / (ms * 1e-3),
             "tok_s_single_pass": T / (ms1 * 1e-3), "n_segments": n_segments, "bytes": bytes_,
-            "gbs": bytes_ / (ms * 1e-3) / 1e9}
+            "gbs": bytes_ / (ms * 1e-3) / 1e9,
+            "bwd_ms": msb, "bwd_ms_single_pass": msb1, "bwd_n_segments": nsb}
 
 
 def cpu_baseline(min_seconds=10.0, B=8, T=2048):
