@@ -63,40 +63,23 @@ __global__ void k_da_sum(const float* __restrict__ part, float* __restrict__ da,
     da[i] = s;
 }
 
-// The DV scan alone (units x value slices), for the segment states of the
-// segmented backward.
-template <int DKV>
-__global__ __launch_bounds__(NTHREADS_W) void k_bwd_dv(Args p)
+// The state passes of the segmented backward in one launch: the forward scan
+// over segments 0 .. nseg-2 (blocks [0, nf)) and the DV scan over segments
+// 1 .. nseg-1 (the blocks after), which are independent of each other. Each
+// role's blocks map to (unit, value slice) as in k_fwd.
+template <int DK>
+__global__ __launch_bounds__(NTHREADS_W) void k_seg_states(Args af, Args adv, int nf)
 {
-    __shared__ __attribute__((aligned(16))) char smem[LayW<WDv<DKV>>::LDS];
-    const int b = blockIdx.x;
+    constexpr int LDS = LayW<WFwd<DK>>::LDS > LayW<WDv<DK>>::LDS ? LayW<WFwd<DK>>::LDS : LayW<WDv<DK>>::LDS;
+    __shared__ __attribute__((aligned(16))) char smem[LDS];
+    const bool fwd = (int)blockIdx.x < nf;
+    const Args& p = fwd ? af : adv;
+    const int b = fwd ? (int)blockIdx.x : (int)blockIdx.x - nf;
     const int slice = (b >> 3) % p.nsl;
     const int unit = ((b >> 3) / p.nsl) * 8 + (b & 7);
     if (unit >= p.n_units) return;
-    body_wide<WDv<DKV>>(p, unit, slice, smem);
-}
-
-// Reverse scan of the state gradients over segments: with loc[n][g] the
-// gradient state leaving segment g at its front (segment nseg-1 from
-// d_final_state, the others from zero), the one entering segment g from the
-// back is in[n][nseg-2] = loc[n][nseg-1], in[n][g] = lam^L in[n][g+1] + loc[n][g+1].
-__global__ void k_seg_rscan(const float* __restrict__ loc, float* __restrict__ in,
-                            const float* __restrict__ lambda, int nseg, int H, int ssz4, int seg_len)
-{
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    const int nh = blockIdx.y;
-    if (i >= ssz4) return;
-    const int n = nh / H, h = nh - n * H;
-    const float fL = __builtin_amdgcn_exp2f((float)seg_len * log2f(lambda[h]));
-    typedef float f4 __attribute__((ext_vector_type(4)));
-    auto at = [&](int g) -> size_t { return (((size_t)n * nseg + g) * H + h) * (size_t)ssz4 + i; };
-    f4 s = reinterpret_cast<const f4*>(loc)[at(nseg - 1)];
-    reinterpret_cast<f4*>(in)[at(nseg - 2)] = s;
-    for (int g = nseg - 3; g >= 0; --g) {
-        const f4 l = reinterpret_cast<const f4*>(loc)[at(g + 1)];
-        s = fL * s + l;
-        reinterpret_cast<f4*>(in)[at(g)] = s;
-    }
+    if (fwd) body_wide<WFwd<DK>>(p, unit, slice, smem);
+    else body_wide<WDv<DK>>(p, unit, slice, smem);
 }
 
 template <int DKV, int DKG>
@@ -117,7 +100,8 @@ hipError_t run_bwd(const Args& av, const Args& aq, const Args& ak, hipStream_t s
 // sgla_chunk_bwd_segmented). ws holds four [n_seq][nseg][H][d_k][d_v] arrays:
 // forward states leaving / entering segments, gradient states leaving /
 // entering segments; da_partial holds n_seq nseg H d_k floats. dv serves as
-// scratch for the provisional outputs of the state passes.
+// scratch for the provisional outputs of the state passes, whose contents
+// step 3 replaces entirely.
 hipError_t launch_bwd_bf16_segmented(const ChunkProblem& p, const void* q, const void* k, const void* v,
                                      const void* dO, const float* init_state, const float* d_final_state,
                                      void* dq, void* dk, void* dv, float* da, float* d_init_state,
@@ -129,9 +113,6 @@ hipError_t launch_bwd_bf16_segmented(const ChunkProblem& p, const void* q, const
     float* f_in = ws + arr;
     float* g_loc = ws + 2 * arr;
     float* g_in = ws + 3 * arr;
-    // 1. forward states entering segments 1 .. nseg-1
-    hipError_t e = launch_fwd_bf16_seg_states(p, q, k, v, init_state, dv, nseg, seg_len, f_loc, f_in, stream);
-    if (e != hipSuccess) return e;
 
     typedef const uint16_t* cp;
     scan::Args base{};
@@ -142,33 +123,54 @@ hipError_t launch_bwd_bf16_segmented(const ChunkProblem& p, const void* q, const
     base.T = p.T;
     base.nseg = nseg;
     base.seg_len = seg_len;
+    base.nsl = (p.d_v + scan::DVS - 1) / scan::DVS;
+    base.dkr = p.d_k;
+    base.dvr = p.d_v;
+
+    // 1. in one launch: the forward over segments 0 .. nseg-2 (segment 0 from
+    // init_state, the rest from zero) keeping the states they leave, and the
+    // dv scan over segments 1 .. nseg-1 from their ends (the last from
+    // d_final_state, the rest from zero) keeping the gradient states they
+    // leave at their fronts; both write provisional outputs into dv
+    scan::Args af = base;
+    af.q = reinterpret_cast<cp>(q);
+    af.k = reinterpret_cast<cp>(k);
+    af.v = reinterpret_cast<cp>(v);
+    af.o = reinterpret_cast<uint16_t*>(dv);
+    af.s_init = init_state;
+    af.s_out_seg = f_loc;
+    af.seg_first = 0;
+    af.seg_count = nseg - 1;
+    af.n_units = p.n_seq * (nseg - 1) * p.H;
     scan::Args av = base;
     av.q = reinterpret_cast<cp>(k);
     av.k = reinterpret_cast<cp>(q);
     av.v = reinterpret_cast<cp>(dO);
     av.o = reinterpret_cast<uint16_t*>(dv);
-    av.dkr = p.d_k;
-    av.dvr = p.d_v;
-    av.nsl = (p.d_v + scan::DVS - 1) / scan::DVS;
-
-    // 2. gradient states leaving segments 1 .. nseg-1 at their fronts (the last
-    // from d_final_state, the others from zero), then their reverse scan
     scan::Args a2 = av;
     a2.s_init = d_final_state;
-    a2.s_final = nullptr;
-    a2.s_in_seg = nullptr;
     a2.s_out_seg = g_loc;
     a2.seg_first = 1;
     a2.seg_count = nseg - 1;
     a2.n_units = p.n_seq * (nseg - 1) * p.H;
-    {
-        const int grid = ((a2.n_units + 7) / 8) * 8 * a2.nsl;
-        if (p.d_k <= 32) hipLaunchKernelGGL(scan::k_bwd_dv<32>, dim3(grid), dim3(scan::NTHREADS_W), 0, stream, a2);
-        else hipLaunchKernelGGL(scan::k_bwd_dv<96>, dim3(grid), dim3(scan::NTHREADS_W), 0, stream, a2);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
+    const int nf = ((af.n_units + 7) / 8) * 8 * af.nsl;
+    const int nd = ((a2.n_units + 7) / 8) * 8 * a2.nsl;
+    if (p.d_k <= 32)
+        hipLaunchKernelGGL(scan::k_seg_states<32>, dim3(nf + nd), dim3(scan::NTHREADS_W), 0, stream, af, a2, nf);
+    else if (p.d_k <= 64)
+        hipLaunchKernelGGL(scan::k_seg_states<64>, dim3(nf + nd), dim3(scan::NTHREADS_W), 0, stream, af, a2, nf);
+    else
+        hipLaunchKernelGGL(scan::k_seg_states<96>, dim3(nf + nd), dim3(scan::NTHREADS_W), 0, stream, af, a2, nf);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    // 2. the forward scan of the leaving states and the reverse scan of the
+    // gradient states
     const int ssz4 = (int)(ssz / 4);
+    hipLaunchKernelGGL(scan::k_seg_scan, dim3((ssz4 + 255) / 256, p.n_seq * p.H), dim3(256), 0, stream, f_loc,
+                       f_in, p.lambda, p.n_seq, nseg, p.H, ssz4, seg_len);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(scan::k_seg_rscan, dim3((ssz4 + 255) / 256, p.n_seq * p.H), dim3(256), 0, stream, g_loc,
                        g_in, p.lambda, nseg, p.H, ssz4, seg_len);
     e = hipGetLastError();

@@ -795,6 +795,56 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
     }
 }
 
+// ----------------------------------------------------------------------------
+// Segment scan of the states: a run of L tokens maps the state S entering it
+// to lam^L S + S_loc, with S_loc the state it leaves from a zero start. With
+// loc[n][g] the state leaving segment g (segment 0 from the true initial
+// state, the others from zero), the state entering segment g >= 1 is
+//   in[n][1] = loc[n][0],  in[n][g] = lam^L in[n][g-1] + loc[n][g-1].
+// One thread per four state elements of one (sequence, head), in order over g.
+static __global__ void k_seg_scan(const float* __restrict__ loc, float* __restrict__ in,
+                           const float* __restrict__ lambda, int n_seq, int nseg, int H,
+                           int ssz4, int seg_len)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    const int nh = blockIdx.y;                 // n H + h
+    if (i >= ssz4) return;
+    const int n = nh / H, h = nh - n * H;
+    const float fL = __builtin_amdgcn_exp2f((float)seg_len * log2f(lambda[h]));
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    auto at = [&](int g) -> size_t { return (((size_t)n * nseg + g) * H + h) * (size_t)ssz4 + i; };
+    f4 s = reinterpret_cast<const f4*>(loc)[at(0)];
+    reinterpret_cast<f4*>(in)[at(1)] = s;
+    for (int g = 2; g < nseg; ++g) {
+        const f4 l = reinterpret_cast<const f4*>(loc)[at(g - 1)];
+        s = fL * s + l;
+        reinterpret_cast<f4*>(in)[at(g)] = s;
+    }
+}
+
+// Reverse scan of the state gradients over segments: with loc[n][g] the
+// gradient state leaving segment g at its front (segment nseg-1 from
+// d_final_state, the others from zero), the one entering segment g from the
+// back is in[n][nseg-2] = loc[n][nseg-1], in[n][g] = lam^L in[n][g+1] + loc[n][g+1].
+static __global__ void k_seg_rscan(const float* __restrict__ loc, float* __restrict__ in,
+                            const float* __restrict__ lambda, int nseg, int H, int ssz4, int seg_len)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    const int nh = blockIdx.y;
+    if (i >= ssz4) return;
+    const int n = nh / H, h = nh - n * H;
+    const float fL = __builtin_amdgcn_exp2f((float)seg_len * log2f(lambda[h]));
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    auto at = [&](int g) -> size_t { return (((size_t)n * nseg + g) * H + h) * (size_t)ssz4 + i; };
+    f4 s = reinterpret_cast<const f4*>(loc)[at(nseg - 1)];
+    reinterpret_cast<f4*>(in)[at(nseg - 2)] = s;
+    for (int g = nseg - 3; g >= 0; --g) {
+        const f4 l = reinterpret_cast<const f4*>(loc)[at(g + 1)];
+        s = fL * s + l;
+        reinterpret_cast<f4*>(in)[at(g)] = s;
+    }
+}
+
 }  // namespace scan
 }  // namespace sgla
 
