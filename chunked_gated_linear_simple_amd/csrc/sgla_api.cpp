@@ -255,6 +255,12 @@ sgla_status sgla_chunk_bwd_segmented(const void* q, const void* k, const void* v
             if (overlaps(outs[i], outsz[i], outs[j], outsz[j]))
                 return fail(SGLA_ERR_INVALID_ARG, "dq, dk and dv must not overlap each other");
     }
+    {
+        // the state gradient written at the front must not overlap a state read elsewhere
+        const size_t nst = (size_t)p.n_seq * H * d_k * d_v * sizeof(float);
+        if (overlaps(d_init_state, nst, d_final_state, nst) || overlaps(d_init_state, nst, init_state, nst))
+            return fail(SGLA_ERR_INVALID_ARG, "d_init_state must not overlap d_final_state or init_state");
+    }
     const int tiles = (T + 63) / 64;
     const int g = n_segments < tiles ? n_segments : tiles;
     const int seg_len = ((tiles + g - 1) / g) * 64;
@@ -315,6 +321,12 @@ sgla_status sgla_chunk_bwd(const void* q, const void* k, const void* v, const vo
         for (int j = 0; j < 4; ++j)
             if (overlaps(outs[i], outsz[i], ins[j], insz[j]))
                 return fail(SGLA_ERR_INVALID_ARG, "dq, dk and dv must not alias q, k, v or dO");
+    {
+        // the state gradient written at the front must not overlap a state read elsewhere
+        const size_t nst = (size_t)p.n_seq * H * d_k * d_v * sizeof(float);
+        if (overlaps(d_init_state, nst, d_final_state, nst) || overlaps(d_init_state, nst, init_state, nst))
+            return fail(SGLA_ERR_INVALID_ARG, "d_init_state must not overlap d_final_state or init_state");
+    }
     hipError_t e = sgla::launch_chunk_bwd(p, q, k, v, dO, init_state, d_final_state, dq, dk, dv,
                                           da, d_init_state, reinterpret_cast<float*>(workspace),
                                           reinterpret_cast<hipStream_t>(hip_stream));

@@ -244,7 +244,8 @@ size_t sgla_chunk_bwd_workspace_bytes(int N, int H, int d_k);
  * dq, dk, dv:  outputs (dtype), shaped like q, k, v; must not alias inputs.
  * da:          [H, d_k] fp32, overwritten with dL/da (at a = 0 when a is NULL;
  *              not zero then, since sigmoid'(0) = 1/4).
- * d_init_state: [N, H, d_k, d_v] or NULL (not written).
+ * d_init_state: [N, H, d_k, d_v] or NULL (not written); must not overlap
+ *              d_final_state or init_state (they are read while it is written).
  * workspace:   device buffer of at least sgla_chunk_bwd_workspace_bytes()
  *              bytes, 16-byte aligned, owned by the caller; its contents on
  *              entry do not matter and are clobbered.

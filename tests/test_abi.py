@@ -175,6 +175,8 @@ BWD_BAD = [
     ("workspace misaligned", dict(ws=P["ws"] + 4), B.SGLA_ERR_WORKSPACE),
     ("dq aliases dO", dict(dq=P["dO"]), B.SGLA_ERR_INVALID_ARG),
     ("dv aliases v", dict(dv=P["v"]), B.SGLA_ERR_INVALID_ARG),
+    ("d_init aliases d_final", dict(ds0=P["sf"]), B.SGLA_ERR_INVALID_ARG),
+    ("d_init overlaps init", dict(ds0=P["s0"] + 4096), B.SGLA_ERR_INVALID_ARG),
     ("unsupported dims", dict(d_v=200), B.SGLA_ERR_UNSUPPORTED),
     ("T zero", dict(T=0), B.SGLA_ERR_INVALID_ARG),
 ]
@@ -429,6 +431,7 @@ SEGB_BAD = [
     ("workspace small", dict(wsb=1 << 20), B.SGLA_ERR_WORKSPACE),
     ("dq aliases dO", dict(dq=P["dO"]), B.SGLA_ERR_INVALID_ARG),
     ("dv overlaps dk", dict(dv=P["dk"] + 1024), B.SGLA_ERR_INVALID_ARG),
+    ("d_init aliases d_final", dict(ds0=P["sf"]), B.SGLA_ERR_INVALID_ARG),
 ]
 
 
