@@ -437,45 +437,50 @@ hipError_t run_conv_fwd(const void* u, const float* w, const float* b, const flo
 //   du_s   = w_3 dpre_s + w_2 dpre_{s+1} + w_1 dpre_{s+2} + w_0 dpre_{s+3}
 //            (dpre = 0 past the sequence) + d_final[s - (L - 3)] for s >= L - 3
 //   dw_j   = sum_t dpre_t x_{t-3+j},  db = sum_t dpre_t
-// k_conv_bwd: a thread owns four channels and a run of BWD_RUN rows; for
+// k_conv_bwd: a thread owns two channels and a run of BWD_RUN rows; for
 // each sequence meeting the run it walks tau from max(run start, sequence
 // start) to three rows past the run's end (within the sequence), computing
 // dpre_tau and, three rows behind, du. dw and db of the run's rows go to
 // part[run][5][D]. k_conv_bwd_init writes the initial state's gradient (also
 // for empty sequences) and k_conv_wsum adds the run partials in a fixed order.
-constexpr int BWD_RUN = 32;
+constexpr int BWD_RUN = 64;
 constexpr int BWD_THREADS = 128;
+constexpr int BWD_PF = 4;  // rows of u and dy in flight per thread
 
-// Four channels per access for the backward (8 bytes of bf16, 16 of fp32),
-// so that a thread's windows fit a register budget of four or more waves per SIMD.
-template <typename E> struct Q4;
-template <> struct Q4<u16> {
-    static constexpr int V = 4;
-    typedef uint2 Raw;
-    static __device__ __forceinline__ Raw ld(const u16* p) { return *reinterpret_cast<const uint2*>(p); }
-    static __device__ __forceinline__ Raw zero() { return uint2{0u, 0u}; }
+// Two channels per access for the backward (4 bytes of bf16, 8 of fp32): a
+// thread's windows, weights and partial sums then fit seven waves per SIMD.
+template <typename E> struct Q2;
+template <> struct Q2<u16> {
+    static constexpr int V = 2;
+    typedef uint32_t Raw;
+    static __device__ __forceinline__ Raw ld(const u16* p) { return *reinterpret_cast<const uint32_t*>(p); }
+    static __device__ __forceinline__ Raw zero() { return 0u; }
     static __device__ __forceinline__ void unpack(Raw r, float* x)
     {
-        x[0] = __uint_as_float(r.x << 16);
-        x[1] = __uint_as_float(r.x & 0xffff0000u);
-        x[2] = __uint_as_float(r.y << 16);
-        x[3] = __uint_as_float(r.y & 0xffff0000u);
+        x[0] = __uint_as_float(r << 16);
+        x[1] = __uint_as_float(r & 0xffff0000u);
     }
     static __device__ __forceinline__ void store(u16* p, const float* y)
     {
         typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
         const bf16x2 lo = {static_cast<__bf16>(y[0]), static_cast<__bf16>(y[1])};
-        const bf16x2 hi = {static_cast<__bf16>(y[2]), static_cast<__bf16>(y[3])};
-        *reinterpret_cast<uint2*>(p) = uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+        *reinterpret_cast<uint32_t*>(p) = __builtin_bit_cast(uint32_t, lo);
     }
 };
-template <> struct Q4<float> {
-    static constexpr int V = 4;
-    typedef u32x4 Raw;
-    static __device__ __forceinline__ Raw ld(const float* p) { return *reinterpret_cast<const u32x4*>(p); }
-    static __device__ __forceinline__ Raw zero() { return u32x4{0u, 0u, 0u, 0u}; }
-    static __device__ __forceinline__ void unpack(Raw r, float* x) { Grp<float>::unpack(r, x); }
-    static __device__ __forceinline__ void store(float* p, const float* y) { Grp<float>::store(p, y); }
+template <> struct Q2<float> {
+    static constexpr int V = 2;
+    typedef uint2 Raw;
+    static __device__ __forceinline__ Raw ld(const float* p) { return *reinterpret_cast<const uint2*>(p); }
+    static __device__ __forceinline__ Raw zero() { return uint2{0u, 0u}; }
+    static __device__ __forceinline__ void unpack(Raw r, float* x)
+    {
+        x[0] = __uint_as_float(r.x);
+        x[1] = __uint_as_float(r.y);
+    }
+    static __device__ __forceinline__ void store(float* p, const float* y)
+    {
+        *reinterpret_cast<uint2*>(p) = uint2{__float_as_uint(y[0]), __float_as_uint(y[1])};
+    }
 };
 
 __device__ __forceinline__ float ld_elem(const u16* p, size_t i) { return __uint_as_float((uint32_t)p[i] << 16); }
@@ -492,14 +497,16 @@ __global__ __launch_bounds__(BWD_THREADS) void k_conv_bwd(const E* __restrict__ 
                                                           const float* __restrict__ w, const float* __restrict__ b,
                                                           const float* __restrict__ init,
                                                           const float* __restrict__ dfin, E* __restrict__ du,
-                                                          float* __restrict__ part, Seqs sq, int D)
+                                                          float* __restrict__ part, Seqs sq, int D, int nblk)
 {
-    typedef Q4<E> G;
+    typedef Q2<E> G;
     constexpr int V = G::V;
-    const int grp = blockIdx.y * BWD_THREADS + threadIdx.x;
+    // the channel blocks of one run are consecutive blocks, so the rows they
+    // share are read from HBM at about the same time
+    const int run = blockIdx.x / nblk;
+    const int grp = (blockIdx.x - run * nblk) * BWD_THREADS + threadIdx.x;
     if (grp * V >= D) return;
     const int c0 = grp * V;
-    const int run = blockIdx.x;
     const int r0 = run * BWD_RUN, r1 = min(r0 + BWD_RUN, sq.S);
 
     float wt[V][4], bias[V];
@@ -544,60 +551,78 @@ __global__ __launch_bounds__(BWD_THREADS) void k_conv_bwd(const E* __restrict__ 
         float p1[V], p2[V], p3[V];  // dpre_{tau-1}, dpre_{tau-2}, dpre_{tau-3}
 #pragma unroll
         for (int v = 0; v < V; ++v) p1[v] = p2[v] = p3[v] = 0.0f;
-        // rows are loaded one step ahead of their use
+        // rows are loaded BWD_PF steps ahead of their use, into a register
+        // ring; past the last row the loads repeat it (a cache hit), so every
+        // step issues the same loads and the waits stay counted
         const int e_in = min(e, s1);
-        typename G::Raw nu = G::zero(), ng = G::zero();
-        if (a < e_in) {
-            nu = G::ld(u + (size_t)a * D + c0);
-            ng = G::ld(dy + (size_t)a * D + c0);
+        const int last = e_in - 1;
+        typename G::Raw bu[BWD_PF], bg[BWD_PF];
+#pragma unroll
+        for (int i = 0; i < BWD_PF; ++i) {
+            bu[i] = G::zero();
+            bg[i] = G::zero();
         }
-        for (int tau = a; tau < e; ++tau) {
-            float p0[V];
-            if (tau < s1) {
-                float xu[V], g[V];
-                G::unpack(nu, xu);
-                G::unpack(ng, g);
-                if (tau + 1 < e_in) {
-                    nu = G::ld(u + (size_t)(tau + 1) * D + c0);
-                    ng = G::ld(dy + (size_t)(tau + 1) * D + c0);
-                }
-                const bool own = tau < r1;
+        if (a <= last) {
 #pragma unroll
-                for (int v = 0; v < V; ++v) {
-                    const float pre = bias[v] + wt[v][0] * x3[v] + wt[v][1] * x2[v] + wt[v][2] * x1[v] + wt[v][3] * xu[v];
-                    p0[v] = g[v] * dsilu_f(pre);
-                    if (own) {
-                        aw[v][0] = fmaf(p0[v], x3[v], aw[v][0]);
-                        aw[v][1] = fmaf(p0[v], x2[v], aw[v][1]);
-                        aw[v][2] = fmaf(p0[v], x1[v], aw[v][2]);
-                        aw[v][3] = fmaf(p0[v], xu[v], aw[v][3]);
-                        ab[v] += p0[v];
+            for (int i = 0; i < BWD_PF; ++i) {
+                const size_t r = (size_t)min(a + i, last) * D + c0;
+                bu[i] = G::ld(u + r);
+                bg[i] = G::ld(dy + r);
+            }
+        }
+        for (int t0 = a; t0 < e; t0 += BWD_PF) {
+#pragma unroll
+            for (int i = 0; i < BWD_PF; ++i) {
+                const int tau = t0 + i;
+                if (tau >= e) break;
+                float p0[V];
+                if (tau < s1) {
+                    float xu[V], g[V];
+                    G::unpack(bu[i], xu);
+                    G::unpack(bg[i], g);
+                    {
+                        const size_t r = (size_t)min(tau + BWD_PF, last) * D + c0;
+                        bu[i] = G::ld(u + r);
+                        bg[i] = G::ld(dy + r);
                     }
-                    x3[v] = x2[v];
-                    x2[v] = x1[v];
-                    x1[v] = xu[v];
-                }
-            } else {
+                    const bool own = tau < r1;
 #pragma unroll
-                for (int v = 0; v < V; ++v) p0[v] = 0.0f;
-            }
-            // du of row tau - 3, complete now
-            const int s = tau - 3;
-            if (s >= a && s < min(r1, s1)) {
-                const int k = s - (s1 - 3);
-                float o[V];
+                    for (int v = 0; v < V; ++v) {
+                        const float pre = bias[v] + wt[v][0] * x3[v] + wt[v][1] * x2[v] + wt[v][2] * x1[v] + wt[v][3] * xu[v];
+                        p0[v] = g[v] * dsilu_f(pre);
+                        if (own) {
+                            aw[v][0] = fmaf(p0[v], x3[v], aw[v][0]);
+                            aw[v][1] = fmaf(p0[v], x2[v], aw[v][1]);
+                            aw[v][2] = fmaf(p0[v], x1[v], aw[v][2]);
+                            aw[v][3] = fmaf(p0[v], xu[v], aw[v][3]);
+                            ab[v] += p0[v];
+                        }
+                        x3[v] = x2[v];
+                        x2[v] = x1[v];
+                        x1[v] = xu[v];
+                    }
+                } else {
+#pragma unroll
+                    for (int v = 0; v < V; ++v) p0[v] = 0.0f;
+                }
+                // du of row tau - 3, complete now
+                const int s = tau - 3;
+                if (s >= a && s < min(r1, s1)) {
+                    const int k = s - (s1 - 3);
+                    float o[V];
+#pragma unroll
+                    for (int v = 0; v < V; ++v) {
+                        o[v] = wt[v][3] * p3[v] + wt[v][2] * p2[v] + wt[v][1] * p1[v] + wt[v][0] * p0[v];
+                        if (dfin != nullptr && k >= 0) o[v] += dfin[((size_t)n * 3 + k) * D + c0 + v];
+                    }
+                    G::store(du + (size_t)s * D + c0, o);
+                }
 #pragma unroll
                 for (int v = 0; v < V; ++v) {
-                    o[v] = wt[v][3] * p3[v] + wt[v][2] * p2[v] + wt[v][1] * p1[v] + wt[v][0] * p0[v];
-                    if (dfin != nullptr && k >= 0) o[v] += dfin[((size_t)n * 3 + k) * D + c0 + v];
+                    p3[v] = p2[v];
+                    p2[v] = p1[v];
+                    p1[v] = p0[v];
                 }
-                G::store(du + (size_t)s * D + c0, o);
-            }
-#pragma unroll
-            for (int v = 0; v < V; ++v) {
-                p3[v] = p2[v];
-                p2[v] = p1[v];
-                p1[v] = p0[v];
             }
         }
     }
@@ -682,10 +707,11 @@ hipError_t run_conv_bwd(const void* u, const void* dy, const float* w, const flo
     sq.T = T;
     sq.S = (cu != nullptr) ? T : B * T;
     const int n_runs = (sq.S + BWD_RUN - 1) / BWD_RUN;
-    const int groups = D / Q4<E>::V;
-    const int gy = (groups + BWD_THREADS - 1) / BWD_THREADS;
-    hipLaunchKernelGGL(k_conv_bwd<E>, dim3(n_runs, gy), dim3(BWD_THREADS), 0, stream, reinterpret_cast<const E*>(u),
-                       reinterpret_cast<const E*>(dy), w, b, init, dfin, reinterpret_cast<E*>(du), part, sq, D);
+    const int groups = D / Q2<E>::V;
+    const int nblk = (groups + BWD_THREADS - 1) / BWD_THREADS;
+    hipLaunchKernelGGL(k_conv_bwd<E>, dim3(n_runs * nblk), dim3(BWD_THREADS), 0, stream,
+                       reinterpret_cast<const E*>(u), reinterpret_cast<const E*>(dy), w, b, init, dfin,
+                       reinterpret_cast<E*>(du), part, sq, D, nblk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (dinit != nullptr) {

@@ -315,7 +315,7 @@ sgla_status sgla_conv_fwd(const void* u, const float* w, const float* b,
                           sgla_dtype dtype, void* hip_stream);
 
 /*
- * Bytes of device workspace sgla_conv_bwd needs: five fp32 rows of D per 32
+ * Bytes of device workspace sgla_conv_bwd needs: five fp32 rows of D per 64
  * token rows (the per-run partial sums of the tap and bias gradients). T is
  * the total token count when packed (B = 1).
  */

@@ -405,9 +405,10 @@ def test_conv_bwd_rejects(L, name, kw, code):
 
 
 def test_conv_bwd_workspace_bytes(L):
-    # five fp32 rows of D per 32 token rows
-    assert B.sgla_conv_bwd_workspace_bytes(8, 2048, 3072) == 512 * 5 * 3072 * 4
-    assert B.sgla_conv_bwd_workspace_bytes(1, 33, 16) == 2 * 5 * 16 * 4
+    # five fp32 rows of D per 64 token rows
+    assert B.sgla_conv_bwd_workspace_bytes(8, 2048, 3072) == 256 * 5 * 3072 * 4
+    assert B.sgla_conv_bwd_workspace_bytes(1, 65, 16) == 2 * 5 * 16 * 4
+    assert B.sgla_conv_bwd_workspace_bytes(1, 64, 16) == 1 * 5 * 16 * 4
     assert B.sgla_conv_bwd_workspace_bytes(0, 33, 16) == 0
 
 

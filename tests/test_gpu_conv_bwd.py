@@ -1,6 +1,6 @@
 """GPU parity of the conv prologue's gradients (sgla_conv_bwd) against the
 fp64 oracle, which differentiates the conv sequence by sequence and channel
-by channel: dense rows whose 32-row runs straddle sequence boundaries, packed
+by channel: dense rows whose 64-row runs straddle sequence boundaries, packed
 sequences of 0 to 70 tokens (shorter than the history included), no bias or
 initial state, fp32, the full Laplace width, and a bitwise repeat."""
 import numpy as np
@@ -64,7 +64,7 @@ def _check(inp, got, ref):
 
 
 def test_conv_bwd_dense_runs_straddle_sequences():
-    """B=2, T=100: the 32-row runs over the 200 rows cross the boundary at 100."""
+    """B=2, T=100: the 64-row runs over the 200 rows cross the boundary at 100."""
     inp = I.conv_inputs(801, (2, 100, 64), 64, "bf16", 2, with_grad=True)
     _check(inp, _run(inp), _ref(inp))
 
