@@ -674,6 +674,8 @@ __global__ __launch_bounds__(BWD_THREADS) void k_conv_bwd_init(const E* __restri
     }
 }
 
+constexpr int WSUM_BATCH = 8;
+
 // dw[c][j] and db[c]: the run partials, split 64 ways (thread k of a block of
 // 16 channels adds runs k, k + 64, ... in order) and the 64 sums added in order.
 __global__ __launch_bounds__(1024) void k_conv_wsum(const float* __restrict__ part, float* __restrict__ dw,
@@ -685,7 +687,18 @@ __global__ __launch_bounds__(1024) void k_conv_wsum(const float* __restrict__ pa
     const int c = blockIdx.x * 16 + cl;
     float acc = 0.0f;
     if (c < D)
-        for (int r = k; r < n_runs; r += 64) acc += part[((size_t)r * 5 + j) * D + c];
+        // eight loads in flight, added in the same order as one at a time
+        for (int r0 = k; r0 < n_runs; r0 += 64 * WSUM_BATCH) {
+            float x[WSUM_BATCH];
+#pragma unroll
+            for (int i = 0; i < WSUM_BATCH; ++i) {
+                const int r = r0 + 64 * i;
+                x[i] = r < n_runs ? part[((size_t)r * 5 + j) * D + c] : 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < WSUM_BATCH; ++i)
+                if (r0 + 64 * i < n_runs) acc += x[i];
+        }
     red[k][cl] = acc;
     __syncthreads();
     if (k == 0 && c < D) {

@@ -353,6 +353,8 @@ __global__ __launch_bounds__(NORM_THREADS) void k_head_norm_gate_bwd(
     }
 }
 
+constexpr int SUM_BATCH = 8;
+
 // dgamma[tier][c] = sum over b, the tier's heads and the token blocks, in
 // that fixed order split 64 ways: thread (k, c) of a block of 16 channels sums
 // entries k, k + 64, ...; then the 64 sums are added in order.
@@ -366,12 +368,24 @@ __global__ __launch_bounds__(1024) void k_dgamma_sum(const float* __restrict__ p
     const int n_ent = B * per_tier * nTB;
     float t = 0.0f;
     if (c < d_v) {
-        for (int e = k; e < n_ent; e += 64) {
-            const int bb = e / (per_tier * nTB);
-            const int rem = e - bb * per_tier * nTB;
-            const int hh = tier * per_tier + rem / nTB;
-            const int tb = rem - (rem / nTB) * nTB;
-            t += part[(((size_t)bb * H + hh) * nTB + tb) * d_v + c];
+        // eight loads in flight, added in the same order as one at a time
+        for (int e0 = k; e0 < n_ent; e0 += 64 * SUM_BATCH) {
+            float x[SUM_BATCH];
+#pragma unroll
+            for (int i = 0; i < SUM_BATCH; ++i) {
+                const int e = e0 + 64 * i;
+                x[i] = 0.0f;
+                if (e < n_ent) {
+                    const int bb = e / (per_tier * nTB);
+                    const int rem = e - bb * per_tier * nTB;
+                    const int hh = tier * per_tier + rem / nTB;
+                    const int tb = rem - (rem / nTB) * nTB;
+                    x[i] = part[(((size_t)bb * H + hh) * nTB + tb) * d_v + c];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < SUM_BATCH; ++i)
+                if (e0 + 64 * i < n_ent) t += x[i];
         }
     }
     red[k][cl] = t;
