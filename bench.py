@@ -56,29 +56,57 @@ MIN_WARM_S = 1.5               # untimed warm-up floor per workload, seconds
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_fwd__laplace_fwd_B8_hbm_traffic.txt")
-FWD_SOURCES = [os.path.join(ROOT, "chunked_gated_linear_simple_amd", "csrc", f)
-               for f in ("sgla_scan.hpp", "sgla_fwd.hip")]
+MFMA_FILE = os.path.join(ROOT, "profiles", "k_fwd_k_bwd__laplace_mfma_counters.txt")
+CSRC = os.path.join(ROOT, "chunked_gated_linear_simple_amd", "csrc")
+FWD_SOURCES = [os.path.join(CSRC, f) for f in ("sgla_scan.hpp", "sgla_fwd.hip")]
+CHUNK_SOURCES = FWD_SOURCES + [os.path.join(CSRC, "sgla_bwd.hip")]
+# algorithmic matrix-core FLOPs per head-token with the causal mask exploited
+# (C = 128): forward C(d_k + d_v) + 4 d_k d_v + 2 d_k + 2 d_v; backward
+# C(3 d_k + 2 d_v) + 10 d_k d_v + 8 d_k + 4 d_v
+FWD_FLOPS_HT = 128 * (DK + DV) + 4 * DK * DV + 2 * DK + 2 * DV
+BWD_FLOPS_HT = 128 * (3 * DK + 2 * DV) + 10 * DK * DV + 8 * DK + 4 * DV
+
+
+def _profile_values(path, sources):
+    """The key: value lines of a committed counter summary, or None when the
+    kernel sources have changed since its counters were taken."""
+    import hashlib
+    try:
+        kv = {}
+        for line in open(path):
+            if line.startswith("#") or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+        h = hashlib.sha256()
+        for f in sources:
+            h.update(open(f, "rb").read())
+        if h.hexdigest()[:16] != kv.get("sources_sha256"):
+            return None
+        return kv
+    except OSError:
+        return None
 
 
 def measured_traffic():
     """HBM bytes per launch of the forward kernel from the committed counter
     summary (FETCH_SIZE and WRITE_SIZE scaled by a copy kernel of known
     size), or None when the kernel sources have changed since it was taken."""
-    import hashlib
+    kv = _profile_values(TRAFFIC_FILE, FWD_SOURCES)
     try:
-        kv = {}
-        for line in open(TRAFFIC_FILE):
-            if line.startswith("#") or ":" not in line:
-                continue
-            k, v = line.split(":", 1)
-            kv[k.strip()] = v.strip()
-        h = hashlib.sha256()
-        for f in FWD_SOURCES:
-            h.update(open(f, "rb").read())
-        if h.hexdigest()[:16] != kv.get("sources_sha256"):
-            return None
-        return int(kv["traffic_bytes_per_launch"])
-    except (OSError, KeyError, ValueError):
+        return None if kv is None else int(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def executed_mfma_flops(key):
+    """Executed bf16 matrix-core FLOPs per launch (SQ_INSTS_VALU_MFMA_MOPS_BF16
+    x 512) of one chunk kernel on one workload ("fwd_b8", "fwd_b4", "bwd_b4"),
+    or None when the sources have changed since the counters were taken."""
+    kv = _profile_values(MFMA_FILE, CHUNK_SOURCES)
+    try:
+        return None if kv is None else int(kv[key + "_executed_flops"])
+    except (KeyError, ValueError):
         return None
 
 
@@ -108,7 +136,14 @@ def gen(shape, seed, std=1.0, scale=1.0, dtype=None):
 
 
 def timed(fn, steps, warmup, min_warm_s=None):
-    """Mean milliseconds per call of fn(i), from HIP events on the current stream.
+    """(mean, wall-clock mean) milliseconds per call of fn(i); see timed_stats."""
+    st = timed_stats(fn, steps, warmup, min_warm_s)
+    return st["mean"], st["wall"]
+
+
+def timed_stats(fn, steps, warmup, min_warm_s=None):
+    """Mean, median and minimum milliseconds per call of fn(i), from HIP events
+    on the current stream, and the wall-clock mean.
 
     Runs `warmup` untimed calls, then keeps calling (untimed) until at least
     `min_warm_s` seconds of warm-up have passed: the chip's clocks take on the
@@ -135,8 +170,10 @@ def timed(fn, steps, warmup, min_warm_s=None):
         ends[i].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return sum(per) / len(per), wall * 1e3 / steps
+    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    n = len(per)
+    median = per[n // 2] if n % 2 else 0.5 * (per[n // 2 - 1] + per[n // 2])
+    return {"mean": sum(per) / n, "median": median, "min": per[0], "wall": wall * 1e3 / steps}
 
 
 def bench_fwd(args, B=8, T=2048, nsets=3):
@@ -157,11 +194,14 @@ def bench_fwd(args, B=8, T=2048, nsets=3):
         q, k, v, o, sf = sets[i % nsets]
         Bd.sgla_chunk_fwd(q, k, v, lam, a, final_state=sf, o=o, chunk=128)
 
-    ms, wall_ms = timed(step, args.steps, args.warmup)
+    st = timed_stats(step, args.steps, args.warmup)
+    ms = st["mean"]
     toks = B * T
     bytes_ = B * H * T * HT_BYTES + B * H * STATE_BYTES
-    return {"ms": ms, "wall_ms": wall_ms, "tokens": toks, "tok_s": toks / (ms * 1e-3),
-            "bytes": bytes_, "gbs": bytes_ / (ms * 1e-3) / 1e9}
+    flops = B * H * T * FWD_FLOPS_HT
+    return {"ms": ms, "ms_median": st["median"], "ms_min": st["min"], "wall_ms": st["wall"],
+            "tokens": toks, "tok_s": toks / (ms * 1e-3),
+            "bytes": bytes_, "gbs": bytes_ / (ms * 1e-3) / 1e9, "flops": flops}
 
 
 def bench_fwdbwd(args, B=4, T=2048):
@@ -185,9 +225,15 @@ def bench_fwdbwd(args, B=4, T=2048):
     toks = B * T
     # algorithmic bytes, fwd: q,k,v,o (1152/ht); bwd: reads q,k,v,dO 1152 + writes dq,dk,dv 768
     bytes_ = B * H * T * (1152 + 1920)
-    return {"ms_fwd": ms_f, "ms_bwd": ms_b, "tokens": toks,
-            "tok_s": toks / ((ms_f + ms_b) * 1e-3), "bytes": bytes_,
-            "gbs": bytes_ / ((ms_f + ms_b) * 1e-3) / 1e9}
+    t_s = (ms_f + ms_b) * 1e-3
+    flops = B * H * T * (FWD_FLOPS_HT + BWD_FLOPS_HT)
+    r = {"ms_fwd": ms_f, "ms_bwd": ms_b, "tokens": toks, "tok_s": toks / t_s, "bytes": bytes_,
+         "gbs": bytes_ / t_s / 1e9, "flops": flops,
+         "mfma_frac_algorithmic": flops / t_s / (BF16_PEAK_TFLOPS * 1e12)}
+    ex_f, ex_b = executed_mfma_flops("fwd_b4"), executed_mfma_flops("bwd_b4")
+    r["mfma_frac_executed"] = (None if ex_f is None or ex_b is None
+                               else (ex_f + ex_b) / t_s / (BF16_PEAK_TFLOPS * 1e12))
+    return r
 
 
 def bench_decode(args, N=1280, steps=64):
@@ -510,10 +556,17 @@ def main():
                                    "bf16, fp32 state, final state written",
                        "batch": 8, "seq_len": 2048, "heads": H, "d_k": DK, "d_v": DV,
                        "chunk": 128},
+            "ms_median": fwd["ms_median"], "ms_min": fwd["ms_min"],
             "roofline": {"bound": "hbm", "kernel": "k_fwd", "achieved": fwd["gbs"],
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": fwd["gbs"] / HBM_PEAK_GBS,
-                         "traffic": measured_traffic(), "bytes_per_launch": fwd["bytes"]},
+                         "traffic": measured_traffic(), "bytes_per_launch": fwd["bytes"],
+                         "flops_per_launch": fwd["flops"],
+                         "mfma_frac_algorithmic": fwd["flops"] / (fwd["ms"] * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+                         "mfma_frac_executed": None},
         })
+        ex = executed_mfma_flops("fwd_b8")
+        if ex is not None:
+            line["roofline"]["mfma_frac_executed"] = ex / (fwd["ms"] * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)
     else:
         first = next(iter(secondary.values()))
         line.update({"value": first["tok_s"], "config": {"workload": next(iter(secondary))}})

@@ -1,0 +1,40 @@
+"""Host-side pieces of bench.py: the one-GPU refusal, the algorithmic work
+per head-token, and the source-hash guard on committed counter summaries."""
+import hashlib
+import json
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "one GPU" in line["error"] and line["n_gpus"] == 2
+
+
+def test_algorithmic_flops_per_head_token():
+    # forward: causal scores and P V average C d_k + C d_v, plus the readout and
+    # the state update (2 d_k d_v each) and the gate's two dot products
+    assert bench.FWD_FLOPS_HT == 128 * 96 + 128 * 192 + 2 * 96 * 192 * 2 + 2 * 96 + 2 * 192 == 111_168
+    assert bench.BWD_FLOPS_HT == 271_872
+    # bytes per head-token of the forward: q, k (d_k) and v, o (d_v) in bf16
+    assert bench.HT_BYTES == 1152
+
+
+def test_profile_values_follow_the_source_hash(tmp_path):
+    src = tmp_path / "k.hip"
+    src.write_bytes(b"kernel source")
+    digest = hashlib.sha256(b"kernel source").hexdigest()[:16]
+    prof = tmp_path / "p.txt"
+    prof.write_text(f"# comment: ignored\nx_executed_flops: 123\nsources_sha256: {digest}\n")
+    assert bench._profile_values(str(prof), [str(src)])["x_executed_flops"] == "123"
+    src.write_bytes(b"kernel source, changed")
+    assert bench._profile_values(str(prof), [str(src)]) is None
+    assert bench._profile_values(str(tmp_path / "missing.txt"), [str(src)]) is None
