@@ -17,7 +17,7 @@ Also measured in the same run and reported under "secondary" (same clock):
   varlen: 32 packed sequences, lengths log-uniform in [128, 32768] (one of
           32768), init states ~ N(0, 0.02), tokens/s = sum T / t
   long:   one sequence of T=32768 (B=1, H=16) with initial and final state,
-          single pass and segmented (9 segments joined by a state scan), and
+          single pass and segmented (8 segments joined by a state scan), and
           its backward, single pass and segmented (4 segments),
           tokens/s = 32768 / t
   norm:   the mixer epilogue (Head RMSNorm per decay tier, 4 tiers, + SiLU(g)
@@ -419,13 +419,13 @@ def bench_varlen(args):
             "gbs": bytes_ / (ms * 1e-3) / 1e9, "n_seq": int(len(L)), "max_len": int(np.max(L))}
 
 
-def bench_long(args, T=32768, n_segments=9):
+def bench_long(args, T=32768, n_segments=8):
     """One long sequence (B=1, H=16, T=32768: the longest sequence of the
     packed workload as a batch of its own), initial and final state: the
     single-pass forward runs 32 workgroups down a 512-tile chain; the
     segmented forward cuts it into n_segments runs joined by a state scan
-    (9: each of its two forward launches then has 8 x 32 = 256 workgroups,
-    one per CU)."""
+    (8: its full forward launch then has 8 x 32 = 256 workgroups, one per
+    CU, after a state-only launch over the first 7)."""
     import torch
     from chunked_gated_linear_simple_amd import binding as Bd
     lam = Bd.sgla_decay_schedule(H, 1.0, 2048.0).cuda()

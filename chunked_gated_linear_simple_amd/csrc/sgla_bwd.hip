@@ -63,14 +63,16 @@ __global__ void k_da_sum(const float* __restrict__ part, float* __restrict__ da,
     da[i] = s;
 }
 
-// The state passes of the segmented backward in one launch: the forward scan
-// over segments 0 .. nseg-2 (blocks [0, nf)) and the DV scan over segments
-// 1 .. nseg-1 (the blocks after), which are independent of each other. Each
-// role's blocks map to (unit, value slice) as in k_fwd.
+// The state passes of the segmented backward in one launch: the forward state
+// scan over segments 0 .. nseg-2 (blocks [0, nf)) and the gradient state scan
+// over segments 1 .. nseg-1 (the blocks after), which are independent of each
+// other and write no outputs. Each role's blocks map to (unit, value slice) as
+// in k_fwd.
 template <int DK>
 __global__ __launch_bounds__(NTHREADS_W) void k_seg_states(Args af, Args adv, int nf)
 {
-    constexpr int LDS = LayW<WFwd<DK>>::LDS > LayW<WDv<DK>>::LDS ? LayW<WFwd<DK>>::LDS : LayW<WDv<DK>>::LDS;
+    constexpr int LF = LayW<WFwdState<DK>>::LDS, LD = LayW<WDvState<DK>>::LDS;
+    constexpr int LDS = LF > LD ? LF : LD;
     __shared__ __attribute__((aligned(16))) char smem[LDS];
     const bool fwd = (int)blockIdx.x < nf;
     const Args& p = fwd ? af : adv;
@@ -78,8 +80,8 @@ __global__ __launch_bounds__(NTHREADS_W) void k_seg_states(Args af, Args adv, in
     const int slice = (b >> 3) % p.nsl;
     const int unit = ((b >> 3) / p.nsl) * 8 + (b & 7);
     if (unit >= p.n_units) return;
-    if (fwd) body_wide<WFwd<DK>>(p, unit, slice, smem);
-    else body_wide<WDv<DK>>(p, unit, slice, smem);
+    if (fwd) body_wide<WFwdState<DK>>(p, unit, slice, smem);
+    else body_wide<WDvState<DK>>(p, unit, slice, smem);
 }
 
 template <int DKV, int DKG>
@@ -127,16 +129,16 @@ hipError_t launch_bwd_bf16_segmented(const ChunkProblem& p, const void* q, const
     base.dkr = p.d_k;
     base.dvr = p.d_v;
 
-    // 1. in one launch: the forward over segments 0 .. nseg-2 (segment 0 from
-    // init_state, the rest from zero) keeping the states they leave, and the
-    // dv scan over segments 1 .. nseg-1 from their ends (the last from
-    // d_final_state, the rest from zero) keeping the gradient states they
-    // leave at their fronts; both write provisional outputs into dv
+    // 1. in one launch: the forward state scan over segments 0 .. nseg-2
+    // (segment 0 from init_state, the rest from zero) keeping the states they
+    // leave, and the gradient state scan over segments 1 .. nseg-1 from their
+    // ends (the last from d_final_state, the rest from zero) keeping the
+    // states they leave at their fronts; neither writes outputs
     scan::Args af = base;
-    af.q = reinterpret_cast<cp>(q);
+    af.q = nullptr;
     af.k = reinterpret_cast<cp>(k);
     af.v = reinterpret_cast<cp>(v);
-    af.o = reinterpret_cast<uint16_t*>(dv);
+    af.o = nullptr;
     af.s_init = init_state;
     af.s_out_seg = f_loc;
     af.seg_first = 0;
@@ -148,6 +150,8 @@ hipError_t launch_bwd_bf16_segmented(const ChunkProblem& p, const void* q, const
     av.v = reinterpret_cast<cp>(dO);
     av.o = reinterpret_cast<uint16_t*>(dv);
     scan::Args a2 = av;
+    a2.q = nullptr;
+    a2.o = nullptr;
     a2.s_init = d_final_state;
     a2.s_out_seg = g_loc;
     a2.seg_first = 1;
@@ -168,7 +172,7 @@ hipError_t launch_bwd_bf16_segmented(const ChunkProblem& p, const void* q, const
     // gradient states
     const int ssz4 = (int)(ssz / 4);
     hipLaunchKernelGGL(scan::k_seg_scan, dim3((ssz4 + 255) / 256, p.n_seq * p.H), dim3(256), 0, stream, f_loc,
-                       f_in, p.lambda, p.n_seq, nseg, p.H, ssz4, seg_len);
+                       f_in, p.lambda, p.n_seq, nseg, p.H, ssz4, seg_len, 0, nullptr);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(scan::k_seg_rscan, dim3((ssz4 + 255) / 256, p.n_seq * p.H), dim3(256), 0, stream, g_loc,

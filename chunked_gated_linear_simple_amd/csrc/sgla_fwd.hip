@@ -23,11 +23,24 @@ __global__ __launch_bounds__(NTHREADS_W) void k_fwd(Args p)
     body_wide<WFwd<DK>>(p, unit, slice, smem);
 }
 
+// The state scan alone over each unit's run (no outputs), mapped as k_fwd.
 template <int DK>
-hipError_t run_fwd(const Args& a, hipStream_t stream)
+__global__ __launch_bounds__(NTHREADS_W) void k_fwd_state(Args p)
+{
+    __shared__ __attribute__((aligned(16))) char smem[LayW<WFwdState<DK>>::LDS];
+    const int b = blockIdx.x;
+    const int slice = (b >> 3) % p.nsl;
+    const int unit = ((b >> 3) / p.nsl) * 8 + (b & 7);
+    if (unit >= p.n_units) return;
+    body_wide<WFwdState<DK>>(p, unit, slice, smem);
+}
+
+template <int DK>
+hipError_t run_fwd(const Args& a, hipStream_t stream, bool out = true)
 {
     const int grid = ((a.n_units + 7) / 8) * 8 * a.nsl;
-    hipLaunchKernelGGL(k_fwd<DK>, dim3(grid), dim3(NTHREADS_W), 0, stream, a);
+    if (out) hipLaunchKernelGGL(k_fwd<DK>, dim3(grid), dim3(NTHREADS_W), 0, stream, a);
+    else hipLaunchKernelGGL(k_fwd_state<DK>, dim3(grid), dim3(NTHREADS_W), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -57,21 +70,22 @@ static scan::Args fwd_args(const ChunkProblem& p, const void* q, const void* k, 
     return a;
 }
 
-static hipError_t run_fwd_any(const scan::Args& a, int d_k, hipStream_t stream)
+static hipError_t run_fwd_any(const scan::Args& a, int d_k, hipStream_t stream, bool out = true)
 {
-    if (d_k <= 32) return scan::run_fwd<32>(a, stream);
-    if (d_k <= 64) return scan::run_fwd<64>(a, stream);
-    return scan::run_fwd<96>(a, stream);
+    if (d_k <= 32) return scan::run_fwd<32>(a, stream, out);
+    if (d_k <= 64) return scan::run_fwd<64>(a, stream, out);
+    return scan::run_fwd<96>(a, stream, out);
 }
 
-// The states entering segments 1 .. nseg-1 of dense sequences (ws_in): the
-// forward over segments 0 .. nseg-2 (provisional outputs into o) keeping the
-// states they leave (ws_loc), then the scan of those states.
-hipError_t launch_fwd_bf16_seg_states(const ChunkProblem& p, const void* q, const void* k, const void* v,
-                                      const float* init_state, void* o, int nseg, int seg_len, float* ws_loc,
+// The states entering segments 0 .. nseg-1 of dense sequences (ws_in): the
+// state scan alone over segments 0 .. nseg-2 keeping the states they leave
+// (ws_loc), then the scan of those states, which also copies init_state into
+// segment 0's entry.
+hipError_t launch_fwd_bf16_seg_states(const ChunkProblem& p, const void* k, const void* v,
+                                      const float* init_state, int nseg, int seg_len, float* ws_loc,
                                       float* ws_in, hipStream_t stream)
 {
-    scan::Args a = fwd_args(p, q, k, v, init_state, nullptr, o);
+    scan::Args a = fwd_args(p, nullptr, k, v, init_state, nullptr, nullptr);
     a.nseg = nseg;
     a.seg_len = seg_len;
     a.seg_first = 0;
@@ -79,30 +93,34 @@ hipError_t launch_fwd_bf16_seg_states(const ChunkProblem& p, const void* q, cons
     a.s_in_seg = nullptr;
     a.s_out_seg = ws_loc;
     a.n_units = p.n_seq * (nseg - 1) * p.H;
-    hipError_t e = run_fwd_any(a, p.d_k, stream);
+    hipError_t e = run_fwd_any(a, p.d_k, stream, false);
     if (e != hipSuccess) return e;
     const int ssz4 = p.d_k * p.d_v / 4;
     hipLaunchKernelGGL(scan::k_seg_scan, dim3((ssz4 + 255) / 256, p.n_seq * p.H), dim3(256), 0, stream,
-                       ws_loc, ws_in, p.lambda, p.n_seq, nseg, p.H, ssz4, seg_len);
+                       ws_loc, ws_in, p.lambda, p.n_seq, nseg, p.H, ssz4, seg_len, 1, init_state);
     return hipGetLastError();
 }
 
 // Segment-parallel bf16 forward of dense sequences (see sgla_chunk_fwd_segmented):
-// segments 0 .. nseg-2 from their provisional starts, the scan of the states,
-// then segments 1 .. nseg-1 from their true starts (rewriting their outputs).
+// the state scan of segments 0 .. nseg-2 from zero (segment 0 from
+// init_state), the scan of the states, then the forward of every segment from
+// its true entering state.
 hipError_t launch_fwd_bf16_segmented(const ChunkProblem& p, const void* q, const void* k,
                                      const void* v, const float* init_state, float* final_state,
                                      void* o, int nseg, int seg_len, float* ws_loc, float* ws_in,
                                      hipStream_t stream)
 {
-    hipError_t e = launch_fwd_bf16_seg_states(p, q, k, v, init_state, o, nseg, seg_len, ws_loc, ws_in, stream);
+    hipError_t e = launch_fwd_bf16_seg_states(p, k, v, init_state, nseg, seg_len, ws_loc, ws_in, stream);
     if (e != hipSuccess) return e;
     scan::Args a = fwd_args(p, q, k, v, init_state, final_state, o);
     a.nseg = nseg;
     a.seg_len = seg_len;
-    a.seg_count = nseg - 1;
-    a.n_units = p.n_seq * (nseg - 1) * p.H;
-    a.seg_first = 1;
+    a.seg_first = 0;
+    a.seg_count = nseg;
+    a.n_units = p.n_seq * nseg * p.H;
+    // segment 0 too starts from ws_in (where the scan copied init_state), so
+    // final_state may alias init_state: this launch reads it nowhere
+    a.seg_in_all = 1;
     a.s_in_seg = ws_in;
     a.s_out_seg = nullptr;
     return run_fwd_any(a, p.d_k, stream);

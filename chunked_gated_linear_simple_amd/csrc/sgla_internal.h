@@ -36,10 +36,10 @@ hipError_t launch_fwd_bf16_segmented(const ChunkProblem& p, const void* q, const
                                      void* o, int nseg, int seg_len, float* ws_loc, float* ws_in,
                                      hipStream_t stream);
 
-// The forward states entering segments 1 .. nseg-1 (ws_in), with provisional
-// outputs of segments 0 .. nseg-2 written into o (sgla_fwd.hip).
-hipError_t launch_fwd_bf16_seg_states(const ChunkProblem& p, const void* q, const void* k, const void* v,
-                                      const float* init_state, void* o, int nseg, int seg_len, float* ws_loc,
+// The forward states entering segments 1 .. nseg-1 (ws_in), from the state
+// scan alone over segments 0 .. nseg-2 (sgla_fwd.hip).
+hipError_t launch_fwd_bf16_seg_states(const ChunkProblem& p, const void* k, const void* v,
+                                      const float* init_state, int nseg, int seg_len, float* ws_loc,
                                       float* ws_in, hipStream_t stream);
 
 // bf16 backward of dense sequences cut into nseg >= 2 segments (sgla_bwd.hip);

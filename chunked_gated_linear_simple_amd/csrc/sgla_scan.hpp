@@ -210,8 +210,9 @@ struct Args {
     // enters the sequence (0, or the last for a reverse scan) starts from
     // s_init, the one where it leaves writes s_final; the others start from
     // s_in_seg and write s_out_seg, both [n][nseg][H][state] (NULL: zero / not
-    // written).
-    int nseg, seg_len, seg_first, seg_count;
+    // written). With seg_in_all set the entering segment reads s_in_seg too,
+    // so that a launch whose last segment writes s_final never reads s_init.
+    int nseg, seg_len, seg_first, seg_count, seg_in_all;
     const float* s_in_seg;
     float* s_out_seg;
 };
@@ -252,14 +253,18 @@ constexpr int LOADER_W = NOW_W, SCORER_W = NOW_W + 1;
 constexpr int NR_W = 4;                    // ring depth
 
 // Roles of the eight-wave body: as Role, plus the tile length CT.
-template <int DK_, bool REV_, bool GRAD_, bool DA_, bool INIT_T_, int CT_>
+// OUT = false keeps only the state scan: no q' tile, gate, scores, readout
+// or output, for passes whose only product is the state a run leaves.
+template <int DK_, bool REV_, bool GRAD_, bool DA_, bool INIT_T_, int CT_, bool OUT_ = true>
 struct WRole {
     static constexpr int DK = DK_, CT = CT_;
-    static constexpr bool REV = REV_, GRAD = GRAD_, DA = DA_, INIT_T = INIT_T_;
+    static constexpr bool REV = REV_, GRAD = GRAD_, DA = DA_, INIT_T = INIT_T_, OUT = OUT_;
     static constexpr int E = REV_ ? 0 : 1;
 };
 template <int DK> using WFwd = WRole<DK, false, false, false, false, 64>;
 template <int DK> using WDv = WRole<DK, true, false, false, false, 64>;
+template <int DK> using WFwdState = WRole<DK, false, false, false, false, 64, false>;
+template <int DK> using WDvState = WRole<DK, true, false, false, false, 64, false>;
 template <int DK> using WDq = WRole<DK, false, true, true, true, 32>;
 template <int DK> using WDk = WRole<DK, true, true, false, true, 32>;
 
@@ -297,7 +302,8 @@ struct LayW {
     static constexpr int LDS = OFF_A + (R::GRAD ? DVS * 4 : 0);
     static constexpr int NLQ = SZ_Q / 1024;
     static constexpr int NLV = SZ_V / 1024;
-    static constexpr int NLOAD = 2 * NLQ + (R::GRAD ? 2 : 1) * NLV;
+    static constexpr int NLOAD = (R::OUT ? 2 : 1) * NLQ + (R::GRAD ? 2 : 1) * NLV;
+    static_assert(R::OUT || !R::GRAD, "state-only roles carry no gradient tiles");
     static_assert(CT == 32 || CT == 64, "CT");
     static_assert(DK % 32 == 0 && DK <= (R::GRAD ? 192 : 96), "DK");
     static_assert(SZ_Q % 1024 == 0 && SZ_V % 1024 == 0, "load blocks");
@@ -391,12 +397,12 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
             const int cl = min(CT, len - c * CT);
             if (c == nch - 1 && clast < CT) offsets(clast);
             const long rb = R::REV ? grow(c, cl - 1) : grow(c, 0);
-            const char* qb = reinterpret_cast<const char*>(p.q + rb * dkr);
+            const char* qb = R::OUT ? reinterpret_cast<const char*>(p.q + rb * dkr) : nullptr;
             const char* kb = reinterpret_cast<const char*>(p.k + rb * dkr);
             const char* vb = reinterpret_cast<const char*>(p.v + rb * dvr);
 #pragma unroll
             for (int m = 0; m < Ly::NLQ; ++m) {
-                dma16(qb, offq[m], st + 1024 * m);
+                if constexpr (R::OUT) dma16(qb, offq[m], st + 1024 * m);
                 dma16(kb, offq[m], st + Ly::OFF_K + 1024 * m);
             }
 #pragma unroll
@@ -496,7 +502,7 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
                 wait_vm<0>();
             }
             fixup(0);
-            gate(0);
+            if constexpr (R::OUT) gate(0);
             if (nch > 1) {
                 if (nch > 2) {
                     issue(2);
@@ -505,7 +511,7 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
                     wait_vm<0>();
                 }
                 fixup(1);
-                gate(1);
+                if constexpr (R::OUT) gate(1);
             }
         }
         lds_barrier();
@@ -516,7 +522,7 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
                 if (c + 3 < nch) wait_vm<Ly::NLOAD>();
                 else wait_vm<0>();
                 fixup(c + 2);
-                gate(c + 2);
+                if constexpr (R::OUT) gate(c + 2);
             }
             lds_barrier();
         }
@@ -588,10 +594,10 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
             }
         };
         lds_barrier();
-        if (nch > 0) scores(0);
+        if (R::OUT && nch > 0) scores(0);
         lds_barrier();
         for (int c = 0; c < nch; ++c) {
-            if (c + 1 < nch) scores(c + 1);
+            if (R::OUT && c + 1 < nch) scores(c + 1);
             lds_barrier();
         }
         return;
@@ -611,8 +617,8 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
     const bool last_seg = p.nseg <= 1 || g == p.nseg - 1;
     const bool enters_seq = R::REV ? last_seg : g == 0;
     const bool leaves_seq = R::REV ? g == 0 : last_seg;
-    const float* s_in = enters_seq ? (p.s_init != nullptr ? p.s_init + shead : nullptr)
-                                   : (p.s_in_seg != nullptr ? p.s_in_seg + sseg : nullptr);
+    const float* s_in = (enters_seq && !p.seg_in_all) ? (p.s_init != nullptr ? p.s_init + shead : nullptr)
+                                                      : (p.s_in_seg != nullptr ? p.s_in_seg + sseg : nullptr);
     float* s_out = leaves_seq ? (p.s_final != nullptr ? p.s_final + shead : nullptr)
                               : (p.s_out_seg != nullptr ? p.s_out_seg + sseg : nullptr);
 
@@ -653,80 +659,87 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
         for (int ks = 0; ks < NKT; ++ks)
             vf[ks] = frag(tr_read<SEGV>(Vs, 32 * ks + 8 * qg, OWC * w, lane),
                           tr_read<SEGV>(Vs, 32 * ks + 8 * qg + 4, OWC * w, lane));
-        bf16x8_t pf[NPB];
+        if constexpr (R::OUT) {
+            bf16x8_t pf[NPB];
 #pragma unroll
-        for (int b = 0; b < NPB; ++b)
-            pf[b] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(Pb + (b * 64 + lane) * 16));
+            for (int b = 0; b < NPB; ++b)
+                pf[b] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(Pb + (b * 64 + lane) * 16));
 
-        // ---- readout: O^T = S^T Q'^T, the state as a bf16 pair: hi = the
-        // truncated upper half, lo = the remainder (exact in fp32) rounded
-        f32x4_t oq[NTB] = {};
+            // ---- readout: O^T = S^T Q'^T, the state as a bf16 pair: hi = the
+            // truncated upper half, lo = the remainder (exact in fp32) rounded
+            f32x4_t oq[NTB] = {};
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            u32x4_t hw, lw;
+            for (int ks = 0; ks < NKS; ++ks) {
+                u32x4_t hw, lw;
 #pragma unroll
-            for (int s2 = 0; s2 < 4; ++s2) {
-                const f32x4_t& blk = (s2 < 2) ? sacc[2 * ks] : sacc[2 * ks + 1];
-                const float x0 = blk[2 * (s2 & 1)], x1 = blk[2 * (s2 & 1) + 1];
-                const uint32_t b0 = __float_as_uint(x0), b1 = __float_as_uint(x1);
-                hw[s2] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
-                lw[s2] = pack2(x0 - __uint_as_float(b0 & 0xffff0000u), x1 - __uint_as_float(b1 & 0xffff0000u));
+                for (int s2 = 0; s2 < 4; ++s2) {
+                    const f32x4_t& blk = (s2 < 2) ? sacc[2 * ks] : sacc[2 * ks + 1];
+                    const float x0 = blk[2 * (s2 & 1)], x1 = blk[2 * (s2 & 1) + 1];
+                    const uint32_t b0 = __float_as_uint(x0), b1 = __float_as_uint(x1);
+                    hw[s2] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+                    lw[s2] = pack2(x0 - __uint_as_float(b0 & 0xffff0000u), x1 - __uint_as_float(b1 & 0xffff0000u));
+                }
+                const bf16x8_t sh = __builtin_bit_cast(bf16x8_t, hw), sl = __builtin_bit_cast(bf16x8_t, lw);
+#pragma unroll
+                for (int tb = 0; tb < NTB; ++tb) {
+                    // Q' row 16 tb + l16, d = 32 ks + 8 qg + 0..7
+                    const bf16x8_t qf = __builtin_bit_cast(
+                        bf16x8_t, *reinterpret_cast<const u32x4_t*>(Qs + toff<SEGK>(16 * tb + l16, 32 * ks + 8 * qg)));
+                    oq[tb] = mma16(sh, qf, oq[tb]);
+                    oq[tb] = mma16(sl, qf, oq[tb]);
+                }
             }
-            const bf16x8_t sh = __builtin_bit_cast(bf16x8_t, hw), sl = __builtin_bit_cast(bf16x8_t, lw);
+#pragma unroll
+            for (int db = 0; db < NDB16; ++db)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sacc[db][r] *= fcl;
+
+            // ---- intra-tile part and output (lane = token 16 tb + l16, columns 4 qg + r)
+            f32x4_t acol = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (R::GRAD) acol = *reinterpret_cast<const f32x4_t*>(smem + Ly::OFF_A + 4 * (OWC * w + 4 * qg));
 #pragma unroll
             for (int tb = 0; tb < NTB; ++tb) {
-                // Q' row 16 tb + l16, d = 32 ks + 8 qg + 0..7
-                const bf16x8_t qf = __builtin_bit_cast(
-                    bf16x8_t, *reinterpret_cast<const u32x4_t*>(Qs + toff<SEGK>(16 * tb + l16, 32 * ks + 8 * qg)));
-                oq[tb] = mma16(sh, qf, oq[tb]);
-                oq[tb] = mma16(sl, qf, oq[tb]);
-            }
-        }
+                f32x4_t o = {};
 #pragma unroll
-        for (int db = 0; db < NDB16; ++db)
+                for (int ks = 0; ks <= (tb >> 1); ++ks) o = mma16(vf[ks], pf[pblk(tb, ks)], o);
+                const int t = 16 * tb + l16;
+                float val[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sacc[db][r] *= fcl;
-
-        // ---- intra-tile part and output (lane = token 16 tb + l16, columns 4 qg + r)
-        f32x4_t acol = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (R::GRAD) acol = *reinterpret_cast<const f32x4_t*>(smem + Ly::OFF_A + 4 * (OWC * w + 4 * qg));
+                for (int r = 0; r < 4; ++r) val[r] = fmaf(tdec[tb], oq[tb][r], o[r]);
+                if constexpr (R::GRAD) {
+                    // + c_t a (.) v'_t ; DA: column sums of c_t x_t (.) v'_t
+                    const float ct = cgb[(c & 1) * CT + t];
+                    const u32x2_t yw = lds_u32x2(Vs, toff<SEGV>(t, OWC * w + 4 * qg));
+                    const float y[4] = {bf_lo(yw[0]), bf_hi(yw[0]), bf_lo(yw[1]), bf_hi(yw[1])};
+                    float xv[4] = {0.f, 0.f, 0.f, 0.f};
+                    if constexpr (R::DA) {
+                        const u32x2_t xw = lds_u32x2(st + Ly::OFF_X, toff<SEGV>(t, OWC * w + 4 * qg));
+                        xv[0] = bf_lo(xw[0]);
+                        xv[1] = bf_hi(xw[0]);
+                        xv[2] = bf_lo(xw[1]);
+                        xv[3] = bf_hi(xw[1]);
+                    }
 #pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) {
-            f32x4_t o = {};
-#pragma unroll
-            for (int ks = 0; ks <= (tb >> 1); ++ks) o = mma16(vf[ks], pf[pblk(tb, ks)], o);
-            const int t = 16 * tb + l16;
-            float val[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) val[r] = fmaf(tdec[tb], oq[tb][r], o[r]);
-            if constexpr (R::GRAD) {
-                // + c_t a (.) v'_t ; DA: column sums of c_t x_t (.) v'_t
-                const float ct = cgb[(c & 1) * CT + t];
-                const u32x2_t yw = lds_u32x2(Vs, toff<SEGV>(t, OWC * w + 4 * qg));
-                const float y[4] = {bf_lo(yw[0]), bf_hi(yw[0]), bf_lo(yw[1]), bf_hi(yw[1])};
-                float xv[4] = {0.f, 0.f, 0.f, 0.f};
-                if constexpr (R::DA) {
-                    const u32x2_t xw = lds_u32x2(st + Ly::OFF_X, toff<SEGV>(t, OWC * w + 4 * qg));
-                    xv[0] = bf_lo(xw[0]);
-                    xv[1] = bf_hi(xw[0]);
-                    xv[2] = bf_lo(xw[1]);
-                    xv[3] = bf_hi(xw[1]);
+                    for (int r = 0; r < 4; ++r) {
+                        const float cy = ct * y[r];
+                        val[r] = fmaf(cy, acol[r], val[r]);
+                        if constexpr (R::DA) dpart[r] = fmaf(cy, xv[r], dpart[r]);
+                    }
                 }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float cy = ct * y[r];
-                    val[r] = fmaf(cy, acol[r], val[r]);
-                    if constexpr (R::DA) dpart[r] = fmaf(cy, xv[r], dpart[r]);
+                if (FULL || t < cl) {
+                    const int col = n0 + OWC * w + 4 * qg;
+                    if (FULL || col < dvr) {
+                        uint16_t* orow = p.o + grow(c, t) * dvr + col;
+                        const u32x2_t w2 = {pack2(val[0], val[1]), pack2(val[2], val[3])};
+                        *reinterpret_cast<u32x2_t*>(orow) = w2;
+                    }
                 }
             }
-            if (FULL || t < cl) {
-                const int col = n0 + OWC * w + 4 * qg;
-                if (FULL || col < dvr) {
-                    uint16_t* orow = p.o + grow(c, t) * dvr + col;
-                    const u32x2_t w2 = {pack2(val[0], val[1]), pack2(val[2], val[3])};
-                    *reinterpret_cast<u32x2_t*>(orow) = w2;
-                }
-            }
+        } else {
+#pragma unroll
+            for (int db = 0; db < NDB16; ++db)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sacc[db][r] *= fcl;
         }
 
         // ---- state advance: S = lam^cl S + K'^T V' - K'^T (c V')
@@ -800,11 +813,12 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
 // to lam^L S + S_loc, with S_loc the state it leaves from a zero start. With
 // loc[n][g] the state leaving segment g (segment 0 from the true initial
 // state, the others from zero), the state entering segment g >= 1 is
-//   in[n][1] = loc[n][0],  in[n][g] = lam^L in[n][g-1] + loc[n][g-1].
+//   in[n][1] = loc[n][0],  in[n][g] = lam^L in[n][g-1] + loc[n][g-1],
+// and with copy_init in[n][0] = the initial state itself.
 // One thread per four state elements of one (sequence, head), in order over g.
 static __global__ void k_seg_scan(const float* __restrict__ loc, float* __restrict__ in,
                            const float* __restrict__ lambda, int n_seq, int nseg, int H,
-                           int ssz4, int seg_len)
+                           int ssz4, int seg_len, int copy_init, const float* __restrict__ init)
 {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     const int nh = blockIdx.y;                 // n H + h
@@ -813,6 +827,12 @@ static __global__ void k_seg_scan(const float* __restrict__ loc, float* __restri
     const float fL = __builtin_amdgcn_exp2f((float)seg_len * log2f(lambda[h]));
     typedef float f4 __attribute__((ext_vector_type(4)));
     auto at = [&](int g) -> size_t { return (((size_t)n * nseg + g) * H + h) * (size_t)ssz4 + i; };
+    if (copy_init) {
+        // in[n][0] = the initial state [n][H][state] (zero when NULL)
+        const f4 z = {0.f, 0.f, 0.f, 0.f};
+        reinterpret_cast<f4*>(in)[at(0)] =
+            init != nullptr ? reinterpret_cast<const f4*>(init)[((size_t)n * H + h) * (size_t)ssz4 + i] : z;
+    }
     f4 s = reinterpret_cast<const f4*>(loc)[at(0)];
     reinterpret_cast<f4*>(in)[at(1)] = s;
     for (int g = 2; g < nseg; ++g) {

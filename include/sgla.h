@@ -138,25 +138,26 @@ size_t sgla_chunk_fwd_segmented_workspace_bytes(int B, int H, int d_k, int d_v, 
  * run's own decayed key/value sum (the chunk state-advance equation applied
  * over the run). Each sequence is cut into segments of whole 64-token tiles,
  * ceil(T / n_segments) tokens rounded up (fewer segments when T is short):
- *   1. the forward over segments 0 .. G-2, segment 0 from init_state and the
- *      others from zero, keeping the state each one leaves;
+ *   1. the state scan alone (k and v only, no outputs) over segments
+ *      0 .. G-2, segment 0 from init_state and the others from zero, keeping
+ *      the state each one leaves;
  *   2. a scan of those states: entering segment g, lam^L (entering g-1) plus
  *      (leaving g-1 from zero), the first being the state leaving segment 0;
- *   3. the forward over segments 1 .. G-1 from their true entering states,
- *      which rewrites their outputs and writes final_state.
- * Three kernel launches on hip_stream, about (2G - 2) / G times the work of
- * sgla_chunk_fwd over G times as many workgroups.
+ *   3. the forward over every segment from its true entering state, which
+ *      writes o and final_state.
+ * Three kernel launches on hip_stream: one forward's work over G times as
+ * many workgroups, plus the cheaper state scan of G - 1 segments.
  *
  * q, k, v, lambda, a, init_state, final_state, o, B, H, T, d_k, d_v, chunk:
  *              as for sgla_chunk_fwd, dense layout only (no cu_seqlens);
  *              final_state may equal init_state.
  * dtype:       SGLA_BF16 only (SGLA_ERR_UNSUPPORTED otherwise).
  * n_segments:  segments per sequence requested, >= 1; 1 is sgla_chunk_fwd.
- *              Each forward launch runs (G - 1) * B * H * ceil(d_v / 96)
- *              workgroups of one per CU, so G - 1 = CUs / (B * H * ceil(d_v
- *              / 96)) fills the GPU once (on 256 CUs at H = 16, d_v = 192:
- *              G = 9 for B = 1, 5 for B = 2); at B * H * ceil(d_v / 96) >=
- *              CUs / 2 the single pass is as fast or faster.
+ *              The full forward launch runs G * B * H * ceil(d_v / 96)
+ *              workgroups of one per CU, so G = CUs / (B * H * ceil(d_v / 96))
+ *              fills the GPU once (on 256 CUs at H = 16, d_v = 192: G = 8 for
+ *              B = 1, 4 for B = 2); at B * H * ceil(d_v / 96) >= CUs / 2 the
+ *              single pass is as fast or faster.
  * workspace:   device buffer of at least
  *              sgla_chunk_fwd_segmented_workspace_bytes(B, H, d_k, d_v,
  *              n_segments) bytes, 16-byte aligned, owned by the caller, not
@@ -189,11 +190,12 @@ size_t sgla_chunk_bwd_segmented_workspace_bytes(int B, int H, int d_k, int d_v, 
  * ("Challenge 3: Backward-pass unrolling for a sequential recurrence": the
  * state gradient flows back through every state update). Four steps on
  * hip_stream:
- *   1. the forward over segments 0 .. G-2 (provisional outputs into dv) and
- *      the scan of their leaving states;
- *   2. the dv scan over segments 1 .. G-1 from their ends (the last from
- *      d_final_state, the others from zero; provisional outputs into dv),
- *      keeping the G each leaves at its front;
+ *   1. the forward state scan alone over segments 0 .. G-2 and the scan of
+ *      their leaving states;
+ *   2. the gradient state scan alone over segments 1 .. G-1 from their ends
+ *      (the last from d_final_state, the others from zero), keeping the G
+ *      each leaves at its front (steps 1 and 2 share one launch; neither
+ *      writes outputs);
  *   3. the reverse scan of those: G entering segment g from its end is
  *      lam^L (G entering g+1) + (G leaving g+1 from zero);
  *   4. the full backward over every segment from its true states, which
@@ -203,6 +205,9 @@ size_t sgla_chunk_bwd_segmented_workspace_bytes(int B, int H, int d_k, int d_v, 
  * Arguments as for sgla_chunk_bwd, dense layout only (no cu_seqlens), plus:
  * dtype:       SGLA_BF16 only (SGLA_ERR_UNSUPPORTED otherwise).
  * n_segments:  segments per sequence requested, >= 1; 1 is sgla_chunk_bwd.
+ *              Step 4 runs 4 * G * B * H workgroups at d_k <= 96, d_v <= 192
+ *              (dq, dk and two dv slices), so G = CUs / (4 B H) fills the GPU
+ *              once (on 256 CUs at H = 16: G = 4 for B = 1, 2 for B = 2).
  * workspace:   device buffer of at least
  *              sgla_chunk_bwd_segmented_workspace_bytes(B, H, d_k, d_v,
  *              n_segments) bytes, 16-byte aligned, owned by the caller, not
