@@ -86,6 +86,32 @@ def test_segmented_fwd_in_place_carry_and_repeat():
     assert torch.equal(S_a, state)
 
 
+def test_segmented_fwd_without_initial_state():
+    """No init_state: the scan starts segment 0 from zero (its workspace
+    entry is cleared, not read from a caller pointer)."""
+    inp = I.chunk_inputs(1, 4, 1300, 96, 192, "bf16", seed=95, a_std=0.1, s0_std=None)
+    run_segmented_case(inp, schedule32(4, 1.0, 2048.0), 5)
+
+
+def test_segmented_fwd_in_place_carry_two_rounds_of_workgroups():
+    """final_state == init_state when the full launch has more workgroups than
+    the GPU holds at once (B=1, H=16, 16 segments: 512 workgroups of one per
+    CU), so segment 0 may start after the last segment has finished: the
+    result must still equal the call with a separate final_state, bit for bit."""
+    inp = I.chunk_inputs(1, 16, 4096, 96, 192, "bf16", seed=97, a_std=0.1, s0_std=0.02)
+    lam_d = to_dev(schedule32(16, 1.0, 2048.0))
+    d = device_inputs(inp)
+    print("  segmented fwd in place B=1 H=16 T=4096 n_segments=16", flush=True)
+    o_a, S_a = Bd.sgla_chunk_fwd_segmented(d["q"], d["k"], d["v"], lam_d, d["a"],
+                                           init_state=d["S0"], n_segments=16, want_final=True)
+    state = d["S0"].clone()
+    o_b, _ = Bd.sgla_chunk_fwd_segmented(d["q"], d["k"], d["v"], lam_d, d["a"], init_state=state,
+                                         final_state=state, n_segments=16)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_b)
+    assert torch.equal(S_a, state)
+
+
 def test_segmented_fwd_long_sequence_sampled_heads():
     """The long-context shape the segments are for: B = 1, H = 16, T = 32768
     (the longest sequence of the packed workload), d_k = 96, d_v = 192, eight
