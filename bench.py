@@ -1,6 +1,6 @@
 """Benchmark of the Simple GLA hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only fwd|fwdbwd|decode|varlen|long|norm|conv]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only fwd|fwdbwd|decode|varlen|long|norm|conv|tiny]
                     [--no-cpu]
 
 Prints ONE JSON line. The headline ("value") is the Laplace-layer forward:
@@ -26,7 +26,9 @@ Also measured in the same run and reported under "secondary" (same clock):
           dg, dgamma out)
   conv:   the conv prologue (depthwise causal width-4 Conv1d + SiLU) at the
           layer's width D=3072: forward B=8 T=2048 bf16 with conv states in and
-          out, and 64 decode steps of 1280 sequences' conv states
+          out, and 64 decode steps of 1280 sequences' conv states, and its
+          gradients (B=8 T=2048)
+  tiny:   the fp32 case B=1 H=2 T=256 d_k=16 d_v=32 chunk 64 (reported only)
 
 "roofline" is for the dominant kernel of the headline step (k_fwd, bf16 forward):
 achieved = algorithmic HBM bytes per launch / mean launch time from HIP events
@@ -115,7 +117,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--only", choices=["fwd", "fwdbwd", "decode", "varlen", "long", "norm", "conv"],
+    ap.add_argument("--only", choices=["fwd", "fwdbwd", "decode", "varlen", "long", "norm", "conv",
+                                       "tiny"],
                     default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--min-warm-s", type=float, default=1.5,
@@ -395,6 +398,26 @@ def bench_norm_bwd(args, B=8, T=2048, n_tiers=4, nsets=2):
             "gbs": bytes_ / (ms * 1e-3) / 1e9}
 
 
+def bench_tiny(args, B=1, Ht=2, T=256, dk=16, dv=32):
+    """The tiny fp32 case (B=1, H=2, T=256, d_k=16, d_v=32, chunk 64, schedule
+    1..256, zero initial state): reported, not a target; it is launch-bound."""
+    import torch
+    from chunked_gated_linear_simple_amd import binding as Bd
+    lam = Bd.sgla_decay_schedule(Ht, 1.0, 256.0).cuda()
+    a = gen((Ht, dk), 71, 0.1)
+    q = gen((B, Ht, T, dk), 700, scale=dk ** -0.5)
+    k = gen((B, Ht, T, dk), 701)
+    v = gen((B, Ht, T, dv), 702)
+    o = torch.empty_like(v)
+    sf = torch.empty((B, Ht, dk, dv), dtype=torch.float32, device="cuda")
+    ms, _ = timed(lambda i: Bd.sgla_chunk_fwd(q, k, v, lam, a, final_state=sf, o=o, chunk=64),
+                  args.steps, args.warmup)
+    toks = B * T
+    bytes_ = B * Ht * T * 4 * (2 * dk + 2 * dv) + B * Ht * dk * dv * 4
+    return {"ms": ms, "tokens": toks, "tok_s": toks / (ms * 1e-3), "bytes": bytes_,
+            "gbs": bytes_ / (ms * 1e-3) / 1e9, "dtype": "f32"}
+
+
 def bench_varlen(args):
     import numpy as np
     import torch
@@ -538,6 +561,8 @@ def main():
     if only in (None, "norm"):
         secondary["head_norm_gate_B8_T2048"] = bench_norm(args)
         secondary["head_norm_gate_bwd_B8_T2048"] = bench_norm_bwd(args)
+    if only in (None, "tiny"):
+        secondary["tiny_fp32_B1_H2_T256"] = bench_tiny(args)
     if only in (None, "conv"):
         secondary["conv_fwd_B8_T2048_D3072"] = bench_conv(args)
         secondary["conv_decode_N1280_D3072_64steps"] = bench_conv_decode(args)
