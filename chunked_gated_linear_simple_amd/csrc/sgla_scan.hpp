@@ -311,6 +311,41 @@ struct LayW {
     static_assert(LDS <= 160 * 1024, "LDS");
 };
 
+// Packed sequences are taken longest first, so that the long ones do not
+// start behind a queue of short ones and finish last: position pos (in block
+// order) runs the sequence of rank pos by length, descending, ties by index.
+// The ranks are a permutation, so every sequence is still run exactly once.
+// Every thread of the workgroup calls this before the waves take their roles
+// (smem is free then); above LPT_MAX sequences the packed order is kept.
+constexpr int LPT_MAX = 256;
+__device__ __forceinline__ int longest_first(const Args& p, int pos, char* smem)
+{
+    const int ns = p.n_units / p.H;
+    if (ns <= 1 || ns > LPT_MAX) return pos;
+    int* lens = reinterpret_cast<int*>(smem);
+    int* pick = lens + LPT_MAX;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < ns; i += NTHREADS_W) {
+        const int s0 = min(max(p.cu[i], 0), p.T);
+        const int s1 = min(max(p.cu[i + 1], s0), p.T);
+        lens[i] = s1 - s0;
+    }
+    __syncthreads();
+    for (int i = tid; i < ns; i += NTHREADS_W) {
+        const int li = lens[i];
+        int r = 0;
+        for (int j = 0; j < ns; ++j) {
+            const int lj = lens[j];
+            r += (lj > li || (lj == li && j < i)) ? 1 : 0;
+        }
+        if (r == pos) *pick = i;
+    }
+    __syncthreads();
+    const int seq = *pick;
+    __syncthreads();
+    return seq;
+}
+
 template <class R>
 __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, char* smem)
 {
@@ -325,6 +360,7 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
     const int H = p.H;
     int seq = unit / H;
     const int h = unit - seq * H;
+    if (p.cu != nullptr) seq = longest_first(p, seq, smem);
     int g = 0;                     // segment
     if (p.nseg > 1) {
         g = p.seg_first + seq % p.seg_count;

@@ -159,6 +159,37 @@ def test_varlen_bf16_fwd_bwd():
     run_bwd_case(inp, lam, 128, cu=cu)
 
 
+def test_varlen_bf16_equal_lengths_and_repeat():
+    """Packed sequences run longest first, equal lengths in packed order: with
+    ties, an empty sequence and a one-token one, every output still matches
+    the oracle, and a second call is bitwise identical."""
+    L = [64, 200, 64, 0, 64, 1, 200]
+    cu = I.cu_from_lengths(L)
+    inp = I.chunk_inputs(1, 4, int(cu[-1]), 96, 192, "bf16", seed=104, a_std=0.1, s0_std=0.02,
+                         n_seq=len(L), with_grad=True, dsf_std=0.02)
+    lam = schedule32(4, 1.0, 2048.0)
+    o1, S1 = run_fwd_case(inp, lam, 128, cu=cu)
+    g1 = run_bwd_case(inp, lam, 128, cu=cu)
+    o2, S2 = run_fwd_case(inp, lam, 128, cu=cu)
+    g2 = run_bwd_case(inp, lam, 128, cu=cu)
+    for x, y in [(o1, o2), (S1, S2)] + list(zip(g1, g2)):
+        assert torch.equal(x, y)
+
+
+def test_varlen_bf16_many_sequences_keep_packed_order():
+    """Above 256 packed sequences the longest-first order is not used: 300
+    short sequences of 0 to 9 tokens, forward and backward, against the oracle
+    on a sample of (sequence, head) units."""
+    L = [(7 * i) % 10 for i in range(300)]
+    cu = I.cu_from_lengths(L)
+    inp = I.chunk_inputs(1, 2, int(cu[-1]), 32, 64, "bf16", seed=105, a_std=0.1, s0_std=0.02,
+                         n_seq=len(L), with_grad=True, dsf_std=0.02)
+    lam = schedule32(2, 1.0, 2048.0)
+    units = [(n, h) for n in (0, 1, 9, 150, 298, 299) for h in (0, 1)]
+    run_fwd_case(inp, lam, 64, cu=cu, units=units)
+    run_bwd_case(inp, lam, 64, cu=cu, units=units)
+
+
 # ------------------------------------------------------------------ invariants
 
 
