@@ -360,7 +360,10 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
     const int H = p.H;
     int seq = unit / H;
     const int h = unit - seq * H;
-    if (p.cu != nullptr) seq = longest_first(p, seq, smem);
+    // (the state-only roles serve dense segments only: no reordering there)
+    if constexpr (R::OUT) {
+        if (p.cu != nullptr) seq = longest_first(p, seq, smem);
+    }
     int g = 0;                     // segment
     if (p.nseg > 1) {
         g = p.seg_first + seq % p.seg_count;
