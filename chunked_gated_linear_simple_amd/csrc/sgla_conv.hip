@@ -441,8 +441,9 @@ hipError_t run_conv_fwd(const void* u, const float* w, const float* b, const flo
 // each sequence meeting the run it walks tau from max(run start, sequence
 // start) to three rows past the run's end (within the sequence), computing
 // dpre_tau and, three rows behind, du. dw and db of the run's rows go to
-// part[run][5][D]. k_conv_bwd_init writes the initial state's gradient (also
-// for empty sequences) and k_conv_wsum adds the run partials in a fixed order.
+// part[run][5][D]. Extra blocks of the same launch write the initial states'
+// gradient (also for empty sequences), and k_conv_wsum adds the run partials
+// in a fixed order.
 constexpr int BWD_RUN = 64;
 constexpr int BWD_THREADS = 128;
 constexpr int BWD_PF = 4;  // rows of u and dy in flight per thread
@@ -492,13 +493,60 @@ __device__ __forceinline__ float dsilu_f(float x)
     return sg * fmaf(x, 1.0f - sg, 1.0f);
 }
 
+// The initial state's gradient of sequence n: d_init[i] = sum_{j <= i} w_j
+// dpre_{i-j} (rows inside the sequence) + d_final[i - L] when the final state
+// reaches back into the initial state (L < 3). One thread per channel; block
+// idx takes sequence idx / ceil(D / BWD_THREADS) and the channel block after.
+template <typename E>
+__device__ __forceinline__ void conv_bwd_init_block(const E* __restrict__ u, const E* __restrict__ dy,
+                                                    const float* __restrict__ w, const float* __restrict__ b,
+                                                    const float* __restrict__ init,
+                                                    const float* __restrict__ dfin, float* __restrict__ dinit,
+                                                    const Seqs& sq, int D, int idx)
+{
+    const int iblk = (D + BWD_THREADS - 1) / BWD_THREADS;
+    const int n = idx / iblk;
+    const int c = (idx - n * iblk) * BWD_THREADS + threadIdx.x;
+    if (c >= D) return;
+    int s0, s1;
+    sq.range(n, s0, s1);
+    const int L = s1 - s0;
+    const f32x4 wv = *reinterpret_cast<const f32x4*>(w + (size_t)c * 4);
+    const float bc = (b != nullptr) ? b[c] : 0.0f;
+    // x_{-3..2} of this channel and dpre_{0..2}
+    float x[6], p[3];
+    for (int i = 0; i < 3; ++i) x[i] = (init != nullptr) ? init[((size_t)n * 3 + i) * D + c] : 0.0f;
+    for (int t = 0; t < 3; ++t) {
+        float xu = 0.0f, g = 0.0f;
+        if (t < L) {
+            xu = ld_elem(u, (size_t)(s0 + t) * D + c);
+            g = ld_elem(dy, (size_t)(s0 + t) * D + c);
+        }
+        x[3 + t] = xu;
+        const float pre = bc + wv[0] * x[t] + wv[1] * x[t + 1] + wv[2] * x[t + 2] + wv[3] * xu;
+        p[t] = (t < L) ? g * dsilu_f(pre) : 0.0f;
+    }
+    for (int i = 0; i < 3; ++i) {
+        float acc = 0.0f;
+        for (int j = 0; j <= i; ++j) acc += wv[j] * p[i - j];
+        if (dfin != nullptr && i - L >= 0) acc += dfin[((size_t)n * 3 + (i - L)) * D + c];
+        dinit[((size_t)n * 3 + i) * D + c] = acc;
+    }
+}
+
 template <typename E>
 __global__ __launch_bounds__(BWD_THREADS) void k_conv_bwd(const E* __restrict__ u, const E* __restrict__ dy,
                                                           const float* __restrict__ w, const float* __restrict__ b,
                                                           const float* __restrict__ init,
                                                           const float* __restrict__ dfin, E* __restrict__ du,
-                                                          float* __restrict__ part, Seqs sq, int D, int nblk)
+                                                          float* __restrict__ part, float* __restrict__ dinit,
+                                                          Seqs sq, int D, int nblk, int n_main)
 {
+    // blocks past the runs' ones write the initial states' gradient
+    if ((int)blockIdx.x >= n_main) {
+        conv_bwd_init_block<E>(u, dy, w, b, init, dfin, dinit, sq, D, (int)blockIdx.x - n_main);
+        return;
+    }
     typedef Q2<E> G;
     constexpr int V = G::V;
     // the channel blocks of one run are consecutive blocks, so the rows they
@@ -634,46 +682,6 @@ __global__ __launch_bounds__(BWD_THREADS) void k_conv_bwd(const E* __restrict__ 
     }
 }
 
-// The initial state's gradient of sequence n: d_init[i] = sum_{j <= i} w_j
-// dpre_{i-j} (rows inside the sequence) + d_final[i - L] when the final state
-// reaches back into the initial state (L < 3). One thread per channel.
-template <typename E>
-__global__ __launch_bounds__(BWD_THREADS) void k_conv_bwd_init(const E* __restrict__ u, const E* __restrict__ dy,
-                                                               const float* __restrict__ w,
-                                                               const float* __restrict__ b,
-                                                               const float* __restrict__ init,
-                                                               const float* __restrict__ dfin,
-                                                               float* __restrict__ dinit, Seqs sq, int D)
-{
-    const int c = blockIdx.y * BWD_THREADS + threadIdx.x;
-    if (c >= D) return;
-    const int n = blockIdx.x;
-    int s0, s1;
-    sq.range(n, s0, s1);
-    const int L = s1 - s0;
-    const f32x4 wv = *reinterpret_cast<const f32x4*>(w + (size_t)c * 4);
-    const float bc = (b != nullptr) ? b[c] : 0.0f;
-    // x_{-3..2} of this channel and dpre_{0..2}
-    float x[6], p[3];
-    for (int i = 0; i < 3; ++i) x[i] = (init != nullptr) ? init[((size_t)n * 3 + i) * D + c] : 0.0f;
-    for (int t = 0; t < 3; ++t) {
-        float xu = 0.0f, g = 0.0f;
-        if (t < L) {
-            xu = ld_elem(u, (size_t)(s0 + t) * D + c);
-            g = ld_elem(dy, (size_t)(s0 + t) * D + c);
-        }
-        x[3 + t] = xu;
-        const float pre = bc + wv[0] * x[t] + wv[1] * x[t + 1] + wv[2] * x[t + 2] + wv[3] * xu;
-        p[t] = (t < L) ? g * dsilu_f(pre) : 0.0f;
-    }
-    for (int i = 0; i < 3; ++i) {
-        float acc = 0.0f;
-        for (int j = 0; j <= i; ++j) acc += wv[j] * p[i - j];
-        if (dfin != nullptr && i - L >= 0) acc += dfin[((size_t)n * 3 + (i - L)) * D + c];
-        dinit[((size_t)n * 3 + i) * D + c] = acc;
-    }
-}
-
 constexpr int WSUM_BATCH = 8;
 
 // dw[c][j] and db[c]: the run partials, split 64 ways (thread k of a block of
@@ -722,19 +730,13 @@ hipError_t run_conv_bwd(const void* u, const void* dy, const float* w, const flo
     const int n_runs = (sq.S + BWD_RUN - 1) / BWD_RUN;
     const int groups = D / Q2<E>::V;
     const int nblk = (groups + BWD_THREADS - 1) / BWD_THREADS;
-    hipLaunchKernelGGL(k_conv_bwd<E>, dim3(n_runs * nblk), dim3(BWD_THREADS), 0, stream,
+    const int n_main = n_runs * nblk;
+    const int n_init = (dinit != nullptr) ? n_seq * ((D + BWD_THREADS - 1) / BWD_THREADS) : 0;
+    hipLaunchKernelGGL(k_conv_bwd<E>, dim3(n_main + n_init), dim3(BWD_THREADS), 0, stream,
                        reinterpret_cast<const E*>(u), reinterpret_cast<const E*>(dy), w, b, init, dfin,
-                       reinterpret_cast<E*>(du), part, sq, D, nblk);
+                       reinterpret_cast<E*>(du), part, dinit, sq, D, nblk, n_main);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (dinit != nullptr) {
-        hipLaunchKernelGGL(k_conv_bwd_init<E>, dim3(n_seq, (D + BWD_THREADS - 1) / BWD_THREADS), dim3(BWD_THREADS), 0,
-                           stream,
-                           reinterpret_cast<const E*>(u), reinterpret_cast<const E*>(dy), w, b, init, dfin, dinit, sq,
-                           D);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
     hipLaunchKernelGGL(k_conv_wsum, dim3((D + 15) / 16, 5), dim3(1024), 0, stream, part, dw, db, n_runs, D);
     return hipGetLastError();
 }
