@@ -518,7 +518,16 @@ def cpu_baseline(min_seconds=10.0, B=8, T=2048):
             if dt >= min_seconds:
                 break
     tokens = passes * B * T
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "host_cpus": os.cpu_count(), "cpu_model": model,
             "sample": f"the full headline forward (B={B}, H={H}, T={T}: {B * H} sequence-head "
                       f"units) run {passes} times in {dt:.1f} s; fp64 token recurrence, one "
                       f"thread per unit"}
