@@ -188,3 +188,12 @@ def test_segmented_bwd_long_sequence_sampled_heads():
     inp = I.chunk_inputs(1, 16, 16384, 96, 192, "bf16", seed=99, a_std=0.1, s0_std=0.02,
                          with_grad=True, dsf_std=0.02)
     run_segmented_bwd_case(inp, schedule32(16, 1.0, 2048.0), 8, units=[(0, 0), (0, 15)])
+
+
+def test_segmented_bwd_bench_shape_sampled_heads():
+    """The backward as the long-sequence benchmark runs it: B = 1, H = 16,
+    T = 32768, four segments; the oracle checks the shortest- and the
+    longest-memory heads."""
+    inp = I.chunk_inputs(1, 16, 32768, 96, 192, "bf16", seed=101, a_std=0.1, s0_std=0.02,
+                         with_grad=True, dsf_std=0.02)
+    run_segmented_bwd_case(inp, schedule32(16, 1.0, 2048.0), 4, units=[(0, 0), (0, 15)])
