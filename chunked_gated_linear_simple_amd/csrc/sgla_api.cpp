@@ -140,6 +140,23 @@ sgla_status sgla_decay_schedule(int H, double t_min, double t_max, float* lambda
     return ok();
 }
 
+// final_state (n_seq states) may be init_state itself (in-place carry) but may
+// not overlap it otherwise, nor q, k, v or o: workgroups read one sequence's
+// initial state while others write their final states.
+static sgla_status check_final_state(const float* final_state, const float* init_state, const void* q,
+                                     const void* k, const void* v, const void* o, int n_seq, int H,
+                                     int d_k, int d_v, size_t nqk, size_t nvo)
+{
+    if (final_state == nullptr) return SGLA_OK;
+    const size_t nst = (size_t)n_seq * H * d_k * d_v * sizeof(float);
+    if (final_state != init_state && overlaps(final_state, nst, init_state, nst))
+        return fail(SGLA_ERR_INVALID_ARG, "final_state must equal init_state or not overlap it");
+    if (overlaps(final_state, nst, q, nqk) || overlaps(final_state, nst, k, nqk) ||
+        overlaps(final_state, nst, v, nvo) || overlaps(final_state, nst, o, nvo))
+        return fail(SGLA_ERR_INVALID_ARG, "final_state must not overlap q, k, v or o");
+    return SGLA_OK;
+}
+
 sgla_status sgla_chunk_fwd(const void* q, const void* k, const void* v, const float* lambda,
                            const float* a, const float* init_state, float* final_state, void* o,
                            const int32_t* cu_seqlens, int n_seq, int B, int H, int T, int d_k,
@@ -156,6 +173,8 @@ sgla_status sgla_chunk_fwd(const void* q, const void* k, const void* v, const fl
     const size_t nqk = (size_t)B * H * T * d_k * es, nvo = (size_t)B * H * T * d_v * es;
     if (overlaps(o, nvo, q, nqk) || overlaps(o, nvo, k, nqk) || overlaps(o, nvo, v, nvo))
         return fail(SGLA_ERR_INVALID_ARG, "o must not alias q, k or v");
+    st = check_final_state(final_state, init_state, q, k, v, o, p.n_seq, H, d_k, d_v, nqk, nvo);
+    if (st != SGLA_OK) return st;
     hipError_t e = sgla::launch_chunk_fwd(p, q, k, v, init_state, final_state, o,
                                           reinterpret_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return fail(SGLA_ERR_HIP, "chunk_fwd launch: %s", hipGetErrorString(e));
@@ -191,6 +210,15 @@ sgla_status sgla_chunk_fwd_segmented(const void* q, const void* k, const void* v
     const size_t nqk = (size_t)B * H * T * d_k * 2, nvo = (size_t)B * H * T * d_v * 2;
     if (overlaps(o, nvo, q, nqk) || overlaps(o, nvo, k, nqk) || overlaps(o, nvo, v, nvo))
         return fail(SGLA_ERR_INVALID_ARG, "o must not alias q, k or v");
+    st = check_final_state(final_state, init_state, q, k, v, o, p.n_seq, H, d_k, d_v, nqk, nvo);
+    if (st != SGLA_OK) return st;
+    {
+        const size_t nst = (size_t)p.n_seq * H * d_k * d_v * sizeof(float);
+        if (overlaps(workspace, need, q, nqk) || overlaps(workspace, need, k, nqk) ||
+            overlaps(workspace, need, v, nvo) || overlaps(workspace, need, o, nvo) ||
+            overlaps(workspace, need, init_state, nst) || overlaps(workspace, need, final_state, nst))
+            return fail(SGLA_ERR_WORKSPACE, "workspace must not overlap any other argument");
+    }
     // segments of whole 64-token tiles (the tile of the bf16 kernels)
     const int tiles = (T + 63) / 64;
     const int g = n_segments < tiles ? n_segments : tiles;

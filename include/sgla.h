@@ -110,7 +110,9 @@ sgla_status sgla_decay_schedule(int H, double t_min, double t_max, float* lambda
  * a:           [H, d_k] self-augmentation scale (aug_balance), or NULL = 0.
  * init_state:  [N, H, d_k, d_v] state before the first token, or NULL = 0.
  * final_state: [N, H, d_k, d_v] state after the last token, or NULL (not
- *              written). May equal init_state (in-place carry).
+ *              written). May equal init_state (in-place carry); any other
+ *              overlap with init_state, q, k, v or o is rejected
+ *              (SGLA_ERR_INVALID_ARG).
  * o:           output [.., d_v] (dtype). Must not alias any input.
  * cu_seqlens:  packed-sequence offsets (see layouts) or NULL (dense).
  * n_seq:       number of sequences when cu_seqlens != NULL; ignored otherwise.
@@ -161,7 +163,8 @@ size_t sgla_chunk_fwd_segmented_workspace_bytes(int B, int H, int d_k, int d_v, 
  * workspace:   device buffer of at least
  *              sgla_chunk_fwd_segmented_workspace_bytes(B, H, d_k, d_v,
  *              n_segments) bytes, 16-byte aligned, owned by the caller, not
- *              overlapping any other argument; contents on entry do not
+ *              overlapping any other argument (SGLA_ERR_WORKSPACE if it
+ *              overlaps q, k, v, o or a state); contents on entry do not
  *              matter and are clobbered.
  * Errors: as sgla_chunk_fwd, plus SGLA_ERR_INVALID_ARG for n_segments < 1
  * and SGLA_ERR_WORKSPACE if workspace is NULL, unaligned or too small.

@@ -108,6 +108,10 @@ FWD_BAD = [
     ("packed with B=2", dict(cu=P["cu"], n_seq=3), B.SGLA_ERR_INVALID_ARG),
     ("packed n_seq 0", dict(cu=P["cu"], n_seq=0, B=1), B.SGLA_ERR_INVALID_ARG),
     ("cu misaligned", dict(cu=P["cu"] + 4, n_seq=2, B=1), B.SGLA_ERR_INVALID_ARG),
+    ("final overlaps init", dict(sf=P["s0"] + 1024), B.SGLA_ERR_INVALID_ARG),
+    ("init overlaps final", dict(s0=P["sf"] + 1024), B.SGLA_ERR_INVALID_ARG),
+    ("final overlaps v", dict(sf=P["v"] + 4096), B.SGLA_ERR_INVALID_ARG),
+    ("final aliases o", dict(sf=P["o"]), B.SGLA_ERR_INVALID_ARG),
 ]
 
 
@@ -138,6 +142,10 @@ SEG_BAD = [
     ("workspace misaligned", dict(ws=P["ws"] + 8), B.SGLA_ERR_WORKSPACE),
     ("o aliases k", dict(o=P["k"]), B.SGLA_ERR_INVALID_ARG),
     ("final misaligned", dict(sf=P["sf"] + 4), B.SGLA_ERR_INVALID_ARG),
+    ("final overlaps init", dict(sf=P["s0"] + 2048), B.SGLA_ERR_INVALID_ARG),
+    ("final aliases q", dict(sf=P["q"]), B.SGLA_ERR_INVALID_ARG),
+    ("workspace overlaps o", dict(ws=P["o"] + 4096), B.SGLA_ERR_WORKSPACE),
+    ("workspace overlaps init", dict(ws=P["s0"]), B.SGLA_ERR_WORKSPACE),
 ]
 
 
