@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstring>
 
 #include "sgla_internal.h"
 
@@ -157,6 +158,45 @@ static sgla_status check_final_state(const float* final_state, const float* init
     return SGLA_OK;
 }
 
+// Every buffer the backward writes (outputs, state gradient, workspace) must
+// be disjoint from every buffer it reads and from every other one it writes.
+struct Span {
+    const void* p;
+    size_t n;
+    const char* name;
+};
+static sgla_status check_bwd_buffers(const Span* wr, int nw, const Span* rd, int nr)
+{
+    for (int i = 0; i < nw; ++i) {
+        const sgla_status code = std::strcmp(wr[i].name, "workspace") == 0 ? SGLA_ERR_WORKSPACE
+                                                                          : SGLA_ERR_INVALID_ARG;
+        for (int j = 0; j < nr; ++j)
+            if (overlaps(wr[i].p, wr[i].n, rd[j].p, rd[j].n))
+                return fail(code, "%s must not overlap %s", wr[i].name, rd[j].name);
+        for (int j = 0; j < i; ++j)
+            if (overlaps(wr[i].p, wr[i].n, wr[j].p, wr[j].n))
+                return fail(code, "%s must not overlap %s", wr[i].name, wr[j].name);
+    }
+    return SGLA_OK;
+}
+
+static sgla_status check_bwd_all(const void* q, const void* k, const void* v, const void* dO,
+                                 const float* lambda, const float* a, const float* init_state,
+                                 const float* d_final_state, void* dq, void* dk, void* dv, float* da,
+                                 float* d_init_state, void* workspace, size_t ws_bytes, int n_seq, int B,
+                                 int H, int T, int d_k, int d_v, size_t es)
+{
+    const size_t nqk = (size_t)B * H * T * d_k * es, nvo = (size_t)B * H * T * d_v * es;
+    const size_t nst = (size_t)n_seq * H * d_k * d_v * sizeof(float);
+    const size_t nda = (size_t)H * d_k * sizeof(float);
+    const Span rd[8] = {{q, nqk, "q"}, {k, nqk, "k"}, {v, nvo, "v"}, {dO, nvo, "dO"},
+                        {lambda, (size_t)H * sizeof(float), "lambda"}, {a, nda, "a"},
+                        {init_state, nst, "init_state"}, {d_final_state, nst, "d_final_state"}};
+    const Span wr[6] = {{dq, nqk, "dq"}, {dk, nqk, "dk"}, {dv, nvo, "dv"}, {da, nda, "da"},
+                        {d_init_state, nst, "d_init_state"}, {workspace, ws_bytes, "workspace"}};
+    return check_bwd_buffers(wr, 6, rd, 8);
+}
+
 sgla_status sgla_chunk_fwd(const void* q, const void* k, const void* v, const float* lambda,
                            const float* a, const float* init_state, float* final_state, void* o,
                            const int32_t* cu_seqlens, int n_seq, int B, int H, int T, int d_k,
@@ -270,25 +310,9 @@ sgla_status sgla_chunk_bwd_segmented(const void* q, const void* k, const void* v
     if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
         return fail(SGLA_ERR_WORKSPACE, "workspace needs %zu bytes, 16-byte aligned (got %zu at %p)",
                     need, workspace_bytes, workspace);
-    const size_t nqk = (size_t)B * H * T * d_k * 2, nvo = (size_t)B * H * T * d_v * 2;
-    const void* ins[4] = {q, k, v, dO};
-    const size_t insz[4] = {nqk, nqk, nvo, nvo};
-    void* outs[3] = {dq, dk, dv};
-    const size_t outsz[3] = {nqk, nqk, nvo};
-    for (int i = 0; i < 3; ++i) {
-        for (int j = 0; j < 4; ++j)
-            if (overlaps(outs[i], outsz[i], ins[j], insz[j]))
-                return fail(SGLA_ERR_INVALID_ARG, "dq, dk and dv must not alias q, k, v or dO");
-        for (int j = 0; j < i; ++j)
-            if (overlaps(outs[i], outsz[i], outs[j], outsz[j]))
-                return fail(SGLA_ERR_INVALID_ARG, "dq, dk and dv must not overlap each other");
-    }
-    {
-        // the state gradient written at the front must not overlap a state read elsewhere
-        const size_t nst = (size_t)p.n_seq * H * d_k * d_v * sizeof(float);
-        if (overlaps(d_init_state, nst, d_final_state, nst) || overlaps(d_init_state, nst, init_state, nst))
-            return fail(SGLA_ERR_INVALID_ARG, "d_init_state must not overlap d_final_state or init_state");
-    }
+    st = check_bwd_all(q, k, v, dO, lambda, a, init_state, d_final_state, dq, dk, dv, da, d_init_state,
+                       workspace, need, p.n_seq, B, H, T, d_k, d_v, 2);
+    if (st != SGLA_OK) return st;
     const int tiles = (T + 63) / 64;
     const int g = n_segments < tiles ? n_segments : tiles;
     const int seg_len = ((tiles + g - 1) / g) * 64;
@@ -339,22 +363,9 @@ sgla_status sgla_chunk_bwd(const void* q, const void* k, const void* v, const vo
     if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
         return fail(SGLA_ERR_WORKSPACE, "workspace needs %zu bytes, 16-byte aligned (got %zu at %p)",
                     need, workspace_bytes, workspace);
-    const size_t es = (dtype == SGLA_BF16) ? 2 : 4;
-    const size_t nqk = (size_t)B * H * T * d_k * es, nvo = (size_t)B * H * T * d_v * es;
-    const void* ins[4] = {q, k, v, dO};
-    const size_t insz[4] = {nqk, nqk, nvo, nvo};
-    void* outs[3] = {dq, dk, dv};
-    const size_t outsz[3] = {nqk, nqk, nvo};
-    for (int i = 0; i < 3; ++i)
-        for (int j = 0; j < 4; ++j)
-            if (overlaps(outs[i], outsz[i], ins[j], insz[j]))
-                return fail(SGLA_ERR_INVALID_ARG, "dq, dk and dv must not alias q, k, v or dO");
-    {
-        // the state gradient written at the front must not overlap a state read elsewhere
-        const size_t nst = (size_t)p.n_seq * H * d_k * d_v * sizeof(float);
-        if (overlaps(d_init_state, nst, d_final_state, nst) || overlaps(d_init_state, nst, init_state, nst))
-            return fail(SGLA_ERR_INVALID_ARG, "d_init_state must not overlap d_final_state or init_state");
-    }
+    st = check_bwd_all(q, k, v, dO, lambda, a, init_state, d_final_state, dq, dk, dv, da, d_init_state,
+                       workspace, need, p.n_seq, B, H, T, d_k, d_v, (dtype == SGLA_BF16) ? 2 : 4);
+    if (st != SGLA_OK) return st;
     hipError_t e = sgla::launch_chunk_bwd(p, q, k, v, dO, init_state, d_final_state, dq, dk, dv,
                                           da, d_init_state, reinterpret_cast<float*>(workspace),
                                           reinterpret_cast<hipStream_t>(hip_stream));

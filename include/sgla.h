@@ -257,8 +257,11 @@ size_t sgla_chunk_bwd_workspace_bytes(int N, int H, int d_k);
  * workspace:   device buffer of at least sgla_chunk_bwd_workspace_bytes()
  *              bytes, 16-byte aligned, owned by the caller; its contents on
  *              entry do not matter and are clobbered.
- * Errors: as sgla_chunk_fwd, plus SGLA_ERR_WORKSPACE if workspace is NULL or
- * too small.
+ * Every buffer written (dq, dk, dv, da, d_init_state, workspace) must be
+ * disjoint from every buffer read and from every other one written.
+ * Errors: as sgla_chunk_fwd, plus SGLA_ERR_WORKSPACE if workspace is NULL,
+ * too small or overlapping another argument, and SGLA_ERR_INVALID_ARG for any
+ * other overlap above.
  */
 sgla_status sgla_chunk_bwd(const void* q, const void* k, const void* v, const void* dO,
                            const float* lambda, const float* a,

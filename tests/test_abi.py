@@ -185,6 +185,12 @@ BWD_BAD = [
     ("dv aliases v", dict(dv=P["v"]), B.SGLA_ERR_INVALID_ARG),
     ("d_init aliases d_final", dict(ds0=P["sf"]), B.SGLA_ERR_INVALID_ARG),
     ("d_init overlaps init", dict(ds0=P["s0"] + 4096), B.SGLA_ERR_INVALID_ARG),
+    ("dk overlaps dq", dict(dk=P["dq"] + 4096), B.SGLA_ERR_INVALID_ARG),
+    ("da inside dv", dict(da=P["dv"] + 4096), B.SGLA_ERR_INVALID_ARG),
+    ("da overlaps a", dict(da=P["a"]), B.SGLA_ERR_INVALID_ARG),
+    ("d_init overlaps dq", dict(ds0=P["dq"]), B.SGLA_ERR_INVALID_ARG),
+    ("workspace overlaps q", dict(ws=P["q"] + 4096), B.SGLA_ERR_WORKSPACE),
+    ("workspace overlaps da", dict(ws=P["da"]), B.SGLA_ERR_WORKSPACE),
     ("unsupported dims", dict(d_v=200), B.SGLA_ERR_UNSUPPORTED),
     ("T zero", dict(T=0), B.SGLA_ERR_INVALID_ARG),
 ]
@@ -441,6 +447,9 @@ SEGB_BAD = [
     ("dq aliases dO", dict(dq=P["dO"]), B.SGLA_ERR_INVALID_ARG),
     ("dv overlaps dk", dict(dv=P["dk"] + 1024), B.SGLA_ERR_INVALID_ARG),
     ("d_init aliases d_final", dict(ds0=P["sf"]), B.SGLA_ERR_INVALID_ARG),
+    ("da overlaps d_init", dict(da=P["ds0"] + 4096), B.SGLA_ERR_INVALID_ARG),
+    ("workspace overlaps dv", dict(ws=P["dv"]), B.SGLA_ERR_WORKSPACE),
+    ("workspace overlaps init", dict(ws=P["s0"] + 4096), B.SGLA_ERR_WORKSPACE),
 ]
 
 
