@@ -158,14 +158,15 @@ static sgla_status check_final_state(const float* final_state, const float* init
     return SGLA_OK;
 }
 
-// Every buffer the backward writes (outputs, state gradient, workspace) must
-// be disjoint from every buffer it reads and from every other one it writes.
+// Every buffer a call writes must be disjoint from every buffer it reads and
+// from every other one it writes (an in-place buffer is listed once, as
+// written).
 struct Span {
     const void* p;
     size_t n;
     const char* name;
 };
-static sgla_status check_bwd_buffers(const Span* wr, int nw, const Span* rd, int nr)
+static sgla_status check_disjoint(const Span* wr, int nw, const Span* rd, int nr)
 {
     for (int i = 0; i < nw; ++i) {
         const sgla_status code = std::strcmp(wr[i].name, "workspace") == 0 ? SGLA_ERR_WORKSPACE
@@ -194,7 +195,7 @@ static sgla_status check_bwd_all(const void* q, const void* k, const void* v, co
                         {init_state, nst, "init_state"}, {d_final_state, nst, "d_final_state"}};
     const Span wr[6] = {{dq, nqk, "dq"}, {dk, nqk, "dk"}, {dv, nvo, "dv"}, {da, nda, "da"},
                         {d_init_state, nst, "d_init_state"}, {workspace, ws_bytes, "workspace"}};
-    return check_bwd_buffers(wr, 6, rd, 8);
+    return check_disjoint(wr, 6, rd, 8);
 }
 
 sgla_status sgla_chunk_fwd(const void* q, const void* k, const void* v, const float* lambda,
@@ -395,6 +396,17 @@ sgla_status sgla_decode_step(const void* q, const void* k, const void* v, const 
     if (!((d_k == 96 && d_v == 192) || (d_k == 16 && d_v == 32)))
         return fail(SGLA_ERR_UNSUPPORTED, "decode supports (d_k, d_v) = (96, 192) or (16, 32), got (%d, %d)",
                     d_k, d_v);
+    {
+        const size_t es = (dtype == SGLA_BF16) ? 2 : 4;
+        const size_t nqk = (size_t)N * H * d_k * es, nvo = (size_t)N * H * d_v * es;
+        const Span rd[6] = {{q, nqk, "q"}, {k, nqk, "k"}, {v, nvo, "v"},
+                            {lambda, (size_t)H * sizeof(float), "lambda"},
+                            {a, (size_t)H * d_k * sizeof(float), "a"},
+                            {slot, (size_t)N * sizeof(int32_t), "slot"}};
+        const Span wr[2] = {{state, (size_t)P * H * d_k * d_v * sizeof(float), "state"}, {o, nvo, "o"}};
+        const sgla_status st = check_disjoint(wr, 2, rd, 6);
+        if (st != SGLA_OK) return st;
+    }
     hipError_t e = sgla::launch_decode_step(dtype == SGLA_BF16, q, k, v, lambda, a, state, slot, o,
                                             N, P, H, d_k, d_v,
                                             reinterpret_cast<hipStream_t>(hip_stream));

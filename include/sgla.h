@@ -286,6 +286,8 @@ sgla_status sgla_chunk_bwd(const void* q, const void* k, const void* v, const vo
  *          an entry outside [0, P) skips that sequence and writes NaN to its o.
  * Supported: d_k = 96, d_v = 192 or d_k = 16, d_v = 32, either dtype.
  * The output of one sequence does not depend on N or on the other sequences.
+ * state and o must be disjoint from each other and from q, k, v, lambda, a
+ * and slot (SGLA_ERR_INVALID_ARG otherwise).
  */
 sgla_status sgla_decode_step(const void* q, const void* k, const void* v,
                              const float* lambda, const float* a,

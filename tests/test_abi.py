@@ -223,6 +223,10 @@ DEC_BAD = [
     ("slot misaligned", dict(slot=P["slot"] + 4), B.SGLA_ERR_INVALID_ARG),
     ("dims", dict(d_k=64, d_v=64), B.SGLA_ERR_UNSUPPORTED),
     ("dtype", dict(dt=3), B.SGLA_ERR_INVALID_ARG),
+    ("o inside state", dict(o=P["state"] + 4096), B.SGLA_ERR_INVALID_ARG),
+    ("state aliases q", dict(state=P["q"]), B.SGLA_ERR_INVALID_ARG),
+    ("o aliases v", dict(o=P["v"]), B.SGLA_ERR_INVALID_ARG),
+    ("state overlaps slot", dict(slot=P["state"] + 1024), B.SGLA_ERR_INVALID_ARG),
 ]
 
 
