@@ -500,6 +500,16 @@ sgla_status sgla_conv_bwd(const void* u, const float* w, const float* b, const f
     if (overlaps(d_init_state, ns, du, nb) || overlaps(d_init_state, ns, init_state, ns) ||
         overlaps(d_init_state, ns, d_final_state, ns))
         return fail(SGLA_ERR_INVALID_ARG, "d_init_state must not overlap du, init_state or d_final_state");
+    {
+        const Span rd[6] = {{u, nb, "u"}, {dy, nb, "dy"}, {w, (size_t)D * 4 * sizeof(float), "w"},
+                            {b, (size_t)D * sizeof(float), "b"}, {init_state, ns, "init_state"},
+                            {d_final_state, ns, "d_final_state"}};
+        const Span wr[5] = {{du, nb, "du"}, {dw, (size_t)D * 4 * sizeof(float), "dw"},
+                            {db, (size_t)D * sizeof(float), "db"}, {d_init_state, ns, "d_init_state"},
+                            {workspace, need, "workspace"}};
+        const sgla_status st = check_disjoint(wr, 5, rd, 6);
+        if (st != SGLA_OK) return st;
+    }
     hipError_t e = sgla::launch_conv_bwd(dtype == SGLA_BF16, u, dy, w, b, init_state, d_final_state, du, dw, db,
                                          d_init_state, cu_seqlens, n_seq, B, T, D,
                                          reinterpret_cast<float*>(workspace), reinterpret_cast<hipStream_t>(hip_stream));
@@ -611,6 +621,16 @@ sgla_status sgla_head_norm_gate_bwd(const void* o, const void* g, const float* g
     if (dg != dout && overlaps(dg, nb, dout, nb))
         return fail(SGLA_ERR_INVALID_ARG, "dg must equal dout or not overlap it");
     if (overlaps(d_o, nb, dg, nb)) return fail(SGLA_ERR_INVALID_ARG, "d_o must not overlap dg");
+    if (dgamma != nullptr) {
+        // (dg may be dout itself, so the two bf16 outputs are checked above)
+        const size_t ng = (size_t)n_tiers * d_v * sizeof(float);
+        const Span rd[6] = {{o, nb, "o"}, {g, nb, "g"}, {dout, nb, "dout"}, {gamma, ng, "gamma"},
+                            {d_o, nb, "d_o"}, {dg, nb, "dg"}};
+        const Span wr[2] = {{dgamma, ng, "dgamma"},
+                            {workspace, sgla_head_norm_gate_bwd_workspace_bytes(B, H, T, d_v), "workspace"}};
+        const sgla_status st = check_disjoint(wr, 2, rd, 6);
+        if (st != SGLA_OK) return st;
+    }
     hipError_t e = sgla::launch_head_norm_gate_bwd(dtype == SGLA_BF16, o, g, gamma, dout, d_o, dg, dgamma,
                                                    reinterpret_cast<float*>(workspace), B, H, T, d_v, n_tiers,
                                                    eps, reinterpret_cast<hipStream_t>(hip_stream));

@@ -356,7 +356,11 @@ size_t sgla_conv_bwd_workspace_bytes(int B, int T, int D);
  *                init_state or d_final_state.
  * workspace:     device buffer of at least sgla_conv_bwd_workspace_bytes(B,
  *                T, D) bytes, 16-byte aligned, owned by the caller, clobbered.
- * Errors: as sgla_conv_fwd, plus SGLA_ERR_WORKSPACE.
+ * du, dw, db, d_init_state and workspace must be disjoint from every input
+ * and from each other.
+ * Errors: as sgla_conv_fwd, plus SGLA_ERR_WORKSPACE (workspace NULL,
+ * misaligned, too small or overlapping another argument) and
+ * SGLA_ERR_INVALID_ARG for any other overlap above.
  */
 sgla_status sgla_conv_bwd(const void* u, const float* w, const float* b, const float* init_state,
                           const void* dy, const float* d_final_state, void* du, float* dw, float* db,
@@ -442,8 +446,11 @@ size_t sgla_head_norm_gate_bwd_workspace_bytes(int B, int H, int T, int d_v);
  *          sgla_head_norm_gate_bwd_workspace_bytes(B, H, T, d_v) bytes,
  *          16-byte aligned, owned by the caller, clobbered; needed only when
  *          dgamma is not NULL (may be NULL otherwise).
+ * dgamma and workspace must be disjoint from o, g, gamma, dout, d_o, dg and
+ * each other.
  * Errors: as sgla_head_norm_gate, plus SGLA_ERR_WORKSPACE (dgamma wanted
- * and workspace NULL, misaligned or too small).
+ * and workspace NULL, misaligned, too small or overlapping another argument)
+ * and SGLA_ERR_INVALID_ARG for any other overlap above.
  */
 sgla_status sgla_head_norm_gate_bwd(const void* o, const void* g, const float* gamma, const void* dout,
                                     void* d_o, void* dg, float* dgamma, int B, int H, int T, int d_v,

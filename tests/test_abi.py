@@ -374,6 +374,9 @@ HNGB_BAD = [
     ("dg aliases g", dict(dg=P["ng"]), B.SGLA_ERR_INVALID_ARG),
     ("dg overlaps dout", dict(dg=P["ndout"] + 256), B.SGLA_ERR_INVALID_ARG),
     ("d_o overlaps dg", dict(do=P["ndg"] + 512), B.SGLA_ERR_INVALID_ARG),
+    ("dgamma aliases gamma", dict(dgm=P["gm"]), B.SGLA_ERR_INVALID_ARG),
+    ("dgamma inside d_o", dict(dgm=P["ndo"] + 1024), B.SGLA_ERR_INVALID_ARG),
+    ("workspace overlaps dg", dict(ws=P["ndg"]), B.SGLA_ERR_WORKSPACE),
 ]
 
 
@@ -413,6 +416,10 @@ CBWD_BAD = [
     ("du aliases u", dict(du=P["u"]), B.SGLA_ERR_INVALID_ARG),
     ("du overlaps dy", dict(du=P["dO"] + 4096), B.SGLA_ERR_INVALID_ARG),
     ("d_init aliases init", dict(ds0=P["s0"]), B.SGLA_ERR_INVALID_ARG),
+    ("dw inside du", dict(dw=P["y"] + 4096), B.SGLA_ERR_INVALID_ARG),
+    ("db aliases w", dict(db=P["w"]), B.SGLA_ERR_INVALID_ARG),
+    ("d_init overlaps dw", dict(ds0=P["dq"]), B.SGLA_ERR_INVALID_ARG),
+    ("workspace overlaps du", dict(ws=P["y"]), B.SGLA_ERR_WORKSPACE),
 ]
 
 
