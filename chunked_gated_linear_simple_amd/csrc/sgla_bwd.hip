@@ -101,9 +101,8 @@ hipError_t run_bwd(const Args& av, const Args& aq, const Args& ak, hipStream_t s
 // bf16 backward of dense sequences cut into nseg >= 2 segments (see
 // sgla_chunk_bwd_segmented). ws holds four [n_seq][nseg][H][d_k][d_v] arrays:
 // forward states leaving / entering segments, gradient states leaving /
-// entering segments; da_partial holds n_seq nseg H d_k floats. dv serves as
-// scratch for the provisional outputs of the state passes, whose contents
-// step 3 replaces entirely.
+// entering segments; da_partial holds n_seq nseg H d_k floats. The state
+// passes of step 1 write states only; step 3 writes dq, dk and dv.
 hipError_t launch_bwd_bf16_segmented(const ChunkProblem& p, const void* q, const void* k, const void* v,
                                      const void* dO, const float* init_state, const float* d_final_state,
                                      void* dq, void* dk, void* dv, float* da, float* d_init_state,
