@@ -176,6 +176,21 @@ def test_varlen_bf16_equal_lengths_and_repeat():
         assert torch.equal(x, y)
 
 
+def test_varlen_bf16_longest_first_at_its_limit():
+    """256 packed sequences, the most that run longest first (the length table
+    fills the workgroup's LDS slot): lengths 0 to 40 with many ties, forward
+    and backward against the oracle on a sample of units."""
+    L = [(37 * i) % 41 for i in range(256)]
+    cu = I.cu_from_lengths(L)
+    inp = I.chunk_inputs(1, 2, int(cu[-1]), 32, 64, "bf16", seed=106, a_std=0.1, s0_std=0.02,
+                         n_seq=len(L), with_grad=True, dsf_std=0.02)
+    lam = schedule32(2, 1.0, 2048.0)
+    longest = int(np.argmax(L))
+    units = [(n, h) for n in (0, 1, 2, 127, 254, 255, longest) for h in (0, 1)]
+    run_fwd_case(inp, lam, 64, cu=cu, units=units)
+    run_bwd_case(inp, lam, 64, cu=cu, units=units)
+
+
 def test_varlen_bf16_many_sequences_keep_packed_order():
     """Above 256 packed sequences the longest-first order is not used: 300
     short sequences of 0 to 9 tokens, forward and backward, against the oracle
