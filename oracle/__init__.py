@@ -11,8 +11,17 @@ Layouts follow the library's: q, k are [B, H, T, d_k]; v, o, dO are
 N+1 offsets) the token axis is packed ([1, H, sum T, d]) and sequence n is the
 token range [cu[n], cu[n+1]).
 
-Parity status of each function is recorded in the test suite's pins
-(tests/test_oracle_pins.py); none is "parity unpinned".
+Pins (tests/oracle_pins.py) tie every function here to something other than
+itself: the unit functions to brute force, closed forms and finite
+differences (also with a = None, the gradient at a = 0), and the batch
+wrappers fwd, bwd and conv_fwd to per-sequence brute force, finite
+differences of the packed loss and numpy's cross-correlation, with distinct
+states per sequence. tests/test_oracle_mutations.py plants mistakes in
+oracle.c and in this file and shows that a pin catches each. What no pin can
+fix is a reading, not code: the decay schedule's intermediate heads follow
+the reading that half-lives are geometric in the head index (the page prints
+only the two end values), and the Head RMSNorm's tier grouping follows the
+reading of contiguous tiers.
 """
 from __future__ import annotations
 

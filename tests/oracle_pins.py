@@ -258,6 +258,84 @@ def check_bwd_lambda_zero():
     _close(dS0, np.zeros((dk, dv)), 0, "lam=0 dS0")
 
 
+def check_bwd_at_a_null():
+    """a = NULL is the gradient at a = 0 (the initial value of aug_balance,
+    "GLA mixer"): dq, dk, dv, da and dS0 from bwd_unit(a=None) equal central
+    finite differences of L computed with an explicit zero a, in every
+    coordinate. da is not zero there: sigmoid'(0) = 1/4."""
+    T, dk, dv, lam = 12, 3, 5, 0.83
+    q, k, v, _, S0 = _rand_unit(24, T, dk, dv)
+    r = _rng(124)
+    dO = r.standard_normal((T, dv))
+    dSf = r.standard_normal((dk, dv)) * 0.3
+    a0 = np.zeros(dk)
+    # the NULL forward branch is the a = 0 brute force
+    o, Sf = oracle.fwd_unit(q, k, v, lam, None, S0)
+    ob, Sb = brute_force(q, k, v, lam, a0, S0)
+    _close(o, ob, 1e-12, "fwd a=NULL vs brute force at a=0")
+    _close(Sf, Sb, 1e-12, "fwd a=NULL final state")
+    dq, dk_, dv_, da, dS0 = oracle.bwd_unit(q, k, v, dO, lam, None, S0, dSf)
+    params = {"q": q, "k": k, "v": v, "a": a0, "S0": S0}
+    grads = {"q": dq, "k": dk_, "v": dv_, "a": da, "S0": dS0}
+    for name, x in params.items():
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            h = 1e-5 * max(1.0, abs(x[idx]))
+            keep = x[idx]
+            x[idx] = keep + h
+            lp = _loss(**params, lam=lam, dO=dO, dSf=dSf)
+            x[idx] = keep - h
+            lm = _loss(**params, lam=lam, dO=dO, dSf=dSf)
+            x[idx] = keep
+            fd[idx] = (lp - lm) / (2 * h)
+        scale = max(1e-3, float(np.max(np.abs(fd))))
+        err = float(np.max(np.abs(fd - grads[name])))
+        assert err <= 1e-6 * scale, f"d{name} at a=NULL: FD err {err:.3e} (scale {scale:.3e})"
+    assert float(np.max(np.abs(da))) > 1e-3, "da at a = 0 must not vanish"
+
+
+def check_bwd_varlen_wrapper():
+    """The packed batch backward (oracle.bwd with cu_seqlens) against central
+    finite differences of the packed batch loss L = sum dO.o + sum dS_final.S_final
+    computed through the packed forward (itself pinned to brute force), in
+    every coordinate of q, k, v, a and the initial states: distinct initial
+    states and final-state gradients per sequence, an empty and a one-token
+    sequence, and da summed over sequences."""
+    r = _rng(26)
+    L = [3, 0, 5, 1]
+    cu = np.concatenate([[0], np.cumsum(L)])
+    H, dk, dv = 2, 2, 3
+    Tt = int(cu[-1])
+    q = r.standard_normal((1, H, Tt, dk)) * 0.7
+    k = r.standard_normal((1, H, Tt, dk))
+    v = r.standard_normal((1, H, Tt, dv))
+    a = r.standard_normal((H, dk)) * 0.5
+    S0 = r.standard_normal((len(L), H, dk, dv)) * 0.3
+    dO = r.standard_normal((1, H, Tt, dv))
+    dSf = r.standard_normal((len(L), H, dk, dv)) * 0.3
+    lam = np.array([0.6, 0.9])
+
+    def loss():
+        o, Sf = oracle.fwd(q, k, v, lam, a, S0, cu_seqlens=cu)
+        return float(np.sum(dO * o) + np.sum(dSf * Sf))
+
+    dq, dk_, dv_, da, dS0 = oracle.bwd(q, k, v, dO, lam, a, S0, dSf, cu_seqlens=cu)
+    for name, x, gr in (("q", q, dq), ("k", k, dk_), ("v", v, dv_), ("a", a, da), ("S0", S0, dS0)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            h = 1e-5 * max(1.0, abs(x[idx]))
+            keep = x[idx]
+            x[idx] = keep + h
+            lp = loss()
+            x[idx] = keep - h
+            lm = loss()
+            x[idx] = keep
+            fd[idx] = (lp - lm) / (2 * h)
+        scale = max(1e-3, float(np.max(np.abs(fd))))
+        err = float(np.max(np.abs(fd - gr)))
+        assert err <= 1e-6 * scale, f"packed d{name}: FD err {err:.3e} (scale {scale:.3e})"
+
+
 # ---------------------------------------------------------- conv prologue
 
 
@@ -325,6 +403,37 @@ def check_conv_decode_steps():
     yd = np.stack([oracle.conv_decode_step_unit(u[t], w, b, st) for t in range(6)])
     _close(yd, y, 1e-14, "conv decode y")
     _close(st, sf, 0, "conv decode state")
+
+
+def check_conv_varlen_wrapper():
+    """The packed conv (oracle.conv_fwd with cu_seqlens) against numpy's
+    cross-correlation per sequence, each sequence with its own initial conv
+    state (empty and one-token sequences included), and the final states
+    against the last three entries of each sequence's history."""
+    r = _rng(39)
+    L = [5, 1, 0, 7, 2]
+    cu = np.concatenate([[0], np.cumsum(L)])
+    D = 3
+    u = r.standard_normal((int(cu[-1]), D))
+    w = r.standard_normal((D, 4)) * 0.5
+    b = r.standard_normal(D) * 0.3
+    st = r.standard_normal((len(L), 3, D))
+    y, fin = oracle.conv_fwd(u, w, b, st, cu_seqlens=cu)
+    for n in range(len(L)):
+        p = np.concatenate([st[n], u[cu[n]:cu[n + 1]]], axis=0)
+        ref = np.stack([np.correlate(p[:, c], w[c], mode="valid") for c in range(D)], axis=1) + b
+        _close(y[cu[n]:cu[n + 1]], _silu(ref[:L[n]]) if L[n] else np.zeros((0, D)), 1e-13,
+               f"packed conv y, sequence {n}")
+        _close(fin[n], p[-3:], 0, f"packed conv final state, sequence {n}")
+    # dense batch rows: the same, one initial state per row
+    ud = r.standard_normal((3, 4, D))
+    std = r.standard_normal((3, 3, D))
+    yd, fd = oracle.conv_fwd(ud, w, None, std)
+    for n in range(3):
+        p = np.concatenate([std[n], ud[n]], axis=0)
+        ref = np.stack([np.correlate(p[:, c], w[c], mode="valid") for c in range(D)], axis=1)
+        _close(yd[n], _silu(ref), 1e-13, f"dense conv y, row {n}")
+        _close(fd[n], p[-3:], 0, f"dense conv final state, row {n}")
 
 
 # ------------------------------------------------- mixer epilogue (Head RMSNorm + gate)
@@ -518,10 +627,13 @@ ALL_CHECKS = [
     check_decode_brute_force,
     check_bwd_finite_differences,
     check_bwd_lambda_zero,
+    check_bwd_at_a_null,
+    check_bwd_varlen_wrapper,
     check_conv_correlate,
     check_conv_single_taps,
     check_conv_state_carry,
     check_conv_decode_steps,
+    check_conv_varlen_wrapper,
     check_hng_unit_rms,
     check_hng_scale_sign,
     check_hng_tiers_and_channels,

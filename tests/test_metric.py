@@ -33,3 +33,29 @@ def test_bf16_copy_of_exact_decode_output_fails_raw_metric():
     print(f"bf16 copy of the exact output: raw {raw:.3e}, gated {gated:.3e}")
     assert raw > 1e-2          # storage rounding alone is of the order of the 2e-2 gate
     assert gated < 1e-6        # and the gated metric charges none of it
+
+
+def test_bf16_copy_of_exact_laplace_output_fails_raw_metric():
+    """At the Laplace layer's forward (B=8, H=16, T=2048, d_k=96, d_v=192, the
+    six sampled units and both a variants of the full-size parity test), a
+    bf16 copy of the exact fp64 output scores at least the 2e-2 gate on the
+    raw metric max|x - ref| / RMS(ref), so the raw metric would fail a perfect
+    kernel there; the gated metric charges the copy nothing."""
+    B, H, T, dk, dv = 8, 16, 2048, 96, 192
+    lam = schedule32(H, 1.0, 2048.0)
+    units = [(0, 0), (0, 15), (3, 7), (7, 0), (7, 15), (5, 11)]
+    base = I.chunk_inputs(B, H, T, dk, dv, "bf16", seed=2, a_std=None)
+    for a_std in (None, 0.1):
+        a = (np.zeros((H, dk)) if a_std is None
+             else I.gaussian(2, I.STREAM_A, (H, dk), a_std).astype(np.float64))
+        ref = []
+        for (n, h) in units:
+            o, _ = oracle.fwd_unit(I.widen(base["q"][n, h], "bf16"), I.widen(base["k"][n, h], "bf16"),
+                                   I.widen(base["v"][n, h], "bf16"), float(lam[h]), a[h], None)
+            ref.append(o.ravel())
+        ref = np.concatenate(ref)
+        copy = I.bf16_bits_to_f32(I.f32_to_bf16_bits(ref.astype(np.float32))).astype(np.float64)
+        gated, raw = rel_err(copy, ref, store="bf16")
+        print(f"a_std={a_std}: bf16 copy of the exact output: raw {raw:.3e}, gated {gated:.3e}")
+        assert raw >= 2e-2
+        assert gated < 1e-6

@@ -37,6 +37,10 @@ MUTATIONS = [
     ("dS0 not decayed", "dS0[e] = (T > 0) ? lam * G[e] : G[e];", "dS0[e] = G[e];"),
     ("dv aug sigma' instead of sigma", "dvt[j] = acc + s * dot[j];", "dvt[j] = acc + s * (1.0 - s) * dot[j];"),
     ("da uses q twice", "da[i] += c * qt[i] * kt[i];", "da[i] += c * qt[i] * qt[i];"),
+    ("da only when a is given", "da[i] += c * qt[i] * kt[i];",
+     "if (a != NULL) da[i] += c * qt[i] * kt[i];"),
+    ("gate argument at a = NULL is one", "    if (a == NULL) {\n        return 0.0;",
+     "    if (a == NULL) {\n        return 1.0;"),
     ("dk aug sign", "dkt[i] = acc + ((a != NULL) ? c * a[i] * qt[i] : 0.0);",
      "dkt[i] = acc - ((a != NULL) ? c * a[i] * qt[i] : 0.0);"),
     ("dv reads G transposed wrong", "acc += G[(size_t)i * d_v + j] * kt[i];", "acc += G[(size_t)i * d_v + j] * qt[i];"),
@@ -108,4 +112,45 @@ def test_mutation_is_caught(name, find, repl, tmp_path):
                 caught.append(check.__name__)
     finally:
         oracle._lib = good
+    assert caught, f"no pin detects the planted mistake '{name}'"
+
+
+# Mistakes in the Python batch wrappers of oracle/__init__.py (slicing of
+# sequences, per-sequence states, the sum of da over sequences). The mutated
+# module is loaded on its own and its functions replace the package's while
+# the pins run.
+PY_SRC = os.path.join(os.path.dirname(oracle.__file__), "__init__.py")
+PY_MUTATIONS = [
+    ("packed conv: first sequence's state for every sequence",
+     "s0 = None if st is None else st[n]", "s0 = None if st is None else st[0]"),
+    ("packed conv: final state of the wrong sequence",
+     "y[sp[0]:sp[1]], fin[n] = conv_fwd_unit(", "y[sp[0]:sp[1]], fin[max(n - 1, 0)] = conv_fwd_unit("),
+    ("packed fwd: first sequence's initial state for every sequence",
+     "None if a is None else a[h], None if S0 is None else S0[n, h])",
+     "None if a is None else a[h], None if S0 is None else S0[0, h])"),
+    ("packed bwd: first sequence's final-state gradient for every sequence",
+     "None if dSf is None else dSf[n, h])", "None if dSf is None else dSf[0, h])"),
+    ("packed bwd: da of the last sequence only",
+     "da[h] += da_parts[(n, h)]", "da[h] = da_parts[(n, h)]"),
+    ("packed bwd: sequence slice off by one",
+     "out.append((n, h, 0, slice(cu[n], cu[n + 1])))", "out.append((n, h, 0, slice(cu[n], cu[n + 1] + 1)))"),
+]
+
+
+@pytest.mark.parametrize("name,find,repl", PY_MUTATIONS, ids=[m[0] for m in PY_MUTATIONS])
+def test_wrapper_mutation_is_caught(name, find, repl, monkeypatch):
+    import types
+    src = open(PY_SRC).read()
+    assert src.count(find) == 1, f"mutation site for '{name}' not unique ({src.count(find)})"
+    mod = types.ModuleType("oracle_mutated")
+    mod.__file__ = PY_SRC
+    exec(compile(src.replace(find, repl), PY_SRC, "exec"), mod.__dict__)
+    for fn in ("fwd", "bwd", "conv_fwd", "head_norm_gate", "head_norm_gate_bwd"):
+        monkeypatch.setattr(oracle, fn, getattr(mod, fn))
+    caught = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check()
+        except (AssertionError, ValueError, IndexError):
+            caught.append(check.__name__)
     assert caught, f"no pin detects the planted mistake '{name}'"
