@@ -76,13 +76,14 @@ sgla_status check_chunk(const void* q, const void* k, const void* v, const float
         if (d_k > 96 || d_v > 192 || d_k % 8 != 0 || d_v % 8 != 0)
             return fail(SGLA_ERR_UNSUPPORTED,
                         "bf16 needs d_k <= 96 and d_v <= 192, multiples of 8 (got %d, %d)", d_k, d_v);
-        if (chunk != 64 && chunk != 128)
-            return fail(SGLA_ERR_UNSUPPORTED, "bf16 chunk must be 64 or 128, got %d", chunk);
+        if (chunk != 32 && chunk != 64 && chunk != 128)
+            return fail(SGLA_ERR_UNSUPPORTED, "bf16 chunk must be 32, 64 or 128, got %d", chunk);
     } else {
         if (d_k > 32 || d_v > 32 || d_k % 4 != 0 || d_v % 4 != 0)
             return fail(SGLA_ERR_UNSUPPORTED,
                         "f32 needs d_k <= 32 and d_v <= 32, multiples of 4 (got %d, %d)", d_k, d_v);
-        if (chunk != 64) return fail(SGLA_ERR_UNSUPPORTED, "f32 chunk must be 64, got %d", chunk);
+        if (chunk != 32 && chunk != 64 && chunk != 128)
+            return fail(SGLA_ERR_UNSUPPORTED, "f32 chunk must be 32, 64 or 128, got %d", chunk);
     }
     out->bf16 = dtype == SGLA_BF16;
     out->B = B;
@@ -106,6 +107,15 @@ bool overlaps(const void* x, size_t nx, const void* y, size_t ny)
 }
 
 }  // namespace
+
+namespace sgla {
+// Sets the calling thread's error message for entry points defined in other
+// source files.
+sgla_status api_fail(sgla_status st, const char* msg)
+{
+    return fail(st, "%s", msg);
+}
+}  // namespace sgla
 
 extern "C" {
 
@@ -197,6 +207,34 @@ static sgla_status check_bwd_all(const void* q, const void* k, const void* v, co
                         {d_init_state, nst, "d_init_state"}, {workspace, ws_bytes, "workspace"}};
     return check_disjoint(wr, 6, rd, 8);
 }
+
+}  // extern "C"
+
+namespace sgla {
+// Every argument check of the chunked backward except those of its workspace
+// (sizes, pointers, alignment, and the overlaps among the other buffers).
+sgla_status check_chunk_bwd(const void* q, const void* k, const void* v, const void* dO, const float* lambda,
+                            const float* a, const float* init_state, const float* d_final_state, void* dq,
+                            void* dk, void* dv, float* da, float* d_init_state, const int32_t* cu_seqlens,
+                            int n_seq, int B, int H, int T, int d_k, int d_v, int chunk, sgla_dtype dtype,
+                            ChunkProblem* p)
+{
+    sgla_status st = check_chunk(q, k, v, lambda, a, cu_seqlens, n_seq, B, H, T, d_k, d_v, chunk, dtype, p);
+    if (st != SGLA_OK) return st;
+    REQUIRE_PTR(dO);
+    REQUIRE_PTR(dq);
+    REQUIRE_PTR(dk);
+    REQUIRE_PTR(dv);
+    REQUIRE_PTR(da);
+    OPTIONAL_PTR(init_state);
+    OPTIONAL_PTR(d_final_state);
+    OPTIONAL_PTR(d_init_state);
+    return check_bwd_all(q, k, v, dO, lambda, a, init_state, d_final_state, dq, dk, dv, da, d_init_state,
+                         nullptr, 0, p->n_seq, B, H, T, d_k, d_v, (dtype == SGLA_BF16) ? 2 : 4);
+}
+}  // namespace sgla
+
+extern "C" {
 
 sgla_status sgla_chunk_fwd(const void* q, const void* k, const void* v, const float* lambda,
                            const float* a, const float* init_state, float* final_state, void* o,
@@ -349,17 +387,10 @@ sgla_status sgla_chunk_bwd(const void* q, const void* k, const void* v, const vo
                            void* workspace, size_t workspace_bytes, void* hip_stream)
 {
     sgla::ChunkProblem p;
-    sgla_status st = check_chunk(q, k, v, lambda, a, cu_seqlens, n_seq, B, H, T, d_k, d_v, chunk,
-                                 dtype, &p);
+    sgla_status st = sgla::check_chunk_bwd(q, k, v, dO, lambda, a, init_state, d_final_state, dq, dk, dv, da,
+                                           d_init_state, cu_seqlens, n_seq, B, H, T, d_k, d_v, chunk, dtype,
+                                           &p);
     if (st != SGLA_OK) return st;
-    REQUIRE_PTR(dO);
-    REQUIRE_PTR(dq);
-    REQUIRE_PTR(dk);
-    REQUIRE_PTR(dv);
-    REQUIRE_PTR(da);
-    OPTIONAL_PTR(init_state);
-    OPTIONAL_PTR(d_final_state);
-    OPTIONAL_PTR(d_init_state);
     const size_t need = sgla_chunk_bwd_workspace_bytes(p.n_seq, H, d_k);
     if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
         return fail(SGLA_ERR_WORKSPACE, "workspace needs %zu bytes, 16-byte aligned (got %zu at %p)",

@@ -34,10 +34,10 @@ struct BwdArgs {
     Args role[3];
 };
 
-template <int DKV, int DKG>
+template <int DKV, int DKG, int CTV>
 __global__ __launch_bounds__(NTHREADS_W) void k_bwd(BwdArgs ba)
 {
-    constexpr int LDS = cmax(LayW<WDv<DKV>>::LDS, cmax(LayW<WDq<DKG>>::LDS, LayW<WDk<DKG>>::LDS));
+    constexpr int LDS = cmax(LayW<WDv<DKV, CTV>>::LDS, cmax(LayW<WDq<DKG>>::LDS, LayW<WDk<DKG>>::LDS));
     __shared__ __attribute__((aligned(16))) char smem[LDS];
     const int nr = ba.role[2].nsl + 2;
     const int b = blockIdx.x;
@@ -49,7 +49,7 @@ __global__ __launch_bounds__(NTHREADS_W) void k_bwd(BwdArgs ba)
     const Args& p = ba.role[ri];
     if (r == 0) body_wide<WDq<DKG>>(p, unit, 0, smem);
     else if (r == 1) body_wide<WDk<DKG>>(p, unit, 0, smem);
-    else body_wide<WDv<DKV>>(p, unit, r - 2, smem);
+    else body_wide<WDv<DKV, CTV>>(p, unit, r - 2, smem);
 }
 
 // da[h][d] = sum over sequences n (in order) of part[n H + h][d]
@@ -84,19 +84,33 @@ __global__ __launch_bounds__(NTHREADS_W) void k_seg_states(Args af, Args adv, in
     else body_wide<WDvState<DK>>(p, unit, slice, smem);
 }
 
+// ctv: tile length of the dv scan (32 or 64 tokens); dq and dk always run
+// 32-token tiles (their 192-wide operands fill the LDS ring at 32).
 template <int DKV, int DKG>
-hipError_t run_bwd(const Args& av, const Args& aq, const Args& ak, hipStream_t stream)
+hipError_t run_bwd(const Args& av, const Args& aq, const Args& ak, hipStream_t stream, int ctv)
 {
     BwdArgs ba;
     ba.role[0] = aq;
     ba.role[1] = ak;
     ba.role[2] = av;
     const int grid = ((av.n_units + 7) / 8) * 8 * (av.nsl + 2);
-    hipLaunchKernelGGL((k_bwd<DKV, DKG>), dim3(grid), dim3(NTHREADS_W), 0, stream, ba);
+    if (ctv == 32) hipLaunchKernelGGL((k_bwd<DKV, DKG, 32>), dim3(grid), dim3(NTHREADS_W), 0, stream, ba);
+    else hipLaunchKernelGGL((k_bwd<DKV, DKG, 64>), dim3(grid), dim3(NTHREADS_W), 0, stream, ba);
     return hipGetLastError();
 }
 
 }  // namespace scan
+
+static hipError_t run_bwd_any(const ChunkProblem& p, const scan::Args& av, const scan::Args& aq,
+                              const scan::Args& ak, hipStream_t stream)
+{
+    const int ct = bf16_tile(p.chunk);
+    if (p.d_k <= 32)
+        return (p.d_v <= 96) ? scan::run_bwd<32, 96>(av, aq, ak, stream, ct)
+                             : scan::run_bwd<32, 192>(av, aq, ak, stream, ct);
+    return (p.d_v <= 96) ? scan::run_bwd<96, 96>(av, aq, ak, stream, ct)
+                         : scan::run_bwd<96, 192>(av, aq, ak, stream, ct);
+}
 
 // bf16 backward of dense sequences cut into nseg >= 2 segments (see
 // sgla_chunk_bwd_segmented). ws holds four [n_seq][nseg][H][d_k][d_v] arrays:
@@ -209,11 +223,7 @@ hipError_t launch_bwd_bf16_segmented(const ChunkProblem& p, const void* q, const
     ak.s_init = d_final_state;
     ak.s_in_seg = g_in;
     ak.da_part = nullptr;
-    if (p.d_k <= 32) {
-        e = (p.d_v <= 96) ? scan::run_bwd<32, 96>(av, aq, ak, stream) : scan::run_bwd<32, 192>(av, aq, ak, stream);
-    } else {
-        e = (p.d_v <= 96) ? scan::run_bwd<96, 96>(av, aq, ak, stream) : scan::run_bwd<96, 192>(av, aq, ak, stream);
-    }
+    e = run_bwd_any(p, av, aq, ak, stream);
     if (e != hipSuccess) return e;
     const int nda = p.H * p.d_k;
     hipLaunchKernelGGL(scan::k_da_sum, dim3((nda + 255) / 256), dim3(256), 0, stream, da_partial, da,
@@ -269,12 +279,7 @@ hipError_t launch_bwd_bf16(const ChunkProblem& p, const void* q, const void* k, 
     ak.s_init = d_final_state;
     ak.da_part = nullptr;
 
-    hipError_t e;
-    if (p.d_k <= 32) {
-        e = (p.d_v <= 96) ? scan::run_bwd<32, 96>(av, aq, ak, stream) : scan::run_bwd<32, 192>(av, aq, ak, stream);
-    } else {
-        e = (p.d_v <= 96) ? scan::run_bwd<96, 96>(av, aq, ak, stream) : scan::run_bwd<96, 192>(av, aq, ak, stream);
-    }
+    hipError_t e = run_bwd_any(p, av, aq, ak, stream);
     if (e != hipSuccess) return e;
     const int nda = p.H * p.d_k;
     hipLaunchKernelGGL(scan::k_da_sum, dim3((nda + 255) / 256), dim3(256), 0, stream, da_partial, da,

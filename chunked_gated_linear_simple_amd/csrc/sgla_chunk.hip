@@ -839,11 +839,11 @@ hipError_t run_bwd(const ChunkProblem& p, const RoleArgs& aq, const RoleArgs& ak
 }
 
 // Role instantiations (fp32 tensors; bf16 runs on the kernels of sgla_fwd.hip
-// and sgla_bwd.hip)
-typedef Role<float, 32, 32, 64, AUG_FWD, false> F32Fwd;
-typedef Role<float, 32, 32, 64, AUG_GRAD, false> F32Dq;
-typedef Role<float, 32, 32, 64, AUG_GRAD, true> F32Dk;
-typedef Role<float, 32, 32, 64, AUG_FWD, true> F32Dv;
+// and sgla_bwd.hip); C is the chunk length, 32, 64 or 128 tokens
+template <int C> using F32Fwd = Role<float, 32, 32, C, AUG_FWD, false>;
+template <int C> using F32Dq = Role<float, 32, 32, C, AUG_GRAD, false>;
+template <int C> using F32Dk = Role<float, 32, 32, C, AUG_GRAD, true>;
+template <int C> using F32Dv = Role<float, 32, 32, C, AUG_FWD, true>;
 
 }  // namespace
 
@@ -854,7 +854,10 @@ hipError_t launch_chunk_fwd(const ChunkProblem& p, const void* q, const void* k,
     // bf16 shapes are limited to d_k <= 96, d_v <= 192 by the host checks
     if (p.bf16) return launch_fwd_bf16(p, q, k, v, init_state, final_state, o, stream);
     RoleArgs ra{q, k, v, nullptr, o, init_state, final_state, nullptr, p.d_k, p.d_v, 0, 0, 0};
-    return run_fwd<F32Fwd>(p, ra, (p.d_v + 31) / 32, stream);
+    const int nsl = (p.d_v + 31) / 32;
+    if (p.chunk == 32) return run_fwd<F32Fwd<32>>(p, ra, nsl, stream);
+    if (p.chunk == 128) return run_fwd<F32Fwd<128>>(p, ra, nsl, stream);
+    return run_fwd<F32Fwd<64>>(p, ra, nsl, stream);
 }
 
 hipError_t launch_chunk_bwd(const ChunkProblem& p, const void* q, const void* k, const void* v,
@@ -871,7 +874,9 @@ hipError_t launch_chunk_bwd(const ChunkProblem& p, const void* q, const void* k,
     RoleArgs ak{v, dO, q, k, dk, d_final_state, nullptr, nullptr, p.d_v, p.d_k, 1, 0, 1};
     // dv: reverse scan of G ([d_k][d_v]); q'=k, k'=q, v'=dO; final G -> d_init_state
     RoleArgs av{k, q, dO, nullptr, dv, d_final_state, d_init_state, nullptr, p.d_k, p.d_v, 0, 1, 1};
-    return run_bwd<F32Dq, F32Dk, F32Dv>(p, aq, ak, av, da, stream);
+    if (p.chunk == 32) return run_bwd<F32Dq<32>, F32Dk<32>, F32Dv<32>>(p, aq, ak, av, da, stream);
+    if (p.chunk == 128) return run_bwd<F32Dq<128>, F32Dk<128>, F32Dv<128>>(p, aq, ak, av, da, stream);
+    return run_bwd<F32Dq<64>, F32Dk<64>, F32Dv<64>>(p, aq, ak, av, da, stream);
 }
 
 }  // namespace sgla

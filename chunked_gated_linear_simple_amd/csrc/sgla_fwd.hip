@@ -12,15 +12,15 @@ namespace scan {
 // One workgroup of eight waves per (sequence, head, 96-column value slice);
 // the slices of one unit share an XCD (blocks are dealt to the eight XCDs
 // round-robin) and so share its L2.
-template <int DK>
+template <int DK, int CT>
 __global__ __launch_bounds__(NTHREADS_W) void k_fwd(Args p)
 {
-    __shared__ __attribute__((aligned(16))) char smem[LayW<WFwd<DK>>::LDS];
+    __shared__ __attribute__((aligned(16))) char smem[LayW<WFwd<DK, CT>>::LDS];
     const int b = blockIdx.x;
     const int slice = (b >> 3) % p.nsl;
     const int unit = ((b >> 3) / p.nsl) * 8 + (b & 7);
     if (unit >= p.n_units) return;
-    body_wide<WFwd<DK>>(p, unit, slice, smem);
+    body_wide<WFwd<DK, CT>>(p, unit, slice, smem);
 }
 
 // The state scan alone over each unit's run (no outputs), mapped as k_fwd.
@@ -35,12 +35,15 @@ __global__ __launch_bounds__(NTHREADS_W) void k_fwd_state(Args p)
     body_wide<WFwdState<DK>>(p, unit, slice, smem);
 }
 
+// ct: tile length of the output scan (32 or 64 tokens); the state-only scan
+// always runs 64-token tiles.
 template <int DK>
-hipError_t run_fwd(const Args& a, hipStream_t stream, bool out = true)
+hipError_t run_fwd(const Args& a, hipStream_t stream, bool out, int ct)
 {
     const int grid = ((a.n_units + 7) / 8) * 8 * a.nsl;
-    if (out) hipLaunchKernelGGL(k_fwd<DK>, dim3(grid), dim3(NTHREADS_W), 0, stream, a);
-    else hipLaunchKernelGGL(k_fwd_state<DK>, dim3(grid), dim3(NTHREADS_W), 0, stream, a);
+    if (!out) hipLaunchKernelGGL(k_fwd_state<DK>, dim3(grid), dim3(NTHREADS_W), 0, stream, a);
+    else if (ct == 32) hipLaunchKernelGGL((k_fwd<DK, 32>), dim3(grid), dim3(NTHREADS_W), 0, stream, a);
+    else hipLaunchKernelGGL((k_fwd<DK, 64>), dim3(grid), dim3(NTHREADS_W), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -70,11 +73,15 @@ static scan::Args fwd_args(const ChunkProblem& p, const void* q, const void* k, 
     return a;
 }
 
-static hipError_t run_fwd_any(const scan::Args& a, int d_k, hipStream_t stream, bool out = true)
+// Tile length of the bf16 output scans for a chunk length: 32-token tiles for
+// chunk 32, else 64 (a 128-token tile does not fit the four-deep LDS ring).
+int bf16_tile(int chunk) { return chunk == 32 ? 32 : 64; }
+
+static hipError_t run_fwd_any(const scan::Args& a, int d_k, hipStream_t stream, bool out, int ct)
 {
-    if (d_k <= 32) return scan::run_fwd<32>(a, stream, out);
-    if (d_k <= 64) return scan::run_fwd<64>(a, stream, out);
-    return scan::run_fwd<96>(a, stream, out);
+    if (d_k <= 32) return scan::run_fwd<32>(a, stream, out, ct);
+    if (d_k <= 64) return scan::run_fwd<64>(a, stream, out, ct);
+    return scan::run_fwd<96>(a, stream, out, ct);
 }
 
 // The states entering segments 0 .. nseg-1 of dense sequences (ws_in): the
@@ -93,7 +100,7 @@ hipError_t launch_fwd_bf16_seg_states(const ChunkProblem& p, const void* k, cons
     a.s_in_seg = nullptr;
     a.s_out_seg = ws_loc;
     a.n_units = p.n_seq * (nseg - 1) * p.H;
-    hipError_t e = run_fwd_any(a, p.d_k, stream, false);
+    hipError_t e = run_fwd_any(a, p.d_k, stream, false, 64);
     if (e != hipSuccess) return e;
     const int ssz4 = p.d_k * p.d_v / 4;
     hipLaunchKernelGGL(scan::k_seg_scan, dim3((ssz4 + 255) / 256, p.n_seq * p.H), dim3(256), 0, stream,
@@ -123,7 +130,7 @@ hipError_t launch_fwd_bf16_segmented(const ChunkProblem& p, const void* q, const
     a.seg_in_all = 1;
     a.s_in_seg = ws_in;
     a.s_out_seg = nullptr;
-    return run_fwd_any(a, p.d_k, stream);
+    return run_fwd_any(a, p.d_k, stream, true, bf16_tile(p.chunk));
 }
 
 // bf16 forward with d_k <= 96 (padded to 32, 64 or 96) and any d_v (96-column slices).
@@ -131,7 +138,8 @@ hipError_t launch_fwd_bf16(const ChunkProblem& p, const void* q, const void* k, 
                            const float* init_state, float* final_state, void* o,
                            hipStream_t stream)
 {
-    return run_fwd_any(fwd_args(p, q, k, v, init_state, final_state, o), p.d_k, stream);
+    return run_fwd_any(fwd_args(p, q, k, v, init_state, final_state, o), p.d_k, stream, true,
+                       bf16_tile(p.chunk));
 }
 
 }  // namespace sgla

@@ -6,7 +6,22 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "sgla.h"
+
 namespace sgla {
+
+// Records msg as the calling thread's sgla_last_error() and returns st.
+sgla_status api_fail(sgla_status st, const char* msg);
+
+struct ChunkProblem;
+
+// Every argument check of sgla_chunk_bwd except those of its workspace; fills
+// the launch description. Enqueues nothing.
+sgla_status check_chunk_bwd(const void* q, const void* k, const void* v, const void* dO, const float* lambda,
+                            const float* a, const float* init_state, const float* d_final_state, void* dq,
+                            void* dk, void* dv, float* da, float* d_init_state, const int32_t* cu_seqlens,
+                            int n_seq, int B, int H, int T, int d_k, int d_v, int chunk, sgla_dtype dtype,
+                            ChunkProblem* p);
 
 // Everything a chunked launch needs, already validated on the host.
 struct ChunkProblem {
@@ -19,6 +34,9 @@ struct ChunkProblem {
     const float* a;
     const int32_t* cu;  // NULL when dense
 };
+
+// Tile length of the bf16 output scans (forward, dv) for a chunk length.
+int bf16_tile(int chunk);
 
 hipError_t launch_chunk_fwd(const ChunkProblem& p, const void* q, const void* k, const void* v,
                             const float* init_state, float* final_state, void* o,

@@ -46,12 +46,17 @@
 //     column l%32, rows 8(i/4) + 4(l/32) + i%4 in register i; an accumulator
 //     used as an operand of a contraction over its rows carries, for the
 //     16-wide step h, rows 16h + 8a + 4g + b in slot 4a + b (g = l/32).
-//   * The state update enters the decayed values as the exact bf16 V' plus a
-//     bf16-rounded correction whose size is 1 - lam^m of it:
-//       S = lam^C S + K'^T V' - K'^T (c * V'),   c_j = 1 - lam^(C_c-e-j);
-//     for the long-memory heads, whose states dominate, the correction is a
-//     few percent of the term and its rounding negligible. The readout takes
-//     the state as a bf16 hi + lo pair.
+//   * The state update enters each decayed value lam^m v'_j (m = C_c-e-j) as
+//     two bf16 operands A_j + B_j of two products K'^T A + K'^T B, chosen so
+//     that the rounding never exceeds 2^-9 of the term itself:
+//       lam^m >= 1/2:  A_j = v'_j (exact), B_j = bf16(-(1 - lam^m) v'_j)
+//                      (|B_j| <= |term|; a few percent of it for the
+//                      long-memory heads, whose states dominate);
+//       lam^m <  1/2:  A_j = 0,           B_j = bf16(lam^m v'_j)
+//                      (a plain correction would be nearly -v'_j here, and
+//                      its rounding, 2^-9 |v'_j|, would not decay with the
+//                      term: the short-memory heads' states would carry it).
+//     The readout takes the state as a bf16 hi + lo pair.
 #ifndef SGLA_SCAN_HPP
 #define SGLA_SCAN_HPP
 
@@ -261,8 +266,8 @@ struct WRole {
     static constexpr bool REV = REV_, GRAD = GRAD_, DA = DA_, INIT_T = INIT_T_, OUT = OUT_;
     static constexpr int E = REV_ ? 0 : 1;
 };
-template <int DK> using WFwd = WRole<DK, false, false, false, false, 64>;
-template <int DK> using WDv = WRole<DK, true, false, false, false, 64>;
+template <int DK, int CT = 64> using WFwd = WRole<DK, false, false, false, false, CT>;
+template <int DK, int CT = 64> using WDv = WRole<DK, true, false, false, false, CT>;
 template <int DK> using WFwdState = WRole<DK, false, false, false, false, 64, false>;
 template <int DK> using WDvState = WRole<DK, true, false, false, false, 64, false>;
 template <int DK> using WDq = WRole<DK, false, true, true, true, 32>;
@@ -295,8 +300,9 @@ struct LayW {
     static constexpr int SLOT = 2 * SZ_Q + SZ_V + SZ_X;
     static constexpr int OFF_P = NR_W * SLOT;               // 2 x [NPB][64 lanes][16 B]
     static constexpr int SZ_P = NPB * 64 * 16;
-    static constexpr int OFF_CORR = OFF_P + 2 * SZ_P;       // [2][CT]
-    static constexpr int OFF_GT = OFF_CORR + 2 * CT * 4;    // gate sigmoid(z) [2][CT]
+    static constexpr int OFF_CORR = OFF_P + 2 * SZ_P;       // update coefficients of B [2][CT]
+    static constexpr int OFF_KEEP = OFF_CORR + 2 * CT * 4;  // masks of A, one word per token pair [2][CT/2]
+    static constexpr int OFF_GT = OFF_KEEP + CT * 4;        // gate sigmoid(z) [2][CT]
     static constexpr int OFF_CG = OFF_GT + 2 * CT * 4;      // gate-derivative factors [2][CT]
     static constexpr int OFF_A = OFF_CG + (R::GRAD ? 2 * CT * 4 : 0);  // a at the v' columns [DVS]
     static constexpr int LDS = OFF_A + (R::GRAD ? DVS * 4 : 0);
@@ -394,11 +400,23 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
     const float lam = p.lambda[h];
     const float l2 = log2f(lam);
 
+    // The update's operand pair per token (row 0: full tiles, row 1: the last
+    // tile of clast tokens): B_j = corr[j] v'_j and A_j = v'_j masked by the
+    // 16-bit half of keep[j / 2] (all ones when v'_j enters exactly).
     float* corr = reinterpret_cast<float*>(smem + Ly::OFF_CORR);
+    uint32_t* keep = reinterpret_cast<uint32_t*>(smem + Ly::OFF_KEEP);
     for (int i = tid; i < 2 * CT; i += NTHREADS_W) {
         const int cl = (i < CT) ? CT : clast;
         const int j = i & (CT - 1);
-        corr[i] = (j < cl) ? 1.0f - powl2(cl - E - j, l2) : 0.0f;
+        const float d = powl2(cl - E - j, l2);
+        corr[i] = (j >= cl) ? 0.0f : (d >= 0.5f ? -(1.0f - d) : d);
+    }
+    for (int i = tid; i < CT; i += NTHREADS_W) {
+        const int cl = (i < CT / 2) ? CT : clast;
+        const int j0 = 2 * (i & (CT / 2 - 1));
+        const bool k0 = j0 < cl && powl2(cl - E - j0, l2) >= 0.5f;
+        const bool k1 = j0 + 1 < cl && powl2(cl - E - j0 - 1, l2) >= 0.5f;
+        keep[i] = (k0 ? 0x0000ffffu : 0u) | (k1 ? 0xffff0000u : 0u);
     }
     if constexpr (R::GRAD) {
         float* at = reinterpret_cast<float*>(smem + Ly::OFF_A);
@@ -687,7 +705,9 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
         const char* Pb = smem + Ly::OFF_P + (c & 1) * Ly::SZ_P;
         const int cstart = c * CT;
         const int cl = FULL ? CT : min(CT, len - cstart);
-        const float* cf = corr + ((!FULL && c == nch - 1) ? CT : 0);
+        const bool last_row = !FULL && c == nch - 1;
+        const float* cf = corr + (last_row ? CT : 0);
+        const uint32_t* kw = keep + (last_row ? CT / 2 : 0);
         const float fcl = FULL ? fC : __builtin_amdgcn_exp2f((float)cl * l2);
 
         // V'^T (A operand of P V') and V' (B operand of the update) share one
@@ -781,19 +801,22 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
                 for (int r = 0; r < 4; ++r) sacc[db][r] *= fcl;
         }
 
-        // ---- state advance: S = lam^cl S + K'^T V' - K'^T (c V')
-        bf16x8_t vc[NKT];
+        // ---- state advance: S = lam^cl S + K'^T A + K'^T B (the operand
+        // pair of the decayed values, see the top of this file)
+        bf16x8_t va[NKT], vc[NKT];
 #pragma unroll
         for (int ks = 0; ks < NKT; ++ks) {
             const f32x4_t c0 = *reinterpret_cast<const f32x4_t*>(cf + 32 * ks + 8 * qg);
             const f32x4_t c1 = *reinterpret_cast<const f32x4_t*>(cf + 32 * ks + 8 * qg + 4);
+            const u32x4_t km = *reinterpret_cast<const u32x4_t*>(kw + 16 * ks + 4 * qg);
             const u32x4_t vw = __builtin_bit_cast(u32x4_t, vf[ks]);
             u32x4_t cw;
-            cw[0] = pack2(-c0[0] * bf_lo(vw[0]), -c0[1] * bf_hi(vw[0]));
-            cw[1] = pack2(-c0[2] * bf_lo(vw[1]), -c0[3] * bf_hi(vw[1]));
-            cw[2] = pack2(-c1[0] * bf_lo(vw[2]), -c1[1] * bf_hi(vw[2]));
-            cw[3] = pack2(-c1[2] * bf_lo(vw[3]), -c1[3] * bf_hi(vw[3]));
+            cw[0] = pack2(c0[0] * bf_lo(vw[0]), c0[1] * bf_hi(vw[0]));
+            cw[1] = pack2(c0[2] * bf_lo(vw[1]), c0[3] * bf_hi(vw[1]));
+            cw[2] = pack2(c1[0] * bf_lo(vw[2]), c1[1] * bf_hi(vw[2]));
+            cw[3] = pack2(c1[2] * bf_lo(vw[3]), c1[3] * bf_hi(vw[3]));
             vc[ks] = __builtin_bit_cast(bf16x8_t, cw);
+            va[ks] = __builtin_bit_cast(bf16x8_t, vw & km);
         }
 #pragma unroll
         for (int db = 0; db < NDB16; ++db)
@@ -804,7 +827,7 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
                 const int kc0 = 32 * (db >> 1) + 4 * (db & 1);
                 const bf16x8_t kf = frag(tr_read8<SEGK>(Ks, 32 * ks + 8 * qg, kc0, lane),
                                          tr_read8<SEGK>(Ks, 32 * ks + 8 * qg + 4, kc0, lane));
-                sacc[db] = mma16(kf, vf[ks], sacc[db]);
+                sacc[db] = mma16(kf, va[ks], sacc[db]);
                 sacc[db] = mma16(kf, vc[ks], sacc[db]);
             }
     };

@@ -27,8 +27,16 @@
  *   default stream) and the call returns without synchronizing. Outputs are
  *   valid once the stream reaches them.
  * dtype: q, k, v, o (and dO, dq, dk, dv) are all SGLA_BF16 or all SGLA_F32.
- *   States, lambda, a and da are always fp32. Arithmetic is fp32 throughout
- *   (bf16 operands into fp32-accumulating matrix cores for SGLA_BF16).
+ *   States, lambda, a and da are always fp32. Arithmetic is fp32 (bf16
+ *   operands into fp32-accumulating matrix cores for SGLA_BF16), with these
+ *   roundings in the SGLA_BF16 chunk kernels: the state enters the readout as a
+ *   bf16 hi + lo pair (about 16 significant bits); the decayed values of the
+ *   state update enter as the exact bf16 value plus a bf16-rounded correction;
+ *   the intra-chunk scores enter the second product rounded to bf16; and the
+ *   gate argument z = sum_i a_i x_i y_i is formed on the matrix cores from a
+ *   rounded to bf16 and the products a_i x_i rounded to bf16 (a relative error
+ *   of about 2^-9 per term, accumulated in fp32), so its absolute error grows
+ *   with |a|. The decode step and the SGLA_F32 kernels use a in fp32.
  * Layouts (row-major, last index fastest):
  *   dense:  q, k [B, H, T, d_k];  v, o [B, H, T, d_v];  N = B sequences.
  *   packed: with cu_seqlens != NULL: B must be 1, T is the total token count,
@@ -47,8 +55,8 @@
  * Determinism: the same inputs on the same device give bitwise-identical
  *   outputs, including da (fixed-order reductions, no float atomics).
  * Supported shapes:
- *   SGLA_BF16: d_k <= 96, d_v <= 192, both multiples of 8; chunk 64 or 128.
- *   SGLA_F32:  d_k <= 32, d_v <= 32, both multiples of 4; chunk 64.
+ *   SGLA_BF16: d_k <= 96, d_v <= 192, both multiples of 8; chunk 32, 64 or 128.
+ *   SGLA_F32:  d_k <= 32, d_v <= 32, both multiples of 4; chunk 32, 64 or 128.
  *   Anything else returns SGLA_ERR_UNSUPPORTED.
  */
 #ifndef SGLA_H
@@ -116,7 +124,15 @@ sgla_status sgla_decay_schedule(int H, double t_min, double t_max, float* lambda
  * o:           output [.., d_v] (dtype). Must not alias any input.
  * cu_seqlens:  packed-sequence offsets (see layouts) or NULL (dense).
  * n_seq:       number of sequences when cu_seqlens != NULL; ignored otherwise.
- * chunk:       tokens per chunk (64 or 128 for SGLA_BF16, 64 for SGLA_F32).
+ * chunk:       chunk length C of the chunk form (32, 64 or 128). It sets the
+ *              length of the tiles the kernels scan with, which changes only
+ *              the rounding: SGLA_F32 tiles by C tokens; SGLA_BF16 tiles the
+ *              forward (and the dv scan of sgla_chunk_bwd) by 32 tokens for
+ *              C = 32 and by 64 for C = 64 or 128, because a 128-token tile of
+ *              q, k and v does not fit the four-deep LDS ring the bf16
+ *              kernels stream through (the dq and dk scans of the backward
+ *              always tile by 32, and the state-only passes of the segmented
+ *              calls by 64).
  */
 sgla_status sgla_chunk_fwd(const void* q, const void* k, const void* v,
                            const float* lambda, const float* a,

@@ -74,6 +74,21 @@ def assert_close(gpu, ref, tol, what, store="f32", ref_store=None):
     return e
 
 
+def per_head_report(what, gpu_units, ref_units, store="f32"):
+    """Print the error metric per head (diagnostic, no gate): the long-memory
+    heads' outputs are many times larger than the short-memory heads', so the
+    whole tensor's RMS hides how well the small heads are matched."""
+    heads = sorted(set(h for (_, h) in gpu_units))
+    parts = []
+    for h in heads:
+        us = [u for u in gpu_units if u[1] == h]
+        g = np.concatenate([np.ravel(gpu_units[u]) for u in us])
+        r = np.concatenate([np.ravel(ref_units[u]) for u in us])
+        e, _ = rel_err(g, r, store)
+        parts.append(f"h{h} {e:.2e}")
+    print(f"    {what} per head (err / that head's RMS): " + ", ".join(parts), flush=True)
+
+
 def schedule32(H, t_min, t_max):
     """fp32 decays from the oracle's schedule (fed to both sides)."""
     return oracle.decay_schedule(H, t_min, t_max).astype(np.float32)

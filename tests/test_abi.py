@@ -100,9 +100,10 @@ FWD_BAD = [
     ("d_k too big", dict(d_k=128), B.SGLA_ERR_UNSUPPORTED),
     ("d_v too big", dict(d_v=256), B.SGLA_ERR_UNSUPPORTED),
     ("d_k not mult 8", dict(d_k=20), B.SGLA_ERR_UNSUPPORTED),
-    ("chunk 32", dict(chunk=32), B.SGLA_ERR_UNSUPPORTED),
+    ("chunk 16", dict(chunk=16), B.SGLA_ERR_UNSUPPORTED),
+    ("chunk 256", dict(chunk=256), B.SGLA_ERR_UNSUPPORTED),
     ("f32 d_k 96", dict(dt=B.SGLA_F32), B.SGLA_ERR_UNSUPPORTED),
-    ("f32 chunk 128", dict(dt=B.SGLA_F32, d_k=16, d_v=32, chunk=128), B.SGLA_ERR_UNSUPPORTED),
+    ("f32 chunk 96", dict(dt=B.SGLA_F32, d_k=16, d_v=32, chunk=96), B.SGLA_ERR_UNSUPPORTED),
     ("o aliases q", dict(o=P["q"]), B.SGLA_ERR_INVALID_ARG),
     ("o overlaps v", dict(o=P["v"] + 1024), B.SGLA_ERR_INVALID_ARG),
     ("packed with B=2", dict(cu=P["cu"], n_seq=3), B.SGLA_ERR_INVALID_ARG),

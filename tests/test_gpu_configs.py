@@ -18,7 +18,7 @@ import oracle
 from chunked_gated_linear_simple_amd import binding as Bd
 from chunked_gated_linear_simple_amd import inputs as I
 from tests.parity_util import (TOL, assert_close, device_inputs, gpu_unit, oracle_bwd_units,
-                               oracle_fwd_units, schedule32, to_dev, to_host64)
+                               oracle_fwd_units, per_head_report, schedule32, to_dev, to_host64)
 
 pytestmark = pytest.mark.gpu
 
@@ -42,6 +42,7 @@ def test_laplace_fwd_full(a_std):
     units = [(0, 0), (0, 15), (3, 7), (7, 0), (7, 15), (5, 11)]
     ref = oracle_fwd_units(inp, LAM, units)
     oh, Sh = to_host64(o), to_host64(Sf)
+    per_head_report("o", {u: oh[u] for u in units}, {u: ref[u][0] for u in units}, "bf16")
     assert_close(np.concatenate([oh[u].ravel() for u in units]),
                  np.concatenate([ref[u][0].ravel() for u in units]), TOL["bf16"], "o",
                  store="bf16")
@@ -64,6 +65,7 @@ def test_laplace_fwd_bwd_full(a_std):
     ref = oracle_bwd_units(inp, LAM, units)
     for idx, (nm, t) in enumerate((("dq", dq), ("dk", dk), ("dv", dv))):
         th = to_host64(t)
+        per_head_report(nm, {u: th[u] for u in units}, {u: ref[u][idx] for u in units}, "bf16")
         assert_close(np.concatenate([th[u].ravel() for u in units]),
                      np.concatenate([ref[u][idx].ravel() for u in units]), TOL["bf16"], nm,
                      store="bf16")
@@ -78,9 +80,12 @@ def test_laplace_fwd_bwd_full(a_std):
 
 
 def test_laplace_bwd_slice_finite_differences():
-    """GPU gradients on the T=64 slice (batch row 0, all heads) against central
-    finite differences of the fp64 oracle loss L = sum dO . o, on 128 sampled
-    coordinates of each of dq, dk, dv, da."""
+    """GPU gradients on the T=64 slice (batch row 0, all 16 heads, zero initial
+    state) against central finite differences of the fp64 oracle loss
+    L = sum dO . o: 512 sampled coordinates of each of q, k, v and a, plus 8
+    random directions through all four at once (the directional derivative
+    against sum grad . direction)."""
+    from concurrent.futures import ThreadPoolExecutor
     full = I.chunk_inputs(4, H, 2048, DK, DV, "bf16", seed=3, a_std=0.1, with_grad=True)
     sl = {k: (v[0:1, :, :64].copy() if isinstance(v, np.ndarray) and v.ndim == 4 else v)
           for k, v in full.items()}
@@ -90,31 +95,48 @@ def test_laplace_bwd_slice_finite_differences():
     torch.cuda.synchronize()
     g = {"q": to_host64(dq)[0], "k": to_host64(dk)[0], "v": to_host64(dv)[0], "a": to_host64(da)}
     X = {nm: I.widen(sl[nm][0], "bf16") for nm in ("q", "k", "v")}
+    X["a"] = sl["a"].astype(np.float64)
     dO = I.widen(sl["dO"][0], "bf16")
-    A = sl["a"].astype(np.float64)
 
-    def loss(h):
-        o, _ = oracle.fwd_unit(X["q"][h], X["k"][h], X["v"][h], float(LAM[h]), A[h], None)
+    def loss_head(P, h):
+        """L restricted to head h (the other heads do not depend on its inputs)."""
+        o, _ = oracle.fwd_unit(P["q"][h], P["k"][h], P["v"][h], float(LAM[h]), P["a"][h], None)
         return float(np.sum(dO[h] * o))
 
+    def fd_coord(nm, idx):
+        h = idx[0]
+        keep = X[nm][idx]
+        step = 1e-4 * max(1.0, abs(keep))
+        P = {k: v.copy() if k == nm else v for k, v in X.items()}
+        P[nm][idx] = keep + step
+        lp = loss_head(P, h)
+        P[nm][idx] = keep - step
+        lm = loss_head(P, h)
+        return (lp - lm) / (2 * step)
+
     rng = np.random.default_rng(64)
-    for nm in ("q", "k", "v", "a"):
-        arr = A if nm == "a" else X[nm]
-        idxs = [tuple(int(rng.integers(0, s)) for s in arr.shape) for _ in range(128)]
-        fd, an = [], []
-        for idx in idxs:
-            h = idx[0]
-            keep = arr[idx]
-            step = 1e-4 * max(1.0, abs(keep))
-            arr[idx] = keep + step
-            lp = loss(h)
-            arr[idx] = keep - step
-            lm = loss(h)
-            arr[idx] = keep
-            fd.append((lp - lm) / (2 * step))
-            an.append(g[nm][idx])
-        assert_close(np.array(an), np.array(fd), TOL["bf16"], f"d{nm} vs finite differences",
-                     store="f32" if nm == "a" else "bf16")
+    with ThreadPoolExecutor(8) as ex:
+        for nm in ("q", "k", "v", "a"):
+            arr = X[nm]
+            idxs = [tuple(int(rng.integers(0, s)) for s in arr.shape) for _ in range(512)]
+            fd = np.array(list(ex.map(lambda i: fd_coord(nm, i), idxs)))
+            an = np.array([g[nm][i] for i in idxs])
+            assert_close(an, fd, TOL["bf16"], f"d{nm} vs finite differences (512 coordinates)",
+                         store="f32" if nm == "a" else "bf16")
+        # 8 random directions through q, k, v and a at once
+        for r in range(8):
+            D = {nm: rng.standard_normal(X[nm].shape) for nm in X}
+            want = sum(float(np.sum(g[nm] * D[nm])) for nm in X)
+            eps = 1e-4
+
+            def shifted(sign):
+                P = {nm: X[nm] + sign * eps * D[nm] for nm in X}
+                return sum(ex.map(lambda h: loss_head(P, h), range(H)))
+
+            fd = (shifted(1.0) - shifted(-1.0)) / (2 * eps)
+            err = abs(want - fd) / max(abs(fd), 1e-12)
+            print(f"    direction {r}: analytic {want:.6e} fd {fd:.6e} rel err {err:.2e}", flush=True)
+            assert err <= TOL["bf16"], f"direction {r}: relative error {err:.3e}"
 
 
 def test_decode_full_64_steps():
