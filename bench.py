@@ -207,24 +207,35 @@ def bench_fwd(args, B=8, T=2048, nsets=3):
             "bytes": bytes_, "gbs": bytes_ / (ms * 1e-3) / 1e9, "flops": flops}
 
 
-def bench_fwdbwd(args, B=4, T=2048):
+def bench_fwdbwd(args, B=4, T=2048, nsets=3):
+    """B=4 forward, then backward, each timed on its own over 3 rotated
+    input/output sets (q, k, v, dO in and o, dq, dk, dv out: 0.75 GB in all,
+    beyond the 256 MB last-level cache, so every call streams from HBM)."""
     import torch
     from chunked_gated_linear_simple_amd import binding as Bd
     lam = Bd.sgla_decay_schedule(H, 1.0, 2048.0).cuda()
     a = gen((H, DK), 31, 0.1)
-    q = gen((B, H, T, DK), 200, scale=DK ** -0.5, dtype=torch.bfloat16)
-    k = gen((B, H, T, DK), 201, dtype=torch.bfloat16)
-    v = gen((B, H, T, DV), 202, dtype=torch.bfloat16)
-    dO = gen((B, H, T, DV), 203, dtype=torch.bfloat16)
-    o = torch.empty_like(v)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     da = torch.empty((H, DK), dtype=torch.float32, device="cuda")
     ws = torch.empty(Bd.sgla_chunk_bwd_workspace_bytes(B, H, DK), dtype=torch.uint8, device="cuda")
-    ms_f, _ = timed(lambda i: Bd.sgla_chunk_fwd(q, k, v, lam, a, o=o, chunk=128),
-                    args.steps, args.warmup)
-    ms_b, _ = timed(lambda i: Bd.sgla_chunk_bwd(q, k, v, dO, lam, a, chunk=128, dq=dq, dk=dk,
-                                                dv=dv, da=da, workspace=ws),
-                    args.steps, args.warmup)
+    sets = []
+    for s in range(nsets):
+        q = gen((B, H, T, DK), 200 + 10 * s, scale=DK ** -0.5, dtype=torch.bfloat16)
+        k = gen((B, H, T, DK), 201 + 10 * s, dtype=torch.bfloat16)
+        v = gen((B, H, T, DV), 202 + 10 * s, dtype=torch.bfloat16)
+        dO = gen((B, H, T, DV), 203 + 10 * s, dtype=torch.bfloat16)
+        sets.append((q, k, v, dO, torch.empty_like(v), torch.empty_like(q), torch.empty_like(k),
+                     torch.empty_like(v)))
+
+    def fwd(i):
+        q, k, v, _, o, _, _, _ = sets[i % nsets]
+        Bd.sgla_chunk_fwd(q, k, v, lam, a, o=o, chunk=128)
+
+    def bwd(i):
+        q, k, v, dO, _, dq, dk, dv = sets[i % nsets]
+        Bd.sgla_chunk_bwd(q, k, v, dO, lam, a, chunk=128, dq=dq, dk=dk, dv=dv, da=da, workspace=ws)
+
+    ms_f, _ = timed(fwd, args.steps, args.warmup)
+    ms_b, _ = timed(bwd, args.steps, args.warmup)
     toks = B * T
     # algorithmic bytes, fwd: q,k,v,o (1152/ht); bwd: reads q,k,v,dO 1152 + writes dq,dk,dv 768
     bytes_ = B * H * T * (1152 + 1920)
@@ -502,7 +513,13 @@ def cpu_baseline(min_seconds=10.0, B=8, T=2048):
     from chunked_gated_linear_simple_amd import inputs as I
     if not os.path.exists(os.path.join(ROOT, "oracle", "liboracle.so")):
         oracle.build(force=True)
-    cores = min(os.cpu_count() or 1, 16)
+    # one thread per core of the host share this process may use; the GPU
+    # hosts here give a one-GPU job 16 CPUs whatever the machine reports
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    cores = min(avail, 16)
     lam = oracle.decay_schedule(H, 1.0, 2048.0)
     inp = I.chunk_inputs(B, H, T, DK, DV, "bf16", seed=2, a_std=0.1)
     work = [(I.widen(inp["q"][n, h], "bf16"), I.widen(inp["k"][n, h], "bf16"),
@@ -589,7 +606,7 @@ def main():
             "config": {"workload": "Laplace layer fwd B=8 H=16 T=2048 dk=96 dv=192 chunk=128 "
                                    "bf16, fp32 state, final state written",
                        "batch": 8, "seq_len": 2048, "heads": H, "d_k": DK, "d_v": DV,
-                       "chunk": 128},
+                       "chunk": 128, "tile_tokens": 64},
             "ms_median": fwd["ms_median"], "ms_min": fwd["ms_min"],
             "roofline": {"bound": "hbm", "kernel": "k_fwd", "achieved": fwd["gbs"],
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": fwd["gbs"] / HBM_PEAK_GBS,
