@@ -68,6 +68,9 @@ def lib() -> ctypes.CDLL:
                                      _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp,
                                      ctypes.c_size_t, _vp]
         L.sgla_chunk_bwd.restype = _i
+        L.sgla_chunk_bwd_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                             _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp]
+        L.sgla_chunk_bwd_noalloc.restype = _i
         L.sgla_decode_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
                                        _i, _vp]
         L.sgla_decode_step.restype = _i
@@ -294,6 +297,39 @@ def sgla_chunk_bwd(q, k, v, dO, lam, a=None, init_state=None, d_final_state=None
                                 _ptr(dv), _ptr(da), _ptr(d_init_state), _ptr(cu_seqlens), n_seq,
                                 B, H, T, d_k, d_v, int(chunk), _dtype_code(q), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(dev)))
+    return dq, dk, dv, da, d_init_state
+
+
+def sgla_chunk_bwd_noalloc(q, k, v, dO, lam, a=None, init_state=None, d_final_state=None,
+                           cu_seqlens=None, chunk: int = 128, dq=None, dk=None, dv=None, da=None,
+                           d_init_state=None):
+    """sgla_chunk_bwd without a workspace: the library's fixed device scratch
+    holds the partial sums. All outputs must be passed (the entry point is for
+    callers that allocate nothing while it runs). Returns (dq, dk, dv, da,
+    d_init_state)."""
+    dev = q.device
+    B, H, T, d_k, d_v, n_seq = _geometry(q, v, cu_seqlens)
+    for t, nm in ((dq, "dq"), (dk, "dk"), (dv, "dv"), (da, "da")):
+        if t is None:
+            raise ValueError(f"{nm} must be passed")
+    _need(q, "q", device=dev)
+    _need(k, "k", q.dtype, dev, q.shape)
+    _need(v, "v", q.dtype, dev, (B, H, T, d_v))
+    _need(dO, "dO", q.dtype, dev, (B, H, T, d_v))
+    _need(lam, "lambda", torch.float32, dev, (H,))
+    _need(a, "a", torch.float32, dev, (H, d_k))
+    _need(init_state, "init_state", torch.float32, dev, (n_seq, H, d_k, d_v))
+    _need(d_final_state, "d_final_state", torch.float32, dev, (n_seq, H, d_k, d_v))
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    for t, nm, shp in ((dq, "dq", q.shape), (dk, "dk", q.shape), (dv, "dv", v.shape)):
+        _need(t, nm, q.dtype, dev, shp)
+    _need(da, "da", torch.float32, dev, (H, d_k))
+    _need(d_init_state, "d_init_state", torch.float32, dev, (n_seq, H, d_k, d_v))
+    _check(lib().sgla_chunk_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lam), _ptr(a),
+                                        _ptr(init_state), _ptr(d_final_state), _ptr(dq), _ptr(dk),
+                                        _ptr(dv), _ptr(da), _ptr(d_init_state), _ptr(cu_seqlens),
+                                        n_seq, B, H, T, d_k, d_v, int(chunk), _dtype_code(q),
+                                        _stream(dev)))
     return dq, dk, dv, da, d_init_state
 
 

@@ -17,7 +17,7 @@ LIB = os.path.join(PKG, "libsgla.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["sgla_api.cpp", "sgla_chunk.hip", "sgla_fwd.hip", "sgla_bwd.hip", "sgla_decode.hip",
-           "sgla_conv.hip", "sgla_norm.hip"]
+           "sgla_conv.hip", "sgla_norm.hip", "sgla_noalloc.hip"]
 # Per-source flags. The column-owner kernels keep matrix-core accumulators in
 # architectural VGPRs: their state and output tiles are read by VALU code every
 # tile, and accumulators placed in AGPRs cost a copy in each direction.

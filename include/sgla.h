@@ -289,6 +289,38 @@ sgla_status sgla_chunk_bwd(const void* q, const void* k, const void* v, const vo
                            void* hip_stream);
 
 /*
+ * Bytes of the fixed device scratch array behind sgla_chunk_bwd_noalloc.
+ */
+#define SGLA_NOALLOC_SCRATCH_BYTES (4 * 1024 * 1024)
+
+/*
+ * sgla_chunk_bwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. It computes exactly what sgla_chunk_bwd
+ * computes, with the same kernels, and calls no allocating routine. The
+ * scratch those kernels need (the partial sums of da, sgla_chunk_bwd_workspace_bytes
+ * bytes) comes from a fixed array of SGLA_NOALLOC_SCRATCH_BYTES in device
+ * memory that the library holds on every GPU it runs on until the process
+ * ends; its device address is looked up on the first call made on each
+ * device. Every call on a GPU reuses that GPU's array, and every call
+ * overwrites all of the scratch it reads, so no state carries between calls;
+ * calls that overlap in time on one GPU (on different streams, or from
+ * different threads) race on the array and must not be issued.
+ *
+ * Arguments, layouts and errors: as sgla_chunk_bwd, without workspace and
+ * workspace_bytes; argument errors are reported before any GPU call, and
+ * SGLA_ERR_WORKSPACE when the da partial sums (N * H * d_k floats, N = n_seq
+ * or B) exceed SGLA_NOALLOC_SCRATCH_BYTES (for H = 16, d_k = 96: N <= 682).
+ */
+sgla_status sgla_chunk_bwd_noalloc(const void* q, const void* k, const void* v, const void* dO,
+                                   const float* lambda, const float* a,
+                                   const float* init_state, const float* d_final_state,
+                                   void* dq, void* dk, void* dv, float* da, float* d_init_state,
+                                   const int32_t* cu_seqlens, int n_seq,
+                                   int B, int H, int T, int d_k, int d_v, int chunk,
+                                   sgla_dtype dtype, void* hip_stream);
+
+/*
  * One decode step for N sequences, in place on their states. Laplace 3B post,
  * "Inference optimization on Trainium2", paragraphs "Constant serving state"
  * and "Unmodified vLLM": each sequence keeps a fixed-size recurrent state in

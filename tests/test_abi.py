@@ -203,6 +203,26 @@ def test_chunk_bwd_rejects(L, name, kw, code):
     assert L.sgla_last_error().decode() != ""
 
 
+NOALLOC_BAD = [x for x in BWD_BAD if "workspace" not in x[0]] + [
+    ("scratch too small for 700 sequences", dict(B=700), B.SGLA_ERR_WORKSPACE),
+    ("scratch too small for 683 packed sequences",
+     dict(B=1, cu=P["cu"], n_seq=683, T=4096), B.SGLA_ERR_WORKSPACE),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", NOALLOC_BAD, ids=[x[0] for x in NOALLOC_BAD])
+def test_chunk_bwd_noalloc_rejects(L, name, kw, code):
+    """The allocation-free backward reports argument errors before any GPU
+    call, and refuses sizes whose da partial sums exceed its fixed scratch."""
+    args = bwd_args(**kw)
+    del args[22:24]  # no workspace arguments
+    assert L.sgla_chunk_bwd_noalloc(*args) == code
+    msg = L.sgla_last_error().decode()
+    assert msg != ""
+    if "scratch" in name:
+        assert "scratch" in msg and str(4 * 1024 * 1024) in msg
+
+
 def test_workspace_bytes(L):
     assert B.sgla_chunk_bwd_workspace_bytes(4, 16, 96) == 4 * 16 * 96 * 4
     assert B.sgla_chunk_bwd_workspace_bytes(0, 16, 96) == 0
