@@ -27,20 +27,17 @@
 //   Qs, Ks   [C][DK]   natural (rows = tokens)      -- scores, Q'S, (q'.k')
 //   KTs      [DK][C]   k' transposed, unscaled      -- state update
 //   VTs      [DVS][C]  v' slice transposed          -- P.V', state update, epilogue
-//   STh, STl [DVS][DK] state^T as a bf16 hi + lo pair -- Q'S
+//   STh      [DVS][DK] state^T                       -- Q'S
 //   ksc      [C]       lam^(C_c-1-j), the key decays of the state update
 // Waves 0..C/32-1 each own 32 query rows: they compute Q'S, the decay-masked
 // score tiles K' Q'^T (kept in registers and fed straight back as the A
 // operand of P.V'), the epilogue, and store. The state tiles are spread over
 // the waves by a compile-time balance of the per-chunk matrix-core work.
 //
-// Precision (bf16 operands, fp32 accumulation): the two operands that carry
-// the long-memory state -- the state itself in Q'S and the decayed keys
-// lam^m k' of the state update -- are split into bf16 hi + lo pairs and fed
-// as two MFMAs, so they keep ~16 significant bits; only the per-chunk decayed
-// scores P enter the matrix cores rounded once to bf16.
+// Precision: every operand and product is fp32 (v_mfma_f32_32x32x2_f32); the
+// only roundings are those of fp32 arithmetic.
 //
-// MFMA: v_mfma_f32_32x32x16_bf16 (bf16) or v_mfma_f32_32x32x2_f32 (fp32).
+// MFMA: v_mfma_f32_32x32x2_f32 (one contraction step of 2 per instruction).
 // For a 32x32 result, lane l holds column l%32 and rows 8*(i/4)+4*(l/32)+i%4
 // in accumulator i. Operand lanes hold row (A) / column (B) l%32; lane group
 // l/32 selects the slice of the contraction index. The pairing of contraction
@@ -55,10 +52,6 @@
 namespace sgla {
 namespace {
 
-typedef unsigned short u16;
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef u16 u16x8_t __attribute__((ext_vector_type(8)));
-typedef u16 u16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -66,16 +59,10 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int NTHREADS = 256;
 constexpr int NWAVES = 4;
 
-__device__ __forceinline__ float to_f(u16 x) { return __uint_as_float((uint32_t)x << 16); }
 __device__ __forceinline__ float to_f(float x) { return x; }
 
 template <typename E> __device__ __forceinline__ E from_f(float x);
 template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
-template <> __device__ __forceinline__ u16 from_f<u16>(float x)
-{
-    // round to nearest even (the C++ conversion to __bf16)
-    return __builtin_bit_cast(u16, static_cast<__bf16>(x));
-}
 
 // 2^x on the transcendental unit (v_exp_f32). Results below the smallest
 // normal fp32 flush to zero; decays that small contribute nothing here.
@@ -97,35 +84,15 @@ __device__ __forceinline__ float sigmoidf_(float z)
 // Element e of a 16-byte register vector holding E values, widened to fp32.
 // (Bit operations on native vectors keep these registers out of memory.)
 template <typename E> __device__ __forceinline__ float vget(const u32x4_t& v, int e);
-template <> __device__ __forceinline__ float vget<u16>(const u32x4_t& v, int e)
-{
-    const uint32_t w = v[e >> 1];
-    return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
-}
 template <> __device__ __forceinline__ float vget<float>(const u32x4_t& v, int e)
 {
     return __uint_as_float(v[e]);
 }
 
 template <typename E> struct Mfma;
-template <> struct Mfma<u16> {
-    static constexpr int KSTEP = 16;  // contraction per instruction
-    static constexpr int NE = 8;      // operand elements per lane
-    static constexpr int HILO = 2;    // instructions per split operand
-    typedef bf16x8_t op_t;
-    static __device__ __forceinline__ op_t load(const u16* p)
-    {
-        return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u16x8_t*>(p));
-    }
-    static __device__ __forceinline__ f32x16_t mma(op_t a, op_t b, f32x16_t c)
-    {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-    }
-};
 template <> struct Mfma<float> {
     static constexpr int KSTEP = 2;
     static constexpr int NE = 1;
-    static constexpr int HILO = 1;
     typedef float op_t;
     static __device__ __forceinline__ op_t load(const float* p) { return *p; }
     static __device__ __forceinline__ f32x16_t mma(op_t a, op_t b, f32x16_t c)
@@ -186,17 +153,16 @@ struct Role {
     typedef Mfma<E> M;
     static constexpr int DK = DK_, DVS = DVS_, C = C_, AUG = AUG_;
     static constexpr bool REV = REV_;
-    static constexpr int HILO = M::HILO;
     static constexpr int PE = 16 / (int)sizeof(E);  // 16-byte row padding
-    static constexpr int LDQ = DK + PE;             // Qs, Ks, STh, STl row stride
+    static constexpr int LDQ = DK + PE;             // Qs, Ks, STh row stride
     static constexpr int LDT = C + PE;              // KTs, VTs, XTs row stride
     static constexpr int NSTRIP = C / 32;
     static constexpr int NNT = DVS / 32;
     static constexpr int NDB = DK / 32;
     static constexpr int NTILES = NDB * NNT;
     static constexpr Owners OWN =
-        balance(NSTRIP, (DK / M::KSTEP) * NNT * HILO, DK / M::KSTEP + NNT * (32 / M::KSTEP),
-                NNT * (C / M::KSTEP) * HILO, NDB);
+        balance(NSTRIP, (DK / M::KSTEP) * NNT, DK / M::KSTEP + NNT * (32 / M::KSTEP),
+                NNT * (C / M::KSTEP), NDB);
     static constexpr int NDBW = OWN.max_count;  // d-blocks per wave (at most)
     static constexpr size_t SZ_ROWS = (size_t)C * LDQ * sizeof(E);
     static constexpr size_t SZ_ST = (size_t)DVS * LDQ * sizeof(E);
@@ -205,8 +171,7 @@ struct Role {
     static constexpr size_t OFF_KT = OFF_K + SZ_ROWS;
     static constexpr size_t OFF_VT = OFF_KT + (size_t)DK * LDT * sizeof(E);
     static constexpr size_t OFF_STH = OFF_VT + (size_t)DVS * LDT * sizeof(E);
-    static constexpr size_t OFF_STL = OFF_STH + SZ_ST;
-    static constexpr size_t OFF_XT = OFF_STL + (HILO == 2 ? SZ_ST : 0);
+    static constexpr size_t OFF_XT = OFF_STH + SZ_ST;
     static constexpr size_t OFF_COEF = OFF_XT + (AUG == AUG_GRAD ? (size_t)DVS * LDT * sizeof(E) : 0);
     static constexpr size_t OFF_KSC = OFF_COEF + (size_t)C * sizeof(float);
     static constexpr int AWN = DK > 128 ? DK : 128;  // staged width of a
@@ -262,7 +227,6 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
     constexpr int C = R::C, DK = R::DK, DVS = R::DVS, LDQ = R::LDQ, LDT = R::LDT;
     constexpr int NSTRIP = R::NSTRIP, NNT = R::NNT, NDBW = R::NDBW;
     constexpr int KSTEP = M::KSTEP, NE = M::NE;
-    constexpr bool SPLIT = (R::HILO == 2);
     constexpr int V16 = 16 / (int)sizeof(E);  // elements per 16-byte segment
 
     E* Qs = reinterpret_cast<E*>(smem + R::OFF_Q);
@@ -270,7 +234,6 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
     E* KTs = reinterpret_cast<E*>(smem + R::OFF_KT);
     E* VTs = reinterpret_cast<E*>(smem + R::OFF_VT);
     E* STh = reinterpret_cast<E*>(smem + R::OFF_STH);
-    E* STl = reinterpret_cast<E*>(smem + R::OFF_STL);
     E* XTs = reinterpret_cast<E*>(smem + R::OFF_XT);
     float* coef = reinterpret_cast<float*>(smem + R::OFF_COEF);
     float* ksc = reinterpret_cast<float*>(smem + R::OFF_KSC);
@@ -405,15 +368,10 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
     };
     // element e of two rows, packed for a single transposed LDS write
     auto put_pair = [](E* dst, const u32x4_t& r0, const u32x4_t& r1, int e) {
-        if constexpr (sizeof(E) == 2) {
-            const uint32_t w0 = r0[e >> 1], w1 = r1[e >> 1];
-            *reinterpret_cast<uint32_t*>(dst) =
-                (e & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u)) : ((w0 & 0xffffu) | (w1 << 16));
-        } else {
-            typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-            u32x2_t pr = {r0[e], r1[e]};
-            *reinterpret_cast<u32x2_t*>(dst) = pr;
-        }
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        u32x2_t pr = {r0[e], r1[e]};
+        *reinterpret_cast<u32x2_t*>(dst) = pr;
+    
     };
     const u32x4_t zero4 = {0u, 0u, 0u, 0u};
     auto store_chunk = [&](int cl) {
@@ -470,7 +428,7 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
 
         lds_barrier();  // previous chunk's LDS readers are done
 
-        // state before this chunk -> STh (+ STl), transposed; the four
+        // state before this chunk -> STh, transposed; the four
         // consecutive state rows of an accumulator group go out as one write
 #pragma unroll
         for (int kt = 0; kt < NDBW * NNT; ++kt) {
@@ -481,23 +439,11 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
 #pragma unroll
                 for (int qd = 0; qd < 4; ++qd) {
                     const int off = nl * LDQ + 32 * db + 8 * qd + 4 * g;
-                    if constexpr (sizeof(E) == 2) {
-                        u16x4_t hv, lv;
+                    f32x4_t hv;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float x = acc[4 * qd + e];
-                            const u16 hb = from_f<u16>(x);
-                            hv[e] = hb;
-                            lv[e] = from_f<u16>(x - to_f(hb));
-                        }
-                        *reinterpret_cast<u16x4_t*>(STh + off) = hv;
-                        *reinterpret_cast<u16x4_t*>(STl + off) = lv;
-                    } else {
-                        f32x4_t hv;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) hv[e] = acc[4 * qd + e];
-                        *reinterpret_cast<f32x4_t*>(STh + off) = hv;
-                    }
+                    for (int e = 0; e < 4; ++e) hv[e] = acc[4 * qd + e];
+                    *reinterpret_cast<f32x4_t*>(STh + off) = hv;
+                
                 }
             }
         }
@@ -564,7 +510,6 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
                 for (int nt = 0; nt < NNT; ++nt) {
                     const int boff = (32 * nt + l32) * LDQ + kb * KSTEP + g * NE;
                     oacc[nt] = M::mma(av, M::load(STh + boff), oacc[nt]);
-                    if (SPLIT) oacc[nt] = M::mma(av, M::load(STl + boff), oacc[nt]);
                 }
             }
             // rows scale by lam^(t+1), or lam^t where the carried state enters
@@ -595,34 +540,15 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
                     const float f = (diff == 0) ? 1.0f : fast_exp2((float)diff * l2);
                     sc[i] = (diff < 0) ? 0.0f : sc[i] * f;
                 }
-                if constexpr (sizeof(E) == 2) {
-                    // two contraction steps of 16 keys: step hh uses sc[8hh..8hh+7],
-                    // i.e. keys 16hh + {4g..4g+3, 8+4g..8+4g+3}
 #pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        u16x8_t pw;
+                for (int s = 0; s < 16; ++s) {
 #pragma unroll
-                        for (int s = 0; s < 8; ++s) pw[s] = from_f<u16>(sc[8 * hh + s]);
-                        const bf16x8_t pa = __builtin_bit_cast(bf16x8_t, pw);
-#pragma unroll
-                        for (int nt = 0; nt < NNT; ++nt) {
-                            const E* vb = VTs + (32 * nt + l32) * LDT + 32 * jb + 16 * hh + 4 * g;
-                            const u16x4_t lo = *reinterpret_cast<const u16x4_t*>(vb);
-                            const u16x4_t hi = *reinterpret_cast<const u16x4_t*>(vb + 8);
-                            const u16x8_t bw = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                            oacc[nt] = M::mma(pa, __builtin_bit_cast(bf16x8_t, bw), oacc[nt]);
-                        }
-                    }
-                } else {
-#pragma unroll
-                    for (int s = 0; s < 16; ++s) {
-#pragma unroll
-                        for (int nt = 0; nt < NNT; ++nt) {
-                            const float bv = to_f(VTs[(32 * nt + l32) * LDT + 32 * jb + acc_row(s, g)]);
-                            oacc[nt] = M::mma(sc[s], bv, oacc[nt]);
-                        }
+                    for (int nt = 0; nt < NNT; ++nt) {
+                        const float bv = to_f(VTs[(32 * nt + l32) * LDT + 32 * jb + acc_row(s, g)]);
+                        oacc[nt] = M::mma(sc[s], bv, oacc[nt]);
                     }
                 }
+            
             }
 
             // epilogue: + coef_t * w_n * v'_t[n]  (w = 1, or a for the gradient
@@ -638,25 +564,15 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
                     const int t = t0 + 8 * qd + 4 * g;
                     const f32x4_t cf = *reinterpret_cast<const f32x4_t*>(coef + t);
                     float vt[4], xt[4];
-                    if constexpr (sizeof(E) == 2) {
-                        const u16x4_t v4 = *reinterpret_cast<const u16x4_t*>(VTs + nl * LDT + t);
-                        u16x4_t x4 = {0, 0, 0, 0};
-                        if (R::AUG == AUG_GRAD) x4 = *reinterpret_cast<const u16x4_t*>(XTs + nl * LDT + t);
+                    const f32x4_t v4 = *reinterpret_cast<const f32x4_t*>(VTs + nl * LDT + t);
+                    f32x4_t x4 = {0.f, 0.f, 0.f, 0.f};
+                    if (R::AUG == AUG_GRAD) x4 = *reinterpret_cast<const f32x4_t*>(XTs + nl * LDT + t);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            vt[e] = to_f((u16)v4[e]);
-                            xt[e] = to_f((u16)x4[e]);
-                        }
-                    } else {
-                        const f32x4_t v4 = *reinterpret_cast<const f32x4_t*>(VTs + nl * LDT + t);
-                        f32x4_t x4 = {0.f, 0.f, 0.f, 0.f};
-                        if (R::AUG == AUG_GRAD) x4 = *reinterpret_cast<const f32x4_t*>(XTs + nl * LDT + t);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            vt[e] = v4[e];
-                            xt[e] = x4[e];
-                        }
+                    for (int e = 0; e < 4; ++e) {
+                        vt[e] = v4[e];
+                        xt[e] = x4[e];
                     }
+                
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         oacc[nt][4 * qd + e] += cf[e] * wn * vt[e];
@@ -687,34 +603,13 @@ __device__ __forceinline__ void role_body(const Common& cm, const RoleArgs& ra, 
                 for (int kb = 0; kb < C / KSTEP; ++kb) {
                     const int j0 = kb * KSTEP + g * NE;
                     const E* kr = KTs + (32 * db + l32) * LDT + j0;
-                    if constexpr (sizeof(E) == 2) {
-                        const u16x8_t kw = *reinterpret_cast<const u16x8_t*>(kr);
-                        const f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(ksc + j0);
-                        const f32x4_t s1 = *reinterpret_cast<const f32x4_t*>(ksc + j0 + 4);
-                        u16x8_t hw, lw;
+                    const float av = to_f(*kr) * ksc[j0];
 #pragma unroll
-                        for (int s = 0; s < 8; ++s) {
-                            const float x = to_f((u16)kw[s]) * (s < 4 ? s0[s] : s1[s - 4]);
-                            const u16 hb = from_f<u16>(x);
-                            hw[s] = hb;
-                            lw[s] = from_f<u16>(x - to_f(hb));
-                        }
-                        const bf16x8_t ha = __builtin_bit_cast(bf16x8_t, hw);
-                        const bf16x8_t la = __builtin_bit_cast(bf16x8_t, lw);
-#pragma unroll
-                        for (int nb = 0; nb < NNT; ++nb) {
-                            const typename M::op_t bv = M::load(VTs + (32 * nb + l32) * LDT + j0);
-                            sacc[kk * NNT + nb] = M::mma(ha, bv, sacc[kk * NNT + nb]);
-                            sacc[kk * NNT + nb] = M::mma(la, bv, sacc[kk * NNT + nb]);
-                        }
-                    } else {
-                        const float av = to_f(*kr) * ksc[j0];
-#pragma unroll
-                        for (int nb = 0; nb < NNT; ++nb) {
-                            const typename M::op_t bv = M::load(VTs + (32 * nb + l32) * LDT + j0);
-                            sacc[kk * NNT + nb] = M::mma(av, bv, sacc[kk * NNT + nb]);
-                        }
+                    for (int nb = 0; nb < NNT; ++nb) {
+                        const typename M::op_t bv = M::load(VTs + (32 * nb + l32) * LDT + j0);
+                        sacc[kk * NNT + nb] = M::mma(av, bv, sacc[kk * NNT + nb]);
                     }
+                
                 }
             }
         }
