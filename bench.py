@@ -1,6 +1,6 @@
 """Benchmark of the Simple GLA hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only fwd|fwdbwd|decode|varlen|long|norm|conv|tiny]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only fwd|fwdbwd|decode|varlen|long|norm|fused|conv|tiny]
                     [--no-cpu]
 
 Prints ONE JSON line. The headline ("value") is the Laplace-layer forward:
@@ -117,8 +117,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--only", choices=["fwd", "fwdbwd", "decode", "varlen", "long", "norm", "conv",
-                                       "tiny"],
+    ap.add_argument("--only", choices=["fwd", "fwdbwd", "decode", "varlen", "long", "norm", "fused",
+                                       "conv", "tiny"],
                     default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--min-warm-s", type=float, default=1.5,
@@ -380,6 +380,50 @@ def bench_norm(args, B=8, T=2048, n_tiers=4, nsets=3):
             "gbs": bytes_ / (ms * 1e-3) / 1e9}
 
 
+def bench_fused(args, B=8, T=2048, n_tiers=4, nsets=3):
+    """The forward with the mixer epilogue applied before the store (one
+    cooperative launch) against the two-launch pipeline sgla_chunk_fwd then
+    sgla_head_norm_gate, on the same inputs: the headline workload plus the
+    gate stream g [B, T, H, d_v], out [B, T, H, d_v], final state written;
+    3 input sets rotated (1.5 GB)."""
+    import torch
+    from chunked_gated_linear_simple_amd import binding as Bd
+    lam = Bd.sgla_decay_schedule(H, 1.0, 2048.0).cuda()
+    a = gen((H, DK), 41, 0.1)
+    gm = (1.0 + gen((n_tiers, DV), 42, 0.1)).contiguous()
+    x = torch.zeros(Bd.FWD_NORM_GATE_EXCHANGE_BYTES, dtype=torch.uint8, device="cuda")
+    sets = []
+    for s in range(nsets):
+        q = gen((B, H, T, DK), 300 + 10 * s, scale=DK ** -0.5, dtype=torch.bfloat16)
+        k = gen((B, H, T, DK), 301 + 10 * s, dtype=torch.bfloat16)
+        v = gen((B, H, T, DV), 302 + 10 * s, dtype=torch.bfloat16)
+        g = gen((B, T, H, DV), 303 + 10 * s, dtype=torch.bfloat16)
+        sets.append((q, k, v, g, torch.empty_like(g), torch.empty_like(v),
+                     torch.empty((B, H, DK, DV), dtype=torch.float32, device="cuda")))
+
+    def fused(i):
+        q, k, v, g, out, _, sf = sets[i % nsets]
+        Bd.sgla_chunk_fwd_norm_gate(q, k, v, lam, g, a=a, gamma=gm, n_tiers=n_tiers, eps=1e-6,
+                                    final_state=sf, out=out, chunk=128, exchange=x)
+
+    def pair(i):
+        q, k, v, g, out, o, sf = sets[i % nsets]
+        Bd.sgla_chunk_fwd(q, k, v, lam, a, final_state=sf, o=o, chunk=128)
+        Bd.sgla_head_norm_gate(o, g, gm, n_tiers, 1e-6, out=out)
+
+    st = timed_stats(fused, args.steps, args.warmup)
+    ms_pair, _ = timed(pair, args.steps, args.warmup)
+    torch.cuda.synchronize()
+    if int(torch.count_nonzero(x).item()) != 0:
+        raise RuntimeError("fused forward: the exchange buffer is not zero-filled after the calls")
+    toks = B * T
+    # q, k, v, g read and out written (bf16), the final state written (fp32)
+    bytes_ = B * H * T * (2 * DK + 3 * DV) * 2 + B * H * STATE_BYTES + n_tiers * DV * 4
+    return {"ms": st["mean"], "ms_median": st["median"], "ms_two_launches": ms_pair, "tokens": toks,
+            "tok_s": toks / (st["mean"] * 1e-3), "tok_s_two_launches": toks / (ms_pair * 1e-3),
+            "bytes": bytes_, "gbs": bytes_ / (st["mean"] * 1e-3) / 1e9}
+
+
 def bench_norm_bwd(args, B=8, T=2048, n_tiers=4, nsets=2):
     """Gradients of the mixer epilogue at the Laplace layer's size: o, g,
     dout in (bf16), d_o and dg out (bf16), dgamma [4, 192] fp32 through the
@@ -587,6 +631,8 @@ def main():
     if only in (None, "norm"):
         secondary["head_norm_gate_B8_T2048"] = bench_norm(args)
         secondary["head_norm_gate_bwd_B8_T2048"] = bench_norm_bwd(args)
+    if only in (None, "fused"):
+        secondary["fwd_norm_gate_B8_T2048"] = bench_fused(args)
     if only in (None, "tiny"):
         secondary["tiny_fp32_B1_H2_T256"] = bench_tiny(args)
     if only in (None, "conv"):

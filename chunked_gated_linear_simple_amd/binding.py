@@ -21,6 +21,8 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "sgla.h")
 
 SGLA_OK, SGLA_ERR_INVALID_ARG, SGLA_ERR_UNSUPPORTED, SGLA_ERR_WORKSPACE, SGLA_ERR_HIP = range(5)
 SGLA_F32, SGLA_BF16 = 0, 1
+# SGLA_FWD_NORM_GATE_EXCHANGE_BYTES of include/sgla.h
+FWD_NORM_GATE_EXCHANGE_BYTES = 2 * 1024 * 1024 + 256
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -51,6 +53,10 @@ def lib() -> ctypes.CDLL:
         L.sgla_chunk_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i,
                                      _i, _i, _i, _i, _i, _i, _i, _vp]
         L.sgla_chunk_fwd.restype = _i
+        L.sgla_chunk_fwd_norm_gate.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                               _i, _i, _i, _i, _i, _i, _i, _i, ctypes.c_float, _i, _vp,
+                                               ctypes.c_size_t, _vp]
+        L.sgla_chunk_fwd_norm_gate.restype = _i
         L.sgla_chunk_fwd_segmented_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
         L.sgla_chunk_fwd_segmented_workspace_bytes.restype = ctypes.c_size_t
         L.sgla_chunk_fwd_segmented.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i,
@@ -179,6 +185,57 @@ def sgla_chunk_fwd(q, k, v, lam, a=None, init_state=None, final_state=None, o=No
                                 n_seq, B, H, T, d_k, d_v, int(chunk), _dtype_code(q),
                                 _stream(dev)))
     return o, final_state
+
+
+_exchange = {}
+
+
+def fwd_norm_gate_exchange(device) -> torch.Tensor:
+    """The device's zero-filled exchange buffer for sgla_chunk_fwd_norm_gate
+    (allocated on first use; every completed call leaves it zero-filled). A
+    caller running calls on several streams at once passes its own buffers."""
+    device = torch.device(device)
+    if device not in _exchange:
+        _exchange[device] = torch.zeros(FWD_NORM_GATE_EXCHANGE_BYTES, dtype=torch.uint8, device=device)
+    return _exchange[device]
+
+
+def sgla_chunk_fwd_norm_gate(q, k, v, lam, g, a=None, gamma=None, n_tiers: int = 1, eps: float = 1e-6,
+                             init_state=None, final_state=None, out=None, o=None, cu_seqlens=None,
+                             chunk: int = 128, want_final: bool = False, want_o: bool = False, exchange=None):
+    """Chunked forward with the mixer epilogue before the store. g and out are
+    [B, T, H, d_v] (or [B, T, H * d_v]), token-major. Returns (out, o,
+    final_state); o and final_state are None unless passed or wanted."""
+    dev = q.device
+    B, H, T, d_k, d_v, n_seq = _geometry(q, v, cu_seqlens)
+    _need(q, "q", device=dev)
+    _need(k, "k", q.dtype, dev, q.shape)
+    _need(v, "v", q.dtype, dev, (B, H, T, d_v))
+    _need(lam, "lambda", torch.float32, dev, (H,))
+    _need(a, "a", torch.float32, dev, (H, d_k))
+    _need(gamma, "gamma", torch.float32, dev, (n_tiers, d_v))
+    _need(init_state, "init_state", torch.float32, dev, (n_seq, H, d_k, d_v))
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    gshape = (B, T, H * d_v) if g.dim() == 3 else (B, T, H, d_v)
+    _need(g, "g", q.dtype, dev, gshape)
+    if out is None:
+        out = torch.empty(gshape, dtype=q.dtype, device=dev)
+    _need(out, "out", q.dtype, dev, gshape)
+    if o is None and want_o:
+        o = torch.empty((B, H, T, d_v), dtype=q.dtype, device=dev)
+    _need(o, "o", q.dtype, dev, (B, H, T, d_v))
+    if final_state is None and want_final:
+        final_state = torch.empty((n_seq, H, d_k, d_v), dtype=torch.float32, device=dev)
+    _need(final_state, "final_state", torch.float32, dev, (n_seq, H, d_k, d_v))
+    if exchange is None:
+        exchange = fwd_norm_gate_exchange(dev)
+    _need(exchange, "exchange", torch.uint8, dev)
+    _check(lib().sgla_chunk_fwd_norm_gate(_ptr(q), _ptr(k), _ptr(v), _ptr(lam), _ptr(a), _ptr(init_state),
+                                          _ptr(final_state), _ptr(g), _ptr(gamma), _ptr(out), _ptr(o),
+                                          _ptr(cu_seqlens), n_seq, B, H, T, d_k, d_v, int(chunk), int(n_tiers),
+                                          float(eps), _dtype_code(q), _ptr(exchange), exchange.numel(),
+                                          _stream(dev)))
+    return out, o, final_state
 
 
 def sgla_chunk_fwd_segmented_workspace_bytes(B: int, H: int, d_k: int, d_v: int,

@@ -260,6 +260,55 @@ sgla_status sgla_chunk_fwd(const void* q, const void* k, const void* v, const fl
     return ok();
 }
 
+sgla_status sgla_chunk_fwd_norm_gate(const void* q, const void* k, const void* v, const float* lambda,
+                                     const float* a, const float* init_state, float* final_state, const void* g,
+                                     const float* gamma, void* out, void* o, const int32_t* cu_seqlens, int n_seq,
+                                     int B, int H, int T, int d_k, int d_v, int chunk, int n_tiers, float eps,
+                                     sgla_dtype dtype, void* exchange, size_t exchange_bytes, void* hip_stream)
+{
+    sgla::ChunkProblem p;
+    sgla_status st = check_chunk(q, k, v, lambda, a, cu_seqlens, n_seq, B, H, T, d_k, d_v, chunk,
+                                 dtype, &p);
+    if (st != SGLA_OK) return st;
+    if (dtype != SGLA_BF16)
+        return fail(SGLA_ERR_UNSUPPORTED, "the fused forward and epilogue is bf16 only");
+    REQUIRE_PTR(g);
+    REQUIRE_PTR(out);
+    OPTIONAL_PTR(o);
+    OPTIONAL_PTR(gamma);
+    OPTIONAL_PTR(init_state);
+    OPTIONAL_PTR(final_state);
+    if (exchange == nullptr || !aligned16(exchange))
+        return fail(SGLA_ERR_WORKSPACE, "exchange must be a 16-byte aligned device buffer");
+    if (exchange_bytes < SGLA_FWD_NORM_GATE_EXCHANGE_BYTES)
+        return fail(SGLA_ERR_WORKSPACE, "exchange holds %zu bytes, needs %zu", exchange_bytes,
+                    (size_t)SGLA_FWD_NORM_GATE_EXCHANGE_BYTES);
+    if (n_tiers <= 0 || H % n_tiers != 0)
+        return fail(SGLA_ERR_INVALID_ARG, "n_tiers (%d) must be positive and divide H (%d)", n_tiers, H);
+    if (!(eps >= 0.0f) || !std::isfinite(eps))
+        return fail(SGLA_ERR_INVALID_ARG, "eps must be finite and >= 0 (got %g)", (double)eps);
+    const size_t nqk = (size_t)B * H * T * d_k * 2, nvo = (size_t)B * H * T * d_v * 2;
+    const size_t nst = (size_t)p.n_seq * H * d_k * d_v * sizeof(float);
+    const size_t nexc = SGLA_FWD_NORM_GATE_EXCHANGE_BYTES;
+    st = check_final_state(final_state, init_state, q, k, v, o, p.n_seq, H, d_k, d_v, nqk, nvo);
+    if (st != SGLA_OK) return st;
+    // out may be g itself (each lane reads its gate values before it writes
+    // them), and final_state init_state (in-place carry): then only the
+    // written buffer is listed
+    const Span rd[8] = {{q, nqk, "q"}, {k, nqk, "k"}, {v, nvo, "v"}, {lambda, (size_t)H * sizeof(float), "lambda"},
+                        {a, (size_t)H * d_k * sizeof(float), "a"},
+                        {final_state == init_state ? nullptr : init_state, nst, "init_state"},
+                        {gamma, (size_t)n_tiers * d_v * sizeof(float), "gamma"}, {out == g ? nullptr : g, nvo, "g"}};
+    const Span wr[4] = {{out, nvo, "out"}, {o, nvo, "o"}, {final_state, nst, "final_state"},
+                        {exchange, nexc, "workspace"}};
+    st = check_disjoint(wr, 4, rd, 8);
+    if (st != SGLA_OK) return st;
+    hipError_t e = sgla::launch_fwd_norm_gate_bf16(p, q, k, v, init_state, final_state, g, gamma, out, o, n_tiers,
+                                                   eps, exchange, reinterpret_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(SGLA_ERR_HIP, "chunk_fwd_norm_gate launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 size_t sgla_chunk_fwd_segmented_workspace_bytes(int B, int H, int d_k, int d_v, int n_segments)
 {
     if (B <= 0 || H <= 0 || d_k <= 0 || d_v <= 0 || n_segments <= 0) return 0;

@@ -23,6 +23,29 @@ __global__ __launch_bounds__(NTHREADS_W) void k_fwd(Args p)
     body_wide<WFwd<DK, CT>>(p, unit, slice, smem);
 }
 
+// The forward with the mixer epilogue applied before the store: one group of
+// nsl workgroups (the value slices, on one XCD as in k_fwd) per (sequence,
+// head) unit, units unit_base + group. The slices of a unit exchange the
+// per-token sums of o^2 while they scan, so all workgroups of a group must be
+// resident at once: the grid is launched cooperatively, no larger than the
+// device holds, and more units take further launches. (A persistent grid
+// looping over units keeps every unit-invariant value of all roles live
+// across the loop and spills.)
+template <int DK, int CT>
+__global__ __launch_bounds__(NTHREADS_W) void k_fwd_ng(Args p)
+{
+    typedef LayW<WFwdNg<DK, CT>> Ly;
+    __shared__ __attribute__((aligned(16))) char smem[Ly::LDS];
+    const int b = blockIdx.x;
+    const int slice = (b >> 3) % p.nsl;
+    const int grp = ((b >> 3) / p.nsl) * 8 + (b & 7);
+    const int unit = p.unit_base + grp;
+    if (unit >= p.n_units) return;
+    if (threadIdx.x < 4) reinterpret_cast<int*>(smem + Ly::OFF_CNT)[threadIdx.x] = 0;
+    __syncthreads();
+    body_wide<WFwdNg<DK, CT>>(p, unit, slice, smem, grp, 0);
+}
+
 // The state scan alone over each unit's run (no outputs), mapped as k_fwd.
 template <int DK>
 __global__ __launch_bounds__(NTHREADS_W) void k_fwd_state(Args p)
@@ -45,6 +68,41 @@ hipError_t run_fwd(const Args& a, hipStream_t stream, bool out, int ct)
     else if (ct == 32) hipLaunchKernelGGL((k_fwd<DK, 32>), dim3(grid), dim3(NTHREADS_W), 0, stream, a);
     else hipLaunchKernelGGL((k_fwd<DK, 64>), dim3(grid), dim3(NTHREADS_W), 0, stream, a);
     return hipGetLastError();
+}
+
+// Groups per launch of the fused forward: a multiple of 8 (the XCD mapping),
+// with all their workgroups resident at once and at most NG_MAX_WG of them.
+template <int DK, int CT>
+static hipError_t ng_groups(int n_units, int nsl, int* groups)
+{
+    int dev = 0, ncu = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k_fwd_ng<DK, CT>),
+                                                         NTHREADS_W, 0);
+    if (e != hipSuccess) return e;
+    const int cap = min(ncu * per_cu, NG_MAX_WG) / nsl / 8 * 8;
+    if (cap <= 0) return hipErrorInvalidConfiguration;
+    *groups = min(cap, (n_units + 7) / 8 * 8);
+    return hipSuccess;
+}
+
+template <int DK, int CT>
+static hipError_t run_fwd_ng(Args a, hipStream_t stream)
+{
+    int groups = 0;
+    hipError_t e = ng_groups<DK, CT>(a.n_units, a.nsl, &groups);
+    if (e != hipSuccess) return e;
+    for (int base = 0; base < a.n_units; base += groups) {
+        a.unit_base = base;
+        const int g = min(groups, (a.n_units - base + 7) / 8 * 8);
+        void* args[] = {&a};
+        e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_fwd_ng<DK, CT>), dim3(g * a.nsl),
+                                       dim3(NTHREADS_W), args, 0, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace scan
@@ -131,6 +189,31 @@ hipError_t launch_fwd_bf16_segmented(const ChunkProblem& p, const void* q, const
     a.s_in_seg = ws_in;
     a.s_out_seg = nullptr;
     return run_fwd_any(a, p.d_k, stream, true, bf16_tile(p.chunk));
+}
+
+static_assert(SGLA_FWD_NORM_GATE_EXCHANGE_BYTES ==
+                  (size_t)scan::NG_XHEAD + (size_t)scan::NG_MAX_WG * scan::NG_XR * 64 * 8,
+              "exchange buffer size");
+
+// bf16 forward with the mixer epilogue fused into the store (see k_fwd_ng).
+hipError_t launch_fwd_norm_gate_bf16(const ChunkProblem& p, const void* q, const void* k, const void* v,
+                                     const float* init_state, float* final_state, const void* g,
+                                     const float* gamma, void* out, void* o, int n_tiers, float eps,
+                                     void* exchange, hipStream_t stream)
+{
+    scan::Args a = fwd_args(p, q, k, v, init_state, final_state, o);
+    a.ng_g = reinterpret_cast<const uint16_t*>(g);
+    a.ng_gamma = gamma;
+    a.ng_out = reinterpret_cast<uint16_t*>(out);
+    a.xerr = reinterpret_cast<int*>(exchange);
+    a.xch = reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(exchange) + scan::NG_XHEAD);
+    a.per_tier = p.H / n_tiers;
+    a.inv_dv = 1.0f / (float)p.d_v;
+    a.eps = eps;
+    const bool t32 = bf16_tile(p.chunk) == 32;
+    if (p.d_k <= 32) return t32 ? scan::run_fwd_ng<32, 32>(a, stream) : scan::run_fwd_ng<32, 64>(a, stream);
+    if (p.d_k <= 64) return t32 ? scan::run_fwd_ng<64, 32>(a, stream) : scan::run_fwd_ng<64, 64>(a, stream);
+    return t32 ? scan::run_fwd_ng<96, 32>(a, stream) : scan::run_fwd_ng<96, 64>(a, stream);
 }
 
 // bf16 forward with d_k <= 96 (padded to 32, 64 or 96) and any d_v (96-column slices).

@@ -104,6 +104,13 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// x sigmoid(x); e^-x overflows to inf for very negative x, giving -0
+__device__ __forceinline__ float silu_f(float x)
+{
+    const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * x);
+    return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 __device__ __forceinline__ float sigmoid_f(float z)
 {
     // 1 / (1 + e^-z) without overflow for either sign
@@ -220,7 +227,31 @@ struct Args {
     int nseg, seg_len, seg_first, seg_count, seg_in_all;
     const float* s_in_seg;
     float* s_out_seg;
+    // Mixer epilogue applied to the output tile before the store (NG roles):
+    // out[row][h][c] = silu(g[row][h][c]) gamma[h / per_tier][c] o[c] / rms,
+    // token-major rows (b T + t dense, cu[n] + t packed); o is then optional.
+    // The slices of one unit exchange their per-token sums of o^2 through
+    // xch, [groups][nsl][NG_XR][CT] words of (tag << 32 | bits of the sum).
+    // A launch runs units unit_base + group.
+    const uint16_t* ng_g;
+    const float* ng_gamma;   // [n_tiers][dvr] or NULL (one)
+    uint16_t* ng_out;
+    unsigned long long* xch;
+    int* xerr;               // set to 1 when an exchange wait gives up
+    int per_tier, unit_base;
+    float inv_dv, eps;
 };
+
+// Exchange slots per slice of a group (a ring over its tiles), the most
+// workgroups of one fused grid, and the exchange buffer's header (its first
+// int is the error flag).
+constexpr int NG_XR = 4;
+constexpr int NG_MAX_WG = 1024;
+constexpr int NG_XHEAD = 256;
+// Upper bound of the polls of one exchange wait (each after a short sleep)
+// before the wait gives up: the tile's output is NaN, and the workgroup's
+// later waits give up at once.
+constexpr int NG_SPIN_MAX = 1 << 20;
 
 // ----------------------------------------------------------------------------
 // Eight-wave body.
@@ -260,13 +291,16 @@ constexpr int NR_W = 4;                    // ring depth
 // Roles of the eight-wave body: as Role, plus the tile length CT.
 // OUT = false keeps only the state scan: no q' tile, gate, scores, readout
 // or output, for passes whose only product is the state a run leaves.
-template <int DK_, bool REV_, bool GRAD_, bool DA_, bool INIT_T_, int CT_, bool OUT_ = true>
+// NG = true (forward only) applies the mixer epilogue to each output tile
+// before its store.
+template <int DK_, bool REV_, bool GRAD_, bool DA_, bool INIT_T_, int CT_, bool OUT_ = true, bool NG_ = false>
 struct WRole {
     static constexpr int DK = DK_, CT = CT_;
-    static constexpr bool REV = REV_, GRAD = GRAD_, DA = DA_, INIT_T = INIT_T_, OUT = OUT_;
+    static constexpr bool REV = REV_, GRAD = GRAD_, DA = DA_, INIT_T = INIT_T_, OUT = OUT_, NG = NG_;
     static constexpr int E = REV_ ? 0 : 1;
 };
 template <int DK, int CT = 64> using WFwd = WRole<DK, false, false, false, false, CT>;
+template <int DK, int CT = 64> using WFwdNg = WRole<DK, false, false, false, false, CT, true, true>;
 template <int DK, int CT = 64> using WDv = WRole<DK, true, false, false, false, CT>;
 template <int DK> using WFwdState = WRole<DK, false, false, false, false, 64, false>;
 template <int DK> using WDvState = WRole<DK, true, false, false, false, 64, false>;
@@ -298,18 +332,24 @@ struct LayW {
     static constexpr int OFF_V = 2 * SZ_Q;
     static constexpr int OFF_X = 2 * SZ_Q + SZ_V;
     static constexpr int SLOT = 2 * SZ_Q + SZ_V + SZ_X;
-    static constexpr int OFF_P = NR_W * SLOT;               // 2 x [NPB][64 lanes][16 B]
+    // P: 2 x [NPB][64 lanes][16 B], the tiles c and c+1 (NG: one tile's
+    // hi and lo halves)
+    static constexpr int OFF_P = NR_W * SLOT;
     static constexpr int SZ_P = NPB * 64 * 16;
     static constexpr int OFF_CORR = OFF_P + 2 * SZ_P;       // update coefficients of B [2][CT]
     static constexpr int OFF_KEEP = OFF_CORR + 2 * CT * 4;  // masks of A, one word per token pair [2][CT/2]
     static constexpr int OFF_GT = OFF_KEEP + CT * 4;        // gate sigmoid(z) [2][CT]
     static constexpr int OFF_CG = OFF_GT + 2 * CT * 4;      // gate-derivative factors [2][CT]
     static constexpr int OFF_A = OFF_CG + (R::GRAD ? 2 * CT * 4 : 0);  // a at the v' columns [DVS]
-    static constexpr int LDS = OFF_A + (R::GRAD ? DVS * 4 : 0);
+    static constexpr int OFF_SS = OFF_A + (R::GRAD ? DVS * 4 : 0);     // NG: owners' sums of o^2 [NOW_W][CT]
+    static constexpr int OFF_INV = OFF_SS + (R::NG ? NOW_W * CT * 4 : 0);  // NG: 1 / rms per token [CT]
+    static constexpr int OFF_CNT = OFF_INV + (R::NG ? CT * 4 : 0);     // NG: sums ready, 1 / rms ready
+    static constexpr int LDS = OFF_CNT + (R::NG ? 16 : 0);
     static constexpr int NLQ = SZ_Q / 1024;
     static constexpr int NLV = SZ_V / 1024;
     static constexpr int NLOAD = (R::OUT ? 2 : 1) * NLQ + (R::GRAD ? 2 : 1) * NLV;
     static_assert(R::OUT || !R::GRAD, "state-only roles carry no gradient tiles");
+    static_assert(!R::NG || (R::OUT && !R::GRAD && !R::REV), "the epilogue belongs to the forward");
     static_assert(CT == 32 || CT == 64, "CT");
     static_assert(DK % 32 == 0 && DK <= (R::GRAD ? 192 : 96), "DK");
     static_assert(SZ_Q % 1024 == 0 && SZ_V % 1024 == 0, "load blocks");
@@ -352,8 +392,12 @@ __device__ __forceinline__ int longest_first(const Args& p, int pos, char* smem)
     return seq;
 }
 
+// Returns the number of tiles of the unit. NG roles: grp is the unit's group
+// (the workgroups of its slices) and tseq0 the number of tiles the group has
+// run before this unit, which numbers the exchange's tags.
 template <class R>
-__device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, char* smem)
+__device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, char* smem, int grp = 0,
+                                         int tseq0 = 0)
 {
     typedef LayW<R> Ly;
     constexpr int DK = R::DK, CT = R::CT;
@@ -379,15 +423,18 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
     const int n0 = slice * DVS;
 
     long row0;
+    long trow0;                    // token-major row of the run's first token (NG)
     int len;
     if (p.cu != nullptr) {
         int s0 = p.cu[seq], s1 = p.cu[seq + 1];
         s0 = min(max(s0, 0), p.T);
         s1 = min(max(s1, s0), p.T);
         row0 = (long)h * p.T + s0;
+        trow0 = s0;
         len = s1 - s0;
     } else {
         row0 = ((long)seq * H + h) * p.T;
+        trow0 = (long)seq * p.T;
         len = p.T;
         if (p.nseg > 1) {
             row0 += (long)g * p.seg_len;
@@ -409,7 +456,8 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
         const int cl = (i < CT) ? CT : clast;
         const int j = i & (CT - 1);
         const float d = powl2(cl - E - j, l2);
-        corr[i] = (j >= cl) ? 0.0f : (d >= 0.5f ? -(1.0f - d) : d);
+        // NG: the decay itself (the update takes lam^m v'_j as a hi + lo pair)
+        corr[i] = (j >= cl) ? 0.0f : (R::NG ? d : (d >= 0.5f ? -(1.0f - d) : d));
     }
     for (int i = tid; i < CT; i += NTHREADS_W) {
         const int cl = (i < CT / 2) ? CT : clast;
@@ -583,7 +631,10 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
             }
             lds_barrier();
         }
-        return;
+        if constexpr (R::NG) {
+            if (nch > 0) lds_barrier();     // the owners finish the last tile
+        }
+        return nch;
     }
 
     if (wave == SCORER_W) {
@@ -650,14 +701,152 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
                 }
             }
         };
+        // NG: the scores of tile c as a bf16 hi + lo pair in the one P buffer.
+        // They are formed in fp32 first; ready() returns once the owners no
+        // longer read the buffer (they have finished tile c-1's output).
+        auto scores_ng = [&](int c, auto ready) {
+            const char* st = smem + (c % NR_W) * Ly::SLOT;
+            const char* Qs = st;
+            const char* Ks = st + Ly::OFF_K;
+            char* Ph = smem + Ly::OFF_P;
+            char* Pl = Ph + Ly::SZ_P;
+            f32x16_t acc[NKT * (NKT + 1) / 2];
+#pragma unroll
+            for (int s = 0; s < NKT; ++s) {
+                bf16x8_t qf[DK / 16];
+#pragma unroll
+                for (int kb = 0; kb < DK / 16; ++kb)
+                    qf[kb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
+                                                              Qs + toff<SEGK>(32 * s + l32, 16 * kb + 8 * g)));
+                const float gt = gtb[(c & 1) * CT + 32 * s + l32];
+#pragma unroll
+                for (int jb = 0; jb <= s; ++jb) {
+                    f32x16_t sc = {};
+#pragma unroll
+                    for (int kb = 0; kb < DK / 16; ++kb) {
+                        const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
+                                                                             Ks + toff<SEGK>(32 * jb + l32, 16 * kb + 8 * g)));
+                        sc = mma(kf, qf[kb], sc);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        if (jb == s) sc[i] = fmaf(dsel[i], gt, sc[i]) * dmd[i];
+                        else sc[i] *= dmo[i];
+                    }
+                    acc[s * (s + 1) / 2 + jb] = sc;
+                }
+            }
+            ready();
+#pragma unroll
+            for (int s = 0; s < NKT; ++s) {
+                const int tb = 2 * s + (l32 >> 4);
+#pragma unroll
+                for (int jb = 0; jb <= s; ++jb) {
+                    const f32x16_t& sc = acc[s * (s + 1) / 2 + jb];
+#pragma unroll
+                    for (int a4 = 0; a4 < 4; ++a4) {
+                        const int i0 = 4 * a4;
+                        const u32x2_t hw = {pack2(sc[i0], sc[i0 + 1]), pack2(sc[i0 + 2], sc[i0 + 3])};
+                        const u32x2_t lw = {pack2(sc[i0] - bf_lo(hw[0]), sc[i0 + 1] - bf_hi(hw[0])),
+                                            pack2(sc[i0 + 2] - bf_lo(hw[1]), sc[i0 + 3] - bf_hi(hw[1]))};
+                        const int off = pblk(tb, jb) * 1024 + ((l32 & 15) + 16 * a4) * 16 + 8 * g;
+                        *reinterpret_cast<u32x2_t*>(Ph + off) = hw;
+                        *reinterpret_cast<u32x2_t*>(Pl + off) = lw;
+                    }
+                }
+            }
+        };
         lds_barrier();
-        if (R::OUT && nch > 0) scores(0);
+        if constexpr (R::NG) {
+            if (nch > 0) scores_ng(0, [] {});
+        } else {
+            if (R::OUT && nch > 0) scores(0);
+        }
         lds_barrier();
+        if constexpr (R::NG) {
+            // The epilogue's statistic. In iteration c the scorer adds the six
+            // owners' sums of o^2 of tile c (publish), then forms 1 / rms of
+            // tile c-1 from its own sum and the other slice's (combine), which
+            // that slice published one iteration earlier; the owners store
+            // tile c-1 once it is in LDS. Lane t handles token t of a tile.
+            const float* ssb = reinterpret_cast<const float*>(smem + Ly::OFF_SS);
+            float* invb = reinterpret_cast<float*>(smem + Ly::OFF_INV);
+            int* cnt = reinterpret_cast<int*>(smem + Ly::OFF_CNT);
+            unsigned long long* xg = p.xch + (size_t)grp * p.nsl * NG_XR * CT;
+            float mine[2] = {0.0f, 0.0f};
+            bool gave_up = false;
+            auto publish = [&](int c) {
+                const int ts = tseq0 + c;
+                while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < NOW_W * (ts + 1))
+                    __builtin_amdgcn_s_sleep(1);
+                float part = 0.0f;
+                if (lane < CT) {
+#pragma unroll
+                    for (int w2 = 0; w2 < NOW_W; ++w2) part += ssb[w2 * CT + lane];
+                }
+                mine[c & 1] = part;
+                if (p.nsl > 1 && lane < CT) {
+                    const unsigned long long word =
+                        ((unsigned long long)(unsigned)(ts + 1) << 32) | __float_as_uint(part);
+                    __hip_atomic_store(xg + ((size_t)slice * NG_XR + (ts & (NG_XR - 1))) * CT + lane, word,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            };
+            auto combine = [&](int c) {
+                const int ts = tseq0 + c;
+                const unsigned want = (unsigned)(ts + 1);
+                float tot = 0.0f;
+                bool bad = gave_up;
+                for (int s2 = 0; s2 < p.nsl; ++s2) {
+                    if (s2 == slice) {
+                        tot += mine[c & 1];
+                        continue;
+                    }
+                    unsigned long long* slot = xg + ((size_t)s2 * NG_XR + (ts & (NG_XR - 1))) * CT + lane;
+                    unsigned long long wv = (unsigned long long)want << 32;
+                    for (int tries = 0; !bad; ++tries) {
+                        if (lane < CT) wv = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        if (__all((unsigned)(wv >> 32) == want)) break;
+                        if (tries >= NG_SPIN_MAX) {
+                            bad = true;
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(2);
+                    }
+                    if (!bad && lane < CT) {
+                        // consumed: clear the word unless the next tag is already there
+                        unsigned long long expect = wv;
+                        __hip_atomic_compare_exchange_strong(slot, &expect, 0ull, __ATOMIC_RELAXED,
+                                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                    tot += __uint_as_float((unsigned)wv);
+                }
+                gave_up = bad;
+                if (bad && lane == 0) __hip_atomic_store(p.xerr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (lane < CT)
+                    invb[lane] = bad ? __builtin_nanf("") : __builtin_amdgcn_rsqf(fmaf(tot, p.inv_dv, p.eps));
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                if (lane == 0) __hip_atomic_store(cnt + 1, ts + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            };
+            for (int c = 0; c < nch; ++c) {
+                // publish waits for the owners' sums of tile c, after which
+                // they no longer read the P buffer
+                if (c + 1 < nch) scores_ng(c + 1, [&] { publish(c); });
+                else publish(c);
+                if (c > 0) combine(c - 1);
+                lds_barrier();
+            }
+            if (nch > 0) {
+                combine(nch - 1);
+                lds_barrier();
+            }
+            return nch;
+        }
         for (int c = 0; c < nch; ++c) {
             if (R::OUT && c + 1 < nch) scores(c + 1);
             lds_barrier();
         }
-        return;
+        return nch;
     }
 
     // -------------------------------------------------------------- owners
@@ -696,13 +885,79 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
     const float fC = __builtin_amdgcn_exp2f((float)CT * l2);
     f32x4_t dpart = {0.f, 0.f, 0.f, 0.f};      // DA: column sums of c_t x_t (.) v'_t
 
+    // NG: the output tile is stored one iteration late, once 1 / rms of its
+    // tokens is known; prv holds it (fp32) and gpv its gate values.
+    const int ccol = n0 + OWC * w + 4 * qg;    // this lane's first output column
+    f32x4_t gam = {1.f, 1.f, 1.f, 1.f};
+    f32x4_t prv[NTB];
+    u32x2_t gpv[NTB];
+    if constexpr (R::NG) {
+        if (p.ng_gamma != nullptr) {
+            const float* gr = p.ng_gamma + (size_t)(h / p.per_tier) * dvr;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) gam[r] = (ccol < dvr) ? gr[ccol + r] : 0.0f;
+        }
+    }
+    if constexpr (R::NG) {
+        // Wait for the initial state and the scales here: with vector loads
+        // inside the tile loop (the gate values) the compiler would wait for
+        // them at their first read in the loop, every tile, and that wait
+        // would take in the gate loads just issued as well.
+#pragma unroll
+        for (int db = 0; db < NDB16; ++db) asm volatile("" ::"v"(sacc[db]));
+        asm volatile("" ::"v"(gam));
+    }
+    auto ng_at = [&](int c, int t) -> size_t { return ((size_t)(trow0 + c * CT + t) * H + h) * dvr + ccol; };
+    // FULL: tile c has CT tokens and the slice d_v columns, so no lane is
+    // masked. (Guarded loads and stores each sit in a branch, and at every
+    // join the compiler waits for all outstanding memory operations.)
+    auto load_g = [&](int c, auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        const int cl = FULL ? CT : min(CT, len - c * CT);
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) {
+            const int t = 16 * tb + l16;
+            const u32x2_t z2 = {0u, 0u};
+            if (FULL) gpv[tb] = *reinterpret_cast<const u32x2_t*>(p.ng_g + ng_at(c, t));
+            else gpv[tb] = (t < cl && ccol < dvr) ? *reinterpret_cast<const u32x2_t*>(p.ng_g + ng_at(c, t)) : z2;
+        }
+    };
+    auto finish = [&](int c, auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        const int* cnt = reinterpret_cast<const int*>(smem + Ly::OFF_CNT);
+        const float* invb = reinterpret_cast<const float*>(smem + Ly::OFF_INV);
+        while (__hip_atomic_load(cnt + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < tseq0 + c + 1)
+            __builtin_amdgcn_s_sleep(1);
+        const int cl = FULL ? CT : min(CT, len - c * CT);
+        u32x2_t w2[NTB];
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) {
+            const float inv = invb[16 * tb + l16];
+            const float gv[4] = {bf_lo(gpv[tb][0]), bf_hi(gpv[tb][0]), bf_lo(gpv[tb][1]), bf_hi(gpv[tb][1])};
+            float y[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) y[r] = silu_f(gv[r]) * (gam[r] * (prv[tb][r] * inv));
+            w2[tb] = u32x2_t{pack2(y[0], y[1]), pack2(y[2], y[3])};
+        }
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) {
+            const int t = 16 * tb + l16;
+            if (FULL || (t < cl && ccol < dvr)) *reinterpret_cast<u32x2_t*>(p.ng_out + ng_at(c, t)) = w2[tb];
+        }
+    };
+
     auto tile = [&](int c, auto full_tag) {
         constexpr bool FULL = decltype(full_tag)::value;
+        f32x4_t cur[NTB];
+        if constexpr (R::NG) {
+            // used at the end of the tile; tile c-1 is full when tile c is
+            if (c > 0) load_g(c - 1, full_tag);
+        }
         const char* st = smem + (c % NR_W) * Ly::SLOT;
         const char* Qs = st;
         const char* Ks = st + Ly::OFF_K;
         const char* Vs = st + Ly::OFF_V;
-        const char* Pb = smem + Ly::OFF_P + (c & 1) * Ly::SZ_P;
+        const char* Pb = smem + Ly::OFF_P + (R::NG ? 0 : (c & 1) * Ly::SZ_P);
         const int cstart = c * CT;
         const int cl = FULL ? CT : min(CT, len - cstart);
         const bool last_row = !FULL && c == nch - 1;
@@ -719,10 +974,16 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
             vf[ks] = frag(tr_read<SEGV>(Vs, 32 * ks + 8 * qg, OWC * w, lane),
                           tr_read<SEGV>(Vs, 32 * ks + 8 * qg + 4, OWC * w, lane));
         if constexpr (R::OUT) {
-            bf16x8_t pf[NPB];
+            bf16x8_t pf[NPB], pfl[R::NG ? NPB : 1];
 #pragma unroll
             for (int b = 0; b < NPB; ++b)
                 pf[b] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(Pb + (b * 64 + lane) * 16));
+            if constexpr (R::NG) {
+#pragma unroll
+                for (int b = 0; b < NPB; ++b)
+                    pfl[b] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
+                                                              Pb + Ly::SZ_P + (b * 64 + lane) * 16));
+            }
 
             // ---- readout: O^T = S^T Q'^T, the state as a bf16 pair: hi = the
             // truncated upper half, lo = the remainder (exact in fp32) rounded
@@ -760,7 +1021,10 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
             for (int tb = 0; tb < NTB; ++tb) {
                 f32x4_t o = {};
 #pragma unroll
-                for (int ks = 0; ks <= (tb >> 1); ++ks) o = mma16(vf[ks], pf[pblk(tb, ks)], o);
+                for (int ks = 0; ks <= (tb >> 1); ++ks) {
+                    o = mma16(vf[ks], pf[pblk(tb, ks)], o);
+                    if constexpr (R::NG) o = mma16(vf[ks], pfl[pblk(tb, ks)], o);
+                }
                 const int t = 16 * tb + l16;
                 float val[4];
 #pragma unroll
@@ -785,14 +1049,32 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
                         if constexpr (R::DA) dpart[r] = fmaf(cy, xv[r], dpart[r]);
                     }
                 }
-                if (FULL || t < cl) {
-                    const int col = n0 + OWC * w + 4 * qg;
-                    if (FULL || col < dvr) {
-                        uint16_t* orow = p.o + grow(c, t) * dvr + col;
-                        const u32x2_t w2 = {pack2(val[0], val[1]), pack2(val[2], val[3])};
-                        *reinterpret_cast<u32x2_t*>(orow) = w2;
+                if (!R::NG || p.o != nullptr) {
+                    if (FULL || t < cl) {
+                        const int col = n0 + OWC * w + 4 * qg;
+                        if (FULL || col < dvr) {
+                            uint16_t* orow = p.o + grow(c, t) * dvr + col;
+                            const u32x2_t w2 = {pack2(val[0], val[1]), pack2(val[2], val[3])};
+                            *reinterpret_cast<u32x2_t*>(orow) = w2;
+                        }
                     }
                 }
+                if constexpr (R::NG) {
+                    // this owner's sum of o^2 over its 16 columns, per token
+                    float x = val[0] * val[0];
+#pragma unroll
+                    for (int r = 1; r < 4; ++r) x = fmaf(val[r], val[r], x);
+                    x += __shfl_xor(x, 16);
+                    x += __shfl_xor(x, 32);
+                    if (qg == 0) reinterpret_cast<float*>(smem + Ly::OFF_SS)[w * CT + t] = x;
+                    cur[tb] = f32x4_t{val[0], val[1], val[2], val[3]};
+                }
+            }
+            if constexpr (R::NG) {
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                if (lane == 0)
+                    __hip_atomic_fetch_add(reinterpret_cast<int*>(smem + Ly::OFF_CNT), 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_WORKGROUP);
             }
         } else {
 #pragma unroll
@@ -808,15 +1090,30 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
         for (int ks = 0; ks < NKT; ++ks) {
             const f32x4_t c0 = *reinterpret_cast<const f32x4_t*>(cf + 32 * ks + 8 * qg);
             const f32x4_t c1 = *reinterpret_cast<const f32x4_t*>(cf + 32 * ks + 8 * qg + 4);
-            const u32x4_t km = *reinterpret_cast<const u32x4_t*>(kw + 16 * ks + 4 * qg);
             const u32x4_t vw = __builtin_bit_cast(u32x4_t, vf[ks]);
-            u32x4_t cw;
-            cw[0] = pack2(c0[0] * bf_lo(vw[0]), c0[1] * bf_hi(vw[0]));
-            cw[1] = pack2(c0[2] * bf_lo(vw[1]), c0[3] * bf_hi(vw[1]));
-            cw[2] = pack2(c1[0] * bf_lo(vw[2]), c1[1] * bf_hi(vw[2]));
-            cw[3] = pack2(c1[2] * bf_lo(vw[3]), c1[3] * bf_hi(vw[3]));
-            vc[ks] = __builtin_bit_cast(bf16x8_t, cw);
-            va[ks] = __builtin_bit_cast(bf16x8_t, vw & km);
+            if constexpr (R::NG) {
+                // lam^m v'_j as a bf16 hi + lo pair
+                const float x[8] = {c0[0] * bf_lo(vw[0]), c0[1] * bf_hi(vw[0]), c0[2] * bf_lo(vw[1]),
+                                    c0[3] * bf_hi(vw[1]), c1[0] * bf_lo(vw[2]), c1[1] * bf_hi(vw[2]),
+                                    c1[2] * bf_lo(vw[3]), c1[3] * bf_hi(vw[3])};
+                u32x4_t hw, lw;
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) {
+                    hw[s2] = pack2(x[2 * s2], x[2 * s2 + 1]);
+                    lw[s2] = pack2(x[2 * s2] - bf_lo(hw[s2]), x[2 * s2 + 1] - bf_hi(hw[s2]));
+                }
+                va[ks] = __builtin_bit_cast(bf16x8_t, hw);
+                vc[ks] = __builtin_bit_cast(bf16x8_t, lw);
+            } else {
+                const u32x4_t km = *reinterpret_cast<const u32x4_t*>(kw + 16 * ks + 4 * qg);
+                u32x4_t cw;
+                cw[0] = pack2(c0[0] * bf_lo(vw[0]), c0[1] * bf_hi(vw[0]));
+                cw[1] = pack2(c0[2] * bf_lo(vw[1]), c0[3] * bf_hi(vw[1]));
+                cw[2] = pack2(c1[0] * bf_lo(vw[2]), c1[1] * bf_hi(vw[2]));
+                cw[3] = pack2(c1[2] * bf_lo(vw[3]), c1[3] * bf_hi(vw[3]));
+                vc[ks] = __builtin_bit_cast(bf16x8_t, cw);
+                va[ks] = __builtin_bit_cast(bf16x8_t, vw & km);
+            }
         }
 #pragma unroll
         for (int db = 0; db < NDB16; ++db)
@@ -830,6 +1127,11 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
                 sacc[db] = mma16(kf, va[ks], sacc[db]);
                 sacc[db] = mma16(kf, vc[ks], sacc[db]);
             }
+        if constexpr (R::NG) {
+            if (c > 0) finish(c - 1, full_tag);
+#pragma unroll
+            for (int tb = 0; tb < NTB; ++tb) prv[tb] = cur[tb];
+        }
     };
 
     const bool cols_full = (n0 + DVS <= dvr);
@@ -839,6 +1141,13 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
         if (cols_full && (c < nch - 1 || clast == CT)) tile(c, std::true_type{});
         else tile(c, std::false_type{});
         lds_barrier();
+    }
+    if constexpr (R::NG) {
+        if (nch > 0) {
+            load_g(nch - 1, std::false_type{});
+            finish(nch - 1, std::false_type{});
+            lds_barrier();
+        }
     }
 
     // (the gradient scans of q and k end without a state output)
@@ -868,6 +1177,7 @@ __device__ __forceinline__ void body_wide(const Args& p, int unit, int slice, ch
             }
         }
     }
+    return nch;
 }
 
 // ----------------------------------------------------------------------------

@@ -142,6 +142,62 @@ sgla_status sgla_chunk_fwd(const void* q, const void* k, const void* v,
                            sgla_dtype dtype, void* hip_stream);
 
 /*
+ * Size in bytes of the exchange buffer sgla_chunk_fwd_norm_gate takes.
+ */
+#define SGLA_FWD_NORM_GATE_EXCHANGE_BYTES ((size_t)2 * 1024 * 1024 + 256)
+
+/*
+ * Chunked forward with the mixer epilogue applied to each output tile before
+ * it is stored: sgla_chunk_fwd followed by sgla_head_norm_gate in one kernel,
+ * so that o need not go to memory and back. Laplace 3B post, "Challenge 1:
+ * Using native PyTorch on Trainium for GLA" (the chunk form), and "i14 and
+ * the Laplace 3B architecture", the end of the "GLA mixer" paragraph and
+ * "Decay schedule's reach" (Head RMSNorm per decay tier, heads concatenated,
+ * SiLU(g) gate):
+ *   out[b,t,h,c] = silu(g[b,t,h,c]) * gamma[tier(h)][c] * o[b,h,t,c]
+ *                  / sqrt(mean_c' o[b,h,t,c']^2 + eps),   tier(h) = h / (H / n_tiers)
+ * with o the chunked forward's output, taken here in fp32 (sgla_chunk_fwd
+ * rounds it to bf16 before the epilogue would read it).
+ *
+ * q, k, v, lambda, a, init_state, final_state, cu_seqlens, n_seq, B, H, T,
+ * d_k, d_v, chunk: as sgla_chunk_fwd (bf16 only).
+ * g:        [B, T, H, d_v] bf16 gate stream, token-major (packed: B = 1,
+ *           T = total tokens).
+ * gamma:    [n_tiers, d_v] fp32 scales, or NULL (one).
+ * out:      [B, T, H, d_v] bf16, token-major. It may equal g (in place);
+ *           otherwise it must not overlap g. It must not overlap any other
+ *           argument.
+ * o:        [B, H, T, d_v] bf16 (the layout of sgla_chunk_fwd), also written
+ *           when not NULL (e.g. for sgla_head_norm_gate_bwd).
+ * n_tiers:  divides H. eps: finite, >= 0.
+ * exchange: device buffer of SGLA_FWD_NORM_GATE_EXCHANGE_BYTES that must be
+ *           zero-filled before its first use. The two 96-column workgroups of
+ *           a (sequence, head) with d_v > 96 pass each other their per-token
+ *           sums of o^2 through it; a call that completes leaves it
+ *           zero-filled again. Calls that may run at the same time need
+ *           distinct buffers. The workgroups are launched cooperatively (all
+ *           resident at once); when the (sequence, head) units need more
+ *           workgroups than the device holds, the call makes several such
+ *           launches in turn on the stream. Should an exchange never arrive,
+ *           the wait gives up after a bounded number of polls: the affected
+ *           outputs are NaN and the buffer's first int is set to 1 (zero-fill
+ *           it again before the next call).
+ * Errors: as sgla_chunk_fwd; SGLA_ERR_UNSUPPORTED for SGLA_F32 (compose
+ * sgla_chunk_fwd and sgla_head_norm_gate); SGLA_ERR_INVALID_ARG for n_tiers
+ * not dividing H, a bad eps, or overlapping buffers; SGLA_ERR_WORKSPACE for a
+ * NULL, misaligned or short exchange buffer; SGLA_ERR_HIP for a launch
+ * failure, including a device that cannot hold the cooperative grid.
+ */
+sgla_status sgla_chunk_fwd_norm_gate(const void* q, const void* k, const void* v,
+                                     const float* lambda, const float* a,
+                                     const float* init_state, float* final_state,
+                                     const void* g, const float* gamma, void* out, void* o,
+                                     const int32_t* cu_seqlens, int n_seq,
+                                     int B, int H, int T, int d_k, int d_v, int chunk,
+                                     int n_tiers, float eps, sgla_dtype dtype,
+                                     void* exchange, size_t exchange_bytes, void* hip_stream);
+
+/*
  * Bytes of device workspace sgla_chunk_fwd_segmented needs: two arrays of
  * B * n_segments * H states of d_k * d_v fp32.
  */

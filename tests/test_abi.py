@@ -122,6 +122,59 @@ def test_chunk_fwd_rejects(L, name, kw, code):
     assert L.sgla_last_error().decode() != ""
 
 
+def fng_args(**kw):
+    a = dict(q=P["q"], k=P["k"], v=P["v"], lam=P["lam"], a=P["a"], s0=P["s0"], sf=P["sf"], g=P["ng"],
+             gm=P["gm"], out=P["nout"], o=P["o"], cu=None, n_seq=0, B=2, H=16, T=256, d_k=96, d_v=192,
+             chunk=128, tiers=4, eps=1e-6, dt=B.SGLA_BF16, x=P["ws"], xb=B.FWD_NORM_GATE_EXCHANGE_BYTES)
+    a.update(kw)
+    return [a["q"], a["k"], a["v"], a["lam"], a["a"], a["s0"], a["sf"], a["g"], a["gm"], a["out"], a["o"],
+            a["cu"], a["n_seq"], a["B"], a["H"], a["T"], a["d_k"], a["d_v"], a["chunk"], a["tiers"],
+            ctypes.c_float(a["eps"]), a["dt"], a["x"], a["xb"], None]
+
+
+FNG_BAD = [
+    ("q null", dict(q=None), B.SGLA_ERR_INVALID_ARG),
+    ("g null", dict(g=None), B.SGLA_ERR_INVALID_ARG),
+    ("out null", dict(out=None), B.SGLA_ERR_INVALID_ARG),
+    ("out misaligned", dict(out=P["nout"] + 8), B.SGLA_ERR_INVALID_ARG),
+    ("gamma misaligned", dict(gm=P["gm"] + 4), B.SGLA_ERR_INVALID_ARG),
+    ("o misaligned", dict(o=P["o"] + 8), B.SGLA_ERR_INVALID_ARG),
+    ("f32", dict(dt=B.SGLA_F32, d_k=16, d_v=32), B.SGLA_ERR_UNSUPPORTED),
+    ("d_v too big", dict(d_v=256), B.SGLA_ERR_UNSUPPORTED),
+    ("chunk 16", dict(chunk=16), B.SGLA_ERR_UNSUPPORTED),
+    ("exchange null", dict(x=None), B.SGLA_ERR_WORKSPACE),
+    ("exchange misaligned", dict(x=P["ws"] + 8), B.SGLA_ERR_WORKSPACE),
+    ("exchange short", dict(xb=B.FWD_NORM_GATE_EXCHANGE_BYTES - 1), B.SGLA_ERR_WORKSPACE),
+    ("exchange overlaps out", dict(x=P["nout"] + 4096), B.SGLA_ERR_WORKSPACE),
+    ("tiers zero", dict(tiers=0), B.SGLA_ERR_INVALID_ARG),
+    ("tiers not dividing H", dict(tiers=3), B.SGLA_ERR_INVALID_ARG),
+    ("eps negative", dict(eps=-1.0), B.SGLA_ERR_INVALID_ARG),
+    ("eps nan", dict(eps=float("nan")), B.SGLA_ERR_INVALID_ARG),
+    ("out overlaps q", dict(out=P["q"] + 1024), B.SGLA_ERR_INVALID_ARG),
+    ("out overlaps g", dict(out=P["ng"] + 1024), B.SGLA_ERR_INVALID_ARG),
+    ("o aliases out", dict(o=P["nout"]), B.SGLA_ERR_INVALID_ARG),
+    ("o overlaps v", dict(o=P["v"] + 1024), B.SGLA_ERR_INVALID_ARG),
+    ("final overlaps init", dict(sf=P["s0"] + 1024), B.SGLA_ERR_INVALID_ARG),
+    ("final overlaps out", dict(sf=P["nout"] + 1024), B.SGLA_ERR_INVALID_ARG),
+    ("final overlaps g", dict(sf=P["ng"] + 1024), B.SGLA_ERR_INVALID_ARG),
+    ("packed with B=2", dict(cu=P["cu"], n_seq=3), B.SGLA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", FNG_BAD, ids=[x[0] for x in FNG_BAD])
+def test_chunk_fwd_norm_gate_rejects(L, name, kw, code):
+    """The fused forward and epilogue validates on the host, before any GPU call."""
+    assert L.sgla_chunk_fwd_norm_gate(*fng_args(**kw)) == code
+    assert L.sgla_last_error().decode() != ""
+
+
+def test_exchange_bytes_match_header():
+    text = open(os.path.join(ROOT, "include", "sgla.h")).read()
+    m = re.search(r"#define SGLA_FWD_NORM_GATE_EXCHANGE_BYTES \(\(size_t\)2 \* 1024 \* 1024 \+ 256\)", text)
+    assert m is not None
+    assert B.FWD_NORM_GATE_EXCHANGE_BYTES == 2 * 1024 * 1024 + 256
+
+
 def seg_args(**kw):
     a = dict(q=P["q"], k=P["k"], v=P["v"], lam=P["lam"], a=P["a"], s0=P["s0"], sf=P["sf"],
              o=P["o"], B=2, H=16, T=4096, d_k=96, d_v=192, chunk=128, dt=B.SGLA_BF16, nseg=4,
