@@ -285,6 +285,9 @@ sgla_status sgla_chunk_fwd_norm_gate(const void* q, const void* k, const void* v
                     (size_t)SGLA_FWD_NORM_GATE_EXCHANGE_BYTES);
     if (n_tiers <= 0 || H % n_tiers != 0)
         return fail(SGLA_ERR_INVALID_ARG, "n_tiers (%d) must be positive and divide H (%d)", n_tiers, H);
+    // the kernel addresses a tile's token rows (H d_v elements apart) with 32-bit offsets
+    if ((long long)H * d_v > (1LL << 24))
+        return fail(SGLA_ERR_UNSUPPORTED, "H * d_v must be at most 2^24 (got %lld)", (long long)H * d_v);
     if (!(eps >= 0.0f) || !std::isfinite(eps))
         return fail(SGLA_ERR_INVALID_ARG, "eps must be finite and >= 0 (got %g)", (double)eps);
     const size_t nqk = (size_t)B * H * T * d_k * 2, nvo = (size_t)B * H * T * d_v * 2;

@@ -273,6 +273,10 @@ constexpr int NG_SPIN_MAX = 1 << 20;
 //     the raw diagonal instead, which the owners apply in their epilogue.
 // A tile's data is waited for by the loader two iterations before the owners
 // use it, so the gate and the scores of tile c+1 both run during iteration c.
+// The NG role (the epilogue applied before the store) differs: its ring is
+// three deep, the fourth slot's LDS holding three tiles of the gate stream g;
+// the loader forms the gate of tile c+1 on the VALU, in fp32, right after the
+// tile arrives, and the scorer waits for it.
 // Tiles are 64 tokens for the 96-wide contractions (FWD, DV) and 32 tokens
 // for the 192-wide ones (DQ, DK), so that four tiles fit the LDS ring. Per
 // 64 tokens and owner wave: state readout 4 x (d'/32) x (hi, lo), P V' 6, and
@@ -332,9 +336,11 @@ struct LayW {
     static constexpr int OFF_V = 2 * SZ_Q;
     static constexpr int OFF_X = 2 * SZ_Q + SZ_V;
     static constexpr int SLOT = 2 * SZ_Q + SZ_V + SZ_X;
+    // ring depth: the NG role gives a slot to the gate values (OFF_G)
+    static constexpr int NR = R::NG ? 3 : NR_W;
     // P: 2 x [NPB][64 lanes][16 B], the tiles c and c+1 (NG: one tile's
     // hi and lo halves)
-    static constexpr int OFF_P = NR_W * SLOT;
+    static constexpr int OFF_P = NR * SLOT;
     static constexpr int SZ_P = NPB * 64 * 16;
     static constexpr int OFF_CORR = OFF_P + 2 * SZ_P;       // update coefficients of B [2][CT]
     static constexpr int OFF_KEEP = OFF_CORR + 2 * CT * 4;  // masks of A, one word per token pair [2][CT/2]
@@ -343,8 +349,11 @@ struct LayW {
     static constexpr int OFF_A = OFF_CG + (R::GRAD ? 2 * CT * 4 : 0);  // a at the v' columns [DVS]
     static constexpr int OFF_SS = OFF_A + (R::GRAD ? DVS * 4 : 0);     // NG: owners' sums of o^2 [NOW_W][CT]
     static constexpr int OFF_INV = OFF_SS + (R::NG ? NOW_W * CT * 4 : 0);  // NG: 1 / rms per token [CT]
-    static constexpr int OFF_CNT = OFF_INV + (R::NG ? CT * 4 : 0);     // NG: sums ready, 1 / rms ready
-    static constexpr int LDS = OFF_CNT + (R::NG ? 16 : 0);
+    // NG: sums ready, 1 / rms ready, tile and gate ready
+    static constexpr int OFF_CNT = OFF_INV + (R::NG ? CT * 4 : 0);
+    static constexpr int OFF_G = OFF_CNT + (R::NG ? 16 : 0);            // NG: 3 x [CT][96] gate values g
+    static constexpr int OFF_AQ = OFF_G + (R::NG ? 3 * SZ_V : 0);       // NG: a [DK] fp32
+    static constexpr int LDS = OFF_AQ + (R::NG ? DK * 4 : 0);
     static constexpr int NLQ = SZ_Q / 1024;
     static constexpr int NLV = SZ_V / 1024;
     static constexpr int NLOAD = (R::OUT ? 2 : 1) * NLQ + (R::GRAD ? 2 : 1) * NLV;
@@ -354,6 +363,7 @@ struct LayW {
     static_assert(DK % 32 == 0 && DK <= (R::GRAD ? 192 : 96), "DK");
     static_assert(SZ_Q % 1024 == 0 && SZ_V % 1024 == 0, "load blocks");
     static_assert(NLOAD <= 63, "vmcnt");
+    static_assert(!R::NG || NLOAD + 2 * NLV <= 63, "vmcnt");
     static_assert(LDS <= 160 * 1024, "LDS");
 };
 
@@ -471,8 +481,40 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
         for (int i = tid; i < DVS; i += NTHREADS_W)
             at[i] = (p.a != nullptr && n0 + i < dvr) ? p.a[(size_t)h * dvr + n0 + i] : 0.0f;
     }
+    if constexpr (R::NG) {
+        float* aq = reinterpret_cast<float*>(smem + Ly::OFF_AQ);
+        for (int i = tid; i < DK; i += NTHREADS_W) aq[i] = (p.a != nullptr && i < dkr) ? p.a[(size_t)h * dkr + i] : 0.0f;
+    }
     float* gtb = reinterpret_cast<float*>(smem + Ly::OFF_GT);
     float* cgb = reinterpret_cast<float*>(smem + Ly::OFF_CG);
+    // NG: sigmoid(z_t) of tile c on the VALU in fp32, lane = token, a in fp32.
+    // All row reads are issued first and four partial sums break the chain.
+    auto gate_valu = [&](int c) {
+        const char* st = smem + (c % Ly::NR) * Ly::SLOT;
+        const float* aq = reinterpret_cast<const float*>(smem + Ly::OFF_AQ);
+        if (lane < CT) {
+            u32x4_t qw[SEGK], kw[SEGK];
+#pragma unroll
+            for (int sg = 0; sg < SEGK; ++sg) {
+                qw[sg] = *reinterpret_cast<const u32x4_t*>(st + toff<SEGK>(lane, 8 * sg));
+                kw[sg] = *reinterpret_cast<const u32x4_t*>(st + Ly::OFF_K + toff<SEGK>(lane, 8 * sg));
+            }
+            float zp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int sg = 0; sg < SEGK; ++sg) {
+                const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(aq + 8 * sg);
+                const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(aq + 8 * sg + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float ae0 = (e < 2) ? a0[2 * e] : a1[2 * e - 4];
+                    const float ae1 = (e < 2) ? a0[2 * e + 1] : a1[2 * e - 3];
+                    zp[e] = fmaf(ae0 * bf_lo(qw[sg][e]), bf_lo(kw[sg][e]), zp[e]);
+                    zp[e] = fmaf(ae1 * bf_hi(qw[sg][e]), bf_hi(kw[sg][e]), zp[e]);
+                }
+            }
+            gtb[(c & 1) * CT + lane] = sigmoid_f((zp[0] + zp[1]) + (zp[2] + zp[3]));
+        }
+    };
 
     if (wave == LOADER_W) {
         // ---------------------------------------------------------- loader
@@ -498,7 +540,7 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
         };
         offsets(nch > 1 ? CT : clast);
         auto issue = [&](int c) {
-            char* st = smem + (c % NR_W) * Ly::SLOT;
+            char* st = smem + (c % Ly::NR) * Ly::SLOT;
             const int cl = min(CT, len - c * CT);
             if (c == nch - 1 && clast < CT) offsets(clast);
             const long rb = R::REV ? grow(c, cl - 1) : grow(c, 0);
@@ -521,7 +563,7 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
         auto fixup = [&](int c) {
             const int cl = min(CT, len - c * CT);
             if (cl == CT && dkr == DK && n0 + DVS <= dvr) return;
-            char* st = smem + (c % NR_W) * Ly::SLOT;
+            char* st = smem + (c % Ly::NR) * Ly::SLOT;
             const u32x4_t zero = {0u, 0u, 0u, 0u};
             for (int P = lane; P < CT * SEGK; P += 64) {
                 const int r = P / SEGK;
@@ -565,7 +607,7 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
             }
         // sigmoid(z_t) of tile c: z_t = (Y (diag(a) X^T))[t][t] on the matrix cores
         auto gate = [&](int c) {
-            const char* st = smem + (c % NR_W) * Ly::SLOT;
+            const char* st = smem + (c % Ly::NR) * Ly::SLOT;
             const char* Gb = R::GRAD ? st + Ly::OFF_X : st;           // X rows (B operand)
             const char* Ga = R::GRAD ? st + Ly::OFF_V : st + Ly::OFF_K;  // Y rows (A operand)
 #pragma unroll
@@ -598,6 +640,65 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
                 if (g == 0) gtb[(c & 1) * CT + 32 * s + l32] = sigmoid_f(z);
             }
         };
+        if constexpr (R::NG) {
+            // Three-deep ring. In iteration c the loader issues tile c+2,
+            // waits for tile c+1 and forms its gate sigmoid(z) (cnt[2] = c+2
+            // tells the scorer), issues the gate values g of tile c+1, then
+            // waits for g of tile c, which the owners read in iteration c+1.
+            constexpr int NLG = Ly::NLV;
+            uint32_t offg[NLG];
+            auto offsets_g = [&](int cl) {
+#pragma unroll
+                for (int m = 0; m < NLG; ++m) {
+                    const int P = 64 * m + lane;
+                    const int r = P / SEGV;
+                    const int cs = (P - r * SEGV) ^ sw<SEGV>(r);
+                    offg[m] = (uint32_t)(min(r, cl - 1) * H * dvr + min(n0 + 8 * cs, dvr - 8)) * 2u;
+                }
+            };
+            offsets_g(nch > 1 ? CT : clast);
+            auto issue_g = [&](int c) {
+                if (c == nch - 1 && clast < CT) offsets_g(clast);
+                const char* gb = reinterpret_cast<const char*>(p.ng_g + ((size_t)(trow0 + c * CT) * H + h) * dvr);
+                char* dst = smem + Ly::OFF_G + (c % 3) * Ly::SZ_V;
+#pragma unroll
+                for (int m = 0; m < NLG; ++m) dma16(gb, offg[m], dst + 1024 * m);
+            };
+            int* cnt = reinterpret_cast<int*>(smem + Ly::OFF_CNT);
+            if (nch > 0) {
+                issue(0);
+                if (nch > 1) issue(1);
+                issue_g(0);
+                if (nch > 1) wait_vm<Ly::NLOAD + NLG>();
+                else wait_vm<NLG>();
+                fixup(0);
+                gate_valu(0);
+            }
+            lds_barrier();
+            lds_barrier();
+            for (int c = 0; c < nch; ++c) {
+                const bool n1 = c + 1 < nch, n2 = c + 2 < nch;
+                if (n2) issue(c + 2);
+                if (n1) {
+                    // tile c+1: younger are g of tile c and tile c+2
+                    if (n2) wait_vm<NLG + Ly::NLOAD>();
+                    else wait_vm<NLG>();
+                    fixup(c + 1);
+                    gate_valu(c + 1);
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                    if (lane == 0)
+                        __hip_atomic_store(cnt + 2, c + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    issue_g(c + 1);
+                }
+                // g of tile c: younger are tile c+2 and g of tile c+1
+                if (n2) wait_vm<NLG + Ly::NLOAD>();
+                else if (n1) wait_vm<NLG>();
+                else wait_vm<0>();
+                lds_barrier();
+            }
+            if (nch > 0) lds_barrier();     // the owners finish the last tile
+            return nch;
+        }
         if (nch > 0) {
             issue(0);
             if (nch > 1) {
@@ -631,9 +732,6 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
             }
             lds_barrier();
         }
-        if constexpr (R::NG) {
-            if (nch > 0) lds_barrier();     // the owners finish the last tile
-        }
         return nch;
     }
 
@@ -654,7 +752,7 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
         // fragments of the owners: token block tb = t / 16, step ks = jb, lane
         // (t % 16) + 16 (i / 4), slots 4 g + i % 4
         auto scores = [&](int c) {
-            const char* st = smem + (c % NR_W) * Ly::SLOT;
+            const char* st = smem + (c % Ly::NR) * Ly::SLOT;
             const char* Qs = st;
             const char* Ks = st + Ly::OFF_K;
             char* Pb = smem + Ly::OFF_P + (c & 1) * Ly::SZ_P;
@@ -702,10 +800,11 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
             }
         };
         // NG: the scores of tile c as a bf16 hi + lo pair in the one P buffer.
-        // They are formed in fp32 first; ready() returns once the owners no
-        // longer read the buffer (they have finished tile c-1's output).
+        // They are formed in fp32 first (masked; the gate enters the
+        // diagonal afterwards); ready() returns once the owners no longer
+        // read the buffer (they have finished tile c-1's output).
         auto scores_ng = [&](int c, auto ready) {
-            const char* st = smem + (c % NR_W) * Ly::SLOT;
+            const char* st = smem + (c % Ly::NR) * Ly::SLOT;
             const char* Qs = st;
             const char* Ks = st + Ly::OFF_K;
             char* Ph = smem + Ly::OFF_P;
@@ -718,7 +817,6 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
                 for (int kb = 0; kb < DK / 16; ++kb)
                     qf[kb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
                                                               Qs + toff<SEGK>(32 * s + l32, 16 * kb + 8 * g)));
-                const float gt = gtb[(c & 1) * CT + 32 * s + l32];
 #pragma unroll
                 for (int jb = 0; jb <= s; ++jb) {
                     f32x16_t sc = {};
@@ -729,14 +827,19 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
                         sc = mma(kf, qf[kb], sc);
                     }
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        if (jb == s) sc[i] = fmaf(dsel[i], gt, sc[i]) * dmd[i];
-                        else sc[i] *= dmo[i];
-                    }
+                    for (int i = 0; i < 16; ++i) sc[i] *= (jb == s) ? dmd[i] : dmo[i];
                     acc[s * (s + 1) / 2 + jb] = sc;
                 }
             }
             ready();
+            // the gate on the diagonal (where the mask is 1)
+#pragma unroll
+            for (int s = 0; s < NKT; ++s) {
+                const float gt = gtb[(c & 1) * CT + 32 * s + l32];
+                f32x16_t& sc = acc[s * (s + 1) / 2 + s];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sc[i] = fmaf(dsel[i], gt, sc[i]);
+            }
 #pragma unroll
             for (int s = 0; s < NKT; ++s) {
                 const int tb = 2 * s + (l32 >> 4);
@@ -764,11 +867,12 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
         }
         lds_barrier();
         if constexpr (R::NG) {
-            // The epilogue's statistic. In iteration c the scorer adds the six
-            // owners' sums of o^2 of tile c (publish), then forms 1 / rms of
-            // tile c-1 from its own sum and the other slice's (combine), which
-            // that slice published one iteration earlier; the owners store
-            // tile c-1 once it is in LDS. Lane t handles token t of a tile.
+            // The epilogue's statistic. In iteration c the scorer forms 1 / rms
+            // of tile c-1 from its own sum and the other slice's, published an
+            // iteration earlier (combine), then adds the six owners' sums of
+            // o^2 of tile c and publishes them (publish); the owners store
+            // tile c-1 once its 1 / rms is in LDS. Lane t handles token t.
+            // The loader's gate is in gtb once cnt[2] says so.
             const float* ssb = reinterpret_cast<const float*>(smem + Ly::OFF_SS);
             float* invb = reinterpret_cast<float*>(smem + Ly::OFF_INV);
             int* cnt = reinterpret_cast<int*>(smem + Ly::OFF_CNT);
@@ -831,9 +935,16 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
             for (int c = 0; c < nch; ++c) {
                 // publish waits for the owners' sums of tile c, after which
                 // they no longer read the P buffer
-                if (c + 1 < nch) scores_ng(c + 1, [&] { publish(c); });
-                else publish(c);
+                // 1 / rms of tile c-1 first (the other slice published its
+                // sums an iteration ago), so the owners never wait for it
                 if (c > 0) combine(c - 1);
+                if (c + 1 < nch) {
+                    while (__hip_atomic_load(cnt + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < c + 2)
+                        __builtin_amdgcn_s_sleep(1);
+                    scores_ng(c + 1, [&] { publish(c); });
+                } else {
+                    publish(c);
+                }
                 lds_barrier();
             }
             if (nch > 0) {
@@ -886,11 +997,10 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
     f32x4_t dpart = {0.f, 0.f, 0.f, 0.f};      // DA: column sums of c_t x_t (.) v'_t
 
     // NG: the output tile is stored one iteration late, once 1 / rms of its
-    // tokens is known; prv holds it (fp32) and gpv its gate values.
+    // tokens is known; prv holds it (fp32).
     const int ccol = n0 + OWC * w + 4 * qg;    // this lane's first output column
     f32x4_t gam = {1.f, 1.f, 1.f, 1.f};
     f32x4_t prv[NTB];
-    u32x2_t gpv[NTB];
     if constexpr (R::NG) {
         if (p.ng_gamma != nullptr) {
             const float* gr = p.ng_gamma + (size_t)(h / p.per_tier) * dvr;
@@ -898,30 +1008,10 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
             for (int r = 0; r < 4; ++r) gam[r] = (ccol < dvr) ? gr[ccol + r] : 0.0f;
         }
     }
-    if constexpr (R::NG) {
-        // Wait for the initial state and the scales here: with vector loads
-        // inside the tile loop (the gate values) the compiler would wait for
-        // them at their first read in the loop, every tile, and that wait
-        // would take in the gate loads just issued as well.
-#pragma unroll
-        for (int db = 0; db < NDB16; ++db) asm volatile("" ::"v"(sacc[db]));
-        asm volatile("" ::"v"(gam));
-    }
+    // FULL: tile c has CT tokens and the slice d_v columns, so no store is
+    // masked. (Guarded stores each sit in a branch, and at every join the
+    // compiler waits for all outstanding memory operations.)
     auto ng_at = [&](int c, int t) -> size_t { return ((size_t)(trow0 + c * CT + t) * H + h) * dvr + ccol; };
-    // FULL: tile c has CT tokens and the slice d_v columns, so no lane is
-    // masked. (Guarded loads and stores each sit in a branch, and at every
-    // join the compiler waits for all outstanding memory operations.)
-    auto load_g = [&](int c, auto full_tag) {
-        constexpr bool FULL = decltype(full_tag)::value;
-        const int cl = FULL ? CT : min(CT, len - c * CT);
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) {
-            const int t = 16 * tb + l16;
-            const u32x2_t z2 = {0u, 0u};
-            if (FULL) gpv[tb] = *reinterpret_cast<const u32x2_t*>(p.ng_g + ng_at(c, t));
-            else gpv[tb] = (t < cl && ccol < dvr) ? *reinterpret_cast<const u32x2_t*>(p.ng_g + ng_at(c, t)) : z2;
-        }
-    };
     auto finish = [&](int c, auto full_tag) {
         constexpr bool FULL = decltype(full_tag)::value;
         const int* cnt = reinterpret_cast<const int*>(smem + Ly::OFF_CNT);
@@ -929,11 +1019,13 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
         while (__hip_atomic_load(cnt + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < tseq0 + c + 1)
             __builtin_amdgcn_s_sleep(1);
         const int cl = FULL ? CT : min(CT, len - c * CT);
+        const char* gt_ = smem + Ly::OFF_G + (c % 3) * Ly::SZ_V;
         u32x2_t w2[NTB];
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb) {
             const float inv = invb[16 * tb + l16];
-            const float gv[4] = {bf_lo(gpv[tb][0]), bf_hi(gpv[tb][0]), bf_lo(gpv[tb][1]), bf_hi(gpv[tb][1])};
+            const u32x2_t gw = lds_u32x2(gt_, toff<SEGV>(16 * tb + l16, OWC * w + 4 * qg));
+            const float gv[4] = {bf_lo(gw[0]), bf_hi(gw[0]), bf_lo(gw[1]), bf_hi(gw[1])};
             float y[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) y[r] = silu_f(gv[r]) * (gam[r] * (prv[tb][r] * inv));
@@ -949,11 +1041,7 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
     auto tile = [&](int c, auto full_tag) {
         constexpr bool FULL = decltype(full_tag)::value;
         f32x4_t cur[NTB];
-        if constexpr (R::NG) {
-            // used at the end of the tile; tile c-1 is full when tile c is
-            if (c > 0) load_g(c - 1, full_tag);
-        }
-        const char* st = smem + (c % NR_W) * Ly::SLOT;
+        const char* st = smem + (c % Ly::NR) * Ly::SLOT;
         const char* Qs = st;
         const char* Ks = st + Ly::OFF_K;
         const char* Vs = st + Ly::OFF_V;
@@ -1128,6 +1216,7 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
                 sacc[db] = mma16(kf, vc[ks], sacc[db]);
             }
         if constexpr (R::NG) {
+            // tile c-1 is full when tile c is
             if (c > 0) finish(c - 1, full_tag);
 #pragma unroll
             for (int tb = 0; tb < NTB; ++tb) prv[tb] = cur[tb];
@@ -1144,7 +1233,6 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
     }
     if constexpr (R::NG) {
         if (nch > 0) {
-            load_g(nch - 1, std::false_type{});
             finish(nch - 1, std::false_type{});
             lds_barrier();
         }

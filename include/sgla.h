@@ -183,7 +183,8 @@ sgla_status sgla_chunk_fwd(const void* q, const void* k, const void* v,
  *           outputs are NaN and the buffer's first int is set to 1 (zero-fill
  *           it again before the next call).
  * Errors: as sgla_chunk_fwd; SGLA_ERR_UNSUPPORTED for SGLA_F32 (compose
- * sgla_chunk_fwd and sgla_head_norm_gate); SGLA_ERR_INVALID_ARG for n_tiers
+ * sgla_chunk_fwd and sgla_head_norm_gate) or H * d_v above 2^24;
+ * SGLA_ERR_INVALID_ARG for n_tiers
  * not dividing H, a bad eps, or overlapping buffers; SGLA_ERR_WORKSPACE for a
  * NULL, misaligned or short exchange buffer; SGLA_ERR_HIP for a launch
  * failure, including a device that cannot hold the cooperative grid.

@@ -158,6 +158,7 @@ FNG_BAD = [
     ("final overlaps out", dict(sf=P["nout"] + 1024), B.SGLA_ERR_INVALID_ARG),
     ("final overlaps g", dict(sf=P["ng"] + 1024), B.SGLA_ERR_INVALID_ARG),
     ("packed with B=2", dict(cu=P["cu"], n_seq=3), B.SGLA_ERR_INVALID_ARG),
+    ("H * d_v above 2^24", dict(H=1 << 18, T=1, B=1, tiers=1), B.SGLA_ERR_UNSUPPORTED),
 ]
 
 
