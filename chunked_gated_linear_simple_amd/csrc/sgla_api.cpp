@@ -264,7 +264,8 @@ sgla_status sgla_chunk_fwd_norm_gate(const void* q, const void* k, const void* v
                                      const float* a, const float* init_state, float* final_state, const void* g,
                                      const float* gamma, void* out, void* o, const int32_t* cu_seqlens, int n_seq,
                                      int B, int H, int T, int d_k, int d_v, int chunk, int n_tiers, float eps,
-                                     sgla_dtype dtype, void* exchange, size_t exchange_bytes, void* hip_stream)
+                                     sgla_dtype dtype, void* exchange, size_t exchange_bytes, unsigned flags,
+                                     void* hip_stream)
 {
     sgla::ChunkProblem p;
     sgla_status st = check_chunk(q, k, v, lambda, a, cu_seqlens, n_seq, B, H, T, d_k, d_v, chunk,
@@ -272,6 +273,8 @@ sgla_status sgla_chunk_fwd_norm_gate(const void* q, const void* k, const void* v
     if (st != SGLA_OK) return st;
     if (dtype != SGLA_BF16)
         return fail(SGLA_ERR_UNSUPPORTED, "the fused forward and epilogue is bf16 only");
+    if ((flags & ~SGLA_FNG_PLAIN_LAUNCH) != 0u)
+        return fail(SGLA_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
     REQUIRE_PTR(g);
     REQUIRE_PTR(out);
     OPTIONAL_PTR(o);
@@ -307,7 +310,8 @@ sgla_status sgla_chunk_fwd_norm_gate(const void* q, const void* k, const void* v
     st = check_disjoint(wr, 4, rd, 8);
     if (st != SGLA_OK) return st;
     hipError_t e = sgla::launch_fwd_norm_gate_bf16(p, q, k, v, init_state, final_state, g, gamma, out, o, n_tiers,
-                                                   eps, exchange, reinterpret_cast<hipStream_t>(hip_stream));
+                                                   eps, exchange, (flags & SGLA_FNG_PLAIN_LAUNCH) == 0u,
+                                                   reinterpret_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return fail(SGLA_ERR_HIP, "chunk_fwd_norm_gate launch: %s", hipGetErrorString(e));
     return ok();
 }

@@ -89,7 +89,7 @@ static hipError_t ng_groups(int n_units, int nsl, int* groups)
 }
 
 template <int DK, int CT>
-static hipError_t run_fwd_ng(Args a, hipStream_t stream)
+static hipError_t run_fwd_ng(Args a, bool cooperative, hipStream_t stream)
 {
     int groups = 0;
     hipError_t e = ng_groups<DK, CT>(a.n_units, a.nsl, &groups);
@@ -97,9 +97,14 @@ static hipError_t run_fwd_ng(Args a, hipStream_t stream)
     for (int base = 0; base < a.n_units; base += groups) {
         a.unit_base = base;
         const int g = min(groups, (a.n_units - base + 7) / 8 * 8);
-        void* args[] = {&a};
-        e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_fwd_ng<DK, CT>), dim3(g * a.nsl),
-                                       dim3(NTHREADS_W), args, 0, stream);
+        if (cooperative) {
+            void* args[] = {&a};
+            e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_fwd_ng<DK, CT>), dim3(g * a.nsl),
+                                           dim3(NTHREADS_W), args, 0, stream);
+        } else {
+            hipLaunchKernelGGL((k_fwd_ng<DK, CT>), dim3(g * a.nsl), dim3(NTHREADS_W), 0, stream, a);
+            e = hipGetLastError();
+        }
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -199,7 +204,7 @@ static_assert(SGLA_FWD_NORM_GATE_EXCHANGE_BYTES ==
 hipError_t launch_fwd_norm_gate_bf16(const ChunkProblem& p, const void* q, const void* k, const void* v,
                                      const float* init_state, float* final_state, const void* g,
                                      const float* gamma, void* out, void* o, int n_tiers, float eps,
-                                     void* exchange, hipStream_t stream)
+                                     void* exchange, bool cooperative, hipStream_t stream)
 {
     scan::Args a = fwd_args(p, q, k, v, init_state, final_state, o);
     a.ng_g = reinterpret_cast<const uint16_t*>(g);
@@ -211,9 +216,11 @@ hipError_t launch_fwd_norm_gate_bf16(const ChunkProblem& p, const void* q, const
     a.inv_dv = 1.0f / (float)p.d_v;
     a.eps = eps;
     const bool t32 = bf16_tile(p.chunk) == 32;
-    if (p.d_k <= 32) return t32 ? scan::run_fwd_ng<32, 32>(a, stream) : scan::run_fwd_ng<32, 64>(a, stream);
-    if (p.d_k <= 64) return t32 ? scan::run_fwd_ng<64, 32>(a, stream) : scan::run_fwd_ng<64, 64>(a, stream);
-    return t32 ? scan::run_fwd_ng<96, 32>(a, stream) : scan::run_fwd_ng<96, 64>(a, stream);
+    if (p.d_k <= 32)
+        return t32 ? scan::run_fwd_ng<32, 32>(a, cooperative, stream) : scan::run_fwd_ng<32, 64>(a, cooperative, stream);
+    if (p.d_k <= 64)
+        return t32 ? scan::run_fwd_ng<64, 32>(a, cooperative, stream) : scan::run_fwd_ng<64, 64>(a, cooperative, stream);
+    return t32 ? scan::run_fwd_ng<96, 32>(a, cooperative, stream) : scan::run_fwd_ng<96, 64>(a, cooperative, stream);
 }
 
 // bf16 forward with d_k <= 96 (padded to 32, 64 or 96) and any d_v (96-column slices).

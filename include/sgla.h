@@ -147,6 +147,12 @@ sgla_status sgla_chunk_fwd(const void* q, const void* k, const void* v,
 #define SGLA_FWD_NORM_GATE_EXCHANGE_BYTES ((size_t)2 * 1024 * 1024 + 256)
 
 /*
+ * Flag of sgla_chunk_fwd_norm_gate: an ordinary kernel launch instead of a
+ * cooperative one (see there).
+ */
+#define SGLA_FNG_PLAIN_LAUNCH 1u
+
+/*
  * Chunked forward with the mixer epilogue applied to each output tile before
  * it is stored: sgla_chunk_fwd followed by sgla_head_norm_gate in one kernel,
  * so that o need not go to memory and back. Laplace 3B post, "Challenge 1:
@@ -182,6 +188,12 @@ sgla_status sgla_chunk_fwd(const void* q, const void* k, const void* v,
  *           the wait gives up after a bounded number of polls: the affected
  *           outputs are NaN and the buffer's first int is set to 1 (zero-fill
  *           it again before the next call).
+ * flags:    0, or SGLA_FNG_PLAIN_LAUNCH: ordinary launches of the same grids
+ *           (sized to what the device holds), which skip the cooperative
+ *           launch's own cost (about 14 us per call on MI355X). Residency then
+ *           rests on the device running nothing else meanwhile; should other
+ *           work hold compute units for longer than the bounded wait, the
+ *           outputs concerned are NaN and the flag above is set.
  * Errors: as sgla_chunk_fwd; SGLA_ERR_UNSUPPORTED for SGLA_F32 (compose
  * sgla_chunk_fwd and sgla_head_norm_gate) or H * d_v above 2^24;
  * SGLA_ERR_INVALID_ARG for n_tiers
@@ -196,7 +208,8 @@ sgla_status sgla_chunk_fwd_norm_gate(const void* q, const void* k, const void* v
                                      const int32_t* cu_seqlens, int n_seq,
                                      int B, int H, int T, int d_k, int d_v, int chunk,
                                      int n_tiers, float eps, sgla_dtype dtype,
-                                     void* exchange, size_t exchange_bytes, void* hip_stream);
+                                     void* exchange, size_t exchange_bytes, unsigned flags,
+                                     void* hip_stream);
 
 /*
  * Bytes of device workspace sgla_chunk_fwd_segmented needs: two arrays of

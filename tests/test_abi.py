@@ -125,11 +125,11 @@ def test_chunk_fwd_rejects(L, name, kw, code):
 def fng_args(**kw):
     a = dict(q=P["q"], k=P["k"], v=P["v"], lam=P["lam"], a=P["a"], s0=P["s0"], sf=P["sf"], g=P["ng"],
              gm=P["gm"], out=P["nout"], o=P["o"], cu=None, n_seq=0, B=2, H=16, T=256, d_k=96, d_v=192,
-             chunk=128, tiers=4, eps=1e-6, dt=B.SGLA_BF16, x=P["ws"], xb=B.FWD_NORM_GATE_EXCHANGE_BYTES)
+             chunk=128, tiers=4, eps=1e-6, dt=B.SGLA_BF16, x=P["ws"], xb=B.FWD_NORM_GATE_EXCHANGE_BYTES, fl=0)
     a.update(kw)
     return [a["q"], a["k"], a["v"], a["lam"], a["a"], a["s0"], a["sf"], a["g"], a["gm"], a["out"], a["o"],
             a["cu"], a["n_seq"], a["B"], a["H"], a["T"], a["d_k"], a["d_v"], a["chunk"], a["tiers"],
-            ctypes.c_float(a["eps"]), a["dt"], a["x"], a["xb"], None]
+            ctypes.c_float(a["eps"]), a["dt"], a["x"], a["xb"], a["fl"], None]
 
 
 FNG_BAD = [
@@ -159,6 +159,7 @@ FNG_BAD = [
     ("final overlaps g", dict(sf=P["ng"] + 1024), B.SGLA_ERR_INVALID_ARG),
     ("packed with B=2", dict(cu=P["cu"], n_seq=3), B.SGLA_ERR_INVALID_ARG),
     ("H * d_v above 2^24", dict(H=1 << 18, T=1, B=1, tiers=1), B.SGLA_ERR_UNSUPPORTED),
+    ("unknown flag", dict(fl=2), B.SGLA_ERR_INVALID_ARG),
 ]
 
 

@@ -9,6 +9,9 @@ Workloads (H=16, d_k=96, d_v=192, bf16, decays from the 1..2048 schedule):
   Decode:                 1280 sequences, state ~ N(0, 0.02), 64 steps
   Packed varlen fwd:      32 sequences, lengths log-uniform in [128, 32768]
                           (one of 32768), init states ~ N(0, 0.02)
+  Fused fwd + epilogue:   the Laplace layer fwd with g ~ N(0, 1), 4 tiers of
+                          gamma = 1 + N(0, 0.1), out against the oracle's
+                          forward followed by its epilogue
 """
 import numpy as np
 import pytest
@@ -187,3 +190,32 @@ def test_varlen_full():
                  store="bf16")
     assert_close(np.concatenate([Sh[u].ravel() for u in units]),
                  np.concatenate([ref[u][1].ravel() for u in units]), TOL["bf16"], "final_states")
+
+
+def test_laplace_fwd_norm_gate_full():
+    """sgla_chunk_fwd_norm_gate at B=8, T=2048 (one cooperative launch of 256
+    workgroups), the launch the bench times: sampled units' out rows and
+    final states against the oracle."""
+    tiers, eps = 4, 1e-6
+    inp = I.chunk_inputs(8, H, 2048, DK, DV, "bf16", seed=6, a_std=0.1)
+    gi = I.norm_inputs(6, 8, H, 2048, DV, tiers, "bf16")
+    d = device_inputs(inp)
+    x = torch.zeros(Bd.FWD_NORM_GATE_EXCHANGE_BYTES, dtype=torch.uint8, device="cuda")
+    out, _, Sf = Bd.sgla_chunk_fwd_norm_gate(d["q"], d["k"], d["v"], to_dev(LAM), to_dev(gi["g"], "bf16"),
+                                             a=d["a"], gamma=to_dev(gi["gamma"]), n_tiers=tiers, eps=eps,
+                                             chunk=128, want_final=True, exchange=x)
+    torch.cuda.synchronize()
+    _finite(out, "out")
+    assert int(torch.count_nonzero(x).item()) == 0, "exchange buffer not zero-filled after the call"
+    units = [(0, 0), (0, 15), (3, 7), (7, 0), (7, 15), (5, 11)]
+    fw = oracle_fwd_units(inp, LAM, units)
+    oh, Sh = to_host64(out), to_host64(Sf)
+    got, want = [], []
+    for (n, h) in units:
+        g = I.widen(gi["g"][n, :, h, :], "bf16")
+        gm = gi["gamma"][h // (H // tiers)][None].astype(np.float64)
+        want.append(oracle.head_norm_gate(fw[(n, h)][0][None, None], g[None, :, None, :], gm, 1, eps)[0, :, 0, :].ravel())
+        got.append(oh[n, :, h, :].ravel())
+    assert_close(np.concatenate(got), np.concatenate(want), TOL["bf16"], "out", store="bf16")
+    assert_close(np.concatenate([Sh[u].ravel() for u in units]),
+                 np.concatenate([fw[u][1].ravel() for u in units]), TOL["bf16"], "final_state")

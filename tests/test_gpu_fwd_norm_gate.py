@@ -167,3 +167,48 @@ def test_fused_in_place_and_default_exchange():
         assert out.data_ptr() == g2.data_ptr()
         assert torch.equal(out, ref)
     _check_exchange(Bd.fwd_norm_gate_exchange(g_d.device))
+
+
+def test_fused_a_null_equals_zero_a():
+    """a = NULL (aug_balance starts at zero) gives the explicit zero a's
+    result bit for bit, and matches the oracle given a = None."""
+    B, H, T, dk, dv, tiers = 1, 4, 150, 96, 192, 2
+    inp = I.chunk_inputs(B, H, T, dk, dv, "bf16", seed=174, a_std=None, s0_std=0.02)
+    gi = _gate_inputs(174, B, H, T, dv, tiers)
+    lam = schedule32(H, 1.0, 2048.0)
+    d = device_inputs(inp)
+    args = (d["q"], d["k"], d["v"], to_dev(lam), to_dev(gi["g"], "bf16"))
+    kw = dict(gamma=to_dev(gi["gamma"]), n_tiers=tiers, eps=EPS, init_state=d["S0"], want_final=True)
+    out0, _, S0f = Bd.sgla_chunk_fwd_norm_gate(*args, a=None, **kw)
+    out1, _, S1f = Bd.sgla_chunk_fwd_norm_gate(*args, a=torch.zeros_like(d["a"]), **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out0, out1) and torch.equal(S0f, S1f)
+    units = [(0, h) for h in range(H)]
+    oh = to_host64(out0)
+    want = []
+    for (n, h) in units:
+        o, _ = oracle.fwd_unit(*(I.widen(inp[x][n, h], "bf16") for x in ("q", "k", "v")), float(lam[h]), None,
+                               inp["S0"][n, h].astype(np.float64))
+        g = I.widen(gi["g"][n, :, h, :], "bf16")
+        gm = gi["gamma"][h // (H // tiers)][None].astype(np.float64)
+        want.append(oracle.head_norm_gate(o[None, None], g[None, :, None, :], gm, 1, EPS)[0, :, 0, :].ravel())
+    assert_close(np.concatenate([_out_unit(oh, n, h).ravel() for n, h in units]), np.concatenate(want),
+                 TOL["bf16"], "out (a=NULL)", store="bf16")
+
+
+@pytest.mark.parametrize("B,T", [(2, 300), (20, 70)], ids=["one_launch", "several_launches"])
+def test_fused_plain_launch_equals_cooperative(B, T):
+    """SGLA_FNG_PLAIN_LAUNCH runs the same grids with ordinary launches: the
+    same bits as the cooperative launches, and the exchange left zero-filled."""
+    H, dk, dv, tiers = 16, 96, 192, 4
+    inp = I.chunk_inputs(B, H, T, dk, dv, "bf16", seed=175, a_std=0.1, s0_std=0.02)
+    gi = _gate_inputs(175, B, H, T, dv, tiers)
+    d = device_inputs(inp)
+    args = (d["q"], d["k"], d["v"], to_dev(schedule32(H, 1.0, 2048.0)), to_dev(gi["g"], "bf16"))
+    kw = dict(a=d["a"], gamma=to_dev(gi["gamma"]), n_tiers=tiers, eps=EPS, init_state=d["S0"], want_final=True)
+    x = torch.zeros(Bd.FWD_NORM_GATE_EXCHANGE_BYTES, dtype=torch.uint8, device="cuda")
+    out0, _, S0f = Bd.sgla_chunk_fwd_norm_gate(*args, exchange=x, **kw)
+    _check_exchange(x)
+    out1, _, S1f = Bd.sgla_chunk_fwd_norm_gate(*args, exchange=x, plain_launch=True, **kw)
+    _check_exchange(x)
+    assert torch.equal(out0, out1) and torch.equal(S0f, S1f)
