@@ -1,6 +1,7 @@
 """The benchmark workloads at their full sizes, in the launch configuration the
-bench times, checked against the oracle on sampled (sequence, head) units
-(every output of a sampled unit is compared) plus properties over all units.
+bench times, checked against the oracle on every (sequence, head) unit (the
+oracle runs one thread per unit on the host's cores), except decode, which
+samples 256 of its 20,480 sequence-heads over all 64 steps.
 
 Workloads (H=16, d_k=96, d_v=192, bf16, decays from the 1..2048 schedule):
   Laplace layer fwd:      B=8,  T=2048, chunk 128, a = 0 and a ~ N(0, 0.1)
@@ -13,6 +14,8 @@ Workloads (H=16, d_k=96, d_v=192, bf16, decays from the 1..2048 schedule):
                           gamma = 1 + N(0, 0.1), out against the oracle's
                           forward followed by its epilogue
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -20,13 +23,18 @@ import torch
 import oracle
 from chunked_gated_linear_simple_amd import binding as Bd
 from chunked_gated_linear_simple_amd import inputs as I
-from tests.parity_util import (TOL, assert_close, device_inputs, gpu_unit, oracle_bwd_units,
-                               oracle_fwd_units, per_head_report, schedule32, to_dev, to_host64)
+from tests.parity_util import TOL, assert_close, device_inputs, per_head_report, schedule32, to_dev, to_host64
 
 pytestmark = pytest.mark.gpu
 
 H, DK, DV = 16, 96, 192
 LAM = schedule32(H, 1.0, 2048.0)
+# host threads for the oracle (the GPU machine's CPU share is 16)
+THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _wide(inp, names):
+    return [None if inp.get(n) is None else I.widen(inp[n], inp["dtype"]) for n in names]
 
 
 def _finite(t, what):
@@ -42,15 +50,13 @@ def test_laplace_fwd_full(a_std):
     torch.cuda.synchronize()
     _finite(o, "o")
     _finite(Sf, "final_state")
-    units = [(0, 0), (0, 15), (3, 7), (7, 0), (7, 15), (5, 11)]
-    ref = oracle_fwd_units(inp, LAM, units)
+    q, k, v = _wide(inp, ("q", "k", "v"))
+    o_ref, S_ref = oracle.fwd(q, k, v, LAM.astype(np.float64), inp["a"].astype(np.float64), threads=THREADS)
     oh, Sh = to_host64(o), to_host64(Sf)
-    per_head_report("o", {u: oh[u] for u in units}, {u: ref[u][0] for u in units}, "bf16")
-    assert_close(np.concatenate([oh[u].ravel() for u in units]),
-                 np.concatenate([ref[u][0].ravel() for u in units]), TOL["bf16"], "o",
-                 store="bf16")
-    assert_close(np.concatenate([Sh[u].ravel() for u in units]),
-                 np.concatenate([ref[u][1].ravel() for u in units]), TOL["bf16"], "final_state")
+    units = [(n, h) for n in range(8) for h in range(H)]
+    per_head_report("o", {u: oh[u] for u in units}, {u: o_ref[u] for u in units}, "bf16")
+    assert_close(oh, o_ref, TOL["bf16"], "o (all 128 units)", store="bf16")
+    assert_close(Sh, S_ref, TOL["bf16"], "final_state (all 128 units)")
 
 
 @pytest.mark.parametrize("a_std", [None, 0.1], ids=["a_zero", "a_normal"])
@@ -63,23 +69,17 @@ def test_laplace_fwd_bwd_full(a_std):
     torch.cuda.synchronize()
     for t, nm in ((o, "o"), (dq, "dq"), (dk, "dk"), (dv, "dv"), (da, "da")):
         _finite(t, nm)
-    heads = (0, 9, 15)
-    units = [(b, h) for b in range(4) for h in heads]  # all b for these heads -> exact da
-    ref = oracle_bwd_units(inp, LAM, units)
+    q, k, v, dO = _wide(inp, ("q", "k", "v", "dO"))
+    lam64, a64 = LAM.astype(np.float64), inp["a"].astype(np.float64)
+    ref = oracle.bwd(q, k, v, dO, lam64, a64, threads=THREADS)
+    units = [(b, h) for b in range(4) for h in range(H)]
     for idx, (nm, t) in enumerate((("dq", dq), ("dk", dk), ("dv", dv))):
         th = to_host64(t)
-        per_head_report(nm, {u: th[u] for u in units}, {u: ref[u][idx] for u in units}, "bf16")
-        assert_close(np.concatenate([th[u].ravel() for u in units]),
-                     np.concatenate([ref[u][idx].ravel() for u in units]), TOL["bf16"], nm,
-                     store="bf16")
-    da_ref = np.stack([sum(ref[(b, h)][3] for b in range(4)) for h in heads])
-    dah = to_host64(da)[list(heads)]
-    assert_close(dah, da_ref, TOL["bf16"], "da")
-    fref = oracle_fwd_units(inp, LAM, units)
-    oh = to_host64(o)
-    assert_close(np.concatenate([oh[u].ravel() for u in units]),
-                 np.concatenate([fref[u][0].ravel() for u in units]), TOL["bf16"], "o",
-                 store="bf16")
+        per_head_report(nm, {u: th[u] for u in units}, {u: ref[idx][u] for u in units}, "bf16")
+        assert_close(th, ref[idx], TOL["bf16"], nm + " (all 64 units)", store="bf16")
+    assert_close(to_host64(da), ref[3], TOL["bf16"], "da (all 16 heads)")
+    o_ref, _ = oracle.fwd(q, k, v, lam64, a64, threads=THREADS)
+    assert_close(to_host64(o), o_ref, TOL["bf16"], "o (all 64 units)", store="bf16")
 
 
 def test_laplace_bwd_slice_finite_differences():
@@ -147,7 +147,8 @@ def test_decode_full_64_steps():
     S0 = I.gaussian(4, I.STREAM_S0, (N, H, DK, DV), 0.02)
     a = I.gaussian(4, I.STREAM_A, (H, DK), 0.1)
     state = to_dev(S0)
-    units = [(0, 0), (0, 15), (640, 3), (1279, 15), (77, 8), (1001, 12)]
+    units = sorted(set([(0, 0), (0, 15), (1279, 0), (1279, 15)] +
+                       [(int(n), int(h)) for n, h in zip(np.linspace(0, N - 1, 252).round(), np.arange(252) % H)]))
     Sref = {u: S0[u].astype(np.float64).copy() for u in units}
     del S0
     lam_d, a_d = to_dev(LAM), to_dev(a)
@@ -180,22 +181,17 @@ def test_varlen_full():
     torch.cuda.synchronize()
     _finite(o, "o")
     _finite(Sf, "final_states")
-    longest = int(np.argmax(L))
-    shortest = int(np.argmin(L))
-    units = [(longest, 0), (longest, 15), (shortest, 0), (shortest, 15), (3, 8), (17, 12)]
-    ref = oracle_fwd_units(inp, LAM, units, cu)
-    oh, Sh = to_host64(o), to_host64(Sf)
-    assert_close(np.concatenate([gpu_unit(oh, n, h, cu).ravel() for n, h in units]),
-                 np.concatenate([ref[u][0].ravel() for u in units]), TOL["bf16"], "o",
-                 store="bf16")
-    assert_close(np.concatenate([Sh[u].ravel() for u in units]),
-                 np.concatenate([ref[u][1].ravel() for u in units]), TOL["bf16"], "final_states")
+    q, k, v = _wide(inp, ("q", "k", "v"))
+    o_ref, S_ref = oracle.fwd(q, k, v, LAM.astype(np.float64), inp["a"].astype(np.float64),
+                              inp["S0"].astype(np.float64), cu_seqlens=cu, threads=THREADS)
+    assert_close(to_host64(o), o_ref, TOL["bf16"], "o (all 512 units)", store="bf16")
+    assert_close(to_host64(Sf), S_ref, TOL["bf16"], "final_states (all 512 units)")
 
 
 def test_laplace_fwd_norm_gate_full():
     """sgla_chunk_fwd_norm_gate at B=8, T=2048 (one cooperative launch of 256
-    workgroups), the launch the bench times: sampled units' out rows and
-    final states against the oracle."""
+    workgroups), the launch the bench times: every unit's out rows and final
+    state against the oracle."""
     tiers, eps = 4, 1e-6
     inp = I.chunk_inputs(8, H, 2048, DK, DV, "bf16", seed=6, a_std=0.1)
     gi = I.norm_inputs(6, 8, H, 2048, DV, tiers, "bf16")
@@ -207,15 +203,8 @@ def test_laplace_fwd_norm_gate_full():
     torch.cuda.synchronize()
     _finite(out, "out")
     assert int(torch.count_nonzero(x).item()) == 0, "exchange buffer not zero-filled after the call"
-    units = [(0, 0), (0, 15), (3, 7), (7, 0), (7, 15), (5, 11)]
-    fw = oracle_fwd_units(inp, LAM, units)
-    oh, Sh = to_host64(out), to_host64(Sf)
-    got, want = [], []
-    for (n, h) in units:
-        g = I.widen(gi["g"][n, :, h, :], "bf16")
-        gm = gi["gamma"][h // (H // tiers)][None].astype(np.float64)
-        want.append(oracle.head_norm_gate(fw[(n, h)][0][None, None], g[None, :, None, :], gm, 1, eps)[0, :, 0, :].ravel())
-        got.append(oh[n, :, h, :].ravel())
-    assert_close(np.concatenate(got), np.concatenate(want), TOL["bf16"], "out", store="bf16")
-    assert_close(np.concatenate([Sh[u].ravel() for u in units]),
-                 np.concatenate([fw[u][1].ravel() for u in units]), TOL["bf16"], "final_state")
+    q, k, v = _wide(inp, ("q", "k", "v"))
+    o_ref, S_ref = oracle.fwd(q, k, v, LAM.astype(np.float64), inp["a"].astype(np.float64), threads=THREADS)
+    out_ref = oracle.head_norm_gate(o_ref, I.widen(gi["g"], "bf16"), gi["gamma"].astype(np.float64), tiers, eps)
+    assert_close(to_host64(out), out_ref, TOL["bf16"], "out (all 128 units)", store="bf16")
+    assert_close(to_host64(Sf), S_ref, TOL["bf16"], "final_state (all 128 units)")
