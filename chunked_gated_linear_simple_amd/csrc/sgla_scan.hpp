@@ -151,10 +151,14 @@ __device__ __forceinline__ int toff(int r, int e)
 // 16 bytes per lane from global memory straight into LDS: lane l's bytes land
 // at dst + 16 l (global_load_lds_dwordx4; completion is counted by vmcnt).
 // The address is a uniform base plus a 32-bit lane offset in bytes, so the
-// load takes its base from scalar registers.
+// load takes its base from scalar registers. POL is the load's cache policy:
+// 0, or POL_NT (the non-temporal hint) for data no later access of the launch
+// wants from the caches.
+constexpr int POL_NT = 2;
+template <int POL = 0>
 __device__ __forceinline__ void dma16(const char* base, uint32_t off, char* dst)
 {
-    __builtin_amdgcn_global_load_lds(base + off, (lds_void*)dst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(base + off, (lds_void*)dst, 16, 0, POL);
 }
 
 __device__ __forceinline__ u32x2_t lds_u32x2(const char* base, int off)
@@ -547,13 +551,18 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
             const char* qb = R::OUT ? reinterpret_cast<const char*>(p.q + rb * dkr) : nullptr;
             const char* kb = reinterpret_cast<const char*>(p.k + rb * dkr);
             const char* vb = reinterpret_cast<const char*>(p.v + rb * dvr);
+            // The forward scans read every tile once (the value slices of a
+            // unit at about the same time), so their tiles stream past the
+            // caches; the backward's roles read the same tiles at different
+            // times and keep the default policy.
+            constexpr int POL = (!R::GRAD && !R::REV) ? POL_NT : 0;
 #pragma unroll
             for (int m = 0; m < Ly::NLQ; ++m) {
-                if constexpr (R::OUT) dma16(qb, offq[m], st + 1024 * m);
-                dma16(kb, offq[m], st + Ly::OFF_K + 1024 * m);
+                if constexpr (R::OUT) dma16<POL>(qb, offq[m], st + 1024 * m);
+                dma16<POL>(kb, offq[m], st + Ly::OFF_K + 1024 * m);
             }
 #pragma unroll
-            for (int m = 0; m < Ly::NLV; ++m) dma16(vb, offv[m], st + Ly::OFF_V + 1024 * m);
+            for (int m = 0; m < Ly::NLV; ++m) dma16<POL>(vb, offv[m], st + Ly::OFF_V + 1024 * m);
             if constexpr (R::GRAD) {
                 const char* xb = reinterpret_cast<const char*>(p.x + rb * dvr);
 #pragma unroll
@@ -662,7 +671,7 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
                 const char* gb = reinterpret_cast<const char*>(p.ng_g + ((size_t)(trow0 + c * CT) * H + h) * dvr);
                 char* dst = smem + Ly::OFF_G + (c % 3) * Ly::SZ_V;
 #pragma unroll
-                for (int m = 0; m < NLG; ++m) dma16(gb, offg[m], dst + 1024 * m);
+                for (int m = 0; m < NLG; ++m) dma16<POL_NT>(gb, offg[m], dst + 1024 * m);
             };
             int* cnt = reinterpret_cast<int*>(smem + Ly::OFF_CNT);
             if (nch > 0) {
