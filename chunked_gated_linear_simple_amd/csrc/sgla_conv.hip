@@ -55,7 +55,10 @@ __device__ __forceinline__ float silu_f(float x)
     return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-// A channel group: 8 bf16 or 4 fp32 values in 16 bytes.
+// A channel group: 8 bf16 or 4 fp32 values in 16 bytes. The forward's rows
+// stream through once (a run's three-row halo was read a whole run earlier
+// and is gone from the caches either way), so its loads and stores carry the
+// non-temporal hint.
 template <typename E> struct Grp;
 template <> struct Grp<u16> {
     static constexpr int V = 8;
@@ -69,7 +72,7 @@ template <> struct Grp<u16> {
     }
     static __device__ __forceinline__ void load(const u16* p, float* x)
     {
-        unpack(*reinterpret_cast<const u32x4*>(p), x);
+        unpack(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)), x);
     }
     static __device__ __forceinline__ void store(u16* p, const float* y)
     {
@@ -80,7 +83,7 @@ template <> struct Grp<u16> {
             bf16x2 v = {static_cast<__bf16>(y[2 * i]), static_cast<__bf16>(y[2 * i + 1])};
             w[i] = __builtin_bit_cast(uint32_t, v);
         }
-        *reinterpret_cast<u32x4*>(p) = w;
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
     }
 };
 template <> struct Grp<float> {
@@ -92,12 +95,12 @@ template <> struct Grp<float> {
     }
     static __device__ __forceinline__ void load(const float* p, float* x)
     {
-        unpack(*reinterpret_cast<const u32x4*>(p), x);
+        unpack(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)), x);
     }
     static __device__ __forceinline__ void store(float* p, const float* y)
     {
         const f32x4 v = {y[0], y[1], y[2], y[3]};
-        *reinterpret_cast<f32x4*>(p) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
     }
 };
 
@@ -450,6 +453,9 @@ constexpr int BWD_PF = 4;  // rows of u and dy in flight per thread
 
 // Two channels per access for the backward (4 bytes of bf16, 8 of fp32): a
 // thread's windows, weights and partial sums then fit seven waves per SIMD.
+// Its stores carry the non-temporal hint; its loads keep the default policy
+// (the rows around a run's ends are read again, and the prefetch past the
+// last row repeats it).
 template <typename E> struct Q2;
 template <> struct Q2<u16> {
     static constexpr int V = 2;
@@ -465,7 +471,7 @@ template <> struct Q2<u16> {
     {
         typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
         const bf16x2 lo = {static_cast<__bf16>(y[0]), static_cast<__bf16>(y[1])};
-        *reinterpret_cast<uint32_t*>(p) = __builtin_bit_cast(uint32_t, lo);
+        __builtin_nontemporal_store(__builtin_bit_cast(uint32_t, lo), reinterpret_cast<uint32_t*>(p));
     }
 };
 template <> struct Q2<float> {
@@ -480,7 +486,8 @@ template <> struct Q2<float> {
     }
     static __device__ __forceinline__ void store(float* p, const float* y)
     {
-        *reinterpret_cast<uint2*>(p) = uint2{__float_as_uint(y[0]), __float_as_uint(y[1])};
+        typedef unsigned int u32v2 __attribute__((ext_vector_type(2)));
+        __builtin_nontemporal_store(u32v2{__float_as_uint(y[0]), __float_as_uint(y[1])}, reinterpret_cast<u32v2*>(p));
     }
 };
 

@@ -46,11 +46,18 @@ __device__ __forceinline__ float silu_g(float x)
     return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-// 4 channels: 8 bytes of bf16 or 16 of fp32
+// 4 channels: 8 bytes of bf16 or 16 of fp32. The rows stream through once
+// (every element is read and written by one lane, once), so loads and stores
+// carry the non-temporal hint.
+typedef unsigned int u32v2 __attribute__((ext_vector_type(2)));
 template <typename E> struct Ch4;
 template <> struct Ch4<u16> {
     typedef uint2 Raw;
-    static __device__ __forceinline__ Raw load(const u16* p) { return *reinterpret_cast<const uint2*>(p); }
+    static __device__ __forceinline__ Raw load(const u16* p)
+    {
+        const u32v2 w = __builtin_nontemporal_load(reinterpret_cast<const u32v2*>(p));
+        return uint2{w[0], w[1]};
+    }
     static __device__ __forceinline__ Raw zero() { return uint2{0u, 0u}; }
     static __device__ __forceinline__ void unpack(Raw r, float* x)
     {
@@ -64,12 +71,16 @@ template <> struct Ch4<u16> {
         typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
         const bf16x2 lo = {static_cast<__bf16>(y[0]), static_cast<__bf16>(y[1])};
         const bf16x2 hi = {static_cast<__bf16>(y[2]), static_cast<__bf16>(y[3])};
-        *reinterpret_cast<uint2*>(p) = uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+        const u32v2 w = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32v2*>(p));
     }
 };
 template <> struct Ch4<float> {
     typedef f32x4 Raw;
-    static __device__ __forceinline__ Raw load(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+    static __device__ __forceinline__ Raw load(const float* p)
+    {
+        return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    }
     static __device__ __forceinline__ Raw zero() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
     static __device__ __forceinline__ void unpack(Raw r, float* x)
     {
@@ -78,7 +89,7 @@ template <> struct Ch4<float> {
     }
     static __device__ __forceinline__ void store(float* p, const float* y)
     {
-        *reinterpret_cast<f32x4*>(p) = f32x4{y[0], y[1], y[2], y[3]};
+        __builtin_nontemporal_store(f32x4{y[0], y[1], y[2], y[3]}, reinterpret_cast<f32x4*>(p));
     }
 };
 
