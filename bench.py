@@ -62,6 +62,29 @@ MFMA_FILE = os.path.join(ROOT, "profiles", "k_fwd_k_bwd__laplace_mfma_counters.t
 CSRC = os.path.join(ROOT, "chunked_gated_linear_simple_amd", "csrc")
 FWD_SOURCES = [os.path.join(CSRC, f) for f in ("sgla_scan.hpp", "sgla_fwd.hip")]
 CHUNK_SOURCES = FWD_SOURCES + [os.path.join(CSRC, "sgla_bwd.hip")]
+_CONV, _NORM, _DEC = (os.path.join(CSRC, f) for f in ("sgla_conv.hip", "sgla_norm.hip", "sgla_decode.hip"))
+# HBM bytes per call (per step for decode) of the secondary workloads from the
+# committed counter summaries: file, the sources its hash covers, and the keys
+# whose values add up to one call. For the gradient legs it is the row kernel's
+# bytes alone (the small fixed-order sums after it are not counted).
+COUNTER_BYTES = {
+    "fwdbwd_B4": ("k_bwd__fwdbwd_B4_hbm_traffic.txt", CHUNK_SOURCES,
+                  ("fwd_b4_traffic_bytes_per_launch", "bwd_b4_traffic_bytes_per_launch")),
+    "decode_N1280_64steps": ("k_decode__decode_N1280_hbm_traffic.txt", [_DEC],
+                             ("decode_traffic_bytes_per_step",)),
+    "head_norm_gate_B8_T2048": ("k_head_norm_gate__laplace_B8_T2048_hbm_traffic.txt", [_NORM],
+                                ("traffic_bytes_per_launch",)),
+    "head_norm_gate_bwd_B8_T2048": ("k_conv_bwd_k_head_norm_gate_bwd__B8_T2048_hbm_traffic.txt", [_CONV, _NORM],
+                                    ("norm_bwd_traffic_bytes_per_launch",)),
+    "fwd_norm_gate_B8_T2048": ("k_fwd_ng__laplace_fwd_norm_gate_B8_hbm_traffic.txt", FWD_SOURCES,
+                               ("traffic_bytes_per_launch",)),
+    "conv_fwd_B8_T2048_D3072": ("k_conv__prologue_B8_T2048_D3072_and_decode_N1280_hbm_traffic.txt", [_CONV],
+                                ("conv_fwd_traffic_bytes_per_launch",)),
+    "conv_decode_N1280_D3072_64steps": ("k_conv__prologue_B8_T2048_D3072_and_decode_N1280_hbm_traffic.txt", [_CONV],
+                                        ("conv_decode_traffic_bytes_per_step",)),
+    "conv_bwd_B8_T2048_D3072": ("k_conv_bwd_k_head_norm_gate_bwd__B8_T2048_hbm_traffic.txt", [_CONV, _NORM],
+                                ("conv_bwd_traffic_bytes_per_launch",)),
+}
 # algorithmic matrix-core FLOPs per head-token with the causal mask exploited
 # (C = 128): forward C(d_k + d_v) + 4 d_k d_v + 2 d_k + 2 d_v; backward
 # C(3 d_k + 2 d_v) + 10 d_k d_v + 8 d_k + 4 d_v
@@ -110,6 +133,28 @@ def executed_mfma_flops(key):
         return None if kv is None else int(kv[key + "_executed_flops"])
     except (KeyError, ValueError):
         return None
+
+
+def counter_bytes(name):
+    """Measured HBM bytes per call of secondary workload name, or None when
+    there is no summary or its kernel sources have changed since."""
+    if name not in COUNTER_BYTES:
+        return None
+    fname, sources, keys = COUNTER_BYTES[name]
+    kv = _profile_values(os.path.join(ROOT, "profiles", fname), sources)
+    try:
+        return None if kv is None else sum(int(kv[k]) for k in keys)
+    except (KeyError, ValueError):
+        return None
+
+
+def call_seconds(r):
+    """The time one call (one step for decode) of a secondary leg takes."""
+    if "us_per_step" in r:
+        return r["us_per_step"] * 1e-6
+    if "ms_bwd" in r:
+        return (r["ms_fwd"] + r["ms_bwd"]) * 1e-3
+    return r["ms"] * 1e-3
 
 
 def parse():
@@ -641,8 +686,12 @@ def main():
         secondary["conv_fwd_B8_T2048_D3072"] = bench_conv(args)
         secondary["conv_decode_N1280_D3072_64steps"] = bench_conv_decode(args)
         secondary["conv_bwd_B8_T2048_D3072"] = bench_conv_bwd(args)
-    for r in secondary.values():
+    for name, r in secondary.items():
         r["hbm_frac_algorithmic"] = r["gbs"] / HBM_PEAK_GBS
+        tb = counter_bytes(name)
+        if tb is not None:
+            r["traffic_bytes"] = tb
+            r["hbm_frac_counter"] = tb / call_seconds(r) / 1e9 / HBM_PEAK_GBS
 
     line = {"metric": "GLA tokens/s (fwd, fwd+bwd, decode) at H=16 dk=96 dv=192; % MFMA/HBM peak",
             "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True, "scaling": "weak",
@@ -663,6 +712,8 @@ def main():
                          "mfma_frac_algorithmic": fwd["flops"] / (fwd["ms"] * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
                          "mfma_frac_executed": None},
         })
+        tr = line["roofline"]["traffic"]
+        line["roofline"]["frac_traffic"] = None if tr is None else tr / (fwd["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS
         ex = executed_mfma_flops("fwd_b8")
         if ex is not None:
             line["roofline"]["mfma_frac_executed"] = ex / (fwd["ms"] * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)
