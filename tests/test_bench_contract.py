@@ -38,3 +38,23 @@ def test_profile_values_follow_the_source_hash(tmp_path):
     src.write_bytes(b"kernel source, changed")
     assert bench._profile_values(str(prof), [str(src)]) is None
     assert bench._profile_values(str(tmp_path / "missing.txt"), [str(src)]) is None
+
+
+def test_counter_byte_map_names_real_summaries():
+    # every leg's counter bytes come from a committed summary that holds the
+    # keys the map names and a source hash (checked or not, the keys must exist)
+    for name, (fname, sources, keys) in bench.COUNTER_BYTES.items():
+        path = os.path.join(ROOT, "profiles", fname)
+        text = open(path).read()
+        for k in keys:
+            assert f"\n{k}: " in text, (name, k)
+        assert "\nsources_sha256: " in text, name
+        for f in sources:
+            assert os.path.exists(f), f
+    assert bench.counter_bytes("no such leg") is None
+
+
+def test_call_seconds_per_leg_kind():
+    assert bench.call_seconds({"us_per_step": 500.0, "ms": 9.0}) == 500e-6
+    assert abs(bench.call_seconds({"ms_fwd": 0.07, "ms_bwd": 0.13}) - 0.2e-3) < 1e-12
+    assert bench.call_seconds({"ms": 0.05}) == 0.05e-3
