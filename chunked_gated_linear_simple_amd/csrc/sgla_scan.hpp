@@ -272,9 +272,11 @@ constexpr int NG_SPIN_MAX = 1 << 20;
 //     gate sigmoid(z) of the tile two ahead;
 //   * wave 7 ("scorer") computes the decay-masked scores of the next tile and
 //     writes P^T in the owners' operand order (a 16-token x 32-key block is one
-//     1 KB fragment, 16 B per lane). For FWD and DV it adds the gate on the
-//     diagonal; for DQ and DK it forms c_t = sigmoid'(z_t) (q'_t . k'_t) from
-//     the raw diagonal instead, which the owners apply in their epilogue.
+//     1 KB fragment, 16 B per lane). P leaves out the diagonal: the scorer
+//     passes the raw diagonal q'_t . k'_t to the owners in fp32 (plus the gate
+//     for FWD and DV), and for DQ and DK also c_t = sigmoid'(z_t) (q'_t . k'_t);
+//     the owners apply both in their epilogue. (A bf16 diagonal costs 2^-9 of
+//     the term that dominates a short-memory head's output.)
 // A tile's data is waited for by the loader two iterations before the owners
 // use it, so the gate and the scores of tile c+1 both run during iteration c.
 // The NG role (the epilogue applied before the store) differs: its ring is
@@ -350,7 +352,11 @@ struct LayW {
     static constexpr int OFF_KEEP = OFF_CORR + 2 * CT * 4;  // masks of A, one word per token pair [2][CT/2]
     static constexpr int OFF_GT = OFF_KEEP + CT * 4;        // gate sigmoid(z) [2][CT]
     static constexpr int OFF_CG = OFF_GT + 2 * CT * 4;      // gate-derivative factors [2][CT]
-    static constexpr int OFF_A = OFF_CG + (R::GRAD ? 2 * CT * 4 : 0);  // a at the v' columns [DVS]
+    // The diagonal of the scores in fp32 [2][CT] (with the gate for FWD and
+    // DV): it stays out of the bf16 P, and the owners add it times v'_t.
+    static constexpr bool DIAG32 = R::OUT && !R::NG;
+    static constexpr int OFF_DG = OFF_CG + (R::GRAD ? 2 * CT * 4 : 0);
+    static constexpr int OFF_A = OFF_DG + (DIAG32 ? 2 * CT * 4 : 0);  // a at the v' columns [DVS]
     static constexpr int OFF_SS = OFF_A + (R::GRAD ? DVS * 4 : 0);     // NG: owners' sums of o^2 [NOW_W][CT]
     static constexpr int OFF_INV = OFF_SS + (R::NG ? NOW_W * CT * 4 : 0);  // NG: 1 / rms per token [CT]
     // NG: sums ready, 1 / rms ready, tile and gate ready
@@ -491,6 +497,7 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
     }
     float* gtb = reinterpret_cast<float*>(smem + Ly::OFF_GT);
     float* cgb = reinterpret_cast<float*>(smem + Ly::OFF_CG);
+    float* dgb = reinterpret_cast<float*>(smem + Ly::OFF_DG);
     // NG: sigmoid(z_t) of tile c on the VALU in fp32, lane = token, a in fp32.
     // All row reads are issued first and four partial sums break the chain.
     auto gate_valu = [&](int c) {
@@ -784,24 +791,30 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
                         sc = mma(kf, qf[kb], sc);
                     }
                     if (jb == s) {
-                        if constexpr (R::GRAD) {
-                            // c_t = sigmoid'(z_t) (q'_t . k'_t), the raw score's diagonal
-                            float u = 0.0f;
+                        // the raw diagonal q'_t . k'_t, which P leaves out: the owners
+                        // add it in fp32 (with the gate for FWD and DV); for DQ and DK
+                        // also c_t = sigmoid'(z_t) (q'_t . k'_t)
+                        float u = 0.0f;
 #pragma unroll
-                            for (int i = 0; i < 16; ++i) u = fmaf(dsel[i], sc[i], u);
-                            u += __shfl_xor(u, 32);
-                            if (g == 0) cgb[(c & 1) * CT + 32 * s + l32] = gt * (1.0f - gt) * u;
-                        } else {
-#pragma unroll
-                            for (int i = 0; i < 16; ++i) sc[i] = fmaf(dsel[i], gt, sc[i]);
+                        for (int i = 0; i < 16; ++i) u = fmaf(dsel[i], sc[i], u);
+                        u += __shfl_xor(u, 32);
+                        if (g == 0) {
+                            if constexpr (R::GRAD) cgb[(c & 1) * CT + 32 * s + l32] = gt * (1.0f - gt) * u;
+                            // token t at (t % 16) NTB + t / 16: an owner lane reads its
+                            // tokens' values in one access
+                            const int t = 32 * s + l32;
+                            dgb[(c & 1) * CT + (t & 15) * NTB + (t >> 4)] = R::GRAD ? u : u + gt;
                         }
                     }
                     char* blk = Pb + pblk(tb, jb) * 1024;
 #pragma unroll
                     for (int a4 = 0; a4 < 4; ++a4) {
                         const int i0 = 4 * a4;
-                        const float m0 = (jb == s) ? dmd[i0] : dmo[i0], m1 = (jb == s) ? dmd[i0 + 1] : dmo[i0 + 1];
-                        const float m2 = (jb == s) ? dmd[i0 + 2] : dmo[i0 + 2], m3 = (jb == s) ? dmd[i0 + 3] : dmo[i0 + 3];
+                        // the diagonal block's mask without the diagonal (there dmd is 1)
+                        const float m0 = (jb == s) ? dmd[i0] - dsel[i0] : dmo[i0];
+                        const float m1 = (jb == s) ? dmd[i0 + 1] - dsel[i0 + 1] : dmo[i0 + 1];
+                        const float m2 = (jb == s) ? dmd[i0 + 2] - dsel[i0 + 2] : dmo[i0 + 2];
+                        const float m3 = (jb == s) ? dmd[i0 + 3] - dsel[i0 + 3] : dmo[i0 + 3];
                         const u32x2_t w2 = {pack2(sc[i0] * m0, sc[i0 + 1] * m1), pack2(sc[i0 + 2] * m2, sc[i0 + 3] * m3)};
                         *reinterpret_cast<u32x2_t*>(blk + ((l32 & 15) + 16 * a4) * 16 + 8 * g) = w2;
                     }
@@ -1082,6 +1095,20 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
                                                               Pb + Ly::SZ_P + (b * 64 + lane) * 16));
             }
 
+            // the fp32 diagonal of this lane's tokens 16 tb + l16, in one access
+            float dgv[Ly::DIAG32 ? NTB : 1];
+            if constexpr (Ly::DIAG32) {
+                const float* dgl = dgb + (c & 1) * CT + l16 * NTB;
+                if constexpr (NTB == 4) {
+                    const f32x4_t x = *reinterpret_cast<const f32x4_t*>(dgl);
+#pragma unroll
+                    for (int tb = 0; tb < NTB; ++tb) dgv[tb] = x[tb];
+                } else {
+#pragma unroll
+                    for (int tb = 0; tb < NTB; ++tb) dgv[tb] = dgl[tb];
+                }
+            }
+
             // ---- readout: O^T = S^T Q'^T, the state as a bf16 pair: hi = the
             // truncated upper half, lo = the remainder (exact in fp32) rounded
             f32x4_t oq[NTB] = {};
@@ -1126,11 +1153,21 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
                 float val[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) val[r] = fmaf(tdec[tb], oq[tb][r], o[r]);
+                float y[4] = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (Ly::DIAG32) {
+                    // + the diagonal term in fp32: the raw diagonal (plus the gate
+                    // for FWD and DV) times v'_t
+                    const u32x2_t yw = lds_u32x2(Vs, toff<SEGV>(t, OWC * w + 4 * qg));
+                    y[0] = bf_lo(yw[0]);
+                    y[1] = bf_hi(yw[0]);
+                    y[2] = bf_lo(yw[1]);
+                    y[3] = bf_hi(yw[1]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) val[r] = fmaf(dgv[tb], y[r], val[r]);
+                }
                 if constexpr (R::GRAD) {
                     // + c_t a (.) v'_t ; DA: column sums of c_t x_t (.) v'_t
                     const float ct = cgb[(c & 1) * CT + t];
-                    const u32x2_t yw = lds_u32x2(Vs, toff<SEGV>(t, OWC * w + 4 * qg));
-                    const float y[4] = {bf_lo(yw[0]), bf_hi(yw[0]), bf_lo(yw[1]), bf_hi(yw[1])};
                     float xv[4] = {0.f, 0.f, 0.f, 0.f};
                     if constexpr (R::DA) {
                         const u32x2_t xw = lds_u32x2(st + Ly::OFF_X, toff<SEGV>(t, OWC * w + 4 * qg));

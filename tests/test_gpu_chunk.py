@@ -132,6 +132,37 @@ def test_bf16_special_decays_and_short():
     run_bwd_case(inp, lam, 128)
 
 
+@pytest.mark.parametrize("dk,chunk", [(8, 128), (96, 64), (8, 32)])
+def test_bf16_single_short_memory_head(dk, chunk):
+    """One head of half-life 1 (lambda = 0.5) with a = 0: its output is led by
+    the diagonal term (q_t . k_t + sigmoid(0)) v_t, and with no long-memory
+    head in the tensor the metric's RMS does not hide that term's rounding. A
+    bf16 diagonal in the intra-tile scores scored 3.0e-2 on o and 3.2e-2 on dv
+    here; the kernels carry the diagonal in fp32."""
+    inp = I.chunk_inputs(1, 1, 438, dk, 192, "bf16", seed=6008, a_std=None, with_grad=True, dsf_std=0.05)
+    lam = np.array([0.5], np.float32)
+    run_fwd_case(inp, lam, chunk)
+    run_bwd_case(inp, lam, chunk)
+
+
+def test_bf16_zero_decay_is_the_diagonal_alone():
+    """With lambda = 0 every token sees only itself: o_t = (q_t . k_t +
+    sigmoid(z_t)) v_t, carried in fp32 with no bf16 score on the way. With
+    a = 0 (z = 0 exactly; a nonzero a enters z through bf16 operands of the
+    gate's matrix-core product) o matches the oracle to fp32 rounding."""
+    inp = I.chunk_inputs(1, 2, 300, 8, 192, "bf16", seed=6013, a_std=None, with_grad=True, dsf_std=0.05)
+    lam = np.array([0.0, 0.0], np.float32)
+    d = device_inputs(inp)
+    o, _ = Bd.sgla_chunk_fwd(d["q"], d["k"], d["v"], to_dev(lam), d["a"], chunk=128)
+    torch.cuda.synchronize()
+    units = _units(1, 2)
+    ref = oracle_fwd_units(inp, lam, units)
+    oh = to_host64(o)
+    assert_close(np.concatenate([gpu_unit(oh, n, h).ravel() for n, h in units]),
+                 np.concatenate([ref[u][0].ravel() for u in units]), 1e-5, "o (lambda = 0)", store="bf16")
+    run_bwd_case(inp, lam, 128)
+
+
 def test_bf16_narrow_dims():
     inp = I.chunk_inputs(1, 2, 140, 32, 64, "bf16", seed=95, a_std=0.2, s0_std=0.05,
                          with_grad=True, dsf_std=0.05)
