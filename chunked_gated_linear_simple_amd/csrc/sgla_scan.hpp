@@ -558,15 +558,18 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
             const char* qb = R::OUT ? reinterpret_cast<const char*>(p.q + rb * dkr) : nullptr;
             const char* kb = reinterpret_cast<const char*>(p.k + rb * dkr);
             const char* vb = reinterpret_cast<const char*>(p.v + rb * dvr);
-            // The forward scans read every tile once (the value slices of a
-            // unit at about the same time), so their tiles stream past the
-            // caches; the backward's roles read the same tiles at different
-            // times and keep the default policy.
+            // The forward scans read every tile once, so their tiles stream
+            // past the caches with the non-temporal hint, except the forward's
+            // q' and k': its value slices read those too, at slightly different
+            // times, and with the hint the second reader misses in L2. The
+            // backward's roles read the same tiles at different times and keep
+            // the default policy throughout.
             constexpr int POL = (!R::GRAD && !R::REV) ? POL_NT : 0;
+            constexpr int POLQK = (R::OUT && !R::NG) ? 0 : POL;
 #pragma unroll
             for (int m = 0; m < Ly::NLQ; ++m) {
-                if constexpr (R::OUT) dma16<POL>(qb, offq[m], st + 1024 * m);
-                dma16<POL>(kb, offq[m], st + Ly::OFF_K + 1024 * m);
+                if constexpr (R::OUT) dma16<POLQK>(qb, offq[m], st + 1024 * m);
+                dma16<POLQK>(kb, offq[m], st + Ly::OFF_K + 1024 * m);
             }
 #pragma unroll
             for (int m = 0; m < Ly::NLV; ++m) dma16<POL>(vb, offv[m], st + Ly::OFF_V + 1024 * m);
