@@ -69,6 +69,7 @@ namespace sgla {
 namespace scan {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -85,7 +86,6 @@ __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 
 __device__ __forceinline__ uint32_t pack2(float a, float b)
 {
     // round to nearest even, a in the low half
-    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     bf16x2_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
     return __builtin_bit_cast(uint32_t, v);
 }
@@ -109,6 +109,28 @@ __device__ __forceinline__ float silu_f(float x)
 {
     const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * x);
     return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// For each of four words holding a bf16 pair (low half first):
+// S_e = x_0 y_0 + x_1 y_1 and D_e = x_0 y_0 - x_1 y_1 (exact products, one fp32
+// sum). One block of VOP3 dot products with the negate modifier on the second
+// pair; a dot product's result needs three wait states before a VALU reads
+// it, which the trailing s_nop provides (the compiler cannot see inside the
+// block), and the outputs are early-clobber because the inputs are read after
+// the first write.
+__device__ __forceinline__ void dot2_sd4(const u32x4_t& x, const u32x4_t& y, float (&S)[4], float (&D)[4])
+{
+    asm("v_dot2_f32_bf16 %0, %8, %12, 0\n\t"
+        "v_dot2_f32_bf16 %1, %8, %12, 0 neg_hi:[0,1,0]\n\t"
+        "v_dot2_f32_bf16 %2, %9, %13, 0\n\t"
+        "v_dot2_f32_bf16 %3, %9, %13, 0 neg_hi:[0,1,0]\n\t"
+        "v_dot2_f32_bf16 %4, %10, %14, 0\n\t"
+        "v_dot2_f32_bf16 %5, %10, %14, 0 neg_hi:[0,1,0]\n\t"
+        "v_dot2_f32_bf16 %6, %11, %15, 0\n\t"
+        "v_dot2_f32_bf16 %7, %11, %15, 0 neg_hi:[0,1,0]\n\t"
+        "s_nop 2"
+        : "=&v"(S[0]), "=&v"(D[0]), "=&v"(S[1]), "=&v"(D[1]), "=&v"(S[2]), "=&v"(D[2]), "=&v"(S[3]), "=&v"(D[3])
+        : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(y[0]), "v"(y[1]), "v"(y[2]), "v"(y[3]));
 }
 
 __device__ __forceinline__ float sigmoid_f(float z)
@@ -269,7 +291,7 @@ constexpr int NG_SPIN_MAX = 1 << 20;
 //     4(l/16) + r of each 16-row block; A and B operands: row or column l%16,
 //     contraction index 8(l/16) + slot);
 //   * wave 6 ("loader") streams tiles into a 4-deep LDS ring and computes the
-//     gate sigmoid(z) of the tile two ahead;
+//     gate sigmoid(z) of the tile two ahead, in fp32 (lane = token);
 //   * wave 7 ("scorer") computes the decay-masked scores of the next tile and
 //     writes P^T in the owners' operand order (a 16-token x 32-key block is one
 //     1 KB fragment, 16 B per lane). P leaves out the diagonal: the scorer
@@ -351,19 +373,21 @@ struct LayW {
     static constexpr int OFF_CORR = OFF_P + 2 * SZ_P;       // update coefficients of B [2][CT]
     static constexpr int OFF_KEEP = OFF_CORR + 2 * CT * 4;  // masks of A, one word per token pair [2][CT/2]
     static constexpr int OFF_GT = OFF_KEEP + CT * 4;        // gate sigmoid(z) [2][CT]
-    static constexpr int OFF_CG = OFF_GT + 2 * CT * 4;      // gate-derivative factors [2][CT]
-    // The diagonal of the scores in fp32 [2][CT] (with the gate for FWD and
-    // DV): it stays out of the bf16 P, and the owners add it times v'_t.
+    // The raw diagonal of the scores in fp32 [2][CT]: it stays out of the
+    // bf16 P, and the owners add it (with the gate for FWD and DV) times v'_t.
     static constexpr bool DIAG32 = R::OUT && !R::NG;
-    static constexpr int OFF_DG = OFF_CG + (R::GRAD ? 2 * CT * 4 : 0);
+    static constexpr int OFF_DG = OFF_GT + 2 * CT * 4;
     static constexpr int OFF_A = OFF_DG + (DIAG32 ? 2 * CT * 4 : 0);  // a at the v' columns [DVS]
     static constexpr int OFF_SS = OFF_A + (R::GRAD ? DVS * 4 : 0);     // NG: owners' sums of o^2 [NOW_W][CT]
     static constexpr int OFF_INV = OFF_SS + (R::NG ? NOW_W * CT * 4 : 0);  // NG: 1 / rms per token [CT]
     // NG: sums ready, 1 / rms ready, tile and gate ready
     static constexpr int OFF_CNT = OFF_INV + (R::NG ? CT * 4 : 0);
     static constexpr int OFF_G = OFF_CNT + (R::NG ? 16 : 0);            // NG: 3 x [CT][96] gate values g
-    static constexpr int OFF_AQ = OFF_G + (R::NG ? 3 * SZ_V : 0);       // NG: a [DK] fp32
-    static constexpr int LDS = OFF_AQ + (R::NG ? DK * 4 : 0);
+    // the gate's channel weights as pairs (a_2j + a_2j+1, a_2j - a_2j+1) / 2,
+    // fp32, over the q'/k' channels [DK] (FWD, DV, NG) or the slice's x/v'
+    // channels [DVS] (DQ, DK)
+    static constexpr int OFF_AB = OFF_G + (R::NG ? 3 * SZ_V : 0);
+    static constexpr int LDS = OFF_AB + (R::OUT ? (R::GRAD ? DVS : DK) * 4 : 0);
     static constexpr int NLQ = SZ_Q / 1024;
     static constexpr int NLV = SZ_V / 1024;
     static constexpr int NLOAD = (R::OUT ? 2 : 1) * NLQ + (R::GRAD ? 2 : 1) * NLV;
@@ -491,45 +515,69 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
         for (int i = tid; i < DVS; i += NTHREADS_W)
             at[i] = (p.a != nullptr && n0 + i < dvr) ? p.a[(size_t)h * dvr + n0 + i] : 0.0f;
     }
-    if constexpr (R::NG) {
-        float* aq = reinterpret_cast<float*>(smem + Ly::OFF_AQ);
-        for (int i = tid; i < DK; i += NTHREADS_W) aq[i] = (p.a != nullptr && i < dkr) ? p.a[(size_t)h * dkr + i] : 0.0f;
+    if constexpr (R::OUT) {
+        constexpr int NAB = R::GRAD ? DVS : DK;
+        auto aval = [&](int i) -> float {
+            if (p.a == nullptr) return 0.0f;
+            if constexpr (R::GRAD) return n0 + i < dvr ? p.a[(size_t)h * dvr + n0 + i] : 0.0f;
+            else return i < dkr ? p.a[(size_t)h * dkr + i] : 0.0f;
+        };
+        float* ab = reinterpret_cast<float*>(smem + Ly::OFF_AB);
+        for (int i = tid; i < NAB; i += NTHREADS_W) {
+            const float a0 = aval(i & ~1), a1 = aval(i | 1);
+            ab[i] = 0.5f * ((i & 1) ? a0 - a1 : a0 + a1);
+        }
     }
     float* gtb = reinterpret_cast<float*>(smem + Ly::OFF_GT);
-    float* cgb = reinterpret_cast<float*>(smem + Ly::OFF_CG);
     float* dgb = reinterpret_cast<float*>(smem + Ly::OFF_DG);
-    // NG: sigmoid(z_t) of tile c on the VALU in fp32, lane = token, a in fp32.
-    // All row reads are issued first and four partial sums break the chain.
+    // sigmoid(z_t) of tile c, z_t = sum_i a_i x_{t,i} y_{t,i}, in fp32 with a in
+    // fp32 (bf16 operands for a and a (.) x would cost 2^-9 of each term,
+    // coherently over the channels, which shows in the gate terms of the
+    // gradients once |a| grows past ~1), by the loader's wave with lane =
+    // token: the q'/k' rows for FWD, DV and NG, the x/v' rows (the 96-wide
+    // slice) for DQ and DK. A channel pair (i, i+1) costs two bf16 dot
+    // products, S = x_i y_i + x_{i+1} y_{i+1} and D = x_i y_i - x_{i+1} y_{i+1}
+    // (exact products, one fp32 sum), and two fma:
+    // a_i x_i y_i + a_{i+1} x_{i+1} y_{i+1} = alpha S + beta D with alpha, beta
+    // = (a_i +- a_{i+1}) / 2 from the pair table. All row reads are issued
+    // first, and four partial sums break the chain.
+    constexpr int GSEG = R::GRAD ? SEGV : SEGK;
     auto gate_valu = [&](int c) {
         const char* st = smem + (c % Ly::NR) * Ly::SLOT;
-        const float* aq = reinterpret_cast<const float*>(smem + Ly::OFF_AQ);
+        const char* Xs = R::GRAD ? st + Ly::OFF_X : st;
+        const char* Ys = R::GRAD ? st + Ly::OFF_V : st + Ly::OFF_K;
+        const float* ab = reinterpret_cast<const float*>(smem + Ly::OFF_AB);
         if (lane < CT) {
-            u32x4_t qw[SEGK], kw[SEGK];
+            u32x4_t xw[GSEG], yw[GSEG];
 #pragma unroll
-            for (int sg = 0; sg < SEGK; ++sg) {
-                qw[sg] = *reinterpret_cast<const u32x4_t*>(st + toff<SEGK>(lane, 8 * sg));
-                kw[sg] = *reinterpret_cast<const u32x4_t*>(st + Ly::OFF_K + toff<SEGK>(lane, 8 * sg));
+            for (int sg = 0; sg < GSEG; ++sg) {
+                xw[sg] = *reinterpret_cast<const u32x4_t*>(Xs + toff<GSEG>(lane, 8 * sg));
+                yw[sg] = *reinterpret_cast<const u32x4_t*>(Ys + toff<GSEG>(lane, 8 * sg));
             }
             float zp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int sg = 0; sg < SEGK; ++sg) {
-                const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(aq + 8 * sg);
-                const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(aq + 8 * sg + 4);
+            for (int sg = 0; sg < GSEG; ++sg) {
+                const f32x4_t w0 = *reinterpret_cast<const f32x4_t*>(ab + 8 * sg);
+                const f32x4_t w1 = *reinterpret_cast<const f32x4_t*>(ab + 8 * sg + 4);
+                float S[4], D[4];
+                dot2_sd4(xw[sg], yw[sg], S, D);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float ae0 = (e < 2) ? a0[2 * e] : a1[2 * e - 4];
-                    const float ae1 = (e < 2) ? a0[2 * e + 1] : a1[2 * e - 3];
-                    zp[e] = fmaf(ae0 * bf_lo(qw[sg][e]), bf_lo(kw[sg][e]), zp[e]);
-                    zp[e] = fmaf(ae1 * bf_hi(qw[sg][e]), bf_hi(kw[sg][e]), zp[e]);
+                    const float al = (e < 2) ? w0[2 * e] : w1[2 * e - 4];
+                    const float be = (e < 2) ? w0[2 * e + 1] : w1[2 * e - 3];
+                    zp[e] = fmaf(al, S[e], zp[e]);
+                    zp[e] = fmaf(be, D[e], zp[e]);
                 }
             }
-            gtb[(c & 1) * CT + lane] = sigmoid_f((zp[0] + zp[1]) + (zp[2] + zp[3]));
+            // NG: token order (its scorer adds the gate); the others: token t at
+            // (t % 16) NTB + t / 16, read by the owners in one access
+            const int gi = R::NG ? lane : (lane & 15) * NTB + (lane >> 4);
+            gtb[(c & 1) * CT + gi] = sigmoid_f((zp[0] + zp[1]) + (zp[2] + zp[3]));
         }
     };
 
     if (wave == LOADER_W) {
         // ---------------------------------------------------------- loader
-        const int l32 = lane & 31, g = lane >> 5;
         uint32_t offq[Ly::NLQ], offv[Ly::NLV];
         auto offsets = [&](int cl) {
 #pragma unroll
@@ -601,64 +649,6 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
                 }
             }
         };
-        float dsel[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) dsel[i] = (l32 == acc_row(i, g)) ? 1.0f : 0.0f;
-        // The gate operands: q'/k' rows for FWD and DV, x/v' rows (the 96-wide
-        // slice) for DQ and DK.
-        constexpr int GW = R::GRAD ? DVS : DK;     // padded gate width
-        constexpr int GDB = GW / 32;
-        constexpr int GSEG = GW / 8;
-        const int gwr = R::GRAD ? dvr : dkr;       // real gate width (= row width of a)
-        bf16x8_t adiag[GDB][2];
-#pragma unroll
-        for (int db = 0; db < GDB; ++db)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const int j = l32 - 16 * hh - 8 * g;
-                const int dcol = 32 * db + l32;
-                const float ad = (p.a != nullptr && dcol < gwr) ? p.a[(size_t)h * gwr + dcol] : 0.0f;
-                u32x4_t w;
-#pragma unroll
-                for (int s2 = 0; s2 < 4; ++s2)
-                    w[s2] = pack2(j == 2 * s2 ? ad : 0.0f, j == 2 * s2 + 1 ? ad : 0.0f);
-                adiag[db][hh] = __builtin_bit_cast(bf16x8_t, w);
-            }
-        // sigmoid(z_t) of tile c: z_t = (Y (diag(a) X^T))[t][t] on the matrix cores
-        auto gate = [&](int c) {
-            const char* st = smem + (c % Ly::NR) * Ly::SLOT;
-            const char* Gb = R::GRAD ? st + Ly::OFF_X : st;           // X rows (B operand)
-            const char* Ga = R::GRAD ? st + Ly::OFF_V : st + Ly::OFF_K;  // Y rows (A operand)
-#pragma unroll
-            for (int s = 0; s < NKT; ++s) {
-                f32x16_t zt = {};
-#pragma unroll
-                for (int db = 0; db < GDB; ++db) {
-                    f32x16_t qa = {};
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        const bf16x8_t xf = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
-                                                                            Gb + toff<GSEG>(32 * s + l32, 32 * db + 16 * hh + 8 * g)));
-                        qa = mma(adiag[db][hh], xf, qa);
-                    }
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        u32x4_t bw;
-#pragma unroll
-                        for (int s2 = 0; s2 < 4; ++s2) bw[s2] = pack2(qa[8 * hh + 2 * s2], qa[8 * hh + 2 * s2 + 1]);
-                        const int e0 = 32 * db + 16 * hh + 4 * g;
-                        const bf16x8_t kz = frag(lds_u32x2(Ga, toff<GSEG>(32 * s + l32, e0)),
-                                                 lds_u32x2(Ga, toff<GSEG>(32 * s + l32, e0 + 8)));
-                        zt = mma(kz, __builtin_bit_cast(bf16x8_t, bw), zt);
-                    }
-                }
-                float z = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) z = fmaf(dsel[i], zt[i], z);
-                z += __shfl_xor(z, 32);
-                if (g == 0) gtb[(c & 1) * CT + 32 * s + l32] = sigmoid_f(z);
-            }
-        };
         if constexpr (R::NG) {
             // Three-deep ring. In iteration c the loader issues tile c+2,
             // waits for tile c+1 and forms its gate sigmoid(z) (cnt[2] = c+2
@@ -727,7 +717,7 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
                 wait_vm<0>();
             }
             fixup(0);
-            if constexpr (R::OUT) gate(0);
+            if constexpr (R::OUT) gate_valu(0);
             if (nch > 1) {
                 if (nch > 2) {
                     issue(2);
@@ -736,18 +726,22 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
                     wait_vm<0>();
                 }
                 fixup(1);
-                if constexpr (R::OUT) gate(1);
             }
         }
         lds_barrier();
         lds_barrier();
+        // Iteration c: issue tile c+3, form the gate of tile c+1 (the owners'
+        // tile of the next iteration; it arrived an iteration ago) while the
+        // loads fly, then wait for tile c+2.
         for (int c = 0; c < nch; ++c) {
             if (c + 3 < nch) issue(c + 3);
+            if constexpr (R::OUT) {
+                if (c + 1 < nch) gate_valu(c + 1);
+            }
             if (c + 2 < nch) {
                 if (c + 3 < nch) wait_vm<Ly::NLOAD>();
                 else wait_vm<0>();
                 fixup(c + 2);
-                if constexpr (R::OUT) gate(c + 2);
             }
             lds_barrier();
         }
@@ -782,7 +776,6 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
                 for (int kb = 0; kb < DK / 16; ++kb)
                     qf[kb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
                                                               Qs + toff<SEGK>(32 * s + l32, 16 * kb + 8 * g)));
-                const float gt = gtb[(c & 1) * CT + 32 * s + l32];
                 const int tb = 2 * s + (l32 >> 4);
 #pragma unroll
                 for (int jb = 0; jb <= s; ++jb) {
@@ -795,18 +788,17 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
                     }
                     if (jb == s) {
                         // the raw diagonal q'_t . k'_t, which P leaves out: the owners
-                        // add it in fp32 (with the gate for FWD and DV); for DQ and DK
-                        // also c_t = sigmoid'(z_t) (q'_t . k'_t)
+                        // add it in fp32 (with the gate for FWD and DV), and DQ and DK
+                        // form c_t = sigmoid'(z_t) (q'_t . k'_t) from it
                         float u = 0.0f;
 #pragma unroll
                         for (int i = 0; i < 16; ++i) u = fmaf(dsel[i], sc[i], u);
                         u += __shfl_xor(u, 32);
                         if (g == 0) {
-                            if constexpr (R::GRAD) cgb[(c & 1) * CT + 32 * s + l32] = gt * (1.0f - gt) * u;
                             // token t at (t % 16) NTB + t / 16: an owner lane reads its
                             // tokens' values in one access
                             const int t = 32 * s + l32;
-                            dgb[(c & 1) * CT + (t & 15) * NTB + (t >> 4)] = R::GRAD ? u : u + gt;
+                            dgb[(c & 1) * CT + (t & 15) * NTB + (t >> 4)] = u;
                         }
                     }
                     char* blk = Pb + pblk(tb, jb) * 1024;
@@ -1098,17 +1090,26 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
                                                               Pb + Ly::SZ_P + (b * 64 + lane) * 16));
             }
 
-            // the fp32 diagonal of this lane's tokens 16 tb + l16, in one access
-            float dgv[Ly::DIAG32 ? NTB : 1];
+            // the fp32 raw diagonal and the gate of this lane's tokens 16 tb + l16,
+            // one access each
+            float dgv[Ly::DIAG32 ? NTB : 1], gtv[Ly::DIAG32 ? NTB : 1];
             if constexpr (Ly::DIAG32) {
                 const float* dgl = dgb + (c & 1) * CT + l16 * NTB;
+                const float* gtl = gtb + (c & 1) * CT + l16 * NTB;
                 if constexpr (NTB == 4) {
                     const f32x4_t x = *reinterpret_cast<const f32x4_t*>(dgl);
+                    const f32x4_t y = *reinterpret_cast<const f32x4_t*>(gtl);
 #pragma unroll
-                    for (int tb = 0; tb < NTB; ++tb) dgv[tb] = x[tb];
+                    for (int tb = 0; tb < NTB; ++tb) {
+                        dgv[tb] = x[tb];
+                        gtv[tb] = y[tb];
+                    }
                 } else {
 #pragma unroll
-                    for (int tb = 0; tb < NTB; ++tb) dgv[tb] = dgl[tb];
+                    for (int tb = 0; tb < NTB; ++tb) {
+                        dgv[tb] = dgl[tb];
+                        gtv[tb] = gtl[tb];
+                    }
                 }
             }
 
@@ -1165,12 +1166,14 @@ __device__ __forceinline__ int body_wide(const Args& p, int unit, int slice, cha
                     y[1] = bf_hi(yw[0]);
                     y[2] = bf_lo(yw[1]);
                     y[3] = bf_hi(yw[1]);
+                    const float dgt = R::GRAD ? dgv[tb] : dgv[tb] + gtv[tb];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) val[r] = fmaf(dgv[tb], y[r], val[r]);
+                    for (int r = 0; r < 4; ++r) val[r] = fmaf(dgt, y[r], val[r]);
                 }
                 if constexpr (R::GRAD) {
-                    // + c_t a (.) v'_t ; DA: column sums of c_t x_t (.) v'_t
-                    const float ct = cgb[(c & 1) * CT + t];
+                    // + c_t a (.) v'_t with c_t = sigmoid'(z_t) (q'_t . k'_t); DA:
+                    // column sums of c_t x_t (.) v'_t
+                    const float ct = gtv[tb] * (1.0f - gtv[tb]) * dgv[tb];
                     float xv[4] = {0.f, 0.f, 0.f, 0.f};
                     if constexpr (R::DA) {
                         const u32x2_t xw = lds_u32x2(st + Ly::OFF_X, toff<SEGV>(t, OWC * w + 4 * qg));

@@ -32,11 +32,12 @@
  *   roundings in the SGLA_BF16 chunk kernels: the state enters the readout as a
  *   bf16 hi + lo pair (about 16 significant bits); the decayed values of the
  *   state update enter as the exact bf16 value plus a bf16-rounded correction;
- *   the intra-chunk scores enter the second product rounded to bf16; and the
- *   gate argument z = sum_i a_i x_i y_i is formed on the matrix cores from a
- *   rounded to bf16 and the products a_i x_i rounded to bf16 (a relative error
- *   of about 2^-9 per term, accumulated in fp32), so its absolute error grows
- *   with |a|. The decode step and the SGLA_F32 kernels use a in fp32.
+ *   and the intra-chunk scores below the diagonal enter the second product
+ *   rounded to bf16 (sgla_chunk_fwd_norm_gate: all of them as a bf16 hi + lo
+ *   pair), while the diagonal term (q_t . k_t + sigmoid(z_t)) v_t is applied
+ *   in fp32. The gate argument z_t = sum_i a_i q_{t,i} k_{t,i} is formed in
+ *   fp32 from a in fp32 and the exact products of the bf16 inputs, in every
+ *   kernel.
  * Layouts (row-major, last index fastest):
  *   dense:  q, k [B, H, T, d_k];  v, o [B, H, T, d_v];  N = B sequences.
  *   packed: with cu_seqlens != NULL: B must be 1, T is the total token count,

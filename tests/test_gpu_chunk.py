@@ -145,12 +145,14 @@ def test_bf16_single_short_memory_head(dk, chunk):
     run_bwd_case(inp, lam, chunk)
 
 
-def test_bf16_zero_decay_is_the_diagonal_alone():
+@pytest.mark.parametrize("a_std", [None, 2.0])
+def test_bf16_zero_decay_is_the_diagonal_alone(a_std):
     """With lambda = 0 every token sees only itself: o_t = (q_t . k_t +
-    sigmoid(z_t)) v_t, carried in fp32 with no bf16 score on the way. With
-    a = 0 (z = 0 exactly; a nonzero a enters z through bf16 operands of the
-    gate's matrix-core product) o matches the oracle to fp32 rounding."""
-    inp = I.chunk_inputs(1, 2, 300, 8, 192, "bf16", seed=6013, a_std=None, with_grad=True, dsf_std=0.05)
+    sigmoid(z_t)) v_t, carried in fp32 with no bf16 score on the way, and z_t
+    is formed in fp32 from a in fp32 and the exact products of the bf16
+    inputs. So o matches the oracle to fp32 rounding, with a = 0 and with a
+    large a alike (bf16 operands in the gate gave 1.1e-3 here)."""
+    inp = I.chunk_inputs(1, 2, 300, 8, 192, "bf16", seed=6013, a_std=a_std, with_grad=True, dsf_std=0.05)
     lam = np.array([0.0, 0.0], np.float32)
     d = device_inputs(inp)
     o, _ = Bd.sgla_chunk_fwd(d["q"], d["k"], d["v"], to_dev(lam), d["a"], chunk=128)
@@ -161,6 +163,25 @@ def test_bf16_zero_decay_is_the_diagonal_alone():
     assert_close(np.concatenate([gpu_unit(oh, n, h).ravel() for n, h in units]),
                  np.concatenate([ref[u][0].ravel() for u in units]), 1e-5, "o (lambda = 0)", store="bf16")
     run_bwd_case(inp, lam, 128)
+
+
+@pytest.mark.parametrize("B,T,d_k,d_v,lengths,s0_std,dsf_std,seed", [
+    (2, 311, 96, 56, None, 1.0, 0.05, 5506),
+    (1, 419, 72, 136, [129, 257, 0, 33], 5.0, 0.05, 6334),
+    (2, 240, 96, 136, None, 0.05, None, 5722),
+])
+def test_bf16_short_memory_head_large_a(B, T, d_k, d_v, lengths, s0_std, dsf_std, seed):
+    """One head of half-life 1 (lambda = 0.5) with a ~ N(0, 2^2): z_t spreads
+    over several units and the gate terms sigmoid'(z_t) (dO_t . v_t) of dq, dk
+    and da carry much of their RMS. With the gate argument formed from bf16(a)
+    and bf16(a (.) q) these configurations scored 2.5e-2 (dq), 2.8e-2 (dq)
+    and 2.4e-2 (dk); the kernels form it in fp32."""
+    cu = None if lengths is None else I.cu_from_lengths(lengths)
+    inp = I.chunk_inputs(B, 1, T, d_k, d_v, "bf16", seed=seed, a_std=2.0, s0_std=s0_std,
+                         n_seq=None if lengths is None else len(lengths), with_grad=True, dsf_std=dsf_std)
+    lam = np.array([0.5], np.float32)
+    run_fwd_case(inp, lam, 64, cu=cu)
+    run_bwd_case(inp, lam, 64, cu=cu)
 
 
 def test_bf16_narrow_dims():
