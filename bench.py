@@ -92,10 +92,24 @@ FWD_FLOPS_HT = 128 * (DK + DV) + 4 * DK * DV + 2 * DK + 2 * DV
 BWD_FLOPS_HT = 128 * (3 * DK + 2 * DV) + 10 * DK * DV + 8 * DK + 4 * DV
 
 
+def code_digest(sources):
+    """First 16 hex digits of sha256 over the code lines of the sources, in
+    order: each line up to any `//`, trailing blanks cut, empty lines dropped.
+    Comments can change without invalidating the committed counters; any
+    change to the code itself does."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sources:
+        for line in open(f, encoding="utf-8"):
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                h.update(code.encode("utf-8") + b"\n")
+    return h.hexdigest()[:16]
+
+
 def _profile_values(path, sources):
     """The key: value lines of a committed counter summary, or None when the
-    kernel sources have changed since its counters were taken."""
-    import hashlib
+    kernel code has changed since its counters were taken."""
     try:
         kv = {}
         for line in open(path):
@@ -103,10 +117,7 @@ def _profile_values(path, sources):
                 continue
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-        h = hashlib.sha256()
-        for f in sources:
-            h.update(open(f, "rb").read())
-        if h.hexdigest()[:16] != kv.get("sources_sha256"):
+        if code_digest(sources) != kv.get("sources_sha256"):
             return None
         return kv
     except OSError:

@@ -42,7 +42,7 @@
 //     tiles through ds_read_b64_tr_b16: within a 16-lane group, lanes 4s + q
 //     address token T0 + s at columns c0 + 4q (tr_read), and lane i receives
 //     column c0 + i of the four tokens T0..T0+3.
-//   * v_mfma_f32_32x32x16_bf16 (gate and scores): accumulator lane l holds
+//   * v_mfma_f32_32x32x16_bf16 (scores): accumulator lane l holds
 //     column l%32, rows 8(i/4) + 4(l/32) + i%4 in register i; an accumulator
 //     used as an operand of a contraction over its rows carries, for the
 //     16-wide step h, rows 16h + 8a + 4g + b in slot 4a + b (g = l/32).
@@ -291,14 +291,16 @@ constexpr int NG_SPIN_MAX = 1 << 20;
 //     4(l/16) + r of each 16-row block; A and B operands: row or column l%16,
 //     contraction index 8(l/16) + slot);
 //   * wave 6 ("loader") streams tiles into a 4-deep LDS ring and computes the
-//     gate sigmoid(z) of the tile two ahead, in fp32 (lane = token);
+//     gate sigmoid(z) of the next tile, in fp32 (lane = token), while the
+//     loads of the tile three ahead fly;
 //   * wave 7 ("scorer") computes the decay-masked scores of the next tile and
 //     writes P^T in the owners' operand order (a 16-token x 32-key block is one
 //     1 KB fragment, 16 B per lane). P leaves out the diagonal: the scorer
-//     passes the raw diagonal q'_t . k'_t to the owners in fp32 (plus the gate
-//     for FWD and DV), and for DQ and DK also c_t = sigmoid'(z_t) (q'_t . k'_t);
-//     the owners apply both in their epilogue. (A bf16 diagonal costs 2^-9 of
-//     the term that dominates a short-memory head's output.)
+//     passes the raw diagonal q'_t . k'_t to the owners in fp32. FWD and DV add
+//     (q'_t . k'_t + sigmoid(z_t)) v'_t in their epilogue; DQ and DK add
+//     (q'_t . k'_t) v'_t and apply c_t = sigmoid'(z_t) (q'_t . k'_t). (A bf16
+//     diagonal costs 2^-9 of the term that dominates a short-memory head's
+//     output.)
 // A tile's data is waited for by the loader two iterations before the owners
 // use it, so the gate and the scores of tile c+1 both run during iteration c.
 // The NG role (the epilogue applied before the store) differs: its ring is

@@ -30,12 +30,20 @@ def test_algorithmic_flops_per_head_token():
 
 def test_profile_values_follow_the_source_hash(tmp_path):
     src = tmp_path / "k.hip"
-    src.write_bytes(b"kernel source")
-    digest = hashlib.sha256(b"kernel source").hexdigest()[:16]
+    src.write_text("int x; // a comment\n\n    int y;   \n")
+    # the digest covers the code lines alone: "int x;" and "    int y;"
+    digest = hashlib.sha256(b"int x;\n    int y;\n").hexdigest()[:16]
+    assert bench.code_digest([str(src)]) == digest
     prof = tmp_path / "p.txt"
     prof.write_text(f"# comment: ignored\nx_executed_flops: 123\nsources_sha256: {digest}\n")
     assert bench._profile_values(str(prof), [str(src)])["x_executed_flops"] == "123"
-    src.write_bytes(b"kernel source, changed")
+    # comments and blank lines may change
+    src.write_text("// header\nint x; // another comment\n    int y;\n\n")
+    assert bench._profile_values(str(prof), [str(src)])["x_executed_flops"] == "123"
+    # code may not
+    src.write_text("int x;\n    int y = 1;\n")
+    assert bench._profile_values(str(prof), [str(src)]) is None
+    src.write_text("int x;\n  int y;\n")      # indentation is part of the code line
     assert bench._profile_values(str(prof), [str(src)]) is None
     assert bench._profile_values(str(tmp_path / "missing.txt"), [str(src)]) is None
 
