@@ -438,8 +438,8 @@ def bench_norm(args, B=8, T=2048, n_tiers=4, nsets=3):
 
 def bench_fused(args, B=8, T=2048, n_tiers=4, nsets=3):
     """The forward with the mixer epilogue applied before the store (one
-    cooperative launch; also timed with SGLA_FNG_PLAIN_LAUNCH) against the
-    two-launch pipeline sgla_chunk_fwd then sgla_head_norm_gate, on the same
+    launch) against the two-launch pipeline sgla_chunk_fwd then
+    sgla_head_norm_gate, on the same
     inputs: the headline workload plus the gate stream g [B, T, H, d_v], out
     [B, T, H, d_v], final state written; 3 input sets rotated (1.5 GB)."""
     import torch
@@ -457,10 +457,10 @@ def bench_fused(args, B=8, T=2048, n_tiers=4, nsets=3):
         sets.append((q, k, v, g, torch.empty_like(g), torch.empty_like(v),
                      torch.empty((B, H, DK, DV), dtype=torch.float32, device="cuda")))
 
-    def fused(i, plain=False):
+    def fused(i):
         q, k, v, g, out, _, sf = sets[i % nsets]
         Bd.sgla_chunk_fwd_norm_gate(q, k, v, lam, g, a=a, gamma=gm, n_tiers=n_tiers, eps=1e-6,
-                                    final_state=sf, out=out, chunk=128, exchange=x, plain_launch=plain)
+                                    final_state=sf, out=out, chunk=128, exchange=x)
 
     def pair(i):
         q, k, v, g, out, o, sf = sets[i % nsets]
@@ -468,7 +468,6 @@ def bench_fused(args, B=8, T=2048, n_tiers=4, nsets=3):
         Bd.sgla_head_norm_gate(o, g, gm, n_tiers, 1e-6, out=out)
 
     st = timed_stats(fused, args.steps, args.warmup)
-    ms_plain, _ = timed(lambda i: fused(i, True), args.steps, args.warmup)
     ms_pair, _ = timed(pair, args.steps, args.warmup)
     torch.cuda.synchronize()
     if int(torch.count_nonzero(x).item()) != 0:
@@ -476,7 +475,7 @@ def bench_fused(args, B=8, T=2048, n_tiers=4, nsets=3):
     toks = B * T
     # q, k, v, g read and out written (bf16), the final state written (fp32)
     bytes_ = B * H * T * (2 * DK + 3 * DV) * 2 + B * H * STATE_BYTES + n_tiers * DV * 4
-    return {"ms": st["mean"], "ms_median": st["median"], "ms_plain_launch": ms_plain,
+    return {"ms": st["mean"], "ms_median": st["median"],
             "ms_two_launches": ms_pair, "tokens": toks,
             "tok_s": toks / (st["mean"] * 1e-3), "tok_s_two_launches": toks / (ms_pair * 1e-3),
             "bytes": bytes_, "gbs": bytes_ / (st["mean"] * 1e-3) / 1e9}

@@ -23,7 +23,6 @@ SGLA_OK, SGLA_ERR_INVALID_ARG, SGLA_ERR_UNSUPPORTED, SGLA_ERR_WORKSPACE, SGLA_ER
 SGLA_F32, SGLA_BF16 = 0, 1
 # SGLA_FWD_NORM_GATE_EXCHANGE_BYTES of include/sgla.h
 FWD_NORM_GATE_EXCHANGE_BYTES = 2 * 1024 * 1024 + 256
-SGLA_FNG_PLAIN_LAUNCH = 1
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -203,12 +202,10 @@ def fwd_norm_gate_exchange(device) -> torch.Tensor:
 
 def sgla_chunk_fwd_norm_gate(q, k, v, lam, g, a=None, gamma=None, n_tiers: int = 1, eps: float = 1e-6,
                              init_state=None, final_state=None, out=None, o=None, cu_seqlens=None,
-                             chunk: int = 128, want_final: bool = False, want_o: bool = False, exchange=None,
-                             plain_launch: bool = False):
+                             chunk: int = 128, want_final: bool = False, want_o: bool = False, exchange=None):
     """Chunked forward with the mixer epilogue before the store. g and out are
     [B, T, H, d_v] (or [B, T, H * d_v]), token-major. Returns (out, o,
-    final_state); o and final_state are None unless passed or wanted.
-    plain_launch selects SGLA_FNG_PLAIN_LAUNCH (ordinary launches)."""
+    final_state); o and final_state are None unless passed or wanted."""
     dev = q.device
     B, H, T, d_k, d_v, n_seq = _geometry(q, v, cu_seqlens)
     _need(q, "q", device=dev)
@@ -236,8 +233,8 @@ def sgla_chunk_fwd_norm_gate(q, k, v, lam, g, a=None, gamma=None, n_tiers: int =
     _check(lib().sgla_chunk_fwd_norm_gate(_ptr(q), _ptr(k), _ptr(v), _ptr(lam), _ptr(a), _ptr(init_state),
                                           _ptr(final_state), _ptr(g), _ptr(gamma), _ptr(out), _ptr(o),
                                           _ptr(cu_seqlens), n_seq, B, H, T, d_k, d_v, int(chunk), int(n_tiers),
-                                          float(eps), _dtype_code(q), _ptr(exchange), exchange.numel(),
-                                          SGLA_FNG_PLAIN_LAUNCH if plain_launch else 0, _stream(dev)))
+                                          float(eps), _dtype_code(q), _ptr(exchange), exchange.numel(), 0,
+                                          _stream(dev)))
     return out, o, final_state
 
 

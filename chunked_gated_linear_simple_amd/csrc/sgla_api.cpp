@@ -273,8 +273,7 @@ sgla_status sgla_chunk_fwd_norm_gate(const void* q, const void* k, const void* v
     if (st != SGLA_OK) return st;
     if (dtype != SGLA_BF16)
         return fail(SGLA_ERR_UNSUPPORTED, "the fused forward and epilogue is bf16 only");
-    if ((flags & ~SGLA_FNG_PLAIN_LAUNCH) != 0u)
-        return fail(SGLA_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+    if (flags != 0u) return fail(SGLA_ERR_INVALID_ARG, "unknown flags 0x%x (none are defined)", flags);
     REQUIRE_PTR(g);
     REQUIRE_PTR(out);
     OPTIONAL_PTR(o);
@@ -310,8 +309,7 @@ sgla_status sgla_chunk_fwd_norm_gate(const void* q, const void* k, const void* v
     st = check_disjoint(wr, 4, rd, 8);
     if (st != SGLA_OK) return st;
     hipError_t e = sgla::launch_fwd_norm_gate_bf16(p, q, k, v, init_state, final_state, g, gamma, out, o, n_tiers,
-                                                   eps, exchange, (flags & SGLA_FNG_PLAIN_LAUNCH) == 0u,
-                                                   reinterpret_cast<hipStream_t>(hip_stream));
+                                                   eps, exchange, reinterpret_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return fail(SGLA_ERR_HIP, "chunk_fwd_norm_gate launch: %s", hipGetErrorString(e));
     return ok();
 }

@@ -24,26 +24,47 @@ __global__ __launch_bounds__(NTHREADS_W) void k_fwd(Args p)
 }
 
 // The forward with the mixer epilogue applied before the store: one group of
-// nsl workgroups (the value slices, on one XCD as in k_fwd) per (sequence,
-// head) unit, units unit_base + group. The slices of a unit exchange the
-// per-token sums of o^2 while they scan, so all workgroups of a group must be
-// resident at once: the grid is launched cooperatively, no larger than the
-// device holds, and more units take further launches. (A persistent grid
-// looping over units keeps every unit-invariant value of all roles live
+// nsl workgroups (the value slices) per (sequence, head) unit, units
+// unit_base + group. The slices of a unit exchange the per-token sums of o^2
+// while they scan, so they must run at the same time. A workgroup's group
+// and slice therefore come from a ticket it takes when it starts, from the
+// counter of its XCD index (blockIdx % 8): tickets nsl j .. nsl j + nsl - 1
+// of counter x form group 8 j + x, so a group's slices share an XCD (and
+// its L2 for q and k) as in k_fwd. The workgroups holding the tickets of a
+// group have all started except, per counter, at most the group of the
+// latest tickets, whose missing slices take the next tickets: every other
+// group can finish and free its compute unit, so the launch needs no
+// guarantee of residency (an ordinary launch, any grid size). The last
+// workgroup to finish clears the counters for the next call. (A persistent
+// grid looping over units keeps every unit-invariant value of all roles live
 // across the loop and spills.)
 template <int DK, int CT>
 __global__ __launch_bounds__(NTHREADS_W) void k_fwd_ng(Args p)
 {
     typedef LayW<WFwdNg<DK, CT>> Ly;
     __shared__ __attribute__((aligned(16))) char smem[Ly::LDS];
-    const int b = blockIdx.x;
-    const int slice = (b >> 3) % p.nsl;
-    const int grp = ((b >> 3) / p.nsl) * 8 + (b & 7);
-    const int unit = p.unit_base + grp;
-    if (unit >= p.n_units) return;
-    if (threadIdx.x < 4) reinterpret_cast<int*>(smem + Ly::OFF_CNT)[threadIdx.x] = 0;
+    int* cnt = reinterpret_cast<int*>(smem + Ly::OFF_CNT);
+    const int x = blockIdx.x & 7;
+    if (threadIdx.x < 3) cnt[threadIdx.x] = 0;
+    if (threadIdx.x == 0)
+        cnt[3] = __hip_atomic_fetch_add(p.xtick + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    body_wide<WFwdNg<DK, CT>>(p, unit, slice, smem, grp, 0);
+    const int tk = cnt[3];
+    // a counter that did not start at zero (an exchange buffer not
+    // zero-filled) is caught here, before it could address past the slots
+    const bool bad = tk < 0 || tk >= (int)(gridDim.x >> 3);
+    if (bad && threadIdx.x == 0) __hip_atomic_store(p.xerr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int slice = tk % p.nsl;
+    const int grp = (tk / p.nsl) * 8 + x;
+    const int unit = p.unit_base + grp;
+    if (!bad && unit < p.n_units) body_wide<WFwdNg<DK, CT>>(p, unit, slice, smem, grp, 0);
+    __syncthreads();
+    if (threadIdx.x == 0 &&
+        __hip_atomic_fetch_add(p.xdone, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1) {
+        // every workgroup of the grid has taken its ticket and finished
+        for (int i = 0; i < 8; ++i) __hip_atomic_store(p.xtick + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.xdone, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 // The state scan alone over each unit's run (no outputs), mapped as k_fwd.
@@ -70,41 +91,18 @@ hipError_t run_fwd(const Args& a, hipStream_t stream, bool out, int ct)
     return hipGetLastError();
 }
 
-// Groups per launch of the fused forward: a multiple of 8 (the XCD mapping),
-// with all their workgroups resident at once and at most NG_MAX_WG of them.
+// Launches of the fused forward: groups (a multiple of 8, the XCD mapping)
+// of at most NG_MAX_WG workgroups each, as the exchange has slots for, in
+// turn on the stream.
 template <int DK, int CT>
-static hipError_t ng_groups(int n_units, int nsl, int* groups)
+static hipError_t run_fwd_ng(Args a, hipStream_t stream)
 {
-    int dev = 0, ncu = 0, per_cu = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k_fwd_ng<DK, CT>),
-                                                         NTHREADS_W, 0);
-    if (e != hipSuccess) return e;
-    const int cap = min(ncu * per_cu, NG_MAX_WG) / nsl / 8 * 8;
-    if (cap <= 0) return hipErrorInvalidConfiguration;
-    *groups = min(cap, (n_units + 7) / 8 * 8);
-    return hipSuccess;
-}
-
-template <int DK, int CT>
-static hipError_t run_fwd_ng(Args a, bool cooperative, hipStream_t stream)
-{
-    int groups = 0;
-    hipError_t e = ng_groups<DK, CT>(a.n_units, a.nsl, &groups);
-    if (e != hipSuccess) return e;
+    const int groups = NG_MAX_WG / a.nsl / 8 * 8;
     for (int base = 0; base < a.n_units; base += groups) {
         a.unit_base = base;
         const int g = min(groups, (a.n_units - base + 7) / 8 * 8);
-        if (cooperative) {
-            void* args[] = {&a};
-            e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_fwd_ng<DK, CT>), dim3(g * a.nsl),
-                                           dim3(NTHREADS_W), args, 0, stream);
-        } else {
-            hipLaunchKernelGGL((k_fwd_ng<DK, CT>), dim3(g * a.nsl), dim3(NTHREADS_W), 0, stream, a);
-            e = hipGetLastError();
-        }
+        hipLaunchKernelGGL((k_fwd_ng<DK, CT>), dim3(g * a.nsl), dim3(NTHREADS_W), 0, stream, a);
+        const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -204,23 +202,25 @@ static_assert(SGLA_FWD_NORM_GATE_EXCHANGE_BYTES ==
 hipError_t launch_fwd_norm_gate_bf16(const ChunkProblem& p, const void* q, const void* k, const void* v,
                                      const float* init_state, float* final_state, const void* g,
                                      const float* gamma, void* out, void* o, int n_tiers, float eps,
-                                     void* exchange, bool cooperative, hipStream_t stream)
+                                     void* exchange, hipStream_t stream)
 {
     scan::Args a = fwd_args(p, q, k, v, init_state, final_state, o);
     a.ng_g = reinterpret_cast<const uint16_t*>(g);
     a.ng_gamma = gamma;
     a.ng_out = reinterpret_cast<uint16_t*>(out);
     a.xerr = reinterpret_cast<int*>(exchange);
+    a.xtick = a.xerr + scan::NG_XTICK;
+    a.xdone = a.xerr + scan::NG_XDONE;
     a.xch = reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(exchange) + scan::NG_XHEAD);
     a.per_tier = p.H / n_tiers;
     a.inv_dv = 1.0f / (float)p.d_v;
     a.eps = eps;
     const bool t32 = bf16_tile(p.chunk) == 32;
     if (p.d_k <= 32)
-        return t32 ? scan::run_fwd_ng<32, 32>(a, cooperative, stream) : scan::run_fwd_ng<32, 64>(a, cooperative, stream);
+        return t32 ? scan::run_fwd_ng<32, 32>(a, stream) : scan::run_fwd_ng<32, 64>(a, stream);
     if (p.d_k <= 64)
-        return t32 ? scan::run_fwd_ng<64, 32>(a, cooperative, stream) : scan::run_fwd_ng<64, 64>(a, cooperative, stream);
-    return t32 ? scan::run_fwd_ng<96, 32>(a, cooperative, stream) : scan::run_fwd_ng<96, 64>(a, cooperative, stream);
+        return t32 ? scan::run_fwd_ng<64, 32>(a, stream) : scan::run_fwd_ng<64, 64>(a, stream);
+    return t32 ? scan::run_fwd_ng<96, 32>(a, stream) : scan::run_fwd_ng<96, 64>(a, stream);
 }
 
 // bf16 forward with d_k <= 96 (padded to 32, 64 or 96) and any d_v (96-column slices).

@@ -48,12 +48,11 @@ hipError_t launch_fwd_bf16(const ChunkProblem& p, const void* q, const void* k, 
                            hipStream_t stream);
 
 // bf16 forward with the mixer epilogue applied before the store (sgla_fwd.hip);
-// exchange holds SGLA_FWD_NORM_GATE_EXCHANGE_BYTES, zero-filled; cooperative:
-// cooperative launches (else ordinary ones of the same grids).
+// exchange holds SGLA_FWD_NORM_GATE_EXCHANGE_BYTES, zero-filled.
 hipError_t launch_fwd_norm_gate_bf16(const ChunkProblem& p, const void* q, const void* k, const void* v,
                                      const float* init_state, float* final_state, const void* g,
                                      const float* gamma, void* out, void* o, int n_tiers, float eps,
-                                     void* exchange, bool cooperative, hipStream_t stream);
+                                     void* exchange, hipStream_t stream);
 
 // bf16 forward of dense sequences cut into nseg >= 2 segments of seg_len
 // tokens (sgla_fwd.hip); ws_loc and ws_in hold [n_seq][nseg][H][d_k][d_v] fp32.

@@ -264,16 +264,20 @@ struct Args {
     uint16_t* ng_out;
     unsigned long long* xch;
     int* xerr;               // set to 1 when an exchange wait gives up
+    int* xtick;              // [8] tickets taken per XCD index (blockIdx % 8)
+    int* xdone;              // workgroups finished
     int per_tier, unit_base;
     float inv_dv, eps;
 };
 
 // Exchange slots per slice of a group (a ring over its tiles), the most
-// workgroups of one fused grid, and the exchange buffer's header (its first
-// int is the error flag).
+// workgroups of one fused grid, and the exchange buffer's header: int 0 is
+// the error flag, ints NG_XTICK .. NG_XTICK+7 the tickets per XCD index and
+// int NG_XDONE the count of finished workgroups.
 constexpr int NG_XR = 4;
 constexpr int NG_MAX_WG = 1024;
 constexpr int NG_XHEAD = 256;
+constexpr int NG_XTICK = 16, NG_XDONE = 32;
 // Upper bound of the polls of one exchange wait (each after a short sleep)
 // before the wait gives up: the tile's output is NaN, and the workgroup's
 // later waits give up at once.

@@ -148,12 +148,6 @@ sgla_status sgla_chunk_fwd(const void* q, const void* k, const void* v,
 #define SGLA_FWD_NORM_GATE_EXCHANGE_BYTES ((size_t)2 * 1024 * 1024 + 256)
 
 /*
- * Flag of sgla_chunk_fwd_norm_gate: an ordinary kernel launch instead of a
- * cooperative one (see there).
- */
-#define SGLA_FNG_PLAIN_LAUNCH 1u
-
-/*
  * Chunked forward with the mixer epilogue applied to each output tile before
  * it is stored: sgla_chunk_fwd followed by sgla_head_norm_gate in one kernel,
  * so that o need not go to memory and back. Laplace 3B post, "Challenge 1:
@@ -180,27 +174,25 @@ sgla_status sgla_chunk_fwd(const void* q, const void* k, const void* v,
  * exchange: device buffer of SGLA_FWD_NORM_GATE_EXCHANGE_BYTES that must be
  *           zero-filled before its first use. The two 96-column workgroups of
  *           a (sequence, head) with d_v > 96 pass each other their per-token
- *           sums of o^2 through it; a call that completes leaves it
- *           zero-filled again. Calls that may run at the same time need
- *           distinct buffers. The workgroups are launched cooperatively (all
- *           resident at once); when the (sequence, head) units need more
- *           workgroups than the device holds, the call makes several such
- *           launches in turn on the stream. Should an exchange never arrive,
- *           the wait gives up after a bounded number of polls: the affected
- *           outputs are NaN and the buffer's first int is set to 1 (zero-fill
- *           it again before the next call).
- * flags:    0, or SGLA_FNG_PLAIN_LAUNCH: ordinary launches of the same grids
- *           (sized to what the device holds), which skip the cooperative
- *           launch's own cost (about 14 us per call on MI355X). Residency then
- *           rests on the device running nothing else meanwhile; should other
- *           work hold compute units for longer than the bounded wait, the
- *           outputs concerned are NaN and the flag above is set.
+ *           sums of o^2 through it, and every workgroup takes a ticket from
+ *           counters in it when it starts; consecutive tickets make up a
+ *           (sequence, head), so the two partners have always both started,
+ *           and ordinary launches suffice with no assumption about residency.
+ *           A call that completes leaves the buffer zero-filled again. Calls
+ *           that may run at the same time need distinct buffers. Units beyond
+ *           512 (sequence, head) pairs take further launches in turn on the
+ *           stream. Should an exchange never arrive (other work holding the
+ *           device longer than a bounded number of polls), or the buffer not
+ *           have been zero-filled, the affected outputs are NaN or not
+ *           written and the buffer's first int is set to 1 (zero-fill it
+ *           again before the next call).
+ * flags:    0 (no flags are defined).
  * Errors: as sgla_chunk_fwd; SGLA_ERR_UNSUPPORTED for SGLA_F32 (compose
  * sgla_chunk_fwd and sgla_head_norm_gate) or H * d_v above 2^24;
  * SGLA_ERR_INVALID_ARG for n_tiers
- * not dividing H, a bad eps, or overlapping buffers; SGLA_ERR_WORKSPACE for a
+ * not dividing H, a bad eps, nonzero flags, or overlapping buffers; SGLA_ERR_WORKSPACE for a
  * NULL, misaligned or short exchange buffer; SGLA_ERR_HIP for a launch
- * failure, including a device that cannot hold the cooperative grid.
+ * failure.
  */
 sgla_status sgla_chunk_fwd_norm_gate(const void* q, const void* k, const void* v,
                                      const float* lambda, const float* a,

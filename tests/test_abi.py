@@ -160,6 +160,7 @@ FNG_BAD = [
     ("packed with B=2", dict(cu=P["cu"], n_seq=3), B.SGLA_ERR_INVALID_ARG),
     ("H * d_v above 2^24", dict(H=1 << 18, T=1, B=1, tiers=1), B.SGLA_ERR_UNSUPPORTED),
     ("unknown flag", dict(fl=2), B.SGLA_ERR_INVALID_ARG),
+    ("no flags are defined", dict(fl=1), B.SGLA_ERR_INVALID_ARG),
 ]
 
 

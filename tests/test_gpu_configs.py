@@ -189,9 +189,9 @@ def test_varlen_full():
 
 
 def test_laplace_fwd_norm_gate_full():
-    """sgla_chunk_fwd_norm_gate at B=8, T=2048 (one cooperative launch of 256
-    workgroups), the launch the bench times: every unit's out rows and final
-    state against the oracle."""
+    """sgla_chunk_fwd_norm_gate at B=8, T=2048 (one launch of 256 workgroups),
+    the launch the bench times: every unit's out rows and final state against
+    the oracle."""
     tiers, eps = 4, 1e-6
     inp = I.chunk_inputs(8, H, 2048, DK, DV, "bf16", seed=6, a_std=0.1)
     gi = I.norm_inputs(6, 8, H, 2048, DV, tiers, "bf16")

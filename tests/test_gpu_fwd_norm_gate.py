@@ -11,7 +11,7 @@ single rounding of the scores alone scores about 2.4e-2 on the metric on
 these inputs. So o (when asked for) and the final state are checked against
 the oracle too. Also checked: the exchange buffer is zero-filled again after
 every call and its error flag is clear; out may be g itself; more (sequence,
-head) units than one cooperative launch holds.
+head) units than one launch has exchange slots for.
 """
 import numpy as np
 import pytest
@@ -127,9 +127,11 @@ def test_fused_packed():
 
 
 def test_fused_several_launches():
-    """320 (sequence, head) units: more pairs of workgroups than the device
-    holds at once, so the call makes several cooperative launches."""
-    B, H, T, dk, dv, tiers = 20, 16, 70, 96, 192, 4
+    """640 (sequence, head) units: 1,280 workgroups, five times what the
+    device holds at once, so the slice pairs form from tickets as
+    workgroups start; and more units than one launch's 512 exchange slots,
+    so the call makes two launches."""
+    B, H, T, dk, dv, tiers = 40, 16, 70, 96, 192, 4
     inp = I.chunk_inputs(B, H, T, dk, dv, "bf16", seed=172, a_std=0.1)
     gi = _gate_inputs(172, B, H, T, dv, tiers)
     lam = schedule32(H, 1.0, 2048.0)
@@ -139,7 +141,8 @@ def test_fused_several_launches():
                                             a=d["a"], gamma=to_dev(gi["gamma"]), n_tiers=tiers, eps=EPS,
                                             exchange=x)
     _check_exchange(x)
-    units = [(0, 0), (0, 15), (7, 9), (8, 0), (15, 3), (19, 15), (19, 0), (12, 12)]
+    # units 0..511 run in the first launch, 512..639 (n >= 32) in the second
+    units = [(0, 0), (0, 15), (7, 9), (8, 0), (15, 3), (19, 15), (31, 15), (32, 0), (35, 7), (39, 0), (39, 15)]
     ref = _ref_out(inp, lam, gi, tiers, units)
     oh = to_host64(out)
     assert np.isfinite(oh).all()
@@ -196,10 +199,12 @@ def test_fused_a_null_equals_zero_a():
                  TOL["bf16"], "out (a=NULL)", store="bf16")
 
 
-@pytest.mark.parametrize("B,T", [(2, 300), (20, 70)], ids=["one_launch", "several_launches"])
-def test_fused_plain_launch_equals_cooperative(B, T):
-    """SGLA_FNG_PLAIN_LAUNCH runs the same grids with ordinary launches: the
-    same bits as the cooperative launches, and the exchange left zero-filled."""
+@pytest.mark.parametrize("B,T", [(2, 300), (40, 70)], ids=["one_launch", "several_launches"])
+def test_fused_repeat_is_bitwise(B, T):
+    """Two calls give the same bits, whichever workgroup's ticket pairs it
+    with which (sequence, head), and each leaves the exchange (its ticket
+    counters included) zero-filled: a second call that found the counters
+    where the first left them would pair slices of different units."""
     H, dk, dv, tiers = 16, 96, 192, 4
     inp = I.chunk_inputs(B, H, T, dk, dv, "bf16", seed=175, a_std=0.1, s0_std=0.02)
     gi = _gate_inputs(175, B, H, T, dv, tiers)
@@ -209,6 +214,37 @@ def test_fused_plain_launch_equals_cooperative(B, T):
     x = torch.zeros(Bd.FWD_NORM_GATE_EXCHANGE_BYTES, dtype=torch.uint8, device="cuda")
     out0, _, S0f = Bd.sgla_chunk_fwd_norm_gate(*args, exchange=x, **kw)
     _check_exchange(x)
-    out1, _, S1f = Bd.sgla_chunk_fwd_norm_gate(*args, exchange=x, plain_launch=True, **kw)
+    out1, _, S1f = Bd.sgla_chunk_fwd_norm_gate(*args, exchange=x, **kw)
     _check_exchange(x)
     assert torch.equal(out0, out1) and torch.equal(S0f, S1f)
+
+
+def test_fused_flags_an_exchange_not_zero_filled():
+    """A ticket counter that does not start at zero (ints 16..23 of the
+    exchange buffer's header count the tickets per XCD index) is caught
+    before it can address past the exchange slots: those workgroups skip
+    their units and set the error flag, the others finish, and the counters
+    are cleared. Zero-filled again, the buffer serves a correct call."""
+    B, H, T, dk, dv, tiers = 2, 4, 130, 96, 192, 2
+    inp = I.chunk_inputs(B, H, T, dk, dv, "bf16", seed=176, a_std=0.1)
+    gi = _gate_inputs(176, B, H, T, dv, tiers)
+    lam = schedule32(H, 1.0, 2048.0)
+    d = device_inputs(inp)
+    args = (d["q"], d["k"], d["v"], to_dev(lam), to_dev(gi["g"], "bf16"))
+    kw = dict(a=d["a"], gamma=to_dev(gi["gamma"]), n_tiers=tiers, eps=EPS)
+    x = torch.zeros(Bd.FWD_NORM_GATE_EXCHANGE_BYTES, dtype=torch.uint8, device="cuda")
+    x.view(torch.int32)[16] = 1000
+    Bd.sgla_chunk_fwd_norm_gate(*args, exchange=x, **kw)
+    torch.cuda.synchronize()
+    xi = x.view(torch.int32)
+    assert int(xi[0].item()) == 1, "the error flag is not set"
+    assert int(torch.count_nonzero(xi[1:]).item()) == 0, "the counters are not cleared"
+    x.zero_()
+    out, _, _ = Bd.sgla_chunk_fwd_norm_gate(*args, exchange=x, **kw)
+    _check_exchange(x)
+    units = [(n, h) for n in range(B) for h in range(H)]
+    ref = _ref_out(inp, lam, gi, tiers, units)
+    oh = to_host64(out)
+    assert_close(np.concatenate([_out_unit(oh, n, h).ravel() for n, h in units]),
+                 np.concatenate([ref[u].ravel() for u in units]), TOL["bf16"], "out (after the error)",
+                 store="bf16")
