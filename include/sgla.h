@@ -179,9 +179,10 @@ sgla_status sgla_chunk_fwd(const void* q, const void* k, const void* v,
  *           (sequence, head), so the two partners have always both started,
  *           and ordinary launches suffice with no assumption about residency.
  *           A call that completes leaves the buffer zero-filled again. Calls
- *           that may run at the same time need distinct buffers. Units beyond
- *           512 (sequence, head) pairs take further launches in turn on the
- *           stream. Should an exchange never arrive (other work holding the
+ *           that may run at the same time need distinct buffers. One launch
+ *           has exchange slots for 1,024 workgroups (512 (sequence, head)
+ *           units with d_v > 96, 1,024 otherwise); more units take further
+ *           launches in turn on the stream. Should an exchange never arrive (other work holding the
  *           device longer than a bounded number of polls), or the buffer not
  *           have been zero-filled, the affected outputs are NaN or not
  *           written and the buffer's first int is set to 1 (zero-fill it
