@@ -1,6 +1,7 @@
 """GPU parity against the fp64 oracle over seeded random configurations of the
 entry points beside the chunk forward and backward: the segmented forward and
-backward (segment counts, ragged lengths, widths, decays 0 and 1), the decode
+backward (segment counts, ragged lengths, widths, decays 0 and 1, a absent,
+moderate or large), the decode
 step (pool size, slot tables, both head shapes, several steps), the conv
 prologue forward and gradients (width, dense or packed with empty and short
 sequences, bias and state on or off) with its decode step, and the mixer
@@ -46,7 +47,7 @@ def _seg_cases(n=12):
         out.append(dict(id=i, B=int(rng.integers(1, 3)), H=H, T=int(rng.integers(1, 1000)),
                         G=int(rng.integers(1, 13)),
                         d_k=int(rng.choice([8, 32, 48, 96])), d_v=int(rng.choice([8, 64, 104, 192])),
-                        a_std=None if rng.integers(0, 3) == 0 else 0.3,
+                        a_std=[None, 0.3, 2.0][int(rng.integers(0, 3))],
                         s0_std=None if rng.integers(0, 2) == 0 else 0.05,
                         dsf_std=None if rng.integers(0, 2) == 0 else 0.05, lam=_lam(rng, H)))
     return out
