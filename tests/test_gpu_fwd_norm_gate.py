@@ -248,3 +248,41 @@ def test_fused_flags_an_exchange_not_zero_filled():
     assert_close(np.concatenate([_out_unit(oh, n, h).ravel() for n, h in units]),
                  np.concatenate([ref[u].ravel() for u in units]), TOL["bf16"], "out (after the error)",
                  store="bf16")
+
+
+def test_fused_two_streams_at_once():
+    """Two fused calls running at the same time on two streams, each with its
+    own exchange buffer: 2 x 1,280 workgroups compete for the compute units,
+    so neither grid is resident at once and the workgroups of the two
+    launches interleave. The ticket pairing needs no residency, so both
+    finish, bit for bit equal to the same calls made one after the other,
+    with both exchange buffers zero-filled and no error flag."""
+    B, H, T, dk, dv, tiers = 40, 16, 70, 96, 192, 4
+    lam = to_dev(schedule32(H, 1.0, 2048.0))
+    calls = []
+    for seed in (177, 178):
+        inp = I.chunk_inputs(B, H, T, dk, dv, "bf16", seed=seed, a_std=0.1)
+        gi = _gate_inputs(seed, B, H, T, dv, tiers)
+        d = device_inputs(inp)
+        calls.append((d, to_dev(gi["g"], "bf16"), to_dev(gi["gamma"])))
+    xs = [torch.zeros(Bd.FWD_NORM_GATE_EXCHANGE_BYTES, dtype=torch.uint8, device="cuda") for _ in calls]
+
+    def run(i, out):
+        d, g, gm = calls[i]
+        Bd.sgla_chunk_fwd_norm_gate(d["q"], d["k"], d["v"], lam, g, a=d["a"], gamma=gm, n_tiers=tiers, eps=EPS,
+                                    out=out, exchange=xs[i])
+
+    want = [torch.empty_like(c[1]) for c in calls]
+    for i in range(2):
+        run(i, want[i])
+    torch.cuda.synchronize()
+    got = [torch.empty_like(c[1]) for c in calls]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for i, s in enumerate(streams):
+        with torch.cuda.stream(s):
+            run(i, got[i])
+    torch.cuda.synchronize()
+    for i in range(2):
+        _check_exchange(xs[i])
+        assert torch.equal(got[i], want[i]), f"call {i}"
