@@ -126,12 +126,15 @@ def test_fused_packed():
                  np.concatenate([fw[u][1].ravel() for u in units]), TOL["bf16"], "final_states (packed)")
 
 
-def test_fused_several_launches():
-    """640 (sequence, head) units: 1,280 workgroups, five times what the
-    device holds at once, so the slice pairs form from tickets as
-    workgroups start; and more units than one launch's 512 exchange slots,
-    so the call makes two launches."""
-    B, H, T, dk, dv, tiers = 40, 16, 70, 96, 192, 4
+@pytest.mark.parametrize("B,T,dv,per_launch", [(40, 70, 192, 512), (70, 40, 96, 1024)],
+                         ids=["two_slices", "one_slice"])
+def test_fused_several_launches(B, T, dv, per_launch):
+    """More (sequence, head) units than one launch's 1,024 exchange slots
+    hold, so the call makes two launches: 640 units of two value slices (512
+    a launch, 1,280 workgroups in all, five times what the device holds at
+    once, the slice pairs forming from tickets as workgroups start), and
+    1,120 units of one slice (1,024 a launch)."""
+    H, dk, tiers = 16, 96, 4
     inp = I.chunk_inputs(B, H, T, dk, dv, "bf16", seed=172, a_std=0.1)
     gi = _gate_inputs(172, B, H, T, dv, tiers)
     lam = schedule32(H, 1.0, 2048.0)
@@ -141,8 +144,10 @@ def test_fused_several_launches():
                                             a=d["a"], gamma=to_dev(gi["gamma"]), n_tiers=tiers, eps=EPS,
                                             exchange=x)
     _check_exchange(x)
-    # units 0..511 run in the first launch, 512..639 (n >= 32) in the second
-    units = [(0, 0), (0, 15), (7, 9), (8, 0), (15, 3), (19, 15), (31, 15), (32, 0), (35, 7), (39, 0), (39, 15)]
+    # units n H + h below per_launch run in the first launch, the rest in the second
+    first = per_launch // H
+    units = [(0, 0), (0, 15), (7, 9), (8, 0), (15, 3), (first - 1, 15), (first, 0), (first + 3, 7),
+             (B - 1, 0), (B - 1, 15)]
     ref = _ref_out(inp, lam, gi, tiers, units)
     oh = to_host64(out)
     assert np.isfinite(oh).all()
