@@ -478,9 +478,9 @@ sgla_status sgla_decode_step(const void* q, const void* k, const void* v, const 
     if (slot == nullptr && P < N)
         return fail(SGLA_ERR_INVALID_ARG, "without slot, the pool needs P >= N (P=%d N=%d)", P, N);
     if ((double)N * H > 2.0e9) return fail(SGLA_ERR_INVALID_ARG, "N*H too large");
-    if (!((d_k == 96 && d_v == 192) || (d_k == 16 && d_v == 32)))
-        return fail(SGLA_ERR_UNSUPPORTED, "decode supports (d_k, d_v) = (96, 192) or (16, 32), got (%d, %d)",
-                    d_k, d_v);
+    if (d_k < 4 || d_k > 96 || d_k % 4 != 0 || d_v < 4 || d_v > 192 || d_v % 4 != 0)
+        return fail(SGLA_ERR_UNSUPPORTED,
+                    "decode needs d_k in 4..96 and d_v in 4..192, multiples of 4 (got %d, %d)", d_k, d_v);
     {
         const size_t es = (dtype == SGLA_BF16) ? 2 : 4;
         const size_t nqk = (size_t)N * H * d_k * es, nvo = (size_t)N * H * d_v * es;

@@ -11,7 +11,9 @@
 // bytes in and out per sequence-head, 0.5 flop/byte), so the kernel is built
 // for HBM bandwidth: one workgroup per (sequence, head); thread (rg, cg) owns
 // four adjacent state columns (one 16-byte vector) in rows rg, rg+RG, ... (12
-// row groups of 8 rows for a 96 x 192 state, 576 threads); all
+// row groups of 8 rows for a 96 x 192 state, 576 threads; other head widths
+// run in the thread layout of the next larger width, the unused rows and
+// column groups masked); all
 // of its state loads are issued before any use; loads and stores are
 // non-temporal (the pool is far larger than the caches and is not re-read
 // within a step); the readout reduction over rows is per-thread partial sums
@@ -44,20 +46,26 @@ __device__ __forceinline__ float sigmoid_dec(float z)
     return e / (1.0f + e);
 }
 
-// DK x DV state per unit; CG = DV/4 column groups; RG row groups.
-template <typename E, int DK, int DV, int RG>
+// A dk x dv state per unit, dk <= DK and dv <= DV (EXACT: equal); CG = DV/4
+// column groups; RG row groups. Column groups at or past dv / 4 and rows at or
+// past dk do nothing.
+template <typename E, int DK, int DV, int RG, bool EXACT>
 __global__ __launch_bounds__((DV / 4) * RG) void k_decode(const E* __restrict__ q, const E* __restrict__ k,
                                                            const E* __restrict__ v,
                                                            const float* __restrict__ lambda,
                                                            const float* __restrict__ a,
                                                            float* __restrict__ state,
                                                            const int32_t* __restrict__ slot,
-                                                           E* __restrict__ o, int N, int P, int H)
+                                                           E* __restrict__ o, int N, int P, int H, int dk_rt,
+                                                           int dv_rt)
 {
     constexpr int CG = DV / 4;
     constexpr int NT = CG * RG;
     constexpr int RPT = (DK + RG - 1) / RG;  // rows per thread
     static_assert(DV % 4 == 0, "DV");
+    const int dk = EXACT ? DK : dk_rt;
+    const int dv = EXACT ? DV : dv_rt;
+    const int cgn = EXACT ? CG : dv / 4;       // column groups in use (dv is a multiple of 4)
 
     __shared__ float qs[DK], ks[DK];
     __shared__ float zsh;
@@ -67,27 +75,28 @@ __global__ __launch_bounds__((DV / 4) * RG) void k_decode(const E* __restrict__ 
     const int n = unit / H, h = unit - (unit / H) * H;
     const int tid = threadIdx.x;
     const int cg = tid % CG, rg = tid / CG;
+    const bool col = EXACT || cg < cgn;
 
     int page = (slot != nullptr) ? slot[n] : n;
     const bool valid = page >= 0 && page < P;
 
-    const size_t qk_base = (size_t)unit * DK;
-    const size_t v_base = (size_t)unit * DV;
+    const size_t qk_base = (size_t)unit * dk;
+    const size_t v_base = (size_t)unit * dv;
     if (!valid) {
-        for (int c = tid; c < DV; c += NT) st_f(o, v_base + c, __builtin_nanf(""));
+        for (int c = tid; c < dv; c += NT) st_f(o, v_base + c, __builtin_nanf(""));
         return;
     }
-    f32x4* S = reinterpret_cast<f32x4*>(state + ((size_t)page * H + h) * (size_t)DK * DV);
+    f32x4* S = reinterpret_cast<f32x4*>(state + ((size_t)page * H + h) * (size_t)dk * dv);
 
     // issue the state loads first (the bandwidth-critical part)
     f32x4 s[RPT];
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
         const int d = rg + RG * m;
-        if (d < DK) s[m] = __builtin_nontemporal_load(&S[(size_t)d * CG + cg]);
+        if (d < dk && col) s[m] = __builtin_nontemporal_load(&S[(size_t)d * cgn + cg]);
     }
 
-    for (int d = tid; d < DK; d += NT) {
+    for (int d = tid; d < dk; d += NT) {
         qs[d] = ld_f(q, qk_base + d);
         ks[d] = ld_f(k, qk_base + d);
     }
@@ -95,31 +104,33 @@ __global__ __launch_bounds__((DV / 4) * RG) void k_decode(const E* __restrict__ 
     if (tid < 64) {
         float z = 0.0f;
         if (a != nullptr)
-            for (int d = tid; d < DK; d += 64) z += a[(size_t)h * DK + d] * qs[d] * ks[d];
+            for (int d = tid; d < dk; d += 64) z += a[(size_t)h * dk + d] * qs[d] * ks[d];
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
         if (tid == 0) zsh = z;
     }
 
     const float lam = lambda[h];
-    f32x4 vv;
-    vv.x = ld_f(v, v_base + 4 * cg + 0);
-    vv.y = ld_f(v, v_base + 4 * cg + 1);
-    vv.z = ld_f(v, v_base + 4 * cg + 2);
-    vv.w = ld_f(v, v_base + 4 * cg + 3);
+    f32x4 vv = {0.f, 0.f, 0.f, 0.f};
+    if (col) {
+        vv.x = ld_f(v, v_base + 4 * cg + 0);
+        vv.y = ld_f(v, v_base + 4 * cg + 1);
+        vv.z = ld_f(v, v_base + 4 * cg + 2);
+        vv.w = ld_f(v, v_base + 4 * cg + 3);
+    }
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
         const int d = rg + RG * m;
-        if (d < DK) {
+        if (d < dk && col) {
             const float kd = ks[d], qd = qs[d];
             f32x4 x = s[m];
             x.x = lam * x.x + kd * vv.x;
             x.y = lam * x.y + kd * vv.y;
             x.z = lam * x.z + kd * vv.z;
             x.w = lam * x.w + kd * vv.w;
-            __builtin_nontemporal_store(x, &S[(size_t)d * CG + cg]);
+            __builtin_nontemporal_store(x, &S[(size_t)d * cgn + cg]);
             acc.x += x.x * qd;
             acc.y += x.y * qd;
             acc.z += x.z * qd;
@@ -128,7 +139,7 @@ __global__ __launch_bounds__((DV / 4) * RG) void k_decode(const E* __restrict__ 
     }
     red[rg][cg] = acc;
     __syncthreads();
-    if (rg == 0) {
+    if (rg == 0 && col) {
         f32x4 r = red[0][cg];
 #pragma unroll
         for (int j = 1; j < RG; ++j) {
@@ -146,17 +157,44 @@ __global__ __launch_bounds__((DV / 4) * RG) void k_decode(const E* __restrict__ 
     }
 }
 
-template <typename E, int DK, int DV, int RG>
+template <typename E, int DK, int DV, int RG, bool EXACT>
 hipError_t run_decode(const void* q, const void* k, const void* v, const float* lambda,
                       const float* a, float* state, const int32_t* slot, void* o, int N, int P,
-                      int H, hipStream_t stream)
+                      int H, int d_k, int d_v, hipStream_t stream)
 {
     const int units = N * H;
-    hipLaunchKernelGGL((k_decode<E, DK, DV, RG>), dim3(units), dim3((DV / 4) * RG), 0, stream,
+    hipLaunchKernelGGL((k_decode<E, DK, DV, RG, EXACT>), dim3(units), dim3((DV / 4) * RG), 0, stream,
                        reinterpret_cast<const E*>(q), reinterpret_cast<const E*>(k),
                        reinterpret_cast<const E*>(v), lambda, a, state, slot,
-                       reinterpret_cast<E*>(o), N, P, H);
+                       reinterpret_cast<E*>(o), N, P, H, d_k, d_v);
     return hipGetLastError();
+}
+
+// Other widths: the thread layout of the next larger width, eight rows a row group.
+template <typename E, int DK>
+hipError_t run_decode_dk(const void* q, const void* k, const void* v, const float* lambda, const float* a,
+                         float* state, const int32_t* slot, void* o, int N, int P, int H, int d_k, int d_v,
+                         hipStream_t stream)
+{
+    if (d_v <= 64)
+        return run_decode<E, DK, 64, DK / 8, false>(q, k, v, lambda, a, state, slot, o, N, P, H, d_k, d_v, stream);
+    if (d_v <= 128)
+        return run_decode<E, DK, 128, DK / 8, false>(q, k, v, lambda, a, state, slot, o, N, P, H, d_k, d_v, stream);
+    return run_decode<E, DK, 192, DK / 8, false>(q, k, v, lambda, a, state, slot, o, N, P, H, d_k, d_v, stream);
+}
+
+template <typename E>
+hipError_t run_decode_any(const void* q, const void* k, const void* v, const float* lambda, const float* a,
+                          float* state, const int32_t* slot, void* o, int N, int P, int H, int d_k, int d_v,
+                          hipStream_t stream)
+{
+    if (d_k == 96 && d_v == 192)
+        return run_decode<E, 96, 192, 12, true>(q, k, v, lambda, a, state, slot, o, N, P, H, d_k, d_v, stream);
+    if (d_k == 16 && d_v == 32)
+        return run_decode<E, 16, 32, 8, true>(q, k, v, lambda, a, state, slot, o, N, P, H, d_k, d_v, stream);
+    if (d_k <= 32) return run_decode_dk<E, 32>(q, k, v, lambda, a, state, slot, o, N, P, H, d_k, d_v, stream);
+    if (d_k <= 64) return run_decode_dk<E, 64>(q, k, v, lambda, a, state, slot, o, N, P, H, d_k, d_v, stream);
+    return run_decode_dk<E, 96>(q, k, v, lambda, a, state, slot, o, N, P, H, d_k, d_v, stream);
 }
 
 }  // namespace
@@ -166,13 +204,9 @@ hipError_t launch_decode_step(int bf16, const void* q, const void* k, const void
                               const int32_t* slot, void* o, int N, int P, int H, int d_k, int d_v,
                               hipStream_t stream)
 {
-    if (d_k == 96 && d_v == 192) {
-        if (bf16) return run_decode<u16, 96, 192, 12>(q, k, v, lambda, a, state, slot, o, N, P, H, stream);
-        return run_decode<float, 96, 192, 12>(q, k, v, lambda, a, state, slot, o, N, P, H, stream);
-    }
-    // d_k == 16 && d_v == 32 (checked by the caller)
-    if (bf16) return run_decode<u16, 16, 32, 8>(q, k, v, lambda, a, state, slot, o, N, P, H, stream);
-    return run_decode<float, 16, 32, 8>(q, k, v, lambda, a, state, slot, o, N, P, H, stream);
+    // 4 <= d_k <= 96 and 4 <= d_v <= 192, multiples of 4 (checked by the caller)
+    if (bf16) return run_decode_any<u16>(q, k, v, lambda, a, state, slot, o, N, P, H, d_k, d_v, stream);
+    return run_decode_any<float>(q, k, v, lambda, a, state, slot, o, N, P, H, d_k, d_v, stream);
 }
 
 }  // namespace sgla

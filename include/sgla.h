@@ -396,7 +396,8 @@ sgla_status sgla_chunk_bwd_noalloc(const void* q, const void* k, const void* v, 
  * slot:    [N] int32 page index of each sequence, or NULL (sequence n uses
  *          page n, and then P >= N is required). Entries must be distinct;
  *          an entry outside [0, P) skips that sequence and writes NaN to its o.
- * Supported: d_k = 96, d_v = 192 or d_k = 16, d_v = 32, either dtype.
+ * Supported: d_k from 4 to 96 and d_v from 4 to 192, multiples of 4, either
+ * dtype (every head shape the chunk entry points take).
  * The output of one sequence does not depend on N or on the other sequences.
  * state and o must be disjoint from each other and from q, k, v, lambda, a
  * and slot (SGLA_ERR_INVALID_ARG otherwise).

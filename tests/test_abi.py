@@ -298,7 +298,11 @@ DEC_BAD = [
     ("N zero", dict(N=0), B.SGLA_ERR_INVALID_ARG),
     ("pool too small", dict(Pg=4), B.SGLA_ERR_INVALID_ARG),
     ("slot misaligned", dict(slot=P["slot"] + 4), B.SGLA_ERR_INVALID_ARG),
-    ("dims", dict(d_k=64, d_v=64), B.SGLA_ERR_UNSUPPORTED),
+    ("d_k too big", dict(d_k=100), B.SGLA_ERR_UNSUPPORTED),
+    ("d_v too big", dict(d_v=196), B.SGLA_ERR_UNSUPPORTED),
+    ("d_k not a multiple of 4", dict(d_k=66), B.SGLA_ERR_UNSUPPORTED),
+    ("d_v not a multiple of 4", dict(d_v=130), B.SGLA_ERR_UNSUPPORTED),
+    ("d_k zero", dict(d_k=0), B.SGLA_ERR_UNSUPPORTED),
     ("dtype", dict(dt=3), B.SGLA_ERR_INVALID_ARG),
     ("o inside state", dict(o=P["state"] + 4096), B.SGLA_ERR_INVALID_ARG),
     ("state aliases q", dict(state=P["q"]), B.SGLA_ERR_INVALID_ARG),

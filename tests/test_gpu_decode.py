@@ -1,5 +1,6 @@
-"""GPU parity of sgla_decode_step against the fp64 oracle, its page
-indirection, batch invariance and its agreement with the chunked forward."""
+"""GPU parity of sgla_decode_step against the fp64 oracle (the two tuned
+head shapes and a spread of others), its page indirection, batch invariance
+and its agreement with the chunked forward."""
 import numpy as np
 import pytest
 import torch
@@ -26,7 +27,11 @@ def _oracle_steps(qs, ks, vs, lam, a, S, units, dtype):
 
 
 @pytest.mark.parametrize("dtype,dk,dv", [("bf16", 96, 192), ("f32", 96, 192), ("f32", 16, 32),
-                                         ("bf16", 16, 32)])
+                                         ("bf16", 16, 32),
+                                         # other head widths: the next larger thread layout, masked
+                                         ("bf16", 64, 128), ("f32", 32, 64), ("bf16", 72, 136), ("bf16", 8, 8),
+                                         ("f32", 96, 96), ("bf16", 48, 192), ("f32", 4, 4), ("bf16", 40, 20),
+                                         ("f32", 92, 188)])
 def test_decode_steps_vs_oracle(dtype, dk, dv):
     N, H, steps = 19, 16 if dk == 96 else 2, 6
     lam = schedule32(H, 1.0, 2048.0)

@@ -69,7 +69,7 @@ def _dec_cases(n=8):
     rng = np.random.default_rng(RNG_SEED + 1)
     out = []
     for i in range(n):
-        dk, dv = ((96, 192), (16, 32))[int(rng.integers(0, 2))]
+        dk, dv = ((96, 192), (16, 32), (64, 128), (36, 100))[int(rng.integers(0, 4))]
         N = int(rng.integers(1, 41))
         H = int(rng.integers(1, 5))
         P = N + int(rng.integers(0, 9))
