@@ -386,7 +386,8 @@ struct LayW {
     static constexpr int OFF_A = OFF_DG + (DIAG32 ? 2 * CT * 4 : 0);  // a at the v' columns [DVS]
     static constexpr int OFF_SS = OFF_A + (R::GRAD ? DVS * 4 : 0);     // NG: owners' sums of o^2 [NOW_W][CT]
     static constexpr int OFF_INV = OFF_SS + (R::NG ? NOW_W * CT * 4 : 0);  // NG: 1 / rms per token [CT]
-    // NG: sums ready, 1 / rms ready, tile and gate ready
+    // NG: sums ready, 1 / rms ready, tile and gate ready, and the
+    // workgroup's ticket (set by k_fwd_ng before the body runs)
     static constexpr int OFF_CNT = OFF_INV + (R::NG ? CT * 4 : 0);
     static constexpr int OFF_G = OFF_CNT + (R::NG ? 16 : 0);            // NG: 3 x [CT][96] gate values g
     // the gate's channel weights as pairs (a_2j + a_2j+1, a_2j - a_2j+1) / 2,
