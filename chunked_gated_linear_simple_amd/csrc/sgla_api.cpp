@@ -79,9 +79,9 @@ sgla_status check_chunk(const void* q, const void* k, const void* v, const float
         if (chunk != 32 && chunk != 64 && chunk != 128)
             return fail(SGLA_ERR_UNSUPPORTED, "bf16 chunk must be 32, 64 or 128, got %d", chunk);
     } else {
-        if (d_k > 32 || d_v > 32 || d_k % 4 != 0 || d_v % 4 != 0)
+        if (d_k > 96 || d_v > 192 || d_k % 4 != 0 || d_v % 4 != 0)
             return fail(SGLA_ERR_UNSUPPORTED,
-                        "f32 needs d_k <= 32 and d_v <= 32, multiples of 4 (got %d, %d)", d_k, d_v);
+                        "f32 needs d_k <= 96 and d_v <= 192, multiples of 4 (got %d, %d)", d_k, d_v);
         if (chunk != 32 && chunk != 64 && chunk != 128)
             return fail(SGLA_ERR_UNSUPPORTED, "f32 chunk must be 32, 64 or 128, got %d", chunk);
     }

@@ -739,6 +739,23 @@ template <int C> using F32Fwd = Role<float, 32, 32, C, AUG_FWD, false>;
 template <int C> using F32Dq = Role<float, 32, 32, C, AUG_GRAD, false>;
 template <int C> using F32Dk = Role<float, 32, 32, C, AUG_GRAD, true>;
 template <int C> using F32Dv = Role<float, 32, 32, C, AUG_FWD, true>;
+// Wider fp32 heads (contraction widths up to 96 in the forward and the dv
+// scan, up to 192 in the dq and dk scans, whose contraction runs over d_v):
+// 32-token tiles, which keep every such role's operands within the LDS;
+// widths are rounded up to the next of 32, 64, 96 (192) and padded.
+template <int DK> using F32FwdW = Role<float, DK, 32, 32, AUG_FWD, false>;
+template <int DV> using F32DqW = Role<float, DV, 32, 32, AUG_GRAD, false>;
+template <int DV> using F32DkW = Role<float, DV, 32, 32, AUG_GRAD, true>;
+template <int DK> using F32DvW = Role<float, DK, 32, 32, AUG_FWD, true>;
+
+template <int DV>
+hipError_t run_bwd_wide(const ChunkProblem& p, const RoleArgs& aq, const RoleArgs& ak, const RoleArgs& av,
+                        float* da, hipStream_t stream)
+{
+    if (p.d_k <= 32) return run_bwd<F32DqW<DV>, F32DkW<DV>, F32DvW<32>>(p, aq, ak, av, da, stream);
+    if (p.d_k <= 64) return run_bwd<F32DqW<DV>, F32DkW<DV>, F32DvW<64>>(p, aq, ak, av, da, stream);
+    return run_bwd<F32DqW<DV>, F32DkW<DV>, F32DvW<96>>(p, aq, ak, av, da, stream);
+}
 
 }  // namespace
 
@@ -750,6 +767,8 @@ hipError_t launch_chunk_fwd(const ChunkProblem& p, const void* q, const void* k,
     if (p.bf16) return launch_fwd_bf16(p, q, k, v, init_state, final_state, o, stream);
     RoleArgs ra{q, k, v, nullptr, o, init_state, final_state, nullptr, p.d_k, p.d_v, 0, 0, 0};
     const int nsl = (p.d_v + 31) / 32;
+    if (p.d_k > 64) return run_fwd<F32FwdW<96>>(p, ra, nsl, stream);
+    if (p.d_k > 32) return run_fwd<F32FwdW<64>>(p, ra, nsl, stream);
     if (p.chunk == 32) return run_fwd<F32Fwd<32>>(p, ra, nsl, stream);
     if (p.chunk == 128) return run_fwd<F32Fwd<128>>(p, ra, nsl, stream);
     return run_fwd<F32Fwd<64>>(p, ra, nsl, stream);
@@ -769,6 +788,10 @@ hipError_t launch_chunk_bwd(const ChunkProblem& p, const void* q, const void* k,
     RoleArgs ak{v, dO, q, k, dk, d_final_state, nullptr, nullptr, p.d_v, p.d_k, 1, 0, 1};
     // dv: reverse scan of G ([d_k][d_v]); q'=k, k'=q, v'=dO; final G -> d_init_state
     RoleArgs av{k, q, dO, nullptr, dv, d_final_state, d_init_state, nullptr, p.d_k, p.d_v, 0, 1, 1};
+    if (p.d_v > 96) return run_bwd_wide<192>(p, aq, ak, av, da, stream);
+    if (p.d_v > 64) return run_bwd_wide<96>(p, aq, ak, av, da, stream);
+    if (p.d_v > 32) return run_bwd_wide<64>(p, aq, ak, av, da, stream);
+    if (p.d_k > 32) return run_bwd_wide<32>(p, aq, ak, av, da, stream);
     if (p.chunk == 32) return run_bwd<F32Dq<32>, F32Dk<32>, F32Dv<32>>(p, aq, ak, av, da, stream);
     if (p.chunk == 128) return run_bwd<F32Dq<128>, F32Dk<128>, F32Dv<128>>(p, aq, ak, av, da, stream);
     return run_bwd<F32Dq<64>, F32Dk<64>, F32Dv<64>>(p, aq, ak, av, da, stream);

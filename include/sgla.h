@@ -57,7 +57,7 @@
  *   outputs, including da (fixed-order reductions, no float atomics).
  * Supported shapes:
  *   SGLA_BF16: d_k <= 96, d_v <= 192, both multiples of 8; chunk 32, 64 or 128.
- *   SGLA_F32:  d_k <= 32, d_v <= 32, both multiples of 4; chunk 32, 64 or 128.
+ *   SGLA_F32:  d_k <= 96, d_v <= 192, both multiples of 4; chunk 32, 64 or 128.
  *   Anything else returns SGLA_ERR_UNSUPPORTED.
  */
 #ifndef SGLA_H
@@ -127,7 +127,8 @@ sgla_status sgla_decay_schedule(int H, double t_min, double t_max, float* lambda
  * n_seq:       number of sequences when cu_seqlens != NULL; ignored otherwise.
  * chunk:       chunk length C of the chunk form (32, 64 or 128). It sets the
  *              length of the tiles the kernels scan with, which changes only
- *              the rounding: SGLA_F32 tiles by C tokens; SGLA_BF16 tiles the
+ *              the rounding: SGLA_F32 tiles by C tokens for heads of at most
+ *              32 x 32 and by 32 tokens for wider ones; SGLA_BF16 tiles the
  *              forward (and the dv scan of sgla_chunk_bwd) by 32 tokens for
  *              C = 32 and by 64 for C = 64 or 128, because a 128-token tile of
  *              q, k and v does not fit the four-deep LDS ring the bf16

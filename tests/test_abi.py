@@ -102,7 +102,9 @@ FWD_BAD = [
     ("d_k not mult 8", dict(d_k=20), B.SGLA_ERR_UNSUPPORTED),
     ("chunk 16", dict(chunk=16), B.SGLA_ERR_UNSUPPORTED),
     ("chunk 256", dict(chunk=256), B.SGLA_ERR_UNSUPPORTED),
-    ("f32 d_k 96", dict(dt=B.SGLA_F32), B.SGLA_ERR_UNSUPPORTED),
+    ("f32 d_k 100", dict(dt=B.SGLA_F32, d_k=100), B.SGLA_ERR_UNSUPPORTED),
+    ("f32 d_v 196", dict(dt=B.SGLA_F32, d_v=196), B.SGLA_ERR_UNSUPPORTED),
+    ("f32 d_k not mult 4", dict(dt=B.SGLA_F32, d_k=66), B.SGLA_ERR_UNSUPPORTED),
     ("f32 chunk 96", dict(dt=B.SGLA_F32, d_k=16, d_v=32, chunk=96), B.SGLA_ERR_UNSUPPORTED),
     ("o aliases q", dict(o=P["q"]), B.SGLA_ERR_INVALID_ARG),
     ("o overlaps v", dict(o=P["v"] + 1024), B.SGLA_ERR_INVALID_ARG),

@@ -106,6 +106,29 @@ def test_varlen_f32_fwd_bwd():
     run_bwd_case(inp, lam, 64, cu=cu)
 
 
+@pytest.mark.parametrize("dk,dv,T,chunk", [(64, 64, 150, 64), (96, 192, 130, 128), (48, 72, 97, 32),
+                                           (96, 96, 70, 64), (8, 132, 65, 64), (36, 20, 33, 128)])
+def test_f32_wide_heads(dk, dv, T, chunk):
+    """fp32 heads wider than 32 x 32 (32-token tiles, widths padded to the
+    next of 32, 64, 96 or 192), forward and backward at the fp32 bound, with
+    decays 0 and 1 among the heads."""
+    inp = I.chunk_inputs(2, 3, T, dk, dv, "f32", seed=700 + dk + dv, a_std=0.4, s0_std=0.1,
+                         with_grad=True, dsf_std=0.1)
+    lam = np.array([0.0, 0.93, 1.0], np.float32)
+    run_fwd_case(inp, lam, chunk)
+    run_bwd_case(inp, lam, chunk)
+
+
+def test_f32_wide_heads_packed():
+    L = [70, 0, 1, 33]
+    cu = I.cu_from_lengths(L)
+    inp = I.chunk_inputs(1, 2, int(cu[-1]), 96, 160, "f32", seed=710, a_std=0.3, s0_std=0.1,
+                         n_seq=len(L), with_grad=True, dsf_std=0.1)
+    lam = np.array([0.8, 0.999], np.float32)
+    run_fwd_case(inp, lam, 64, cu=cu)
+    run_bwd_case(inp, lam, 64, cu=cu)
+
+
 # ------------------------------------------------------------------ bf16 (2e-2 gate)
 
 
