@@ -59,10 +59,12 @@ __global__ __launch_bounds__(NTHREADS_W) void k_fwd_ng(Args p)
     const int unit = p.unit_base + grp;
     if (!bad && unit < p.n_units) body_wide<WFwdNg<DK, CT>>(p, unit, slice, smem, grp, 0);
     __syncthreads();
-    // (acquire-release: each workgroup's ticket increment happens before the
-    // last workgroup's reset of the counters)
+    // (A workgroup issues this increment only after its ticket increment has
+    // returned and its unit has run, so the reset below follows every ticket
+    // increment in time. An acquire-release increment would say so formally,
+    // but it costs an L2 writeback and invalidation at every workgroup's end.)
     if (threadIdx.x == 0 &&
-        __hip_atomic_fetch_add(p.xdone, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1) {
+        __hip_atomic_fetch_add(p.xdone, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1) {
         // every workgroup of the grid has taken its ticket and finished
         for (int i = 0; i < 8; ++i) __hip_atomic_store(p.xtick + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(p.xdone, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
