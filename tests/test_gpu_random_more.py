@@ -1,5 +1,7 @@
-"""GPU parity against the fp64 oracle over seeded random configurations of the
-entry points beside the chunk forward and backward: the segmented forward and
+"""GPU parity against the fp64 oracle over seeded random configurations: fp32
+chunk forward and backward with heads up to 96 x 192 (widths, dense or
+packed, chunk lengths, decays 0 and 1, a up to N(0, 2^2)); and the entry
+points beside the chunk forward and backward: the segmented forward and
 backward (segment counts, ragged lengths, widths, decays 0 and 1, a absent,
 moderate or large), the decode
 step (pool size, slot tables, both head shapes, several steps), the conv
@@ -25,6 +27,7 @@ from tests.test_gpu_norm import EPS
 from tests.test_gpu_norm import _dev as norm_dev
 from tests.test_gpu_norm import _ref as norm_ref
 from tests.test_gpu_norm_bwd import _case as norm_bwd_case
+from tests.test_gpu_chunk import run_bwd_case, run_fwd_case
 from tests.test_gpu_segmented import run_segmented_bwd_case, run_segmented_case
 
 pytestmark = pytest.mark.gpu
@@ -37,6 +40,38 @@ def _lam(rng, H):
     if rng.integers(0, 3) == 0:
         lam[int(rng.integers(0, H))] = float(rng.choice([0.0, 1.0, 0.5]))
     return lam
+
+
+def _f32_cases(n=24):
+    rng = np.random.default_rng(RNG_SEED + 20)
+    out = []
+    for i in range(n):
+        H = int(rng.integers(1, 4))
+        packed = bool(rng.integers(0, 2))
+        L = None
+        if packed:
+            L = [int(x) for x in rng.choice([0, 1, 2, 31, 33, 64, 65, 100], size=int(rng.integers(2, 5)))]
+            if sum(L) == 0:
+                L[0] = 5
+        out.append(dict(id=i, H=H, L=L, B=1 if packed else int(rng.integers(1, 3)),
+                        T=sum(L) if packed else int(rng.integers(1, 160)),
+                        d_k=4 * int(rng.integers(1, 25)), d_v=4 * int(rng.integers(1, 49)),
+                        chunk=int(rng.choice([32, 64, 128])), a_std=[None, 0.3, 2.0][int(rng.integers(0, 3))],
+                        lam=_lam(rng, H)))
+    return out
+
+
+F32 = _f32_cases()
+
+
+@pytest.mark.parametrize("c", F32, ids=[f"{c['id']}-H{c['H']}-" + (f"packed{c['L']}" if c["L"] else f"B{c['B']}T{c['T']}")
+                                        + f"-dk{c['d_k']}dv{c['d_v']}-C{c['chunk']}" for c in F32])
+def test_random_f32_fwd_bwd(c):
+    cu = None if c["L"] is None else I.cu_from_lengths(c["L"])
+    inp = I.chunk_inputs(c["B"], c["H"], c["T"], c["d_k"], c["d_v"], "f32", seed=6500 + c["id"], a_std=c["a_std"],
+                         s0_std=0.1, n_seq=None if cu is None else len(c["L"]), with_grad=True, dsf_std=0.1)
+    run_fwd_case(inp, c["lam"], c["chunk"], cu=cu)
+    run_bwd_case(inp, c["lam"], c["chunk"], cu=cu)
 
 
 def _seg_cases(n=12):
