@@ -127,8 +127,9 @@ sgla_status sgla_decay_schedule(int H, double t_min, double t_max, float* lambda
  * n_seq:       number of sequences when cu_seqlens != NULL; ignored otherwise.
  * chunk:       chunk length C of the chunk form (32, 64 or 128). It sets the
  *              length of the tiles the kernels scan with, which changes only
- *              the rounding: SGLA_F32 tiles by C tokens for heads of at most
- *              32 x 32 and by 32 tokens for wider ones; SGLA_BF16 tiles the
+ *              the rounding: SGLA_F32 tiles by C tokens, except that the
+ *              forward with d_k > 32 and the backward with d_k or d_v > 32
+ *              tile by 32; SGLA_BF16 tiles the
  *              forward (and the dv scan of sgla_chunk_bwd) by 32 tokens for
  *              C = 32 and by 64 for C = 64 or 128, because a 128-token tile of
  *              q, k and v does not fit the four-deep LDS ring the bf16
